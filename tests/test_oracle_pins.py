@@ -1,0 +1,325 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test names what it pins: the pages' codec definition and byte accounting,
+exact integer arithmetic, a full sort, closed forms, a library GELU, and a dense
+brute force (tests/brute.py) written independently of the oracle.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_moe_bit_amd import synth
+from tests import brute
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------- bf16 rounding
+def test_bf16_rounding_matches_exact_rne():
+    rng = np.random.default_rng(11)
+    vals = list(rng.standard_normal(3000) * np.exp(rng.uniform(-20, 20, 3000)))
+    # exact midpoints between adjacent bf16 values: ties must go to the even pattern
+    for m in range(128, 256):
+        vals.append((m + 0.5) * 2.0 ** -7)
+        vals.append(-(m + 0.5) * 2.0 ** 3)
+    vals += [1.0, -1.0, 255.5 * 2 ** -7, 2.0 ** -130, 3.5 * 2 ** -133, 1e-40, 0.0]
+    for v in vals:
+        got = oracle.f64_to_bf16(float(v))
+        exp = brute.rne_bf16_exact(float(v))
+        got_v = float(brute.bf16_value(np.array([got], np.uint16))[0])
+        assert got_v == exp, (v, hex(got), got_v, exp)
+
+
+# ----------------------------------------------------------------------------- codec
+def _golden_groups():
+    groups = {}
+    for line in open(os.path.join(GOLD, "codec_groups.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        name, key, *vals = line.split()
+        g = groups.setdefault(name, {})
+        if key == "bits":
+            g[key] = int(vals[0])
+        elif key in ("scale", "bias"):
+            g[key] = int(vals[0], 16)
+        elif key == "bytes":
+            g[key] = np.array([int(v, 16) for v in vals], np.uint8)
+        elif key == "weights":
+            g[key] = np.array([float(v) for v in vals])
+    return groups
+
+
+@pytest.mark.parametrize("name", ["A", "B", "C"])
+def test_codec_hand_built_groups(name):
+    g = _golden_groups()[name]
+    got = oracle.dequant_row(g["bits"], g["bytes"], np.array([g["scale"]], np.uint16),
+                             np.array([g["bias"]], np.uint16), 64)
+    np.testing.assert_array_equal(got, g["weights"])
+
+
+def test_codec_group_boundaries():
+    """Scales/biases switch exactly every 64 elements; 4-bit low nibble is the even element."""
+    K = 256
+    codes = np.zeros(K // 2, np.uint8)
+    codes[0] = 0x21          # element 0 -> 1, element 1 -> 2
+    codes[32] = 0x03         # element 64 -> 3 (first of group 1)
+    codes[31] = 0x50         # element 63 -> 5 (last of group 0)
+    scales = synth.f32_to_bf16_bits(np.array([1.0, 2.0, 4.0, 8.0], np.float32))
+    biases = synth.f32_to_bf16_bits(np.array([0.0, 10.0, 100.0, 1000.0], np.float32))
+    w = oracle.dequant_row(4, codes, scales, biases, K)
+    assert w[0] == 1.0 and w[1] == 2.0 and w[63] == 5.0 and w[62] == 0.0
+    assert w[64] == 2.0 * 3 + 10.0 and w[65] == 10.0
+    assert w[128] == 100.0 and w[255] == 1000.0
+
+
+def test_expert_blob_byte_accounting():
+    """The canonical 4-bit g64 format reproduces the Mference expert blob size and totals."""
+    kv = {}
+    for line in open(os.path.join(GOLD, "expert_blob_bytes.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        k, v = line.split()
+        kv[k] = int(v)
+    dims = synth.Dims(kv["d_model"], kv["n_experts"], 8, kv["d_expert"], 2112)
+    rng = np.random.default_rng(0)
+    per_expert = 0
+    for out_dim, in_dim in ((dims.d_expert, dims.d_model),) * 2 + ((dims.d_model, dims.d_expert),):
+        m = synth.uniform_qmat(rng, (), out_dim, in_dim, 4)
+        per_expert += m.codes.nbytes + m.scales.nbytes + m.biases.nbytes
+    page = kv["page"]
+    blob = -(-per_expert // page) * page
+    assert blob == kv["blob_bytes"]
+    assert blob * kv["n_experts"] * kv["n_layers"] == kv["total_bytes"]
+
+
+# ----------------------------------------------------------------------------- router
+def _dyadic_router_case(rng, T=3, E=5, d=128):
+    """Inputs on which every fp32 operation of the router is exact."""
+    x = rng.integers(-4, 5, size=(T, d)).astype(np.float32)
+    q = rng.integers(0, 256, size=(E, d)).astype(np.uint8)
+    s = np.float32(2.0) ** -rng.integers(3, 7, size=(E, d // 64)).astype(np.float32)
+    b = -np.float32(2.0) ** -rng.integers(0, 3, size=(E, d // 64)).astype(np.float32)
+    return x, q, s, b
+
+
+def test_router_exact_integer_case():
+    rng = np.random.default_rng(3)
+    x, q, s, b = _dyadic_router_case(rng)
+    xb = synth.f32_to_bf16_bits(x)
+    sb, bb = synth.f32_to_bf16_bits(s), synth.f32_to_bf16_bits(b)
+    bias = np.array([0.5, -0.25, 0.0, 1.0, -2.0], np.float32)
+    got = oracle.router_logits(xb, q, sb, bb, bias)
+    T, d = x.shape
+    for t in range(T):
+        for e in range(q.shape[0]):
+            exact = Fraction(0)
+            for i in range(d):
+                w = Fraction(float(s[e, i // 64])) * int(q[e, i]) + Fraction(float(b[e, i // 64]))
+                exact += Fraction(float(x[t, i])) * w
+            exact += Fraction(float(bias[e]))
+            assert Fraction(float(got[t, e])) == exact
+
+
+def test_router_fp32_within_error_bound_of_fp64():
+    w = synth.Workload("r", synth.Dims(512, 16, 4, 64, 64), tokens=8, seed=5)
+    lay = synth.workload_layer(w)
+    x, _, _ = synth.workload_tokens(w, lay)
+    got = oracle.router_logits(x, lay.router.codes, lay.router.scales, lay.router.biases).astype(np.float64)
+    Wr = brute.dense(lay.router)
+    xv = brute.bf16_value(x)
+    exact = xv @ Wr.T
+    mag = np.abs(xv) @ np.abs(Wr).T + np.abs(xv) @ np.abs(brute.bf16_value(
+        np.repeat(lay.router.biases, 64, axis=1))).T
+    u = 2.0 ** -24
+    bound = 2 * (64 + lay.dims.G + 4) * u * mag
+    err = np.abs(got - exact)
+    assert np.all(err <= bound), (err.max(), bound.min())
+    # and the bound is tight enough to see a single dropped term
+    assert np.median(np.abs(xv[:, :1] * Wr[:, 0][None, :]) / bound) > 10
+
+
+def test_router_matches_brute_force_selection():
+    w = synth.WORKLOADS["tiny"]
+    lay = synth.workload_layer(w)
+    x, _, _ = synth.workload_tokens(w, lay, T=32)
+    r = oracle.route(lay, x)
+    b = brute.layer(lay, x[:6])
+    np.testing.assert_array_equal(r["idx"][:6], b["idx"])
+
+
+# ----------------------------------------------------------------------------- top-k
+def test_topk_equals_full_sort_with_ties():
+    rng = np.random.default_rng(7)
+    T, E = 200, 128
+    logits = rng.integers(-6, 6, size=(T, E)).astype(np.float32) * np.float32(0.5)   # many ties
+    logits[:50] = rng.standard_normal((50, E)).astype(np.float32)
+    for k in (1, 2, 8, 9, E):
+        idx, w = oracle.topk(logits, k)
+        for t in range(T):
+            order = np.lexsort((np.arange(E), -logits[t].astype(np.float64)))
+            np.testing.assert_array_equal(idx[t], order[:k])
+
+
+def test_softmax_weights_closed_forms():
+    rng = np.random.default_rng(8)
+    logits = rng.standard_normal((64, 16)).astype(np.float32) * 3
+    idx, w = oracle.topk(logits, 2)
+    l0 = logits[np.arange(64), idx[:, 0]].astype(np.float64)
+    l1 = logits[np.arange(64), idx[:, 1]].astype(np.float64)
+    np.testing.assert_allclose(w[:, 0], 1.0 / (1.0 + np.exp(l1 - l0)), rtol=1e-14)
+    idx, w = oracle.topk(logits, 8)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    assert np.all(np.diff(w, axis=1) <= 1e-15)                     # listed largest first
+    flat = np.zeros((1, 16), np.float32)
+    idx, w = oracle.topk(flat, 8)
+    np.testing.assert_array_equal(idx[0], np.arange(8))           # all tied: lowest indices
+    np.testing.assert_allclose(w[0], 1.0 / 8, rtol=1e-15)
+
+
+# ----------------------------------------------------------------------------- bucketing
+def test_bucket_matches_lexsort_and_invariants():
+    rng = np.random.default_rng(9)
+    T, E, k = 300, 128, 8
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    idx[:40] = np.arange(k)                   # a hot expert set
+    counts, offsets, perm, pos = oracle.bucket(idx, E)
+    np.testing.assert_array_equal(counts, np.bincount(idx.ravel(), minlength=E))
+    np.testing.assert_array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
+    pairs = np.arange(T * k)
+    ref = pairs[np.lexsort((pairs // k, idx.ravel()))]
+    np.testing.assert_array_equal(perm, ref)
+    np.testing.assert_array_equal(pos[perm], np.arange(T * k))
+    np.testing.assert_array_equal(np.sort(perm), pairs)
+
+
+# ----------------------------------------------------------------------------- GELU
+def test_gelu_tanh_matches_library():
+    xs = np.concatenate([np.linspace(-12, 12, 481), [0.0, 1.0, -1.0, 1e-8, 30.0, -30.0]])
+    ref = torch.nn.functional.gelu(torch.from_numpy(xs), approximate="tanh").numpy()
+    got = np.array([oracle.gelu_tanh(v) for v in xs])
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-15)
+    assert oracle.gelu_tanh(0.0) == 0.0
+    assert oracle.gelu_tanh(30.0) == 30.0 and oracle.gelu_tanh(-30.0) == 0.0
+
+
+# ----------------------------------------------------------------------------- layer
+def _cmp_layer(lay, x, ntok):
+    r = oracle.route(lay, x[:ntok])
+    y = oracle.layer_tokens(lay, x[:ntok], r["idx"], r["w"])
+    b = brute.layer(lay, x[:ntok])
+    np.testing.assert_array_equal(r["idx"], b["idx"])
+    np.testing.assert_allclose(r["w"], b["w"], rtol=2e-6)        # fp32 vs fp64 logits
+    scale = np.sqrt(np.mean(b["y"] ** 2))
+    assert np.max(np.abs(y - b["y"])) <= 1e-5 * scale, np.max(np.abs(y - b["y"])) / scale
+    return y, b
+
+
+def test_layer_matches_dense_brute_force_tiny_workload():
+    w = synth.WORKLOADS["tiny"]
+    lay = synth.workload_layer(w)
+    x, _, _ = synth.workload_tokens(w, lay)
+    _cmp_layer(lay, x, w.tokens)
+
+
+def test_layer_matches_dense_brute_force_odd_shapes():
+    dims = synth.Dims(d_model=192, n_experts=5, top_k=3, d_expert=64, d_shared=128)
+    lay = synth.gen_layer(dims, 21, router="normal", zipf_s=1.0)
+    x, _, _ = synth.gen_tokens(dims, 3, 21)
+    _cmp_layer(lay, x, 3)
+
+
+def test_identical_experts_make_output_independent_of_routing():
+    dims = synth.Dims(d_model=128, n_experts=6, top_k=2, d_expert=64, d_shared=64)
+    lay = synth.gen_layer(dims, 31, router="uniform")
+    for m in (lay.gate, lay.up, lay.down):
+        m.codes[:] = m.codes[0]
+        m.scales[:] = m.scales[0]
+        m.biases[:] = m.biases[0]
+    x, _, _ = synth.gen_tokens(dims, 5, 31)
+    y1, r1 = oracle.layer_forward(lay, x)
+    lay.router.codes[:] = np.random.default_rng(1).integers(0, 256, lay.router.codes.shape, dtype=np.uint8)
+    y2, r2 = oracle.layer_forward(lay, x)
+    assert not np.array_equal(r1["idx"], r2["idx"])
+    scale = np.sqrt(np.mean(y1 ** 2))
+    assert np.max(np.abs(y1 - y2)) <= 1e-13 * scale
+
+
+def test_shared_branch_added_without_weight():
+    dims = synth.Dims(d_model=128, n_experts=4, top_k=2, d_expert=64, d_shared=128)
+    lay = synth.gen_layer(dims, 41, router="uniform")
+    x, _, _ = synth.gen_tokens(dims, 3, 41)
+    y_full, sh, r = oracle.layer_tokens(lay, x, *oracle.topk(oracle.route(lay, x)["logits"], 2),
+                                        want_parts=True)
+    # shared part equals the dense brute force of the shared expert alone, unscaled
+    for t in range(3):
+        ref = brute.ffn_dense(brute.bf16_value(x[t]), brute.dense(lay.sh_gate), brute.dense(lay.sh_up),
+                              brute.dense(lay.sh_down))
+        np.testing.assert_allclose(sh[t], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    # zero routed down projections: output is exactly the shared branch
+    lay.down.scales[:] = 0
+    lay.down.biases[:] = 0
+    y0 = oracle.layer_forward(lay, x)[0]
+    np.testing.assert_array_equal(y0, sh)
+
+
+def test_constructed_ties_pick_lowest_indices():
+    dims = synth.Dims(d_model=512, n_experts=40, top_k=8, d_expert=64, d_shared=64)
+    lay = synth.gen_layer(dims, 51, router="normal", zipf_s=1.3, tie_groups=True)
+    x, tied, grp = synth.gen_tokens(dims, 50, 51, layer=lay, tie_frac=0.1)
+    r = oracle.route(lay, x)
+    assert len(tied) == 5
+    for t, g in zip(tied, grp):
+        members = lay.tie_groups[g]
+        lg = r["logits"][t]
+        assert np.all(lg[members] == lg[members[0]])               # bit-equal logits
+        order = np.sort(lg)[::-1]
+        assert order[7] == order[8]                                  # ranks 8 and 9 tie
+        full = np.lexsort((np.arange(dims.n_experts), -lg.astype(np.float64)))
+        np.testing.assert_array_equal(r["idx"][t], full[:8])
+        kept = np.intersect1d(r["idx"][t], members)
+        np.testing.assert_array_equal(kept, members[:len(kept)])    # lowest indices kept
+        assert len(kept) < 9
+    # brute force (fp64, its own summation) agrees on the tied tokens' selection
+    b = brute.layer(lay, x[tied[:2]])
+    np.testing.assert_array_equal(b["idx"], r["idx"][tied[:2]])
+
+
+def test_threads_do_not_change_results():
+    w = synth.Workload("t", synth.Dims(256, 16, 4, 64, 128), tokens=24, seed=61)
+    lay = synth.workload_layer(w)
+    x, _, _ = synth.workload_tokens(w, lay)
+    n0 = oracle.get_threads()
+    try:
+        oracle.set_threads(1)
+        y1, r1 = oracle.layer_forward(lay, x)
+        oracle.set_threads(max(2, n0))
+        y2, r2 = oracle.layer_forward(lay, x)
+    finally:
+        oracle.set_threads(n0)
+    np.testing.assert_array_equal(r1["logits"], r2["logits"])
+    np.testing.assert_array_equal(y1, y2)
+
+
+# ----------------------------------------------------------------------------- stack glue
+def test_stack_glue_closed_forms():
+    d = 256
+    h = synth.f32_to_bf16_bits(np.full((1, d), 3.0, np.float32))
+    y = np.full((1, d), 1.0)
+    hn, xn = oracle.stack_glue(h, y, eps=0.0)
+    assert np.all(brute.bf16_value(hn) == 4.0)
+    assert np.all(brute.bf16_value(xn) == 1.0)                 # constant vector normalizes to 1
+    rng = np.random.default_rng(71)
+    h = synth.f32_to_bf16_bits(rng.standard_normal((4, d)).astype(np.float32) * 5)
+    y = rng.standard_normal((4, d))
+    hn, xn = oracle.stack_glue(h, y)
+    ref_h = brute.bf16_value(h) + y
+    for t in range(4):
+        for i in range(0, d, 17):
+            assert float(brute.bf16_value(hn[t, i])) == brute.rne_bf16_exact(float(ref_h[t, i]))
+    xv = brute.bf16_value(xn)
+    np.testing.assert_allclose(np.sqrt(np.mean(xv ** 2, axis=1)), 1.0, rtol=4e-3)

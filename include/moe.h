@@ -1,0 +1,208 @@
+/*
+ * moe.h -- C ABI of the MI355X quantized mixture-of-experts FFN layer.
+ *
+ * One layer of a Gemma-4-style MoE transformer FFN, as the Mference system
+ * design describes it ("Why the runtime has this shape"; "Decode"; "Prefill"):
+ *
+ *   - an 8-bit group-64 affine router projection gives one logit per routed
+ *     expert (no softcap); the top-k logits are kept, largest first, ties going
+ *     to the lower expert index, and their softmax gives the routing weights;
+ *   - each routed expert is a GELU-gated FFN (gate and up projections, tanh-form
+ *     GELU of the gate times up, down projection) with 4-bit group-64 affine
+ *     weights: weight = scale * code + bias, one BF16 scale and one BF16 bias
+ *     per 64 consecutive input elements;
+ *   - a dense shared expert of the same form runs on the same input and is added
+ *     without a routing weight;
+ *   - the routed outputs are reduced with their routing weights (Mference,
+ *     "Decode", cb2 phase) in the fixed slot order 0..k-1, in fp32.
+ *
+ * All compute runs in gfx950 HIP kernels on the stream the caller passes. Every
+ * entry point validates its arguments on the host before enqueuing anything; on
+ * error nothing is enqueued, nothing is written, and the handle stays usable.
+ * No entry point reads device memory back to the host.
+ *
+ * Memory ownership:
+ *   - weights are caller-owned device buffers in the device layout moe_repack
+ *     produces; the layer borrows them (never copies or writes them) and they
+ *     must stay valid and unchanged until moe_layer_destroy;
+ *   - the layer owns one workspace, allocated at moe_layer_create for
+ *     dims.max_tokens tokens and reused in stream order; calls on one handle must
+ *     be issued on one stream, or serialized by the caller, because a queued
+ *     kernel owns the workspace until it completes (Mference, "Correctness and
+ *     safety invariants");
+ *   - activations and outputs are caller-owned device buffers.
+ *
+ * Device pointers must be 16-byte aligned. Activations are bf16 bit patterns
+ * (uint16_t), outputs fp32.
+ */
+#ifndef QMOE_MOE_H
+#define QMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_layer moe_layer; /* opaque handle */
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_E_INVALID = 1,  /* null required pointer, unknown flag, bad enum value */
+    MOE_E_SHAPE = 2,    /* dimension not a multiple of 64 / 32, top_k out of range, T < 0 */
+    MOE_E_QUANT = 3,    /* group != 64, router bits != 8, expert bits != 4 */
+    MOE_E_ALIGN = 4,    /* a device pointer is not 16-byte aligned */
+    MOE_E_CAPACITY = 5, /* T above max_tokens (or above MOE_MAX_DECODE_TOKENS for decode) */
+    MOE_E_NOMEM = 6,    /* workspace allocation failed */
+    MOE_E_DEVICE = 7    /* a HIP call or kernel launch reported an error */
+} moe_status;
+
+/* Largest token count moe_forward_decode accepts; larger chunks use moe_forward_prefill. */
+#define MOE_MAX_DECODE_TOKENS 16
+/* Largest top_k the kernels support. */
+#define MOE_MAX_TOP_K 16
+/* Largest number of routed experts the kernels support. */
+#define MOE_MAX_EXPERTS 1024
+
+typedef struct {
+    int32_t d_model;     /* model width d; multiple of 64, at most 8192 */
+    int32_t n_experts;   /* routed experts E, 1..MOE_MAX_EXPERTS */
+    int32_t top_k;       /* experts per token k, 1..min(E, MOE_MAX_TOP_K) */
+    int32_t d_expert;    /* routed expert width I; multiple of 64 */
+    int32_t d_shared;    /* shared expert width I_s; multiple of 64 */
+    int32_t group;       /* quantization group; must be 64 */
+    int32_t router_bits; /* must be 8 */
+    int32_t expert_bits; /* must be 4 */
+    int32_t max_tokens;  /* workspace capacity in tokens per call, >= 1 */
+} moe_dims;
+
+/*
+ * One quantized matrix (or a stack of E of them) in the device layout:
+ *   codes: device bytes, layout per moe_repack;
+ *   sb:    device uint32 words, each (bf16 scale) | (bf16 bias << 16), one per
+ *          (row, group of 64 inputs), layout per moe_repack.
+ */
+typedef struct {
+    const void *codes;
+    const uint32_t *sb;
+} moe_qmat;
+
+typedef struct {
+    moe_qmat router;          /* [E, d] 8-bit */
+    moe_qmat gate, up;        /* E x [I, d] 4-bit */
+    moe_qmat down;            /* E x [d, I] 4-bit */
+    moe_qmat sh_gate, sh_up;  /* [I_s, d] 4-bit */
+    moe_qmat sh_down;         /* [d, I_s] 4-bit */
+    const float *logit_bias;  /* optional fp32 [E] added to every token's router logits (routing skew); may be NULL */
+} moe_weights;
+
+/*
+ * Create a layer handle. Validates dims (MOE_E_QUANT, MOE_E_SHAPE), the weight
+ * pointers (MOE_E_INVALID if any required pointer is NULL, MOE_E_ALIGN if not
+ * 16-byte aligned) and flags (must be 0, else MOE_E_INVALID), then allocates the
+ * workspace for dims->max_tokens tokens on the current HIP device (MOE_E_NOMEM).
+ * *out is written only on MOE_OK.
+ */
+moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t flags,
+                            moe_layer **out);
+
+/* Frees the workspace. Waits for the device to finish work that may use it. NULL is a no-op. */
+void moe_layer_destroy(moe_layer *layer);
+
+/*
+ * Router and grouping only (Mference, "Decode": the router listing, without the
+ * norm prologue and per-expert scale; "Prefill": token/expert pairs grouped by
+ * expert). For T tokens x (bf16 [T, d]):
+ *   logits     fp32 [T, E]   optional (NULL to skip): router logits (+ logit_bias)
+ *   topk_idx   int32 [T, k]  the k selected experts, largest logit first, ties to lower index
+ *   topk_w     fp32 [T, k]   softmax of the selected logits
+ *   expert_offsets int32 [E+1] optional: offsets[e] = number of pairs routed to experts < e
+ *   pair_perm  int32 [T*k]   optional: pair ids p = t*k + slot ordered by (expert, token)
+ * expert_offsets and pair_perm must be both given or both NULL.
+ * T = 0 is a no-op; T > max_tokens is MOE_E_CAPACITY.
+ */
+moe_status moe_route(moe_layer *layer, const uint16_t *x, int32_t T, int32_t *topk_idx,
+                     float *topk_w, float *logits, int32_t *expert_offsets, int32_t *pair_perm,
+                     void *hip_stream);
+
+/*
+ * Full layer, decode path (wavefront GEMV kernels), for 1 <= T <= MOE_MAX_DECODE_TOKENS:
+ *   y[t] = shared(x[t]) + sum_{s<k} w[t,s] * expert_{idx[t,s]}(x[t])      fp32 [T, d]
+ * T = 0 is a no-op; T above MOE_MAX_DECODE_TOKENS or max_tokens is MOE_E_CAPACITY.
+ */
+moe_status moe_forward_decode(moe_layer *layer, const uint16_t *x, int32_t T, float *y,
+                              void *hip_stream);
+
+/*
+ * Full layer, prefill path (grouped MFMA GEMM over expert-bucketed rows), for
+ * 1 <= T <= max_tokens. Same result definition as moe_forward_decode.
+ */
+moe_status moe_forward_prefill(moe_layer *layer, const uint16_t *x, int32_t T, float *y,
+                               void *hip_stream);
+
+/*
+ * Residual stream between stacked layers (device, bf16 bit patterns):
+ *   h_next = bf16(h + y)                                  (y may be NULL: h_next = h)
+ *   x_next = bf16(h_next / sqrt(mean(h_next^2) + 1e-6))   (norm without a learned scale)
+ * h, h_next, x_next: [T, d] bf16; y: [T, d] fp32. h_next may alias h.
+ */
+moe_status moe_stack_glue(const uint16_t *h, const float *y, uint16_t *h_next, uint16_t *x_next,
+                          int32_t T, int32_t d, void *hip_stream);
+
+/* ---------------------------------------------------------------- host-side weight layout */
+
+/* Canonical host layout of one matrix or a stack of n_mats matrices [out, in]:
+ *   codes  [n_mats, out, in*bits/8] bytes; 4-bit codes two per byte, the lower-indexed
+ *          element in the low nibble (eight per little-endian u32); 8-bit one per byte
+ *   scales [n_mats, out, in/64] bf16 bits;  biases [n_mats, out, in/64] bf16 bits */
+typedef struct {
+    const uint8_t *codes;
+    const uint16_t *scales;
+    const uint16_t *biases;
+} moe_host_qmat;
+
+/* Bytes of the device layout: part 0 = codes, part 1 = sb words. 0 on invalid arguments. */
+size_t moe_packed_bytes(int32_t bits, int32_t n_mats, int32_t out_dim, int32_t in_dim, int32_t part);
+
+/*
+ * Host-to-host lossless repack from the canonical layout to the device layout: codes
+ * are moved, never re-quantized (Mference, "Source weights and bounded repack";
+ * "Correctness and safety invariants": repack must be exactly invertible).
+ *   bits 8 (router): codes stay [n_mats, out, in]; sb is [n_mats, out, in/64].
+ *   bits 4 (experts): out must be a multiple of 32. Per matrix, 1 KiB tiles of 32 rows x
+ *     64 inputs, ordered (row block, group); inside a tile, 64 lanes x 16 bytes, lane l
+ *     holding row (l % 32), inputs 16*s + 8*(l / 32) + j for step s = 0..3 and j = 0..7,
+ *     one u32 per step with element j in nibble (j even ? j/2 : 4 + j/2).
+ *     sb words ordered (row block, group, row in block).
+ * Returns MOE_E_SHAPE / MOE_E_QUANT / MOE_E_INVALID on bad arguments (nothing written).
+ */
+moe_status moe_repack(int32_t bits, int32_t n_mats, int32_t out_dim, int32_t in_dim,
+                      const moe_host_qmat *canonical, void *codes_out, uint32_t *sb_out);
+
+/* Exact inverse of moe_repack (host to host). */
+moe_status moe_unrepack(int32_t bits, int32_t n_mats, int32_t out_dim, int32_t in_dim,
+                        const void *codes_in, const uint32_t *sb_in, uint8_t *codes,
+                        uint16_t *scales, uint16_t *biases);
+
+/* ---------------------------------------------------------------- diagnostics */
+
+const char *moe_status_str(moe_status s);
+/* Message of the last failed call on this thread ("" if none). */
+const char *moe_last_error(void);
+
+/*
+ * Per-kernel timing with HIP events recorded around each kernel on the caller's
+ * stream. Off by default; it never changes results. moe_profile_read synchronizes
+ * the recorded events and returns the summed milliseconds and launch count of
+ * kernel id since the last reset. moe_kernel_name(id) is NULL past the last id.
+ */
+moe_status moe_profile_enable(moe_layer *layer, int32_t on);
+moe_status moe_profile_read(moe_layer *layer, int32_t kernel_id, double *total_ms, int64_t *launches);
+moe_status moe_profile_reset(moe_layer *layer);
+const char *moe_kernel_name(int32_t kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMOE_MOE_H */

@@ -1,0 +1,198 @@
+"""Thin Python binding of the C ABI in include/moe.h (ctypes; argument marshalling only).
+
+Every function here has the name of the C entry point it calls and does no
+computation of its own: all of the layer runs in the gfx950 kernels of
+libmoe.so. PyTorch supplies device memory and the HIP stream. If the library
+is missing, loading fails loudly; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import numpy as np
+
+from . import build as _build
+
+LIB_PATH = _build.LIB
+_lib = None
+
+MOE_OK, MOE_E_INVALID, MOE_E_SHAPE, MOE_E_QUANT, MOE_E_ALIGN, MOE_E_CAPACITY, MOE_E_NOMEM, MOE_E_DEVICE = range(8)
+MOE_MAX_DECODE_TOKENS = 16
+KERNEL_NAMES = []
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str, msg: str):
+        super().__init__(f"{what}: {status_str(status)}: {msg}")
+        self.status = status
+
+
+class moe_dims(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("d_model", "n_experts", "top_k", "d_expert", "d_shared", "group",
+                                         "router_bits", "expert_bits", "max_tokens")]
+
+
+class moe_qmat(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("sb", C.c_void_p)]
+
+
+class moe_weights(C.Structure):
+    _fields_ = [(n, moe_qmat) for n in ("router", "gate", "up", "down", "sh_gate", "sh_up", "sh_down")] + \
+               [("logit_bias", C.c_void_p)]
+
+
+class moe_host_qmat(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("biases", C.c_void_p)]
+
+
+def lib() -> C.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m quantized_moe_bit_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, st = C.c_void_p, C.c_int32, C.c_int
+        sig = {
+            "moe_layer_create": (st, [C.POINTER(moe_dims), C.POINTER(moe_weights), C.c_uint32, C.POINTER(vp)]),
+            "moe_layer_destroy": (None, [vp]),
+            "moe_route": (st, [vp, vp, i32, vp, vp, vp, vp, vp, vp]),
+            "moe_forward_decode": (st, [vp, vp, i32, vp, vp]),
+            "moe_forward_prefill": (st, [vp, vp, i32, vp, vp]),
+            "moe_stack_glue": (st, [vp, vp, vp, vp, i32, i32, vp]),
+            "moe_packed_bytes": (C.c_size_t, [i32, i32, i32, i32, i32]),
+            "moe_repack": (st, [i32, i32, i32, i32, C.POINTER(moe_host_qmat), vp, vp]),
+            "moe_unrepack": (st, [i32, i32, i32, i32, vp, vp, vp, vp, vp]),
+            "moe_status_str": (C.c_char_p, [st]),
+            "moe_last_error": (C.c_char_p, []),
+            "moe_profile_enable": (st, [vp, i32]),
+            "moe_profile_read": (st, [vp, i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
+            "moe_profile_reset": (st, [vp]),
+            "moe_kernel_name": (C.c_char_p, [i32]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+        KERNEL_NAMES.clear()
+        i = 0
+        while True:
+            nm = L.moe_kernel_name(i)
+            if nm is None:
+                break
+            KERNEL_NAMES.append(nm.decode())
+            i += 1
+    return _lib
+
+
+def status_str(s: int) -> str:
+    return lib().moe_status_str(s).decode()
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def _check(status: int, what: str):
+    if status != MOE_OK:
+        raise MoeError(status, what, moe_last_error())
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ----------------------------------------------------------------------------- entry points
+def moe_layer_create(dims: moe_dims, weights: moe_weights, flags: int = 0) -> int:
+    h = C.c_void_p()
+    _check(lib().moe_layer_create(C.byref(dims), C.byref(weights), flags, C.byref(h)), "moe_layer_create")
+    return h.value
+
+
+def moe_layer_destroy(handle: int) -> None:
+    lib().moe_layer_destroy(handle)
+
+
+def moe_route(handle, x, T, topk_idx, topk_w, logits=None, expert_offsets=None, pair_perm=None, stream=None):
+    _check(lib().moe_route(handle, _ptr(x), T, _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _ptr(expert_offsets),
+                           _ptr(pair_perm), _stream(stream)), "moe_route")
+
+
+def moe_forward_decode(handle, x, T, y, stream=None):
+    _check(lib().moe_forward_decode(handle, _ptr(x), T, _ptr(y), _stream(stream)), "moe_forward_decode")
+
+
+def moe_forward_prefill(handle, x, T, y, stream=None):
+    _check(lib().moe_forward_prefill(handle, _ptr(x), T, _ptr(y), _stream(stream)), "moe_forward_prefill")
+
+
+def moe_stack_glue(h, y, h_next, x_next, T, d, stream=None):
+    _check(lib().moe_stack_glue(_ptr(h), _ptr(y), _ptr(h_next), _ptr(x_next), T, d, _stream(stream)),
+           "moe_stack_glue")
+
+
+def moe_packed_bytes(bits, n_mats, out_dim, in_dim, part) -> int:
+    return int(lib().moe_packed_bytes(bits, n_mats, out_dim, in_dim, part))
+
+
+def moe_repack(bits, n_mats, out_dim, in_dim, codes, scales, biases):
+    """Canonical host arrays -> (device-layout codes uint8, sb uint32), both host NumPy arrays."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint16)
+    biases = np.ascontiguousarray(biases, np.uint16)
+    nc = moe_packed_bytes(bits, n_mats, out_dim, in_dim, 0)
+    ns = moe_packed_bytes(bits, n_mats, out_dim, in_dim, 1)
+    out_c = np.empty(max(nc, 1), np.uint8)
+    out_s = np.empty(max(ns // 4, 1), np.uint32)
+    src = moe_host_qmat(codes.ctypes.data, scales.ctypes.data, biases.ctypes.data)
+    _check(lib().moe_repack(bits, n_mats, out_dim, in_dim, C.byref(src), out_c.ctypes.data, out_s.ctypes.data),
+           "moe_repack")
+    return out_c, out_s
+
+
+def moe_unrepack(bits, n_mats, out_dim, in_dim, codes_dev, sb_dev):
+    G = in_dim // 64
+    codes = np.empty((n_mats, out_dim, in_dim * bits // 8), np.uint8)
+    scales = np.empty((n_mats, out_dim, G), np.uint16)
+    biases = np.empty((n_mats, out_dim, G), np.uint16)
+    codes_dev = np.ascontiguousarray(codes_dev, np.uint8)
+    sb_dev = np.ascontiguousarray(sb_dev, np.uint32)
+    _check(lib().moe_unrepack(bits, n_mats, out_dim, in_dim, codes_dev.ctypes.data, sb_dev.ctypes.data,
+                              codes.ctypes.data, scales.ctypes.data, biases.ctypes.data), "moe_unrepack")
+    return codes, scales, biases
+
+
+def moe_profile_enable(handle, on: bool):
+    _check(lib().moe_profile_enable(handle, int(bool(on))), "moe_profile_enable")
+
+
+def moe_profile_read(handle, kernel_id: int):
+    ms, n = C.c_double(), C.c_int64()
+    _check(lib().moe_profile_read(handle, kernel_id, C.byref(ms), C.byref(n)), "moe_profile_read")
+    return ms.value, n.value
+
+
+def moe_profile_reset(handle):
+    _check(lib().moe_profile_reset(handle), "moe_profile_reset")
+
+
+def kernel_id(name: str) -> int:
+    lib()
+    return KERNEL_NAMES.index(name)

@@ -1,0 +1,59 @@
+// Device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace qmoe {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// float -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Two bf16 values (1 + q/16) built from the nibbles of one device-layout word.
+// Pair p (0..3) holds elements 2p and 2p+1 of the word's eight inputs; element j sits in
+// nibble (j even ? j/2 : 4 + j/2), so pair p is nibbles p and 4+p: shifting them to bits 3..6
+// and 19..22 and or-ing the exponent of 1.0 gives bf16 values 1 + q/16 (exact).
+template <int P>
+__device__ __forceinline__ uint32_t nib_pair(uint32_t w) {
+    uint32_t t;
+    if constexpr (P == 0) t = w << 3;
+    else t = w >> (4 * P - 3);
+    return (t & 0x00780078u) | 0x3F803F80u;
+}
+
+// One 16-byte MFMA B fragment (8 bf16) from one device-layout word.
+__device__ __forceinline__ bf16x8_t nib_frag(uint32_t w) {
+    u32x4_t v = {nib_pair<0>(w), nib_pair<1>(w), nib_pair<2>(w), nib_pair<3>(w)};
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                          false);
+}
+
+// tanh-form GELU, fp32.
+__device__ __forceinline__ float gelu_tanh_f32(float v) {
+    const float c = 0.7978845608028654f;
+    float z = c * (v + 0.044715f * v * v * v);
+    // tanh(z) = 1 - 2 / (exp(2z) + 1), saturating for large |z|
+    float e = __expf(2.0f * z);
+    float t = 1.0f - 2.0f / (e + 1.0f);
+    return 0.5f * v * (1.0f + t);
+}
+
+__device__ __forceinline__ u32x4_t ld16(const void *p) { return *reinterpret_cast<const u32x4_t *>(p); }
+
+}  // namespace qmoe

@@ -1,0 +1,417 @@
+// Host side of the C ABI: argument validation (entirely before any enqueue), the
+// layer-owned workspace, and the stream-ordered kernel sequences of the decode and
+// prefill paths. Errors never cross the ABI as exceptions; a failed call leaves the
+// handle usable and writes nothing.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "moe_internal.h"
+
+namespace qmoe {
+
+static thread_local char g_err[512] = "";
+
+moe_status fail(moe_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+namespace {
+
+const char *kKernelNames[K_COUNT] = {"router",       "topk",        "bucket_rank", "bucket_scan",
+                                     "bucket_scatter", "dec_gateup", "dec_down",    "pre_gateup",
+                                     "pre_down",     "combine",     "glue"};
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status check_dims(const moe_dims *D) {
+    if (!D) return fail(MOE_E_INVALID, "dims is NULL");
+    if (D->group != 64) return fail(MOE_E_QUANT, "group must be 64, got %d", D->group);
+    if (D->router_bits != 8) return fail(MOE_E_QUANT, "router_bits must be 8, got %d", D->router_bits);
+    if (D->expert_bits != 4) return fail(MOE_E_QUANT, "expert_bits must be 4, got %d", D->expert_bits);
+    if (D->d_model < 64 || D->d_model % 128 || D->d_model > 8192)
+        return fail(MOE_E_SHAPE, "d_model %d must be a multiple of 128 in [128, 8192]", D->d_model);
+    if (D->d_expert < 64 || D->d_expert % 64)
+        return fail(MOE_E_SHAPE, "d_expert %d must be a positive multiple of 64", D->d_expert);
+    if (D->d_shared < 64 || D->d_shared % 64)
+        return fail(MOE_E_SHAPE, "d_shared %d must be a positive multiple of 64", D->d_shared);
+    if (D->n_experts < 1 || D->n_experts > MOE_MAX_EXPERTS)
+        return fail(MOE_E_SHAPE, "n_experts %d out of range [1, %d]", D->n_experts, MOE_MAX_EXPERTS);
+    if (D->top_k < 1 || D->top_k > D->n_experts || D->top_k > MOE_MAX_TOP_K)
+        return fail(MOE_E_SHAPE, "top_k %d out of range [1, min(n_experts, %d)]", D->top_k, MOE_MAX_TOP_K);
+    if (D->max_tokens < 1 || D->max_tokens > (1 << 20))
+        return fail(MOE_E_SHAPE, "max_tokens %d out of range [1, 2^20]", D->max_tokens);
+    return MOE_OK;
+}
+
+moe_status check_qmat(const moe_qmat &m, const char *name) {
+    if (!m.codes || !m.sb) return fail(MOE_E_INVALID, "weight %s: NULL pointer", name);
+    if (!aligned16(m.codes) || !aligned16(m.sb)) return fail(MOE_E_ALIGN, "weight %s: pointer not 16-byte aligned", name);
+    return MOE_OK;
+}
+
+moe_status check_weights(const moe_weights *w) {
+    if (!w) return fail(MOE_E_INVALID, "weights is NULL");
+    moe_status s;
+    if ((s = check_qmat(w->router, "router")) != MOE_OK) return s;
+    if ((s = check_qmat(w->gate, "gate")) != MOE_OK) return s;
+    if ((s = check_qmat(w->up, "up")) != MOE_OK) return s;
+    if ((s = check_qmat(w->down, "down")) != MOE_OK) return s;
+    if ((s = check_qmat(w->sh_gate, "sh_gate")) != MOE_OK) return s;
+    if ((s = check_qmat(w->sh_up, "sh_up")) != MOE_OK) return s;
+    if ((s = check_qmat(w->sh_down, "sh_down")) != MOE_OK) return s;
+    if (w->logit_bias && !aligned16(w->logit_bias)) return fail(MOE_E_ALIGN, "logit_bias not 16-byte aligned");
+    return MOE_OK;
+}
+
+moe_status check_call(moe_layer *L, const void *x, int32_t T, const void *out, const char *what) {
+    if (!L) return fail(MOE_E_INVALID, "%s: layer is NULL", what);
+    if (T < 0) return fail(MOE_E_SHAPE, "%s: T = %d is negative", what, T);
+    if (T > L->dims.max_tokens)
+        return fail(MOE_E_CAPACITY, "%s: T = %d exceeds max_tokens %d", what, T, L->dims.max_tokens);
+    if (T == 0) return MOE_OK;
+    if (!x || !out) return fail(MOE_E_INVALID, "%s: NULL input or output", what);
+    if (!aligned16(x) || !aligned16(out)) return fail(MOE_E_ALIGN, "%s: input/output not 16-byte aligned", what);
+    return MOE_OK;
+}
+
+// Bump allocator over one device allocation; every region 256-byte aligned.
+struct Plan {
+    size_t off = 0;
+    template <class T>
+    size_t take(T **p, size_t count) {
+        off = (off + 255) & ~size_t(255);
+        const size_t at = off;
+        off += sizeof(T) * (count ? count : 1);
+        *p = reinterpret_cast<T *>(at);  // offset for now; rebased after allocation
+        return at;
+    }
+};
+
+template <class T>
+void rebase(T *&p, char *base) {
+    p = reinterpret_cast<T *>(base + reinterpret_cast<uintptr_t>(p));
+}
+
+hipError_t prof_begin(moe_layer *L, int id, hipStream_t s, hipEvent_t *a, hipEvent_t *b) {
+    (void)id;
+    if (!L->prof_on) return hipSuccess;
+    auto grab = [&](hipEvent_t *e) -> hipError_t {
+        if (!L->prof_pool.empty()) {
+            *e = L->prof_pool.back();
+            L->prof_pool.pop_back();
+            return hipSuccess;
+        }
+        return hipEventCreate(e);
+    };
+    hipError_t err = grab(a);
+    if (err != hipSuccess) return err;
+    if ((err = grab(b)) != hipSuccess) return err;
+    return hipEventRecord(*a, s);
+}
+
+hipError_t prof_end(moe_layer *L, int id, hipStream_t s, hipEvent_t a, hipEvent_t b) {
+    if (!L->prof_on) return hipSuccess;
+    hipError_t err = hipEventRecord(b, s);
+    L->prof_pending.push_back(ProfEvent{id, a, b});
+    return err;
+}
+
+// Runs one launcher, with optional event timing, mapping errors to MOE_E_DEVICE.
+template <class F>
+moe_status run(moe_layer *L, int id, hipStream_t s, F &&f) {
+    hipEvent_t a = nullptr, b = nullptr;
+    hipError_t err = prof_begin(L, id, s, &a, &b);
+    if (err == hipSuccess) err = f();
+    if (err == hipSuccess) err = prof_end(L, id, s, a, b);
+    if (err != hipSuccess) return fail(MOE_E_DEVICE, "kernel %s: %s", kKernelNames[id], hipGetErrorString(err));
+    return MOE_OK;
+}
+
+#define RUN(id, expr)                                              \
+    do {                                                           \
+        moe_status _st = run(L, id, s, [&]() { return (expr); }); \
+        if (_st != MOE_OK) return _st;                             \
+    } while (0)
+
+moe_status route_impl(moe_layer *L, const uint16_t *x, int T, hipStream_t s, float *logits, int32_t *idx,
+                      float *w, bool bucket, int32_t *perm_out) {
+    RUN(K_ROUTER, launch_router(L, x, T, logits, s));
+    RUN(K_TOPK, launch_topk(L, T, logits, idx, w, s));
+    if (bucket) {
+        RUN(K_BUCKET_RANK, launch_bucket_rank(L, T, idx, s));
+        RUN(K_BUCKET_SCAN, launch_bucket_scan(L, T, s));
+        RUN(K_BUCKET_SCATTER, launch_bucket_scatter(L, T, idx, perm_out, s));
+    }
+    return MOE_OK;
+}
+
+}  // namespace
+}  // namespace qmoe
+
+using namespace qmoe;
+
+extern "C" {
+
+const char *moe_status_str(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_E_INVALID: return "MOE_E_INVALID";
+        case MOE_E_SHAPE: return "MOE_E_SHAPE";
+        case MOE_E_QUANT: return "MOE_E_QUANT";
+        case MOE_E_ALIGN: return "MOE_E_ALIGN";
+        case MOE_E_CAPACITY: return "MOE_E_CAPACITY";
+        case MOE_E_NOMEM: return "MOE_E_NOMEM";
+        case MOE_E_DEVICE: return "MOE_E_DEVICE";
+    }
+    return "MOE_E_UNKNOWN";
+}
+
+const char *moe_last_error(void) { return g_err; }
+
+const char *moe_kernel_name(int32_t id) { return (id >= 0 && id < K_COUNT) ? kKernelNames[id] : nullptr; }
+
+moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t flags, moe_layer **out) {
+    clear_error();
+    if (!out) return fail(MOE_E_INVALID, "out is NULL");
+    moe_status st = check_dims(dims);
+    if (st != MOE_OK) return st;
+    if ((st = check_weights(w)) != MOE_OK) return st;
+    if (flags != 0) return fail(MOE_E_INVALID, "unknown flags 0x%x", flags);
+
+    moe_layer *L = new (std::nothrow) moe_layer();
+    if (!L) return fail(MOE_E_NOMEM, "host allocation failed");
+    L->dims = *dims;
+    L->w = *w;
+    L->prof_on = false;
+    for (int i = 0; i < K_COUNT; ++i) {
+        L->prof_ms[i] = 0.0;
+        L->prof_n[i] = 0;
+    }
+    const moe_dims &D = *dims;
+    const int E = D.n_experts, k = D.top_k, d = D.d_model, I = D.d_expert, Is = D.d_shared;
+    const size_t Tm = (size_t)D.max_tokens, P = Tm * k;
+    L->G_d = d / 64;
+    L->G_I = I / 64;
+    L->G_Is = Is / 64;
+    L->Gp_d = roundup(L->G_d, 16);
+    L->Gp_I = roundup(L->G_I, 16);
+    L->Gp_Is = roundup(L->G_Is, 16);
+    L->max_dec = D.max_tokens < MOE_MAX_DECODE_TOKENS ? D.max_tokens : MOE_MAX_DECODE_TOKENS;
+    L->dec_parts_r = cdiv(L->G_I, kDecodeChunkGroups);
+    L->dec_parts_s = cdiv(L->G_Is, kDecodeChunkGroups);
+    const size_t Dm = (size_t)L->max_dec;
+    const size_t nchunks = (size_t)cdiv((int)P, kChunk);
+    const size_t NP = (size_t)k * L->dec_parts_r + L->dec_parts_s;
+
+    Plan plan;
+    Workspace &ws = L->ws;
+    plan.take(&ws.logits, Tm * E);
+    plan.take(&ws.idx, P);
+    plan.take(&ws.wts, P);
+    plan.take(&ws.xsum, Tm * L->G_d);
+    plan.take(&ws.xsplit, Tm * 3 * L->Gp_d);
+    plan.take(&ws.counts, E);
+    plan.take(&ws.offsets, E + 1);
+    plan.take(&ws.tile_off, E + 1);
+    plan.take(&ws.chunk_base, nchunks * E);
+    plan.take(&ws.rank, P);
+    plan.take(&ws.perm, P);
+    plan.take(&ws.pos, P);
+    plan.take(&ws.h_r, P * I);
+    plan.take(&ws.hsplit_r, P * 3 * L->Gp_I);
+    plan.take(&ws.h_s, Tm * Is);
+    plan.take(&ws.hsplit_s, Tm * 3 * L->Gp_Is);
+    plan.take(&ws.r, P * d);
+    plan.take(&ws.sh, Tm * d);
+    plan.take(&ws.dh_r, Dm * k * I);
+    plan.take(&ws.dh_s, Dm * Is);
+    plan.take(&ws.dhsum_r, Dm * k * (I / 32));
+    plan.take(&ws.dhsum_s, Dm * (Is / 32));
+    plan.take(&ws.dpart, Dm * NP * d);
+    plan.take(&ws.dcount, Dm * (d / 32));
+    L->ws_bytes = (plan.off + 255) & ~size_t(255);
+
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) {
+        delete L;
+        return fail(MOE_E_DEVICE, "hipGetDevice: %s", hipGetErrorString(err));
+    }
+    L->device = dev;
+    err = hipMalloc(&L->ws_base, L->ws_bytes);
+    if (err != hipSuccess) {
+        (void)hipGetLastError();
+        delete L;
+        return fail(MOE_E_NOMEM, "workspace of %zu bytes: %s", plan.off, hipGetErrorString(err));
+    }
+    char *base = static_cast<char *>(L->ws_base);
+    rebase(ws.logits, base);
+    rebase(ws.idx, base);
+    rebase(ws.wts, base);
+    rebase(ws.xsum, base);
+    rebase(ws.xsplit, base);
+    rebase(ws.counts, base);
+    rebase(ws.offsets, base);
+    rebase(ws.tile_off, base);
+    rebase(ws.chunk_base, base);
+    rebase(ws.rank, base);
+    rebase(ws.perm, base);
+    rebase(ws.pos, base);
+    rebase(ws.h_r, base);
+    rebase(ws.hsplit_r, base);
+    rebase(ws.h_s, base);
+    rebase(ws.hsplit_s, base);
+    rebase(ws.r, base);
+    rebase(ws.sh, base);
+    rebase(ws.dh_r, base);
+    rebase(ws.dh_s, base);
+    rebase(ws.dhsum_r, base);
+    rebase(ws.dhsum_s, base);
+    rebase(ws.dpart, base);
+    rebase(ws.dcount, base);
+    // zero once: padding columns of the split sums and the self-resetting counters rely on it
+    err = hipMemset(L->ws_base, 0, L->ws_bytes);
+    if (err == hipSuccess) err = hipDeviceSynchronize();
+    if (err != hipSuccess) {
+        (void)hipFree(L->ws_base);
+        delete L;
+        return fail(MOE_E_DEVICE, "workspace init: %s", hipGetErrorString(err));
+    }
+    *out = L;
+    return MOE_OK;
+}
+
+void moe_layer_destroy(moe_layer *L) {
+    if (!L) return;
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(L->device);
+    (void)hipDeviceSynchronize();
+    if (L->ws_base) (void)hipFree(L->ws_base);
+    for (auto &p : L->prof_pending) {
+        (void)hipEventDestroy(p.a);
+        (void)hipEventDestroy(p.b);
+    }
+    for (auto e : L->prof_pool) (void)hipEventDestroy(e);
+    (void)hipSetDevice(cur);
+    delete L;
+}
+
+moe_status moe_route(moe_layer *L, const uint16_t *x, int32_t T, int32_t *topk_idx, float *topk_w, float *logits,
+                     int32_t *expert_offsets, int32_t *pair_perm, void *hip_stream) {
+    clear_error();
+    moe_status st = check_call(L, x, T, topk_idx, "moe_route");
+    if (st != MOE_OK || T == 0) return st;
+    if (!topk_w) return fail(MOE_E_INVALID, "moe_route: topk_w is NULL");
+    if (!aligned16(topk_w) || (logits && !aligned16(logits)))
+        return fail(MOE_E_ALIGN, "moe_route: output not 16-byte aligned");
+    if ((expert_offsets == nullptr) != (pair_perm == nullptr))
+        return fail(MOE_E_INVALID, "moe_route: expert_offsets and pair_perm must be given together");
+    if (expert_offsets && (!aligned16(expert_offsets) || !aligned16(pair_perm)))
+        return fail(MOE_E_ALIGN, "moe_route: grouping outputs not 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    float *lg = logits ? logits : L->ws.logits;
+    st = route_impl(L, x, T, s, lg, topk_idx, topk_w, expert_offsets != nullptr, pair_perm);
+    if (st != MOE_OK) return st;
+    if (expert_offsets) {
+        hipError_t err = hipMemcpyAsync(expert_offsets, L->ws.offsets, sizeof(int32_t) * (L->dims.n_experts + 1),
+                                        hipMemcpyDeviceToDevice, s);
+        if (err != hipSuccess) return fail(MOE_E_DEVICE, "offsets copy: %s", hipGetErrorString(err));
+    }
+    return MOE_OK;
+}
+
+moe_status moe_forward_decode(moe_layer *L, const uint16_t *x, int32_t T, float *y, void *hip_stream) {
+    clear_error();
+    moe_status st = check_call(L, x, T, y, "moe_forward_decode");
+    if (st != MOE_OK || T == 0) return st;
+    if (T > L->max_dec)
+        return fail(MOE_E_CAPACITY, "moe_forward_decode: T = %d exceeds the decode capacity %d", T, L->max_dec);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    st = route_impl(L, x, T, s, L->ws.logits, L->ws.idx, L->ws.wts, false, nullptr);
+    if (st != MOE_OK) return st;
+    RUN(K_DEC_GATEUP, launch_dec_gateup(L, x, T, s));
+    RUN(K_DEC_DOWN, launch_dec_down(L, T, y, s));
+    return MOE_OK;
+}
+
+moe_status moe_forward_prefill(moe_layer *L, const uint16_t *x, int32_t T, float *y, void *hip_stream) {
+    clear_error();
+    moe_status st = check_call(L, x, T, y, "moe_forward_prefill");
+    if (st != MOE_OK || T == 0) return st;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    st = route_impl(L, x, T, s, L->ws.logits, L->ws.idx, L->ws.wts, true, nullptr);
+    if (st != MOE_OK) return st;
+    RUN(K_PRE_GATEUP, launch_pre_gateup(L, x, T, s));
+    RUN(K_PRE_DOWN, launch_pre_down(L, T, s));
+    RUN(K_COMBINE, launch_combine(L, T, y, s));
+    return MOE_OK;
+}
+
+moe_status moe_stack_glue(const uint16_t *h, const float *y, uint16_t *h_next, uint16_t *x_next, int32_t T,
+                          int32_t d, void *hip_stream) {
+    clear_error();
+    if (T < 0) return fail(MOE_E_SHAPE, "moe_stack_glue: T = %d is negative", T);
+    if (d < 1) return fail(MOE_E_SHAPE, "moe_stack_glue: d = %d", d);
+    if (T == 0) return MOE_OK;
+    if (!h || !h_next || !x_next) return fail(MOE_E_INVALID, "moe_stack_glue: NULL pointer");
+    if (!aligned16(h) || !aligned16(h_next) || !aligned16(x_next) || (y && !aligned16(y)))
+        return fail(MOE_E_ALIGN, "moe_stack_glue: pointer not 16-byte aligned");
+    hipError_t err = launch_glue(h, y, h_next, x_next, T, d, static_cast<hipStream_t>(hip_stream));
+    if (err != hipSuccess) return fail(MOE_E_DEVICE, "kernel glue: %s", hipGetErrorString(err));
+    return MOE_OK;
+}
+
+moe_status moe_profile_enable(moe_layer *L, int32_t on) {
+    clear_error();
+    if (!L) return fail(MOE_E_INVALID, "layer is NULL");
+    L->prof_on = on != 0;
+    return MOE_OK;
+}
+
+static moe_status prof_drain(moe_layer *L) {
+    for (auto &p : L->prof_pending) {
+        hipError_t err = hipEventSynchronize(p.b);
+        float ms = 0.0f;
+        if (err == hipSuccess) err = hipEventElapsedTime(&ms, p.a, p.b);
+        if (err != hipSuccess) return fail(MOE_E_DEVICE, "profile events: %s", hipGetErrorString(err));
+        L->prof_ms[p.id] += ms;
+        L->prof_n[p.id] += 1;
+        L->prof_pool.push_back(p.a);
+        L->prof_pool.push_back(p.b);
+    }
+    L->prof_pending.clear();
+    return MOE_OK;
+}
+
+moe_status moe_profile_read(moe_layer *L, int32_t id, double *total_ms, int64_t *launches) {
+    clear_error();
+    if (!L || !total_ms || !launches) return fail(MOE_E_INVALID, "NULL argument");
+    if (id < 0 || id >= K_COUNT) return fail(MOE_E_INVALID, "kernel id %d out of range", id);
+    moe_status st = prof_drain(L);
+    if (st != MOE_OK) return st;
+    *total_ms = L->prof_ms[id];
+    *launches = L->prof_n[id];
+    return MOE_OK;
+}
+
+moe_status moe_profile_reset(moe_layer *L) {
+    clear_error();
+    if (!L) return fail(MOE_E_INVALID, "layer is NULL");
+    moe_status st = prof_drain(L);
+    for (int i = 0; i < K_COUNT; ++i) {
+        L->prof_ms[i] = 0.0;
+        L->prof_n[i] = 0;
+    }
+    return st;
+}
+
+}  // extern "C"

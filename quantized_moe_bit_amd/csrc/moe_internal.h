@@ -1,0 +1,116 @@
+// Internal definitions shared by the host runtime and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "moe.h"
+
+namespace qmoe {
+
+// ----------------------------------------------------------------------------- errors
+moe_status fail(moe_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+// ----------------------------------------------------------------------------- tiling constants
+constexpr int kGroup = 64;          // quantization group (inputs per scale/bias)
+constexpr int kTileRows = 32;       // rows per 1 KiB weight tile
+constexpr int kMT = 128;            // prefill GEMM rows per workgroup tile
+constexpr int kChunk = 256;         // pairs per bucketing chunk
+constexpr int kDecodeChunkGroups = 12;  // K groups per decode down-projection part
+constexpr int kRouterTokens = 8;    // tokens per router workgroup
+
+__host__ __device__ inline int roundup(int a, int b) { return (a + b - 1) / b * b; }
+__host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Kernel ids for per-kernel timing.
+enum KernelId {
+    K_ROUTER = 0,
+    K_TOPK,
+    K_BUCKET_RANK,
+    K_BUCKET_SCAN,
+    K_BUCKET_SCATTER,
+    K_DEC_GATEUP,
+    K_DEC_DOWN,
+    K_PRE_GATEUP,
+    K_PRE_DOWN,
+    K_COMBINE,
+    K_GLUE,
+    K_COUNT
+};
+
+// Device pointers of the layer workspace.
+struct Workspace {
+    float *logits;        // [maxT, E]
+    int32_t *idx;         // [maxT, k]
+    float *wts;           // [maxT, k]
+    float *xsum;          // [maxT, G]          router-order group sums of x
+    uint16_t *xsplit;     // [maxT, 3*Gp_d]     bf16 hi | lo | hi of the group sums
+    int32_t *counts;      // [E]
+    int32_t *offsets;     // [E+1]
+    int32_t *tile_off;    // [E+1]              prefix sum of ceil(count/kMT)
+    int32_t *chunk_base;  // [nchunks, E]
+    int32_t *rank;        // [maxT*k]
+    int32_t *perm;        // [maxT*k]
+    int32_t *pos;         // [maxT*k]
+    uint16_t *h_r;        // [maxT*k, I]        routed hidden activations (bucket order)
+    uint16_t *hsplit_r;   // [maxT*k, 3*Gp_I]
+    uint16_t *h_s;        // [maxT, I_s]        shared hidden activations
+    uint16_t *hsplit_s;   // [maxT, 3*Gp_Is]
+    float *r;             // [maxT*k, d]        routed expert outputs (bucket order)
+    float *sh;            // [maxT, d]          shared expert outputs
+    // decode path
+    uint16_t *dh_r;       // [D*k, I]
+    uint16_t *dh_s;       // [D, I_s]
+    float *dhsum_r;       // [D*k, I/32]        sums of 32 consecutive hidden values
+    float *dhsum_s;       // [D, I_s/32]
+    float *dpart;         // [D, parts, d]
+    uint32_t *dcount;     // [D, d/32]          arrival counters (self-resetting)
+};
+
+struct ProfEvent {
+    int id;
+    hipEvent_t a, b;
+};
+
+}  // namespace qmoe
+
+struct moe_layer {
+    moe_dims dims;
+    moe_weights w;
+    int device;
+    int G_d, G_I, G_Is;        // groups along d, I, I_s
+    int Gp_d, Gp_I, Gp_Is;     // padded to a multiple of 16
+    int max_dec;               // decode capacity = min(max_tokens, MOE_MAX_DECODE_TOKENS)
+    int dec_parts_r, dec_parts_s;  // decode down-projection parts per routed slot / for the shared expert
+    void *ws_base;
+    size_t ws_bytes;
+    qmoe::Workspace ws;
+    // profiling
+    bool prof_on;
+    std::vector<qmoe::ProfEvent> prof_pending;
+    std::vector<hipEvent_t> prof_pool;
+    double prof_ms[qmoe::K_COUNT];
+    int64_t prof_n[qmoe::K_COUNT];
+};
+
+namespace qmoe {
+
+// Kernel launchers (each enqueues on stream, returns hipGetLastError()).
+hipError_t launch_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s);
+hipError_t launch_topk(const moe_layer *L, int T, const float *logits, int32_t *idx, float *w, hipStream_t s);
+hipError_t launch_bucket_rank(const moe_layer *L, int T, const int32_t *idx, hipStream_t s);
+hipError_t launch_bucket_scan(const moe_layer *L, int T, hipStream_t s);
+hipError_t launch_bucket_scatter(const moe_layer *L, int T, const int32_t *idx, int32_t *perm, hipStream_t s);
+hipError_t launch_dec_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s);
+hipError_t launch_dec_down(const moe_layer *L, int T, float *y, hipStream_t s);
+hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s);
+hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s);
+hipError_t launch_combine(const moe_layer *L, int T, float *y, hipStream_t s);
+hipError_t launch_glue(const uint16_t *h, const float *y, uint16_t *h_next, uint16_t *x_next, int T, int d,
+                       hipStream_t s);
+
+}  // namespace qmoe

@@ -1,0 +1,150 @@
+// Host-side lossless repack between the canonical weight layout and the device
+// layout the gfx950 kernels stream. Codes are moved bit-for-bit, never
+// re-quantized: the importer keeps source affine values unchanged and a layout
+// change must be exactly invertible (Mference system design, "Source weights and
+// bounded repack"; "Correctness and safety invariants").
+//
+// Device layout of a 4-bit matrix [out, in] (out % 32 == 0, in % 64 == 0):
+//   tiles of 32 rows x 64 inputs, 1 KiB each, ordered (row block rb, group g);
+//   inside a tile, lane l in 0..63 owns 16 bytes at l*16: row rb*32 + l%32 and,
+//   for step s in 0..3, the u32 at l*16 + 4*s holds inputs 64g + 16s + 8*(l/32) + j,
+//   j = 0..7, element j in nibble (j even ? j/2 : 4 + j/2).
+// That is the operand order of one lane of a 32x32x16 MFMA B fragment, and the nibble
+// order lets two bf16 values be built from one shift and one and-or per pair.
+// Scale/bias words: (scale | bias << 16), ordered (rb, g, row in block).
+//
+// Device layout of an 8-bit matrix [out, in]: codes unchanged (row-major bytes),
+// scale/bias words ordered (row, group).
+#include <cstdint>
+#include <cstring>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+inline int nibble_slot(int j) { return (j & 1) ? 4 + (j >> 1) : (j >> 1); }
+
+moe_status check(int32_t bits, int32_t n_mats, int32_t out_dim, int32_t in_dim) {
+    if (bits != 4 && bits != 8) return qmoe::fail(MOE_E_QUANT, "repack: bits must be 4 or 8, got %d", bits);
+    if (n_mats < 1 || out_dim < 1 || in_dim < 64)
+        return qmoe::fail(MOE_E_SHAPE, "repack: bad sizes n_mats=%d out=%d in=%d", n_mats, out_dim, in_dim);
+    if (in_dim % 64) return qmoe::fail(MOE_E_SHAPE, "repack: in_dim %d not a multiple of 64", in_dim);
+    if (bits == 4 && out_dim % 32)
+        return qmoe::fail(MOE_E_SHAPE, "repack: 4-bit out_dim %d not a multiple of 32", out_dim);
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" size_t moe_packed_bytes(int32_t bits, int32_t n_mats, int32_t out_dim, int32_t in_dim,
+                                   int32_t part) {
+    if ((bits != 4 && bits != 8) || n_mats < 1 || out_dim < 1 || in_dim < 64 || in_dim % 64) return 0;
+    if (bits == 4 && out_dim % 32) return 0;
+    const size_t n = (size_t)n_mats * out_dim;
+    if (part == 0) return n * (size_t)in_dim * bits / 8;
+    if (part == 1) return n * (size_t)(in_dim / 64) * 4;
+    return 0;
+}
+
+extern "C" moe_status moe_repack(int32_t bits, int32_t n_mats, int32_t out_dim, int32_t in_dim,
+                                 const moe_host_qmat *src, void *codes_out, uint32_t *sb_out) {
+    qmoe::clear_error();
+    moe_status st = check(bits, n_mats, out_dim, in_dim);
+    if (st != MOE_OK) return st;
+    if (!src || !src->codes || !src->scales || !src->biases || !codes_out || !sb_out)
+        return qmoe::fail(MOE_E_INVALID, "repack: null pointer");
+    const int G = in_dim / 64;
+    uint8_t *dst = static_cast<uint8_t *>(codes_out);
+    if (bits == 8) {
+        std::memcpy(dst, src->codes, (size_t)n_mats * out_dim * in_dim);
+        for (size_t i = 0; i < (size_t)n_mats * out_dim * G; ++i)
+            sb_out[i] = (uint32_t)src->scales[i] | ((uint32_t)src->biases[i] << 16);
+        return MOE_OK;
+    }
+    const size_t row_bytes = (size_t)in_dim / 2;
+    const int RB = out_dim / 32;
+    for (int m = 0; m < n_mats; ++m) {
+        const uint8_t *cm = src->codes + (size_t)m * out_dim * row_bytes;
+        const uint16_t *sm = src->scales + (size_t)m * out_dim * G;
+        const uint16_t *bm = src->biases + (size_t)m * out_dim * G;
+        uint8_t *dm = dst + (size_t)m * out_dim * row_bytes;
+        uint32_t *wm = sb_out + (size_t)m * out_dim * G;
+        for (int rb = 0; rb < RB; ++rb)
+            for (int g = 0; g < G; ++g) {
+                uint8_t *tile = dm + ((size_t)rb * G + g) * 1024;
+                for (int l = 0; l < 64; ++l) {
+                    const int row = rb * 32 + (l & 31), half = l >> 5;
+                    const uint8_t *crow = cm + (size_t)row * row_bytes;
+                    for (int s = 0; s < 4; ++s) {
+                        uint32_t word = 0;
+                        for (int j = 0; j < 8; ++j) {
+                            const int k = 64 * g + 16 * s + 8 * half + j;
+                            const uint32_t q = (crow[k >> 1] >> ((k & 1) * 4)) & 0xFu;
+                            word |= q << (4 * nibble_slot(j));
+                        }
+                        std::memcpy(tile + l * 16 + s * 4, &word, 4);
+                    }
+                }
+                for (int r = 0; r < 32; ++r) {
+                    const size_t si = (size_t)(rb * 32 + r) * G + g;
+                    wm[((size_t)rb * G + g) * 32 + r] = (uint32_t)sm[si] | ((uint32_t)bm[si] << 16);
+                }
+            }
+    }
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_unrepack(int32_t bits, int32_t n_mats, int32_t out_dim, int32_t in_dim,
+                                   const void *codes_in, const uint32_t *sb_in, uint8_t *codes,
+                                   uint16_t *scales, uint16_t *biases) {
+    qmoe::clear_error();
+    moe_status st = check(bits, n_mats, out_dim, in_dim);
+    if (st != MOE_OK) return st;
+    if (!codes_in || !sb_in || !codes || !scales || !biases)
+        return qmoe::fail(MOE_E_INVALID, "unrepack: null pointer");
+    const int G = in_dim / 64;
+    const uint8_t *srcb = static_cast<const uint8_t *>(codes_in);
+    if (bits == 8) {
+        std::memcpy(codes, srcb, (size_t)n_mats * out_dim * in_dim);
+        for (size_t i = 0; i < (size_t)n_mats * out_dim * G; ++i) {
+            scales[i] = (uint16_t)(sb_in[i] & 0xFFFFu);
+            biases[i] = (uint16_t)(sb_in[i] >> 16);
+        }
+        return MOE_OK;
+    }
+    const size_t row_bytes = (size_t)in_dim / 2;
+    const int RB = out_dim / 32;
+    std::memset(codes, 0, (size_t)n_mats * out_dim * row_bytes);
+    for (int m = 0; m < n_mats; ++m) {
+        const uint8_t *sm_ = srcb + (size_t)m * out_dim * row_bytes;
+        const uint32_t *wm = sb_in + (size_t)m * out_dim * G;
+        uint8_t *cm = codes + (size_t)m * out_dim * row_bytes;
+        uint16_t *scm = scales + (size_t)m * out_dim * G;
+        uint16_t *bcm = biases + (size_t)m * out_dim * G;
+        for (int rb = 0; rb < RB; ++rb)
+            for (int g = 0; g < G; ++g) {
+                const uint8_t *tile = sm_ + ((size_t)rb * G + g) * 1024;
+                for (int l = 0; l < 64; ++l) {
+                    const int row = rb * 32 + (l & 31), half = l >> 5;
+                    uint8_t *crow = cm + (size_t)row * row_bytes;
+                    for (int s = 0; s < 4; ++s) {
+                        uint32_t word;
+                        std::memcpy(&word, tile + l * 16 + s * 4, 4);
+                        for (int j = 0; j < 8; ++j) {
+                            const int k = 64 * g + 16 * s + 8 * half + j;
+                            const uint32_t q = (word >> (4 * nibble_slot(j))) & 0xFu;
+                            crow[k >> 1] |= (uint8_t)(q << ((k & 1) * 4));
+                        }
+                    }
+                }
+                for (int r = 0; r < 32; ++r) {
+                    const uint32_t v = wm[((size_t)rb * G + g) * 32 + r];
+                    const size_t si = (size_t)(rb * 32 + r) * G + g;
+                    scm[si] = (uint16_t)(v & 0xFFFFu);
+                    bcm[si] = (uint16_t)(v >> 16);
+                }
+            }
+    }
+    return MOE_OK;
+}

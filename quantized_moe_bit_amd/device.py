@@ -1,0 +1,93 @@
+"""Device-side layer object: repacks canonical weights (host, via moe_repack), places
+them in device memory with PyTorch, creates the C-ABI handle and calls its entry
+points. Marshalling only; every step of the layer runs in libmoe.so's kernels."""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+def _dev(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device, non_blocking=False)
+
+
+class DeviceLayer:
+    """One MoE layer resident on a GPU. `layer` is a canonical-layout synth.Layer."""
+
+    def __init__(self, layer, max_tokens: int, device="cuda:0"):
+        self.dims_py = layer.dims
+        self.device = torch.device(device)
+        D = layer.dims
+        self._keep = {}
+        q = {}
+        specs = {
+            "router": (layer.router, 8, 1, D.n_experts, D.d_model),
+            "gate": (layer.gate, 4, D.n_experts, D.d_expert, D.d_model),
+            "up": (layer.up, 4, D.n_experts, D.d_expert, D.d_model),
+            "down": (layer.down, 4, D.n_experts, D.d_model, D.d_expert),
+            "sh_gate": (layer.sh_gate, 4, 1, D.d_shared, D.d_model),
+            "sh_up": (layer.sh_up, 4, 1, D.d_shared, D.d_model),
+            "sh_down": (layer.sh_down, 4, 1, D.d_model, D.d_shared),
+        }
+        for name, (m, bits, n, o, i) in specs.items():
+            c, s = B.moe_repack(bits, n, o, i, m.codes, m.scales, m.biases)
+            tc, ts = _dev(c, self.device), _dev(s.view(np.int32), self.device)
+            self._keep[name] = (tc, ts)
+            q[name] = B.moe_qmat(tc.data_ptr(), ts.data_ptr())
+        lb = None
+        if layer.logit_bias is not None:
+            lb = _dev(layer.logit_bias.astype(np.float32), self.device)
+            self._keep["logit_bias"] = lb
+        w = B.moe_weights(**q, logit_bias=None if lb is None else lb.data_ptr())
+        self.dims = B.moe_dims(D.d_model, D.n_experts, D.top_k, D.d_expert, D.d_shared, D.group, D.router_bits,
+                               D.expert_bits, max_tokens)
+        self.max_tokens = max_tokens
+        self.handle = B.moe_layer_create(self.dims, w, 0)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            B.moe_layer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -------------------------------------------------------------- calls
+    def route(self, x: torch.Tensor, with_logits=True, with_grouping=True):
+        T = x.shape[0]
+        D = self.dims_py
+        dev = self.device
+        idx = torch.empty((T, D.top_k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, D.top_k), dtype=torch.float32, device=dev)
+        lg = torch.empty((T, D.n_experts), dtype=torch.float32, device=dev) if with_logits else None
+        off = torch.empty(D.n_experts + 1, dtype=torch.int32, device=dev) if with_grouping else None
+        perm = torch.empty(T * D.top_k, dtype=torch.int32, device=dev) if with_grouping else None
+        B.moe_route(self.handle, x, T, idx, w, lg, off, perm)
+        return dict(idx=idx, w=w, logits=lg, offsets=off, perm=perm)
+
+    def decode(self, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty((T, self.dims_py.d_model), dtype=torch.float32, device=self.device)
+        B.moe_forward_decode(self.handle, x, T, y)
+        return y
+
+    def prefill(self, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty((T, self.dims_py.d_model), dtype=torch.float32, device=self.device)
+        B.moe_forward_prefill(self.handle, x, T, y)
+        return y
+
+
+def tokens_to_device(x_bits: np.ndarray, device="cuda:0") -> torch.Tensor:
+    """bf16 bit patterns (uint16 [T, d]) -> int16 device tensor holding the same bits."""
+    return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).to(device)

@@ -29,10 +29,10 @@
  *
  * Precision. The router logits decide integers (the top-k set), so they are
  * computed in the one fp32 order the GPU kernels also follow, written out in
- * orc_router_logits. Everything else is float64: dequantized weights, the three
- * projections, GELU, routing weights and the combine. The expert hidden
- * activation is rounded to bf16 (the activation type) before the down
- * projection, at the point the GPU path stores it as bf16.
+ * orc_router_logits. Everything else is float64 and unrounded: dequantized
+ * weights, the three projections, GELU, the expert hidden activation, routing
+ * weights and the combine (the pages quantize weights, never the activation
+ * between the gate/up and down projections).
  *
  * Pins: the tests under tests/ check each function here against hand-built
  * codec groups, exact integer arithmetic, a full sort, a dense brute force
@@ -233,7 +233,7 @@ static void qmatvec(int bits, int out_dim, int in_dim, const orc_qmat *W, const 
 
 /*
  * One GELU-gated expert on one token:
- *   g = W_gate x,  u = W_up x,  h = bf16(gelu_tanh(g) * u),  r = W_down h.
+ *   g = W_gate x,  u = W_up x,  h = gelu_tanh(g) * u,  r = W_down h.
  * x: float64 [d]; r: float64 [d]; I = expert width.
  */
 void orc_ffn(int d, int I, const double *x, const orc_qmat *gate, const orc_qmat *up,
@@ -244,7 +244,7 @@ void orc_ffn(int d, int I, const double *x, const orc_qmat *gate, const orc_qmat
     double *u = (double *)malloc(sizeof(double) * (size_t)I);
     qmatvec(4, I, d, gate, x, g, buf);
     qmatvec(4, I, d, up, x, u, buf);
-    for (int j = 0; j < I; ++j) g[j] = bf16_f64(orc_f64_to_bf16(orc_gelu_tanh(g[j]) * u[j]));
+    for (int j = 0; j < I; ++j) g[j] = orc_gelu_tanh(g[j]) * u[j];
     qmatvec(4, d, I, down, g, r, buf);
     free(buf);
     free(g);

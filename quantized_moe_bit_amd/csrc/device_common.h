@@ -12,6 +12,8 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2_t;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -37,6 +39,36 @@ __device__ __forceinline__ uint32_t nib_pair(uint32_t w) {
 __device__ __forceinline__ bf16x8_t nib_frag(uint32_t w) {
     u32x4_t v = {nib_pair<0>(w), nib_pair<1>(w), nib_pair<2>(w), nib_pair<3>(w)};
     return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// float -> fp16 bits, round to nearest even, saturating at +-65504 (the expert hidden activation).
+__device__ __forceinline__ uint32_t f32_to_f16_sat(float f) {
+    f = fminf(fmaxf(f, -65504.0f), 65504.0f);
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// fp16 version of nib_pair: 1 + q/16 is 0x3C00 | q << 6 in fp16.
+template <int P>
+__device__ __forceinline__ uint32_t nib_pair_f16(uint32_t w) {
+    uint32_t t;
+    if constexpr (P == 0) t = w << 6;
+    else if constexpr (P == 1) t = w << 2;
+    else if constexpr (P == 2) t = w >> 2;
+    else t = w >> 6;
+    return (t & 0x03C003C0u) | 0x3C003C00u;
+}
+
+__device__ __forceinline__ f16x8_t nib_frag_f16(uint32_t w) {
+    u32x4_t v = {nib_pair_f16<0>(w), nib_pair_f16<1>(w), nib_pair_f16<2>(w), nib_pair_f16<3>(w)};
+    return __builtin_bit_cast(f16x8_t, v);
+}
+
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {

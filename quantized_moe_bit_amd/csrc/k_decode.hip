@@ -13,8 +13,9 @@
 //
 // Kernels:
 //   k_dec_gateup: one workgroup per (pair or shared token, 32-row block of the expert
-//     width); streams the gate and up tiles, writes h = bf16(gelu(g) * u) and the sums
-//     of each 32 consecutive h values (for the down projection's bias term).
+//     width); streams the gate and up tiles, writes h = fp16(gelu(g) * u) and the sums
+//     of each 32 consecutive h values (for the down projection's bias term). The down
+//     projection reads h with v_dot2_f32_f16 against fp16 values 1 + q/16.
 //   k_dec_down: one wave per (token, part, 32 output rows); a part is one routed slot
 //     or one chunk of the shared expert's input groups. Each wave writes its partial
 //     rows; the last wave to arrive for a (token, row block) adds the shared parts, then
@@ -137,9 +138,9 @@ __global__ __launch_bounds__(64 * kGUWaves) void k_dec_gateup(
             gv += red[w][0][tid];
             uv += red[w][1][tid];
         }
-        const uint32_t hb = f32_to_bf16(gelu_tanh_f32(gv) * uv);
+        const uint32_t hb = f32_to_f16_sat(gelu_tanh_f32(gv) * uv);
         hout[jb * 32 + tid] = (uint16_t)hb;
-        hv[tid] = bf16_to_f32(hb);
+        hv[tid] = f16_to_f32(hb);
     }
     __syncthreads();
     if (tid == 0) {
@@ -213,10 +214,10 @@ __global__ __launch_bounds__(64) void k_dec_down(int T, int d, int k, int I, int
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const u32x4_t hv = *reinterpret_cast<const u32x4_t *>(hl + 64 * b + 16 * s + 8 * half);
-                a = dot2_bf16(hv[0], nib_pair<0>(w4[b][s]), a);
-                a = dot2_bf16(hv[1], nib_pair<1>(w4[b][s]), a);
-                a = dot2_bf16(hv[2], nib_pair<2>(w4[b][s]), a);
-                a = dot2_bf16(hv[3], nib_pair<3>(w4[b][s]), a);
+                a = dot2_f16(hv[0], nib_pair_f16<0>(w4[b][s]), a);
+                a = dot2_f16(hv[1], nib_pair_f16<1>(w4[b][s]), a);
+                a = dot2_f16(hv[2], nib_pair_f16<2>(w4[b][s]), a);
+                a = dot2_f16(hv[3], nib_pair_f16<3>(w4[b][s]), a);
             }
             const float s16 = 16.0f * bf16_to_f32(sbw[b] & 0xFFFFu);
             acc = fmaf(s16, a, acc);

@@ -8,8 +8,11 @@
 //
 // Exact affine split per 64-input group g of output n:
 //   sum_j x_j (s q_j + b) = 16 s * A''_g + (b - 16 s) * X_g,   A''_g = sum_j x_j (1 + q_j/16)
-// A''_g comes from four v_mfma_f32_32x32x16_bf16 steps (x bf16, 1 + q/16 exact in bf16,
-// fp32 accumulation); 16 s is applied per group on the VALU. The (b - 16 s) X_g terms for
+// A''_g comes from four 32x32x16 MFMA steps with fp32 accumulation: bf16 for the gate/up
+// projections (x is bf16; 1 + q/16 is exact in bf16), fp16 for the down projection, whose
+// input, the hidden activation h = gelu(g) * u, is carried in fp16 (11 significant bits;
+// the Mference prefill likewise stages FP16 tensors for its matrix unit). 16 s is applied
+// per group on the VALU. The (b - 16 s) X_g terms for
 // all groups form a small GEMM with K = 3 * Gp (Gp = groups padded to 16) done on MFMA
 // after the main loop, with both factors split into bf16 hi + lo parts:
 //   c X ~= c_hi X_hi + c_hi X_lo + c_lo X_hi.
@@ -50,6 +53,22 @@ __device__ __forceinline__ int find_expert(const int32_t *tile_off, int E, int m
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+
+__device__ __forceinline__ f32x16_t mfma32(f16x8_t a, f16x8_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// MFMA operand type: bf16 for the gate/up projections (x is bf16), fp16 for the down
+// projection (the hidden activation is carried in fp16).
+template <int MODE> struct OpT;
+template <> struct OpT<0> {
+    typedef bf16x8_t type;
+    static __device__ __forceinline__ type frag(uint32_t w) { return nib_frag(w); }
+};
+template <> struct OpT<1> {
+    typedef f16x8_t type;
+    static __device__ __forceinline__ type frag(uint32_t w) { return nib_frag_f16(w); }
+};
 
 // c = bias - 16*scale as bf16 hi (part 0, 1) or lo (part 2) for the bias-term GEMM.
 __device__ __forceinline__ uint32_t bias_part(uint32_t sbw, int part) {
@@ -203,13 +222,14 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
             f32x16_t acc[2][2];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const bf16x8_t b0 = nib_frag(bw0[s]);
-                const bf16x8_t b1 = nib_frag(bw1[s]);
+                typedef typename OpT<MODE>::type op_t;
+                const op_t b0 = OpT<MODE>::frag(bw0[s]);
+                const op_t b1 = OpT<MODE>::frag(bw1[s]);
 #pragma unroll
                 for (int ms = 0; ms < 2; ++ms) {
                     const int row = wm * 64 + ms * 32 + n;
-                    const bf16x8_t av = __builtin_bit_cast(
-                        bf16x8_t, *reinterpret_cast<const u32x4_t *>(&As[buf][row * kAPitch + 16 * s + 8 * half]));
+                    const op_t av = __builtin_bit_cast(
+                        op_t, *reinterpret_cast<const u32x4_t *>(&As[buf][row * kAPitch + 16 * s + 8 * half]));
                     acc[ms][0] = mfma32(av, b0, s == 0 ? zero : acc[ms][0]);
                     acc[ms][1] = mfma32(av, b1, s == 0 ? zero : acc[ms][1]);
                 }
@@ -289,10 +309,10 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int row = wm * 64 + ms * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-                    const uint32_t hb = f32_to_bf16(gelu_tanh_f32(tot[ms][0][v]) * tot[ms][1][v]);
+                    const uint32_t hb = f32_to_f16_sat(gelu_tanh_f32(tot[ms][0][v]) * tot[ms][1][v]);
                     const int dst = drow[row];
                     if (dst >= 0) hout[(size_t)dst * J + j] = (uint16_t)hb;
-                    rsum[ms][v] = bf16_to_f32(hb);
+                    rsum[ms][v] = f16_to_f32(hb);
                 }
             // sum over this wave's 32 columns (lanes of one half share rows)
 #pragma unroll

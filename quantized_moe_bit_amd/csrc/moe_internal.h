@@ -56,15 +56,15 @@ struct Workspace {
     int32_t *rank;        // [maxT*k]
     int32_t *perm;        // [maxT*k]
     int32_t *pos;         // [maxT*k]
-    uint16_t *h_r;        // [maxT*k, I]        routed hidden activations (bucket order)
+    uint16_t *h_r;        // [maxT*k, I]        routed hidden activations, fp16 bits (bucket order)
     uint16_t *hsplit_r;   // [maxT*k, 3*Gp_I]
-    uint16_t *h_s;        // [maxT, I_s]        shared hidden activations
+    uint16_t *h_s;        // [maxT, I_s]        shared hidden activations, fp16 bits
     uint16_t *hsplit_s;   // [maxT, 3*Gp_Is]
     float *r;             // [maxT*k, d]        routed expert outputs (bucket order)
     float *sh;            // [maxT, d]          shared expert outputs
     // decode path
-    uint16_t *dh_r;       // [D*k, I]
-    uint16_t *dh_s;       // [D, I_s]
+    uint16_t *dh_r;       // [D*k, I]           fp16 bits
+    uint16_t *dh_s;       // [D, I_s]           fp16 bits
     float *dhsum_r;       // [D*k, I/32]        sums of 32 consecutive hidden values
     float *dhsum_s;       // [D, I_s/32]
     float *dpart;         // [D, parts, d]

@@ -2,9 +2,9 @@
 
 Written separately from the oracle (no shared code) and structured differently:
 it dequantizes whole weight tensors with NumPy, evaluates *every* expert on
-*every* token, picks experts with a full sort, and masks. bf16 rounding is
-exact rational round-to-nearest-even via ``fractions``. It is used to pin the
-oracle, never the GPU path directly.
+*every* token, picks experts with a full sort, and masks. Its bf16 rounding
+helper (exact rational round-to-nearest-even via ``fractions``) pins the
+oracle's rounding. It is used to pin the oracle, never the GPU path directly.
 """
 from __future__ import annotations
 
@@ -72,7 +72,7 @@ def gelu_tanh(v: np.ndarray) -> np.ndarray:
 def ffn_dense(x: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray) -> np.ndarray:
     g = rowdot(Wg, x)
     u = rowdot(Wu, x)
-    h = np.array([rne_bf16_exact(float(v)) for v in gelu_tanh(g) * u])
+    h = gelu_tanh(g) * u
     return rowdot(Wd, h)
 
 

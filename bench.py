@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized MoE FFN layer on one MI355X.
+
+One step = one pass of the whole layer (router, top-8 + softmax, expert
+gate/up + GeGLU, down, shared expert, weighted combine) over one batch of
+synthetic input already resident in HBM. The headline workload is single-token
+decode through one 2816-wide layer (128 experts, top-8, expert width 704,
+shared width 2112). To measure HBM rather than the 256 MB Infinity Cache, each
+step uses the next of --layers copies of the layer at distinct device addresses
+and the next of 256 distinct tokens.
+
+Prints one JSON line. Per-kernel durations for the roofline come from HIP events
+the library records around each kernel launch on the same stream, during a
+second pass over the same steps (so the headline timing carries no per-kernel
+events). Also reports a 4096-token prefill chunk (MFMA utilisation) and the CPU
+oracle timed on this host's cores on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 / fp16 MFMA, TFLOP/s
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def qmat_bytes(out_dim, in_dim, bits):
+    return out_dim * in_dim * bits // 8 + out_dim * (in_dim // 64) * 4
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=16, help="distinct-address layer copies the decode steps rotate over")
+    ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (this layer has no cross-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from quantized_moe_bit_amd import binding as B
+    from quantized_moe_bit_amd import synth
+    from quantized_moe_bit_amd.device import DeviceLayer, tokens_to_device
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K, W = args.steps, args.warmup
+
+    # ------------------------------------------------------------------ decode workload
+    wl = synth.WORKLOADS["decode"]
+    D = wl.dims
+    log("generating the 2816-wide layer")
+    lay = synth.workload_layer(wl)
+    base = DeviceLayer(lay, max_tokens=1, device=dev)
+    layers = [base] + [base.replicate() for _ in range(args.layers - 1)]
+    xt, _, _ = synth.gen_tokens(D, 256, wl.seed + 1000)
+    xs = tokens_to_device(xt, dev)
+    y = torch.empty((1, D.d_model), dtype=torch.float32, device=dev)
+    ntok = xs.shape[0]
+
+    def step(i):
+        B.moe_forward_decode(layers[i % len(layers)].handle, xs[i % ntok: i % ntok + 1], 1, y)
+
+    log(f"decode warmup {W}, timed {K} steps over {len(layers)} layer copies")
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(K):
+        step(W + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / K
+
+    # per-kernel durations (HIP events around each launch, same stream), second pass
+    for L in layers:
+        B.moe_profile_reset(L.handle)
+        B.moe_profile_enable(L.handle, True)
+    for i in range(K):
+        step(W + i)
+    torch.cuda.synchronize()
+    kern = {}
+    for kid, name in enumerate(B.KERNEL_NAMES):
+        tot, n = 0.0, 0
+        for L in layers:
+            ms, c = B.moe_profile_read(L.handle, kid)
+            tot += ms
+            n += c
+        if n:
+            kern[name] = dict(avg_us=1000.0 * tot / n, launches=n)
+    for L in layers:
+        B.moe_profile_enable(L.handle, False)
+
+    # algorithmic bytes per token (weights streamed, once each)
+    d, I, Is, E, k = D.d_model, D.d_expert, D.d_shared, D.n_experts, D.top_k
+    b_router = qmat_bytes(E, d, 8)
+    b_gateup = k * 2 * qmat_bytes(I, d, 4) + 2 * qmat_bytes(Is, d, 4)
+    b_down = k * qmat_bytes(d, I, 4) + qmat_bytes(d, Is, 4)
+    b_token = b_router + b_gateup + b_down
+    gu = kern.get("dec_gateup")
+    roofline = None
+    if gu:
+        achieved = b_gateup / (gu["avg_us"] * 1e-6) / 1e9
+        roofline = dict(kernel="dec_gateup", bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+                        unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                        algorithmic_bytes=b_gateup, avg_us=round(gu["avg_us"], 3))
+    layer_gbs = b_token / (ms_step * 1e-3) / 1e9
+
+    result = {
+        "metric": "MoE-layer tokens/s; decode HBM GB/s and prefill MFMA % of MI355X peak",
+        "value": round(1000.0 / ms_step, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode: 1 token through one layer, d_model 2816, 128 experts, top-8, "
+                               "expert width 704, shared width 2112, 8-bit g64 router, 4-bit g64 experts",
+                   "tokens_per_step": 1, "layer_copies_rotated": len(layers), "distinct_tokens": ntok,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "decode": {"bytes_per_token": b_token, "layer_hbm_gbs": round(layer_gbs, 1),
+                   "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4), "host_wall_s": round(wall, 4),
+                   "kernels_us": {n: round(v["avg_us"], 3) for n, v in kern.items()}},
+    }
+
+    # ------------------------------------------------------------------ 4096-token prefill
+    if not args.no_prefill:
+        for L in layers:
+            L.close()
+        del layers, base
+        torch.cuda.empty_cache()
+        wp = synth.WORKLOADS["prefill4096"]
+        log("generating the 4096-token Zipf prefill workload")
+        lp = synth.workload_layer(wp)
+        xp, _, _ = synth.workload_tokens(wp, lp)
+        P = DeviceLayer(lp, max_tokens=wp.tokens, device=dev)
+        xpd = tokens_to_device(xp, dev)
+        yp = torch.empty((wp.tokens, d), dtype=torch.float32, device=dev)
+        T = wp.tokens
+        for _ in range(2):
+            B.moe_forward_prefill(P.handle, xpd, T, yp)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.prefill_steps):
+            B.moe_forward_prefill(P.handle, xpd, T, yp)
+        e1.record()
+        torch.cuda.synchronize()
+        ms_pre = e0.elapsed_time(e1) / args.prefill_steps
+        B.moe_profile_reset(P.handle)
+        B.moe_profile_enable(P.handle, True)
+        for _ in range(args.prefill_steps):
+            B.moe_forward_prefill(P.handle, xpd, T, yp)
+        torch.cuda.synchronize()
+        pk = {}
+        for kid, name in enumerate(B.KERNEL_NAMES):
+            ms, c = B.moe_profile_read(P.handle, kid)
+            if c:
+                pk[name] = 1000.0 * ms / c
+        fl_gateup = 2.0 * (T * k * 2 * I * d + T * 2 * Is * d)
+        fl_down = 2.0 * (T * k * d * I + T * d * Is)
+        flops = fl_gateup + fl_down
+        pre = {"workload": "prefill: 4096 tokens, one 2816-wide layer, Zipf(1.3) logit skew, 2% tied tokens",
+               "tokens_per_s": round(T / (ms_pre * 1e-3), 1), "ms_per_step": round(ms_pre, 4),
+               "mfma_flops_per_step": flops,
+               "mfma_tflops": round(flops / (ms_pre * 1e-3) / 1e12, 2),
+               "mfma_frac": round(flops / (ms_pre * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+               "kernels_us": {n: round(v, 2) for n, v in pk.items()}}
+        if "pre_gateup" in pk:
+            tf = fl_gateup / (pk["pre_gateup"] * 1e-6) / 1e12
+            pre["roofline_gateup"] = dict(bound="mfma", achieved=round(tf, 1), peak=MFMA_PEAK_TFLOPS,
+                                          unit="TFLOP/s", frac=round(tf / MFMA_PEAK_TFLOPS, 4))
+        if "pre_down" in pk:
+            tf = fl_down / (pk["pre_down"] * 1e-6) / 1e12
+            pre["roofline_down"] = dict(bound="mfma", achieved=round(tf, 1), peak=MFMA_PEAK_TFLOPS,
+                                        unit="TFLOP/s", frac=round(tf / MFMA_PEAK_TFLOPS, 4))
+        result["prefill"] = pre
+        P.close()
+
+    # ------------------------------------------------------------------ counter calibration copy
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b_ = torch.empty_like(a)
+        for _ in range(3):
+            b_.copy_(a)
+        torch.cuda.synchronize()
+        result["calib_copy_bytes"] = n * 4
+
+    # ------------------------------------------------------------------ CPU oracle baseline
+    if not args.no_cpu_baseline:
+        import oracle
+        log("timing the CPU oracle on a bounded sample")
+        xs_host = xt
+        done, t_start = 0, time.perf_counter()
+        while True:
+            chunk = xs_host[(done % ntok): (done % ntok) + 16]
+            oracle.layer_forward(lay, chunk)
+            done += chunk.shape[0]
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds or el > 30:
+                break
+        result["cpu_baseline"] = {"value": round(done / el, 3), "unit": "tokens/s", "cores": oracle.get_threads(),
+                                  "kind": "oracle",
+                                  "sample": f"{done} decode tokens of the same 2816-wide layer (router, top-8, "
+                                            f"8 experts + shared, combine) in {el:.1f} s"}
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

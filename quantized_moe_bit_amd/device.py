@@ -49,6 +49,34 @@ class DeviceLayer:
         self.max_tokens = max_tokens
         self.handle = B.moe_layer_create(self.dims, w, 0)
 
+    def replicate(self) -> "DeviceLayer":
+        """A copy of this layer in fresh device memory (same values, new addresses, new handle)."""
+        other = DeviceLayer.__new__(DeviceLayer)
+        other.dims_py = self.dims_py
+        other.device = self.device
+        other.max_tokens = self.max_tokens
+        other._keep = {}
+        q = {}
+        for name, v in self._keep.items():
+            if name == "logit_bias":
+                other._keep[name] = v.clone()
+            else:
+                tc, ts = v[0].clone(), v[1].clone()
+                other._keep[name] = (tc, ts)
+                q[name] = B.moe_qmat(tc.data_ptr(), ts.data_ptr())
+        lb = other._keep.get("logit_bias")
+        w = B.moe_weights(**q, logit_bias=None if lb is None else lb.data_ptr())
+        other.dims = B.moe_dims(*[getattr(self.dims, f) for f, _ in B.moe_dims._fields_])
+        other.handle = B.moe_layer_create(other.dims, w, 0)
+        return other
+
+    def weight_bytes(self) -> int:
+        tot = 0
+        for v in self._keep.values():
+            for t in (v if isinstance(v, tuple) else (v,)):
+                tot += t.numel() * t.element_size()
+        return tot
+
     def close(self):
         if getattr(self, "handle", None):
             B.moe_layer_destroy(self.handle)

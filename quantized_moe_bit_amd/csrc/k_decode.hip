@@ -1,129 +1,165 @@
-// Decode path (a few tokens): wavefront GEMV kernels over 4-bit group-64 weights.
+// Decode path (up to 16 tokens): three launches of wavefront GEMV kernels over
+// 4-bit group-64 affine weights, with no communication between workgroups of a launch.
 //
-// Each selected expert is a GELU-gated FFN (gate, up, tanh-GELU, down) whose weights
-// are affine-quantized: w = scale * q + bias per group of 64 inputs (Mference system
-// design, "Why the runtime has this shape"; "Metal execution": decode uses custom
-// affine INT4 GEMV kernels that consume packed codes and BF16 scale/bias directly, and
-// the routed kernels fuse the affine decode, GeGLU and the weighted reduction).
+// Each selected expert is a GELU-gated FFN whose weights are w = scale * q + bias
+// per group of 64 inputs (Mference system design, "Why the runtime has this shape";
+// "Metal execution": decode uses custom affine INT4/INT8 GEMV kernels that consume the
+// packed codes and BF16 scale/bias directly, and the routed kernels fuse the affine
+// decode, GeGLU and the weighted reduction).
 //
-// Per group the dot product is split exactly as
-//   sum_j x_j (s q_j + b) = 16 s * sum_j x_j (1 + q_j/16) + (b - 16 s) * X_g,
-// where X_g = sum_j x_j. The bf16 values 1 + q/16 come from the nibbles with a shift and
-// an and-or, and v_dot2_f32_bf16 accumulates x * (1 + q/16) in fp32.
+// Exact affine split per group (x the 64 inputs of the group):
+//   sum_j x_j (s q_j + b) = 16 s * sum_j x_j (1 + q_j/16) + (b - 16 s) * sum_j x_j.
+// A lane holds half of a group's inputs; it adds 16 s * (its half of the first sum)
+// + (b - 16 s) * (its half of sum x), which is linear, so the two halves add up to the
+// exact group term. 1 + q/16 comes from the nibbles with one shift and one and-or;
+// v_dot2_f32_bf16 (gate/up, x is bf16) and v_dot2_f32_f16 (down, h is fp16) accumulate
+// in fp32.
 //
-// Kernels:
-//   k_dec_gateup: one workgroup per (pair or shared token, 32-row block of the expert
-//     width); streams the gate and up tiles, writes h = fp16(gelu(g) * u) and the sums
-//     of each 32 consecutive h values (for the down projection's bias term). The down
-//     projection reads h with v_dot2_f32_f16 against fp16 values 1 + q/16.
-//   k_dec_down: one wave per (token, part, 32 output rows); a part is one routed slot
-//     or one chunk of the shared expert's input groups. Each wave writes its partial
-//     rows; the last wave to arrive for a (token, row block) adds the shared parts, then
-//     the routed slots weighted by their routing weights in slot order 0..k-1 (Mference,
-//     "Decode", cb2; fixed reduction order as in TinyTitan, "Invariants").
+// Launch 1 (k_dec_stage1): router logits in the fixed fp32 order the oracle uses (one
+//   wave per expert, one lane per input group), and, in other workgroups, the shared
+//   expert's gate/up (it does not depend on routing; Mference "Decode" likewise starts
+//   the shared branch before the routed one).
+// Launch 2 (k_dec_stage2): each wave derives its token's top-k from the logits with a
+//   DPP argmax over packed (logit, index) keys (identical on every wave), then the routed
+//   gate/up + GeGLU for (pair, 32-row block); other workgroups run the shared down
+//   projection.
+// Launch 3 (k_dec_stage3): one workgroup per (token, 32 output rows), one wave per routed
+//   slot, then y = shared + w_0 r_0 + ... + w_{k-1} r_{k-1} in slot order (Mference
+//   "Decode", cb2; TinyTitan architecture "Invariants": fixed reduction order).
 #include "device_common.h"
 #include "moe_internal.h"
 
 namespace qmoe {
 namespace {
 
-constexpr int kGUWaves = 8;     // waves per gate/up workgroup
-constexpr int kGUBatch = 6;     // groups whose tiles a wave loads before computing
+constexpr int kDW = 8;      // waves per decode workgroup
+constexpr int kDB = 6;      // groups whose tiles a wave loads before computing (gate/up)
+constexpr uint32_t kOneBf16x2 = 0x3F803F80u;
+constexpr uint32_t kOneF16x2 = 0x3C003C00u;
 
-// grid: T*k*(I/32) + T*(I_s/32); block 64*kGUWaves
-__global__ __launch_bounds__(64 * kGUWaves) void k_dec_gateup(
-    const uint16_t *__restrict__ x, int T, int d, int k, int I, int Is, const int32_t *__restrict__ idx,
-    const float *__restrict__ xsum, moe_qmat gate, moe_qmat up, moe_qmat sh_gate, moe_qmat sh_up,
-    uint16_t *__restrict__ h_r, uint16_t *__restrict__ h_s, float *__restrict__ hsum_r, float *__restrict__ hsum_s) {
-    __shared__ __align__(16) uint16_t xs[8192];
-    __shared__ float red[kGUWaves][2][32];
-    __shared__ float hv[32];
-    const int G = d / 64;
-    const int JB = I / 32, JBs = Is / 32;
-    int u = blockIdx.x;
+// ----------------------------------------------------------------------------- router
+// The wave's expert e; lane g handles input group g (and g + 64, ... for d > 4096).
+// P[t][g] into Ps, then lanes t < T sum over g in ascending order. Fixed fp32 order:
+//   X = ((0 + x_0) + x_1) + ...; A = fma chain; P = fma(s, A, fl(b * X)); L = ((0 + P_0) + ...)
+__device__ __forceinline__ void router_wave(const uint16_t *__restrict__ x, int T, int d, int e, const uint8_t *__restrict__ rq,
+                            const uint32_t *__restrict__ rsb, float *Ps) {
+#pragma clang fp contract(off)
+    const int G = d / 64, lane = threadIdx.x & 63;
+    for (int g = lane; g < G; g += 64) {
+        const u32x4_t *cp = reinterpret_cast<const u32x4_t *>(rq + (size_t)e * d + 64 * g);
+        const u32x4_t c0 = cp[0], c1 = cp[1], c2 = cp[2], c3 = cp[3];
+        const uint32_t cw[16] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3],
+                                 c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
+        const uint32_t sbw = rsb[(size_t)e * G + g];
+        const float sc = bf16_to_f32(sbw & 0xFFFFu), bi = bf16_to_f32(sbw >> 16);
+        for (int t = 0; t < T; ++t) {
+            const u32x4_t *xp = reinterpret_cast<const u32x4_t *>(x + (size_t)t * d + 64 * g);
+            u32x4_t xv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xv[i] = xp[i];
+            float X = 0.0f, A = 0.0f;
+#pragma unroll
+            for (int j2 = 0; j2 < 32; ++j2) {          // element pair (2 j2, 2 j2 + 1)
+                const uint32_t xw = xv[j2 >> 2][j2 & 3];
+                const float xa = bf16_to_f32(xw & 0xFFFFu), xb = bf16_to_f32(xw >> 16);
+                const uint32_t c = cw[j2 >> 1];
+                const int sh = (j2 & 1) * 16;
+                const float qa = (float)((c >> sh) & 0xFFu), qb = (float)((c >> (sh + 8)) & 0xFFu);
+                X = X + xa;
+                X = X + xb;
+                A = __builtin_fmaf(xa, qa, A);
+                A = __builtin_fmaf(xb, qb, A);
+            }
+            const float bX = bi * X;
+            Ps[t * G + g] = __builtin_fmaf(sc, A, bX);
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------- gate/up unit
+// 32 rows (block jb) of gate and of up for one token (x staged in LDS as bf16), then
+// h = fp16(gelu(g) * u). All kDW waves of the workgroup take part; wave w owns input groups
+// w, w + kDW, ... The first batch of tiles is loaded before the caller stages x.
+struct GUTiles {
+    u32x4_t wg[kDB], wu[kDB];
+    uint32_t sbg[kDB], sbu[kDB];
+};
+
+struct GUPtrs {
     const uint8_t *Wg, *Wu;
     const uint32_t *Sg, *Su;
-    uint16_t *hout;
-    float *hsum;
-    int t, jb;
-    if (u < T * k * JB) {
-        const int p = u / JB;
-        jb = u % JB;
-        t = p / k;
-        const int e = idx[p];
-        const size_t cstride = (size_t)I * d / 2, sstride = (size_t)I * G;
-        Wg = static_cast<const uint8_t *>(gate.codes) + e * cstride;
-        Wu = static_cast<const uint8_t *>(up.codes) + e * cstride;
-        Sg = gate.sb + e * sstride;
-        Su = up.sb + e * sstride;
-        hout = h_r + (size_t)p * I;
-        hsum = hsum_r + (size_t)p * JB;
-    } else {
-        u -= T * k * JB;
-        t = u / JBs;
-        jb = u % JBs;
-        Wg = static_cast<const uint8_t *>(sh_gate.codes);
-        Wu = static_cast<const uint8_t *>(sh_up.codes);
-        Sg = sh_gate.sb;
-        Su = sh_up.sb;
-        hout = h_s + (size_t)t * Is;
-        hsum = hsum_s + (size_t)t * JBs;
+};
+
+__device__ __forceinline__ GUPtrs gu_ptrs(const uint8_t *Wg, const uint8_t *Wu, const uint32_t *Sg, const uint32_t *Su,
+                                          int G, int jb) {
+    const int lane = threadIdx.x & 63, n = lane & 31;
+    GUPtrs p;
+    p.Wg = Wg + (size_t)jb * G * 1024 + lane * 16;
+    p.Wu = Wu + (size_t)jb * G * 1024 + lane * 16;
+    p.Sg = Sg + (size_t)jb * G * 32 + n;
+    p.Su = Su + (size_t)jb * G * 32 + n;
+    return p;
+}
+
+__device__ __forceinline__ void gu_load(GUTiles &r, const GUPtrs &p, int G, int gb0) {
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int b = 0; b < kDB; ++b) {
+        const int g = gb0 + wave + b * kDW;
+        if (g < G) {
+            r.wg[b] = ld16(p.Wg + (size_t)g * 1024);
+            r.wu[b] = ld16(p.Wu + (size_t)g * 1024);
+            r.sbg[b] = p.Sg[g * 32];
+            r.sbu[b] = p.Su[g * 32];
+        }
     }
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, n = lane & 31, half = lane >> 5;
-    const float *X = xsum + (size_t)t * G;
-    Wg += (size_t)jb * G * 1024 + lane * 16;
-    Wu += (size_t)jb * G * 1024 + lane * 16;
-    Sg += (size_t)jb * G * 32 + n;
-    Su += (size_t)jb * G * 32 + n;
+}
+
+__device__ __forceinline__ void gu_compute(const GUTiles &r, const uint16_t *xs, int G, int gb0, float &accg,
+                                           float &accu) {
+    const int wave = threadIdx.x >> 6, half = (threadIdx.x >> 5) & 1;
+#pragma unroll
+    for (int b = 0; b < kDB; ++b) {
+        const int g = gb0 + wave + b * kDW;
+        if (g < G) {
+            float ag = 0.0f, au = 0.0f, xsum = 0.0f;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xs + 64 * g + 16 * s + 8 * half);
+                ag = dot2_bf16(xv[0], nib_pair<0>(r.wg[b][s]), ag);
+                ag = dot2_bf16(xv[1], nib_pair<1>(r.wg[b][s]), ag);
+                ag = dot2_bf16(xv[2], nib_pair<2>(r.wg[b][s]), ag);
+                ag = dot2_bf16(xv[3], nib_pair<3>(r.wg[b][s]), ag);
+                au = dot2_bf16(xv[0], nib_pair<0>(r.wu[b][s]), au);
+                au = dot2_bf16(xv[1], nib_pair<1>(r.wu[b][s]), au);
+                au = dot2_bf16(xv[2], nib_pair<2>(r.wu[b][s]), au);
+                au = dot2_bf16(xv[3], nib_pair<3>(r.wu[b][s]), au);
+                xsum = dot2_bf16(xv[0], kOneBf16x2, xsum);
+                xsum = dot2_bf16(xv[1], kOneBf16x2, xsum);
+                xsum = dot2_bf16(xv[2], kOneBf16x2, xsum);
+                xsum = dot2_bf16(xv[3], kOneBf16x2, xsum);
+            }
+            const float s16g = 16.0f * bf16_to_f32(r.sbg[b] & 0xFFFFu);
+            const float s16u = 16.0f * bf16_to_f32(r.sbu[b] & 0xFFFFu);
+            accg = fmaf(s16g, ag, fmaf(bf16_to_f32(r.sbg[b] >> 16) - s16g, xsum, accg));
+            accu = fmaf(s16u, au, fmaf(bf16_to_f32(r.sbu[b] >> 16) - s16u, xsum, accu));
+        }
+    }
+}
+
+// Full unit: tiles of the first batch are already in r; x is staged by stage_x() between the
+// first loads and the barrier.
+template <class StageX>
+__device__ __forceinline__ void gateup_unit(GUTiles &r, const GUPtrs &p, const uint16_t *xs, int G, int jb,
+                                            uint16_t *hout, float (*red)[2][32], StageX stage_x) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31;
+    stage_x();
+    __syncthreads();
     float accg = 0.0f, accu = 0.0f;
-    // every wave runs the same number of iterations, so the barrier below is uniform
-    for (int gb0 = 0; gb0 < G; gb0 += kGUWaves * kGUBatch) {
-        const int gb = gb0 + wave;
-        u32x4_t wg[kGUBatch], wu[kGUBatch];
-        uint32_t sbg[kGUBatch], sbu[kGUBatch];
-#pragma unroll
-        for (int b = 0; b < kGUBatch; ++b) {
-            const int g = gb + b * kGUWaves;
-            if (g < G) {
-                wg[b] = ld16(Wg + (size_t)g * 1024);
-                wu[b] = ld16(Wu + (size_t)g * 1024);
-                sbg[b] = Sg[g * 32];
-                sbu[b] = Su[g * 32];
-            }
-        }
-        if (gb0 == 0)
-            for (int i = tid; i < d / 8; i += 64 * kGUWaves)
-                *reinterpret_cast<u32x4_t *>(xs + 8 * i) = ld16(x + (size_t)t * d + 8 * i);
-        __syncthreads();
-#pragma unroll
-        for (int b = 0; b < kGUBatch; ++b) {
-            const int g = gb + b * kGUWaves;
-            if (g < G) {
-                float ag = 0.0f, au = 0.0f;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xs + 64 * g + 16 * s + 8 * half);
-                    ag = dot2_bf16(xv[0], nib_pair<0>(wg[b][s]), ag);
-                    ag = dot2_bf16(xv[1], nib_pair<1>(wg[b][s]), ag);
-                    ag = dot2_bf16(xv[2], nib_pair<2>(wg[b][s]), ag);
-                    ag = dot2_bf16(xv[3], nib_pair<3>(wg[b][s]), ag);
-                    au = dot2_bf16(xv[0], nib_pair<0>(wu[b][s]), au);
-                    au = dot2_bf16(xv[1], nib_pair<1>(wu[b][s]), au);
-                    au = dot2_bf16(xv[2], nib_pair<2>(wu[b][s]), au);
-                    au = dot2_bf16(xv[3], nib_pair<3>(wu[b][s]), au);
-                }
-                const float s16g = 16.0f * bf16_to_f32(sbg[b] & 0xFFFFu);
-                const float s16u = 16.0f * bf16_to_f32(sbu[b] & 0xFFFFu);
-                accg = fmaf(s16g, ag, accg);
-                accu = fmaf(s16u, au, accu);
-                if (half == 0) {
-                    const float Xg = X[g];
-                    accg = fmaf(bf16_to_f32(sbg[b] >> 16) - s16g, Xg, accg);
-                    accu = fmaf(bf16_to_f32(sbu[b] >> 16) - s16u, Xg, accu);
-                }
-            }
-        }
+    gu_compute(r, xs, G, 0, accg, accu);
+    for (int gb0 = kDW * kDB; gb0 < G; gb0 += kDW * kDB) {
+        gu_load(r, p, G, gb0);
+        gu_compute(r, xs, G, gb0, accg, accu);
     }
     accg += __shfl_xor(accg, 32);
     accu += __shfl_xor(accu, 32);
@@ -134,140 +170,361 @@ __global__ __launch_bounds__(64 * kGUWaves) void k_dec_gateup(
     __syncthreads();
     if (tid < 32) {
         float gv = 0.0f, uv = 0.0f;
-        for (int w = 0; w < kGUWaves; ++w) {
+#pragma unroll
+        for (int w = 0; w < kDW; ++w) {
             gv += red[w][0][tid];
             uv += red[w][1][tid];
         }
-        const uint32_t hb = f32_to_f16_sat(gelu_tanh_f32(gv) * uv);
-        hout[jb * 32 + tid] = (uint16_t)hb;
-        hv[tid] = f16_to_f32(hb);
-    }
-    __syncthreads();
-    if (tid == 0) {
-        float s = 0.0f;
-        for (int i = 0; i < 32; ++i) s += hv[i];
-        hsum[jb] = s;
+        hout[jb * 32 + tid] = (uint16_t)f32_to_f16_sat(gelu_tanh_f32(gv) * uv);
     }
 }
 
-// grid: T * NP * (d/32); block 64
-__global__ __launch_bounds__(64) void k_dec_down(int T, int d, int k, int I, int Is, int nR, int nS,
-                                                 const int32_t *__restrict__ idx, const float *__restrict__ wts,
-                                                 moe_qmat down, moe_qmat sh_down, const uint16_t *__restrict__ h_r,
-                                                 const uint16_t *__restrict__ h_s, const float *__restrict__ hsum_r,
-                                                 const float *__restrict__ hsum_s, float *__restrict__ part,
-                                                 uint32_t *__restrict__ counter, float *__restrict__ y) {
-    __shared__ __align__(16) uint16_t hl[kDecodeChunkGroups * 64];
-    const int RB = d / 32, NP = k * nR + nS;
-    int u = blockIdx.x;
-    const int rb = u % RB;
-    u /= RB;
-    const int pidx = u % NP;
-    const int t = u / NP;
-    const int GI = I / 64, GIs = Is / 64;
-    const uint8_t *W;
-    const uint32_t *S;
-    const uint16_t *hin;
-    const float *hs;
-    int Gk, g0, g1;
-    if (pidx < k * nR) {
-        const int slot = pidx / nR, c = pidx % nR;
-        const int p = t * k + slot;
-        const int e = idx[p];
-        W = static_cast<const uint8_t *>(down.codes) + (size_t)e * d * I / 2;
-        S = down.sb + (size_t)e * d * GI;
-        hin = h_r + (size_t)p * I;
-        hs = hsum_r + (size_t)p * (I / 32);
-        Gk = GI;
-        g0 = c * kDecodeChunkGroups;
-        g1 = min(GI, g0 + kDecodeChunkGroups);
-    } else {
-        const int c = pidx - k * nR;
-        W = static_cast<const uint8_t *>(sh_down.codes);
-        S = sh_down.sb;
-        hin = h_s + (size_t)t * Is;
-        hs = hsum_s + (size_t)t * (Is / 32);
-        Gk = GIs;
-        g0 = c * kDecodeChunkGroups;
-        g1 = min(GIs, g0 + kDecodeChunkGroups);
-    }
-    const int lane = threadIdx.x, n = lane & 31, half = lane >> 5;
-    const int ng = g1 - g0;
-    W += ((size_t)rb * Gk + g0) * 1024 + lane * 16;
-    S += ((size_t)rb * Gk + g0) * 32 + n;
+// ----------------------------------------------------------------------------- down part
+// One wave: 32 output rows (block rb) of a down projection over groups [g0, g1) of its fp16
+// input h (staged in LDS at hl, indexed from group 0). The first batch of tiles is loaded
+// before the caller stages h.
+struct DTiles {
     u32x4_t w4[kDecodeChunkGroups];
     uint32_t sbw[kDecodeChunkGroups];
+};
+
+__device__ __forceinline__ void down_load(DTiles &r, const uint8_t *W, const uint32_t *S, int rb, int Gk, int gb,
+                                          int g1) {
+    const int lane = threadIdx.x & 63, n = lane & 31;
+    W += (size_t)rb * Gk * 1024 + lane * 16;
+    S += (size_t)rb * Gk * 32 + n;
 #pragma unroll
     for (int b = 0; b < kDecodeChunkGroups; ++b)
-        if (b < ng) {
-            w4[b] = ld16(W + (size_t)b * 1024);
-            sbw[b] = S[b * 32];
+        if (gb + b < g1) {
+            r.w4[b] = ld16(W + (size_t)(gb + b) * 1024);
+            r.sbw[b] = S[(gb + b) * 32];
         }
-    for (int i = lane; i < ng * 8; i += 64)
-        *reinterpret_cast<u32x4_t *>(hl + 8 * i) = ld16(hin + 64 * g0 + 8 * i);
-    __syncthreads();
-    float acc = 0.0f;
+}
+
+__device__ __forceinline__ float down_compute(const DTiles &r, const uint16_t *hl, int gb, int g1, float acc) {
+    const int half = (threadIdx.x >> 5) & 1;
 #pragma unroll
     for (int b = 0; b < kDecodeChunkGroups; ++b)
-        if (b < ng) {
-            float a = 0.0f;
+        if (gb + b < g1) {
+            const int g = gb + b;
+            float a = 0.0f, hsum = 0.0f;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const u32x4_t hv = *reinterpret_cast<const u32x4_t *>(hl + 64 * b + 16 * s + 8 * half);
-                a = dot2_f16(hv[0], nib_pair_f16<0>(w4[b][s]), a);
-                a = dot2_f16(hv[1], nib_pair_f16<1>(w4[b][s]), a);
-                a = dot2_f16(hv[2], nib_pair_f16<2>(w4[b][s]), a);
-                a = dot2_f16(hv[3], nib_pair_f16<3>(w4[b][s]), a);
+                const u32x4_t hv = *reinterpret_cast<const u32x4_t *>(hl + 64 * g + 16 * s + 8 * half);
+                a = dot2_f16(hv[0], nib_pair_f16<0>(r.w4[b][s]), a);
+                a = dot2_f16(hv[1], nib_pair_f16<1>(r.w4[b][s]), a);
+                a = dot2_f16(hv[2], nib_pair_f16<2>(r.w4[b][s]), a);
+                a = dot2_f16(hv[3], nib_pair_f16<3>(r.w4[b][s]), a);
+                hsum = dot2_f16(hv[0], kOneF16x2, hsum);
+                hsum = dot2_f16(hv[1], kOneF16x2, hsum);
+                hsum = dot2_f16(hv[2], kOneF16x2, hsum);
+                hsum = dot2_f16(hv[3], kOneF16x2, hsum);
             }
-            const float s16 = 16.0f * bf16_to_f32(sbw[b] & 0xFFFFu);
-            acc = fmaf(s16, a, acc);
-            if (half == 0) {
-                const int g = g0 + b;
-                acc = fmaf(bf16_to_f32(sbw[b] >> 16) - s16, hs[2 * g] + hs[2 * g + 1], acc);
-            }
+            const float s16 = 16.0f * bf16_to_f32(r.sbw[b] & 0xFFFFu);
+            acc = fmaf(s16, a, fmaf(bf16_to_f32(r.sbw[b] >> 16) - s16, hsum, acc));
         }
-    acc += __shfl_xor(acc, 32);
-    const int row = rb * 32 + n;
-    if (lane < 32) part[((size_t)t * NP + pidx) * d + row] = acc;
-    __threadfence();
-    uint32_t old = 0;
-    if (lane == 0) old = atomicAdd(&counter[(size_t)t * RB + rb], 1u);
-    old = __shfl(old, 0);
-    if (old != (uint32_t)(NP - 1)) return;
-    __threadfence();
-    if (lane < 32) {
-        const float *pt = part + (size_t)t * NP * d + row;
-        float sh = 0.0f;
-        for (int c = 0; c < nS; ++c) sh += __builtin_nontemporal_load(pt + (size_t)(k * nR + c) * d);
-        float out = sh;
-        for (int s = 0; s < k; ++s) {
-            float r = 0.0f;
-            for (int c = 0; c < nR; ++c) r += __builtin_nontemporal_load(pt + (size_t)(s * nR + c) * d);
-            out = fmaf(wts[(size_t)t * k + s], r, out);
-        }
-        y[(size_t)t * d + row] = out;
+    return acc;
+}
+
+// Rest of a down part after the first batch (loaded by the caller) and the barrier.
+__device__ __forceinline__ float down_finish(DTiles &r, const uint16_t *hl, const uint8_t *W, const uint32_t *S,
+                                             int rb, int Gk, int g0, int g1) {
+    float acc = down_compute(r, hl, g0, g1, 0.0f);
+    for (int gb = g0 + kDecodeChunkGroups; gb < g1; gb += kDecodeChunkGroups) {
+        down_load(r, W, S, rb, Gk, gb, g1);
+        acc = down_compute(r, hl, gb, g1, acc);
     }
-    if (lane == 0) counter[(size_t)t * RB + rb] = 0u;
+    return acc + __shfl_xor(acc, 32);
+}
+
+// ----------------------------------------------------------------------------- top-k
+// Selection key of (logit v, expert e): order-preserving bits of v (with -0 folded into +0)
+// above the inverted index, so a larger key is a larger logit, or an equal logit with a
+// lower index -- the top-k order (ties to the lower expert index).
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+    uint32_t u = __float_as_uint(v + 0.0f);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+__device__ __forceinline__ float key_value(uint64_t k) {
+    uint32_t u = (uint32_t)(k >> 32);
+    u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+    return __uint_as_float(u);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t max_dpp(uint64_t x) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)x, CTRL, 0xF, 0xF, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(x >> 32), CTRL, 0xF, 0xF, true);
+    const uint64_t y = ((uint64_t)hi << 32) | lo;
+    return y > x ? y : x;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t x, int lane) {
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)x, lane);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Largest key of the wave: DPP within rows of 16 (swap pairs, swap halves of quads, half-row
+// mirror, row mirror), then the four row results through scalar registers.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t x) {
+    x = max_dpp<0xB1>(x);    // quad_perm [1,0,3,2]
+    x = max_dpp<0x4E>(x);    // quad_perm [2,3,0,1]
+    x = max_dpp<0x141>(x);   // row_half_mirror
+    x = max_dpp<0x140>(x);   // row_mirror
+    uint64_t m = readlane64(x, 0);
+    const uint64_t r1 = readlane64(x, 16), r2 = readlane64(x, 32), r3 = readlane64(x, 48);
+    m = r1 > m ? r1 : m;
+    m = r2 > m ? r2 : m;
+    m = r3 > m ? r3 : m;
+    return m;
+}
+
+// Slot `slot` of a token's top-k, derived by one wave from its logits row (identical on
+// every lane and every wave). With all_rounds, runs all k rounds and returns the slot's
+// softmax weight over the k selected logits (fp32) in w_out.
+template <int kPer>   // logits per lane: E <= 64 * kPer
+__device__ __forceinline__ int wave_topk(const float *__restrict__ l, int E, int k, int slot, bool all_rounds,
+                                         float &w_out) {
+    const int lane = threadIdx.x & 63;
+    uint64_t key[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int e = lane + 64 * i;
+        key[i] = e < E ? topk_key(l[e], e) : 0ull;     // 0 is below every real key
+    }
+    const int rounds = all_rounds ? k : slot + 1;
+    int target_e = 0;
+    float target_v = 0.0f, m = 0.0f, z = 0.0f;
+    for (int s = 0; s < rounds; ++s) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int i = 1; i < kPer; ++i) best = key[i] > best ? key[i] : best;
+        best = wave_max_key(best);
+        const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
+        const float v = key_value(best);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            if (key[i] == best) key[i] = 0ull;        // taken
+        if (s == 0) m = v;
+        z += __expf(v - m);
+        if (s == slot) {
+            target_e = min(max(e, 0), E - 1);
+            target_v = v;
+        }
+    }
+    w_out = __expf(target_v - m) / z;
+    return target_e;
+}
+
+struct DecArgs {
+    const uint16_t *x;
+    int T, d, E, k, I, Is;
+    const uint8_t *rq;
+    const uint32_t *rsb;
+    const float *logit_bias;
+    float *logits;
+    int32_t *idx;
+    float *wts;
+    moe_qmat gate, up, down, sh_gate, sh_up, sh_down;
+    uint16_t *h_r, *h_s;
+    float *sh;
+    float *y;
+};
+
+// grid: ceil(E / kDW) router workgroups + T * (I_s / 32) shared gate/up workgroups
+__global__ __launch_bounds__(64 * kDW) void k_dec_stage1(DecArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int RW = cdiv(a.E, kDW);
+    const int G = a.d / 64;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if ((int)blockIdx.x < RW) {
+        float *Ps = reinterpret_cast<float *>(smem);     // [kDW][T][G]
+        const int e = blockIdx.x * kDW + wave;
+        float *P = Ps + (size_t)wave * a.T * G;
+        if (e < a.E) router_wave(a.x, a.T, a.d, e, a.rq, a.rsb, P);
+        __syncthreads();
+        if (e < a.E && lane < a.T) {
+#pragma clang fp contract(off)
+            float L = 0.0f;
+            for (int g = 0; g < G; ++g) L = L + P[lane * G + g];
+            if (a.logit_bias) L = L + a.logit_bias[e];
+            a.logits[(size_t)lane * a.E + e] = L;
+        }
+        return;
+    }
+    uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
+    float(*red)[2][32] = reinterpret_cast<float(*)[2][32]>(smem + sizeof(uint16_t) * a.d);
+    const int JBs = a.Is / 32;
+    const int u = blockIdx.x - RW, t = u / JBs, jb = u % JBs;
+    const GUPtrs p = gu_ptrs(static_cast<const uint8_t *>(a.sh_gate.codes), static_cast<const uint8_t *>(a.sh_up.codes),
+                             a.sh_gate.sb, a.sh_up.sb, G, jb);
+    GUTiles r;
+    gu_load(r, p, G, 0);
+    gateup_unit(r, p, xs, G, jb, a.h_s + (size_t)t * a.Is, red, [&]() {
+        for (int i = tid; i < a.d / 8; i += 64 * kDW)
+            *reinterpret_cast<u32x4_t *>(xs + 8 * i) = ld16(a.x + (size_t)t * a.d + 8 * i);
+    });
+}
+
+// grid: T * k * (I / 32) routed gate/up workgroups + T * (d / 32) shared down workgroups
+template <int kPer>
+__global__ __launch_bounds__(64 * kDW) void k_dec_stage2(DecArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int G = a.d / 64, JB = a.I / 32;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int nR = a.T * a.k * JB;
+    if ((int)blockIdx.x < nR) {
+        const int pr = blockIdx.x / JB, jb = blockIdx.x % JB, t = pr / a.k, slot = pr % a.k;
+        // every wave derives the token's selection itself; the first unit of a pair records it
+        const bool record = (jb == 0 && wave == 0);
+        float wsel;
+        const int e = wave_topk<kPer>(a.logits + (size_t)t * a.E, a.E, a.k, slot, record, wsel);
+        if (record && lane == 0) {
+            a.idx[pr] = e;
+            a.wts[pr] = wsel;
+        }
+        uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
+        float(*red)[2][32] = reinterpret_cast<float(*)[2][32]>(smem + sizeof(uint16_t) * a.d);
+        const size_t cstride = (size_t)a.I * a.d / 2, sstride = (size_t)a.I * G;
+        const GUPtrs p = gu_ptrs(static_cast<const uint8_t *>(a.gate.codes) + e * cstride,
+                                 static_cast<const uint8_t *>(a.up.codes) + e * cstride, a.gate.sb + e * sstride,
+                                 a.up.sb + e * sstride, G, jb);
+        GUTiles r;
+        gu_load(r, p, G, 0);
+        gateup_unit(r, p, xs, G, jb, a.h_r + (size_t)pr * a.I, red, [&]() {
+            for (int i = tid; i < a.d / 8; i += 64 * kDW)
+                *reinterpret_cast<u32x4_t *>(xs + 8 * i) = ld16(a.x + (size_t)t * a.d + 8 * i);
+        });
+        return;
+    }
+    // shared down: (token, 32 output rows); the waves split the input groups
+    const int RB = a.d / 32, GIs = a.Is / 64;
+    const int u = blockIdx.x - nR, t = u / RB, rb = u % RB;
+    uint16_t *hl = reinterpret_cast<uint16_t *>(smem);
+    float *part = reinterpret_cast<float *>(smem + sizeof(uint16_t) * a.Is);
+    const int per = cdiv(GIs, kDW);
+    const int g0 = min(GIs, wave * per), g1 = min(GIs, g0 + per);
+    const uint8_t *W = static_cast<const uint8_t *>(a.sh_down.codes);
+    DTiles r;
+    down_load(r, W, a.sh_down.sb, rb, GIs, g0, g1);
+    for (int i = tid; i < a.Is / 8; i += 64 * kDW)
+        *reinterpret_cast<u32x4_t *>(hl + 8 * i) = ld16(a.h_s + (size_t)t * a.Is + 8 * i);
+    __syncthreads();
+    const float rsum = down_finish(r, hl, W, a.sh_down.sb, rb, GIs, g0, g1);
+    if (lane < 32) part[wave * 32 + lane] = rsum;
+    __syncthreads();
+    if (tid < 32) {
+        float sacc = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kDW; ++w) sacc += part[w * 32 + tid];
+        a.sh[(size_t)t * a.d + rb * 32 + tid] = sacc;
+    }
+}
+
+// grid: T * (d / 32); block 64 * k: wave s = routed slot s
+__global__ __launch_bounds__(64 * MOE_MAX_TOP_K) void k_dec_stage3(DecArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int RB = a.d / 32, GI = a.I / 64;
+    const int t = blockIdx.x / RB, rb = blockIdx.x % RB;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    uint16_t *hl = reinterpret_cast<uint16_t *>(smem);                              // [k][I]
+    float *part = reinterpret_cast<float *>(smem + sizeof(uint16_t) * a.k * a.I);  // [k][32]
+    const int pr = t * a.k + wave;
+    const int e = a.idx[pr];
+    const uint8_t *W = static_cast<const uint8_t *>(a.down.codes) + (size_t)e * a.d * a.I / 2;
+    const uint32_t *S = a.down.sb + (size_t)e * a.d * GI;
+    DTiles r;
+    down_load(r, W, S, rb, GI, 0, GI);
+    for (int i = lane; i < a.I / 8; i += 64)
+        *reinterpret_cast<u32x4_t *>(hl + (size_t)wave * a.I + 8 * i) = ld16(a.h_r + (size_t)pr * a.I + 8 * i);
+    __syncthreads();
+    const float rsum = down_finish(r, hl + (size_t)wave * a.I, W, S, rb, GI, 0, GI);
+    if (lane < 32) part[wave * 32 + lane] = rsum;
+    __syncthreads();
+    if (tid < 32) {
+        const int row = rb * 32 + tid;
+        float out = a.sh[(size_t)t * a.d + row];
+        for (int s = 0; s < a.k; ++s) out = fmaf(a.wts[(size_t)t * a.k + s], part[s * 32 + tid], out);
+        a.y[(size_t)t * a.d + row] = out;
+    }
+}
+
+DecArgs dec_args(const moe_layer *L, const uint16_t *x, int T, float *y) {
+    const moe_dims &D = L->dims;
+    DecArgs a;
+    a.x = x;
+    a.T = T;
+    a.d = D.d_model;
+    a.E = D.n_experts;
+    a.k = D.top_k;
+    a.I = D.d_expert;
+    a.Is = D.d_shared;
+    a.rq = static_cast<const uint8_t *>(L->w.router.codes);
+    a.rsb = L->w.router.sb;
+    a.logit_bias = L->w.logit_bias;
+    a.logits = L->ws.logits;
+    a.idx = L->ws.idx;
+    a.wts = L->ws.wts;
+    a.gate = L->w.gate;
+    a.up = L->w.up;
+    a.down = L->w.down;
+    a.sh_gate = L->w.sh_gate;
+    a.sh_up = L->w.sh_up;
+    a.sh_down = L->w.sh_down;
+    a.h_r = L->ws.dh_r;
+    a.h_s = L->ws.dh_s;
+    a.sh = L->ws.sh;
+    a.y = y;
+    return a;
 }
 
 }  // namespace
 
-hipError_t launch_dec_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s) {
+size_t dec_stage3_lds(const moe_dims &D) {
+    return sizeof(uint16_t) * D.top_k * D.d_expert + sizeof(float) * D.top_k * 32;
+}
+
+hipError_t launch_dec_stage1(const moe_layer *L, const uint16_t *x, int T, hipStream_t s) {
     const moe_dims &D = L->dims;
-    const int units = T * D.top_k * (D.d_expert / 32) + T * (D.d_shared / 32);
-    hipLaunchKernelGGL(k_dec_gateup, dim3(units), dim3(64 * kGUWaves), 0, s, x, T, D.d_model, D.top_k, D.d_expert,
-                       D.d_shared, L->ws.idx, L->ws.xsum, L->w.gate, L->w.up, L->w.sh_gate, L->w.sh_up, L->ws.dh_r,
-                       L->ws.dh_s, L->ws.dhsum_r, L->ws.dhsum_s);
+    const int G = D.d_model / 64;
+    const int grid = cdiv(D.n_experts, kDW) + T * (D.d_shared / 32);
+    const size_t lds_router = sizeof(float) * kDW * T * G;
+    const size_t lds_gu = sizeof(uint16_t) * D.d_model + sizeof(float) * kDW * 2 * 32;
+    hipLaunchKernelGGL(k_dec_stage1, dim3(grid), dim3(64 * kDW), lds_router > lds_gu ? lds_router : lds_gu, s,
+                       dec_args(L, x, T, nullptr));
     return hipGetLastError();
 }
 
-hipError_t launch_dec_down(const moe_layer *L, int T, float *y, hipStream_t s) {
+// Router logits only (the stage-1 router workgroups), for moe_route on a few tokens.
+hipError_t launch_dec_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s) {
     const moe_dims &D = L->dims;
-    const int NP = D.top_k * L->dec_parts_r + L->dec_parts_s;
-    const int units = T * NP * (D.d_model / 32);
-    hipLaunchKernelGGL(k_dec_down, dim3(units), dim3(64), 0, s, T, D.d_model, D.top_k, D.d_expert, D.d_shared,
-                       L->dec_parts_r, L->dec_parts_s, L->ws.idx, L->ws.wts, L->w.down, L->w.sh_down, L->ws.dh_r,
-                       L->ws.dh_s, L->ws.dhsum_r, L->ws.dhsum_s, L->ws.dpart, L->ws.dcount, y);
+    DecArgs a = dec_args(L, x, T, nullptr);
+    a.logits = logits;
+    const size_t lds = sizeof(float) * kDW * T * (D.d_model / 64);
+    hipLaunchKernelGGL(k_dec_stage1, dim3(cdiv(D.n_experts, kDW)), dim3(64 * kDW), lds, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dec_stage2(const moe_layer *L, const uint16_t *x, int T, hipStream_t s) {
+    const moe_dims &D = L->dims;
+    const int grid = T * D.top_k * (D.d_expert / 32) + T * (D.d_model / 32);
+    const size_t lds_gu = sizeof(uint16_t) * D.d_model + sizeof(float) * kDW * 2 * 32;
+    const size_t lds_sd = sizeof(uint16_t) * D.d_shared + sizeof(float) * kDW * 32;
+    const size_t lds = lds_gu > lds_sd ? lds_gu : lds_sd;
+    const DecArgs a = dec_args(L, x, T, nullptr);
+    if (D.n_experts <= 128) hipLaunchKernelGGL(k_dec_stage2<2>, dim3(grid), dim3(64 * kDW), lds, s, a);
+    else if (D.n_experts <= 256) hipLaunchKernelGGL(k_dec_stage2<4>, dim3(grid), dim3(64 * kDW), lds, s, a);
+    else hipLaunchKernelGGL(k_dec_stage2<MOE_MAX_EXPERTS / 64>, dim3(grid), dim3(64 * kDW), lds, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dec_stage3(const moe_layer *L, int T, float *y, hipStream_t s) {
+    const moe_dims &D = L->dims;
+    hipLaunchKernelGGL(k_dec_stage3, dim3(T * (D.d_model / 32)), dim3(64 * D.top_k), dec_stage3_lds(D), s,
+                       dec_args(L, nullptr, T, y));
     return hipGetLastError();
 }
 

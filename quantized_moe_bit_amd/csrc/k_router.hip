@@ -1,6 +1,7 @@
 // Router, top-k and token/expert grouping kernels (gfx950).
 //
-// Router: one logit per (token, expert) from the 8-bit group-64 affine router
+// Router (prefill chunks; decode has its own router in k_decode.hip with the same
+// arithmetic): one logit per (token, expert) from the 8-bit group-64 affine router
 // projection, with no softcap (Mference system design, "Why the runtime has this
 // shape"; "Decode", router listing), plus an optional per-expert logit bias. The
 // logits decide an integer result (the top-k set), so they are computed in one fixed
@@ -26,97 +27,125 @@
 namespace qmoe {
 namespace {
 
-constexpr int kRouterWaves = 4;                  // experts per workgroup
-constexpr int kXPitch = 66;                      // bf16 per group in LDS (64 + 2 pad: conflict-free dword reads)
 
-// grid: (ceil(E / 4), ceil(T / kRouterTokens)); block 256
-__global__ __launch_bounds__(256) void k_router(const uint16_t *__restrict__ x, int T, int d, int E,
-                                                const uint8_t *__restrict__ rq, const uint32_t *__restrict__ rsb,
-                                                const float *__restrict__ logit_bias, float *__restrict__ logits,
-                                                float *__restrict__ xsum, uint16_t *__restrict__ xsplit, int Gp) {
-    extern __shared__ __align__(16) unsigned char smem[];
+
+constexpr int kRT = 8;     // tokens per router wave (prefill router)
+
+// Group sums X_g = ((0 + x_0) + x_1) + ... + x_63 of each token (fp32, ascending), and their
+// bf16 hi | lo | hi split for the bias-term GEMM of the prefill gate/up.
+// grid: ceil(T * G / 256); block 256
+__global__ __launch_bounds__(256) void k_xsum(const uint16_t *__restrict__ x, int T, int d,
+                                              float *__restrict__ xsum, uint16_t *__restrict__ xsplit, int Gp) {
     const int G = d / 64;
-    const int t0 = blockIdx.y * kRouterTokens;
-    const int nt = min(kRouterTokens, T - t0);
-    uint16_t *xs = reinterpret_cast<uint16_t *>(smem);                  // [kRouterTokens][G][kXPitch]
-    float *Xs = reinterpret_cast<float *>(smem + sizeof(uint16_t) * kRouterTokens * G * kXPitch);  // [tok][G]
-    float *Ps = Xs + kRouterTokens * G;                                  // [4 waves][tok][G]
-    const int tid = threadIdx.x;
-
-    // stage the token tile (bf16) into LDS, padded per group
-    for (int i = tid; i < kRouterTokens * d / 2; i += 256) {
-        const int t = i / (d / 2), c = (i % (d / 2)) * 2;
-        uint32_t v = 0;
-        if (t < nt) v = *reinterpret_cast<const uint32_t *>(x + (size_t)(t0 + t) * d + c);
-        const int g = c / 64, j = c % 64;
-        *reinterpret_cast<uint32_t *>(xs + (t * G + g) * kXPitch + j) = v;
-    }
-    __syncthreads();
-    // group sums X_g in the fixed ascending order
-    for (int i = tid; i < kRouterTokens * G; i += 256) {
-        const int t = i / G, g = i % G;
-        const uint16_t *row = xs + (t * G + g) * kXPitch;
-        float s = 0.0f;
-        for (int j = 0; j < 64; ++j) s = s + bf16_to_f32(row[j]);
-        Xs[i] = s;
-        if (blockIdx.x == 0 && t < nt) {
-            const size_t tt = (size_t)(t0 + t);
-            xsum[tt * G + g] = s;
-            const uint32_t hi = f32_to_bf16(s);
-            const uint32_t lo = f32_to_bf16(s - bf16_to_f32(hi));
-            xsplit[tt * 3 * Gp + g] = (uint16_t)hi;
-            xsplit[tt * 3 * Gp + Gp + g] = (uint16_t)lo;
-            xsplit[tt * 3 * Gp + 2 * Gp + g] = (uint16_t)hi;
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= T * G) return;
+    const int t = i / G, g = i % G;
+    const u32x4_t *xp = reinterpret_cast<const u32x4_t *>(x + (size_t)t * d + 64 * g);
+    u32x4_t v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = xp[q];
+    float X = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            X = X + bf16_to_f32(v[q][w] & 0xFFFFu);
+            X = X + bf16_to_f32(v[q][w] >> 16);
         }
-    }
-    __syncthreads();
+    xsum[i] = X;
+    const uint32_t hi = f32_to_bf16(X);
+    const uint32_t lo = f32_to_bf16(X - bf16_to_f32(hi));
+    xsplit[(size_t)t * 3 * Gp + g] = (uint16_t)hi;
+    xsplit[(size_t)t * 3 * Gp + Gp + g] = (uint16_t)lo;
+    xsplit[(size_t)t * 3 * Gp + 2 * Gp + g] = (uint16_t)hi;
+}
 
-    const int wave = tid >> 6, lane = tid & 63;
-    const int e = blockIdx.x * kRouterWaves + wave;
-    if (e < E) {
-        for (int g = lane; g < G; g += 64) {
-            // this lane's 64 codes
-            const u32x4_t *cp = reinterpret_cast<const u32x4_t *>(rq + (size_t)e * d + 64 * g);
-            u32x4_t c4[4] = {cp[0], cp[1], cp[2], cp[3]};
-            const uint32_t sbw = rsb[(size_t)e * G + g];
-            const float sc = bf16_to_f32(sbw & 0xFFFFu), bi = bf16_to_f32(sbw >> 16);
-            float A[kRouterTokens];
+// Prefill router: lane = expert, wave = (64 experts, kRT tokens); a workgroup = 4 waves =
+// 128 experts x 2 kRT tokens. For every input group g, in ascending order, the workgroup
+// stages its tokens' 64 inputs of the group as fp32 in LDS; each lane converts its
+// expert's 64 codes once and runs kRT independent fma chains (one per token, ascending j,
+// inputs read by LDS broadcast); P_g = fma(s, A, fl(b * X_g)) is added to each token's
+// running logit. Same fp32 order as the oracle.
+// grid: (ceil(T / (2 kRT)), ceil(E / 128)); block 256
+__global__ __launch_bounds__(256) void k_router_pre(const uint16_t *__restrict__ x, int T, int d, int E,
+                                                   const uint8_t *__restrict__ rq, const uint32_t *__restrict__ rsb,
+                                                   const float *__restrict__ xsum,
+                                                   const float *__restrict__ logit_bias, float *__restrict__ logits) {
+    constexpr int kTok = 2 * kRT;
+    constexpr int kPitch = 68;                       // fp32 per staged token row (64 + 4 pad)
+    __shared__ __align__(16) float xs[2][kTok][kPitch];
+    __shared__ float Xs[2][kTok];
+    const int G = d / 64;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int e = blockIdx.y * 128 + (wave & 1) * 64 + lane;
+    const bool ev = e < E;
+    const int ee = ev ? e : E - 1;
+    const int tb = wave >> 1;                        // token half of the workgroup
+    const int t0 = blockIdx.x * kTok;
+    // staging: thread moves 4 inputs (token tid/16, inputs 4*(tid%16)..+3) and, for tid < kTok, X_g
+    const int st = tid >> 4, sj = (tid & 15) * 4;
+    const int stok = min(t0 + st, T - 1);
+    const uint16_t *xsrc = x + (size_t)stok * d + sj;
+    const uint8_t *qsrc = rq + (size_t)ee * d;
+    const uint32_t *ssrc = rsb + (size_t)ee * G;
+
+    uint2 xr = *reinterpret_cast<const uint2 *>(xsrc);
+    float Xr = (tid < kTok) ? xsum[(size_t)min(t0 + tid, T - 1) * G] : 0.0f;
+    u32x4_t qv[4];
 #pragma unroll
-            for (int t = 0; t < kRouterTokens; ++t) A[t] = 0.0f;
+    for (int i = 0; i < 4; ++i) qv[i] = reinterpret_cast<const u32x4_t *>(qsrc)[i];
+    uint32_t sbw = ssrc[0];
+    float L[kRT];
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
+    for (int i = 0; i < kRT; ++i) L[i] = 0.0f;
+    for (int g = 0; g < G; ++g) {
+        const int buf = g & 1;
+        *reinterpret_cast<f32x4_t *>(&xs[buf][st][sj]) =
+            f32x4_t{bf16_to_f32(xr.x & 0xFFFFu), bf16_to_f32(xr.x >> 16), bf16_to_f32(xr.y & 0xFFFFu),
+                    bf16_to_f32(xr.y >> 16)};
+        if (tid < kTok) Xs[buf][tid] = Xr;
+        float qf[64];
 #pragma unroll
-                for (int wi = 0; wi < 4; ++wi) {
-                    const uint32_t cw = c4[q4][wi];
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int b = 0; b < 4; b += 2) {
-                        const int j = q4 * 16 + wi * 4 + b;     // element index within the group
-                        const float qa = (float)((cw >> (8 * b)) & 0xFFu);
-                        const float qb = (float)((cw >> (8 * (b + 1))) & 0xFFu);
+            for (int w = 0; w < 4; ++w)
 #pragma unroll
-                        for (int t = 0; t < kRouterTokens; ++t) {
-                            const uint32_t xv =
-                                *reinterpret_cast<const uint32_t *>(xs + (t * G + g) * kXPitch + j);
-                            A[t] = __builtin_fmaf(bf16_to_f32(xv & 0xFFFFu), qa, A[t]);
-                            A[t] = __builtin_fmaf(bf16_to_f32(xv >> 16), qb, A[t]);
-                        }
-                    }
-                }
-            }
+                for (int b = 0; b < 4; ++b) qf[i * 16 + w * 4 + b] = (float)((qv[i][w] >> (8 * b)) & 0xFFu);
+        const float sc = bf16_to_f32(sbw & 0xFFFFu), bi = bf16_to_f32(sbw >> 16);
+        __syncthreads();
+        if (g + 1 < G) {                             // prefetch the next group
+            xr = *reinterpret_cast<const uint2 *>(xsrc + 64 * (g + 1));
+            if (tid < kTok) Xr = xsum[(size_t)min(t0 + tid, T - 1) * G + g + 1];
 #pragma unroll
-            for (int t = 0; t < kRouterTokens; ++t) {
-                const float bX = bi * Xs[t * G + g];
-                Ps[(wave * kRouterTokens + t) * G + g] = __builtin_fmaf(sc, A[t], bX);
+            for (int i = 0; i < 4; ++i) qv[i] = reinterpret_cast<const u32x4_t *>(qsrc + 64 * (g + 1))[i];
+            sbw = ssrc[g + 1];
+        }
+        float A[kRT];
+#pragma unroll
+        for (int i = 0; i < kRT; ++i) A[i] = 0.0f;
+#pragma unroll
+        for (int j4 = 0; j4 < 16; ++j4) {
+#pragma unroll
+            for (int i = 0; i < kRT; ++i) {
+                const f32x4_t xv = *reinterpret_cast<const f32x4_t *>(&xs[buf][tb * kRT + i][4 * j4]);
+                A[i] = __builtin_fmaf(xv[0], qf[4 * j4 + 0], A[i]);
+                A[i] = __builtin_fmaf(xv[1], qf[4 * j4 + 1], A[i]);
+                A[i] = __builtin_fmaf(xv[2], qf[4 * j4 + 2], A[i]);
+                A[i] = __builtin_fmaf(xv[3], qf[4 * j4 + 3], A[i]);
             }
         }
+#pragma unroll
+        for (int i = 0; i < kRT; ++i) {
+            const float bX = bi * Xs[buf][tb * kRT + i];
+            L[i] = L[i] + __builtin_fmaf(sc, A[i], bX);
+        }
+        // the next iteration writes the other buffer; the barrier after its staging orders it
     }
-    __syncthreads();
-    if (e < E && lane < nt) {
-        const float *p = Ps + (wave * kRouterTokens + lane) * G;
-        float L = 0.0f;
-        for (int g = 0; g < G; ++g) L = L + p[g];
-        if (logit_bias) L = L + logit_bias[e];
-        logits[(size_t)(t0 + lane) * E + e] = L;
+    if (!ev) return;
+#pragma unroll
+    for (int i = 0; i < kRT; ++i) {
+        const int t = t0 + tb * kRT + i;
+        if (t < T) logits[(size_t)t * E + e] = logit_bias ? L[i] + logit_bias[e] : L[i];
     }
 }
 
@@ -125,14 +154,14 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
     return va > vb || (va == vb && ia < ib);
 }
 
-// grid: ceil(T / 4); block 256 -- one wave per token
+// grid: ceil(T / 4); block 256 -- one wave per token; kPer logits per lane (E <= 64 kPer)
+template <int kPer>
 __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, int T, int E, int k,
                                               int32_t *__restrict__ idx, float *__restrict__ wout) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
     const float *l = logits + (size_t)t * E;
-    constexpr int kPer = MOE_MAX_EXPERTS / 64;
     float v[kPer];
     const int nper = (E + 63) / 64;
 #pragma unroll
@@ -141,8 +170,8 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
         v[i] = (i < nper && e < E) ? l[e] : -__builtin_inff();
     }
     uint32_t taken = 0;   // bit i: element lane + 64 i already selected
-    float sel_v[MOE_MAX_TOP_K];
-    int sel_i[MOE_MAX_TOP_K];
+    float my_v = 0.0f, m = 0.0f, z = 0.0f;   // lane s keeps slot s
+    int my_i = 0;
     for (int s = 0; s < k; ++s) {
         float bv = -__builtin_inff();
         int bi = 0x7FFFFFFF;
@@ -165,22 +194,16 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
             }
         }
         if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-        sel_v[s] = bv;
-        sel_i[s] = bi;
+        if (s == 0) m = bv;
+        z += __expf(bv - m);
+        if (lane == s) {
+            my_v = bv;
+            my_i = bi;
+        }
     }
-    if (lane == 0) {
-        const float m = sel_v[0];
-        float z = 0.0f;
-        float ex[MOE_MAX_TOP_K];
-        for (int s = 0; s < k; ++s) {
-            ex[s] = __expf(sel_v[s] - m);
-            z += ex[s];
-        }
-        const float inv = 1.0f / z;
-        for (int s = 0; s < k; ++s) {
-            idx[(size_t)t * k + s] = min(max(sel_i[s], 0), E - 1);
-            wout[(size_t)t * k + s] = ex[s] * inv;
-        }
+    if (lane < k) {
+        idx[(size_t)t * k + lane] = min(max(my_i, 0), E - 1);
+        wout[(size_t)t * k + lane] = __expf(my_v - m) / z;
     }
 }
 
@@ -222,10 +245,16 @@ __global__ __launch_bounds__(1024) void k_bucket_scan(int nchunks, int E, int32_
     const int e = threadIdx.x;
     int run = 0;
     if (e < E) {
-        for (int c = 0; c < nchunks; ++c) {
-            const int v = chunk_base[(size_t)c * E + e];
-            chunk_base[(size_t)c * E + e] = run;
-            run += v;
+        for (int c0 = 0; c0 < nchunks; c0 += 16) {   // loads of a batch are independent
+            int v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = (c0 + i < nchunks) ? chunk_base[(size_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (c0 + i < nchunks) {
+                    chunk_base[(size_t)(c0 + i) * E + e] = run;
+                    run += v[i];
+                }
         }
         counts[e] = run;
         sc[e] = run;
@@ -248,7 +277,14 @@ __global__ __launch_bounds__(1024) void k_bucket_scan(int nchunks, int E, int32_
     __syncthreads();
     if (e < E) {
         const int base = sc[e];
-        for (int c = 0; c < nchunks; ++c) chunk_base[(size_t)c * E + e] += base;
+        for (int c0 = 0; c0 < nchunks; c0 += 16) {
+            int v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = (c0 + i < nchunks) ? chunk_base[(size_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (c0 + i < nchunks) chunk_base[(size_t)(c0 + i) * E + e] = v[i] + base;
+        }
     }
 }
 
@@ -271,17 +307,19 @@ __global__ __launch_bounds__(256) void k_bucket_scatter(const int32_t *__restric
 
 hipError_t launch_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s) {
     const int d = L->dims.d_model, E = L->dims.n_experts, G = d / 64;
-    dim3 grid(cdiv(E, kRouterWaves), cdiv(T, kRouterTokens));
-    const size_t lds = sizeof(uint16_t) * kRouterTokens * G * kXPitch + sizeof(float) * kRouterTokens * G * 5;
-    hipLaunchKernelGGL(k_router, grid, dim3(256), lds, s, x, T, d, E,
-                       static_cast<const uint8_t *>(L->w.router.codes), L->w.router.sb, L->w.logit_bias, logits,
-                       L->ws.xsum, L->ws.xsplit, L->Gp_d);
+    hipLaunchKernelGGL(k_xsum, dim3(cdiv(T * G, 256)), dim3(256), 0, s, x, T, d, L->ws.xsum, L->ws.xsplit,
+                       L->Gp_d);
+    hipLaunchKernelGGL(k_router_pre, dim3(cdiv(T, 2 * kRT), cdiv(E, 128)), dim3(256), 0, s, x, T, d, E,
+                       static_cast<const uint8_t *>(L->w.router.codes), L->w.router.sb, L->ws.xsum, L->w.logit_bias,
+                       logits);
     return hipGetLastError();
 }
 
 hipError_t launch_topk(const moe_layer *L, int T, const float *logits, int32_t *idx, float *w, hipStream_t s) {
-    hipLaunchKernelGGL(k_topk, dim3(cdiv(T, 4)), dim3(256), 0, s, logits, T, L->dims.n_experts, L->dims.top_k,
-                       idx, w);
+    const int E = L->dims.n_experts, k = L->dims.top_k;
+    if (E <= 128) hipLaunchKernelGGL(k_topk<2>, dim3(cdiv(T, 4)), dim3(256), 0, s, logits, T, E, k, idx, w);
+    else if (E <= 256) hipLaunchKernelGGL(k_topk<4>, dim3(cdiv(T, 4)), dim3(256), 0, s, logits, T, E, k, idx, w);
+    else hipLaunchKernelGGL(k_topk<MOE_MAX_EXPERTS / 64>, dim3(cdiv(T, 4)), dim3(256), 0, s, logits, T, E, k, idx, w);
     return hipGetLastError();
 }
 

@@ -25,9 +25,9 @@ void clear_error() { g_err[0] = 0; }
 
 namespace {
 
-const char *kKernelNames[K_COUNT] = {"router",       "topk",        "bucket_rank", "bucket_scan",
-                                     "bucket_scatter", "dec_gateup", "dec_down",    "pre_gateup",
-                                     "pre_down",     "combine",     "glue"};
+const char *kKernelNames[K_COUNT] = {"router",     "topk",       "bucket_rank", "bucket_scan", "bucket_scatter",
+                                     "dec_route_shared", "dec_gateup", "dec_down", "pre_gateup",  "pre_down",
+                                     "combine",    "glue"};
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -48,6 +48,11 @@ moe_status check_dims(const moe_dims *D) {
         return fail(MOE_E_SHAPE, "top_k %d out of range [1, min(n_experts, %d)]", D->top_k, MOE_MAX_TOP_K);
     if (D->max_tokens < 1 || D->max_tokens > (1 << 20))
         return fail(MOE_E_SHAPE, "max_tokens %d out of range [1, 2^20]", D->max_tokens);
+    if (D->d_expert > 16384 || D->d_shared > 16384)
+        return fail(MOE_E_SHAPE, "d_expert %d / d_shared %d above 16384", D->d_expert, D->d_shared);
+    if (dec_stage3_lds(*D) > 65536)
+        return fail(MOE_E_SHAPE, "top_k * d_expert = %d too large for the decode down projection (LDS)",
+                    D->top_k * D->d_expert);
     return MOE_OK;
 }
 
@@ -142,8 +147,9 @@ moe_status run(moe_layer *L, int id, hipStream_t s, F &&f) {
     } while (0)
 
 moe_status route_impl(moe_layer *L, const uint16_t *x, int T, hipStream_t s, float *logits, int32_t *idx,
-                      float *w, bool bucket, int32_t *perm_out) {
-    RUN(K_ROUTER, launch_router(L, x, T, logits, s));
+                      float *w, bool bucket, int32_t *perm_out, bool prefill) {
+    if (!prefill && T <= L->max_dec) RUN(K_ROUTER, launch_dec_router(L, x, T, logits, s));
+    else RUN(K_ROUTER, launch_router(L, x, T, logits, s));
     RUN(K_TOPK, launch_topk(L, T, logits, idx, w, s));
     if (bucket) {
         RUN(K_BUCKET_RANK, launch_bucket_rank(L, T, idx, s));
@@ -205,11 +211,8 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     L->Gp_I = roundup(L->G_I, 16);
     L->Gp_Is = roundup(L->G_Is, 16);
     L->max_dec = D.max_tokens < MOE_MAX_DECODE_TOKENS ? D.max_tokens : MOE_MAX_DECODE_TOKENS;
-    L->dec_parts_r = cdiv(L->G_I, kDecodeChunkGroups);
-    L->dec_parts_s = cdiv(L->G_Is, kDecodeChunkGroups);
     const size_t Dm = (size_t)L->max_dec;
     const size_t nchunks = (size_t)cdiv((int)P, kChunk);
-    const size_t NP = (size_t)k * L->dec_parts_r + L->dec_parts_s;
 
     Plan plan;
     Workspace &ws = L->ws;
@@ -233,10 +236,6 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.sh, Tm * d);
     plan.take(&ws.dh_r, Dm * k * I);
     plan.take(&ws.dh_s, Dm * Is);
-    plan.take(&ws.dhsum_r, Dm * k * (I / 32));
-    plan.take(&ws.dhsum_s, Dm * (Is / 32));
-    plan.take(&ws.dpart, Dm * NP * d);
-    plan.take(&ws.dcount, Dm * (d / 32));
     L->ws_bytes = (plan.off + 255) & ~size_t(255);
 
     int dev = 0;
@@ -273,11 +272,7 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     rebase(ws.sh, base);
     rebase(ws.dh_r, base);
     rebase(ws.dh_s, base);
-    rebase(ws.dhsum_r, base);
-    rebase(ws.dhsum_s, base);
-    rebase(ws.dpart, base);
-    rebase(ws.dcount, base);
-    // zero once: padding columns of the split sums and the self-resetting counters rely on it
+    // zero once: padding columns of the split sums rely on it
     err = hipMemset(L->ws_base, 0, L->ws_bytes);
     if (err == hipSuccess) err = hipDeviceSynchronize();
     if (err != hipSuccess) {
@@ -319,7 +314,7 @@ moe_status moe_route(moe_layer *L, const uint16_t *x, int32_t T, int32_t *topk_i
         return fail(MOE_E_ALIGN, "moe_route: grouping outputs not 16-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     float *lg = logits ? logits : L->ws.logits;
-    st = route_impl(L, x, T, s, lg, topk_idx, topk_w, expert_offsets != nullptr, pair_perm);
+    st = route_impl(L, x, T, s, lg, topk_idx, topk_w, expert_offsets != nullptr, pair_perm, false);
     if (st != MOE_OK) return st;
     if (expert_offsets) {
         hipError_t err = hipMemcpyAsync(expert_offsets, L->ws.offsets, sizeof(int32_t) * (L->dims.n_experts + 1),
@@ -336,10 +331,9 @@ moe_status moe_forward_decode(moe_layer *L, const uint16_t *x, int32_t T, float 
     if (T > L->max_dec)
         return fail(MOE_E_CAPACITY, "moe_forward_decode: T = %d exceeds the decode capacity %d", T, L->max_dec);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    st = route_impl(L, x, T, s, L->ws.logits, L->ws.idx, L->ws.wts, false, nullptr);
-    if (st != MOE_OK) return st;
-    RUN(K_DEC_GATEUP, launch_dec_gateup(L, x, T, s));
-    RUN(K_DEC_DOWN, launch_dec_down(L, T, y, s));
+    RUN(K_DEC_STAGE1, launch_dec_stage1(L, x, T, s));
+    RUN(K_DEC_STAGE2, launch_dec_stage2(L, x, T, s));
+    RUN(K_DEC_STAGE3, launch_dec_stage3(L, T, y, s));
     return MOE_OK;
 }
 
@@ -348,7 +342,7 @@ moe_status moe_forward_prefill(moe_layer *L, const uint16_t *x, int32_t T, float
     moe_status st = check_call(L, x, T, y, "moe_forward_prefill");
     if (st != MOE_OK || T == 0) return st;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    st = route_impl(L, x, T, s, L->ws.logits, L->ws.idx, L->ws.wts, true, nullptr);
+    st = route_impl(L, x, T, s, L->ws.logits, L->ws.idx, L->ws.wts, true, nullptr, true);
     if (st != MOE_OK) return st;
     RUN(K_PRE_GATEUP, launch_pre_gateup(L, x, T, s));
     RUN(K_PRE_DOWN, launch_pre_down(L, T, s));

@@ -20,8 +20,7 @@ constexpr int kGroup = 64;          // quantization group (inputs per scale/bias
 constexpr int kTileRows = 32;       // rows per 1 KiB weight tile
 constexpr int kMT = 128;            // prefill GEMM rows per workgroup tile
 constexpr int kChunk = 256;         // pairs per bucketing chunk
-constexpr int kDecodeChunkGroups = 12;  // K groups per decode down-projection part
-constexpr int kRouterTokens = 8;    // tokens per router workgroup
+constexpr int kDecodeChunkGroups = 12;  // K groups a decode wave loads before computing (down)
 
 __host__ __device__ inline int roundup(int a, int b) { return (a + b - 1) / b * b; }
 __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
@@ -33,8 +32,9 @@ enum KernelId {
     K_BUCKET_RANK,
     K_BUCKET_SCAN,
     K_BUCKET_SCATTER,
-    K_DEC_GATEUP,
-    K_DEC_DOWN,
+    K_DEC_STAGE1,
+    K_DEC_STAGE2,
+    K_DEC_STAGE3,
     K_PRE_GATEUP,
     K_PRE_DOWN,
     K_COMBINE,
@@ -65,10 +65,6 @@ struct Workspace {
     // decode path
     uint16_t *dh_r;       // [D*k, I]           fp16 bits
     uint16_t *dh_s;       // [D, I_s]           fp16 bits
-    float *dhsum_r;       // [D*k, I/32]        sums of 32 consecutive hidden values
-    float *dhsum_s;       // [D, I_s/32]
-    float *dpart;         // [D, parts, d]
-    uint32_t *dcount;     // [D, d/32]          arrival counters (self-resetting)
 };
 
 struct ProfEvent {
@@ -85,7 +81,6 @@ struct moe_layer {
     int G_d, G_I, G_Is;        // groups along d, I, I_s
     int Gp_d, Gp_I, Gp_Is;     // padded to a multiple of 16
     int max_dec;               // decode capacity = min(max_tokens, MOE_MAX_DECODE_TOKENS)
-    int dec_parts_r, dec_parts_s;  // decode down-projection parts per routed slot / for the shared expert
     void *ws_base;
     size_t ws_bytes;
     qmoe::Workspace ws;
@@ -100,13 +95,16 @@ struct moe_layer {
 namespace qmoe {
 
 // Kernel launchers (each enqueues on stream, returns hipGetLastError()).
+hipError_t launch_dec_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s);
 hipError_t launch_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s);
 hipError_t launch_topk(const moe_layer *L, int T, const float *logits, int32_t *idx, float *w, hipStream_t s);
 hipError_t launch_bucket_rank(const moe_layer *L, int T, const int32_t *idx, hipStream_t s);
 hipError_t launch_bucket_scan(const moe_layer *L, int T, hipStream_t s);
 hipError_t launch_bucket_scatter(const moe_layer *L, int T, const int32_t *idx, int32_t *perm, hipStream_t s);
-hipError_t launch_dec_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s);
-hipError_t launch_dec_down(const moe_layer *L, int T, float *y, hipStream_t s);
+hipError_t launch_dec_stage1(const moe_layer *L, const uint16_t *x, int T, hipStream_t s);
+hipError_t launch_dec_stage2(const moe_layer *L, const uint16_t *x, int T, hipStream_t s);
+hipError_t launch_dec_stage3(const moe_layer *L, int T, float *y, hipStream_t s);
+size_t dec_stage3_lds(const moe_dims &D);
 hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s);
 hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s);
 hipError_t launch_combine(const moe_layer *L, int T, float *y, hipStream_t s);

@@ -1,39 +1,47 @@
-// Decode path (up to 16 tokens): three launches of wavefront GEMV kernels over
-// 4-bit group-64 affine weights, with no communication between workgroups of a launch.
+// Decode path (up to 16 tokens): three launches of wavefront GEMV kernels over 4-bit
+// group-64 affine weights, with no communication between workgroups of a launch.
 //
-// Each selected expert is a GELU-gated FFN whose weights are w = scale * q + bias
-// per group of 64 inputs (Mference system design, "Why the runtime has this shape";
-// "Metal execution": decode uses custom affine INT4/INT8 GEMV kernels that consume the
-// packed codes and BF16 scale/bias directly, and the routed kernels fuse the affine
-// decode, GeGLU and the weighted reduction).
+// Each selected expert is a GELU-gated FFN whose weights are w = scale * q + bias per group
+// of 64 inputs (Mference system design, "Why the runtime has this shape"; "Metal
+// execution": decode uses custom affine INT4/INT8 GEMV kernels that consume the packed codes
+// and BF16 scale/bias directly, and the routed kernels fuse the affine decode, GeGLU and the
+// weighted reduction).
 //
 // Exact affine split per group (x the 64 inputs of the group):
 //   sum_j x_j (s q_j + b) = 16 s * sum_j x_j (1 + q_j/16) + (b - 16 s) * sum_j x_j.
-// A lane holds half of a group's inputs; it adds 16 s * (its half of the first sum)
-// + (b - 16 s) * (its half of sum x), which is linear, so the two halves add up to the
-// exact group term. 1 + q/16 comes from the nibbles with one shift and one and-or;
-// v_dot2_f32_bf16 (gate/up, x is bf16) and v_dot2_f32_f16 (down, h is fp16) accumulate
-// in fp32.
+// A lane holds half of a group's inputs; it adds 16 s * (its half of the first sum) +
+// (b - 16 s) * (its half of sum x), which is linear, so the halves add up to the exact group
+// term. 1 + q/16 comes from the nibbles with one shift and one and-or; v_dot2_f32_bf16
+// (gate/up, x is bf16) and v_dot2_f32_f16 (down, h is fp16) accumulate in fp32.
 //
-// Launch 1 (k_dec_stage1): router logits in the fixed fp32 order the oracle uses (one
-//   wave per expert, one lane per input group), and, in other workgroups, the shared
-//   expert's gate/up (it does not depend on routing; Mference "Decode" likewise starts
-//   the shared branch before the routed one).
-// Launch 2 (k_dec_stage2): each wave derives its token's top-k from the logits with a
-//   DPP argmax over packed (logit, index) keys (identical on every wave), then the routed
-//   gate/up + GeGLU for (pair, 32-row block); other workgroups run the shared down
-//   projection.
+// Work is cut into many thin units: every projection is split along its input dimension into
+// pieces of kGPS groups, each piece a 256-thread workgroup streaming ~25 KB, and the consumer
+// of a projection adds its partial sums in piece order (fixed order, deterministic).
+//
+// Launch 1 (k_dec_stage1): router logits in the fixed fp32 order the oracle uses (one wave
+//   per expert, one lane per input group), and the shared expert's gate/up partial sums (the
+//   shared branch does not depend on routing; Mference "Decode" likewise starts it before
+//   the routed branch).
+// Launch 2 (k_dec_stage2): routed gate/up partial sums per (pair, 32 rows, input piece); each
+//   wave first derives its token's top-k from the logits with a DPP argmax over packed
+//   (logit, index) keys, identical on every wave. Other workgroups: the shared down
+//   projection per (token, 32 rows, input piece), forming h = fp16(gelu(g) * u) for their
+//   piece from the launch-1 partials.
 // Launch 3 (k_dec_stage3): one workgroup per (token, 32 output rows), one wave per routed
-//   slot, then y = shared + w_0 r_0 + ... + w_{k-1} r_{k-1} in slot order (Mference
-//   "Decode", cb2; TinyTitan architecture "Invariants": fixed reduction order).
+//   slot: h of the slot from the launch-2 partials, the down projection, then
+//   y = shared + w_0 r_0 + ... + w_{k-1} r_{k-1} in slot order (Mference "Decode", cb2;
+//   TinyTitan architecture "Invariants": fixed reduction order).
 #include "device_common.h"
 #include "moe_internal.h"
 
 namespace qmoe {
 namespace {
 
-constexpr int kDW = 8;      // waves per decode workgroup
-constexpr int kDB = 6;      // groups whose tiles a wave loads before computing (gate/up)
+constexpr int kRW = 4;      // router experts (waves) per workgroup
+constexpr int kPW = 4;      // waves per partial-sum workgroup
+constexpr int kPB = cdiv_c(kGPS, kPW);   // groups per wave in a piece
+constexpr int kW2 = 8;      // waves per launch-2 workgroup
+constexpr int kB2 = 6;      // groups per wave of a routed gate/up unit (kW2 * kB2 >= 48 input groups)
 constexpr uint32_t kOneBf16x2 = 0x3F803F80u;
 constexpr uint32_t kOneF16x2 = 0x3C003C00u;
 
@@ -76,56 +84,45 @@ __device__ __forceinline__ void router_wave(const uint16_t *__restrict__ x, int 
     }
 }
 
-// ----------------------------------------------------------------------------- gate/up unit
-// 32 rows (block jb) of gate and of up for one token (x staged in LDS as bf16), then
-// h = fp16(gelu(g) * u). All kDW waves of the workgroup take part; wave w owns input groups
-// w, w + kDW, ... The first batch of tiles is loaded before the caller stages x.
+// ----------------------------------------------------------------------------- gate/up piece
+// Partial gate and up sums of 32 rows (block jb) over input groups [g0, g1) (at most kGPS)
+// for one token, x of those groups staged in LDS (xs, indexed from g0). Wave w takes groups
+// g0 + w, g0 + w + kPW, ...; the four waves' sums are added in wave order.
+template <int PB>
 struct GUTiles {
-    u32x4_t wg[kDB], wu[kDB];
-    uint32_t sbg[kDB], sbu[kDB];
+    u32x4_t wg[PB], wu[PB];
+    uint32_t sbg[PB], sbu[PB];
 };
 
-struct GUPtrs {
-    const uint8_t *Wg, *Wu;
-    const uint32_t *Sg, *Su;
-};
-
-__device__ __forceinline__ GUPtrs gu_ptrs(const uint8_t *Wg, const uint8_t *Wu, const uint32_t *Sg, const uint32_t *Su,
-                                          int G, int jb) {
-    const int lane = threadIdx.x & 63, n = lane & 31;
-    GUPtrs p;
-    p.Wg = Wg + (size_t)jb * G * 1024 + lane * 16;
-    p.Wu = Wu + (size_t)jb * G * 1024 + lane * 16;
-    p.Sg = Sg + (size_t)jb * G * 32 + n;
-    p.Su = Su + (size_t)jb * G * 32 + n;
-    return p;
-}
-
-__device__ __forceinline__ void gu_load(GUTiles &r, const GUPtrs &p, int G, int gb0) {
-    const int wave = threadIdx.x >> 6;
+template <int NW, int PB>
+__device__ __forceinline__ void gu_load(GUTiles<PB> &r, const uint8_t *Wg, const uint8_t *Wu, const uint32_t *Sg,
+                                        const uint32_t *Su, int G, int jb, int g0, int g1) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31;
+    const size_t tb = (size_t)jb * G;
 #pragma unroll
-    for (int b = 0; b < kDB; ++b) {
-        const int g = gb0 + wave + b * kDW;
-        if (g < G) {
-            r.wg[b] = ld16(p.Wg + (size_t)g * 1024);
-            r.wu[b] = ld16(p.Wu + (size_t)g * 1024);
-            r.sbg[b] = p.Sg[g * 32];
-            r.sbu[b] = p.Su[g * 32];
+    for (int b = 0; b < PB; ++b) {
+        const int g = g0 + wave + b * NW;
+        if (g < g1) {
+            r.wg[b] = ld16(Wg + (tb + g) * 1024 + lane * 16);
+            r.wu[b] = ld16(Wu + (tb + g) * 1024 + lane * 16);
+            r.sbg[b] = Sg[(tb + g) * 32 + n];
+            r.sbu[b] = Su[(tb + g) * 32 + n];
         }
     }
 }
 
-__device__ __forceinline__ void gu_compute(const GUTiles &r, const uint16_t *xs, int G, int gb0, float &accg,
+template <int NW, int PB>
+__device__ __forceinline__ void gu_compute(const GUTiles<PB> &r, const uint16_t *xs, int g0, int g1, float &accg,
                                            float &accu) {
     const int wave = threadIdx.x >> 6, half = (threadIdx.x >> 5) & 1;
 #pragma unroll
-    for (int b = 0; b < kDB; ++b) {
-        const int g = gb0 + wave + b * kDW;
-        if (g < G) {
+    for (int b = 0; b < PB; ++b) {
+        const int g = g0 + wave + b * NW;
+        if (g < g1) {
             float ag = 0.0f, au = 0.0f, xsum = 0.0f;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xs + 64 * g + 16 * s + 8 * half);
+                const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xs + 64 * (g - g0) + 16 * s + 8 * half);
                 ag = dot2_bf16(xv[0], nib_pair<0>(r.wg[b][s]), ag);
                 ag = dot2_bf16(xv[1], nib_pair<1>(r.wg[b][s]), ag);
                 ag = dot2_bf16(xv[2], nib_pair<2>(r.wg[b][s]), ag);
@@ -147,20 +144,24 @@ __device__ __forceinline__ void gu_compute(const GUTiles &r, const uint16_t *xs,
     }
 }
 
-// Full unit: tiles of the first batch are already in r; x is staged by stage_x() between the
-// first loads and the barrier.
-template <class StageX>
-__device__ __forceinline__ void gateup_unit(GUTiles &r, const GUPtrs &p, const uint16_t *xs, int G, int jb,
-                                            uint16_t *hout, float (*red)[2][32], StageX stage_x) {
+// One gate/up piece over input groups [g0, g1) (at most NW * PB) with NW waves: loads tiles,
+// stages x[g0:g1] of token row xrow, computes, adds the waves' sums in wave order, and either
+// writes the 32 partial gate and up sums to out_g[n], out_u[n] (hout == nullptr) or, when the
+// piece covers the whole input, h = fp16(gelu(g) * u) to hout[n].
+// LDS: xs (NW * PB * 64 bf16), red.
+template <int NW, int PB>
+__device__ __forceinline__ void gateup_piece(const uint16_t *xrow, const uint8_t *Wg, const uint8_t *Wu,
+                                             const uint32_t *Sg, const uint32_t *Su, int G, int jb, int g0, int g1,
+                                             uint16_t *xs, float (*red)[2][32], float *out_g, float *out_u,
+                                             uint16_t *hout) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31;
-    stage_x();
+    GUTiles<PB> r;
+    gu_load<NW, PB>(r, Wg, Wu, Sg, Su, G, jb, g0, g1);
+    for (int i = tid; i < (g1 - g0) * 8; i += 64 * NW)
+        *reinterpret_cast<u32x4_t *>(xs + 8 * i) = ld16(xrow + 64 * g0 + 8 * i);
     __syncthreads();
     float accg = 0.0f, accu = 0.0f;
-    gu_compute(r, xs, G, 0, accg, accu);
-    for (int gb0 = kDW * kDB; gb0 < G; gb0 += kDW * kDB) {
-        gu_load(r, p, G, gb0);
-        gu_compute(r, xs, G, gb0, accg, accu);
-    }
+    gu_compute<NW, PB>(r, xs, g0, g1, accg, accu);
     accg += __shfl_xor(accg, 32);
     accu += __shfl_xor(accu, 32);
     if (lane < 32) {
@@ -171,46 +172,99 @@ __device__ __forceinline__ void gateup_unit(GUTiles &r, const GUPtrs &p, const u
     if (tid < 32) {
         float gv = 0.0f, uv = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kDW; ++w) {
+        for (int w = 0; w < NW; ++w) {
             gv += red[w][0][tid];
             uv += red[w][1][tid];
         }
-        hout[jb * 32 + tid] = (uint16_t)f32_to_f16_sat(gelu_tanh_f32(gv) * uv);
+        if (hout) {
+            hout[tid] = (uint16_t)f32_to_f16_sat(gelu_tanh_f32(gv) * uv);
+        } else {
+            out_g[tid] = gv;
+            out_u[tid] = uv;
+        }
+    }
+}
+
+// h = fp16(gelu(g) * u) for inputs [j0, j0 + nj) of a projection whose gate/up partial sums
+// (KS pieces) are at part[(ks * 2 + {0: gate, 1: up}) * J + j]; pieces added in order. Each
+// thread handles at most NPT inputs; for KS <= kKSFast every partial is loaded before any is
+// used (one round trip), otherwise piece by piece.
+constexpr int kKSFast = 4;
+template <int NPT>
+__device__ __forceinline__ void form_h(const float *part, int KS, int J, int j0, int nj, uint16_t *hl, int tid,
+                                       int nthreads) {
+    float gv[NPT], uv[NPT];
+    if (KS <= kKSFast) {
+        float gp[kKSFast][NPT], up[kKSFast][NPT];
+#pragma unroll
+        for (int ks = 0; ks < kKSFast; ++ks)
+#pragma unroll
+            for (int i = 0; i < NPT; ++i) {
+                const int j = tid + i * nthreads;
+                const bool ok = ks < KS && j < nj;
+                gp[ks][i] = ok ? part[(size_t)(ks * 2) * J + j0 + j] : 0.0f;
+                up[ks][i] = ok ? part[(size_t)(ks * 2 + 1) * J + j0 + j] : 0.0f;
+            }
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) {
+            gv[i] = gp[0][i];
+            uv[i] = up[0][i];
+#pragma unroll
+            for (int ks = 1; ks < kKSFast; ++ks) {
+                gv[i] += gp[ks][i];
+                uv[i] += up[ks][i];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) gv[i] = uv[i] = 0.0f;
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int i = 0; i < NPT; ++i) {
+                const int j = tid + i * nthreads;
+                if (j < nj) {
+                    gv[i] += part[(size_t)(ks * 2) * J + j0 + j];
+                    uv[i] += part[(size_t)(ks * 2 + 1) * J + j0 + j];
+                }
+            }
+    }
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+        const int j = tid + i * nthreads;
+        if (j < nj) hl[j] = (uint16_t)f32_to_f16_sat(gelu_tanh_f32(gv[i]) * uv[i]);
     }
 }
 
 // ----------------------------------------------------------------------------- down part
-// One wave: 32 output rows (block rb) of a down projection over groups [g0, g1) of its fp16
-// input h (staged in LDS at hl, indexed from group 0). The first batch of tiles is loaded
-// before the caller stages h.
+// One wave: 32 output rows (block rb) of a down projection over input groups [g0, g1)
+// (at most kDecodeChunkGroups) of its fp16 input h, staged in LDS at hl (indexed from g0).
 struct DTiles {
     u32x4_t w4[kDecodeChunkGroups];
     uint32_t sbw[kDecodeChunkGroups];
 };
 
-__device__ __forceinline__ void down_load(DTiles &r, const uint8_t *W, const uint32_t *S, int rb, int Gk, int gb,
+__device__ __forceinline__ void down_load(DTiles &r, const uint8_t *W, const uint32_t *S, int rb, int Gk, int g0,
                                           int g1) {
     const int lane = threadIdx.x & 63, n = lane & 31;
-    W += (size_t)rb * Gk * 1024 + lane * 16;
-    S += (size_t)rb * Gk * 32 + n;
+    const size_t tb = (size_t)rb * Gk;
 #pragma unroll
     for (int b = 0; b < kDecodeChunkGroups; ++b)
-        if (gb + b < g1) {
-            r.w4[b] = ld16(W + (size_t)(gb + b) * 1024);
-            r.sbw[b] = S[(gb + b) * 32];
+        if (g0 + b < g1) {
+            r.w4[b] = ld16(W + (tb + g0 + b) * 1024 + lane * 16);
+            r.sbw[b] = S[(tb + g0 + b) * 32 + n];
         }
 }
 
-__device__ __forceinline__ float down_compute(const DTiles &r, const uint16_t *hl, int gb, int g1, float acc) {
+__device__ __forceinline__ float down_compute(const DTiles &r, const uint16_t *hl, int g0, int g1) {
     const int half = (threadIdx.x >> 5) & 1;
+    float acc = 0.0f;
 #pragma unroll
     for (int b = 0; b < kDecodeChunkGroups; ++b)
-        if (gb + b < g1) {
-            const int g = gb + b;
+        if (g0 + b < g1) {
             float a = 0.0f, hsum = 0.0f;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const u32x4_t hv = *reinterpret_cast<const u32x4_t *>(hl + 64 * g + 16 * s + 8 * half);
+                const u32x4_t hv = *reinterpret_cast<const u32x4_t *>(hl + 64 * b + 16 * s + 8 * half);
                 a = dot2_f16(hv[0], nib_pair_f16<0>(r.w4[b][s]), a);
                 a = dot2_f16(hv[1], nib_pair_f16<1>(r.w4[b][s]), a);
                 a = dot2_f16(hv[2], nib_pair_f16<2>(r.w4[b][s]), a);
@@ -223,17 +277,6 @@ __device__ __forceinline__ float down_compute(const DTiles &r, const uint16_t *h
             const float s16 = 16.0f * bf16_to_f32(r.sbw[b] & 0xFFFFu);
             acc = fmaf(s16, a, fmaf(bf16_to_f32(r.sbw[b] >> 16) - s16, hsum, acc));
         }
-    return acc;
-}
-
-// Rest of a down part after the first batch (loaded by the caller) and the barrier.
-__device__ __forceinline__ float down_finish(DTiles &r, const uint16_t *hl, const uint8_t *W, const uint32_t *S,
-                                             int rb, int Gk, int g0, int g1) {
-    float acc = down_compute(r, hl, g0, g1, 0.0f);
-    for (int gb = g0 + kDecodeChunkGroups; gb < g1; gb += kDecodeChunkGroups) {
-        down_load(r, W, S, rb, Gk, gb, g1);
-        acc = down_compute(r, hl, gb, g1, acc);
-    }
     return acc + __shfl_xor(acc, 32);
 }
 
@@ -322,6 +365,7 @@ __device__ __forceinline__ int wave_topk(const float *__restrict__ l, int E, int
 struct DecArgs {
     const uint16_t *x;
     int T, d, E, k, I, Is;
+    int KSd, KSs;           // input pieces of the d-wide gate/up inputs and of the shared down input
     const uint8_t *rq;
     const uint32_t *rsb;
     const float *logit_bias;
@@ -329,20 +373,21 @@ struct DecArgs {
     int32_t *idx;
     float *wts;
     moe_qmat gate, up, down, sh_gate, sh_up, sh_down;
-    uint16_t *h_r, *h_s;
-    float *sh;
+    float *gus;             // [T][KSd][2][I_s] shared gate/up partials
+    uint16_t *h_r;          // [T*k][I]         routed hidden activations (fp16 bits)
+    float *shp;             // [T][KSs][d]      shared down partials
     float *y;
 };
 
-// grid: ceil(E / kDW) router workgroups + T * (I_s / 32) shared gate/up workgroups
-__global__ __launch_bounds__(64 * kDW) void k_dec_stage1(DecArgs a) {
+// grid: ceil(E / kRW) router workgroups + T * (I_s / 32) * KSd shared gate/up pieces; block 256
+__global__ __launch_bounds__(64 * kPW) void k_dec_stage1(DecArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int RW = cdiv(a.E, kDW);
+    const int RW = cdiv(a.E, kRW);
     const int G = a.d / 64;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     if ((int)blockIdx.x < RW) {
-        float *Ps = reinterpret_cast<float *>(smem);     // [kDW][T][G]
-        const int e = blockIdx.x * kDW + wave;
+        float *Ps = reinterpret_cast<float *>(smem);     // [kRW][T][G]
+        const int e = blockIdx.x * kRW + wave;
         float *P = Ps + (size_t)wave * a.T * G;
         if (e < a.E) router_wave(a.x, a.T, a.d, e, a.rq, a.rsb, P);
         __syncthreads();
@@ -356,29 +401,30 @@ __global__ __launch_bounds__(64 * kDW) void k_dec_stage1(DecArgs a) {
         return;
     }
     uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
-    float(*red)[2][32] = reinterpret_cast<float(*)[2][32]>(smem + sizeof(uint16_t) * a.d);
+    float(*red)[2][32] = reinterpret_cast<float(*)[2][32]>(smem + sizeof(uint16_t) * 64 * kGPS);
     const int JBs = a.Is / 32;
-    const int u = blockIdx.x - RW, t = u / JBs, jb = u % JBs;
-    const GUPtrs p = gu_ptrs(static_cast<const uint8_t *>(a.sh_gate.codes), static_cast<const uint8_t *>(a.sh_up.codes),
-                             a.sh_gate.sb, a.sh_up.sb, G, jb);
-    GUTiles r;
-    gu_load(r, p, G, 0);
-    gateup_unit(r, p, xs, G, jb, a.h_s + (size_t)t * a.Is, red, [&]() {
-        for (int i = tid; i < a.d / 8; i += 64 * kDW)
-            *reinterpret_cast<u32x4_t *>(xs + 8 * i) = ld16(a.x + (size_t)t * a.d + 8 * i);
-    });
+    int u = blockIdx.x - RW;
+    const int ks = u % a.KSd;
+    u /= a.KSd;
+    const int jb = u % JBs, t = u / JBs;
+    const int g0 = ks * kGPS, g1 = min(G, g0 + kGPS);
+    float *out = a.gus + ((size_t)t * a.KSd + ks) * 2 * a.Is + jb * 32;
+    gateup_piece<kPW, kPB>(a.x + (size_t)t * a.d, static_cast<const uint8_t *>(a.sh_gate.codes),
+                           static_cast<const uint8_t *>(a.sh_up.codes), a.sh_gate.sb, a.sh_up.sb, G, jb, g0, g1, xs,
+                           red, out, out + a.Is, nullptr);
 }
 
-// grid: T * k * (I / 32) routed gate/up workgroups + T * (d / 32) shared down workgroups
+// grid: T * k * (I / 32) routed gate/up units + T * (d / 32) * KSs shared down pieces;
+// block 64 * kW2
 template <int kPer>
-__global__ __launch_bounds__(64 * kDW) void k_dec_stage2(DecArgs a) {
+__global__ __launch_bounds__(64 * kW2) void k_dec_stage2(DecArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int G = a.d / 64, JB = a.I / 32;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nR = a.T * a.k * JB;
     if ((int)blockIdx.x < nR) {
-        const int pr = blockIdx.x / JB, jb = blockIdx.x % JB, t = pr / a.k, slot = pr % a.k;
-        // every wave derives the token's selection itself; the first unit of a pair records it
+        const int jb = blockIdx.x % JB, pr = blockIdx.x / JB, t = pr / a.k, slot = pr % a.k;
+        // every wave derives the token's selection itself; one unit of the pair records it
         const bool record = (jb == 0 && wave == 0);
         float wsel;
         const int e = wave_topk<kPer>(a.logits + (size_t)t * a.E, a.E, a.k, slot, record, wsel);
@@ -389,43 +435,63 @@ __global__ __launch_bounds__(64 * kDW) void k_dec_stage2(DecArgs a) {
         uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
         float(*red)[2][32] = reinterpret_cast<float(*)[2][32]>(smem + sizeof(uint16_t) * a.d);
         const size_t cstride = (size_t)a.I * a.d / 2, sstride = (size_t)a.I * G;
-        const GUPtrs p = gu_ptrs(static_cast<const uint8_t *>(a.gate.codes) + e * cstride,
-                                 static_cast<const uint8_t *>(a.up.codes) + e * cstride, a.gate.sb + e * sstride,
-                                 a.up.sb + e * sstride, G, jb);
-        GUTiles r;
-        gu_load(r, p, G, 0);
-        gateup_unit(r, p, xs, G, jb, a.h_r + (size_t)pr * a.I, red, [&]() {
-            for (int i = tid; i < a.d / 8; i += 64 * kDW)
-                *reinterpret_cast<u32x4_t *>(xs + 8 * i) = ld16(a.x + (size_t)t * a.d + 8 * i);
-        });
+        const uint8_t *Wg = static_cast<const uint8_t *>(a.gate.codes) + e * cstride;
+        const uint8_t *Wu = static_cast<const uint8_t *>(a.up.codes) + e * cstride;
+        uint16_t *hout = a.h_r + (size_t)pr * a.I + jb * 32;
+        if (G <= kW2 * kB2) {
+            gateup_piece<kW2, kB2>(a.x + (size_t)t * a.d, Wg, Wu, a.gate.sb + e * sstride, a.up.sb + e * sstride, G,
+                                   jb, 0, G, xs, red, nullptr, nullptr, hout);
+        } else {
+            // wide inputs: kW2 * kB2 groups at a time, partial sums carried through red
+            float *acc = reinterpret_cast<float *>(red);   // reuse: [2][32] totals after each batch
+            float tg = 0.0f, tu = 0.0f;
+            for (int g0 = 0; g0 < G; g0 += kW2 * kB2) {
+                gateup_piece<kW2, kB2>(a.x + (size_t)t * a.d, Wg, Wu, a.gate.sb + e * sstride,
+                                       a.up.sb + e * sstride, G, jb, g0, min(G, g0 + kW2 * kB2), xs, red,
+                                       acc + 2 * 64 * kW2, acc + 2 * 64 * kW2 + 32, nullptr);
+                __syncthreads();
+                if (tid < 32) {
+                    tg += acc[2 * 64 * kW2 + tid];
+                    tu += acc[2 * 64 * kW2 + 32 + tid];
+                }
+                __syncthreads();
+            }
+            if (tid < 32) hout[tid] = (uint16_t)f32_to_f16_sat(gelu_tanh_f32(tg) * tu);
+        }
         return;
     }
-    // shared down: (token, 32 output rows); the waves split the input groups
+    // shared down piece: (token, 32 output rows, input groups [g0, g1) of I_s)
     const int RB = a.d / 32, GIs = a.Is / 64;
-    const int u = blockIdx.x - nR, t = u / RB, rb = u % RB;
-    uint16_t *hl = reinterpret_cast<uint16_t *>(smem);
-    float *part = reinterpret_cast<float *>(smem + sizeof(uint16_t) * a.Is);
-    const int per = cdiv(GIs, kDW);
-    const int g0 = min(GIs, wave * per), g1 = min(GIs, g0 + per);
+    int u = blockIdx.x - nR;
+    const int ks = u % a.KSs;
+    u /= a.KSs;
+    const int rb = u % RB, t = u / RB;
+    const int g0 = ks * kGPS, g1 = min(GIs, g0 + kGPS);
+    uint16_t *hl = reinterpret_cast<uint16_t *>(smem);                              // [kGPS * 64]
+    float *part = reinterpret_cast<float *>(smem + sizeof(uint16_t) * 64 * kGPS);   // [kW2][32]
+    // wave w takes a contiguous sub-range of at most kSB groups
+    constexpr int kSB = cdiv_c(kGPS, kW2);
+    const int wg0 = min(g1, g0 + wave * kSB), wg1 = min(g1, wg0 + kSB);
     const uint8_t *W = static_cast<const uint8_t *>(a.sh_down.codes);
     DTiles r;
-    down_load(r, W, a.sh_down.sb, rb, GIs, g0, g1);
-    for (int i = tid; i < a.Is / 8; i += 64 * kDW)
-        *reinterpret_cast<u32x4_t *>(hl + 8 * i) = ld16(a.h_s + (size_t)t * a.Is + 8 * i);
+    down_load(r, W, a.sh_down.sb, rb, GIs, wg0, wg1);
+    form_h<cdiv_c(64 * kGPS, 64 * kW2)>(a.gus + (size_t)t * a.KSd * 2 * a.Is, a.KSd, a.Is, 64 * g0, 64 * (g1 - g0),
+                                        hl, tid, 64 * kW2);
     __syncthreads();
-    const float rsum = down_finish(r, hl, W, a.sh_down.sb, rb, GIs, g0, g1);
+    const float rsum = down_compute(r, hl + 64 * (wg0 - g0), wg0, wg1);
     if (lane < 32) part[wave * 32 + lane] = rsum;
     __syncthreads();
     if (tid < 32) {
         float sacc = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kDW; ++w) sacc += part[w * 32 + tid];
-        a.sh[(size_t)t * a.d + rb * 32 + tid] = sacc;
+        for (int w = 0; w < kW2; ++w) sacc += part[w * 32 + tid];
+        a.shp[((size_t)t * a.KSs + ks) * a.d + rb * 32 + tid] = sacc;
     }
 }
 
-// grid: T * (d / 32); block 64 * k: wave s = routed slot s
-__global__ __launch_bounds__(64 * MOE_MAX_TOP_K) void k_dec_stage3(DecArgs a) {
+// grid: T * (d / 32); block 64 * k (k <= MAXW): wave s = routed slot s
+template <int MAXW>
+__global__ __launch_bounds__(64 * MAXW) void k_dec_stage3(DecArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int RB = a.d / 32, GI = a.I / 64;
     const int t = blockIdx.x / RB, rb = blockIdx.x % RB;
@@ -436,17 +502,23 @@ __global__ __launch_bounds__(64 * MOE_MAX_TOP_K) void k_dec_stage3(DecArgs a) {
     const int e = a.idx[pr];
     const uint8_t *W = static_cast<const uint8_t *>(a.down.codes) + (size_t)e * a.d * a.I / 2;
     const uint32_t *S = a.down.sb + (size_t)e * a.d * GI;
-    DTiles r;
-    down_load(r, W, S, rb, GI, 0, GI);
-    for (int i = lane; i < a.I / 8; i += 64)
-        *reinterpret_cast<u32x4_t *>(hl + (size_t)wave * a.I + 8 * i) = ld16(a.h_r + (size_t)pr * a.I + 8 * i);
-    __syncthreads();
-    const float rsum = down_finish(r, hl + (size_t)wave * a.I, W, S, rb, GI, 0, GI);
+    float rsum = 0.0f;
+    for (int gb = 0; gb < GI; gb += kDecodeChunkGroups) {
+        const int gb1 = min(GI, gb + kDecodeChunkGroups);
+        DTiles r;
+        down_load(r, W, S, rb, GI, gb, gb1);
+        if (gb == 0)
+            for (int i = lane; i < a.I / 8; i += 64)
+                *reinterpret_cast<u32x4_t *>(hl + (size_t)wave * a.I + 8 * i) = ld16(a.h_r + (size_t)pr * a.I + 8 * i);
+        __syncthreads();
+        rsum += down_compute(r, hl + (size_t)wave * a.I + 64 * gb, gb, gb1);
+    }
     if (lane < 32) part[wave * 32 + lane] = rsum;
     __syncthreads();
     if (tid < 32) {
         const int row = rb * 32 + tid;
-        float out = a.sh[(size_t)t * a.d + row];
+        float out = 0.0f;
+        for (int ks = 0; ks < a.KSs; ++ks) out += a.shp[((size_t)t * a.KSs + ks) * a.d + row];
         for (int s = 0; s < a.k; ++s) out = fmaf(a.wts[(size_t)t * a.k + s], part[s * 32 + tid], out);
         a.y[(size_t)t * a.d + row] = out;
     }
@@ -462,6 +534,8 @@ DecArgs dec_args(const moe_layer *L, const uint16_t *x, int T, float *y) {
     a.k = D.top_k;
     a.I = D.d_expert;
     a.Is = D.d_shared;
+    a.KSd = cdiv(D.d_model / 64, kGPS);
+    a.KSs = cdiv(D.d_shared / 64, kGPS);
     a.rq = static_cast<const uint8_t *>(L->w.router.codes);
     a.rsb = L->w.router.sb;
     a.logit_bias = L->w.logit_bias;
@@ -474,9 +548,9 @@ DecArgs dec_args(const moe_layer *L, const uint16_t *x, int T, float *y) {
     a.sh_gate = L->w.sh_gate;
     a.sh_up = L->w.sh_up;
     a.sh_down = L->w.sh_down;
+    a.gus = L->ws.dgus;
     a.h_r = L->ws.dh_r;
-    a.h_s = L->ws.dh_s;
-    a.sh = L->ws.sh;
+    a.shp = L->ws.dshp;
     a.y = y;
     return a;
 }
@@ -487,14 +561,21 @@ size_t dec_stage3_lds(const moe_dims &D) {
     return sizeof(uint16_t) * D.top_k * D.d_expert + sizeof(float) * D.top_k * 32;
 }
 
+size_t dec_workspace_floats(const moe_dims &D, int max_dec, int which) {
+    const size_t KSd = cdiv(D.d_model / 64, kGPS), KSs = cdiv(D.d_shared / 64, kGPS);
+    if (which == 0) return (size_t)max_dec * KSd * 2 * D.d_shared;
+    if (which == 1) return (size_t)max_dec * D.top_k * D.d_expert / 2;   // fp16 h, in floats
+    return (size_t)max_dec * KSs * D.d_model;
+}
+
 hipError_t launch_dec_stage1(const moe_layer *L, const uint16_t *x, int T, hipStream_t s) {
     const moe_dims &D = L->dims;
+    const DecArgs a = dec_args(L, x, T, nullptr);
     const int G = D.d_model / 64;
-    const int grid = cdiv(D.n_experts, kDW) + T * (D.d_shared / 32);
-    const size_t lds_router = sizeof(float) * kDW * T * G;
-    const size_t lds_gu = sizeof(uint16_t) * D.d_model + sizeof(float) * kDW * 2 * 32;
-    hipLaunchKernelGGL(k_dec_stage1, dim3(grid), dim3(64 * kDW), lds_router > lds_gu ? lds_router : lds_gu, s,
-                       dec_args(L, x, T, nullptr));
+    const int grid = cdiv(D.n_experts, kRW) + T * (D.d_shared / 32) * a.KSd;
+    const size_t lds_router = sizeof(float) * kRW * T * G;
+    const size_t lds_gu = sizeof(uint16_t) * 64 * kGPS + sizeof(float) * kPW * 2 * 32;
+    hipLaunchKernelGGL(k_dec_stage1, dim3(grid), dim3(64 * kPW), lds_router > lds_gu ? lds_router : lds_gu, s, a);
     return hipGetLastError();
 }
 
@@ -503,28 +584,33 @@ hipError_t launch_dec_router(const moe_layer *L, const uint16_t *x, int T, float
     const moe_dims &D = L->dims;
     DecArgs a = dec_args(L, x, T, nullptr);
     a.logits = logits;
-    const size_t lds = sizeof(float) * kDW * T * (D.d_model / 64);
-    hipLaunchKernelGGL(k_dec_stage1, dim3(cdiv(D.n_experts, kDW)), dim3(64 * kDW), lds, s, a);
+    const size_t lds = sizeof(float) * kRW * T * (D.d_model / 64);
+    hipLaunchKernelGGL(k_dec_stage1, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kPW), lds, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_dec_stage2(const moe_layer *L, const uint16_t *x, int T, hipStream_t s) {
     const moe_dims &D = L->dims;
-    const int grid = T * D.top_k * (D.d_expert / 32) + T * (D.d_model / 32);
-    const size_t lds_gu = sizeof(uint16_t) * D.d_model + sizeof(float) * kDW * 2 * 32;
-    const size_t lds_sd = sizeof(uint16_t) * D.d_shared + sizeof(float) * kDW * 32;
-    const size_t lds = lds_gu > lds_sd ? lds_gu : lds_sd;
     const DecArgs a = dec_args(L, x, T, nullptr);
-    if (D.n_experts <= 128) hipLaunchKernelGGL(k_dec_stage2<2>, dim3(grid), dim3(64 * kDW), lds, s, a);
-    else if (D.n_experts <= 256) hipLaunchKernelGGL(k_dec_stage2<4>, dim3(grid), dim3(64 * kDW), lds, s, a);
-    else hipLaunchKernelGGL(k_dec_stage2<MOE_MAX_EXPERTS / 64>, dim3(grid), dim3(64 * kDW), lds, s, a);
+    const int grid = T * D.top_k * (D.d_expert / 32) + T * (D.d_model / 32) * a.KSs;
+    const size_t lds_gu = sizeof(uint16_t) * (D.d_model < 64 * kW2 * kB2 ? D.d_model : 64 * kW2 * kB2) +
+                          sizeof(float) * (kW2 * 2 * 32 + 2 * 64 * kW2 + 64);
+    const size_t lds_sd = sizeof(uint16_t) * 64 * kGPS + sizeof(float) * kW2 * 32;
+    const size_t lds = lds_gu > lds_sd ? lds_gu : lds_sd;
+    if (D.n_experts <= 128) hipLaunchKernelGGL(k_dec_stage2<2>, dim3(grid), dim3(64 * kW2), lds, s, a);
+    else if (D.n_experts <= 256) hipLaunchKernelGGL(k_dec_stage2<4>, dim3(grid), dim3(64 * kW2), lds, s, a);
+    else hipLaunchKernelGGL(k_dec_stage2<MOE_MAX_EXPERTS / 64>, dim3(grid), dim3(64 * kW2), lds, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_dec_stage3(const moe_layer *L, int T, float *y, hipStream_t s) {
     const moe_dims &D = L->dims;
-    hipLaunchKernelGGL(k_dec_stage3, dim3(T * (D.d_model / 32)), dim3(64 * D.top_k), dec_stage3_lds(D), s,
-                       dec_args(L, nullptr, T, y));
+    const DecArgs a = dec_args(L, nullptr, T, y);
+    if (D.top_k <= 8)
+        hipLaunchKernelGGL(k_dec_stage3<8>, dim3(T * (D.d_model / 32)), dim3(64 * D.top_k), dec_stage3_lds(D), s, a);
+    else
+        hipLaunchKernelGGL(k_dec_stage3<MOE_MAX_TOP_K>, dim3(T * (D.d_model / 32)), dim3(64 * D.top_k),
+                           dec_stage3_lds(D), s, a);
     return hipGetLastError();
 }
 

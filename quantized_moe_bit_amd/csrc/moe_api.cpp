@@ -211,7 +211,6 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     L->Gp_I = roundup(L->G_I, 16);
     L->Gp_Is = roundup(L->G_Is, 16);
     L->max_dec = D.max_tokens < MOE_MAX_DECODE_TOKENS ? D.max_tokens : MOE_MAX_DECODE_TOKENS;
-    const size_t Dm = (size_t)L->max_dec;
     const size_t nchunks = (size_t)cdiv((int)P, kChunk);
 
     Plan plan;
@@ -234,8 +233,9 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.hsplit_s, Tm * 3 * L->Gp_Is);
     plan.take(&ws.r, P * d);
     plan.take(&ws.sh, Tm * d);
-    plan.take(&ws.dh_r, Dm * k * I);
-    plan.take(&ws.dh_s, Dm * Is);
+    plan.take(&ws.dgus, dec_workspace_floats(D, L->max_dec, 0));
+    plan.take(&ws.dh_r, 2 * dec_workspace_floats(D, L->max_dec, 1));
+    plan.take(&ws.dshp, dec_workspace_floats(D, L->max_dec, 2));
     L->ws_bytes = (plan.off + 255) & ~size_t(255);
 
     int dev = 0;
@@ -270,8 +270,9 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     rebase(ws.hsplit_s, base);
     rebase(ws.r, base);
     rebase(ws.sh, base);
+    rebase(ws.dgus, base);
     rebase(ws.dh_r, base);
-    rebase(ws.dh_s, base);
+    rebase(ws.dshp, base);
     // zero once: padding columns of the split sums rely on it
     err = hipMemset(L->ws_base, 0, L->ws_bytes);
     if (err == hipSuccess) err = hipDeviceSynchronize();

@@ -23,6 +23,8 @@ constexpr int kChunk = 256;         // pairs per bucketing chunk
 constexpr int kDecodeChunkGroups = 12;  // K groups a decode wave loads before computing (down)
 
 __host__ __device__ inline int roundup(int a, int b) { return (a + b - 1) / b * b; }
+constexpr int cdiv_c(int a, int b) { return (a + b - 1) / b; }
+constexpr int kGPS = 12;            // input groups per decode piece
 __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // Kernel ids for per-kernel timing.
@@ -62,9 +64,10 @@ struct Workspace {
     uint16_t *hsplit_s;   // [maxT, 3*Gp_Is]
     float *r;             // [maxT*k, d]        routed expert outputs (bucket order)
     float *sh;            // [maxT, d]          shared expert outputs
-    // decode path
-    uint16_t *dh_r;       // [D*k, I]           fp16 bits
-    uint16_t *dh_s;       // [D, I_s]           fp16 bits
+    // decode path (D = decode capacity, KSd/KSs = input pieces of d / of I_s)
+    float *dgus;          // [D, KSd, 2, I_s]   shared gate/up partial sums
+    uint16_t *dh_r;       // [D*k, I]           routed hidden activations, fp16 bits
+    float *dshp;          // [D, KSs, d]        shared down partial sums
 };
 
 struct ProfEvent {
@@ -105,6 +108,7 @@ hipError_t launch_dec_stage1(const moe_layer *L, const uint16_t *x, int T, hipSt
 hipError_t launch_dec_stage2(const moe_layer *L, const uint16_t *x, int T, hipStream_t s);
 hipError_t launch_dec_stage3(const moe_layer *L, int T, float *y, hipStream_t s);
 size_t dec_stage3_lds(const moe_dims &D);
+size_t dec_workspace_floats(const moe_dims &D, int max_dec, int which);
 hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s);
 hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s);
 hipError_t launch_combine(const moe_layer *L, int T, float *y, hipStream_t s);

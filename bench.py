@@ -46,6 +46,7 @@ def main():
     ap.add_argument("--layers", type=int, default=16, help="distinct-address layer copies the decode steps rotate over")
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode workload (prefill-only runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -69,6 +70,8 @@ def main():
     K, W = args.steps, args.warmup
 
     # ------------------------------------------------------------------ decode workload
+    if args.no_decode:
+        args.layers, K = 1, 1
     wl = synth.WORKLOADS["decode"]
     D = wl.dims
     log("generating the 2816-wide layer")

@@ -81,9 +81,9 @@ __device__ __forceinline__ float gelu_tanh_f32(float v) {
     const float c = 0.7978845608028654f;
     float z = c * (v + 0.044715f * v * v * v);
     // tanh(z) = 1 - 2 / (exp(2z) + 1), saturating for large |z|
-    float e = __expf(2.0f * z);
-    float t = 1.0f - 2.0f / (e + 1.0f);
-    return 0.5f * v * (1.0f + t);
+    // 0.5 (1 + tanh z) = 1 - 1 / (exp(2z) + 1); saturates correctly as exp(2z) -> 0 or inf
+    const float e = __expf(2.0f * z);
+    return v * (1.0f - __builtin_amdgcn_rcpf(e + 1.0f));
 }
 
 __device__ __forceinline__ u32x4_t ld16(const void *p) { return *reinterpret_cast<const u32x4_t *>(p); }

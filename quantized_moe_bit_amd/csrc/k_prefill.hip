@@ -38,6 +38,7 @@ struct PreArgs {
     uint16_t *h_r, *hsplit_r, *h_s, *hsplit_s;
     int Gp_d, Gp_I, Gp_Is;
     float *r, *sh;
+    const uint8_t *bt_gate, *bt_up, *bt_down, *bt_sh_gate, *bt_sh_up, *bt_sh_down;   // bias-term B' tables
 };
 
 __device__ __forceinline__ int find_expert(const int32_t *tile_off, int E, int m) {
@@ -81,9 +82,9 @@ __device__ __forceinline__ uint32_t bias_part(uint32_t sbw, int part) {
 template <int MODE>  // 0: gate/up + GeGLU, 1: down
 __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
     __shared__ __align__(16) uint16_t As[2][kMT * kAPitch];
+    __shared__ __align__(16) uint16_t Bs[2][4 * 512];   // four 1 KiB weight tiles (codes) per group
     __shared__ int32_t srow[kMT];   // A source row (-1: padding)
     __shared__ int32_t drow[kMT];   // destination row
-    __shared__ float hsum[2][kMT];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1, n = lane & 31, half = lane >> 5;
@@ -148,49 +149,45 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
         }
         __syncthreads();
 
-        // this wave's two weight tiles (32 rows each)
-        const uint8_t *B0, *B1;
-        const uint32_t *S0, *S1;
+        // The workgroup's four weight tiles per input group (32 rows each): gate/up -> gate
+        // blocks 2nt, 2nt+1 then up blocks 2nt, 2nt+1; down -> blocks 4nt .. 4nt+3. Wave (wm, wn)
+        // uses tiles t0 = wn and t1 = 2 + wn (gate/up) or t0 = 2wn, t1 = 2wn + 1 (down).
+        const int t0 = MODE == 0 ? wn : 2 * wn, t1 = MODE == 0 ? 2 + wn : 2 * wn + 1;
+        const uint8_t *Bt;        // this thread's copy source: tile tid/64, 16 B at lane tid%64
+        const uint32_t *S0, *S1;  // scale/bias words of the wave's two tiles
         {
-            const moe_qmat *m0, *m1;
-            int rb0, rb1, rows;
-            if (MODE == 0) {
-                m0 = shared_item ? &a.sh_gate : &a.gate;
-                m1 = shared_item ? &a.sh_up : &a.up;
-                rb0 = rb1 = nt * 2 + wn;
-                rows = shared_item ? a.Is : a.I;
-            } else {
-                m0 = m1 = shared_item ? &a.sh_down : &a.down;
-                rb0 = nt * 4 + wn * 2;
-                rb1 = rb0 + 1;
-                rows = a.d;
-            }
+            const moe_qmat *mg = MODE == 0 ? (shared_item ? &a.sh_gate : &a.gate) : (shared_item ? &a.sh_down : &a.down);
+            const moe_qmat *mu = MODE == 0 ? (shared_item ? &a.sh_up : &a.up) : mg;
+            const int rows = MODE == 0 ? (shared_item ? a.Is : a.I) : a.d;
             const size_t cstride = (size_t)rows * K / 2, sstride = (size_t)rows * G;
-            B0 = static_cast<const uint8_t *>(m0->codes) + e * cstride + (size_t)rb0 * G * 1024 + lane * 16;
-            B1 = static_cast<const uint8_t *>(m1->codes) + e * cstride + (size_t)rb1 * G * 1024 + lane * 16;
-            S0 = m0->sb + e * sstride + (size_t)rb0 * G * 32 + n;
-            S1 = m1->sb + e * sstride + (size_t)rb1 * G * 32 + n;
+            auto rb_of = [&](int ti) { return MODE == 0 ? nt * 2 + (ti & 1) : nt * 4 + ti; };
+            auto mat_of = [&](int ti) { return (MODE == 0 && ti >= 2) ? mu : mg; };
+            const int ti = tid >> 6;
+            Bt = static_cast<const uint8_t *>(mat_of(ti)->codes) + e * cstride + (size_t)rb_of(ti) * G * 1024 +
+                 (tid & 63) * 16;
+            S0 = mat_of(t0)->sb + e * sstride + (size_t)rb_of(t0) * G * 32 + n;
+            S1 = mat_of(t1)->sb + e * sstride + (size_t)rb_of(t1) * G * 32 + n;
         }
 
-        // A staging: thread covers 4 pieces of 16 B (row q/8, column chunk q%8)
-        u32x4_t stage[4];
-        auto load_A = [&](int g) {
+        // 2-deep pipeline: register sets hold groups g+1 and g+2 while group g computes from LDS.
+        // A staging: thread covers 4 pieces of 16 B (row q/8, column chunk q%8), q = tid + 256 i.
+        u32x4_t ra0[4], ra1[4], rb0, rb1;
+        auto fetch = [&](int g, u32x4_t(&ra)[4], u32x4_t &rbv) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int q = tid + kPreWG * i;
-                const int row = q >> 3, c8 = q & 7;
-                const int src = srow[row];
-                if (src >= 0) stage[i] = ld16(Asrc + (size_t)src * K + 64 * g + 8 * c8);
-                else stage[i] = u32x4_t{0u, 0u, 0u, 0u};
+                const int src = srow[q >> 3];
+                ra[i] = src >= 0 ? ld16(Asrc + (size_t)src * K + 64 * g + 8 * (q & 7)) : u32x4_t{0u, 0u, 0u, 0u};
             }
+            rbv = ld16(Bt + (size_t)g * 1024);
         };
-        auto store_A = [&](int buf) {
+        auto put = [&](int buf, const u32x4_t(&ra)[4], const u32x4_t &rbv) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int q = tid + kPreWG * i;
-                const int row = q >> 3, c8 = q & 7;
-                *reinterpret_cast<u32x4_t *>(&As[buf][row * kAPitch + 8 * c8]) = stage[i];
+                *reinterpret_cast<u32x4_t *>(&As[buf][(q >> 3) * kAPitch + 8 * (q & 7)]) = ra[i];
             }
+            *reinterpret_cast<u32x4_t *>(&Bs[buf][tid * 8]) = rbv;
         };
 
         f32x16_t tot[2][2];
@@ -202,31 +199,22 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
                 for (int v = 0; v < 16; ++v) tot[i][j][v] = 0.0f;
         const f32x16_t zero = tot[0][0];
 
-        load_A(0);
-        u32x4_t bw0 = ld16(B0), bw1 = ld16(B1);
-        uint32_t sb0 = S0[0], sb1 = S1[0];
-        store_A(0);
-        __syncthreads();
-
-        for (int g = 0; g < G; ++g) {
-            const int buf = g & 1;
-            u32x4_t nb0 = bw0, nb1 = bw1;
-            uint32_t ns0 = sb0, ns1 = sb1;
-            if (g + 1 < G) {
-                load_A(g + 1);
-                nb0 = ld16(B0 + (size_t)(g + 1) * 1024);
-                nb1 = ld16(B1 + (size_t)(g + 1) * 1024);
-                ns0 = S0[(g + 1) * 32];
-                ns1 = S1[(g + 1) * 32];
-            }
+        // 32-row subtiles of this wave that hold at least one real row (wave-uniform)
+        const int live_rows = count - mt * kMT - wm * 64;
+        const bool live0 = live_rows > 0, live1 = live_rows > 32;
+        auto compute = [&](int buf, uint32_t sb0, uint32_t sb1) {
+            typedef typename OpT<MODE>::type op_t;
+            if (!live0) return;
+            const u32x4_t bw0 = *reinterpret_cast<const u32x4_t *>(&Bs[buf][(t0 * 64 + lane) * 8]);
+            const u32x4_t bw1 = *reinterpret_cast<const u32x4_t *>(&Bs[buf][(t1 * 64 + lane) * 8]);
             f32x16_t acc[2][2];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                typedef typename OpT<MODE>::type op_t;
                 const op_t b0 = OpT<MODE>::frag(bw0[s]);
                 const op_t b1 = OpT<MODE>::frag(bw1[s]);
 #pragma unroll
                 for (int ms = 0; ms < 2; ++ms) {
+                    if (ms == 1 && !live1) continue;
                     const int row = wm * 64 + ms * 32 + n;
                     const op_t av = __builtin_bit_cast(
                         op_t, *reinterpret_cast<const u32x4_t *>(&As[buf][row * kAPitch + 16 * s + 8 * half]));
@@ -237,60 +225,74 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
             const float s16_0 = 16.0f * bf16_to_f32(sb0 & 0xFFFFu);
             const float s16_1 = 16.0f * bf16_to_f32(sb1 & 0xFFFFu);
 #pragma unroll
-            for (int ms = 0; ms < 2; ++ms)
+            for (int ms = 0; ms < 2; ++ms) {
+                if (ms == 1 && !live1) continue;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     tot[ms][0][v] = fmaf(s16_0, acc[ms][0][v], tot[ms][0][v]);
                     tot[ms][1][v] = fmaf(s16_1, acc[ms][1][v], tot[ms][1][v]);
                 }
-            if (g + 1 < G) {
-                store_A(buf ^ 1);
-                bw0 = nb0;
-                bw1 = nb1;
-                sb0 = ns0;
-                sb1 = ns1;
+            }
+        };
+
+        fetch(0, ra0, rb0);
+        if (G > 1) fetch(1, ra1, rb1);
+        uint32_t sc0 = S0[0], sc1 = S1[0];
+        uint32_t sn0 = G > 1 ? S0[32] : 0u, sn1 = G > 1 ? S1[32] : 0u;
+        put(0, ra0, rb0);
+        __syncthreads();
+        for (int g = 0; g < G; g += 2) {
+            // even step: group g from buffer 0; ra0 refills with g+2; ra1 (g+1) goes to buffer 1
+            if (g + 2 < G) fetch(g + 2, ra0, rb0);
+            compute(0, sc0, sc1);
+            if (g + 1 < G) put(1, ra1, rb1);
+            sc0 = sn0;
+            sc1 = sn1;
+            if (g + 2 < G) {
+                sn0 = S0[(g + 2) * 32];
+                sn1 = S1[(g + 2) * 32];
+            }
+            __syncthreads();
+            if (g + 1 >= G) break;
+            // odd step: group g+1 from buffer 1; ra1 refills with g+3; ra0 (g+2) goes to buffer 0
+            if (g + 3 < G) fetch(g + 3, ra1, rb1);
+            compute(1, sc0, sc1);
+            if (g + 2 < G) put(0, ra0, rb0);
+            sc0 = sn0;
+            sc1 = sn1;
+            if (g + 3 < G) {
+                sn0 = S0[(g + 3) * 32];
+                sn1 = S1[(g + 3) * 32];
             }
             __syncthreads();
         }
 
-        // bias-term GEMM: K' = 3 Gp; A' = [X_hi | X_lo | X_hi], B' = [c_hi | c_hi | c_lo]
-        {
+        // bias-term GEMM: K' = 3 Gp; A' = [X_hi | X_lo | X_hi], B' = [c_hi | c_hi | c_lo] with
+        // c = bias - 16 scale. B' fragments come from the table built at layer creation.
+        if (live0) {
             const int steps = 3 * Gp / 16;
-            int srcs[2];
-#pragma unroll
-            for (int ms = 0; ms < 2; ++ms) srcs[ms] = srow[wm * 64 + ms * 32 + n];
+            const uint8_t *T0, *T1;
+            {
+                const uint8_t *tg = MODE == 0 ? (shared_item ? a.bt_sh_gate : a.bt_gate)
+                                              : (shared_item ? a.bt_sh_down : a.bt_down);
+                const uint8_t *tu = MODE == 0 ? (shared_item ? a.bt_sh_up : a.bt_up) : tg;
+                const int rows = MODE == 0 ? (shared_item ? a.Is : a.I) : a.d;
+                const size_t estride = (size_t)(rows / 32) * steps * 1024;
+                auto rb_of = [&](int ti) { return MODE == 0 ? nt * 2 + (ti & 1) : nt * 4 + ti; };
+                T0 = ((MODE == 0 && t0 >= 2) ? tu : tg) + e * estride + (size_t)rb_of(t0) * steps * 1024 + lane * 16;
+                T1 = ((MODE == 0 && t1 >= 2) ? tu : tg) + e * estride + (size_t)rb_of(t1) * steps * 1024 + lane * 16;
+            }
+            const int src0 = srow[wm * 64 + n], src1 = srow[wm * 64 + 32 + n];
             for (int st = 0; st < steps; ++st) {
                 const int kk0 = 16 * st + 8 * half;
-                uint32_t w0[4], w1[4];
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    uint32_t lo0 = 0, hi0 = 0, lo1 = 0, hi1 = 0;
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        const int kk = kk0 + 2 * jj + h2;
-                        const int part = kk / Gp, gg = kk % Gp;
-                        uint32_t v0 = 0, v1 = 0;
-                        if (gg < G) {
-                            v0 = bias_part(S0[gg * 32], part);
-                            v1 = bias_part(S1[gg * 32], part);
-                        }
-                        if (h2 == 0) {
-                            lo0 = v0;
-                            lo1 = v1;
-                        } else {
-                            hi0 = v0;
-                            hi1 = v1;
-                        }
-                    }
-                    w0[jj] = lo0 | (hi0 << 16);
-                    w1[jj] = lo1 | (hi1 << 16);
-                }
-                const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w0[2], w0[3]});
-                const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, u32x4_t{w1[0], w1[1], w1[2], w1[3]});
+                const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, ld16(T0 + (size_t)st * 1024));
+                const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, ld16(T1 + (size_t)st * 1024));
 #pragma unroll
                 for (int ms = 0; ms < 2; ++ms) {
+                    if (ms == 1 && !live1) continue;
                     u32x4_t av = u32x4_t{0u, 0u, 0u, 0u};
-                    if (srcs[ms] >= 0) av = ld16(Bsrc + (size_t)srcs[ms] * 3 * Gp + kk0);
+                    const int sr = ms == 0 ? src0 : src1;
+                    if (sr >= 0) av = ld16(Bsrc + (size_t)sr * 3 * Gp + kk0);
                     const bf16x8_t avb = __builtin_bit_cast(bf16x8_t, av);
                     tot[ms][0] = mfma32(avb, b0, tot[ms][0]);
                     tot[ms][1] = mfma32(avb, b1, tot[ms][1]);
@@ -300,41 +302,40 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
 
         // epilogue. Accumulator element v of lane l: row 8*(v/4) + 4*(l/32) + v%4, column l%32.
         if (MODE == 0) {
+            // h = fp16(gelu(g) * u) into an LDS tile [128 rows][64 columns] (reusing As[0]), then
+            // each row leaves as 16-byte stores and its 64-column sum feeds the down bias term
             const int J = shared_item ? a.Is : a.I;
             uint16_t *hout = shared_item ? a.h_s : a.h_r;
-            const int j = (nt * 2 + wn) * 32 + n;
-            float rsum[2][16];
+            uint16_t *Hs = As[0];
 #pragma unroll
             for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int row = wm * 64 + ms * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-                    const uint32_t hb = f32_to_f16_sat(gelu_tanh_f32(tot[ms][0][v]) * tot[ms][1][v]);
-                    const int dst = drow[row];
-                    if (dst >= 0) hout[(size_t)dst * J + j] = (uint16_t)hb;
-                    rsum[ms][v] = f16_to_f32(hb);
+                    Hs[row * kAPitch + wn * 32 + n] =
+                        (uint16_t)f32_to_f16_sat(gelu_tanh_f32(tot[ms][0][v]) * tot[ms][1][v]);
                 }
-            // sum over this wave's 32 columns (lanes of one half share rows)
-#pragma unroll
-            for (int off = 1; off < 32; off <<= 1)
-#pragma unroll
-                for (int ms = 0; ms < 2; ++ms)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) rsum[ms][v] += __shfl_xor(rsum[ms][v], off);
-            if (n == 0) {
-#pragma unroll
-                for (int ms = 0; ms < 2; ++ms)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        hsum[wn][wm * 64 + ms * 32 + 8 * (v >> 2) + 4 * half + (v & 3)] = rsum[ms][v];
-            }
             __syncthreads();
-            if (tid < kMT) {
-                const int dst = drow[tid];
-                if (dst >= 0) {
+            const int row = tid >> 1, hh = tid & 1;
+            const u32x4_t *src = reinterpret_cast<const u32x4_t *>(Hs + row * kAPitch + hh * 32);
+            u32x4_t hv[4];
+            float hsum_part = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                hv[i] = src[i];
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    hsum_part += f16_to_f32(hv[i][w] & 0xFFFFu) + f16_to_f32(hv[i][w] >> 16);
+            }
+            const float H = hsum_part + __shfl_xor(hsum_part, 1);
+            const int dst = drow[row];
+            if (dst >= 0) {
+                u32x4_t *o = reinterpret_cast<u32x4_t *>(hout + (size_t)dst * J + nt * 64 + hh * 32);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = hv[i];
+                if (hh == 0) {
                     const int Gpo = shared_item ? a.Gp_Is : a.Gp_I;
                     uint16_t *hs = (shared_item ? a.hsplit_s : a.hsplit_r) + (size_t)dst * 3 * Gpo;
-                    const float H = hsum[0][tid] + hsum[1][tid];
                     const uint32_t hi = f32_to_bf16(H);
                     const uint32_t lo = f32_to_bf16(H - bf16_to_f32(hi));
                     hs[nt] = (uint16_t)hi;
@@ -358,6 +359,39 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
                 }
         }
     }
+}
+
+// Bias-term B' fragments of one quantized matrix stack (n_mats x [rows, in]): for each
+// (matrix, 32-row block rb, 16-step st, lane l) eight bf16 values for K' indices
+// kk = 16 st + 8 (l / 32) + j, j = 0..7, of row rb*32 + l%32: with part = kk / Gp and
+// g = kk % Gp, c = bias - 16 scale of group g, value c_hi (part 0, 1) or c_lo (part 2),
+// 0 for padding groups g >= G. grid: ceil(n_mats * rows/32 * steps * 64 / 256); block 256
+__global__ __launch_bounds__(256) void k_bias_table(const uint32_t *__restrict__ sb, int n_mats, int rows, int G,
+                                                    int Gp, uint8_t *__restrict__ out) {
+    const int steps = 3 * Gp / 16;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t total = (size_t)n_mats * (rows / 32) * steps * 64;
+    if (i >= total) return;
+    const int lane = (int)(i % 64);
+    size_t r = i / 64;
+    const int st = (int)(r % steps);
+    r /= steps;
+    const int rb = (int)(r % (rows / 32));
+    const size_t m = r / (rows / 32);
+    const uint32_t *sbm = sb + m * (size_t)rows * G + (size_t)rb * G * 32 + (lane & 31);
+    uint32_t w[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        uint32_t v2[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int kk = 16 * st + 8 * (lane >> 5) + 2 * jj + h2;
+            const int part = kk / Gp, gg = kk % Gp;
+            v2[h2] = gg < G ? bias_part(sbm[gg * 32], part) : 0u;
+        }
+        w[jj] = v2[0] | (v2[1] << 16);
+    }
+    *reinterpret_cast<u32x4_t *>(out + i * 16) = u32x4_t{w[0], w[1], w[2], w[3]};
 }
 
 // y[t] = sh[t] + sum_s w[t,s] * r[pos[t*k+s]] in slot order. grid (cdiv(d,1024), T); block 256
@@ -434,6 +468,12 @@ PreArgs make_args(const moe_layer *L, const uint16_t *x, int T) {
     a.Gp_Is = L->Gp_Is;
     a.r = L->ws.r;
     a.sh = L->ws.sh;
+    a.bt_gate = L->ws.bt[0];
+    a.bt_up = L->ws.bt[1];
+    a.bt_down = L->ws.bt[2];
+    a.bt_sh_gate = L->ws.bt[3];
+    a.bt_sh_up = L->ws.bt[4];
+    a.bt_sh_down = L->ws.bt[5];
     return a;
 }
 
@@ -457,6 +497,19 @@ hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipSt
 
 hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s) {
     hipLaunchKernelGGL(k_pre_gemm<1>, dim3(persistent_grid()), dim3(kPreWG), 0, s, make_args(L, nullptr, T));
+    return hipGetLastError();
+}
+
+size_t bias_table_bytes(int n_mats, int rows, int in_dim) {
+    const int Gp = roundup(in_dim / 64, 16);
+    return (size_t)n_mats * (rows / 32) * (3 * Gp / 16) * 1024;
+}
+
+hipError_t launch_bias_table(const moe_qmat &m, int n_mats, int rows, int in_dim, uint8_t *out, hipStream_t s) {
+    const int G = in_dim / 64, Gp = roundup(G, 16);
+    const size_t total = (size_t)n_mats * (rows / 32) * (3 * Gp / 16) * 64;
+    hipLaunchKernelGGL(k_bias_table, dim3((unsigned)cdiv((int)total, 256)), dim3(256), 0, s, m.sb, n_mats, rows, G, Gp,
+                       out);
     return hipGetLastError();
 }
 

@@ -233,6 +233,12 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.hsplit_s, Tm * 3 * L->Gp_Is);
     plan.take(&ws.r, P * d);
     plan.take(&ws.sh, Tm * d);
+    plan.take(&ws.bt[0], bias_table_bytes(E, I, d));
+    plan.take(&ws.bt[1], bias_table_bytes(E, I, d));
+    plan.take(&ws.bt[2], bias_table_bytes(E, d, I));
+    plan.take(&ws.bt[3], bias_table_bytes(1, Is, d));
+    plan.take(&ws.bt[4], bias_table_bytes(1, Is, d));
+    plan.take(&ws.bt[5], bias_table_bytes(1, d, Is));
     plan.take(&ws.dgus, dec_workspace_floats(D, L->max_dec, 0));
     plan.take(&ws.dh_r, 2 * dec_workspace_floats(D, L->max_dec, 1));
     plan.take(&ws.dshp, dec_workspace_floats(D, L->max_dec, 2));
@@ -270,11 +276,19 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     rebase(ws.hsplit_s, base);
     rebase(ws.r, base);
     rebase(ws.sh, base);
+    for (int i = 0; i < 6; ++i) rebase(ws.bt[i], base);
     rebase(ws.dgus, base);
     rebase(ws.dh_r, base);
     rebase(ws.dshp, base);
     // zero once: padding columns of the split sums rely on it
     err = hipMemset(L->ws_base, 0, L->ws_bytes);
+    // derived bias-term tables of the prefill GEMMs (read from the borrowed scale/bias words)
+    if (err == hipSuccess) err = launch_bias_table(w->gate, E, I, d, ws.bt[0], nullptr);
+    if (err == hipSuccess) err = launch_bias_table(w->up, E, I, d, ws.bt[1], nullptr);
+    if (err == hipSuccess) err = launch_bias_table(w->down, E, d, I, ws.bt[2], nullptr);
+    if (err == hipSuccess) err = launch_bias_table(w->sh_gate, 1, Is, d, ws.bt[3], nullptr);
+    if (err == hipSuccess) err = launch_bias_table(w->sh_up, 1, Is, d, ws.bt[4], nullptr);
+    if (err == hipSuccess) err = launch_bias_table(w->sh_down, 1, d, Is, ws.bt[5], nullptr);
     if (err == hipSuccess) err = hipDeviceSynchronize();
     if (err != hipSuccess) {
         (void)hipFree(L->ws_base);

@@ -64,6 +64,7 @@ struct Workspace {
     uint16_t *hsplit_s;   // [maxT, 3*Gp_Is]
     float *r;             // [maxT*k, d]        routed expert outputs (bucket order)
     float *sh;            // [maxT, d]          shared expert outputs
+    uint8_t *bt[6];       // bias-term B' fragment tables of gate, up, down, sh_gate, sh_up, sh_down
     // decode path (D = decode capacity, KSd/KSs = input pieces of d / of I_s)
     float *dgus;          // [D, KSd, 2, I_s]   shared gate/up partial sums
     uint16_t *dh_r;       // [D*k, I]           routed hidden activations, fp16 bits
@@ -112,6 +113,8 @@ size_t dec_workspace_floats(const moe_dims &D, int max_dec, int which);
 hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s);
 hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s);
 hipError_t launch_combine(const moe_layer *L, int T, float *y, hipStream_t s);
+size_t bias_table_bytes(int n_mats, int rows, int in_dim);
+hipError_t launch_bias_table(const moe_qmat &m, int n_mats, int rows, int in_dim, uint8_t *out, hipStream_t s);
 hipError_t launch_glue(const uint16_t *h, const float *y, uint16_t *h_next, uint16_t *x_next, int T, int d,
                        hipStream_t s);
 

@@ -20,23 +20,91 @@
 // Work items: (expert or shared, 128-row tile, output tile). A persistent grid walks them
 // with a static schedule: items are cut into 8 contiguous ranges, one per XCD (workgroup
 // i runs on XCD i % 8), so all tiles of one expert share an L2.
+#include <type_traits>
+
 #include "device_common.h"
 #include "moe_internal.h"
 
 namespace qmoe {
 namespace {
 
-constexpr int kAPitch = 72;   // bf16 per staged A row in LDS (64 + 8 pad: conflict-free 16 B reads)
 constexpr int kPreWG = 256;
+
+// LDS ring of the K loop: three stages, each an A tile (128 rows x 64 inputs, 16-bit, rows
+// of 128 B with the 16-byte chunks XOR-swizzled), the four 1 KiB code tiles of the step and
+// their scale/bias words (64 per wave, rows duplicated). Everything arrives by direct
+// global->LDS loads, so no staging registers are needed.
+constexpr int kStages = 3;
+constexpr int kAStageBytes = kMT * 128;
+constexpr int kBStageBytes = 4 * 1024;
+constexpr int kSStageBytes = 4 * 256;
+constexpr int kStageBytes = kAStageBytes + kBStageBytes + kSStageBytes;
+constexpr int kSmemBytes = kStages * kStageBytes;
+constexpr int kDmaPerStep = 6;   // per thread: 4 A chunks, 1 code chunk, 1 scale/bias word
+// gate/up epilogue tiles (reusing the ring): u in fp32, then h in fp16
+constexpr int kUPitch = 72;
+constexpr int kHPitch = 72;
+static_assert(kMT * kUPitch * 4 + kMT * kHPitch * 2 <= kSmemBytes, "epilogue tiles exceed the LDS ring");
+
+// Physical 16-byte chunk of logical chunk c in A-tile row r is c ^ swz(r). 16 consecutive
+// rows read at one logical chunk then hit 16 distinct 16-byte bank groups (and any 8
+// consecutive rows 8 distinct ones), and swz depends on r mod 32 only, so the four 32-row
+// subtiles of a lane share their offsets up to a constant.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 3); }
+
+// Direct global->LDS load: every lane of the wave moves 16 (or 4) bytes from
+// sbase + voff (sbase wave-uniform, voff a per-lane 32-bit byte offset) to lds_base +
+// 16 lane (4 lane); lds_base is wave-uniform. Issued as inline asm so that the compiler's
+// wait insertion (which would wait for every outstanding direct load before any LDS read)
+// stays out of the ring; the ring waits for them itself (ring_sync). M0 carries the LDS base
+// and is restored afterwards.
+__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, const uint8_t *lds_base) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "v"(voff), "s"(sbase), "s"(m)
+        : "memory");
+}
+__device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, const uint8_t *lds_base) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "global_load_lds_dword %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "v"(voff), "s"(sbase), "s"(m)
+        : "memory");
+}
+
+// Ring barrier. Direct loads retire in issue order and are counted by vmcnt; every load of
+// the ring goes through dma16/dma4 (six per thread per step), so "at most 6 outstanding"
+// means every step but the last issued one has landed. The other vector loads of the
+// workgroup are issued before the ring starts, so they only make the wait stricter.
+// lgkmcnt(0): this wave's LDS reads of the stage about to be refilled are complete.
+__device__ __forceinline__ void ring_sync(bool keep_one_step) {
+    if (keep_one_step) asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+static_assert(kDmaPerStep == 6, "ring_sync encodes vmcnt(6)");
 
 struct PreArgs {
     int T, d, k, I, Is, E;
     const uint16_t *x;          // gate/up A rows [T, d]
     const int32_t *perm, *offsets, *tile_off;
-    const uint16_t *xsplit;     // [T, 3 Gp_d]
+    const uint16_t *xsplit;     // [T, Ks_d]
     moe_qmat gate, up, sh_gate, sh_up, down, sh_down;
     uint16_t *h_r, *hsplit_r, *h_s, *hsplit_s;
     int Gp_d, Gp_I, Gp_Is;
+    int Ks_d, Ks_I, Ks_Is;      // row strides of the split-sum buffers
     float *r, *sh;
     const uint8_t *bt_gate, *bt_up, *bt_down, *bt_sh_gate, *bt_sh_up, *bt_sh_down;   // bias-term B' tables
 };
@@ -81,14 +149,21 @@ __device__ __forceinline__ uint32_t bias_part(uint32_t sbw, int part) {
 
 template <int MODE>  // 0: gate/up + GeGLU, 1: down
 __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
-    __shared__ __align__(16) uint16_t As[2][kMT * kAPitch];
-    __shared__ __align__(16) uint16_t Bs[2][4 * 512];   // four 1 KiB weight tiles (codes) per group
+    __shared__ __align__(16) uint8_t smem[kSmemBytes];
     __shared__ int32_t srow[kMT];   // A source row (-1: padding)
     __shared__ int32_t drow[kMT];   // destination row
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1, n = lane & 31, half = lane >> 5;
+    typedef typename OpT<MODE>::type op_t;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, half = lane >> 5;
     const int E = a.E;
+
+    // A-fragment byte offsets within a stage: row 32 ms + n, logical chunk 2 s + half sits
+    // at aoff[s] + 4096 ms.
+    int aoff[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) aoff[s] = n * 128 + 16 * ((2 * s + half) ^ swz(n));
 
     // item space
     const int Ms = cdiv(a.T, kMT);
@@ -121,17 +196,15 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
         const int K = MODE == 0 ? a.d : (shared_item ? a.Is : a.I);
         const int G = K / 64;
         const int Gp = MODE == 0 ? a.Gp_d : (shared_item ? a.Gp_Is : a.Gp_I);
-        const uint16_t *Asrc;
-        const uint16_t *Bsrc;   // split sums for the bias-term GEMM
-        if (MODE == 0) {
-            Asrc = a.x;
-            Bsrc = a.xsplit;
-        } else {
-            Asrc = shared_item ? a.h_s : a.h_r;
-            Bsrc = shared_item ? a.hsplit_s : a.hsplit_r;
-        }
+        const int Ks = MODE == 0 ? a.Ks_d : (shared_item ? a.Ks_Is : a.Ks_I);
+        const int nbs = 3 * Gp / 16;        // bias-term MFMA steps
+        const int nbp = roundup(nbs, 12);   // ... padded with zero fragments in the table
+        const int V = cdiv(nbs, 4);         // bias-term ring steps (64 K' columns each)
+        const int S = V + G;                // ring steps of the item
+        const uint16_t *Asrc = MODE == 0 ? a.x : (shared_item ? a.h_s : a.h_r);
+        const uint16_t *Bsrc = MODE == 0 ? a.xsplit : (shared_item ? a.hsplit_s : a.hsplit_r);
 
-        __syncthreads();   // previous item is done with the LDS tables
+        __syncthreads();   // previous item is done with the LDS ring and row tables
         if (tid < kMT) {
             const int r = mt * kMT + tid;
             int src = -1, dst = -1;
@@ -149,175 +222,193 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
         }
         __syncthreads();
 
-        // The workgroup's four weight tiles per input group (32 rows each): gate/up -> gate
-        // blocks 2nt, 2nt+1 then up blocks 2nt, 2nt+1; down -> blocks 4nt .. 4nt+3. Wave (wm, wn)
-        // uses tiles t0 = wn and t1 = 2 + wn (gate/up) or t0 = 2wn, t1 = 2wn + 1 (down).
-        const int t0 = MODE == 0 ? wn : 2 * wn, t1 = MODE == 0 ? 2 + wn : 2 * wn + 1;
-        const uint8_t *Bt;        // this thread's copy source: tile tid/64, 16 B at lane tid%64
-        const uint32_t *S0, *S1;  // scale/bias words of the wave's two tiles
+        // Wave w owns one 32-row weight tile for all 128 token rows: gate/up -> gate blocks
+        // 2nt, 2nt+1 (waves 0, 1) and up blocks 2nt, 2nt+1 (waves 2, 3); down -> block 4nt + w.
+        const uint8_t *Bt;        // code tile of step 0 (wave-uniform); lane adds 16 lane
+        const uint8_t *St;        // scale/bias words of step 0 (wave-uniform); lane adds 4 n
+        const uint8_t *Tb;        // bias-term B' fragments, step 0, this lane
         {
-            const moe_qmat *mg = MODE == 0 ? (shared_item ? &a.sh_gate : &a.gate) : (shared_item ? &a.sh_down : &a.down);
-            const moe_qmat *mu = MODE == 0 ? (shared_item ? &a.sh_up : &a.up) : mg;
+            const moe_qmat *m = MODE == 0 ? (wave < 2 ? (shared_item ? &a.sh_gate : &a.gate)
+                                                      : (shared_item ? &a.sh_up : &a.up))
+                                          : (shared_item ? &a.sh_down : &a.down);
+            const uint8_t *tb = MODE == 0 ? (wave < 2 ? (shared_item ? a.bt_sh_gate : a.bt_gate)
+                                                      : (shared_item ? a.bt_sh_up : a.bt_up))
+                                          : (shared_item ? a.bt_sh_down : a.bt_down);
             const int rows = MODE == 0 ? (shared_item ? a.Is : a.I) : a.d;
-            const size_t cstride = (size_t)rows * K / 2, sstride = (size_t)rows * G;
-            auto rb_of = [&](int ti) { return MODE == 0 ? nt * 2 + (ti & 1) : nt * 4 + ti; };
-            auto mat_of = [&](int ti) { return (MODE == 0 && ti >= 2) ? mu : mg; };
-            const int ti = tid >> 6;
-            Bt = static_cast<const uint8_t *>(mat_of(ti)->codes) + e * cstride + (size_t)rb_of(ti) * G * 1024 +
-                 (tid & 63) * 16;
-            S0 = mat_of(t0)->sb + e * sstride + (size_t)rb_of(t0) * G * 32 + n;
-            S1 = mat_of(t1)->sb + e * sstride + (size_t)rb_of(t1) * G * 32 + n;
+            const int rb = MODE == 0 ? 2 * nt + (wave & 1) : 4 * nt + wave;
+            Bt = static_cast<const uint8_t *>(m->codes) + (size_t)e * rows * K / 2 + (size_t)rb * G * 1024;
+            St = reinterpret_cast<const uint8_t *>(m->sb + (size_t)e * rows * G + (size_t)rb * G * 32);
+            Tb = tb + (((size_t)e * (rows / 32) + rb) * 64 + lane) * nbp * 16;
+        }
+        const uint32_t boff = lane * 16, soff = n * 4;
+        // A rows this thread moves: chunk i covers rows 8 (4 i + wave) .. +7, lane -> row
+        // + lane/8 at physical chunk lane%8 (byte offsets from the buffer start). Padding rows
+        // read the tile's first row (finite values; their results are discarded).
+        uint32_t aro[4], apo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 8 * (4 * i + wave) + (lane >> 3);
+            const int c = (lane & 7) ^ swz(r);
+            int src = srow[r];
+            if (src < 0) src = srow[0];
+            aro[i] = ((uint32_t)src * K + 8 * c) * 2;
+            apo[i] = ((uint32_t)src * Ks + 8 * c) * 2;
         }
 
-        // 2-deep pipeline: register sets hold groups g+1 and g+2 while group g computes from LDS.
-        // A staging: thread covers 4 pieces of 16 B (row q/8, column chunk q%8), q = tid + 256 i.
-        u32x4_t ra0[4], ra1[4], rb0, rb1;
-        auto fetch = [&](int g, u32x4_t(&ra)[4], u32x4_t &rbv) {
+        // stage of ring step t: real step g = t - V uses stage g % 3
+        auto stage_of = [&](int t) { return (t - V + 3 * V) % 3; };
+        auto issue = [&](int t) {
+            uint8_t *sA = smem + stage_of(t) * kStageBytes;
+            uint8_t *sB = sA + kAStageBytes;
+            uint8_t *sS = sB + kBStageBytes;
+            int g = 0;   // bias steps move step-0 codes too (unused)
+            if (t < V) {
+                const uint8_t *abase = reinterpret_cast<const uint8_t *>(Bsrc) + 128 * t;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int q = tid + kPreWG * i;
-                const int src = srow[q >> 3];
-                ra[i] = src >= 0 ? ld16(Asrc + (size_t)src * K + 64 * g + 8 * (q & 7)) : u32x4_t{0u, 0u, 0u, 0u};
-            }
-            rbv = ld16(Bt + (size_t)g * 1024);
-        };
-        auto put = [&](int buf, const u32x4_t(&ra)[4], const u32x4_t &rbv) {
+                for (int i = 0; i < 4; ++i) dma16(abase, apo[i], sA + (4 * i + wave) * 1024);
+            } else {
+                g = t - V;
+                const uint8_t *abase = reinterpret_cast<const uint8_t *>(Asrc) + 128 * g;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int q = tid + kPreWG * i;
-                *reinterpret_cast<u32x4_t *>(&As[buf][(q >> 3) * kAPitch + 8 * (q & 7)]) = ra[i];
+                for (int i = 0; i < 4; ++i) dma16(abase, aro[i], sA + (4 * i + wave) * 1024);
             }
-            *reinterpret_cast<u32x4_t *>(&Bs[buf][tid * 8]) = rbv;
+            dma16(Bt + (size_t)g * 1024, boff, sB + wave * 1024);
+            dma4(St + g * 128, soff, sS + wave * 256);
         };
 
-        f32x16_t tot[2][2];
+        f32x16_t tot[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) tot[i][j][v] = 0.0f;
-        const f32x16_t zero = tot[0][0];
+            for (int v = 0; v < 16; ++v) tot[ms][v] = 0.0f;
+        const f32x16_t zero = tot[0];
+        // 32-row subtiles holding at least one real row (uniform)
+        const int live = count - mt * kMT;
+        const int live_ms = live >= kMT ? 4 : (live + 31) >> 5;
 
-        // 32-row subtiles of this wave that hold at least one real row (wave-uniform)
-        const int live_rows = count - mt * kMT - wm * 64;
-        const bool live0 = live_rows > 0, live1 = live_rows > 32;
-        auto compute = [&](int buf, uint32_t sb0, uint32_t sb1) {
-            typedef typename OpT<MODE>::type op_t;
-            if (!live0) return;
-            const u32x4_t bw0 = *reinterpret_cast<const u32x4_t *>(&Bs[buf][(t0 * 64 + lane) * 8]);
-            const u32x4_t bw1 = *reinterpret_cast<const u32x4_t *>(&Bs[buf][(t1 * 64 + lane) * 8]);
-            f32x16_t acc[2][2];
+        // The K loop, instantiated per number of live 32-row subtiles (1..4) so that padding
+        // subtiles cost nothing and the MFMA sequence stays branch-free.
+        auto kloop = [&](auto lms_c) {
+            constexpr int LMS = decltype(lms_c)::value;
+            // ---- bias term first: K' = 3 Gp, A' = [X_hi | X_lo | X_hi] rows of the split-sum
+            // buffer, B' = [c_hi | c_hi | c_lo] (c = bias - 16 scale) from the table built at
+            // layer creation; three ring steps (12 MFMA steps) of B' in registers at a time.
+            for (int vc = 0; vc < V; vc += 3) {
+                u32x4_t bp[12];
+                const uint8_t *tb = Tb + (size_t)vc * 64;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const op_t b0 = OpT<MODE>::frag(bw0[s]);
-                const op_t b1 = OpT<MODE>::frag(bw1[s]);
+                for (int j = 0; j < 12; ++j) bp[j] = ld16(tb + 16 * j);
+                if (vc == 0) {
+                    issue(0);
+                    if (S > 1) issue(1);
+                }
 #pragma unroll
-                for (int ms = 0; ms < 2; ++ms) {
-                    if (ms == 1 && !live1) continue;
-                    const int row = wm * 64 + ms * 32 + n;
-                    const op_t av = __builtin_bit_cast(
-                        op_t, *reinterpret_cast<const u32x4_t *>(&As[buf][row * kAPitch + 16 * s + 8 * half]));
-                    acc[ms][0] = mfma32(av, b0, s == 0 ? zero : acc[ms][0]);
-                    acc[ms][1] = mfma32(av, b1, s == 0 ? zero : acc[ms][1]);
+                for (int vv = 0; vv < 3; ++vv) {
+                    const int t = vc + vv;
+                    if (t < V) {
+                        ring_sync(t + 1 < S);
+                        if (t + 2 < S) issue(t + 2);
+                        const uint8_t *sA = smem + stage_of(t) * kStageBytes;
+                        const int nst = min(4, nbs - 4 * t);
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) {
+                            if (s < nst) {
+                                const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bp[4 * vv + s]);
+#pragma unroll
+                                for (int ms = 0; ms < LMS; ++ms) {
+                                    const bf16x8_t av =
+                                        __builtin_bit_cast(bf16x8_t, ld16(sA + aoff[s] + 4096 * ms));
+                                    tot[ms] = mfma32(av, b, tot[ms]);
+                                }
+                            }
+                        }
+                    }
                 }
             }
-            const float s16_0 = 16.0f * bf16_to_f32(sb0 & 0xFFFFu);
-            const float s16_1 = 16.0f * bf16_to_f32(sb1 & 0xFFFFu);
+            // ---- main loop: one 64-input group per ring step
+            auto real_step = [&](int g, const uint8_t *sA) {
+                const int t = V + g;
+                ring_sync(t + 1 < S);
+                if (t + 2 < S) issue(t + 2);
+                const uint8_t *sB = sA + kAStageBytes;
+                const uint8_t *sS = sB + kBStageBytes;
+                const u32x4_t bw = ld16(sB + wave * 1024 + lane * 16);
+                const uint32_t sbw = *reinterpret_cast<const uint32_t *>(sS + wave * 256 + lane * 4);
+                f32x16_t acc[LMS];
+                // A fragments of step s + 1 are read while step s multiplies
+                u32x4_t af[2][LMS];
 #pragma unroll
-            for (int ms = 0; ms < 2; ++ms) {
-                if (ms == 1 && !live1) continue;
+                for (int ms = 0; ms < LMS; ++ms) af[0][ms] = ld16(sA + aoff[0] + 4096 * ms);
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    tot[ms][0][v] = fmaf(s16_0, acc[ms][0][v], tot[ms][0][v]);
-                    tot[ms][1][v] = fmaf(s16_1, acc[ms][1][v], tot[ms][1][v]);
+                for (int s = 0; s < 4; ++s) {
+                    if (s < 3) {
+#pragma unroll
+                        for (int ms = 0; ms < LMS; ++ms) af[(s + 1) & 1][ms] = ld16(sA + aoff[s + 1] + 4096 * ms);
+                    }
+                    const op_t b = OpT<MODE>::frag(bw[s]);
+#pragma unroll
+                    for (int ms = 0; ms < LMS; ++ms)
+                        acc[ms] = mfma32(__builtin_bit_cast(op_t, af[s & 1][ms]), b, s == 0 ? zero : acc[ms]);
                 }
+                const float s16 = 16.0f * bf16_to_f32(sbw & 0xFFFFu);
+#pragma unroll
+                for (int ms = 0; ms < LMS; ++ms)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) tot[ms][v] = fmaf(s16, acc[ms][v], tot[ms][v]);
+            };
+            if (V == 0) {   // no bias steps (only when Gp == 0, i.e. never for valid shapes)
+                issue(0);
+                if (S > 1) issue(1);
+            }
+            for (int g = 0; g < G; g += 3) {
+                real_step(g, smem);
+                if (g + 1 >= G) break;
+                real_step(g + 1, smem + kStageBytes);
+                if (g + 2 >= G) break;
+                real_step(g + 2, smem + 2 * kStageBytes);
             }
         };
-
-        fetch(0, ra0, rb0);
-        if (G > 1) fetch(1, ra1, rb1);
-        uint32_t sc0 = S0[0], sc1 = S1[0];
-        uint32_t sn0 = G > 1 ? S0[32] : 0u, sn1 = G > 1 ? S1[32] : 0u;
-        put(0, ra0, rb0);
-        __syncthreads();
-        for (int g = 0; g < G; g += 2) {
-            // even step: group g from buffer 0; ra0 refills with g+2; ra1 (g+1) goes to buffer 1
-            if (g + 2 < G) fetch(g + 2, ra0, rb0);
-            compute(0, sc0, sc1);
-            if (g + 1 < G) put(1, ra1, rb1);
-            sc0 = sn0;
-            sc1 = sn1;
-            if (g + 2 < G) {
-                sn0 = S0[(g + 2) * 32];
-                sn1 = S1[(g + 2) * 32];
-            }
-            __syncthreads();
-            if (g + 1 >= G) break;
-            // odd step: group g+1 from buffer 1; ra1 refills with g+3; ra0 (g+2) goes to buffer 0
-            if (g + 3 < G) fetch(g + 3, ra1, rb1);
-            compute(1, sc0, sc1);
-            if (g + 2 < G) put(0, ra0, rb0);
-            sc0 = sn0;
-            sc1 = sn1;
-            if (g + 3 < G) {
-                sn0 = S0[(g + 3) * 32];
-                sn1 = S1[(g + 3) * 32];
-            }
-            __syncthreads();
+        switch (live_ms) {
+            case 1: kloop(std::integral_constant<int, 1>{}); break;
+            case 2: kloop(std::integral_constant<int, 2>{}); break;
+            case 3: kloop(std::integral_constant<int, 3>{}); break;
+            default: kloop(std::integral_constant<int, 4>{}); break;
         }
+        __syncthreads();   // every wave is done with the ring (no loads are outstanding)
 
-        // bias-term GEMM: K' = 3 Gp; A' = [X_hi | X_lo | X_hi], B' = [c_hi | c_hi | c_lo] with
-        // c = bias - 16 scale. B' fragments come from the table built at layer creation.
-        if (live0) {
-            const int steps = 3 * Gp / 16;
-            const uint8_t *T0, *T1;
-            {
-                const uint8_t *tg = MODE == 0 ? (shared_item ? a.bt_sh_gate : a.bt_gate)
-                                              : (shared_item ? a.bt_sh_down : a.bt_down);
-                const uint8_t *tu = MODE == 0 ? (shared_item ? a.bt_sh_up : a.bt_up) : tg;
-                const int rows = MODE == 0 ? (shared_item ? a.Is : a.I) : a.d;
-                const size_t estride = (size_t)(rows / 32) * steps * 1024;
-                auto rb_of = [&](int ti) { return MODE == 0 ? nt * 2 + (ti & 1) : nt * 4 + ti; };
-                T0 = ((MODE == 0 && t0 >= 2) ? tu : tg) + e * estride + (size_t)rb_of(t0) * steps * 1024 + lane * 16;
-                T1 = ((MODE == 0 && t1 >= 2) ? tu : tg) + e * estride + (size_t)rb_of(t1) * steps * 1024 + lane * 16;
-            }
-            const int src0 = srow[wm * 64 + n], src1 = srow[wm * 64 + 32 + n];
-            for (int st = 0; st < steps; ++st) {
-                const int kk0 = 16 * st + 8 * half;
-                const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, ld16(T0 + (size_t)st * 1024));
-                const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, ld16(T1 + (size_t)st * 1024));
-#pragma unroll
-                for (int ms = 0; ms < 2; ++ms) {
-                    if (ms == 1 && !live1) continue;
-                    u32x4_t av = u32x4_t{0u, 0u, 0u, 0u};
-                    const int sr = ms == 0 ? src0 : src1;
-                    if (sr >= 0) av = ld16(Bsrc + (size_t)sr * 3 * Gp + kk0);
-                    const bf16x8_t avb = __builtin_bit_cast(bf16x8_t, av);
-                    tot[ms][0] = mfma32(avb, b0, tot[ms][0]);
-                    tot[ms][1] = mfma32(avb, b1, tot[ms][1]);
-                }
-            }
-        }
-
-        // epilogue. Accumulator element v of lane l: row 8*(v/4) + 4*(l/32) + v%4, column l%32.
+        // ---- epilogue. Accumulator element v of lane l in subtile ms: row 32 ms + 8 (v/4) +
+        // 4 (l/32) + v%4, column l%32 of the wave's weight tile.
         if (MODE == 0) {
-            // h = fp16(gelu(g) * u) into an LDS tile [128 rows][64 columns] (reusing As[0]), then
-            // each row leaves as 16-byte stores and its 64-column sum feeds the down bias term
+            // h = fp16(gelu(g) * u): the up waves hand u over through LDS, the gate waves form
+            // h into an fp16 tile, then each row leaves as 16-byte stores and its 64-column
+            // sum feeds the down projection's bias term
             const int J = shared_item ? a.Is : a.I;
             uint16_t *hout = shared_item ? a.h_s : a.h_r;
-            uint16_t *Hs = As[0];
+            float *U = reinterpret_cast<float *>(smem);
+            uint16_t *Hs = reinterpret_cast<uint16_t *>(smem + kMT * kUPitch * 4);
+            if (wave >= 2) {
 #pragma unroll
-            for (int ms = 0; ms < 2; ++ms)
+                for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = wm * 64 + ms * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-                    Hs[row * kAPitch + wn * 32 + n] =
-                        (uint16_t)f32_to_f16_sat(gelu_tanh_f32(tot[ms][0][v]) * tot[ms][1][v]);
-                }
+                    for (int v = 0; v < 16; ++v) {
+                        const int row = 32 * ms + 8 * (v >> 2) + 4 * half + (v & 3);
+                        U[row * kUPitch + (wave - 2) * 32 + n] = tot[ms][v];
+                    }
+            }
+            __syncthreads();
+            if (wave < 2) {
+#pragma unroll
+                for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int row = 32 * ms + 8 * (v >> 2) + 4 * half + (v & 3);
+                        const float u = U[row * kUPitch + wave * 32 + n];
+                        Hs[row * kHPitch + wave * 32 + n] = (uint16_t)f32_to_f16_sat(gelu_tanh_f32(tot[ms][v]) * u);
+                    }
+            }
             __syncthreads();
             const int row = tid >> 1, hh = tid & 1;
-            const u32x4_t *src = reinterpret_cast<const u32x4_t *>(Hs + row * kAPitch + hh * 32);
+            const u32x4_t *src = reinterpret_cast<const u32x4_t *>(Hs + row * kHPitch + hh * 32);
             u32x4_t hv[4];
             float hsum_part = 0.0f;
 #pragma unroll
@@ -335,7 +426,8 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
                 for (int i = 0; i < 4; ++i) o[i] = hv[i];
                 if (hh == 0) {
                     const int Gpo = shared_item ? a.Gp_Is : a.Gp_I;
-                    uint16_t *hs = (shared_item ? a.hsplit_s : a.hsplit_r) + (size_t)dst * 3 * Gpo;
+                    const int Kso = shared_item ? a.Ks_Is : a.Ks_I;
+                    uint16_t *hs = (shared_item ? a.hsplit_s : a.hsplit_r) + (size_t)dst * Kso;
                     const uint32_t hi = f32_to_bf16(H);
                     const uint32_t lo = f32_to_bf16(H - bf16_to_f32(hi));
                     hs[nt] = (uint16_t)hi;
@@ -345,37 +437,37 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
             }
         } else {
             float *out = shared_item ? a.sh : a.r;
-            const int c0 = (nt * 4 + wn * 2) * 32 + n;
+            const int c0 = (nt * 4 + wave) * 32 + n;
 #pragma unroll
-            for (int ms = 0; ms < 2; ++ms)
+            for (int ms = 0; ms < 4; ++ms)
+                if (ms < live_ms) {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = wm * 64 + ms * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-                    const int dst = drow[row];
-                    if (dst >= 0) {
-                        out[(size_t)dst * a.d + c0] = tot[ms][0][v];
-                        out[(size_t)dst * a.d + c0 + 32] = tot[ms][1][v];
+                    for (int v = 0; v < 16; ++v) {
+                        const int row = 32 * ms + 8 * (v >> 2) + 4 * half + (v & 3);
+                        const int dst = drow[row];
+                        if (dst >= 0) out[(size_t)dst * a.d + c0] = tot[ms][v];
                     }
                 }
         }
     }
 }
 
-// Bias-term B' fragments of one quantized matrix stack (n_mats x [rows, in]): for each
-// (matrix, 32-row block rb, 16-step st, lane l) eight bf16 values for K' indices
-// kk = 16 st + 8 (l / 32) + j, j = 0..7, of row rb*32 + l%32: with part = kk / Gp and
-// g = kk % Gp, c = bias - 16 scale of group g, value c_hi (part 0, 1) or c_lo (part 2),
-// 0 for padding groups g >= G. grid: ceil(n_mats * rows/32 * steps * 64 / 256); block 256
+// Bias-term B' fragments of one quantized matrix stack (n_mats x [rows, in]), laid out
+// [matrix][32-row block rb][lane l][step st][8 bf16] with steps padded to a multiple of 12
+// (zero fragments): the eight values for K' indices kk = 16 st + 8 (l / 32) + j, j = 0..7,
+// of row rb*32 + l%32. With part = kk / Gp and g = kk % Gp, c = bias - 16 scale of group g,
+// the value is c_hi (part 0, 1) or c_lo (part 2), and 0 for padding groups g >= G or part 3.
+// grid: ceil(n_mats * rows/32 * 64 * steps_padded / 256); block 256
 __global__ __launch_bounds__(256) void k_bias_table(const uint32_t *__restrict__ sb, int n_mats, int rows, int G,
                                                     int Gp, uint8_t *__restrict__ out) {
-    const int steps = 3 * Gp / 16;
+    const int steps = 3 * Gp / 16, sp = roundup(steps, 12);
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    const size_t total = (size_t)n_mats * (rows / 32) * steps * 64;
+    const size_t total = (size_t)n_mats * (rows / 32) * 64 * sp;
     if (i >= total) return;
-    const int lane = (int)(i % 64);
-    size_t r = i / 64;
-    const int st = (int)(r % steps);
-    r /= steps;
+    const int st = (int)(i % sp);
+    size_t r = i / sp;
+    const int lane = (int)(r % 64);
+    r /= 64;
     const int rb = (int)(r % (rows / 32));
     const size_t m = r / (rows / 32);
     const uint32_t *sbm = sb + m * (size_t)rows * G + (size_t)rb * G * 32 + (lane & 31);
@@ -387,7 +479,7 @@ __global__ __launch_bounds__(256) void k_bias_table(const uint32_t *__restrict__
         for (int h2 = 0; h2 < 2; ++h2) {
             const int kk = 16 * st + 8 * (lane >> 5) + 2 * jj + h2;
             const int part = kk / Gp, gg = kk % Gp;
-            v2[h2] = gg < G ? bias_part(sbm[gg * 32], part) : 0u;
+            v2[h2] = (part < 3 && gg < G) ? bias_part(sbm[gg * 32], part) : 0u;
         }
         w[jj] = v2[0] | (v2[1] << 16);
     }
@@ -466,6 +558,9 @@ PreArgs make_args(const moe_layer *L, const uint16_t *x, int T) {
     a.Gp_d = L->Gp_d;
     a.Gp_I = L->Gp_I;
     a.Gp_Is = L->Gp_Is;
+    a.Ks_d = L->Ks_d;
+    a.Ks_I = L->Ks_I;
+    a.Ks_Is = L->Ks_Is;
     a.r = L->ws.r;
     a.sh = L->ws.sh;
     a.bt_gate = L->ws.bt[0];
@@ -502,12 +597,12 @@ hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s) {
 
 size_t bias_table_bytes(int n_mats, int rows, int in_dim) {
     const int Gp = roundup(in_dim / 64, 16);
-    return (size_t)n_mats * (rows / 32) * (3 * Gp / 16) * 1024;
+    return (size_t)n_mats * (rows / 32) * 64 * roundup(3 * Gp / 16, 12) * 16;
 }
 
 hipError_t launch_bias_table(const moe_qmat &m, int n_mats, int rows, int in_dim, uint8_t *out, hipStream_t s) {
     const int G = in_dim / 64, Gp = roundup(G, 16);
-    const size_t total = (size_t)n_mats * (rows / 32) * (3 * Gp / 16) * 64;
+    const size_t total = (size_t)n_mats * (rows / 32) * 64 * roundup(3 * Gp / 16, 12);
     hipLaunchKernelGGL(k_bias_table, dim3((unsigned)cdiv((int)total, 256)), dim3(256), 0, s, m.sb, n_mats, rows, G, Gp,
                        out);
     return hipGetLastError();

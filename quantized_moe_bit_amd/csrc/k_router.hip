@@ -35,7 +35,8 @@ constexpr int kRT = 8;     // tokens per router wave (prefill router)
 // bf16 hi | lo | hi split for the bias-term GEMM of the prefill gate/up.
 // grid: ceil(T * G / 256); block 256
 __global__ __launch_bounds__(256) void k_xsum(const uint16_t *__restrict__ x, int T, int d,
-                                              float *__restrict__ xsum, uint16_t *__restrict__ xsplit, int Gp) {
+                                              float *__restrict__ xsum, uint16_t *__restrict__ xsplit, int Gp,
+                                              int Ks) {
     const int G = d / 64;
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= T * G) return;
@@ -55,9 +56,9 @@ __global__ __launch_bounds__(256) void k_xsum(const uint16_t *__restrict__ x, in
     xsum[i] = X;
     const uint32_t hi = f32_to_bf16(X);
     const uint32_t lo = f32_to_bf16(X - bf16_to_f32(hi));
-    xsplit[(size_t)t * 3 * Gp + g] = (uint16_t)hi;
-    xsplit[(size_t)t * 3 * Gp + Gp + g] = (uint16_t)lo;
-    xsplit[(size_t)t * 3 * Gp + 2 * Gp + g] = (uint16_t)hi;
+    xsplit[(size_t)t * Ks + g] = (uint16_t)hi;
+    xsplit[(size_t)t * Ks + Gp + g] = (uint16_t)lo;
+    xsplit[(size_t)t * Ks + 2 * Gp + g] = (uint16_t)hi;
 }
 
 // Prefill router: lane = expert, wave = (64 experts, kRT tokens); a workgroup = 4 waves =
@@ -308,7 +309,7 @@ __global__ __launch_bounds__(256) void k_bucket_scatter(const int32_t *__restric
 hipError_t launch_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s) {
     const int d = L->dims.d_model, E = L->dims.n_experts, G = d / 64;
     hipLaunchKernelGGL(k_xsum, dim3(cdiv(T * G, 256)), dim3(256), 0, s, x, T, d, L->ws.xsum, L->ws.xsplit,
-                       L->Gp_d);
+                       L->Gp_d, L->Ks_d);
     hipLaunchKernelGGL(k_router_pre, dim3(cdiv(T, 2 * kRT), cdiv(E, 128)), dim3(256), 0, s, x, T, d, E,
                        static_cast<const uint8_t *>(L->w.router.codes), L->w.router.sb, L->ws.xsum, L->w.logit_bias,
                        logits);

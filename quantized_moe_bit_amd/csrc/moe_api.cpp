@@ -50,6 +50,13 @@ moe_status check_dims(const moe_dims *D) {
         return fail(MOE_E_SHAPE, "max_tokens %d out of range [1, 2^20]", D->max_tokens);
     if (D->d_expert > 16384 || D->d_shared > 16384)
         return fail(MOE_E_SHAPE, "d_expert %d / d_shared %d above 16384", D->d_expert, D->d_shared);
+    {
+        // the prefill GEMMs address activation rows with 32-bit byte offsets
+        const uint64_t P = (uint64_t)D->max_tokens * D->top_k;
+        const uint64_t wmax = (uint64_t)(D->d_model > D->d_expert ? D->d_model : D->d_expert);
+        if (P * wmax * 2 >= (1ull << 32) || (uint64_t)D->max_tokens * D->d_shared * 2 >= (1ull << 32))
+            return fail(MOE_E_SHAPE, "max_tokens %d too large: activation buffers exceed 4 GiB", D->max_tokens);
+    }
     if (dec_stage3_lds(*D) > 65536)
         return fail(MOE_E_SHAPE, "top_k * d_expert = %d too large for the decode down projection (LDS)",
                     D->top_k * D->d_expert);
@@ -210,6 +217,9 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     L->Gp_d = roundup(L->G_d, 16);
     L->Gp_I = roundup(L->G_I, 16);
     L->Gp_Is = roundup(L->G_Is, 16);
+    L->Ks_d = roundup(3 * L->Gp_d, 64);
+    L->Ks_I = roundup(3 * L->Gp_I, 64);
+    L->Ks_Is = roundup(3 * L->Gp_Is, 64);
     L->max_dec = D.max_tokens < MOE_MAX_DECODE_TOKENS ? D.max_tokens : MOE_MAX_DECODE_TOKENS;
     const size_t nchunks = (size_t)cdiv((int)P, kChunk);
 
@@ -219,7 +229,7 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.idx, P);
     plan.take(&ws.wts, P);
     plan.take(&ws.xsum, Tm * L->G_d);
-    plan.take(&ws.xsplit, Tm * 3 * L->Gp_d);
+    plan.take(&ws.xsplit, Tm * L->Ks_d);
     plan.take(&ws.counts, E);
     plan.take(&ws.offsets, E + 1);
     plan.take(&ws.tile_off, E + 1);
@@ -228,9 +238,9 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.perm, P);
     plan.take(&ws.pos, P);
     plan.take(&ws.h_r, P * I);
-    plan.take(&ws.hsplit_r, P * 3 * L->Gp_I);
+    plan.take(&ws.hsplit_r, P * L->Ks_I);
     plan.take(&ws.h_s, Tm * Is);
-    plan.take(&ws.hsplit_s, Tm * 3 * L->Gp_Is);
+    plan.take(&ws.hsplit_s, Tm * L->Ks_Is);
     plan.take(&ws.r, P * d);
     plan.take(&ws.sh, Tm * d);
     plan.take(&ws.bt[0], bias_table_bytes(E, I, d));

@@ -50,7 +50,7 @@ struct Workspace {
     int32_t *idx;         // [maxT, k]
     float *wts;           // [maxT, k]
     float *xsum;          // [maxT, G]          router-order group sums of x
-    uint16_t *xsplit;     // [maxT, 3*Gp_d]     bf16 hi | lo | hi of the group sums
+    uint16_t *xsplit;     // [maxT, Ks_d]       bf16 hi | lo | hi of the group sums (zero padded)
     int32_t *counts;      // [E]
     int32_t *offsets;     // [E+1]
     int32_t *tile_off;    // [E+1]              prefix sum of ceil(count/kMT)
@@ -59,9 +59,9 @@ struct Workspace {
     int32_t *perm;        // [maxT*k]
     int32_t *pos;         // [maxT*k]
     uint16_t *h_r;        // [maxT*k, I]        routed hidden activations, fp16 bits (bucket order)
-    uint16_t *hsplit_r;   // [maxT*k, 3*Gp_I]
+    uint16_t *hsplit_r;   // [maxT*k, Ks_I]
     uint16_t *h_s;        // [maxT, I_s]        shared hidden activations, fp16 bits
-    uint16_t *hsplit_s;   // [maxT, 3*Gp_Is]
+    uint16_t *hsplit_s;   // [maxT, Ks_Is]
     float *r;             // [maxT*k, d]        routed expert outputs (bucket order)
     float *sh;            // [maxT, d]          shared expert outputs
     uint8_t *bt[6];       // bias-term B' fragment tables of gate, up, down, sh_gate, sh_up, sh_down
@@ -84,6 +84,7 @@ struct moe_layer {
     int device;
     int G_d, G_I, G_Is;        // groups along d, I, I_s
     int Gp_d, Gp_I, Gp_Is;     // padded to a multiple of 16
+    int Ks_d, Ks_I, Ks_Is;     // split-sum row strides: 3 Gp rounded up to a multiple of 64
     int max_dec;               // decode capacity = min(max_tokens, MOE_MAX_DECODE_TOKENS)
     void *ws_base;
     size_t ws_bytes;

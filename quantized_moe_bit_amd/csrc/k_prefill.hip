@@ -17,9 +17,9 @@
 // after the main loop, with both factors split into bf16 hi + lo parts:
 //   c X ~= c_hi X_hi + c_hi X_lo + c_lo X_hi.
 //
-// Work items: (expert or shared, 128-row tile, output tile). A persistent grid walks them
-// with a static schedule: items are cut into 8 contiguous ranges, one per XCD (workgroup
-// i runs on XCD i % 8), so all tiles of one expert share an L2.
+// Work items: (expert or shared, 128-row tile, output tile), one per workgroup; all output
+// tiles of a row tile run on the same XCD (workgroup i runs on XCD i % 8), so the row tile
+// is fetched into one L2.
 #include <type_traits>
 
 #include "device_common.h"
@@ -54,12 +54,19 @@ __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 3); }
 
 // Direct global->LDS load: every lane of the wave moves 16 (or 4) bytes from
 // sbase + voff (sbase wave-uniform, voff a per-lane 32-bit byte offset) to lds_base +
-// 16 lane (4 lane); lds_base is wave-uniform. Issued as inline asm so that the compiler's
+// 16 lane (4 lane); lds_base is wave-uniform (both are read from lane 0). Issued as inline asm so that the compiler's
 // wait insertion (which would wait for every outstanding direct load before any LDS read)
 // stays out of the ring; the ring waits for them itself (ring_sync). M0 carries the LDS base
 // and is restored afterwards.
+__device__ __forceinline__ const void *uniform_ptr(const void *p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, const uint8_t *lds_base) {
     const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+    const void *sb = uniform_ptr(sbase);
     uint32_t save;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
@@ -67,11 +74,12 @@ __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, const ui
         "global_load_lds_dwordx4 %1, %2\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(save)
-        : "v"(voff), "s"(sbase), "s"(m)
+        : "v"(voff), "s"(sb), "s"(m)
         : "memory");
 }
 __device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, const uint8_t *lds_base) {
     const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+    const void *sb = uniform_ptr(sbase);
     uint32_t save;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
@@ -79,7 +87,7 @@ __device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, const uin
         "global_load_lds_dword %1, %2\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(save)
-        : "v"(voff), "s"(sbase), "s"(m)
+        : "v"(voff), "s"(sb), "s"(m)
         : "memory");
 }
 
@@ -165,29 +173,32 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) aoff[s] = n * 128 + 16 * ((2 * s + half) ^ swz(n));
 
-    // item space
-    const int Ms = cdiv(a.T, kMT);
-    const int NTs = MODE == 0 ? a.Is / 64 : a.d / 128;
-    const int NTr = MODE == 0 ? a.I / 64 : a.d / 128;
-    const int S_items = Ms * NTs;
-    const int N = S_items + a.tile_off[E] * NTr;
-    const int nwg = gridDim.x, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_xcd = nwg >> 3;
-    const int lo = (int)((long long)N * xcd / 8), hi = (int)((long long)N * (xcd + 1) / 8);
-
-    for (int item = lo + slot; item < hi; item += per_xcd) {
+    // Work item of this workgroup (one per workgroup). Shared-expert items come first, then
+    // routed ones; within each part, 128-row tiles are dealt to the eight XCDs round-robin
+    // (workgroup b runs on XCD b % 8, parts start at multiples of 8) and every output tile
+    // of a row tile runs on the same XCD, so the row tile is fetched into one L2 only. The
+    // routed part is sized for the worst case; workgroups past the real tiles exit at once.
+    {
+        const int Ms = cdiv(a.T, kMT), Ms8 = roundup(Ms, 8);
+        const int NTs = MODE == 0 ? a.Is / 64 : a.d / 128;
+        const int NTr = MODE == 0 ? a.I / 64 : a.d / 128;
+        const int b = blockIdx.x, Gs = Ms8 * NTs;
         bool shared_item;
         int e = 0, mt, nt, count, rowbase;
-        if (item < S_items) {
+        if (b < Gs) {
+            const int j = b >> 3;
             shared_item = true;
-            mt = item / NTs;
-            nt = item % NTs;
+            mt = 8 * (j / NTs) + (b & 7);
+            nt = j % NTs;
+            if (mt >= Ms) return;
             count = a.T;
             rowbase = 0;
         } else {
+            const int i = b - Gs, j = i >> 3;
             shared_item = false;
-            const int j = item - S_items;
-            const int mg = j / NTr;
+            const int mg = 8 * (j / NTr) + (i & 7);
             nt = j % NTr;
+            if (mg >= a.tile_off[E]) return;
             e = find_expert(a.tile_off, E, mg);
             mt = mg - a.tile_off[e];
             rowbase = a.offsets[e];
@@ -204,7 +215,6 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
         const uint16_t *Asrc = MODE == 0 ? a.x : (shared_item ? a.h_s : a.h_r);
         const uint16_t *Bsrc = MODE == 0 ? a.xsplit : (shared_item ? a.hsplit_s : a.hsplit_r);
 
-        __syncthreads();   // previous item is done with the LDS ring and row tables
         if (tid < kMT) {
             const int r = mt * kMT + tid;
             int src = -1, dst = -1;
@@ -238,6 +248,8 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
             const int rb = MODE == 0 ? 2 * nt + (wave & 1) : 4 * nt + wave;
             Bt = static_cast<const uint8_t *>(m->codes) + (size_t)e * rows * K / 2 + (size_t)rb * G * 1024;
             St = reinterpret_cast<const uint8_t *>(m->sb + (size_t)e * rows * G + (size_t)rb * G * 32);
+            Bt = static_cast<const uint8_t *>(uniform_ptr(Bt));
+            St = static_cast<const uint8_t *>(uniform_ptr(St));
             Tb = tb + (((size_t)e * (rows / 32) + rb) * 64 + lane) * nbp * 16;
         }
         const uint32_t boff = lane * 16, soff = n * 4;
@@ -572,26 +584,26 @@ PreArgs make_args(const moe_layer *L, const uint16_t *x, int T) {
     return a;
 }
 
-int persistent_grid() {
-    static int grid = 0;
-    if (!grid) {
-        int dev = 0, cus = 256;
-        if (hipGetDevice(&dev) == hipSuccess)
-            (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        grid = ((cus * 2 + 7) / 8) * 8;
-    }
-    return grid;
+// Workgroups of one prefill GEMM launch: shared part (row tiles padded to a multiple of 8)
+// plus the routed part sized for the worst case, cdiv(T k, 128) + min(E, T k) row tiles.
+int pre_grid(const moe_layer *L, int T, int mode) {
+    const moe_dims &D = L->dims;
+    const int NTs = mode == 0 ? D.d_shared / 64 : D.d_model / 128;
+    const int NTr = mode == 0 ? D.d_expert / 64 : D.d_model / 128;
+    const int P = T * D.top_k;
+    const int Mr = cdiv(P, kMT) + (D.n_experts < P ? D.n_experts : P);
+    return roundup(cdiv(T, kMT), 8) * NTs + roundup(Mr, 8) * NTr;
 }
 
 }  // namespace
 
 hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s) {
-    hipLaunchKernelGGL(k_pre_gemm<0>, dim3(persistent_grid()), dim3(kPreWG), 0, s, make_args(L, x, T));
+    hipLaunchKernelGGL(k_pre_gemm<0>, dim3(pre_grid(L, T, 0)), dim3(kPreWG), 0, s, make_args(L, x, T));
     return hipGetLastError();
 }
 
 hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s) {
-    hipLaunchKernelGGL(k_pre_gemm<1>, dim3(persistent_grid()), dim3(kPreWG), 0, s, make_args(L, nullptr, T));
+    hipLaunchKernelGGL(k_pre_gemm<1>, dim3(pre_grid(L, T, 1)), dim3(kPreWG), 0, s, make_args(L, nullptr, T));
     return hipGetLastError();
 }
 

@@ -147,18 +147,20 @@ __device__ __forceinline__ void gu_compute(const GUTiles<PB> &r, const uint16_t 
 // One gate/up piece over input groups [g0, g1) (at most NW * PB) with NW waves: loads tiles,
 // stages x[g0:g1] of token row xrow, computes, adds the waves' sums in wave order, and either
 // writes the 32 partial gate and up sums to out_g[n], out_u[n] (hout == nullptr) or, when the
-// piece covers the whole input, h = fp16(gelu(g) * u) to hout[n].
+// piece covers the whole input, h = fp16(gelu(g) * u) to hout[n]. With x_staged, xs already
+// holds x[g0:g1] (written before the call; the call's barrier publishes it).
 // LDS: xs (NW * PB * 64 bf16), red.
 template <int NW, int PB>
 __device__ __forceinline__ void gateup_piece(const uint16_t *xrow, const uint8_t *Wg, const uint8_t *Wu,
                                              const uint32_t *Sg, const uint32_t *Su, int G, int jb, int g0, int g1,
                                              uint16_t *xs, float (*red)[2][32], float *out_g, float *out_u,
-                                             uint16_t *hout) {
+                                             uint16_t *hout, bool x_staged = false) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31;
     GUTiles<PB> r;
     gu_load<NW, PB>(r, Wg, Wu, Sg, Su, G, jb, g0, g1);
-    for (int i = tid; i < (g1 - g0) * 8; i += 64 * NW)
-        *reinterpret_cast<u32x4_t *>(xs + 8 * i) = ld16(xrow + 64 * g0 + 8 * i);
+    if (!x_staged)
+        for (int i = tid; i < (g1 - g0) * 8; i += 64 * NW)
+            *reinterpret_cast<u32x4_t *>(xs + 8 * i) = ld16(xrow + 64 * g0 + 8 * i);
     __syncthreads();
     float accg = 0.0f, accu = 0.0f;
     gu_compute<NW, PB>(r, xs, g0, g1, accg, accu);
@@ -281,81 +283,79 @@ __device__ __forceinline__ float down_compute(const DTiles &r, const uint16_t *h
 }
 
 // ----------------------------------------------------------------------------- top-k
-// Selection key of (logit v, expert e): order-preserving bits of v (with -0 folded into +0)
-// above the inverted index, so a larger key is a larger logit, or an equal logit with a
-// lower index -- the top-k order (ties to the lower expert index).
-__device__ __forceinline__ uint64_t topk_key(float v, int e) {
-    uint32_t u = __float_as_uint(v + 0.0f);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
-}
-
-__device__ __forceinline__ float key_value(uint64_t k) {
-    uint32_t u = (uint32_t)(k >> 32);
-    u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
-    return __uint_as_float(u);
-}
-
+// Largest float of the wave: DPP within rows of 16 (swap pairs, swap halves of quads,
+// half-row mirror, row mirror), then the four row results through scalar registers.
 template <int CTRL>
-__device__ __forceinline__ uint64_t max_dpp(uint64_t x) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)x, CTRL, 0xF, 0xF, true);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(x >> 32), CTRL, 0xF, 0xF, true);
-    const uint64_t y = ((uint64_t)hi << 32) | lo;
-    return y > x ? y : x;
+__device__ __forceinline__ float max_dpp(float x) {
+    const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+    return fmaxf(x, y);
 }
 
-__device__ __forceinline__ uint64_t readlane64(uint64_t x, int lane) {
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)x, lane);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), lane);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// Largest key of the wave: DPP within rows of 16 (swap pairs, swap halves of quads, half-row
-// mirror, row mirror), then the four row results through scalar registers.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t x) {
+__device__ __forceinline__ float wave_max(float x) {
     x = max_dpp<0xB1>(x);    // quad_perm [1,0,3,2]
     x = max_dpp<0x4E>(x);    // quad_perm [2,3,0,1]
     x = max_dpp<0x141>(x);   // row_half_mirror
     x = max_dpp<0x140>(x);   // row_mirror
-    uint64_t m = readlane64(x, 0);
-    const uint64_t r1 = readlane64(x, 16), r2 = readlane64(x, 32), r3 = readlane64(x, 48);
-    m = r1 > m ? r1 : m;
-    m = r2 > m ? r2 : m;
-    m = r3 > m ? r3 : m;
-    return m;
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 // Slot `slot` of a token's top-k, derived by one wave from its logits row (identical on
-// every lane and every wave). With all_rounds, runs all k rounds and returns the slot's
-// softmax weight over the k selected logits (fp32) in w_out.
+// every lane and every wave): each round takes the largest remaining logit, ties to the
+// lowest expert index (the lowest lane of the lowest 64-expert block holding the maximum).
+// If no remaining logit equals the maximum (only NaNs remain), the lowest remaining index
+// is taken. With all_rounds, runs all k rounds and returns the slot's softmax weight over
+// the k selected logits (fp32) in w_out.
 template <int kPer>   // logits per lane: E <= 64 * kPer
 __device__ __forceinline__ int wave_topk(const float *__restrict__ l, int E, int k, int slot, bool all_rounds,
                                          float &w_out) {
     const int lane = threadIdx.x & 63;
-    uint64_t key[kPer];
+    float v[kPer];
+    bool live[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int e = lane + 64 * i;
-        key[i] = e < E ? topk_key(l[e], e) : 0ull;     // 0 is below every real key
+        live[i] = e < E;
+        v[i] = live[i] ? l[e] : 0.0f;
     }
     const int rounds = all_rounds ? k : slot + 1;
     int target_e = 0;
     float target_v = 0.0f, m = 0.0f, z = 0.0f;
     for (int s = 0; s < rounds; ++s) {
-        uint64_t best = key[0];
-#pragma unroll
-        for (int i = 1; i < kPer; ++i) best = key[i] > best ? key[i] : best;
-        best = wave_max_key(best);
-        const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-        const float v = key_value(best);
+        float lb = -INFINITY;
 #pragma unroll
         for (int i = 0; i < kPer; ++i)
-            if (key[i] == best) key[i] = 0ull;        // taken
-        if (s == 0) m = v;
-        z += __expf(v - m);
+            if (live[i]) lb = fmaxf(lb, v[i]);
+        const float mx = wave_max(lb);
+        int e = -1;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const uint64_t bal = __ballot(live[i] && v[i] == mx);
+            if (e < 0 && bal) e = 64 * i + __ffsll((long long)bal) - 1;
+        }
+        if (e < 0) {
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const uint64_t bal = __ballot(live[i]);
+                if (e < 0 && bal) e = 64 * i + __ffsll((long long)bal) - 1;
+            }
+        }
+        e = max(e, 0);
+        float val = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            if ((e >> 6) == i) {
+                val = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), e & 63));
+                if (lane == (e & 63)) live[i] = false;
+            }
+        if (s == 0) m = val;
+        z += __expf(val - m);
         if (s == slot) {
-            target_e = min(max(e, 0), E - 1);
-            target_v = v;
+            target_e = min(e, E - 1);
+            target_v = val;
         }
     }
     w_out = __expf(target_v - m) / z;
@@ -424,6 +424,11 @@ __global__ __launch_bounds__(64 * kW2) void k_dec_stage2(DecArgs a) {
     const int nR = a.T * a.k * JB;
     if ((int)blockIdx.x < nR) {
         const int jb = blockIdx.x % JB, pr = blockIdx.x / JB, t = pr / a.k, slot = pr % a.k;
+        uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
+        // the token's x is fetched while the selection is derived
+        const bool narrow = G <= kW2 * kB2;
+        u32x4_t xv = u32x4_t{0u, 0u, 0u, 0u};
+        if (narrow && tid < G * 8) xv = ld16(a.x + (size_t)t * a.d + 8 * tid);
         // every wave derives the token's selection itself; one unit of the pair records it
         const bool record = (jb == 0 && wave == 0);
         float wsel;
@@ -432,15 +437,15 @@ __global__ __launch_bounds__(64 * kW2) void k_dec_stage2(DecArgs a) {
             a.idx[pr] = e;
             a.wts[pr] = wsel;
         }
-        uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
+        if (narrow && tid < G * 8) *reinterpret_cast<u32x4_t *>(xs + 8 * tid) = xv;
         float(*red)[2][32] = reinterpret_cast<float(*)[2][32]>(smem + sizeof(uint16_t) * a.d);
         const size_t cstride = (size_t)a.I * a.d / 2, sstride = (size_t)a.I * G;
         const uint8_t *Wg = static_cast<const uint8_t *>(a.gate.codes) + e * cstride;
         const uint8_t *Wu = static_cast<const uint8_t *>(a.up.codes) + e * cstride;
         uint16_t *hout = a.h_r + (size_t)pr * a.I + jb * 32;
-        if (G <= kW2 * kB2) {
+        if (narrow) {
             gateup_piece<kW2, kB2>(a.x + (size_t)t * a.d, Wg, Wu, a.gate.sb + e * sstride, a.up.sb + e * sstride, G,
-                                   jb, 0, G, xs, red, nullptr, nullptr, hout);
+                                   jb, 0, G, xs, red, nullptr, nullptr, hout, true);
         } else {
             // wide inputs: kW2 * kB2 groups at a time, partial sums carried through red
             float *acc = reinterpret_cast<float *>(red);   // reuse: [2][32] totals after each batch
@@ -500,6 +505,24 @@ __global__ __launch_bounds__(64 * MAXW) void k_dec_stage3(DecArgs a) {
     float *part = reinterpret_cast<float *>(smem + sizeof(uint16_t) * a.k * a.I);  // [k][32]
     const int pr = t * a.k + wave;
     const int e = a.idx[pr];
+    // loads that do not depend on the expert go out first: the slot's h, and (first 32
+    // threads) the shared-expert partial sums and the slot weights of the combine
+    constexpr int kHL = 4;   // h chunks of 16 bytes per lane: I <= 64 * 8 * kHL
+    u32x4_t hv[kHL];
+#pragma unroll
+    for (int c = 0; c < kHL; ++c) {
+        const int i = lane + 64 * c;
+        hv[c] = i < a.I / 8 ? ld16(a.h_r + (size_t)pr * a.I + 8 * i) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    constexpr int kSP = 4, kWP = MAXW;
+    float shv[kSP], wv[kWP];
+    if (tid < 32) {
+        const int row = rb * 32 + tid;
+#pragma unroll
+        for (int ks = 0; ks < kSP; ++ks) shv[ks] = ks < a.KSs ? a.shp[((size_t)t * a.KSs + ks) * a.d + row] : 0.0f;
+#pragma unroll
+        for (int s = 0; s < kWP; ++s) wv[s] = s < a.k ? a.wts[(size_t)t * a.k + s] : 0.0f;
+    }
     const uint8_t *W = static_cast<const uint8_t *>(a.down.codes) + (size_t)e * a.d * a.I / 2;
     const uint32_t *S = a.down.sb + (size_t)e * a.d * GI;
     float rsum = 0.0f;
@@ -507,9 +530,19 @@ __global__ __launch_bounds__(64 * MAXW) void k_dec_stage3(DecArgs a) {
         const int gb1 = min(GI, gb + kDecodeChunkGroups);
         DTiles r;
         down_load(r, W, S, rb, GI, gb, gb1);
-        if (gb == 0)
-            for (int i = lane; i < a.I / 8; i += 64)
-                *reinterpret_cast<u32x4_t *>(hl + (size_t)wave * a.I + 8 * i) = ld16(a.h_r + (size_t)pr * a.I + 8 * i);
+        if (gb == 0) {
+            if (a.I <= 64 * 8 * kHL) {
+#pragma unroll
+                for (int c = 0; c < kHL; ++c) {
+                    const int i = lane + 64 * c;
+                    if (i < a.I / 8) *reinterpret_cast<u32x4_t *>(hl + (size_t)wave * a.I + 8 * i) = hv[c];
+                }
+            } else {
+                for (int i = lane; i < a.I / 8; i += 64)
+                    *reinterpret_cast<u32x4_t *>(hl + (size_t)wave * a.I + 8 * i) =
+                        ld16(a.h_r + (size_t)pr * a.I + 8 * i);
+            }
+        }
         __syncthreads();
         rsum += down_compute(r, hl + (size_t)wave * a.I + 64 * gb, gb, gb1);
     }
@@ -518,8 +551,16 @@ __global__ __launch_bounds__(64 * MAXW) void k_dec_stage3(DecArgs a) {
     if (tid < 32) {
         const int row = rb * 32 + tid;
         float out = 0.0f;
-        for (int ks = 0; ks < a.KSs; ++ks) out += a.shp[((size_t)t * a.KSs + ks) * a.d + row];
-        for (int s = 0; s < a.k; ++s) out = fmaf(a.wts[(size_t)t * a.k + s], part[s * 32 + tid], out);
+        if (a.KSs <= kSP) {
+#pragma unroll
+            for (int ks = 0; ks < kSP; ++ks)
+                if (ks < a.KSs) out += shv[ks];
+        } else {
+            for (int ks = 0; ks < a.KSs; ++ks) out += a.shp[((size_t)t * a.KSs + ks) * a.d + row];
+        }
+#pragma unroll
+        for (int s = 0; s < kWP; ++s)
+            if (s < a.k) out = fmaf(wv[s], part[s * 32 + tid], out);
         a.y[(size_t)t * a.d + row] = out;
     }
 }

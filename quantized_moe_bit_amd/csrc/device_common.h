@@ -23,6 +23,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// (t & mask) | c in one VALU instruction. The mask comes from a scalar register and c from a
+// vector register (one scalar operand per VALU instruction on gfx9).
+__device__ __forceinline__ uint32_t and_or(uint32_t t, uint32_t mask, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(t), "s"(mask), "v"(c));
+    return r;
+}
+
 // Two bf16 values (1 + q/16) built from the nibbles of one device-layout word.
 // Pair p (0..3) holds elements 2p and 2p+1 of the word's eight inputs; element j sits in
 // nibble (j even ? j/2 : 4 + j/2), so pair p is nibbles p and 4+p: shifting them to bits 3..6
@@ -32,7 +40,7 @@ __device__ __forceinline__ uint32_t nib_pair(uint32_t w) {
     uint32_t t;
     if constexpr (P == 0) t = w << 3;
     else t = w >> (4 * P - 3);
-    return (t & 0x00780078u) | 0x3F803F80u;
+    return and_or(t, 0x00780078u, 0x3F803F80u);
 }
 
 // One 16-byte MFMA B fragment (8 bf16) from one device-layout word.
@@ -59,7 +67,7 @@ __device__ __forceinline__ uint32_t nib_pair_f16(uint32_t w) {
     else if constexpr (P == 1) t = w << 2;
     else if constexpr (P == 2) t = w >> 2;
     else t = w >> 6;
-    return (t & 0x03C003C0u) | 0x3C003C00u;
+    return and_or(t, 0x03C003C0u, 0x3C003C00u);
 }
 
 __device__ __forceinline__ f16x8_t nib_frag_f16(uint32_t w) {

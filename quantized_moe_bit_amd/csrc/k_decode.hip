@@ -47,10 +47,11 @@ constexpr uint32_t kOneF16x2 = 0x3C003C00u;
 
 // ----------------------------------------------------------------------------- router
 // The wave's expert e; lane g handles input group g (and g + 64, ... for d > 4096).
-// P[t][g] into Ps, then lanes t < T sum over g in ascending order. Fixed fp32 order:
+// P[t][g] into Ps, then lanes t < T sum over g in ascending order (the group sums X also go
+// to xg_out when it is given). Fixed fp32 order:
 //   X = ((0 + x_0) + x_1) + ...; A = fma chain; P = fma(s, A, fl(b * X)); L = ((0 + P_0) + ...)
 __device__ __forceinline__ void router_wave(const uint16_t *__restrict__ x, int T, int d, int e, const uint8_t *__restrict__ rq,
-                            const uint32_t *__restrict__ rsb, float *Ps) {
+                            const uint32_t *__restrict__ rsb, float *Ps, float *xg_out) {
 #pragma clang fp contract(off)
     const int G = d / 64, lane = threadIdx.x & 63;
     for (int g = lane; g < G; g += 64) {
@@ -80,6 +81,7 @@ __device__ __forceinline__ void router_wave(const uint16_t *__restrict__ x, int 
             }
             const float bX = bi * X;
             Ps[t * G + g] = __builtin_fmaf(sc, A, bX);
+            if (xg_out) xg_out[t * G + g] = X;
         }
     }
 }
@@ -112,14 +114,14 @@ __device__ __forceinline__ void gu_load(GUTiles<PB> &r, const uint8_t *Wg, const
 }
 
 template <int NW, int PB>
-__device__ __forceinline__ void gu_compute(const GUTiles<PB> &r, const uint16_t *xs, int g0, int g1, float &accg,
-                                           float &accu) {
+__device__ __forceinline__ void gu_compute(const GUTiles<PB> &r, const uint16_t *xs, const float *Xs, int g0, int g1,
+                                           float &accg, float &accu) {
     const int wave = threadIdx.x >> 6, half = (threadIdx.x >> 5) & 1;
 #pragma unroll
     for (int b = 0; b < PB; ++b) {
         const int g = g0 + wave + b * NW;
         if (g < g1) {
-            float ag = 0.0f, au = 0.0f, xsum = 0.0f;
+            float ag = 0.0f, au = 0.0f;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xs + 64 * (g - g0) + 16 * s + 8 * half);
@@ -131,11 +133,9 @@ __device__ __forceinline__ void gu_compute(const GUTiles<PB> &r, const uint16_t 
                 au = dot2_bf16(xv[1], nib_pair<1>(r.wu[b][s]), au);
                 au = dot2_bf16(xv[2], nib_pair<2>(r.wu[b][s]), au);
                 au = dot2_bf16(xv[3], nib_pair<3>(r.wu[b][s]), au);
-                xsum = dot2_bf16(xv[0], kOneBf16x2, xsum);
-                xsum = dot2_bf16(xv[1], kOneBf16x2, xsum);
-                xsum = dot2_bf16(xv[2], kOneBf16x2, xsum);
-                xsum = dot2_bf16(xv[3], kOneBf16x2, xsum);
             }
+            // the (b - 16 s) X_g term once per group (lanes of half 0)
+            const float xsum = half == 0 ? Xs[g - g0] : 0.0f;
             const float s16g = 16.0f * bf16_to_f32(r.sbg[b] & 0xFFFFu);
             const float s16u = 16.0f * bf16_to_f32(r.sbu[b] & 0xFFFFu);
             accg = fmaf(s16g, ag, fmaf(bf16_to_f32(r.sbg[b] >> 16) - s16g, xsum, accg));
@@ -147,23 +147,37 @@ __device__ __forceinline__ void gu_compute(const GUTiles<PB> &r, const uint16_t 
 // One gate/up piece over input groups [g0, g1) (at most NW * PB) with NW waves: loads tiles,
 // stages x[g0:g1] of token row xrow, computes, adds the waves' sums in wave order, and either
 // writes the 32 partial gate and up sums to out_g[n], out_u[n] (hout == nullptr) or, when the
-// piece covers the whole input, h = fp16(gelu(g) * u) to hout[n]. With x_staged, xs already
-// holds x[g0:g1] (written before the call; the call's barrier publishes it).
-// LDS: xs (NW * PB * 64 bf16), red.
+// piece covers the whole input, h = fp16(gelu(g) * u) to hout[n] (and, with hsum_out, the
+// sum of those 32 values to *hsum_out). With x_staged, xs and Xs already hold x[g0:g1] and
+// its group sums (written before the call; the call's barrier publishes them); otherwise
+// they are staged here. LDS: xs (NW * PB * 64 bf16), Xs (NW * PB floats), red.
 template <int NW, int PB>
 __device__ __forceinline__ void gateup_piece(const uint16_t *xrow, const uint8_t *Wg, const uint8_t *Wu,
                                              const uint32_t *Sg, const uint32_t *Su, int G, int jb, int g0, int g1,
-                                             uint16_t *xs, float (*red)[2][32], float *out_g, float *out_u,
-                                             uint16_t *hout, bool x_staged = false) {
+                                             uint16_t *xs, float *Xs, float (*red)[2][32], float *out_g, float *out_u,
+                                             uint16_t *hout, bool x_staged = false, float *hsum_out = nullptr) {
+    static_assert(PB <= 8, "one 16-byte x chunk per thread");
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31;
     GUTiles<PB> r;
     gu_load<NW, PB>(r, Wg, Wu, Sg, Su, G, jb, g0, g1);
-    if (!x_staged)
-        for (int i = tid; i < (g1 - g0) * 8; i += 64 * NW)
-            *reinterpret_cast<u32x4_t *>(xs + 8 * i) = ld16(xrow + 64 * g0 + 8 * i);
+    if (!x_staged) {
+        // stage x[g0:g1] and its group sums (eight consecutive threads per group)
+        const int nch = (g1 - g0) * 8;
+        float ps = 0.0f;
+        if (tid < nch) {
+            const u32x4_t v = ld16(xrow + 64 * g0 + 8 * tid);
+            *reinterpret_cast<u32x4_t *>(xs + 8 * tid) = v;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) ps += bf16_to_f32(v[w] & 0xFFFFu) + bf16_to_f32(v[w] >> 16);
+        }
+        ps += __shfl_xor(ps, 1);
+        ps += __shfl_xor(ps, 2);
+        ps += __shfl_xor(ps, 4);
+        if (tid < nch && (tid & 7) == 0) Xs[tid >> 3] = ps;
+    }
     __syncthreads();
     float accg = 0.0f, accu = 0.0f;
-    gu_compute<NW, PB>(r, xs, g0, g1, accg, accu);
+    gu_compute<NW, PB>(r, xs, Xs, g0, g1, accg, accu);
     accg += __shfl_xor(accg, 32);
     accu += __shfl_xor(accu, 32);
     if (lane < 32) {
@@ -179,11 +193,23 @@ __device__ __forceinline__ void gateup_piece(const uint16_t *xrow, const uint8_t
             uv += red[w][1][tid];
         }
         if (hout) {
-            hout[tid] = (uint16_t)f32_to_f16_sat(gelu_tanh_f32(gv) * uv);
+            const uint32_t hb = f32_to_f16_sat(gelu_tanh_f32(gv) * uv);
+            hout[tid] = (uint16_t)hb;
+            if (hsum_out) red[0][0][tid] = f16_to_f32(hb);
         } else {
             out_g[tid] = gv;
             out_u[tid] = uv;
         }
+    }
+    if (hout && hsum_out && wave == 0) {
+        // sum of the 32 stored h values (after every lane of wave 0 has read red above)
+        float hs = lane < 32 ? red[0][0][lane] : 0.0f;
+        hs += __shfl_xor(hs, 16);
+        hs += __shfl_xor(hs, 8);
+        hs += __shfl_xor(hs, 4);
+        hs += __shfl_xor(hs, 2);
+        hs += __shfl_xor(hs, 1);
+        if (lane == 0) *hsum_out = hs;
     }
 }
 
@@ -257,7 +283,8 @@ __device__ __forceinline__ void down_load(DTiles &r, const uint8_t *W, const uin
         }
 }
 
-__device__ __forceinline__ float down_compute(const DTiles &r, const uint16_t *hl, int g0, int g1) {
+// Hs: group sums of h (indexed from g0), or nullptr to form them from hl here.
+__device__ __forceinline__ float down_compute(const DTiles &r, const uint16_t *hl, const float *Hs, int g0, int g1) {
     const int half = (threadIdx.x >> 5) & 1;
     float acc = 0.0f;
 #pragma unroll
@@ -271,11 +298,14 @@ __device__ __forceinline__ float down_compute(const DTiles &r, const uint16_t *h
                 a = dot2_f16(hv[1], nib_pair_f16<1>(r.w4[b][s]), a);
                 a = dot2_f16(hv[2], nib_pair_f16<2>(r.w4[b][s]), a);
                 a = dot2_f16(hv[3], nib_pair_f16<3>(r.w4[b][s]), a);
-                hsum = dot2_f16(hv[0], kOneF16x2, hsum);
-                hsum = dot2_f16(hv[1], kOneF16x2, hsum);
-                hsum = dot2_f16(hv[2], kOneF16x2, hsum);
-                hsum = dot2_f16(hv[3], kOneF16x2, hsum);
+                if (!Hs) {
+                    hsum = dot2_f16(hv[0], kOneF16x2, hsum);
+                    hsum = dot2_f16(hv[1], kOneF16x2, hsum);
+                    hsum = dot2_f16(hv[2], kOneF16x2, hsum);
+                    hsum = dot2_f16(hv[3], kOneF16x2, hsum);
+                }
             }
+            if (Hs) hsum = half == 0 ? Hs[b] : 0.0f;
             const float s16 = 16.0f * bf16_to_f32(r.sbw[b] & 0xFFFFu);
             acc = fmaf(s16, a, fmaf(bf16_to_f32(r.sbw[b] >> 16) - s16, hsum, acc));
         }
@@ -376,6 +406,8 @@ struct DecArgs {
     float *gus;             // [T][KSd][2][I_s] shared gate/up partials
     uint16_t *h_r;          // [T*k][I]         routed hidden activations (fp16 bits)
     float *shp;             // [T][KSs][d]      shared down partials
+    float *xg;              // [T][d/64]        group sums of x (router, fixed order)
+    float *hs;              // [T*k][I/32]      sums of 32 consecutive routed h values
     float *y;
 };
 
@@ -389,7 +421,7 @@ __global__ __launch_bounds__(64 * kPW) void k_dec_stage1(DecArgs a) {
         float *Ps = reinterpret_cast<float *>(smem);     // [kRW][T][G]
         const int e = blockIdx.x * kRW + wave;
         float *P = Ps + (size_t)wave * a.T * G;
-        if (e < a.E) router_wave(a.x, a.T, a.d, e, a.rq, a.rsb, P);
+        if (e < a.E) router_wave(a.x, a.T, a.d, e, a.rq, a.rsb, P, e == 0 ? a.xg : nullptr);
         __syncthreads();
         if (e < a.E && lane < a.T) {
 #pragma clang fp contract(off)
@@ -401,7 +433,8 @@ __global__ __launch_bounds__(64 * kPW) void k_dec_stage1(DecArgs a) {
         return;
     }
     uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
-    float(*red)[2][32] = reinterpret_cast<float(*)[2][32]>(smem + sizeof(uint16_t) * 64 * kGPS);
+    float *Xs = reinterpret_cast<float *>(smem + sizeof(uint16_t) * 64 * kGPS);
+    float(*red)[2][32] = reinterpret_cast<float(*)[2][32]>(smem + sizeof(uint16_t) * 64 * kGPS + sizeof(float) * 16);
     const int JBs = a.Is / 32;
     int u = blockIdx.x - RW;
     const int ks = u % a.KSd;
@@ -411,7 +444,7 @@ __global__ __launch_bounds__(64 * kPW) void k_dec_stage1(DecArgs a) {
     float *out = a.gus + ((size_t)t * a.KSd + ks) * 2 * a.Is + jb * 32;
     gateup_piece<kPW, kPB>(a.x + (size_t)t * a.d, static_cast<const uint8_t *>(a.sh_gate.codes),
                            static_cast<const uint8_t *>(a.sh_up.codes), a.sh_gate.sb, a.sh_up.sb, G, jb, g0, g1, xs,
-                           red, out, out + a.Is, nullptr);
+                           Xs, red, out, out + a.Is, nullptr);
 }
 
 // grid: T * k * (I / 32) routed gate/up units + T * (d / 32) * KSs shared down pieces;
@@ -428,7 +461,9 @@ __global__ __launch_bounds__(64 * kW2) void k_dec_stage2(DecArgs a) {
         // the token's x is fetched while the selection is derived
         const bool narrow = G <= kW2 * kB2;
         u32x4_t xv = u32x4_t{0u, 0u, 0u, 0u};
+        float xgv = 0.0f;
         if (narrow && tid < G * 8) xv = ld16(a.x + (size_t)t * a.d + 8 * tid);
+        if (narrow && tid < G) xgv = a.xg[(size_t)t * G + tid];
         // every wave derives the token's selection itself; one unit of the pair records it
         const bool record = (jb == 0 && wave == 0);
         float wsel;
@@ -437,22 +472,26 @@ __global__ __launch_bounds__(64 * kW2) void k_dec_stage2(DecArgs a) {
             a.idx[pr] = e;
             a.wts[pr] = wsel;
         }
+        // LDS: xs [min(d, 64 kW2 kB2) bf16] | Xs [64 floats] | red [kW2][2][32] | wide-path totals
+        const int XE = min(a.d, 64 * kW2 * kB2);
+        float *Xs = reinterpret_cast<float *>(smem + sizeof(uint16_t) * XE);
+        float(*red)[2][32] = reinterpret_cast<float(*)[2][32]>(smem + sizeof(uint16_t) * XE + sizeof(float) * 64);
         if (narrow && tid < G * 8) *reinterpret_cast<u32x4_t *>(xs + 8 * tid) = xv;
-        float(*red)[2][32] = reinterpret_cast<float(*)[2][32]>(smem + sizeof(uint16_t) * a.d);
+        if (narrow && tid < G) Xs[tid] = xgv;
         const size_t cstride = (size_t)a.I * a.d / 2, sstride = (size_t)a.I * G;
         const uint8_t *Wg = static_cast<const uint8_t *>(a.gate.codes) + e * cstride;
         const uint8_t *Wu = static_cast<const uint8_t *>(a.up.codes) + e * cstride;
         uint16_t *hout = a.h_r + (size_t)pr * a.I + jb * 32;
         if (narrow) {
             gateup_piece<kW2, kB2>(a.x + (size_t)t * a.d, Wg, Wu, a.gate.sb + e * sstride, a.up.sb + e * sstride, G,
-                                   jb, 0, G, xs, red, nullptr, nullptr, hout, true);
+                                   jb, 0, G, xs, Xs, red, nullptr, nullptr, hout, true, a.hs + (size_t)pr * JB + jb);
         } else {
             // wide inputs: kW2 * kB2 groups at a time, partial sums carried through red
             float *acc = reinterpret_cast<float *>(red);   // reuse: [2][32] totals after each batch
             float tg = 0.0f, tu = 0.0f;
             for (int g0 = 0; g0 < G; g0 += kW2 * kB2) {
                 gateup_piece<kW2, kB2>(a.x + (size_t)t * a.d, Wg, Wu, a.gate.sb + e * sstride,
-                                       a.up.sb + e * sstride, G, jb, g0, min(G, g0 + kW2 * kB2), xs, red,
+                                       a.up.sb + e * sstride, G, jb, g0, min(G, g0 + kW2 * kB2), xs, Xs, red,
                                        acc + 2 * 64 * kW2, acc + 2 * 64 * kW2 + 32, nullptr);
                 __syncthreads();
                 if (tid < 32) {
@@ -461,7 +500,20 @@ __global__ __launch_bounds__(64 * kW2) void k_dec_stage2(DecArgs a) {
                 }
                 __syncthreads();
             }
-            if (tid < 32) hout[tid] = (uint16_t)f32_to_f16_sat(gelu_tanh_f32(tg) * tu);
+            float hv = 0.0f;
+            if (tid < 32) {
+                const uint32_t hb = f32_to_f16_sat(gelu_tanh_f32(tg) * tu);
+                hout[tid] = (uint16_t)hb;
+                hv = f16_to_f32(hb);
+            }
+            if (wave == 0) {
+                hv += __shfl_xor(hv, 16);
+                hv += __shfl_xor(hv, 8);
+                hv += __shfl_xor(hv, 4);
+                hv += __shfl_xor(hv, 2);
+                hv += __shfl_xor(hv, 1);
+                if (lane == 0) a.hs[(size_t)pr * JB + jb] = hv;
+            }
         }
         return;
     }
@@ -483,7 +535,7 @@ __global__ __launch_bounds__(64 * kW2) void k_dec_stage2(DecArgs a) {
     form_h<cdiv_c(64 * kGPS, 64 * kW2)>(a.gus + (size_t)t * a.KSd * 2 * a.Is, a.KSd, a.Is, 64 * g0, 64 * (g1 - g0),
                                         hl, tid, 64 * kW2);
     __syncthreads();
-    const float rsum = down_compute(r, hl + 64 * (wg0 - g0), wg0, wg1);
+    const float rsum = down_compute(r, hl + 64 * (wg0 - g0), nullptr, wg0, wg1);
     if (lane < 32) part[wave * 32 + lane] = rsum;
     __syncthreads();
     if (tid < 32) {
@@ -503,6 +555,7 @@ __global__ __launch_bounds__(64 * MAXW) void k_dec_stage3(DecArgs a) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     uint16_t *hl = reinterpret_cast<uint16_t *>(smem);                              // [k][I]
     float *part = reinterpret_cast<float *>(smem + sizeof(uint16_t) * a.k * a.I);  // [k][32]
+    float *Hs = part + a.k * 32;                                                    // [k][I/64]
     const int pr = t * a.k + wave;
     const int e = a.idx[pr];
     // loads that do not depend on the expert go out first: the slot's h, and (first 32
@@ -514,6 +567,10 @@ __global__ __launch_bounds__(64 * MAXW) void k_dec_stage3(DecArgs a) {
         const int i = lane + 64 * c;
         hv[c] = i < a.I / 8 ? ld16(a.h_r + (size_t)pr * a.I + 8 * i) : u32x4_t{0u, 0u, 0u, 0u};
     }
+    // group sums of the slot's h from the 32-value sums its gate/up units wrote
+    float hg = 0.0f;
+    if (lane < GI && GI <= 64)
+        hg = a.hs[(size_t)pr * (2 * GI) + 2 * lane] + a.hs[(size_t)pr * (2 * GI) + 2 * lane + 1];
     constexpr int kSP = 4, kWP = MAXW;
     float shv[kSP], wv[kWP];
     if (tid < 32) {
@@ -531,6 +588,7 @@ __global__ __launch_bounds__(64 * MAXW) void k_dec_stage3(DecArgs a) {
         DTiles r;
         down_load(r, W, S, rb, GI, gb, gb1);
         if (gb == 0) {
+            if (lane < GI && GI <= 64) Hs[wave * GI + lane] = hg;
             if (a.I <= 64 * 8 * kHL) {
 #pragma unroll
                 for (int c = 0; c < kHL; ++c) {
@@ -544,7 +602,7 @@ __global__ __launch_bounds__(64 * MAXW) void k_dec_stage3(DecArgs a) {
             }
         }
         __syncthreads();
-        rsum += down_compute(r, hl + (size_t)wave * a.I + 64 * gb, gb, gb1);
+        rsum += down_compute(r, hl + (size_t)wave * a.I + 64 * gb, GI <= 64 ? Hs + wave * GI + gb : nullptr, gb, gb1);
     }
     if (lane < 32) part[wave * 32 + lane] = rsum;
     __syncthreads();
@@ -592,6 +650,8 @@ DecArgs dec_args(const moe_layer *L, const uint16_t *x, int T, float *y) {
     a.gus = L->ws.dgus;
     a.h_r = L->ws.dh_r;
     a.shp = L->ws.dshp;
+    a.xg = L->ws.dxg;
+    a.hs = L->ws.dhs;
     a.y = y;
     return a;
 }
@@ -599,13 +659,15 @@ DecArgs dec_args(const moe_layer *L, const uint16_t *x, int T, float *y) {
 }  // namespace
 
 size_t dec_stage3_lds(const moe_dims &D) {
-    return sizeof(uint16_t) * D.top_k * D.d_expert + sizeof(float) * D.top_k * 32;
+    return sizeof(uint16_t) * D.top_k * D.d_expert + sizeof(float) * D.top_k * (32 + D.d_expert / 64);
 }
 
 size_t dec_workspace_floats(const moe_dims &D, int max_dec, int which) {
     const size_t KSd = cdiv(D.d_model / 64, kGPS), KSs = cdiv(D.d_shared / 64, kGPS);
     if (which == 0) return (size_t)max_dec * KSd * 2 * D.d_shared;
     if (which == 1) return (size_t)max_dec * D.top_k * D.d_expert / 2;   // fp16 h, in floats
+    if (which == 3) return (size_t)max_dec * (D.d_model / 64);           // x group sums
+    if (which == 4) return (size_t)max_dec * D.top_k * (D.d_expert / 32); // h 32-value sums
     return (size_t)max_dec * KSs * D.d_model;
 }
 
@@ -615,7 +677,7 @@ hipError_t launch_dec_stage1(const moe_layer *L, const uint16_t *x, int T, hipSt
     const int G = D.d_model / 64;
     const int grid = cdiv(D.n_experts, kRW) + T * (D.d_shared / 32) * a.KSd;
     const size_t lds_router = sizeof(float) * kRW * T * G;
-    const size_t lds_gu = sizeof(uint16_t) * 64 * kGPS + sizeof(float) * kPW * 2 * 32;
+    const size_t lds_gu = sizeof(uint16_t) * 64 * kGPS + sizeof(float) * (16 + kPW * 2 * 32);
     hipLaunchKernelGGL(k_dec_stage1, dim3(grid), dim3(64 * kPW), lds_router > lds_gu ? lds_router : lds_gu, s, a);
     return hipGetLastError();
 }
@@ -635,7 +697,7 @@ hipError_t launch_dec_stage2(const moe_layer *L, const uint16_t *x, int T, hipSt
     const DecArgs a = dec_args(L, x, T, nullptr);
     const int grid = T * D.top_k * (D.d_expert / 32) + T * (D.d_model / 32) * a.KSs;
     const size_t lds_gu = sizeof(uint16_t) * (D.d_model < 64 * kW2 * kB2 ? D.d_model : 64 * kW2 * kB2) +
-                          sizeof(float) * (kW2 * 2 * 32 + 2 * 64 * kW2 + 64);
+                          sizeof(float) * (64 + kW2 * 2 * 32 + 2 * 64 * kW2 + 64);
     const size_t lds_sd = sizeof(uint16_t) * 64 * kGPS + sizeof(float) * kW2 * 32;
     const size_t lds = lds_gu > lds_sd ? lds_gu : lds_sd;
     if (D.n_experts <= 128) hipLaunchKernelGGL(k_dec_stage2<2>, dim3(grid), dim3(64 * kW2), lds, s, a);

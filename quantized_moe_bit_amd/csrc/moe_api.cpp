@@ -252,6 +252,8 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.dgus, dec_workspace_floats(D, L->max_dec, 0));
     plan.take(&ws.dh_r, 2 * dec_workspace_floats(D, L->max_dec, 1));
     plan.take(&ws.dshp, dec_workspace_floats(D, L->max_dec, 2));
+    plan.take(&ws.dxg, dec_workspace_floats(D, L->max_dec, 3));
+    plan.take(&ws.dhs, dec_workspace_floats(D, L->max_dec, 4));
     L->ws_bytes = (plan.off + 255) & ~size_t(255);
 
     int dev = 0;
@@ -290,6 +292,8 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     rebase(ws.dgus, base);
     rebase(ws.dh_r, base);
     rebase(ws.dshp, base);
+    rebase(ws.dxg, base);
+    rebase(ws.dhs, base);
     // zero once: padding columns of the split sums rely on it
     err = hipMemset(L->ws_base, 0, L->ws_bytes);
     // derived bias-term tables of the prefill GEMMs (read from the borrowed scale/bias words)

@@ -69,6 +69,8 @@ struct Workspace {
     float *dgus;          // [D, KSd, 2, I_s]   shared gate/up partial sums
     uint16_t *dh_r;       // [D*k, I]           routed hidden activations, fp16 bits
     float *dshp;          // [D, KSs, d]        shared down partial sums
+    float *dxg;           // [D, d/64]          group sums of x
+    float *dhs;           // [D*k, I/32]        sums of 32 consecutive routed h values
 };
 
 struct ProfEvent {

@@ -127,9 +127,9 @@ def main():
     b_token = b_router + b_gateup + b_down
     # algorithmic bytes of each decode launch: weights it streams once
     stage_bytes = {
-        "dec_route_shared": b_router + 2 * qmat_bytes(Is, d, 4),
-        "dec_gateup": k * 2 * qmat_bytes(I, d, 4) + qmat_bytes(d, Is, 4),
-        "dec_down": k * qmat_bytes(d, I, 4),
+        "dec_router": b_router,
+        "dec_gateup": k * 2 * qmat_bytes(I, d, 4) + 2 * qmat_bytes(Is, d, 4),
+        "dec_down": k * qmat_bytes(d, I, 4) + qmat_bytes(d, Is, 4),
     }
     assert sum(stage_bytes.values()) == b_token
     roofline = None

@@ -9,26 +9,26 @@
 //
 // Exact affine split per group (x the 64 inputs of the group):
 //   sum_j x_j (s q_j + b) = 16 s * sum_j x_j (1 + q_j/16) + (b - 16 s) * sum_j x_j.
-// A lane holds half of a group's inputs; it adds 16 s * (its half of the first sum) +
-// (b - 16 s) * (its half of sum x), which is linear, so the halves add up to the exact group
-// term. 1 + q/16 comes from the nibbles with one shift and one and-or; v_dot2_f32_bf16
-// (gate/up, x is bf16) and v_dot2_f32_f16 (down, h is fp16) accumulate in fp32.
+// 1 + q/16 comes from the nibbles with one shift and one and-or; v_dot2_f32_bf16 (gate/up,
+// x is bf16) and v_dot2_f32_f16 (down, h is fp16) accumulate in fp32. The group sums of the
+// inputs are formed once (x: by the router, in its fixed order; h: from 16-value sums the
+// gate/up units write) and enter once per (row, group).
 //
-// Work is cut into many thin units: every projection is split along its input dimension into
-// pieces of kGPS groups, each piece a 256-thread workgroup streaming ~25 KB, and the consumer
-// of a projection adds its partial sums in piece order (fixed order, deterministic).
+// A decode launch moves a few MB of weights; one compute unit streams only some tens of
+// GB/s, so the work of every launch is cut into units of 16 weight rows (half of a 1 KiB
+// 32-row tile) and spread over all compute units. One 16-byte load per lane then covers two
+// input groups: lane l takes row l % 16, input half (l / 16) % 2 and group (l / 32) of the
+// pair; the four lanes of a row are added with two cross-lane steps.
 //
-// Launch 1 (k_dec_stage1): router logits in the fixed fp32 order the oracle uses (one wave
-//   per expert, one lane per input group), and the shared expert's gate/up partial sums (the
-//   shared branch does not depend on routing; Mference "Decode" likewise starts it before
-//   the routed branch).
-// Launch 2 (k_dec_stage2): routed gate/up partial sums per (pair, 32 rows, input piece); each
-//   wave first derives its token's top-k from the logits with a DPP argmax over packed
-//   (logit, index) keys, identical on every wave. Other workgroups: the shared down
-//   projection per (token, 32 rows, input piece), forming h = fp16(gelu(g) * u) for their
-//   piece from the launch-1 partials.
-// Launch 3 (k_dec_stage3): one workgroup per (token, 32 output rows), one wave per routed
-//   slot: h of the slot from the launch-2 partials, the down projection, then
+// Launch A (k_dec_router): router logits in the fixed fp32 order the oracle uses (one wave
+//   per expert, one lane per input group), and the group sums of x.
+// Launch B (k_dec_gateup): one workgroup per (token, routed slot, 16 rows of I) and per
+//   (token, 16 rows of I_s): h = fp16(gelu(gate x) * (up x)) over the whole input. A routed
+//   unit first derives its token's top-k from the logits (each wave, DPP argmax); shared
+//   units do not depend on routing and stream meanwhile (Mference "Decode" likewise starts
+//   the shared branch before the routed one).
+// Launch C (k_dec_down): one workgroup per (token, 16 output rows): one wave per routed slot
+//   (down projection of that slot's h) and a few waves for the shared down projection, then
 //   y = shared + w_0 r_0 + ... + w_{k-1} r_{k-1} in slot order (Mference "Decode", cb2;
 //   TinyTitan architecture "Invariants": fixed reduction order).
 #include "device_common.h"
@@ -38,12 +38,10 @@ namespace qmoe {
 namespace {
 
 constexpr int kRW = 4;      // router experts (waves) per workgroup
-constexpr int kPW = 4;      // waves per partial-sum workgroup
-constexpr int kPB = cdiv_c(kGPS, kPW);   // groups per wave in a piece
-constexpr int kW2 = 8;      // waves per launch-2 workgroup
-constexpr int kB2 = 6;      // groups per wave of a routed gate/up unit (kW2 * kB2 >= 48 input groups)
-constexpr uint32_t kOneBf16x2 = 0x3F803F80u;
-constexpr uint32_t kOneF16x2 = 0x3C003C00u;
+constexpr int kBW = 8;      // waves per gate/up workgroup
+constexpr int kMPB = 3;     // group pairs a gate/up wave loads before computing
+constexpr int kMPC = 6;     // group pairs a down wave loads before computing
+constexpr int kXC = 2;      // 16-byte x chunks per gate/up thread: d <= 64 kBW * 8 * kXC
 
 // ----------------------------------------------------------------------------- router
 // The wave's expert e; lane g handles input group g (and g + 64, ... for d > 4096).
@@ -84,232 +82,6 @@ __device__ __forceinline__ void router_wave(const uint16_t *__restrict__ x, int 
             if (xg_out) xg_out[t * G + g] = X;
         }
     }
-}
-
-// ----------------------------------------------------------------------------- gate/up piece
-// Partial gate and up sums of 32 rows (block jb) over input groups [g0, g1) (at most kGPS)
-// for one token, x of those groups staged in LDS (xs, indexed from g0). Wave w takes groups
-// g0 + w, g0 + w + kPW, ...; the four waves' sums are added in wave order.
-template <int PB>
-struct GUTiles {
-    u32x4_t wg[PB], wu[PB];
-    uint32_t sbg[PB], sbu[PB];
-};
-
-template <int NW, int PB>
-__device__ __forceinline__ void gu_load(GUTiles<PB> &r, const uint8_t *Wg, const uint8_t *Wu, const uint32_t *Sg,
-                                        const uint32_t *Su, int G, int jb, int g0, int g1) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 31;
-    const size_t tb = (size_t)jb * G;
-#pragma unroll
-    for (int b = 0; b < PB; ++b) {
-        const int g = g0 + wave + b * NW;
-        if (g < g1) {
-            r.wg[b] = ld16(Wg + (tb + g) * 1024 + lane * 16);
-            r.wu[b] = ld16(Wu + (tb + g) * 1024 + lane * 16);
-            r.sbg[b] = Sg[(tb + g) * 32 + n];
-            r.sbu[b] = Su[(tb + g) * 32 + n];
-        }
-    }
-}
-
-template <int NW, int PB>
-__device__ __forceinline__ void gu_compute(const GUTiles<PB> &r, const uint16_t *xs, const float *Xs, int g0, int g1,
-                                           float &accg, float &accu) {
-    const int wave = threadIdx.x >> 6, half = (threadIdx.x >> 5) & 1;
-#pragma unroll
-    for (int b = 0; b < PB; ++b) {
-        const int g = g0 + wave + b * NW;
-        if (g < g1) {
-            float ag = 0.0f, au = 0.0f;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xs + 64 * (g - g0) + 16 * s + 8 * half);
-                ag = dot2_bf16(xv[0], nib_pair<0>(r.wg[b][s]), ag);
-                ag = dot2_bf16(xv[1], nib_pair<1>(r.wg[b][s]), ag);
-                ag = dot2_bf16(xv[2], nib_pair<2>(r.wg[b][s]), ag);
-                ag = dot2_bf16(xv[3], nib_pair<3>(r.wg[b][s]), ag);
-                au = dot2_bf16(xv[0], nib_pair<0>(r.wu[b][s]), au);
-                au = dot2_bf16(xv[1], nib_pair<1>(r.wu[b][s]), au);
-                au = dot2_bf16(xv[2], nib_pair<2>(r.wu[b][s]), au);
-                au = dot2_bf16(xv[3], nib_pair<3>(r.wu[b][s]), au);
-            }
-            // the (b - 16 s) X_g term once per group (lanes of half 0)
-            const float xsum = half == 0 ? Xs[g - g0] : 0.0f;
-            const float s16g = 16.0f * bf16_to_f32(r.sbg[b] & 0xFFFFu);
-            const float s16u = 16.0f * bf16_to_f32(r.sbu[b] & 0xFFFFu);
-            accg = fmaf(s16g, ag, fmaf(bf16_to_f32(r.sbg[b] >> 16) - s16g, xsum, accg));
-            accu = fmaf(s16u, au, fmaf(bf16_to_f32(r.sbu[b] >> 16) - s16u, xsum, accu));
-        }
-    }
-}
-
-// One gate/up piece over input groups [g0, g1) (at most NW * PB) with NW waves: loads tiles,
-// stages x[g0:g1] of token row xrow, computes, adds the waves' sums in wave order, and either
-// writes the 32 partial gate and up sums to out_g[n], out_u[n] (hout == nullptr) or, when the
-// piece covers the whole input, h = fp16(gelu(g) * u) to hout[n] (and, with hsum_out, the
-// sum of those 32 values to *hsum_out). With x_staged, xs and Xs already hold x[g0:g1] and
-// its group sums (written before the call; the call's barrier publishes them); otherwise
-// they are staged here. LDS: xs (NW * PB * 64 bf16), Xs (NW * PB floats), red.
-template <int NW, int PB>
-__device__ __forceinline__ void gateup_piece(const uint16_t *xrow, const uint8_t *Wg, const uint8_t *Wu,
-                                             const uint32_t *Sg, const uint32_t *Su, int G, int jb, int g0, int g1,
-                                             uint16_t *xs, float *Xs, float (*red)[2][32], float *out_g, float *out_u,
-                                             uint16_t *hout, bool x_staged = false, float *hsum_out = nullptr) {
-    static_assert(PB <= 8, "one 16-byte x chunk per thread");
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 31;
-    GUTiles<PB> r;
-    gu_load<NW, PB>(r, Wg, Wu, Sg, Su, G, jb, g0, g1);
-    if (!x_staged) {
-        // stage x[g0:g1] and its group sums (eight consecutive threads per group)
-        const int nch = (g1 - g0) * 8;
-        float ps = 0.0f;
-        if (tid < nch) {
-            const u32x4_t v = ld16(xrow + 64 * g0 + 8 * tid);
-            *reinterpret_cast<u32x4_t *>(xs + 8 * tid) = v;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) ps += bf16_to_f32(v[w] & 0xFFFFu) + bf16_to_f32(v[w] >> 16);
-        }
-        ps += __shfl_xor(ps, 1);
-        ps += __shfl_xor(ps, 2);
-        ps += __shfl_xor(ps, 4);
-        if (tid < nch && (tid & 7) == 0) Xs[tid >> 3] = ps;
-    }
-    __syncthreads();
-    float accg = 0.0f, accu = 0.0f;
-    gu_compute<NW, PB>(r, xs, Xs, g0, g1, accg, accu);
-    accg += __shfl_xor(accg, 32);
-    accu += __shfl_xor(accu, 32);
-    if (lane < 32) {
-        red[wave][0][n] = accg;
-        red[wave][1][n] = accu;
-    }
-    __syncthreads();
-    if (tid < 32) {
-        float gv = 0.0f, uv = 0.0f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            gv += red[w][0][tid];
-            uv += red[w][1][tid];
-        }
-        if (hout) {
-            const uint32_t hb = f32_to_f16_sat(gelu_tanh_f32(gv) * uv);
-            hout[tid] = (uint16_t)hb;
-            if (hsum_out) red[0][0][tid] = f16_to_f32(hb);
-        } else {
-            out_g[tid] = gv;
-            out_u[tid] = uv;
-        }
-    }
-    if (hout && hsum_out && wave == 0) {
-        // sum of the 32 stored h values (after every lane of wave 0 has read red above)
-        float hs = lane < 32 ? red[0][0][lane] : 0.0f;
-        hs += __shfl_xor(hs, 16);
-        hs += __shfl_xor(hs, 8);
-        hs += __shfl_xor(hs, 4);
-        hs += __shfl_xor(hs, 2);
-        hs += __shfl_xor(hs, 1);
-        if (lane == 0) *hsum_out = hs;
-    }
-}
-
-// h = fp16(gelu(g) * u) for inputs [j0, j0 + nj) of a projection whose gate/up partial sums
-// (KS pieces) are at part[(ks * 2 + {0: gate, 1: up}) * J + j]; pieces added in order. Each
-// thread handles at most NPT inputs; for KS <= kKSFast every partial is loaded before any is
-// used (one round trip), otherwise piece by piece.
-constexpr int kKSFast = 4;
-template <int NPT>
-__device__ __forceinline__ void form_h(const float *part, int KS, int J, int j0, int nj, uint16_t *hl, int tid,
-                                       int nthreads) {
-    float gv[NPT], uv[NPT];
-    if (KS <= kKSFast) {
-        float gp[kKSFast][NPT], up[kKSFast][NPT];
-#pragma unroll
-        for (int ks = 0; ks < kKSFast; ++ks)
-#pragma unroll
-            for (int i = 0; i < NPT; ++i) {
-                const int j = tid + i * nthreads;
-                const bool ok = ks < KS && j < nj;
-                gp[ks][i] = ok ? part[(size_t)(ks * 2) * J + j0 + j] : 0.0f;
-                up[ks][i] = ok ? part[(size_t)(ks * 2 + 1) * J + j0 + j] : 0.0f;
-            }
-#pragma unroll
-        for (int i = 0; i < NPT; ++i) {
-            gv[i] = gp[0][i];
-            uv[i] = up[0][i];
-#pragma unroll
-            for (int ks = 1; ks < kKSFast; ++ks) {
-                gv[i] += gp[ks][i];
-                uv[i] += up[ks][i];
-            }
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < NPT; ++i) gv[i] = uv[i] = 0.0f;
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int i = 0; i < NPT; ++i) {
-                const int j = tid + i * nthreads;
-                if (j < nj) {
-                    gv[i] += part[(size_t)(ks * 2) * J + j0 + j];
-                    uv[i] += part[(size_t)(ks * 2 + 1) * J + j0 + j];
-                }
-            }
-    }
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-        const int j = tid + i * nthreads;
-        if (j < nj) hl[j] = (uint16_t)f32_to_f16_sat(gelu_tanh_f32(gv[i]) * uv[i]);
-    }
-}
-
-// ----------------------------------------------------------------------------- down part
-// One wave: 32 output rows (block rb) of a down projection over input groups [g0, g1)
-// (at most kDecodeChunkGroups) of its fp16 input h, staged in LDS at hl (indexed from g0).
-struct DTiles {
-    u32x4_t w4[kDecodeChunkGroups];
-    uint32_t sbw[kDecodeChunkGroups];
-};
-
-__device__ __forceinline__ void down_load(DTiles &r, const uint8_t *W, const uint32_t *S, int rb, int Gk, int g0,
-                                          int g1) {
-    const int lane = threadIdx.x & 63, n = lane & 31;
-    const size_t tb = (size_t)rb * Gk;
-#pragma unroll
-    for (int b = 0; b < kDecodeChunkGroups; ++b)
-        if (g0 + b < g1) {
-            r.w4[b] = ld16(W + (tb + g0 + b) * 1024 + lane * 16);
-            r.sbw[b] = S[(tb + g0 + b) * 32 + n];
-        }
-}
-
-// Hs: group sums of h (indexed from g0), or nullptr to form them from hl here.
-__device__ __forceinline__ float down_compute(const DTiles &r, const uint16_t *hl, const float *Hs, int g0, int g1) {
-    const int half = (threadIdx.x >> 5) & 1;
-    float acc = 0.0f;
-#pragma unroll
-    for (int b = 0; b < kDecodeChunkGroups; ++b)
-        if (g0 + b < g1) {
-            float a = 0.0f, hsum = 0.0f;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const u32x4_t hv = *reinterpret_cast<const u32x4_t *>(hl + 64 * b + 16 * s + 8 * half);
-                a = dot2_f16(hv[0], nib_pair_f16<0>(r.w4[b][s]), a);
-                a = dot2_f16(hv[1], nib_pair_f16<1>(r.w4[b][s]), a);
-                a = dot2_f16(hv[2], nib_pair_f16<2>(r.w4[b][s]), a);
-                a = dot2_f16(hv[3], nib_pair_f16<3>(r.w4[b][s]), a);
-                if (!Hs) {
-                    hsum = dot2_f16(hv[0], kOneF16x2, hsum);
-                    hsum = dot2_f16(hv[1], kOneF16x2, hsum);
-                    hsum = dot2_f16(hv[2], kOneF16x2, hsum);
-                    hsum = dot2_f16(hv[3], kOneF16x2, hsum);
-                }
-            }
-            if (Hs) hsum = half == 0 ? Hs[b] : 0.0f;
-            const float s16 = 16.0f * bf16_to_f32(r.sbw[b] & 0xFFFFu);
-            acc = fmaf(s16, a, fmaf(bf16_to_f32(r.sbw[b] >> 16) - s16, hsum, acc));
-        }
-    return acc + __shfl_xor(acc, 32);
 }
 
 // ----------------------------------------------------------------------------- top-k
@@ -392,10 +164,128 @@ __device__ __forceinline__ int wave_topk(const float *__restrict__ l, int E, int
     return target_e;
 }
 
+// ----------------------------------------------------------------------------- 16-row units
+// Lane roles for 16 rows (block hb of the 32-row tile rb): row l % 16, input half (l/16) % 2,
+// group 2p + l/32 of pair p.
+struct Lane16 {
+    int row, khalf, gsel;
+};
+__device__ __forceinline__ Lane16 lane16() {
+    const int l = threadIdx.x & 63;
+    return Lane16{l & 15, (l >> 4) & 1, l >> 5};
+}
+// Within the tiles of row block rb (starting at W + rb * G * 1024, scale/bias words at
+// S + rb * G * 32), this lane's 16 bytes of group g sit at g * 1024 + code_lane(hb) and its
+// scale/bias word at index g * 32 + sb_lane(hb).
+__device__ __forceinline__ uint32_t code_lane(int hb, const Lane16 &L) { return (32 * L.khalf + 16 * hb + L.row) * 16; }
+__device__ __forceinline__ uint32_t sb_lane(int hb, const Lane16 &L) { return 16 * hb + L.row; }
+// sum of the four lanes holding one row (lanes l, l^16, l^32, l^48); result in lanes 0..15
+__device__ __forceinline__ float row_sum16(float v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Gate and up sums of 16 rows over the group pairs p = wave, wave + NW, ... (< cdiv(G, 2)),
+// x (bf16) and its group sums Xs in LDS, MP pairs per batch. Loads are unconditional
+// (pairs past the input re-read a valid group and are masked), so a batch stays in flight
+// until its first use.
+template <int NW, int MP>
+__device__ __forceinline__ void gateup16(const uint8_t *Wg, const uint8_t *Wu, const uint32_t *Sg, const uint32_t *Su,
+                                         int rb, int hb, int G, const uint16_t *xs, const float *Xs, float &accg,
+                                         float &accu) {
+    const int wave = threadIdx.x >> 6;
+    const Lane16 L = lane16();
+    const int P = cdiv(G, 2);
+    Wg += (size_t)rb * G * 1024;
+    Wu += (size_t)rb * G * 1024;
+    Sg += (size_t)rb * G * 32;
+    Su += (size_t)rb * G * 32;
+    const uint32_t co = code_lane(hb, L), so = sb_lane(hb, L);
+    for (int i0 = 0; wave + NW * i0 < P; i0 += MP) {
+        u32x4_t wg[MP], wu[MP];
+        uint32_t sg[MP], su[MP];
+#pragma unroll
+        for (int i = 0; i < MP; ++i) {
+            const int g = min(2 * (wave + NW * (i0 + i)) + L.gsel, G - 1);
+            wg[i] = ld16(Wg + ((uint32_t)g * 1024 + co));
+            wu[i] = ld16(Wu + ((uint32_t)g * 1024 + co));
+            sg[i] = Sg[(uint32_t)g * 32 + so];
+            su[i] = Su[(uint32_t)g * 32 + so];
+        }
+#pragma unroll
+        for (int i = 0; i < MP; ++i) {
+            const int g = 2 * (wave + NW * (i0 + i)) + L.gsel;
+            const int gc = min(g, G - 1);
+            float ag = 0.0f, au = 0.0f;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xs + 64 * gc + 16 * s + 8 * L.khalf);
+                ag = dot2_bf16(xv[0], nib_pair<0>(wg[i][s]), ag);
+                ag = dot2_bf16(xv[1], nib_pair<1>(wg[i][s]), ag);
+                ag = dot2_bf16(xv[2], nib_pair<2>(wg[i][s]), ag);
+                ag = dot2_bf16(xv[3], nib_pair<3>(wg[i][s]), ag);
+                au = dot2_bf16(xv[0], nib_pair<0>(wu[i][s]), au);
+                au = dot2_bf16(xv[1], nib_pair<1>(wu[i][s]), au);
+                au = dot2_bf16(xv[2], nib_pair<2>(wu[i][s]), au);
+                au = dot2_bf16(xv[3], nib_pair<3>(wu[i][s]), au);
+            }
+            const float on = g < G ? 1.0f : 0.0f;
+            const float X = Xs[gc] * (L.khalf == 0 ? 1.0f : 0.0f);   // the X_g term once per (row, group)
+            const float s16g = 16.0f * bf16_to_f32(sg[i] & 0xFFFFu), s16u = 16.0f * bf16_to_f32(su[i] & 0xFFFFu);
+            accg = fmaf(on, fmaf(s16g, ag, (bf16_to_f32(sg[i] >> 16) - s16g) * X), accg);
+            accu = fmaf(on, fmaf(s16u, au, (bf16_to_f32(su[i] >> 16) - s16u) * X), accu);
+        }
+    }
+}
+
+// Down sum of 16 rows over group pairs p = p0, p0 + PS, ... (< cdiv(G, 2)) of an fp16 input h
+// (LDS, with its group sums Hs), MP pairs per batch.
+template <int MP>
+__device__ __forceinline__ float down16(const uint8_t *W, const uint32_t *S, int rb, int hb, int G, int p0, int PS,
+                                        const uint16_t *hl, const float *Hs) {
+    const Lane16 L = lane16();
+    const int P = cdiv(G, 2);
+    W += (size_t)rb * G * 1024;
+    S += (size_t)rb * G * 32;
+    const uint32_t co = code_lane(hb, L), so = sb_lane(hb, L);
+    float acc = 0.0f;
+    for (int i0 = 0; p0 + PS * i0 < P; i0 += MP) {
+        u32x4_t w[MP];
+        uint32_t sb[MP];
+#pragma unroll
+        for (int i = 0; i < MP; ++i) {
+            const int g = min(2 * (p0 + PS * (i0 + i)) + L.gsel, G - 1);
+            w[i] = ld16(W + ((uint32_t)g * 1024 + co));
+            sb[i] = S[(uint32_t)g * 32 + so];
+        }
+#pragma unroll
+        for (int i = 0; i < MP; ++i) {
+            // keeps the LDS reads of pair i after the arithmetic of pair i - 1 (register use)
+            asm volatile("" ::: "memory");
+            const int g = 2 * (p0 + PS * (i0 + i)) + L.gsel;
+            const int gc = min(g, G - 1);
+            float a = 0.0f;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const u32x4_t hv = *reinterpret_cast<const u32x4_t *>(hl + 64 * gc + 16 * s + 8 * L.khalf);
+                a = dot2_f16(hv[0], nib_pair_f16<0>(w[i][s]), a);
+                a = dot2_f16(hv[1], nib_pair_f16<1>(w[i][s]), a);
+                a = dot2_f16(hv[2], nib_pair_f16<2>(w[i][s]), a);
+                a = dot2_f16(hv[3], nib_pair_f16<3>(w[i][s]), a);
+            }
+            const float on = g < G ? 1.0f : 0.0f;
+            const float H = Hs[gc] * (L.khalf == 0 ? 1.0f : 0.0f);
+            const float s16 = 16.0f * bf16_to_f32(sb[i] & 0xFFFFu);
+            acc = fmaf(on, fmaf(s16, a, (bf16_to_f32(sb[i] >> 16) - s16) * H), acc);
+        }
+    }
+    return acc;
+}
+
 struct DecArgs {
     const uint16_t *x;
     int T, d, E, k, I, Is;
-    int KSd, KSs;           // input pieces of the d-wide gate/up inputs and of the shared down input
     const uint8_t *rq;
     const uint32_t *rsb;
     const float *logit_bias;
@@ -403,223 +293,180 @@ struct DecArgs {
     int32_t *idx;
     float *wts;
     moe_qmat gate, up, down, sh_gate, sh_up, sh_down;
-    float *gus;             // [T][KSd][2][I_s] shared gate/up partials
-    uint16_t *h_r;          // [T*k][I]         routed hidden activations (fp16 bits)
-    float *shp;             // [T][KSs][d]      shared down partials
     float *xg;              // [T][d/64]        group sums of x (router, fixed order)
-    float *hs;              // [T*k][I/32]      sums of 32 consecutive routed h values
+    uint16_t *h_r;          // [T*k][I]         routed hidden activations (fp16 bits)
+    uint16_t *h_s;          // [T][I_s]         shared hidden activations (fp16 bits)
+    float *hs_r;            // [T*k][I/16]      sums of 16 consecutive routed h values
+    float *hs_s;            // [T][I_s/16]      sums of 16 consecutive shared h values
     float *y;
 };
 
-// grid: ceil(E / kRW) router workgroups + T * (I_s / 32) * KSd shared gate/up pieces; block 256
-__global__ __launch_bounds__(64 * kPW) void k_dec_stage1(DecArgs a) {
+// ----------------------------------------------------------------------------- launch A
+// grid: ceil(E / kRW); block 64 * kRW; LDS kRW * T * (d/64) floats
+__global__ __launch_bounds__(64 * kRW) void k_dec_router(DecArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int RW = cdiv(a.E, kRW);
     const int G = a.d / 64;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    if ((int)blockIdx.x < RW) {
-        float *Ps = reinterpret_cast<float *>(smem);     // [kRW][T][G]
-        const int e = blockIdx.x * kRW + wave;
-        float *P = Ps + (size_t)wave * a.T * G;
-        if (e < a.E) router_wave(a.x, a.T, a.d, e, a.rq, a.rsb, P, e == 0 ? a.xg : nullptr);
-        __syncthreads();
-        if (e < a.E && lane < a.T) {
+    float *Ps = reinterpret_cast<float *>(smem);     // [kRW][T][G]
+    const int e = blockIdx.x * kRW + wave;
+    float *P = Ps + (size_t)wave * a.T * G;
+    if (e < a.E) router_wave(a.x, a.T, a.d, e, a.rq, a.rsb, P, e == 0 ? a.xg : nullptr);
+    __syncthreads();
+    if (e < a.E && lane < a.T) {
 #pragma clang fp contract(off)
-            float L = 0.0f;
-            for (int g = 0; g < G; ++g) L = L + P[lane * G + g];
-            if (a.logit_bias) L = L + a.logit_bias[e];
-            a.logits[(size_t)lane * a.E + e] = L;
-        }
-        return;
+        float L = 0.0f;
+        for (int g = 0; g < G; ++g) L = L + P[lane * G + g];
+        if (a.logit_bias) L = L + a.logit_bias[e];
+        a.logits[(size_t)lane * a.E + e] = L;
     }
-    uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
-    float *Xs = reinterpret_cast<float *>(smem + sizeof(uint16_t) * 64 * kGPS);
-    float(*red)[2][32] = reinterpret_cast<float(*)[2][32]>(smem + sizeof(uint16_t) * 64 * kGPS + sizeof(float) * 16);
-    const int JBs = a.Is / 32;
-    int u = blockIdx.x - RW;
-    const int ks = u % a.KSd;
-    u /= a.KSd;
-    const int jb = u % JBs, t = u / JBs;
-    const int g0 = ks * kGPS, g1 = min(G, g0 + kGPS);
-    float *out = a.gus + ((size_t)t * a.KSd + ks) * 2 * a.Is + jb * 32;
-    gateup_piece<kPW, kPB>(a.x + (size_t)t * a.d, static_cast<const uint8_t *>(a.sh_gate.codes),
-                           static_cast<const uint8_t *>(a.sh_up.codes), a.sh_gate.sb, a.sh_up.sb, G, jb, g0, g1, xs,
-                           Xs, red, out, out + a.Is, nullptr);
 }
 
-// grid: T * k * (I / 32) routed gate/up units + T * (d / 32) * KSs shared down pieces;
-// block 64 * kW2
+// ----------------------------------------------------------------------------- launch B
+// grid: T * k * (I / 16) routed units, then T * (I_s / 16) shared units; block 64 * kBW.
+// LDS: x [d bf16] | Xs [d/64 floats] | red [kBW][2][16]
 template <int kPer>
-__global__ __launch_bounds__(64 * kW2) void k_dec_stage2(DecArgs a) {
+__global__ __launch_bounds__(64 * kBW) void k_dec_gateup(DecArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int G = a.d / 64, JB = a.I / 32;
+    const int G = a.d / 64;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int nR = a.T * a.k * JB;
-    if ((int)blockIdx.x < nR) {
-        const int jb = blockIdx.x % JB, pr = blockIdx.x / JB, t = pr / a.k, slot = pr % a.k;
-        uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
-        // the token's x is fetched while the selection is derived
-        const bool narrow = G <= kW2 * kB2;
-        u32x4_t xv = u32x4_t{0u, 0u, 0u, 0u};
-        float xgv = 0.0f;
-        if (narrow && tid < G * 8) xv = ld16(a.x + (size_t)t * a.d + 8 * tid);
-        if (narrow && tid < G) xgv = a.xg[(size_t)t * G + tid];
+    uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
+    float *Xs = reinterpret_cast<float *>(smem + sizeof(uint16_t) * a.d);
+    float(*red)[2][16] = reinterpret_cast<float(*)[2][16]>(smem + sizeof(uint16_t) * a.d + sizeof(float) * G);
+    const int JBr = a.I / 16, JBs = a.Is / 16;
+    const int nR = a.T * a.k * JBr;
+    const bool routed = (int)blockIdx.x < nR;
+    int t, jb, pr = 0;
+    if (routed) {
+        jb = blockIdx.x % JBr;
+        pr = blockIdx.x / JBr;
+        t = pr / a.k;
+    } else {
+        const int u = blockIdx.x - nR;
+        jb = u % JBs;
+        t = u / JBs;
+    }
+    // the token's x and group sums, fetched before any selection
+    const uint16_t *xrow = a.x + (size_t)t * a.d;
+    u32x4_t xv[kXC];
+#pragma unroll
+    for (int c = 0; c < kXC; ++c) xv[c] = ld16(xrow + 8 * min(tid + 64 * kBW * c, a.d / 8 - 1));
+    const float xgv = a.xg[(size_t)t * G + min(tid, G - 1)];
+
+    const moe_qmat *mg = &a.sh_gate, *mu = &a.sh_up;
+    size_t cbase = 0, sbase = 0;
+    if (routed) {
         // every wave derives the token's selection itself; one unit of the pair records it
+        const int slot = pr % a.k;
         const bool record = (jb == 0 && wave == 0);
         float wsel;
-        const int e = wave_topk<kPer>(a.logits + (size_t)t * a.E, a.E, a.k, slot, record, wsel);
+        const int e = __builtin_amdgcn_readfirstlane(wave_topk<kPer>(a.logits + (size_t)t * a.E, a.E, a.k, slot, record, wsel));
         if (record && lane == 0) {
             a.idx[pr] = e;
             a.wts[pr] = wsel;
         }
-        // LDS: xs [min(d, 64 kW2 kB2) bf16] | Xs [64 floats] | red [kW2][2][32] | wide-path totals
-        const int XE = min(a.d, 64 * kW2 * kB2);
-        float *Xs = reinterpret_cast<float *>(smem + sizeof(uint16_t) * XE);
-        float(*red)[2][32] = reinterpret_cast<float(*)[2][32]>(smem + sizeof(uint16_t) * XE + sizeof(float) * 64);
-        if (narrow && tid < G * 8) *reinterpret_cast<u32x4_t *>(xs + 8 * tid) = xv;
-        if (narrow && tid < G) Xs[tid] = xgv;
-        const size_t cstride = (size_t)a.I * a.d / 2, sstride = (size_t)a.I * G;
-        const uint8_t *Wg = static_cast<const uint8_t *>(a.gate.codes) + e * cstride;
-        const uint8_t *Wu = static_cast<const uint8_t *>(a.up.codes) + e * cstride;
-        uint16_t *hout = a.h_r + (size_t)pr * a.I + jb * 32;
-        if (narrow) {
-            gateup_piece<kW2, kB2>(a.x + (size_t)t * a.d, Wg, Wu, a.gate.sb + e * sstride, a.up.sb + e * sstride, G,
-                                   jb, 0, G, xs, Xs, red, nullptr, nullptr, hout, true, a.hs + (size_t)pr * JB + jb);
-        } else {
-            // wide inputs: kW2 * kB2 groups at a time, partial sums carried through red
-            float *acc = reinterpret_cast<float *>(red);   // reuse: [2][32] totals after each batch
-            float tg = 0.0f, tu = 0.0f;
-            for (int g0 = 0; g0 < G; g0 += kW2 * kB2) {
-                gateup_piece<kW2, kB2>(a.x + (size_t)t * a.d, Wg, Wu, a.gate.sb + e * sstride,
-                                       a.up.sb + e * sstride, G, jb, g0, min(G, g0 + kW2 * kB2), xs, Xs, red,
-                                       acc + 2 * 64 * kW2, acc + 2 * 64 * kW2 + 32, nullptr);
-                __syncthreads();
-                if (tid < 32) {
-                    tg += acc[2 * 64 * kW2 + tid];
-                    tu += acc[2 * 64 * kW2 + 32 + tid];
-                }
-                __syncthreads();
-            }
-            float hv = 0.0f;
-            if (tid < 32) {
-                const uint32_t hb = f32_to_f16_sat(gelu_tanh_f32(tg) * tu);
-                hout[tid] = (uint16_t)hb;
-                hv = f16_to_f32(hb);
-            }
-            if (wave == 0) {
-                hv += __shfl_xor(hv, 16);
-                hv += __shfl_xor(hv, 8);
-                hv += __shfl_xor(hv, 4);
-                hv += __shfl_xor(hv, 2);
-                hv += __shfl_xor(hv, 1);
-                if (lane == 0) a.hs[(size_t)pr * JB + jb] = hv;
-            }
-        }
-        return;
+        mg = &a.gate;
+        mu = &a.up;
+        cbase = (size_t)e * a.I * a.d / 2;
+        sbase = (size_t)e * a.I * G;
     }
-    // shared down piece: (token, 32 output rows, input groups [g0, g1) of I_s)
-    const int RB = a.d / 32, GIs = a.Is / 64;
-    int u = blockIdx.x - nR;
-    const int ks = u % a.KSs;
-    u /= a.KSs;
-    const int rb = u % RB, t = u / RB;
-    const int g0 = ks * kGPS, g1 = min(GIs, g0 + kGPS);
-    uint16_t *hl = reinterpret_cast<uint16_t *>(smem);                              // [kGPS * 64]
-    float *part = reinterpret_cast<float *>(smem + sizeof(uint16_t) * 64 * kGPS);   // [kW2][32]
-    // wave w takes a contiguous sub-range of at most kSB groups
-    constexpr int kSB = cdiv_c(kGPS, kW2);
-    const int wg0 = min(g1, g0 + wave * kSB), wg1 = min(g1, wg0 + kSB);
-    const uint8_t *W = static_cast<const uint8_t *>(a.sh_down.codes);
-    DTiles r;
-    down_load(r, W, a.sh_down.sb, rb, GIs, wg0, wg1);
-    form_h<cdiv_c(64 * kGPS, 64 * kW2)>(a.gus + (size_t)t * a.KSd * 2 * a.Is, a.KSd, a.Is, 64 * g0, 64 * (g1 - g0),
-                                        hl, tid, 64 * kW2);
-    __syncthreads();
-    const float rsum = down_compute(r, hl + 64 * (wg0 - g0), nullptr, wg0, wg1);
-    if (lane < 32) part[wave * 32 + lane] = rsum;
-    __syncthreads();
-    if (tid < 32) {
-        float sacc = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kW2; ++w) sacc += part[w * 32 + tid];
-        a.shp[((size_t)t * a.KSs + ks) * a.d + rb * 32 + tid] = sacc;
+    for (int c = 0; c < kXC; ++c) {
+        const int i = tid + 64 * kBW * c;
+        if (i < a.d / 8) *reinterpret_cast<u32x4_t *>(xs + 8 * i) = xv[c];
+    }
+    if (tid < G) Xs[tid] = xgv;
+    __syncthreads();
+    float accg = 0.0f, accu = 0.0f;
+    gateup16<kBW, kMPB>(static_cast<const uint8_t *>(mg->codes) + cbase,
+                              static_cast<const uint8_t *>(mu->codes) + cbase, mg->sb + sbase, mu->sb + sbase, jb >> 1,
+                              jb & 1, G, xs, Xs, accg, accu);
+    accg = row_sum16(accg);
+    accu = row_sum16(accu);
+    if (lane < 16) {
+        red[wave][0][lane] = accg;
+        red[wave][1][lane] = accu;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        float hv = 0.0f;
+        if (lane < 16) {
+            float gv = 0.0f, uv = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kBW; ++w) {
+                gv += red[w][0][lane];
+                uv += red[w][1][lane];
+            }
+            const uint32_t hb = f32_to_f16_sat(gelu_tanh_f32(gv) * uv);
+            if (routed) a.h_r[(size_t)pr * a.I + 16 * jb + lane] = (uint16_t)hb;
+            else a.h_s[(size_t)t * a.Is + 16 * jb + lane] = (uint16_t)hb;
+            hv = f16_to_f32(hb);
+        }
+        hv += __shfl_xor(hv, 8);
+        hv += __shfl_xor(hv, 4);
+        hv += __shfl_xor(hv, 2);
+        hv += __shfl_xor(hv, 1);
+        if (lane == 0) {
+            if (routed) a.hs_r[(size_t)pr * JBr + jb] = hv;
+            else a.hs_s[(size_t)t * JBs + jb] = hv;
+        }
     }
 }
 
-// grid: T * (d / 32); block 64 * k (k <= MAXW): wave s = routed slot s
-template <int MAXW>
-__global__ __launch_bounds__(64 * MAXW) void k_dec_stage3(DecArgs a) {
+// ----------------------------------------------------------------------------- launch C
+// grid: T * (d / 16); block 64 * NW with NW = min(16, k + 4). Wave s < k: routed slot s. The
+// shared down projection's group pairs go round-robin to waves k..NW-1 (to all waves when
+// k == 16).
+// LDS: h_r of the k slots [k][I] | h_s [I_s] | Hr [k][I/64] | Hsh [I_s/64] | Ws [k] |
+//      part_r [k][16] | part_s [NW][16]
+template <int MAXT>
+__global__ __launch_bounds__(MAXT) void k_dec_down(DecArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int RB = a.d / 32, GI = a.I / 64;
-    const int t = blockIdx.x / RB, rb = blockIdx.x % RB;
+    const int RB = a.d / 16, GI = a.I / 64, GS = a.Is / 64;
+    const int t = blockIdx.x / RB, db = blockIdx.x % RB;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    uint16_t *hl = reinterpret_cast<uint16_t *>(smem);                              // [k][I]
-    float *part = reinterpret_cast<float *>(smem + sizeof(uint16_t) * a.k * a.I);  // [k][32]
-    float *Hs = part + a.k * 32;                                                    // [k][I/64]
-    const int pr = t * a.k + wave;
-    const int e = a.idx[pr];
-    // loads that do not depend on the expert go out first: the slot's h, and (first 32
-    // threads) the shared-expert partial sums and the slot weights of the combine
-    constexpr int kHL = 4;   // h chunks of 16 bytes per lane: I <= 64 * 8 * kHL
-    u32x4_t hv[kHL];
-#pragma unroll
-    for (int c = 0; c < kHL; ++c) {
-        const int i = lane + 64 * c;
-        hv[c] = i < a.I / 8 ? ld16(a.h_r + (size_t)pr * a.I + 8 * i) : u32x4_t{0u, 0u, 0u, 0u};
+    const int NW = blockDim.x >> 6, nth = blockDim.x;
+    const int s0 = NW > a.k ? a.k : 0, SN = NW - s0;   // shared waves [s0, NW)
+    uint16_t *hr = reinterpret_cast<uint16_t *>(smem);
+    uint16_t *hsh = hr + (size_t)a.k * a.I;
+    float *Hr = reinterpret_cast<float *>(hsh + a.Is);
+    float *Hsh = Hr + a.k * GI;
+    float *Ws = Hsh + GS;
+    float *part_r = Ws + a.k;
+    float *part_s = part_r + a.k * 16;
+    // the slot experts, then everything the workgroup reads besides the weights
+    int e = 0;
+    if (wave < a.k) e = __builtin_amdgcn_readfirstlane(a.idx[(size_t)t * a.k + wave]);
+    for (int i = tid; i < a.k * a.I / 8; i += nth)
+        *reinterpret_cast<u32x4_t *>(hr + 8 * i) = ld16(a.h_r + (size_t)t * a.k * a.I + 8 * i);
+    for (int i = tid; i < a.Is / 8; i += nth)
+        *reinterpret_cast<u32x4_t *>(hsh + 8 * i) = ld16(a.h_s + (size_t)t * a.Is + 8 * i);
+    for (int i = tid; i < a.k * GI; i += nth) {
+        const float *q = a.hs_r + (size_t)t * a.k * (a.I / 16) + 4 * i;
+        Hr[i] = (q[0] + q[1]) + (q[2] + q[3]);
     }
-    // group sums of the slot's h from the 32-value sums its gate/up units wrote
-    float hg = 0.0f;
-    if (lane < GI && GI <= 64)
-        hg = a.hs[(size_t)pr * (2 * GI) + 2 * lane] + a.hs[(size_t)pr * (2 * GI) + 2 * lane + 1];
-    constexpr int kSP = 4, kWP = MAXW;
-    float shv[kSP], wv[kWP];
-    if (tid < 32) {
-        const int row = rb * 32 + tid;
-#pragma unroll
-        for (int ks = 0; ks < kSP; ++ks) shv[ks] = ks < a.KSs ? a.shp[((size_t)t * a.KSs + ks) * a.d + row] : 0.0f;
-#pragma unroll
-        for (int s = 0; s < kWP; ++s) wv[s] = s < a.k ? a.wts[(size_t)t * a.k + s] : 0.0f;
+    for (int i = tid; i < GS; i += nth) {
+        const float *q = a.hs_s + (size_t)t * (a.Is / 16) + 4 * i;
+        Hsh[i] = (q[0] + q[1]) + (q[2] + q[3]);
     }
-    const uint8_t *W = static_cast<const uint8_t *>(a.down.codes) + (size_t)e * a.d * a.I / 2;
-    const uint32_t *S = a.down.sb + (size_t)e * a.d * GI;
-    float rsum = 0.0f;
-    for (int gb = 0; gb < GI; gb += kDecodeChunkGroups) {
-        const int gb1 = min(GI, gb + kDecodeChunkGroups);
-        DTiles r;
-        down_load(r, W, S, rb, GI, gb, gb1);
-        if (gb == 0) {
-            if (lane < GI && GI <= 64) Hs[wave * GI + lane] = hg;
-            if (a.I <= 64 * 8 * kHL) {
-#pragma unroll
-                for (int c = 0; c < kHL; ++c) {
-                    const int i = lane + 64 * c;
-                    if (i < a.I / 8) *reinterpret_cast<u32x4_t *>(hl + (size_t)wave * a.I + 8 * i) = hv[c];
-                }
-            } else {
-                for (int i = lane; i < a.I / 8; i += 64)
-                    *reinterpret_cast<u32x4_t *>(hl + (size_t)wave * a.I + 8 * i) =
-                        ld16(a.h_r + (size_t)pr * a.I + 8 * i);
-            }
-        }
-        __syncthreads();
-        rsum += down_compute(r, hl + (size_t)wave * a.I + 64 * gb, GI <= 64 ? Hs + wave * GI + gb : nullptr, gb, gb1);
-    }
-    if (lane < 32) part[wave * 32 + lane] = rsum;
+    if (tid < a.k) Ws[tid] = a.wts[(size_t)t * a.k + tid];
     __syncthreads();
-    if (tid < 32) {
-        const int row = rb * 32 + tid;
+    if (wave < a.k) {
+        const uint8_t *W = static_cast<const uint8_t *>(a.down.codes) + (size_t)e * a.d * a.I / 2;
+        const uint32_t *S = a.down.sb + (size_t)e * a.d * GI;
+        const float r = row_sum16(down16<kMPC>(W, S, db >> 1, db & 1, GI, 0, 1, hr + (size_t)wave * a.I, Hr + wave * GI));
+        if (lane < 16) part_r[wave * 16 + lane] = r;
+    }
+    if (wave >= s0) {
+        const float r = row_sum16(down16<kMPC>(static_cast<const uint8_t *>(a.sh_down.codes), a.sh_down.sb, db >> 1,
+                                               db & 1, GS, wave - s0, SN, hsh, Hsh));
+        if (lane < 16) part_s[wave * 16 + lane] = r;
+    }
+    __syncthreads();
+    if (tid < 16) {
         float out = 0.0f;
-        if (a.KSs <= kSP) {
-#pragma unroll
-            for (int ks = 0; ks < kSP; ++ks)
-                if (ks < a.KSs) out += shv[ks];
-        } else {
-            for (int ks = 0; ks < a.KSs; ++ks) out += a.shp[((size_t)t * a.KSs + ks) * a.d + row];
-        }
-#pragma unroll
-        for (int s = 0; s < kWP; ++s)
-            if (s < a.k) out = fmaf(wv[s], part[s * 32 + tid], out);
-        a.y[(size_t)t * a.d + row] = out;
+        for (int w = s0; w < NW; ++w) out += part_s[w * 16 + tid];
+        for (int s = 0; s < a.k; ++s) out = fmaf(Ws[s], part_r[s * 16 + tid], out);
+        a.y[(size_t)t * a.d + 16 * db + tid] = out;
     }
 }
 
@@ -633,8 +480,6 @@ DecArgs dec_args(const moe_layer *L, const uint16_t *x, int T, float *y) {
     a.k = D.top_k;
     a.I = D.d_expert;
     a.Is = D.d_shared;
-    a.KSd = cdiv(D.d_model / 64, kGPS);
-    a.KSs = cdiv(D.d_shared / 64, kGPS);
     a.rq = static_cast<const uint8_t *>(L->w.router.codes);
     a.rsb = L->w.router.sb;
     a.logit_bias = L->w.logit_bias;
@@ -647,73 +492,66 @@ DecArgs dec_args(const moe_layer *L, const uint16_t *x, int T, float *y) {
     a.sh_gate = L->w.sh_gate;
     a.sh_up = L->w.sh_up;
     a.sh_down = L->w.sh_down;
-    a.gus = L->ws.dgus;
-    a.h_r = L->ws.dh_r;
-    a.shp = L->ws.dshp;
     a.xg = L->ws.dxg;
-    a.hs = L->ws.dhs;
+    a.h_r = L->ws.dh_r;
+    a.h_s = L->ws.dh_s;
+    a.hs_r = L->ws.dhs_r;
+    a.hs_s = L->ws.dhs_s;
     a.y = y;
     return a;
 }
 
 }  // namespace
 
-size_t dec_stage3_lds(const moe_dims &D) {
-    return sizeof(uint16_t) * D.top_k * D.d_expert + sizeof(float) * D.top_k * (32 + D.d_expert / 64);
+int dec_down_waves(const moe_dims &D) { return D.top_k + 4 < 16 ? D.top_k + 4 : 16; }
+
+size_t dec_down_lds(const moe_dims &D) {
+    const size_t k = D.top_k, I = D.d_expert, Is = D.d_shared;
+    return sizeof(uint16_t) * (k * I + Is) + sizeof(float) * (k * I / 64 + Is / 64 + k + 16 * k + 16 * dec_down_waves(D));
+}
+
+size_t dec_gateup_lds(const moe_dims &D) {
+    return sizeof(uint16_t) * D.d_model + sizeof(float) * (D.d_model / 64 + kBW * 2 * 16);
 }
 
 size_t dec_workspace_floats(const moe_dims &D, int max_dec, int which) {
-    const size_t KSd = cdiv(D.d_model / 64, kGPS), KSs = cdiv(D.d_shared / 64, kGPS);
-    if (which == 0) return (size_t)max_dec * KSd * 2 * D.d_shared;
-    if (which == 1) return (size_t)max_dec * D.top_k * D.d_expert / 2;   // fp16 h, in floats
-    if (which == 3) return (size_t)max_dec * (D.d_model / 64);           // x group sums
-    if (which == 4) return (size_t)max_dec * D.top_k * (D.d_expert / 32); // h 32-value sums
-    return (size_t)max_dec * KSs * D.d_model;
+    switch (which) {
+        case 0: return (size_t)max_dec * (D.d_model / 64);                      // x group sums
+        case 1: return (size_t)max_dec * D.top_k * D.d_expert / 2;              // routed h (fp16)
+        case 2: return (size_t)max_dec * D.d_shared / 2;                        // shared h (fp16)
+        case 3: return (size_t)max_dec * D.top_k * (D.d_expert / 16);           // routed 16-value h sums
+        default: return (size_t)max_dec * (D.d_shared / 16);                    // shared 16-value h sums
+    }
 }
 
-hipError_t launch_dec_stage1(const moe_layer *L, const uint16_t *x, int T, hipStream_t s) {
-    const moe_dims &D = L->dims;
-    const DecArgs a = dec_args(L, x, T, nullptr);
-    const int G = D.d_model / 64;
-    const int grid = cdiv(D.n_experts, kRW) + T * (D.d_shared / 32) * a.KSd;
-    const size_t lds_router = sizeof(float) * kRW * T * G;
-    const size_t lds_gu = sizeof(uint16_t) * 64 * kGPS + sizeof(float) * (16 + kPW * 2 * 32);
-    hipLaunchKernelGGL(k_dec_stage1, dim3(grid), dim3(64 * kPW), lds_router > lds_gu ? lds_router : lds_gu, s, a);
-    return hipGetLastError();
-}
-
-// Router logits only (the stage-1 router workgroups), for moe_route on a few tokens.
 hipError_t launch_dec_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s) {
     const moe_dims &D = L->dims;
     DecArgs a = dec_args(L, x, T, nullptr);
     a.logits = logits;
     const size_t lds = sizeof(float) * kRW * T * (D.d_model / 64);
-    hipLaunchKernelGGL(k_dec_stage1, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kPW), lds, s, a);
+    hipLaunchKernelGGL(k_dec_router, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_dec_stage2(const moe_layer *L, const uint16_t *x, int T, hipStream_t s) {
+hipError_t launch_dec_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s) {
     const moe_dims &D = L->dims;
     const DecArgs a = dec_args(L, x, T, nullptr);
-    const int grid = T * D.top_k * (D.d_expert / 32) + T * (D.d_model / 32) * a.KSs;
-    const size_t lds_gu = sizeof(uint16_t) * (D.d_model < 64 * kW2 * kB2 ? D.d_model : 64 * kW2 * kB2) +
-                          sizeof(float) * (64 + kW2 * 2 * 32 + 2 * 64 * kW2 + 64);
-    const size_t lds_sd = sizeof(uint16_t) * 64 * kGPS + sizeof(float) * kW2 * 32;
-    const size_t lds = lds_gu > lds_sd ? lds_gu : lds_sd;
-    if (D.n_experts <= 128) hipLaunchKernelGGL(k_dec_stage2<2>, dim3(grid), dim3(64 * kW2), lds, s, a);
-    else if (D.n_experts <= 256) hipLaunchKernelGGL(k_dec_stage2<4>, dim3(grid), dim3(64 * kW2), lds, s, a);
-    else hipLaunchKernelGGL(k_dec_stage2<MOE_MAX_EXPERTS / 64>, dim3(grid), dim3(64 * kW2), lds, s, a);
+    const int grid = T * D.top_k * (D.d_expert / 16) + T * (D.d_shared / 16);
+    const size_t lds = dec_gateup_lds(D);
+    if (D.n_experts <= 128) hipLaunchKernelGGL(k_dec_gateup<2>, dim3(grid), dim3(64 * kBW), lds, s, a);
+    else if (D.n_experts <= 256) hipLaunchKernelGGL(k_dec_gateup<4>, dim3(grid), dim3(64 * kBW), lds, s, a);
+    else hipLaunchKernelGGL(k_dec_gateup<MOE_MAX_EXPERTS / 64>, dim3(grid), dim3(64 * kBW), lds, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_dec_stage3(const moe_layer *L, int T, float *y, hipStream_t s) {
+hipError_t launch_dec_down(const moe_layer *L, int T, float *y, hipStream_t s) {
     const moe_dims &D = L->dims;
     const DecArgs a = dec_args(L, nullptr, T, y);
-    if (D.top_k <= 8)
-        hipLaunchKernelGGL(k_dec_stage3<8>, dim3(T * (D.d_model / 32)), dim3(64 * D.top_k), dec_stage3_lds(D), s, a);
+    const int nw = dec_down_waves(D);
+    if (nw <= 12)
+        hipLaunchKernelGGL(k_dec_down<768>, dim3(T * (D.d_model / 16)), dim3(64 * nw), dec_down_lds(D), s, a);
     else
-        hipLaunchKernelGGL(k_dec_stage3<MOE_MAX_TOP_K>, dim3(T * (D.d_model / 32)), dim3(64 * D.top_k),
-                           dec_stage3_lds(D), s, a);
+        hipLaunchKernelGGL(k_dec_down<1024>, dim3(T * (D.d_model / 16)), dim3(64 * nw), dec_down_lds(D), s, a);
     return hipGetLastError();
 }
 

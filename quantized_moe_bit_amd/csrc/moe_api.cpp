@@ -26,7 +26,7 @@ void clear_error() { g_err[0] = 0; }
 namespace {
 
 const char *kKernelNames[K_COUNT] = {"router",     "topk",       "bucket_rank", "bucket_scan", "bucket_scatter",
-                                     "dec_route_shared", "dec_gateup", "dec_down", "pre_gateup",  "pre_down",
+                                     "dec_router", "dec_gateup", "dec_down", "pre_gateup",  "pre_down",
                                      "combine",    "glue"};
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -57,9 +57,9 @@ moe_status check_dims(const moe_dims *D) {
         if (P * wmax * 2 >= (1ull << 32) || (uint64_t)D->max_tokens * D->d_shared * 2 >= (1ull << 32))
             return fail(MOE_E_SHAPE, "max_tokens %d too large: activation buffers exceed 4 GiB", D->max_tokens);
     }
-    if (dec_stage3_lds(*D) > 65536)
-        return fail(MOE_E_SHAPE, "top_k * d_expert = %d too large for the decode down projection (LDS)",
-                    D->top_k * D->d_expert);
+    if (dec_down_lds(*D) > 65536)
+        return fail(MOE_E_SHAPE, "top_k * d_expert + d_shared = %d too large for the decode down projection (LDS)",
+                    D->top_k * D->d_expert + D->d_shared);
     return MOE_OK;
 }
 
@@ -249,11 +249,11 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.bt[3], bias_table_bytes(1, Is, d));
     plan.take(&ws.bt[4], bias_table_bytes(1, Is, d));
     plan.take(&ws.bt[5], bias_table_bytes(1, d, Is));
-    plan.take(&ws.dgus, dec_workspace_floats(D, L->max_dec, 0));
+    plan.take(&ws.dxg, dec_workspace_floats(D, L->max_dec, 0));
     plan.take(&ws.dh_r, 2 * dec_workspace_floats(D, L->max_dec, 1));
-    plan.take(&ws.dshp, dec_workspace_floats(D, L->max_dec, 2));
-    plan.take(&ws.dxg, dec_workspace_floats(D, L->max_dec, 3));
-    plan.take(&ws.dhs, dec_workspace_floats(D, L->max_dec, 4));
+    plan.take(&ws.dh_s, 2 * dec_workspace_floats(D, L->max_dec, 2));
+    plan.take(&ws.dhs_r, dec_workspace_floats(D, L->max_dec, 3));
+    plan.take(&ws.dhs_s, dec_workspace_floats(D, L->max_dec, 4));
     L->ws_bytes = (plan.off + 255) & ~size_t(255);
 
     int dev = 0;
@@ -289,11 +289,11 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     rebase(ws.r, base);
     rebase(ws.sh, base);
     for (int i = 0; i < 6; ++i) rebase(ws.bt[i], base);
-    rebase(ws.dgus, base);
-    rebase(ws.dh_r, base);
-    rebase(ws.dshp, base);
     rebase(ws.dxg, base);
-    rebase(ws.dhs, base);
+    rebase(ws.dh_r, base);
+    rebase(ws.dh_s, base);
+    rebase(ws.dhs_r, base);
+    rebase(ws.dhs_s, base);
     // zero once: padding columns of the split sums rely on it
     err = hipMemset(L->ws_base, 0, L->ws_bytes);
     // derived bias-term tables of the prefill GEMMs (read from the borrowed scale/bias words)
@@ -360,9 +360,9 @@ moe_status moe_forward_decode(moe_layer *L, const uint16_t *x, int32_t T, float 
     if (T > L->max_dec)
         return fail(MOE_E_CAPACITY, "moe_forward_decode: T = %d exceeds the decode capacity %d", T, L->max_dec);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    RUN(K_DEC_STAGE1, launch_dec_stage1(L, x, T, s));
-    RUN(K_DEC_STAGE2, launch_dec_stage2(L, x, T, s));
-    RUN(K_DEC_STAGE3, launch_dec_stage3(L, T, y, s));
+    RUN(K_DEC_ROUTER, launch_dec_router(L, x, T, L->ws.logits, s));
+    RUN(K_DEC_GATEUP, launch_dec_gateup(L, x, T, s));
+    RUN(K_DEC_DOWN, launch_dec_down(L, T, y, s));
     return MOE_OK;
 }
 

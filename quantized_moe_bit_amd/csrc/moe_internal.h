@@ -20,11 +20,9 @@ constexpr int kGroup = 64;          // quantization group (inputs per scale/bias
 constexpr int kTileRows = 32;       // rows per 1 KiB weight tile
 constexpr int kMT = 128;            // prefill GEMM rows per workgroup tile
 constexpr int kChunk = 256;         // pairs per bucketing chunk
-constexpr int kDecodeChunkGroups = 12;  // K groups a decode wave loads before computing (down)
 
 __host__ __device__ inline int roundup(int a, int b) { return (a + b - 1) / b * b; }
 constexpr int cdiv_c(int a, int b) { return (a + b - 1) / b; }
-constexpr int kGPS = 12;            // input groups per decode piece
 __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // Kernel ids for per-kernel timing.
@@ -34,9 +32,9 @@ enum KernelId {
     K_BUCKET_RANK,
     K_BUCKET_SCAN,
     K_BUCKET_SCATTER,
-    K_DEC_STAGE1,
-    K_DEC_STAGE2,
-    K_DEC_STAGE3,
+    K_DEC_ROUTER,
+    K_DEC_GATEUP,
+    K_DEC_DOWN,
     K_PRE_GATEUP,
     K_PRE_DOWN,
     K_COMBINE,
@@ -66,11 +64,11 @@ struct Workspace {
     float *sh;            // [maxT, d]          shared expert outputs
     uint8_t *bt[6];       // bias-term B' fragment tables of gate, up, down, sh_gate, sh_up, sh_down
     // decode path (D = decode capacity, KSd/KSs = input pieces of d / of I_s)
-    float *dgus;          // [D, KSd, 2, I_s]   shared gate/up partial sums
-    uint16_t *dh_r;       // [D*k, I]           routed hidden activations, fp16 bits
-    float *dshp;          // [D, KSs, d]        shared down partial sums
-    float *dxg;           // [D, d/64]          group sums of x
-    float *dhs;           // [D*k, I/32]        sums of 32 consecutive routed h values
+    float *dxg;           // [D, d/64]          decode: group sums of x
+    uint16_t *dh_r;       // [D*k, I]           decode: routed hidden activations, fp16 bits
+    uint16_t *dh_s;       // [D, I_s]           decode: shared hidden activations, fp16 bits
+    float *dhs_r;         // [D*k, I/16]        decode: sums of 16 consecutive routed h values
+    float *dhs_s;         // [D, I_s/16]        decode: sums of 16 consecutive shared h values
 };
 
 struct ProfEvent {
@@ -108,10 +106,10 @@ hipError_t launch_topk(const moe_layer *L, int T, const float *logits, int32_t *
 hipError_t launch_bucket_rank(const moe_layer *L, int T, const int32_t *idx, hipStream_t s);
 hipError_t launch_bucket_scan(const moe_layer *L, int T, hipStream_t s);
 hipError_t launch_bucket_scatter(const moe_layer *L, int T, const int32_t *idx, int32_t *perm, hipStream_t s);
-hipError_t launch_dec_stage1(const moe_layer *L, const uint16_t *x, int T, hipStream_t s);
-hipError_t launch_dec_stage2(const moe_layer *L, const uint16_t *x, int T, hipStream_t s);
-hipError_t launch_dec_stage3(const moe_layer *L, int T, float *y, hipStream_t s);
-size_t dec_stage3_lds(const moe_dims &D);
+hipError_t launch_dec_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s);
+hipError_t launch_dec_down(const moe_layer *L, int T, float *y, hipStream_t s);
+size_t dec_gateup_lds(const moe_dims &D);
+size_t dec_down_lds(const moe_dims &D);
 size_t dec_workspace_floats(const moe_dims &D, int max_dec, int which);
 hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s);
 hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s);

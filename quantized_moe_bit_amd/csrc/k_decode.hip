@@ -38,10 +38,10 @@ namespace qmoe {
 namespace {
 
 constexpr int kRW = 4;      // router experts (waves) per workgroup
-constexpr int kBW = 8;      // waves per gate/up workgroup
+constexpr int kBW = 4;      // waves per gate/up workgroup
 constexpr int kMPB = 3;     // group pairs a gate/up wave loads before computing
 constexpr int kMPC = 6;     // group pairs a down wave loads before computing
-constexpr int kXC = 2;      // 16-byte x chunks per gate/up thread: d <= 64 kBW * 8 * kXC
+constexpr int kXC = 4;      // 16-byte x chunks per gate/up thread: d <= 64 kBW * 8 * kXC
 
 // ----------------------------------------------------------------------------- router
 // The wave's expert e; lane g handles input group g (and g + 64, ... for d > 4096).
@@ -186,41 +186,55 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;
 }
 
-// Gate and up sums of 16 rows over the group pairs p = wave, wave + NW, ... (< cdiv(G, 2)),
-// x (bf16) and its group sums Xs in LDS, MP pairs per batch. Loads are unconditional
-// (pairs past the input re-read a valid group and are masked), so a batch stays in flight
-// until its first use.
-template <int NW, int MP>
-__device__ __forceinline__ void gateup16(const uint8_t *Wg, const uint8_t *Wu, const uint32_t *Sg, const uint32_t *Su,
-                                         int rb, int hb, int G, const uint16_t *xs, const float *Xs, float &accg,
-                                         float &accu) {
-    const int wave = threadIdx.x >> 6;
-    const Lane16 L = lane16();
-    const int P = cdiv(G, 2);
-    Wg += (size_t)rb * G * 1024;
-    Wu += (size_t)rb * G * 1024;
-    Sg += (size_t)rb * G * 32;
-    Su += (size_t)rb * G * 32;
-    const uint32_t co = code_lane(hb, L), so = sb_lane(hb, L);
-    for (int i0 = 0; wave + NW * i0 < P; i0 += MP) {
-        u32x4_t wg[MP], wu[MP];
-        uint32_t sg[MP], su[MP];
+// Gate and up sums of 16 rows over the group pairs p = p0, p0 + PS, ... (< cdiv(G, 2)), MP
+// pairs per batch. load(i0) issues one batch (unconditionally: pairs past the input re-read
+// a valid group and are masked later), so a caller can put the first batch in flight before
+// it stages the input; compute(i0) consumes it with x (bf16) and its group sums Xs in LDS.
+template <int MP>
+struct GateUp16 {
+    const uint8_t *Wg, *Wu;
+    const uint32_t *Sg, *Su;
+    int G, p0, PS;
+    uint32_t co, so;
+    int gsel, khalf;
+    u32x4_t wg[MP], wu[MP];
+    uint32_t sg[MP], su[MP];
+
+    __device__ __forceinline__ GateUp16(const uint8_t *wg_, const uint8_t *wu_, const uint32_t *sg_, const uint32_t *su_,
+                                        int rb, int hb, int G_, int p0_, int PS_) {
+        const Lane16 L = lane16();
+        Wg = wg_ + (size_t)rb * G_ * 1024;
+        Wu = wu_ + (size_t)rb * G_ * 1024;
+        Sg = sg_ + (size_t)rb * G_ * 32;
+        Su = su_ + (size_t)rb * G_ * 32;
+        G = G_;
+        p0 = p0_;
+        PS = PS_;
+        co = code_lane(hb, L);
+        so = sb_lane(hb, L);
+        gsel = L.gsel;
+        khalf = L.khalf;
+    }
+    __device__ __forceinline__ bool more(int i0) const { return p0 + PS * i0 < cdiv(G, 2); }
+    __device__ __forceinline__ void load(int i0) {
 #pragma unroll
         for (int i = 0; i < MP; ++i) {
-            const int g = min(2 * (wave + NW * (i0 + i)) + L.gsel, G - 1);
+            const int g = min(2 * (p0 + PS * (i0 + i)) + gsel, G - 1);
             wg[i] = ld16(Wg + ((uint32_t)g * 1024 + co));
             wu[i] = ld16(Wu + ((uint32_t)g * 1024 + co));
             sg[i] = Sg[(uint32_t)g * 32 + so];
             su[i] = Su[(uint32_t)g * 32 + so];
         }
+    }
+    __device__ __forceinline__ void compute(int i0, const uint16_t *xs, const float *Xs, float &accg, float &accu) const {
 #pragma unroll
         for (int i = 0; i < MP; ++i) {
-            const int g = 2 * (wave + NW * (i0 + i)) + L.gsel;
+            const int g = 2 * (p0 + PS * (i0 + i)) + gsel;
             const int gc = min(g, G - 1);
             float ag = 0.0f, au = 0.0f;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xs + 64 * gc + 16 * s + 8 * L.khalf);
+                const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xs + 64 * gc + 16 * s + 8 * khalf);
                 ag = dot2_bf16(xv[0], nib_pair<0>(wg[i][s]), ag);
                 ag = dot2_bf16(xv[1], nib_pair<1>(wg[i][s]), ag);
                 ag = dot2_bf16(xv[2], nib_pair<2>(wg[i][s]), ag);
@@ -231,57 +245,72 @@ __device__ __forceinline__ void gateup16(const uint8_t *Wg, const uint8_t *Wu, c
                 au = dot2_bf16(xv[3], nib_pair<3>(wu[i][s]), au);
             }
             const float on = g < G ? 1.0f : 0.0f;
-            const float X = Xs[gc] * (L.khalf == 0 ? 1.0f : 0.0f);   // the X_g term once per (row, group)
+            const float X = Xs[gc] * (khalf == 0 ? 1.0f : 0.0f);   // the X_g term once per (row, group)
             const float s16g = 16.0f * bf16_to_f32(sg[i] & 0xFFFFu), s16u = 16.0f * bf16_to_f32(su[i] & 0xFFFFu);
             accg = fmaf(on, fmaf(s16g, ag, (bf16_to_f32(sg[i] >> 16) - s16g) * X), accg);
             accu = fmaf(on, fmaf(s16u, au, (bf16_to_f32(su[i] >> 16) - s16u) * X), accu);
         }
     }
-}
+};
 
-// Down sum of 16 rows over group pairs p = p0, p0 + PS, ... (< cdiv(G, 2)) of an fp16 input h
-// (LDS, with its group sums Hs), MP pairs per batch.
+// Down sum of 16 rows over group pairs p = p0, p0 + PS, ... of an fp16 input h (LDS, with its
+// group sums Hs), MP pairs per batch; load / compute as in GateUp16.
 template <int MP>
-__device__ __forceinline__ float down16(const uint8_t *W, const uint32_t *S, int rb, int hb, int G, int p0, int PS,
-                                        const uint16_t *hl, const float *Hs) {
-    const Lane16 L = lane16();
-    const int P = cdiv(G, 2);
-    W += (size_t)rb * G * 1024;
-    S += (size_t)rb * G * 32;
-    const uint32_t co = code_lane(hb, L), so = sb_lane(hb, L);
-    float acc = 0.0f;
-    for (int i0 = 0; p0 + PS * i0 < P; i0 += MP) {
-        u32x4_t w[MP];
-        uint32_t sb[MP];
+struct Down16 {
+    const uint8_t *W;
+    const uint32_t *S;
+    int G, p0, PS;
+    uint32_t co, so;
+    int gsel, khalf;
+    u32x4_t w[MP];
+    uint32_t sb[MP];
+
+    __device__ __forceinline__ Down16(const uint8_t *w_, const uint32_t *s_, int rb, int hb, int G_, int p0_, int PS_) {
+        const Lane16 L = lane16();
+        W = w_ + (size_t)rb * G_ * 1024;
+        S = s_ + (size_t)rb * G_ * 32;
+        G = G_;
+        p0 = p0_;
+        PS = PS_;
+        co = code_lane(hb, L);
+        so = sb_lane(hb, L);
+        gsel = L.gsel;
+        khalf = L.khalf;
+    }
+    __device__ __forceinline__ bool more(int i0) const { return p0 + PS * i0 < cdiv(G, 2); }
+    __device__ __forceinline__ void load(int i0) {
 #pragma unroll
         for (int i = 0; i < MP; ++i) {
-            const int g = min(2 * (p0 + PS * (i0 + i)) + L.gsel, G - 1);
+            const int g = min(2 * (p0 + PS * (i0 + i)) + gsel, G - 1);
             w[i] = ld16(W + ((uint32_t)g * 1024 + co));
             sb[i] = S[(uint32_t)g * 32 + so];
         }
+    }
+    __device__ __forceinline__ float compute(int i0, const uint16_t *hl, const float *Hs) const {
+        float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < MP; ++i) {
             // keeps the LDS reads of pair i after the arithmetic of pair i - 1 (register use)
             asm volatile("" ::: "memory");
-            const int g = 2 * (p0 + PS * (i0 + i)) + L.gsel;
+            const int g = 2 * (p0 + PS * (i0 + i)) + gsel;
             const int gc = min(g, G - 1);
             float a = 0.0f;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const u32x4_t hv = *reinterpret_cast<const u32x4_t *>(hl + 64 * gc + 16 * s + 8 * L.khalf);
+                const u32x4_t hv = *reinterpret_cast<const u32x4_t *>(hl + 64 * gc + 16 * s + 8 * khalf);
                 a = dot2_f16(hv[0], nib_pair_f16<0>(w[i][s]), a);
                 a = dot2_f16(hv[1], nib_pair_f16<1>(w[i][s]), a);
                 a = dot2_f16(hv[2], nib_pair_f16<2>(w[i][s]), a);
                 a = dot2_f16(hv[3], nib_pair_f16<3>(w[i][s]), a);
             }
             const float on = g < G ? 1.0f : 0.0f;
-            const float H = Hs[gc] * (L.khalf == 0 ? 1.0f : 0.0f);
+            const float H = Hs[gc] * (khalf == 0 ? 1.0f : 0.0f);
             const float s16 = 16.0f * bf16_to_f32(sb[i] & 0xFFFFu);
             acc = fmaf(on, fmaf(s16, a, (bf16_to_f32(sb[i] >> 16) - s16) * H), acc);
         }
+        return acc;
     }
-    return acc;
-}
+};
 
 struct DecArgs {
     const uint16_t *x;
@@ -369,6 +398,10 @@ __global__ __launch_bounds__(64 * kBW) void k_dec_gateup(DecArgs a) {
         cbase = (size_t)e * a.I * a.d / 2;
         sbase = (size_t)e * a.I * G;
     }
+    // the first batch of weights goes out before x is staged
+    GateUp16<kMPB> gu(static_cast<const uint8_t *>(mg->codes) + cbase, static_cast<const uint8_t *>(mu->codes) + cbase,
+                      mg->sb + sbase, mu->sb + sbase, jb >> 1, jb & 1, G, wave, kBW);
+    gu.load(0);
 #pragma unroll
     for (int c = 0; c < kXC; ++c) {
         const int i = tid + 64 * kBW * c;
@@ -377,9 +410,11 @@ __global__ __launch_bounds__(64 * kBW) void k_dec_gateup(DecArgs a) {
     if (tid < G) Xs[tid] = xgv;
     __syncthreads();
     float accg = 0.0f, accu = 0.0f;
-    gateup16<kBW, kMPB>(static_cast<const uint8_t *>(mg->codes) + cbase,
-                              static_cast<const uint8_t *>(mu->codes) + cbase, mg->sb + sbase, mu->sb + sbase, jb >> 1,
-                              jb & 1, G, xs, Xs, accg, accu);
+    gu.compute(0, xs, Xs, accg, accu);
+    for (int i0 = kMPB; gu.more(i0); i0 += kMPB) {
+        gu.load(i0);
+        gu.compute(i0, xs, Xs, accg, accu);
+    }
     accg = row_sum16(accg);
     accu = row_sum16(accu);
     if (lane < 16) {
@@ -433,32 +468,69 @@ __global__ __launch_bounds__(MAXT) void k_dec_down(DecArgs a) {
     float *Ws = Hsh + GS;
     float *part_r = Ws + a.k;
     float *part_s = part_r + a.k * 16;
-    // the slot experts, then everything the workgroup reads besides the weights
+    // the expert indices, then the (small) staging reads, then this wave's first batch of
+    // weights; loads retire in order, so the staging stores below wait only for the former
+    const int sw = wave >= s0 ? wave - s0 : 0;
     int e = 0;
     if (wave < a.k) e = __builtin_amdgcn_readfirstlane(a.idx[(size_t)t * a.k + wave]);
-    for (int i = tid; i < a.k * a.I / 8; i += nth)
-        *reinterpret_cast<u32x4_t *>(hr + 8 * i) = ld16(a.h_r + (size_t)t * a.k * a.I + 8 * i);
-    for (int i = tid; i < a.Is / 8; i += nth)
-        *reinterpret_cast<u32x4_t *>(hsh + 8 * i) = ld16(a.h_s + (size_t)t * a.Is + 8 * i);
-    for (int i = tid; i < a.k * GI; i += nth) {
+    constexpr int kHC = 2;   // 16-byte chunks of the slot h per thread: k I / 8 <= kHC * 64 * NW
+    u32x4_t hrv[kHC];
+#pragma unroll
+    for (int c = 0; c < kHC; ++c) hrv[c] = ld16(a.h_r + (size_t)t * a.k * a.I + 8 * min(tid + nth * c, a.k * a.I / 8 - 1));
+    const u32x4_t hsv = ld16(a.h_s + (size_t)t * a.Is + 8 * min(tid, a.Is / 8 - 1));
+    const int ih = min(tid, a.k * GI - 1), ihs = min(tid, GS - 1);
+    const float *qr = a.hs_r + (size_t)t * a.k * (a.I / 16) + 4 * ih;
+    const float *qs = a.hs_s + (size_t)t * (a.Is / 16) + 4 * ihs;
+    const float qr0 = qr[0], qr1 = qr[1], qr2 = qr[2], qr3 = qr[3];
+    const float qs0 = qs[0], qs1 = qs[1], qs2 = qs[2], qs3 = qs[3];
+    const float wv = a.wts[(size_t)t * a.k + min(tid, a.k - 1)];
+    Down16<kMPC> dr(static_cast<const uint8_t *>(a.down.codes) + (size_t)e * a.d * a.I / 2,
+                    a.down.sb + (size_t)e * a.d * GI, db >> 1, db & 1, GI, 0, 1);
+    Down16<kMPC> ds(static_cast<const uint8_t *>(a.sh_down.codes), a.sh_down.sb, db >> 1, db & 1, GS, sw, SN);
+    if (wave < a.k) dr.load(0);
+    if (wave >= s0) ds.load(0);
+    if (a.k * a.I / 8 <= kHC * nth) {
+#pragma unroll
+        for (int c = 0; c < kHC; ++c)
+            if (tid + nth * c < a.k * a.I / 8) *reinterpret_cast<u32x4_t *>(hr + 8 * (tid + nth * c)) = hrv[c];
+    } else {
+        for (int i = tid; i < a.k * a.I / 8; i += nth)
+            *reinterpret_cast<u32x4_t *>(hr + 8 * i) = ld16(a.h_r + (size_t)t * a.k * a.I + 8 * i);
+    }
+    if (a.Is / 8 <= nth) {
+        if (tid < a.Is / 8) *reinterpret_cast<u32x4_t *>(hsh + 8 * tid) = hsv;
+    } else {
+        for (int i = tid; i < a.Is / 8; i += nth)
+            *reinterpret_cast<u32x4_t *>(hsh + 8 * i) = ld16(a.h_s + (size_t)t * a.Is + 8 * i);
+    }
+    if (tid < a.k * GI) Hr[tid] = (qr0 + qr1) + (qr2 + qr3);
+    for (int i = tid + nth; i < a.k * GI; i += nth) {
         const float *q = a.hs_r + (size_t)t * a.k * (a.I / 16) + 4 * i;
         Hr[i] = (q[0] + q[1]) + (q[2] + q[3]);
     }
-    for (int i = tid; i < GS; i += nth) {
+    if (tid < GS) Hsh[tid] = (qs0 + qs1) + (qs2 + qs3);
+    for (int i = tid + nth; i < GS; i += nth) {
         const float *q = a.hs_s + (size_t)t * (a.Is / 16) + 4 * i;
         Hsh[i] = (q[0] + q[1]) + (q[2] + q[3]);
     }
-    if (tid < a.k) Ws[tid] = a.wts[(size_t)t * a.k + tid];
+    if (tid < a.k) Ws[tid] = wv;
     __syncthreads();
     if (wave < a.k) {
-        const uint8_t *W = static_cast<const uint8_t *>(a.down.codes) + (size_t)e * a.d * a.I / 2;
-        const uint32_t *S = a.down.sb + (size_t)e * a.d * GI;
-        const float r = row_sum16(down16<kMPC>(W, S, db >> 1, db & 1, GI, 0, 1, hr + (size_t)wave * a.I, Hr + wave * GI));
+        float r = dr.compute(0, hr + (size_t)wave * a.I, Hr + wave * GI);
+        for (int i0 = kMPC; dr.more(i0); i0 += kMPC) {
+            dr.load(i0);
+            r += dr.compute(i0, hr + (size_t)wave * a.I, Hr + wave * GI);
+        }
+        r = row_sum16(r);
         if (lane < 16) part_r[wave * 16 + lane] = r;
     }
     if (wave >= s0) {
-        const float r = row_sum16(down16<kMPC>(static_cast<const uint8_t *>(a.sh_down.codes), a.sh_down.sb, db >> 1,
-                                               db & 1, GS, wave - s0, SN, hsh, Hsh));
+        float r = ds.compute(0, hsh, Hsh);
+        for (int i0 = kMPC; ds.more(i0); i0 += kMPC) {
+            ds.load(i0);
+            r += ds.compute(i0, hsh, Hsh);
+        }
+        r = row_sum16(r);
         if (lane < 16) part_s[wave * 16 + lane] = r;
     }
     __syncthreads();

@@ -47,6 +47,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload (prefill-only runs)")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 30-layer decode stack workload")
+    ap.add_argument("--stack-layers", type=int, default=0, help="layers of the stack workload (0: its 30)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -220,6 +222,47 @@ def main():
                                         unit="TFLOP/s", frac=round(tf / MFMA_PEAK_TFLOPS, 4))
         result["prefill"] = pre
         P.close()
+
+    # ------------------------------------------------------------------ 30-layer decode stack
+    if not args.no_stack:
+        if args.no_prefill:         # the prefill section already released the decode copies
+            for L in layers:
+                L.close()
+            del layers, base
+        torch.cuda.empty_cache()
+        ws = synth.WORKLOADS["stack"]
+        NL = args.stack_layers or ws.layers
+        log(f"generating the {NL}-layer decode stack")
+        stack = []
+        for l in range(NL):
+            stack.append(DeviceLayer(synth.workload_layer(ws, l), max_tokens=1, device=dev))
+        h0 = synth.gen_stack_tokens(ws.dims, ws.tokens, ws.seed)
+        hd = tokens_to_device(h0, dev)
+        xb = torch.empty((1, d), dtype=torch.int16, device=dev)
+        yb = torch.empty((1, d), dtype=torch.float32, device=dev)
+        handles = [L.handle for L in stack]
+        for t in range(8):          # warmup on the first tokens, then the timed pass from h0
+            B.moe_stack_forward_decode(handles, hd[t:t + 1], 1, xb, yb)
+        hd.copy_(tokens_to_device(h0, dev))
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for t in range(ws.tokens):
+            B.moe_stack_forward_decode(handles, hd[t:t + 1], 1, xb, yb)
+        s1.record()
+        torch.cuda.synchronize()
+        ms_tok = s0.elapsed_time(s1) / ws.tokens
+        st_bytes = NL * b_token
+        result["stack"] = {"workload": f"decode stack: {NL} distinct 2816-wide layers, residual stream between "
+                                       f"layers, {ws.tokens} consecutive tokens one at a time",
+                           "tokens_per_s": round(1000.0 / ms_tok, 1), "ms_per_token": round(ms_tok, 4),
+                           "us_per_layer": round(1000.0 * ms_tok / NL, 3), "bytes_per_token": st_bytes,
+                           "hbm_gbs": round(st_bytes / (ms_tok * 1e-3) / 1e9, 1),
+                           "hbm_frac": round(st_bytes / (ms_tok * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        for L in stack:
+            L.close()
+        del stack
+        torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ counter calibration copy
     if args.calib_copy_mib:

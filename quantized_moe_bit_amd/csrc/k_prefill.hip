@@ -515,34 +515,6 @@ __global__ __launch_bounds__(256) void k_combine(int d, int k, const float *__re
     *reinterpret_cast<f32x4_t *>(y + (size_t)t * d + c) = acc;
 }
 
-// Residual stream between stacked layers. grid T; block 256
-__global__ __launch_bounds__(256) void k_glue(const uint16_t *h, const float *y, uint16_t *h_next,
-                                              uint16_t *x_next, int d) {
-    __shared__ float red[256];
-    const int t = blockIdx.x, tid = threadIdx.x;
-    float ss = 0.0f;
-    for (int i = tid; i < d; i += 256) {
-        const size_t o = (size_t)t * d + i;
-        float v = bf16_to_f32(h[o]);
-        if (y) v = v + y[o];
-        const uint32_t b = f32_to_bf16(v);
-        h_next[o] = (uint16_t)b;
-        const float hv = bf16_to_f32(b);
-        ss = fmaf(hv, hv, ss);
-    }
-    red[tid] = ss;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if (tid < w) red[tid] += red[tid + w];
-        __syncthreads();
-    }
-    const float inv = 1.0f / sqrtf(red[0] / (float)d + 1e-6f);
-    for (int i = tid; i < d; i += 256) {
-        const size_t o = (size_t)t * d + i;
-        x_next[o] = (uint16_t)f32_to_bf16(bf16_to_f32(h_next[o]) * inv);
-    }
-}
-
 PreArgs make_args(const moe_layer *L, const uint16_t *x, int T) {
     PreArgs a;
     const moe_dims &D = L->dims;
@@ -624,12 +596,6 @@ hipError_t launch_combine(const moe_layer *L, int T, float *y, hipStream_t s) {
     const int d = L->dims.d_model;
     hipLaunchKernelGGL(k_combine, dim3(cdiv(d, 1024), T), dim3(256), 0, s, d, L->dims.top_k, L->ws.sh, L->ws.r,
                        L->ws.pos, L->ws.wts, y);
-    return hipGetLastError();
-}
-
-hipError_t launch_glue(const uint16_t *h, const float *y, uint16_t *h_next, uint16_t *x_next, int T, int d,
-                       hipStream_t s) {
-    hipLaunchKernelGGL(k_glue, dim3(T), dim3(256), 0, s, h, y, h_next, x_next, d);
     return hipGetLastError();
 }
 

@@ -393,6 +393,39 @@ moe_status moe_stack_glue(const uint16_t *h, const float *y, uint16_t *h_next, u
     return MOE_OK;
 }
 
+moe_status moe_stack_forward_decode(moe_layer *const *layers, int32_t n_layers, uint16_t *h, int32_t T,
+                                    uint16_t *x_buf, float *y_buf, void *hip_stream) {
+    clear_error();
+    if (n_layers < 1 || !layers) return fail(MOE_E_INVALID, "moe_stack_forward_decode: no layers");
+    if (T < 0) return fail(MOE_E_SHAPE, "moe_stack_forward_decode: T = %d is negative", T);
+    for (int l = 0; l < n_layers; ++l) {
+        const moe_layer *L = layers[l];
+        if (!L) return fail(MOE_E_INVALID, "moe_stack_forward_decode: layer %d is NULL", l);
+        if (L->dims.d_model != layers[0]->dims.d_model)
+            return fail(MOE_E_SHAPE, "moe_stack_forward_decode: layer %d has d_model %d, layer 0 has %d", l,
+                        L->dims.d_model, layers[0]->dims.d_model);
+        if (T > L->max_dec)
+            return fail(MOE_E_CAPACITY, "moe_stack_forward_decode: T = %d exceeds layer %d's decode capacity %d", T,
+                        l, L->max_dec);
+    }
+    if (T == 0) return MOE_OK;
+    if (!h || !x_buf || !y_buf) return fail(MOE_E_INVALID, "moe_stack_forward_decode: NULL buffer");
+    if (!aligned16(h) || !aligned16(x_buf) || !aligned16(y_buf))
+        return fail(MOE_E_ALIGN, "moe_stack_forward_decode: buffer not 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const int d = layers[0]->dims.d_model;
+    for (int l = 0; l <= n_layers; ++l) {
+        // residual add of the previous layer's output (none before layer 0), then its input norm
+        moe_layer *L = layers[l < n_layers ? l : n_layers - 1];
+        RUN(K_GLUE, launch_glue(h, l ? y_buf : nullptr, h, x_buf, T, d, s));
+        if (l == n_layers) break;
+        RUN(K_DEC_ROUTER, launch_dec_router(L, x_buf, T, L->ws.logits, s));
+        RUN(K_DEC_GATEUP, launch_dec_gateup(L, x_buf, T, s));
+        RUN(K_DEC_DOWN, launch_dec_down(L, T, y_buf, s));
+    }
+    return MOE_OK;
+}
+
 moe_status moe_profile_enable(moe_layer *L, int32_t on) {
     clear_error();
     if (!L) return fail(MOE_E_INVALID, "layer is NULL");

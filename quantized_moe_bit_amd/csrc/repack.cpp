@@ -23,7 +23,21 @@
 
 namespace {
 
-inline int nibble_slot(int j) { return (j & 1) ? 4 + (j >> 1) : (j >> 1); }
+// Eight consecutive 4-bit elements j = 0..7 sit in nibble j of a canonical little-endian
+// word; the device word holds element j in nibble (j even ? j/2 : 4 + j/2), i.e. the even
+// elements in its low half and the odd ones in its high half.
+inline uint32_t compact_nibbles(uint32_t v) {   // nibbles 0, 2, 4, 6 of v -> nibbles 0..3
+    v &= 0x0F0F0F0Fu;
+    v = (v | (v >> 4)) & 0x00FF00FFu;
+    return (v | (v >> 8)) & 0x0000FFFFu;
+}
+inline uint32_t spread_nibbles(uint32_t v) {    // nibbles 0..3 of v -> nibbles 0, 2, 4, 6
+    v &= 0x0000FFFFu;
+    v = (v | (v << 8)) & 0x00FF00FFu;
+    return (v | (v << 4)) & 0x0F0F0F0Fu;
+}
+inline uint32_t to_device_word(uint32_t c) { return compact_nibbles(c) | (compact_nibbles(c >> 4) << 16); }
+inline uint32_t to_canonical_word(uint32_t w) { return spread_nibbles(w) | (spread_nibbles(w >> 16) << 4); }
 
 moe_status check(int32_t bits, int32_t n_mats, int32_t out_dim, int32_t in_dim) {
     if (bits != 4 && bits != 8) return qmoe::fail(MOE_E_QUANT, "repack: bits must be 4 or 8, got %d", bits);
@@ -77,12 +91,10 @@ extern "C" moe_status moe_repack(int32_t bits, int32_t n_mats, int32_t out_dim, 
                     const int row = rb * 32 + (l & 31), half = l >> 5;
                     const uint8_t *crow = cm + (size_t)row * row_bytes;
                     for (int s = 0; s < 4; ++s) {
-                        uint32_t word = 0;
-                        for (int j = 0; j < 8; ++j) {
-                            const int k = 64 * g + 16 * s + 8 * half + j;
-                            const uint32_t q = (crow[k >> 1] >> ((k & 1) * 4)) & 0xFu;
-                            word |= q << (4 * nibble_slot(j));
-                        }
+                        // elements 64 g + 16 s + 8 half + (0..7): one canonical word
+                        uint32_t c;
+                        std::memcpy(&c, crow + (64 * g + 16 * s + 8 * half) / 2, 4);
+                        const uint32_t word = to_device_word(c);
                         std::memcpy(tile + l * 16 + s * 4, &word, 4);
                     }
                 }
@@ -115,7 +127,6 @@ extern "C" moe_status moe_unrepack(int32_t bits, int32_t n_mats, int32_t out_dim
     }
     const size_t row_bytes = (size_t)in_dim / 2;
     const int RB = out_dim / 32;
-    std::memset(codes, 0, (size_t)n_mats * out_dim * row_bytes);
     for (int m = 0; m < n_mats; ++m) {
         const uint8_t *sm_ = srcb + (size_t)m * out_dim * row_bytes;
         const uint32_t *wm = sb_in + (size_t)m * out_dim * G;
@@ -131,11 +142,8 @@ extern "C" moe_status moe_unrepack(int32_t bits, int32_t n_mats, int32_t out_dim
                     for (int s = 0; s < 4; ++s) {
                         uint32_t word;
                         std::memcpy(&word, tile + l * 16 + s * 4, 4);
-                        for (int j = 0; j < 8; ++j) {
-                            const int k = 64 * g + 16 * s + 8 * half + j;
-                            const uint32_t q = (word >> (4 * nibble_slot(j))) & 0xFu;
-                            crow[k >> 1] |= (uint8_t)(q << ((k & 1) * 4));
-                        }
+                        const uint32_t c = to_canonical_word(word);
+                        std::memcpy(crow + (64 * g + 16 * s + 8 * half) / 2, &c, 4);
                     }
                 }
                 for (int r = 0; r < 32; ++r) {

@@ -34,6 +34,31 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "hbm_counters_decode_prefill.md")
+
+
+def counter_traffic(kernel):
+    """HBM bytes (read + written) per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE
+    summary, or None when there is none or the kernel sources changed since it was taken."""
+    import hashlib
+    import re
+    if not os.path.exists(COUNTER_SUMMARY):
+        return None
+    txt = open(COUNTER_SUMMARY).read()
+    m = re.search(r"sha256 over ([^)]+)\):", txt)
+    m_h = re.search(r"source_sha256: ([0-9a-f]{64})", txt)
+    m_t = re.search(rf"traffic_bytes {kernel}: read (\d+) written (\d+)", txt)
+    if not (m and m_h and m_t):
+        return None
+    h = hashlib.sha256()
+    for src in (s.strip() for s in m.group(1).split(",")):
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != m_h.group(1):
+        return None
+    return int(m_t.group(1)) + int(m_t.group(2))
+
+
 def qmat_bytes(out_dim, in_dim, bits):
     return out_dim * in_dim * bits // 8 + out_dim * (in_dim // 64) * 4
 
@@ -140,7 +165,7 @@ def main():
         dom = max(timed, key=lambda n: timed[n]["avg_us"])
         achieved = stage_bytes[dom] / (timed[dom]["avg_us"] * 1e-6) / 1e9
         roofline = dict(kernel=dom, bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
-                        unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                        unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=counter_traffic(dom),
                         algorithmic_bytes=stage_bytes[dom], avg_us=round(timed[dom]["avg_us"], 3))
     layer_gbs = b_token / (ms_step * 1e-3) / 1e9
 

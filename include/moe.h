@@ -145,7 +145,9 @@ moe_status moe_forward_prefill(moe_layer *layer, const uint16_t *x, int32_t T, f
  * Residual stream between stacked layers (device, bf16 bit patterns):
  *   h_next = bf16(h + y)                                  (y may be NULL: h_next = h)
  *   x_next = bf16(h_next / sqrt(mean(h_next^2) + 1e-6))   (norm without a learned scale)
- * h, h_next, x_next: [T, d] bf16; y: [T, d] fp32. h_next may alias h.
+ * h, h_next, x_next: [T, d] bf16; y: [T, d] fp32. h_next may alias h. d must be a
+ * multiple of 8 in [8, 8192] (MOE_E_SHAPE). Both results are computed in fp64 and rounded
+ * once to bf16 (round to nearest even).
  */
 moe_status moe_stack_glue(const uint16_t *h, const float *y, uint16_t *h_next, uint16_t *x_next,
                           int32_t T, int32_t d, void *hip_stream);

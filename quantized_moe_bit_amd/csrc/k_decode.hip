@@ -601,7 +601,7 @@ hipError_t launch_dec_router(const moe_layer *L, const uint16_t *x, int T, float
     DecArgs a = dec_args(L, x, T, nullptr);
     a.logits = logits;
     const size_t lds = sizeof(float) * kRW * T * (D.d_model / 64);
-    hipLaunchKernelGGL(k_dec_router, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
+    launch(k_dec_router, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
     return hipGetLastError();
 }
 
@@ -610,9 +610,9 @@ hipError_t launch_dec_gateup(const moe_layer *L, const uint16_t *x, int T, hipSt
     const DecArgs a = dec_args(L, x, T, nullptr);
     const int grid = T * D.top_k * (D.d_expert / 16) + T * (D.d_shared / 16);
     const size_t lds = dec_gateup_lds(D);
-    if (D.n_experts <= 128) hipLaunchKernelGGL(k_dec_gateup<2>, dim3(grid), dim3(64 * kBW), lds, s, a);
-    else if (D.n_experts <= 256) hipLaunchKernelGGL(k_dec_gateup<4>, dim3(grid), dim3(64 * kBW), lds, s, a);
-    else hipLaunchKernelGGL(k_dec_gateup<MOE_MAX_EXPERTS / 64>, dim3(grid), dim3(64 * kBW), lds, s, a);
+    if (D.n_experts <= 128) launch(k_dec_gateup<2>, dim3(grid), dim3(64 * kBW), lds, s, a);
+    else if (D.n_experts <= 256) launch(k_dec_gateup<4>, dim3(grid), dim3(64 * kBW), lds, s, a);
+    else launch(k_dec_gateup<MOE_MAX_EXPERTS / 64>, dim3(grid), dim3(64 * kBW), lds, s, a);
     return hipGetLastError();
 }
 
@@ -621,9 +621,9 @@ hipError_t launch_dec_down(const moe_layer *L, int T, float *y, hipStream_t s) {
     const DecArgs a = dec_args(L, nullptr, T, y);
     const int nw = dec_down_waves(D);
     if (nw <= 12)
-        hipLaunchKernelGGL(k_dec_down<768>, dim3(T * (D.d_model / 16)), dim3(64 * nw), dec_down_lds(D), s, a);
+        launch(k_dec_down<768>, dim3(T * (D.d_model / 16)), dim3(64 * nw), dec_down_lds(D), s, a);
     else
-        hipLaunchKernelGGL(k_dec_down<1024>, dim3(T * (D.d_model / 16)), dim3(64 * nw), dec_down_lds(D), s, a);
+        launch(k_dec_down<1024>, dim3(T * (D.d_model / 16)), dim3(64 * nw), dec_down_lds(D), s, a);
     return hipGetLastError();
 }
 

@@ -570,12 +570,12 @@ int pre_grid(const moe_layer *L, int T, int mode) {
 }  // namespace
 
 hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s) {
-    hipLaunchKernelGGL(k_pre_gemm<0>, dim3(pre_grid(L, T, 0)), dim3(kPreWG), 0, s, make_args(L, x, T));
+    launch(k_pre_gemm<0>, dim3(pre_grid(L, T, 0)), dim3(kPreWG), 0, s, make_args(L, x, T));
     return hipGetLastError();
 }
 
 hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s) {
-    hipLaunchKernelGGL(k_pre_gemm<1>, dim3(pre_grid(L, T, 1)), dim3(kPreWG), 0, s, make_args(L, nullptr, T));
+    launch(k_pre_gemm<1>, dim3(pre_grid(L, T, 1)), dim3(kPreWG), 0, s, make_args(L, nullptr, T));
     return hipGetLastError();
 }
 
@@ -587,14 +587,14 @@ size_t bias_table_bytes(int n_mats, int rows, int in_dim) {
 hipError_t launch_bias_table(const moe_qmat &m, int n_mats, int rows, int in_dim, uint8_t *out, hipStream_t s) {
     const int G = in_dim / 64, Gp = roundup(G, 16);
     const size_t total = (size_t)n_mats * (rows / 32) * 64 * roundup(3 * Gp / 16, 12);
-    hipLaunchKernelGGL(k_bias_table, dim3((unsigned)cdiv((int)total, 256)), dim3(256), 0, s, m.sb, n_mats, rows, G, Gp,
+    launch(k_bias_table, dim3((unsigned)cdiv((int)total, 256)), dim3(256), 0, s, m.sb, n_mats, rows, G, Gp,
                        out);
     return hipGetLastError();
 }
 
 hipError_t launch_combine(const moe_layer *L, int T, float *y, hipStream_t s) {
     const int d = L->dims.d_model;
-    hipLaunchKernelGGL(k_combine, dim3(cdiv(d, 1024), T), dim3(256), 0, s, d, L->dims.top_k, L->ws.sh, L->ws.r,
+    launch(k_combine, dim3(cdiv(d, 1024), T), dim3(256), 0, s, d, L->dims.top_k, L->ws.sh, L->ws.r,
                        L->ws.pos, L->ws.wts, y);
     return hipGetLastError();
 }

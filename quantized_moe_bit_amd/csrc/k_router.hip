@@ -29,7 +29,8 @@ namespace {
 
 
 
-constexpr int kRT = 8;     // tokens per router wave (prefill router)
+constexpr int kRNE = 4;                  // experts per wave of the prefill router
+constexpr int kRBlk = 64 * kRNE + 2 * kRNE;   // router table floats per (expert block, group)
 
 // Group sums X_g = ((0 + x_0) + x_1) + ... + x_63 of each token (fp32, ascending), and their
 // bf16 hi | lo | hi split for the bias-term GEMM of the prefill gate/up.
@@ -61,93 +62,112 @@ __global__ __launch_bounds__(256) void k_xsum(const uint16_t *__restrict__ x, in
     xsplit[(size_t)t * Ks + 2 * Gp + g] = (uint16_t)hi;
 }
 
-// Prefill router: lane = expert, wave = (64 experts, kRT tokens); a workgroup = 4 waves =
-// 128 experts x 2 kRT tokens. For every input group g, in ascending order, the workgroup
-// stages its tokens' 64 inputs of the group as fp32 in LDS; each lane converts its
-// expert's 64 codes once and runs kRT independent fma chains (one per token, ascending j,
-// inputs read by LDS broadcast); P_g = fma(s, A, fl(b * X_g)) is added to each token's
-// running logit. Same fp32 order as the oracle.
-// grid: (ceil(T / (2 kRT)), ceil(E / 128)); block 256
-__global__ __launch_bounds__(256) void k_router_pre(const uint16_t *__restrict__ x, int T, int d, int E,
-                                                   const uint8_t *__restrict__ rq, const uint32_t *__restrict__ rsb,
-                                                   const float *__restrict__ xsum,
-                                                   const float *__restrict__ logit_bias, float *__restrict__ logits) {
-    constexpr int kTok = 2 * kRT;
-    constexpr int kPitch = 68;                       // fp32 per staged token row (64 + 4 pad)
-    __shared__ __align__(16) float xs[2][kTok][kPitch];
-    __shared__ float Xs[2][kTok];
+// Prefill router: lane = token, wave = kRNE consecutive experts, workgroup = 4 waves (64 tokens
+// x 4 kRNE experts). The 8-bit codes, scales and biases come as fp32 from a table built at
+// layer creation, read with wave-uniform (scalar) loads at constant offsets from one base, so
+// each fma takes its code from a scalar register. A lane converts its token's 64 inputs of
+// the current group to fp32 once for all kRNE experts and runs kRNE independent fma chains,
+// 16 inputs at a time. Per (token, expert) the arithmetic is the fixed order stated at the top
+// of this file.
+//
+// Table layout, per block of kRNE experts eb and group g (kRBlk floats): codes [4][kRNE][16]
+// (inputs 16 jc + j of expert kRNE eb + i at [jc][i][j]), then kRNE scales, then kRNE biases.
+// Experts past E are zero.
+// grid: (ceil(T / 64), ceil(E / (4 kRNE))); block 256
+__global__ __launch_bounds__(256) void k_router_tok(const uint16_t *__restrict__ x, int T, int d, int E,
+                                                    const float *__restrict__ tab, const float *__restrict__ xsum,
+                                                    const float *__restrict__ logit_bias, float *__restrict__ logits) {
     const int G = d / 64;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int e = blockIdx.y * 128 + (wave & 1) * 64 + lane;
-    const bool ev = e < E;
-    const int ee = ev ? e : E - 1;
-    const int tb = wave >> 1;                        // token half of the workgroup
-    const int t0 = blockIdx.x * kTok;
-    // staging: thread moves 4 inputs (token tid/16, inputs 4*(tid%16)..+3) and, for tid < kTok, X_g
-    const int st = tid >> 4, sj = (tid & 15) * 4;
-    const int stok = min(t0 + st, T - 1);
-    const uint16_t *xsrc = x + (size_t)stok * d + sj;
-    const uint8_t *qsrc = rq + (size_t)ee * d;
-    const uint32_t *ssrc = rsb + (size_t)ee * G;
-
-    uint2 xr = *reinterpret_cast<const uint2 *>(xsrc);
-    float Xr = (tid < kTok) ? xsum[(size_t)min(t0 + tid, T - 1) * G] : 0.0f;
-    u32x4_t qv[4];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int eb = blockIdx.y * 4 + wave;
+    const int e0 = eb * kRNE;
+    if (e0 >= E) return;   // wave-uniform; the kernel has no barriers
+    const int t = blockIdx.x * 64 + lane;
+    const int tc = t < T ? t : T - 1;
+    const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(x + (size_t)tc * d);
+    const float *xs = xsum + (size_t)tc * G;
+    const float *blk = tab + (size_t)eb * G * kRBlk;
+    float L[kRNE];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) qv[i] = reinterpret_cast<const u32x4_t *>(qsrc)[i];
-    uint32_t sbw = ssrc[0];
-    float L[kRT];
+    for (int i = 0; i < kRNE; ++i) L[i] = 0.0f;
+    u32x4_t nxt[8];
 #pragma unroll
-    for (int i = 0; i < kRT; ++i) L[i] = 0.0f;
-    for (int g = 0; g < G; ++g) {
-        const int buf = g & 1;
-        *reinterpret_cast<f32x4_t *>(&xs[buf][st][sj]) =
-            f32x4_t{bf16_to_f32(xr.x & 0xFFFFu), bf16_to_f32(xr.x >> 16), bf16_to_f32(xr.y & 0xFFFFu),
-                    bf16_to_f32(xr.y >> 16)};
-        if (tid < kTok) Xs[buf][tid] = Xr;
-        float qf[64];
+    for (int c = 0; c < 8; ++c) nxt[c] = xr[c];
+    float Xn = xs[0];
+    for (int g = 0; g < G; ++g, blk += kRBlk) {
+        float xf[64];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int c = 0; c < 8; ++c)
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) qf[i * 16 + w * 4 + b] = (float)((qv[i][w] >> (8 * b)) & 0xFFu);
-        const float sc = bf16_to_f32(sbw & 0xFFFFu), bi = bf16_to_f32(sbw >> 16);
-        __syncthreads();
-        if (g + 1 < G) {                             // prefetch the next group
-            xr = *reinterpret_cast<const uint2 *>(xsrc + 64 * (g + 1));
-            if (tid < kTok) Xr = xsum[(size_t)min(t0 + tid, T - 1) * G + g + 1];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) qv[i] = reinterpret_cast<const u32x4_t *>(qsrc + 64 * (g + 1))[i];
-            sbw = ssrc[g + 1];
-        }
-        float A[kRT];
-#pragma unroll
-        for (int i = 0; i < kRT; ++i) A[i] = 0.0f;
-#pragma unroll
-        for (int j4 = 0; j4 < 16; ++j4) {
-#pragma unroll
-            for (int i = 0; i < kRT; ++i) {
-                const f32x4_t xv = *reinterpret_cast<const f32x4_t *>(&xs[buf][tb * kRT + i][4 * j4]);
-                A[i] = __builtin_fmaf(xv[0], qf[4 * j4 + 0], A[i]);
-                A[i] = __builtin_fmaf(xv[1], qf[4 * j4 + 1], A[i]);
-                A[i] = __builtin_fmaf(xv[2], qf[4 * j4 + 2], A[i]);
-                A[i] = __builtin_fmaf(xv[3], qf[4 * j4 + 3], A[i]);
+            for (int w = 0; w < 4; ++w) {
+                xf[8 * c + 2 * w] = bf16_to_f32(nxt[c][w] & 0xFFFFu);
+                xf[8 * c + 2 * w + 1] = __uint_as_float(nxt[c][w] & 0xFFFF0000u);
             }
+        const float X = Xn;
+        {   // next group's inputs in flight during this group's chains (the last group re-reads itself)
+            const int gn = g + 1 < G ? g + 1 : g;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) nxt[c] = xr[8 * gn + c];
+            Xn = xs[gn];
+        }
+        float A[kRNE];
+#pragma unroll
+        for (int i = 0; i < kRNE; ++i) A[i] = 0.0f;
+#pragma unroll
+        for (int jc = 0; jc < 4; ++jc) {
+            // keeps each chunk's code loads next to their use (scalar register pressure)
+            asm volatile("" ::: "memory");
+            float q[kRNE][16];
+#pragma unroll
+            for (int i = 0; i < kRNE; ++i)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) q[i][j] = blk[(jc * kRNE + i) * 16 + j];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+#pragma unroll
+                for (int i = 0; i < kRNE; ++i) A[i] = __builtin_fmaf(xf[16 * jc + j], q[i][j], A[i]);
         }
 #pragma unroll
-        for (int i = 0; i < kRT; ++i) {
-            const float bX = bi * Xs[buf][tb * kRT + i];
+        for (int i = 0; i < kRNE; ++i) {
+            const float sc = blk[64 * kRNE + i], bi = blk[65 * kRNE + i];
+            const float bX = bi * X;
             L[i] = L[i] + __builtin_fmaf(sc, A[i], bX);
         }
-        // the next iteration writes the other buffer; the barrier after its staging orders it
     }
-    if (!ev) return;
+    if (t >= T) return;
 #pragma unroll
-    for (int i = 0; i < kRT; ++i) {
-        const int t = t0 + tb * kRT + i;
-        if (t < T) logits[(size_t)t * E + e] = logit_bias ? L[i] + logit_bias[e] : L[i];
+    for (int i = 0; i < kRNE; ++i) {
+        const int e = e0 + i;
+        if (e < E) logits[(size_t)t * E + e] = logit_bias ? L[i] + logit_bias[e] : L[i];
     }
+}
+
+// The router table k_router_tok reads (codes, scales and biases as exact fp32).
+// grid ceil(n / 256) with n = ceil(E / kRNE) * G * kRBlk; block 256
+__global__ __launch_bounds__(256) void k_router_table(const uint8_t *__restrict__ q, const uint32_t *__restrict__ sb,
+                                                      int E, int d, float *__restrict__ out) {
+    const int G = d / 64;
+    const size_t n = (size_t)cdiv(E, kRNE) * G * kRBlk;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int r = (int)(i % kRBlk);
+    const size_t bg = i / kRBlk;
+    const int g = (int)(bg % G), eb = (int)(bg / G);
+    float v = 0.0f;
+    if (r < 64 * kRNE) {
+        const int jc = r / (16 * kRNE), ii = (r / 16) % kRNE, j = r % 16;
+        const int e = eb * kRNE + ii;
+        if (e < E) v = (float)q[(size_t)e * d + 64 * g + 16 * jc + j];
+    } else {
+        const int ii = (r - 64 * kRNE) % kRNE, part = (r - 64 * kRNE) / kRNE;   // 0: scale, 1: bias
+        const int e = eb * kRNE + ii;
+        if (e < E) {
+            const uint32_t w = sb[(size_t)e * G + g];
+            v = bf16_to_f32(part == 0 ? (w & 0xFFFFu) : (w >> 16));
+        }
+    }
+    out[i] = v;
 }
 
 // (value desc, index asc) ordering
@@ -308,39 +328,48 @@ __global__ __launch_bounds__(256) void k_bucket_scatter(const int32_t *__restric
 
 hipError_t launch_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s) {
     const int d = L->dims.d_model, E = L->dims.n_experts, G = d / 64;
-    hipLaunchKernelGGL(k_xsum, dim3(cdiv(T * G, 256)), dim3(256), 0, s, x, T, d, L->ws.xsum, L->ws.xsplit,
+    launch(k_xsum, dim3(cdiv(T * G, 256)), dim3(256), 0, s, x, T, d, L->ws.xsum, L->ws.xsplit,
                        L->Gp_d, L->Ks_d);
-    hipLaunchKernelGGL(k_router_pre, dim3(cdiv(T, 2 * kRT), cdiv(E, 128)), dim3(256), 0, s, x, T, d, E,
-                       static_cast<const uint8_t *>(L->w.router.codes), L->w.router.sb, L->ws.xsum, L->w.logit_bias,
-                       logits);
+    launch(k_router_tok, dim3(cdiv(T, 64), cdiv(E, 4 * kRNE)), dim3(256), 0, s, x, T, d, E, L->ws.rqf, L->ws.xsum,
+           L->w.logit_bias, logits);
+    return hipGetLastError();
+}
+
+size_t router_table_floats(const moe_dims &D) { return (size_t)cdiv(D.n_experts, kRNE) * (D.d_model / 64) * kRBlk; }
+
+hipError_t launch_router_table(const moe_layer *L, hipStream_t s) {
+    const size_t n = router_table_floats(L->dims);
+    launch(k_router_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+           static_cast<const uint8_t *>(L->w.router.codes), L->w.router.sb, L->dims.n_experts, L->dims.d_model,
+           L->ws.rqf);
     return hipGetLastError();
 }
 
 hipError_t launch_topk(const moe_layer *L, int T, const float *logits, int32_t *idx, float *w, hipStream_t s) {
     const int E = L->dims.n_experts, k = L->dims.top_k;
-    if (E <= 128) hipLaunchKernelGGL(k_topk<2>, dim3(cdiv(T, 4)), dim3(256), 0, s, logits, T, E, k, idx, w);
-    else if (E <= 256) hipLaunchKernelGGL(k_topk<4>, dim3(cdiv(T, 4)), dim3(256), 0, s, logits, T, E, k, idx, w);
-    else hipLaunchKernelGGL(k_topk<MOE_MAX_EXPERTS / 64>, dim3(cdiv(T, 4)), dim3(256), 0, s, logits, T, E, k, idx, w);
+    if (E <= 128) launch(k_topk<2>, dim3(cdiv(T, 4)), dim3(256), 0, s, logits, T, E, k, idx, w);
+    else if (E <= 256) launch(k_topk<4>, dim3(cdiv(T, 4)), dim3(256), 0, s, logits, T, E, k, idx, w);
+    else launch(k_topk<MOE_MAX_EXPERTS / 64>, dim3(cdiv(T, 4)), dim3(256), 0, s, logits, T, E, k, idx, w);
     return hipGetLastError();
 }
 
 hipError_t launch_bucket_rank(const moe_layer *L, int T, const int32_t *idx, hipStream_t s) {
     const int P = T * L->dims.top_k;
-    hipLaunchKernelGGL(k_bucket_rank, dim3(cdiv(P, kChunk)), dim3(kChunk), 0, s, idx, P, L->dims.n_experts,
+    launch(k_bucket_rank, dim3(cdiv(P, kChunk)), dim3(kChunk), 0, s, idx, P, L->dims.n_experts,
                        L->ws.rank, L->ws.chunk_base);
     return hipGetLastError();
 }
 
 hipError_t launch_bucket_scan(const moe_layer *L, int T, hipStream_t s) {
     const int P = T * L->dims.top_k;
-    hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(1024), 0, s, cdiv(P, kChunk), L->dims.n_experts,
+    launch(k_bucket_scan, dim3(1), dim3(1024), 0, s, cdiv(P, kChunk), L->dims.n_experts,
                        L->ws.chunk_base, L->ws.counts, L->ws.offsets, L->ws.tile_off, kMT);
     return hipGetLastError();
 }
 
 hipError_t launch_bucket_scatter(const moe_layer *L, int T, const int32_t *idx, int32_t *perm_out, hipStream_t s) {
     const int P = T * L->dims.top_k;
-    hipLaunchKernelGGL(k_bucket_scatter, dim3(cdiv(P, kChunk)), dim3(kChunk), 0, s, idx, P, L->dims.n_experts,
+    launch(k_bucket_scatter, dim3(cdiv(P, kChunk)), dim3(kChunk), 0, s, idx, P, L->dims.n_experts,
                        L->ws.rank, L->ws.chunk_base, L->ws.perm, L->ws.pos, perm_out);
     return hipGetLastError();
 }

@@ -12,6 +12,7 @@
 namespace qmoe {
 
 static thread_local char g_err[512] = "";
+thread_local LaunchTiming g_timing;
 
 moe_status fail(moe_status s, const char *fmt, ...) {
     va_list ap;
@@ -126,14 +127,18 @@ hipError_t prof_begin(moe_layer *L, int id, hipStream_t s, hipEvent_t *a, hipEve
     hipError_t err = grab(a);
     if (err != hipSuccess) return err;
     if ((err = grab(b)) != hipSuccess) return err;
-    return hipEventRecord(*a, s);
+    (void)s;
+    g_timing.start = *a;   // consumed by the launcher's kernel launches
+    g_timing.stop = *b;
+    return hipSuccess;
 }
 
 hipError_t prof_end(moe_layer *L, int id, hipStream_t s, hipEvent_t a, hipEvent_t b) {
+    (void)s;
     if (!L->prof_on) return hipSuccess;
-    hipError_t err = hipEventRecord(b, s);
+    g_timing = LaunchTiming{};
     L->prof_pending.push_back(ProfEvent{id, a, b});
-    return err;
+    return hipSuccess;
 }
 
 // Runs one launcher, with optional event timing, mapping errors to MOE_E_DEVICE.
@@ -143,6 +148,7 @@ moe_status run(moe_layer *L, int id, hipStream_t s, F &&f) {
     hipError_t err = prof_begin(L, id, s, &a, &b);
     if (err == hipSuccess) err = f();
     if (err == hipSuccess) err = prof_end(L, id, s, a, b);
+    else g_timing = LaunchTiming{};
     if (err != hipSuccess) return fail(MOE_E_DEVICE, "kernel %s: %s", kKernelNames[id], hipGetErrorString(err));
     return MOE_OK;
 }
@@ -249,6 +255,7 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.bt[3], bias_table_bytes(1, Is, d));
     plan.take(&ws.bt[4], bias_table_bytes(1, Is, d));
     plan.take(&ws.bt[5], bias_table_bytes(1, d, Is));
+    plan.take(&ws.rqf, router_table_floats(D));
     plan.take(&ws.dxg, dec_workspace_floats(D, L->max_dec, 0));
     plan.take(&ws.dh_r, 2 * dec_workspace_floats(D, L->max_dec, 1));
     plan.take(&ws.dh_s, 2 * dec_workspace_floats(D, L->max_dec, 2));
@@ -289,6 +296,7 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     rebase(ws.r, base);
     rebase(ws.sh, base);
     for (int i = 0; i < 6; ++i) rebase(ws.bt[i], base);
+    rebase(ws.rqf, base);
     rebase(ws.dxg, base);
     rebase(ws.dh_r, base);
     rebase(ws.dh_s, base);
@@ -297,6 +305,7 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     // zero once: padding columns of the split sums rely on it
     err = hipMemset(L->ws_base, 0, L->ws_bytes);
     // derived bias-term tables of the prefill GEMMs (read from the borrowed scale/bias words)
+    if (err == hipSuccess) err = launch_router_table(L, nullptr);
     if (err == hipSuccess) err = launch_bias_table(w->gate, E, I, d, ws.bt[0], nullptr);
     if (err == hipSuccess) err = launch_bias_table(w->up, E, I, d, ws.bt[1], nullptr);
     if (err == hipSuccess) err = launch_bias_table(w->down, E, d, I, ws.bt[2], nullptr);
@@ -383,7 +392,8 @@ moe_status moe_stack_glue(const uint16_t *h, const float *y, uint16_t *h_next, u
                           int32_t d, void *hip_stream) {
     clear_error();
     if (T < 0) return fail(MOE_E_SHAPE, "moe_stack_glue: T = %d is negative", T);
-    if (d < 1) return fail(MOE_E_SHAPE, "moe_stack_glue: d = %d", d);
+    if (d < 8 || d % 8 || d > 8192)
+        return fail(MOE_E_SHAPE, "moe_stack_glue: d = %d must be a multiple of 8 in [8, 8192]", d);
     if (T == 0) return MOE_OK;
     if (!h || !h_next || !x_next) return fail(MOE_E_INVALID, "moe_stack_glue: NULL pointer");
     if (!aligned16(h) || !aligned16(h_next) || !aligned16(x_next) || (y && !aligned16(y)))

@@ -1,10 +1,12 @@
 // Internal definitions shared by the host runtime and the gfx950 kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
 #include <cstdint>
+#include <utility>
 #include <vector>
 
 #include "moe.h"
@@ -63,6 +65,7 @@ struct Workspace {
     float *r;             // [maxT*k, d]        routed expert outputs (bucket order)
     float *sh;            // [maxT, d]          shared expert outputs
     uint8_t *bt[6];       // bias-term B' fragment tables of gate, up, down, sh_gate, sh_up, sh_down
+    float *rqf;           // router codes, scales and biases as fp32 (prefill router table)
     // decode path (D = decode capacity, KSd/KSs = input pieces of d / of I_s)
     float *dxg;           // [D, d/64]          decode: group sums of x
     uint16_t *dh_r;       // [D*k, I]           decode: routed hidden activations, fp16 bits
@@ -99,9 +102,31 @@ struct moe_layer {
 
 namespace qmoe {
 
+// Kernel timing hook. While `stop` is set (per-kernel profiling of one call), launches go
+// through hipExtLaunchKernelGGL, which attaches the events to the dispatch itself, so the
+// elapsed time is the kernel's execution interval (the same interval a kernel trace reports)
+// rather than the gap between two separately queued markers. A launcher issuing several
+// kernels records `start` on the first and `stop` on each, so the interval spans all of them.
+struct LaunchTiming {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchTiming g_timing;
+
+template <typename F, typename... Args>
+inline void launch(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, Args... args) {
+    if (g_timing.stop) {
+        hipExtLaunchKernelGGL(kernel, grid, block, (std::uint32_t)lds, s, g_timing.start, g_timing.stop, 0u, args...);
+        g_timing.start = nullptr;
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+    }
+}
+
 // Kernel launchers (each enqueues on stream, returns hipGetLastError()).
 hipError_t launch_dec_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s);
 hipError_t launch_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s);
+hipError_t launch_router_table(const moe_layer *L, hipStream_t s);
+size_t router_table_floats(const moe_dims &D);
 hipError_t launch_topk(const moe_layer *L, int T, const float *logits, int32_t *idx, float *w, hipStream_t s);
 hipError_t launch_bucket_rank(const moe_layer *L, int T, const int32_t *idx, hipStream_t s);
 hipError_t launch_bucket_scan(const moe_layer *L, int T, hipStream_t s);

@@ -32,34 +32,34 @@ namespace {
 constexpr int kRNE = 4;                  // experts per wave of the prefill router
 constexpr int kRBlk = 64 * kRNE + 2 * kRNE;   // router table floats per (expert block, group)
 
-// Group sums X_g = ((0 + x_0) + x_1) + ... + x_63 of each token (fp32, ascending), and their
-// bf16 hi | lo | hi split for the bias-term GEMM of the prefill gate/up.
+// Group sums X_g = ((0 + x_0) + x_1) + ... + x_63 of each token (fp32, ascending), and the
+// fp16 copy of x the prefill gate/up GEMM reads (exact for |x| in fp16's normal range).
 // grid: ceil(T * G / 256); block 256
 __global__ __launch_bounds__(256) void k_xsum(const uint16_t *__restrict__ x, int T, int d,
-                                              float *__restrict__ xsum, uint16_t *__restrict__ xsplit, int Gp,
-                                              int Ks) {
+                                              float *__restrict__ xsum, uint16_t *__restrict__ x16) {
     const int G = d / 64;
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= T * G) return;
     const int t = i / G, g = i % G;
     const u32x4_t *xp = reinterpret_cast<const u32x4_t *>(x + (size_t)t * d + 64 * g);
+    u32x4_t *op = reinterpret_cast<u32x4_t *>(x16 + (size_t)t * d + 64 * g);
     u32x4_t v[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] = xp[q];
     float X = 0.0f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+    for (int q = 0; q < 8; ++q) {
+        u32x4_t h;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            X = X + bf16_to_f32(v[q][w] & 0xFFFFu);
-            X = X + bf16_to_f32(v[q][w] >> 16);
+            const float lo = bf16_to_f32(v[q][w] & 0xFFFFu), hi = bf16_to_f32(v[q][w] >> 16);
+            X = X + lo;
+            X = X + hi;
+            h[w] = f32_to_f16_sat(lo) | (f32_to_f16_sat(hi) << 16);
         }
+        op[q] = h;
+    }
     xsum[i] = X;
-    const uint32_t hi = f32_to_bf16(X);
-    const uint32_t lo = f32_to_bf16(X - bf16_to_f32(hi));
-    xsplit[(size_t)t * Ks + g] = (uint16_t)hi;
-    xsplit[(size_t)t * Ks + Gp + g] = (uint16_t)lo;
-    xsplit[(size_t)t * Ks + 2 * Gp + g] = (uint16_t)hi;
 }
 
 // Prefill router: lane = token, wave = kRNE consecutive experts, workgroup = 4 waves (64 tokens
@@ -328,8 +328,7 @@ __global__ __launch_bounds__(256) void k_bucket_scatter(const int32_t *__restric
 
 hipError_t launch_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s) {
     const int d = L->dims.d_model, E = L->dims.n_experts, G = d / 64;
-    launch(k_xsum, dim3(cdiv(T * G, 256)), dim3(256), 0, s, x, T, d, L->ws.xsum, L->ws.xsplit,
-                       L->Gp_d, L->Ks_d);
+    launch(k_xsum, dim3(cdiv(T * G, 256)), dim3(256), 0, s, x, T, d, L->ws.xsum, L->ws.x16);
     launch(k_router_tok, dim3(cdiv(T, 64), cdiv(E, 4 * kRNE)), dim3(256), 0, s, x, T, d, E, L->ws.rqf, L->ws.xsum,
            L->w.logit_bias, logits);
     return hipGetLastError();

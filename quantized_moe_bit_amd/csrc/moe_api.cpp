@@ -220,12 +220,6 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     L->G_d = d / 64;
     L->G_I = I / 64;
     L->G_Is = Is / 64;
-    L->Gp_d = roundup(L->G_d, 16);
-    L->Gp_I = roundup(L->G_I, 16);
-    L->Gp_Is = roundup(L->G_Is, 16);
-    L->Ks_d = roundup(3 * L->Gp_d, 64);
-    L->Ks_I = roundup(3 * L->Gp_I, 64);
-    L->Ks_Is = roundup(3 * L->Gp_Is, 64);
     L->max_dec = D.max_tokens < MOE_MAX_DECODE_TOKENS ? D.max_tokens : MOE_MAX_DECODE_TOKENS;
     const size_t nchunks = (size_t)cdiv((int)P, kChunk);
 
@@ -235,7 +229,7 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.idx, P);
     plan.take(&ws.wts, P);
     plan.take(&ws.xsum, Tm * L->G_d);
-    plan.take(&ws.xsplit, Tm * L->Ks_d);
+    plan.take(&ws.x16, Tm * d);
     plan.take(&ws.counts, E);
     plan.take(&ws.offsets, E + 1);
     plan.take(&ws.tile_off, E + 1);
@@ -244,17 +238,9 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.perm, P);
     plan.take(&ws.pos, P);
     plan.take(&ws.h_r, P * I);
-    plan.take(&ws.hsplit_r, P * L->Ks_I);
     plan.take(&ws.h_s, Tm * Is);
-    plan.take(&ws.hsplit_s, Tm * L->Ks_Is);
     plan.take(&ws.r, P * d);
     plan.take(&ws.sh, Tm * d);
-    plan.take(&ws.bt[0], bias_table_bytes(E, I, d));
-    plan.take(&ws.bt[1], bias_table_bytes(E, I, d));
-    plan.take(&ws.bt[2], bias_table_bytes(E, d, I));
-    plan.take(&ws.bt[3], bias_table_bytes(1, Is, d));
-    plan.take(&ws.bt[4], bias_table_bytes(1, Is, d));
-    plan.take(&ws.bt[5], bias_table_bytes(1, d, Is));
     plan.take(&ws.rqf, router_table_floats(D));
     plan.take(&ws.dxg, dec_workspace_floats(D, L->max_dec, 0));
     plan.take(&ws.dh_r, 2 * dec_workspace_floats(D, L->max_dec, 1));
@@ -281,7 +267,7 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     rebase(ws.idx, base);
     rebase(ws.wts, base);
     rebase(ws.xsum, base);
-    rebase(ws.xsplit, base);
+    rebase(ws.x16, base);
     rebase(ws.counts, base);
     rebase(ws.offsets, base);
     rebase(ws.tile_off, base);
@@ -290,12 +276,9 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     rebase(ws.perm, base);
     rebase(ws.pos, base);
     rebase(ws.h_r, base);
-    rebase(ws.hsplit_r, base);
     rebase(ws.h_s, base);
-    rebase(ws.hsplit_s, base);
     rebase(ws.r, base);
     rebase(ws.sh, base);
-    for (int i = 0; i < 6; ++i) rebase(ws.bt[i], base);
     rebase(ws.rqf, base);
     rebase(ws.dxg, base);
     rebase(ws.dh_r, base);
@@ -306,12 +289,6 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     err = hipMemset(L->ws_base, 0, L->ws_bytes);
     // derived bias-term tables of the prefill GEMMs (read from the borrowed scale/bias words)
     if (err == hipSuccess) err = launch_router_table(L, nullptr);
-    if (err == hipSuccess) err = launch_bias_table(w->gate, E, I, d, ws.bt[0], nullptr);
-    if (err == hipSuccess) err = launch_bias_table(w->up, E, I, d, ws.bt[1], nullptr);
-    if (err == hipSuccess) err = launch_bias_table(w->down, E, d, I, ws.bt[2], nullptr);
-    if (err == hipSuccess) err = launch_bias_table(w->sh_gate, 1, Is, d, ws.bt[3], nullptr);
-    if (err == hipSuccess) err = launch_bias_table(w->sh_up, 1, Is, d, ws.bt[4], nullptr);
-    if (err == hipSuccess) err = launch_bias_table(w->sh_down, 1, d, Is, ws.bt[5], nullptr);
     if (err == hipSuccess) err = hipDeviceSynchronize();
     if (err != hipSuccess) {
         (void)hipFree(L->ws_base);

@@ -50,7 +50,7 @@ struct Workspace {
     int32_t *idx;         // [maxT, k]
     float *wts;           // [maxT, k]
     float *xsum;          // [maxT, G]          router-order group sums of x
-    uint16_t *xsplit;     // [maxT, Ks_d]       bf16 hi | lo | hi of the group sums (zero padded)
+    uint16_t *x16;        // [maxT, d]          fp16 copy of x (prefill gate/up operand)
     int32_t *counts;      // [E]
     int32_t *offsets;     // [E+1]
     int32_t *tile_off;    // [E+1]              prefix sum of ceil(count/kMT)
@@ -59,12 +59,9 @@ struct Workspace {
     int32_t *perm;        // [maxT*k]
     int32_t *pos;         // [maxT*k]
     uint16_t *h_r;        // [maxT*k, I]        routed hidden activations, fp16 bits (bucket order)
-    uint16_t *hsplit_r;   // [maxT*k, Ks_I]
     uint16_t *h_s;        // [maxT, I_s]        shared hidden activations, fp16 bits
-    uint16_t *hsplit_s;   // [maxT, Ks_Is]
     float *r;             // [maxT*k, d]        routed expert outputs (bucket order)
     float *sh;            // [maxT, d]          shared expert outputs
-    uint8_t *bt[6];       // bias-term B' fragment tables of gate, up, down, sh_gate, sh_up, sh_down
     float *rqf;           // router codes, scales and biases as fp32 (prefill router table)
     // decode path (D = decode capacity, KSd/KSs = input pieces of d / of I_s)
     float *dxg;           // [D, d/64]          decode: group sums of x
@@ -86,8 +83,6 @@ struct moe_layer {
     moe_weights w;
     int device;
     int G_d, G_I, G_Is;        // groups along d, I, I_s
-    int Gp_d, Gp_I, Gp_Is;     // padded to a multiple of 16
-    int Ks_d, Ks_I, Ks_Is;     // split-sum row strides: 3 Gp rounded up to a multiple of 64
     int max_dec;               // decode capacity = min(max_tokens, MOE_MAX_DECODE_TOKENS)
     void *ws_base;
     size_t ws_bytes;
@@ -139,8 +134,6 @@ size_t dec_workspace_floats(const moe_dims &D, int max_dec, int which);
 hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s);
 hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s);
 hipError_t launch_combine(const moe_layer *L, int T, float *y, hipStream_t s);
-size_t bias_table_bytes(int n_mats, int rows, int in_dim);
-hipError_t launch_bias_table(const moe_qmat &m, int n_mats, int rows, int in_dim, uint8_t *out, hipStream_t s);
 hipError_t launch_glue(const uint16_t *h, const float *y, uint16_t *h_next, uint16_t *x_next, int T, int d,
                        hipStream_t s);
 

@@ -52,6 +52,10 @@ constexpr int kWaitB0 = 2 * (kBDist - 1) + 4 * kADist;   // after the scale/bias
 constexpr int kUPitch = 72;
 constexpr int kHPitch = 72;
 static_assert(kMT * kUPitch * 4 <= kSmemBytes && kMT * kHPitch * 2 <= kSmemBytes, "epilogue tile exceeds the LDS rings");
+// down epilogue: 64 rows x 128 fp32 per half (row pitch 136: the two rows one store instruction
+// writes start 32 banks apart)
+constexpr int kOPitch = 136;
+static_assert(64 * kOPitch * 4 <= kSmemBytes, "down epilogue tile exceeds the LDS rings");
 static_assert(3 * (kSmemBytes + 2 * kMT * 4) <= 160 * 1024, "three workgroups per compute unit");
 
 // Physical 16-byte chunk of logical chunk c in A-tile row r is c ^ swz(r). 16 consecutive
@@ -139,21 +143,12 @@ __device__ __forceinline__ void ring_sync() {
 struct PreArgs {
     int T, d, k, I, Is, E;
     const uint16_t *x16;        // gate/up A rows [T, d], fp16
-    const int32_t *perm, *offsets, *tile_off;
+    const int32_t *perm, *tile_off;
+    const int4 *items;          // routed work items (expert, row tile, first pair row, pairs)
     moe_qmat gate, up, sh_gate, sh_up, down, sh_down;
     uint16_t *h_r, *h_s;        // hidden activations (fp16): [T k, I] bucket order, [T, I_s]
     float *r, *sh;
 };
-
-__device__ __forceinline__ int find_expert(const int32_t *tile_off, int E, int m) {
-    int lo = 0, hi = E;  // tile_off[lo] <= m < tile_off[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (tile_off[mid] <= m) lo = mid;
-        else hi = mid;
-    }
-    return lo;
-}
 
 // Eight fp16 weights scale * q + bias from one device-layout word (elements j = 0..7 of a
 // K-step; element j in nibble j even ? j/2 : 4 + j/2). Pair p (elements 2p, 2p + 1) is
@@ -212,11 +207,12 @@ __global__ __launch_bounds__(kPreWG, 3) void k_pre_gemm(PreArgs a) {
         shared_item = false;
         const int mg = 8 * (j / NTr) + (i & 7);
         nt = j % NTr;
+        const int4 it = a.items[mg];   // in bounds: the table holds the worst-case tile count
         if (mg >= a.tile_off[E]) return;
-        e = find_expert(a.tile_off, E, mg);
-        mt = mg - a.tile_off[e];
-        rowbase = a.offsets[e];
-        count = a.offsets[e + 1] - rowbase;
+        e = it.x;
+        mt = it.y;
+        rowbase = it.z;
+        count = it.w;
     }
     const int K = MODE == 0 ? a.d : (shared_item ? a.Is : a.I);
     const int G = K / 64;   // ring steps: one 64-input group each
@@ -414,18 +410,33 @@ __global__ __launch_bounds__(kPreWG, 3) void k_pre_gemm(PreArgs a) {
             for (int i = 0; i < 4; ++i) o[i] = src[i];
         }
     } else {
+        // the 128 x 128 fp32 output tile leaves through LDS in two halves of 64 rows, each
+        // row as one 512-byte run of 16-byte stores
         float *out = shared_item ? a.sh : a.r;
-        const int c0 = (nt * 4 + wave) * 32 + n;
+        float *O = reinterpret_cast<float *>(smem);
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms)
-            if (ms < live_ms) {
+        for (int part = 0; part < 2; ++part) {
+            if (2 * part < live_ms) {
+                if (part) __syncthreads();   // the first half has left
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = 32 * ms + 8 * (v >> 2) + 4 * half + (v & 3);
-                    const int dst = drow[row];
-                    if (dst >= 0) out[(size_t)dst * a.d + c0] = acc[ms][v];
+                for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int row = 32 * mh + 8 * (v >> 2) + 4 * half + (v & 3);
+                        O[row * kOPitch + wave * 32 + n] = acc[2 * part + mh][v];
+                    }
+                __syncthreads();
+                const int c = tid & 31;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int row = (tid >> 5) + 8 * i;
+                    const int dst = drow[64 * part + row];
+                    if (dst >= 0)
+                        *reinterpret_cast<f32x4_t *>(out + (size_t)dst * a.d + nt * 128 + 4 * c) =
+                            *reinterpret_cast<const f32x4_t *>(O + row * kOPitch + 4 * c);
                 }
             }
+        }
     }
 }
 
@@ -457,8 +468,8 @@ PreArgs make_args(const moe_layer *L, int T) {
     a.E = D.n_experts;
     a.x16 = L->ws.x16;
     a.perm = L->ws.perm;
-    a.offsets = L->ws.offsets;
     a.tile_off = L->ws.tile_off;
+    a.items = L->ws.items;
     a.gate = L->w.gate;
     a.up = L->w.up;
     a.sh_gate = L->w.sh_gate;
@@ -478,8 +489,7 @@ int pre_grid(const moe_layer *L, int T, int mode) {
     const moe_dims &D = L->dims;
     const int NTs = mode == 0 ? D.d_shared / 64 : D.d_model / 128;
     const int NTr = mode == 0 ? D.d_expert / 64 : D.d_model / 128;
-    const int P = T * D.top_k;
-    const int Mr = cdiv(P, kMT) + (D.n_experts < P ? D.n_experts : P);
+    const int Mr = max_routed_tiles(T, D.top_k, D.n_experts);
     return roundup(cdiv(T, kMT), 8) * NTs + roundup(Mr, 8) * NTr;
 }
 

@@ -257,10 +257,12 @@ __global__ __launch_bounds__(256) void k_bucket_rank(const int32_t *__restrict__
         chunk_cnt[(size_t)blockIdx.x * E + i] = wcnt[0][i] + wcnt[1][i] + wcnt[2][i] + wcnt[3][i];
 }
 
-// Counts, offsets, per-chunk bases and GEMM tile offsets. grid 1; block 1024
+// Counts, offsets, per-chunk bases, GEMM tile offsets and the GEMM's routed work items
+// (expert, row tile, first pair row, pairs of the expert), one per row tile in expert order.
+// grid 1; block 1024
 __global__ __launch_bounds__(1024) void k_bucket_scan(int nchunks, int E, int32_t *__restrict__ chunk_base,
                                                       int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-                                                      int32_t *__restrict__ tile_off, int mt) {
+                                                      int32_t *__restrict__ tile_off, int mt, int4 *__restrict__ items) {
     __shared__ int32_t sc[MOE_MAX_EXPERTS];
     __shared__ int32_t st[MOE_MAX_EXPERTS];
     const int e = threadIdx.x;
@@ -289,6 +291,7 @@ __global__ __launch_bounds__(1024) void k_bucket_scan(int nchunks, int E, int32_
             tile_off[i] = b;
             const int ca = sc[i], cb = st[i];
             sc[i] = a;
+            st[i] = b;
             a += ca;
             b += cb;
         }
@@ -296,6 +299,10 @@ __global__ __launch_bounds__(1024) void k_bucket_scan(int nchunks, int E, int32_
         tile_off[E] = b;
     }
     __syncthreads();
+    if (e < E) {
+        const int ntile = (run + mt - 1) / mt;
+        for (int j = 0; j < ntile; ++j) items[st[e] + j] = make_int4(e, j, sc[e], run);
+    }
     if (e < E) {
         const int base = sc[e];
         for (int c0 = 0; c0 < nchunks; c0 += 16) {
@@ -362,7 +369,7 @@ hipError_t launch_bucket_rank(const moe_layer *L, int T, const int32_t *idx, hip
 hipError_t launch_bucket_scan(const moe_layer *L, int T, hipStream_t s) {
     const int P = T * L->dims.top_k;
     launch(k_bucket_scan, dim3(1), dim3(1024), 0, s, cdiv(P, kChunk), L->dims.n_experts,
-                       L->ws.chunk_base, L->ws.counts, L->ws.offsets, L->ws.tile_off, kMT);
+                       L->ws.chunk_base, L->ws.counts, L->ws.offsets, L->ws.tile_off, kMT, L->ws.items);
     return hipGetLastError();
 }
 

@@ -233,6 +233,7 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.counts, E);
     plan.take(&ws.offsets, E + 1);
     plan.take(&ws.tile_off, E + 1);
+    plan.take(&ws.items, (size_t)roundup(max_routed_tiles((int)Tm, k, E), 8));   // the GEMM grid rounds to 8
     plan.take(&ws.chunk_base, nchunks * E);
     plan.take(&ws.rank, P);
     plan.take(&ws.perm, P);
@@ -271,6 +272,7 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     rebase(ws.counts, base);
     rebase(ws.offsets, base);
     rebase(ws.tile_off, base);
+    rebase(ws.items, base);
     rebase(ws.chunk_base, base);
     rebase(ws.rank, base);
     rebase(ws.perm, base);

@@ -23,6 +23,13 @@ constexpr int kTileRows = 32;       // rows per 1 KiB weight tile
 constexpr int kMT = 128;            // prefill GEMM rows per workgroup tile
 constexpr int kChunk = 256;         // pairs per bucketing chunk
 
+// Routed row tiles of a prefill chunk of T tokens: at most ceil(T k / kMT) + min(E, T k)
+// (every expert with pairs adds at most one partially filled tile).
+inline int max_routed_tiles(int T, int k, int E) {
+    const int P = T * k;
+    return (P + kMT - 1) / kMT + (E < P ? E : P);
+}
+
 __host__ __device__ inline int roundup(int a, int b) { return (a + b - 1) / b * b; }
 constexpr int cdiv_c(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
@@ -54,6 +61,7 @@ struct Workspace {
     int32_t *counts;      // [E]
     int32_t *offsets;     // [E+1]
     int32_t *tile_off;    // [E+1]              prefix sum of ceil(count/kMT)
+    int4 *items;          // [max routed tiles]  (expert, row tile, first pair row, pairs of the expert)
     int32_t *chunk_base;  // [nchunks, E]
     int32_t *rank;        // [maxT*k]
     int32_t *perm;        // [maxT*k]

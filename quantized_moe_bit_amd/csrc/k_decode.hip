@@ -39,7 +39,7 @@ namespace {
 
 constexpr int kRW = 4;      // router experts (waves) per workgroup
 constexpr int kBW = 4;      // waves per gate/up workgroup
-constexpr int kMPB = 3;     // group pairs a gate/up wave loads before computing
+constexpr int kMPB = 6;     // group pairs a gate/up wave loads before computing
 constexpr int kMPC = 6;     // group pairs a down wave loads before computing
 constexpr int kXC = 4;      // 16-byte x chunks per gate/up thread: d <= 64 kBW * 8 * kXC
 

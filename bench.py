@@ -265,15 +265,16 @@ def main():
         hd = tokens_to_device(h0, dev)
         xb = torch.empty((1, d), dtype=torch.int16, device=dev)
         yb = torch.empty((1, d), dtype=torch.float32, device=dev)
+        hb = torch.empty_like(xb)
         handles = [L.handle for L in stack]
         for t in range(8):          # warmup on the first tokens, then the timed pass from h0
-            B.moe_stack_forward_decode(handles, hd[t:t + 1], 1, xb, yb)
+            B.moe_stack_forward_decode(handles, hd[t:t + 1], 1, xb, yb, hb)
         hd.copy_(tokens_to_device(h0, dev))
         torch.cuda.synchronize()
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s0.record()
         for t in range(ws.tokens):
-            B.moe_stack_forward_decode(handles, hd[t:t + 1], 1, xb, yb)
+            B.moe_stack_forward_decode(handles, hd[t:t + 1], 1, xb, yb, hb)
         s1.record()
         torch.cuda.synchronize()
         ms_tok = s0.elapsed_time(s1) / ws.tokens

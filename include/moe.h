@@ -157,14 +157,15 @@ moe_status moe_stack_glue(const uint16_t *h, const float *y, uint16_t *h_next, u
  * 1 <= T <= every layer's decode capacity. h (bf16 [T, d]) is the residual stream on entry
  * and is updated in place; for l = 0 .. n_layers-1 in order:
  *   x = bf16(h / sqrt(mean(h^2) + 1e-6));  y = layer_l(x);  h = bf16(h + y)
- * (moe_stack_glue's two steps around moe_forward_decode). x_buf (bf16 [T, d]) and y_buf
- * (fp32 [T, d]) are caller-owned scratch and hold the last layer's x and y on return.
- * All layers must have the same d_model (MOE_E_SHAPE); every layer handle is used on this
- * stream. MOE_E_INVALID for NULL arguments or n_layers < 1, MOE_E_CAPACITY for T above a
- * layer's decode capacity; T = 0 is a no-op.
+ * (moe_stack_glue's two steps around moe_forward_decode; the residual step before a layer
+ * runs inside that layer's router launch when T * d_model <= 16384). x_buf, h_buf (bf16
+ * [T, d]) and y_buf (fp32 [T, d]) are caller-owned scratch; x_buf and y_buf hold the last
+ * layer's x and y on return. All layers must have the same d_model (MOE_E_SHAPE); every layer
+ * handle is used on this stream. MOE_E_INVALID for NULL arguments or n_layers < 1,
+ * MOE_E_CAPACITY for T above a layer's decode capacity; T = 0 is a no-op.
  */
 moe_status moe_stack_forward_decode(moe_layer *const *layers, int32_t n_layers, uint16_t *h, int32_t T,
-                                    uint16_t *x_buf, float *y_buf, void *hip_stream);
+                                    uint16_t *x_buf, float *y_buf, uint16_t *h_buf, void *hip_stream);
 
 /* ---------------------------------------------------------------- host-side weight layout */
 

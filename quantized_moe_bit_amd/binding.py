@@ -61,7 +61,7 @@ def lib() -> C.CDLL:
             "moe_forward_decode": (st, [vp, vp, i32, vp, vp]),
             "moe_forward_prefill": (st, [vp, vp, i32, vp, vp]),
             "moe_stack_glue": (st, [vp, vp, vp, vp, i32, i32, vp]),
-            "moe_stack_forward_decode": (st, [C.POINTER(vp), i32, vp, i32, vp, vp, vp]),
+            "moe_stack_forward_decode": (st, [C.POINTER(vp), i32, vp, i32, vp, vp, vp, vp]),
             "moe_packed_bytes": (C.c_size_t, [i32, i32, i32, i32, i32]),
             "moe_repack": (st, [i32, i32, i32, i32, C.POINTER(moe_host_qmat), vp, vp]),
             "moe_unrepack": (st, [i32, i32, i32, i32, vp, vp, vp, vp, vp]),
@@ -149,9 +149,9 @@ def moe_stack_glue(h, y, h_next, x_next, T, d, stream=None):
            "moe_stack_glue")
 
 
-def moe_stack_forward_decode(handles, h, T, x_buf, y_buf, stream=None):
+def moe_stack_forward_decode(handles, h, T, x_buf, y_buf, h_buf, stream=None):
     arr = (C.c_void_p * len(handles))(*handles)
-    _check(lib().moe_stack_forward_decode(arr, len(handles), _ptr(h), T, _ptr(x_buf), _ptr(y_buf),
+    _check(lib().moe_stack_forward_decode(arr, len(handles), _ptr(h), T, _ptr(x_buf), _ptr(y_buf), _ptr(h_buf),
                                           _stream(stream)), "moe_stack_forward_decode")
 
 

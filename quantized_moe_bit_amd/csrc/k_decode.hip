@@ -42,6 +42,7 @@ constexpr int kBW = 4;      // waves per gate/up workgroup
 constexpr int kMPB = 6;     // group pairs a gate/up wave loads before computing
 constexpr int kMPC = 6;     // group pairs a down wave loads before computing
 constexpr int kXC = 4;      // 16-byte x chunks per gate/up thread: d <= 64 kBW * 8 * kXC
+constexpr size_t kGlueLdsMax = 32768;   // bf16 bytes of x the fused residual step keeps in LDS
 
 // ----------------------------------------------------------------------------- router
 // The wave's expert e; lane g handles input group g (and g + 64, ... for d > 4096).
@@ -328,18 +329,42 @@ struct DecArgs {
     float *hs_r;            // [T*k][I/16]      sums of 16 consecutive routed h values
     float *hs_s;            // [T][I_s/16]      sums of 16 consecutive shared h values
     float *y;
+    // fused residual step of a layer stack (router launch only): h_in, y_in (null before the
+    // first layer) -> h_out (written by workgroup 0) and x (written by workgroup 0 to x_out,
+    // and kept in LDS by every workgroup for its own router waves)
+    const uint16_t *h_in;
+    const float *y_in;
+    uint16_t *h_out, *x_out;
 };
 
 // ----------------------------------------------------------------------------- launch A
-// grid: ceil(E / kRW); block 64 * kRW; LDS kRW * T * (d/64) floats
+// grid: ceil(E / kRW); block 64 * kRW; LDS kRW * T * (d/64) floats, plus (GLUE) T * d bf16
+// and 4 doubles. With GLUE every workgroup first forms x = norm(bf16(h_in + y_in)) for its
+// own use (the same fp64 residual step as the stack glue kernel; workgroup 0 also stores h_out
+// and x_out for the later launches), so the stack needs no separate residual launch.
+template <bool GLUE>
 __global__ __launch_bounds__(64 * kRW) void k_dec_router(DecArgs a) {
+    static_assert(64 * kRW == kGlueWG, "the residual step runs on one full workgroup");
     extern __shared__ __align__(16) unsigned char smem[];
     const int G = a.d / 64;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     float *Ps = reinterpret_cast<float *>(smem);     // [kRW][T][G]
+    const uint16_t *x = a.x;
+    if (GLUE) {
+        uint16_t *xs = reinterpret_cast<uint16_t *>(smem + sizeof(float) * kRW * a.T * G);
+        double *red = reinterpret_cast<double *>(xs + (size_t)a.T * a.d);
+        for (int t = 0; t < a.T; ++t)
+            glue_token(a.h_in + (size_t)t * a.d, a.y_in ? a.y_in + (size_t)t * a.d : nullptr,
+                       blockIdx.x == 0 ? a.h_out + (size_t)t * a.d : nullptr, xs + (size_t)t * a.d, a.d, red);
+        __syncthreads();
+        if (blockIdx.x == 0)
+            for (int i = tid; i < a.T * a.d / 8; i += 64 * kRW)
+                *reinterpret_cast<u32x4_t *>(a.x_out + 8 * i) = *reinterpret_cast<const u32x4_t *>(xs + 8 * i);
+        x = xs;
+    }
     const int e = blockIdx.x * kRW + wave;
     float *P = Ps + (size_t)wave * a.T * G;
-    if (e < a.E) router_wave(a.x, a.T, a.d, e, a.rq, a.rsb, P, e == 0 ? a.xg : nullptr);
+    if (e < a.E) router_wave(x, a.T, a.d, e, a.rq, a.rsb, P, e == 0 ? a.xg : nullptr);
     __syncthreads();
     if (e < a.E && lane < a.T) {
 #pragma clang fp contract(off)
@@ -544,7 +569,7 @@ __global__ __launch_bounds__(MAXT) void k_dec_down(DecArgs a) {
 
 DecArgs dec_args(const moe_layer *L, const uint16_t *x, int T, float *y) {
     const moe_dims &D = L->dims;
-    DecArgs a;
+    DecArgs a{};
     a.x = x;
     a.T = T;
     a.d = D.d_model;
@@ -601,7 +626,23 @@ hipError_t launch_dec_router(const moe_layer *L, const uint16_t *x, int T, float
     DecArgs a = dec_args(L, x, T, nullptr);
     a.logits = logits;
     const size_t lds = sizeof(float) * kRW * T * (D.d_model / 64);
-    launch(k_dec_router, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
+    launch(k_dec_router<false>, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
+    return hipGetLastError();
+}
+
+bool dec_router_glue_fits(const moe_dims &D, int T) { return (size_t)T * D.d_model * 2 <= kGlueLdsMax; }
+
+hipError_t launch_dec_router_glue(const moe_layer *L, const uint16_t *h_in, const float *y_in, uint16_t *h_out,
+                                  uint16_t *x_out, int T, hipStream_t s) {
+    const moe_dims &D = L->dims;
+    DecArgs a = dec_args(L, x_out, T, nullptr);
+    a.h_in = h_in;
+    a.y_in = y_in;
+    a.h_out = h_out;
+    a.x_out = x_out;
+    const size_t lds = sizeof(float) * kRW * T * (D.d_model / 64) + sizeof(uint16_t) * T * D.d_model +
+                       sizeof(double) * (kGlueWG / 64);
+    launch(k_dec_router<true>, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
     return hipGetLastError();
 }
 

@@ -383,7 +383,7 @@ moe_status moe_stack_glue(const uint16_t *h, const float *y, uint16_t *h_next, u
 }
 
 moe_status moe_stack_forward_decode(moe_layer *const *layers, int32_t n_layers, uint16_t *h, int32_t T,
-                                    uint16_t *x_buf, float *y_buf, void *hip_stream) {
+                                    uint16_t *x_buf, float *y_buf, uint16_t *h_buf, void *hip_stream) {
     clear_error();
     if (n_layers < 1 || !layers) return fail(MOE_E_INVALID, "moe_stack_forward_decode: no layers");
     if (T < 0) return fail(MOE_E_SHAPE, "moe_stack_forward_decode: T = %d is negative", T);
@@ -398,19 +398,30 @@ moe_status moe_stack_forward_decode(moe_layer *const *layers, int32_t n_layers, 
                         l, L->max_dec);
     }
     if (T == 0) return MOE_OK;
-    if (!h || !x_buf || !y_buf) return fail(MOE_E_INVALID, "moe_stack_forward_decode: NULL buffer");
-    if (!aligned16(h) || !aligned16(x_buf) || !aligned16(y_buf))
+    if (!h || !x_buf || !y_buf || !h_buf) return fail(MOE_E_INVALID, "moe_stack_forward_decode: NULL buffer");
+    if (!aligned16(h) || !aligned16(x_buf) || !aligned16(y_buf) || !aligned16(h_buf))
         return fail(MOE_E_ALIGN, "moe_stack_forward_decode: buffer not 16-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const int d = layers[0]->dims.d_model;
-    for (int l = 0; l <= n_layers; ++l) {
-        // residual add of the previous layer's output (none before layer 0), then its input norm
-        moe_layer *L = layers[l < n_layers ? l : n_layers - 1];
-        RUN(K_GLUE, launch_glue(h, l ? y_buf : nullptr, h, x_buf, T, d, s));
-        if (l == n_layers) break;
-        RUN(K_DEC_ROUTER, launch_dec_router(L, x_buf, T, L->ws.logits, s));
+    // the residual stream alternates between h and h_buf: layer l reads the stream before it
+    // from one and leaves the stream after the previous layer's residual add in the other
+    for (int l = 0; l < n_layers; ++l) {
+        moe_layer *L = layers[l];
+        uint16_t *src = (l & 1) ? h_buf : h, *dst = (l & 1) ? h : h_buf;
+        const float *yp = l ? y_buf : nullptr;
+        if (dec_router_glue_fits(L->dims, T)) {
+            RUN(K_DEC_ROUTER, launch_dec_router_glue(L, src, yp, dst, x_buf, T, s));
+        } else {
+            RUN(K_GLUE, launch_glue(src, yp, dst, x_buf, T, d, s));
+            RUN(K_DEC_ROUTER, launch_dec_router(L, x_buf, T, L->ws.logits, s));
+        }
         RUN(K_DEC_GATEUP, launch_dec_gateup(L, x_buf, T, s));
         RUN(K_DEC_DOWN, launch_dec_down(L, T, y_buf, s));
+    }
+    {   // the last layer's residual add, into h
+        moe_layer *L = layers[n_layers - 1];
+        uint16_t *src = ((n_layers - 1) & 1) ? h : h_buf;
+        RUN(K_GLUE, launch_glue(src, y_buf, h, x_buf, T, d, s));
     }
     return MOE_OK;
 }

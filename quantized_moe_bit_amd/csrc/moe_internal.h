@@ -128,6 +128,9 @@ inline void launch(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, A
 // Kernel launchers (each enqueues on stream, returns hipGetLastError()).
 hipError_t launch_dec_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s);
 hipError_t launch_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s);
+bool dec_router_glue_fits(const moe_dims &D, int T);
+hipError_t launch_dec_router_glue(const moe_layer *L, const uint16_t *h_in, const float *y_in, uint16_t *h_out,
+                                  uint16_t *x_out, int T, hipStream_t s);
 hipError_t launch_router_table(const moe_layer *L, hipStream_t s);
 size_t router_table_floats(const moe_dims &D);
 hipError_t launch_topk(const moe_layer *L, int T, const float *logits, int32_t *idx, float *w, hipStream_t s);

@@ -160,9 +160,9 @@ def test_calls_reject_null_layer_and_bad_sizes():
     assert L.moe_stack_glue(None, None, None, None, 2, 8200, None) == B.MOE_E_SHAPE   # d > 8192
     assert L.moe_profile_enable(None, 1) == B.MOE_E_INVALID
     one_null = (C.c_void_p * 1)(None)
-    assert L.moe_stack_forward_decode(None, 1, None, 1, None, None, None) == B.MOE_E_INVALID
-    assert L.moe_stack_forward_decode(one_null, 0, None, 1, None, None, None) == B.MOE_E_INVALID
-    assert L.moe_stack_forward_decode(one_null, 1, None, 1, None, None, None) == B.MOE_E_INVALID
+    assert L.moe_stack_forward_decode(None, 1, None, 1, None, None, None, None) == B.MOE_E_INVALID
+    assert L.moe_stack_forward_decode(one_null, 0, None, 1, None, None, None, None) == B.MOE_E_INVALID
+    assert L.moe_stack_forward_decode(one_null, 1, None, 1, None, None, None, None) == B.MOE_E_INVALID
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -81,14 +81,24 @@ def test_stack_30_layers_256_tokens():
     h = tokens_to_device(h0, dev)
     xb = torch.empty((1, D.d_model), dtype=torch.int16, device=dev)
     yb = torch.empty((1, D.d_model), dtype=torch.float32, device=dev)
+    hb = torch.empty_like(xb)
     handles = [L.handle for L in layers]
     for t in range(T):
-        B.moe_stack_forward_decode(handles, h[t:t + 1], 1, xb, yb)
+        B.moe_stack_forward_decode(handles, h[t:t + 1], 1, xb, yb, hb)
     torch.cuda.synchronize()
     hf = bits(h)
     np.testing.assert_array_equal(hf[sample], bits(hs))
     assert np.all(np.isfinite(synth.bf16_bits_to_f32(hf)))
     say(f"stack entry point: {T} tokens x {NL} layers, sampled rows identical to the layer-by-layer run")
+    # the sampled tokens in one call: the residual step runs in its own launch (T d above the
+    # router's LDS budget) and gives the same bits
+    hS = tokens_to_device(h0[sample], dev)
+    xS, hbS = torch.empty_like(hS), torch.empty_like(hS)
+    yS = torch.empty((S, D.d_model), dtype=torch.float32, device=dev)
+    B.moe_stack_forward_decode(handles, hS, S, xS, yS, hbS)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(hS), bits(hs))
+    say(f"stack entry point with {S} tokens per call: identical")
     for L in layers:
         L.close()
 
@@ -102,14 +112,15 @@ def test_stack_rejects_mixed_widths_and_capacity():
     h = torch.zeros((8, tiny.dims.d_model), dtype=torch.int16, device="cuda:0")
     xb = torch.empty_like(h)
     yb = torch.empty((8, tiny.dims.d_model), dtype=torch.float32, device="cuda:0")
+    hb = torch.empty_like(h)
     with pytest.raises(B.MoeError) as ei:
-        B.moe_stack_forward_decode([a.handle, a.handle], h, 8, xb, yb)
+        B.moe_stack_forward_decode([a.handle, a.handle], h, 8, xb, yb, hb)
     assert ei.value.status == B.MOE_E_CAPACITY
     with pytest.raises(B.MoeError) as ei:
-        B.moe_stack_forward_decode([a.handle, b.handle], h, 1, xb, yb)
+        B.moe_stack_forward_decode([a.handle, b.handle], h, 1, xb, yb, hb)
     assert ei.value.status == B.MOE_E_SHAPE
     h0 = h.clone()
-    B.moe_stack_forward_decode([a.handle, a.handle], h, 0, xb, yb)     # T = 0: no-op
+    B.moe_stack_forward_decode([a.handle, a.handle], h, 0, xb, yb, hb)     # T = 0: no-op
     torch.cuda.synchronize()
     assert torch.equal(h, h0)
     a.close()

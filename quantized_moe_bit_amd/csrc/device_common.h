@@ -96,6 +96,12 @@ __device__ __forceinline__ float gelu_tanh_f32(float v) {
 
 __device__ __forceinline__ u32x4_t ld16(const void *p) { return *reinterpret_cast<const u32x4_t *>(p); }
 
+// 16-byte store with the non-temporal hint (streamed past the caches), for a large output no
+// later kernel of the call reads.
+__device__ __forceinline__ void st16_nt(void *p, u32x4_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(p));
+}
+
 // fp64 -> bf16 bits, round to nearest even with a single rounding: fp64 -> fp32 with
 // round-to-odd (24 significant bits, at least two more than bf16 keeps), then fp32 -> bf16
 // with round-to-nearest-even. Inputs are finite and within the fp32 range.

@@ -454,7 +454,7 @@ __global__ __launch_bounds__(256) void k_combine(int d, int k, const float *__re
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, rv[i], acc[i]);
     }
-    *reinterpret_cast<f32x4_t *>(y + (size_t)t * d + c) = acc;
+    st16_nt(y + (size_t)t * d + c, __builtin_bit_cast(u32x4_t, acc));
 }
 
 PreArgs make_args(const moe_layer *L, int T) {

@@ -62,78 +62,111 @@ __global__ __launch_bounds__(256) void k_xsum(const uint16_t *__restrict__ x, in
     xsum[i] = X;
 }
 
-// Prefill router: lane = token, wave = kRNE consecutive experts, workgroup = 4 waves (64 tokens
-// x 4 kRNE experts). The 8-bit codes, scales and biases come as fp32 from a table built at
-// layer creation, read with wave-uniform (scalar) loads at constant offsets from one base, so
-// each fma takes its code from a scalar register. A lane converts its token's 64 inputs of
-// the current group to fp32 once for all kRNE experts and runs kRNE independent fma chains,
-// 16 inputs at a time. Per (token, expert) the arithmetic is the fixed order stated at the top
-// of this file.
+// Prefill router: lane = token, wave = kRNE = 4 consecutive experts, workgroup = 4 waves (64
+// tokens x 16 experts). Per 64-input group the workgroup stages its tokens' inputs into LDS as
+// fp32, converted once for all waves and double-buffered (the next group's loads are in
+// flight during this group's chains). The codes come as fp32 from a table built at layer
+// creation: one 16-byte load per lane and 16-input chunk puts input j of the chunk for the
+// wave's four experts into lane j of every 16-lane row, and each fma takes its code from
+// there by a row broadcast (DPP row_newbcast), so no instruction is spent on moving codes.
+// Per (token, expert) the arithmetic is the fixed order stated at the top of this file.
 //
-// Table layout, per block of kRNE experts eb and group g (kRBlk floats): codes [4][kRNE][16]
-// (inputs 16 jc + j of expert kRNE eb + i at [jc][i][j]), then kRNE scales, then kRNE biases.
+// Table layout, per block of kRNE experts eb and group g (kRBlk floats): codes [4 jc][16 j][kRNE]
+// (input 16 jc + j of expert kRNE eb + i at [jc][j][i]), then kRNE scales, then kRNE biases.
 // Experts past E are zero.
 // grid: (ceil(T / 64), ceil(E / (4 kRNE))); block 256
+constexpr int kXPitch = 68;   // fp32 per staged token row: 16 lanes of one ds_read_b128 pass hit 64 distinct banks
+static_assert(kRNE == 4, "one 16-byte load per lane holds the four experts' codes of an input");
+
+// a += x * (lane J of q's 16-lane row), one instruction (the DPP source is a loaded register,
+// never one a VALU instruction has just written)
+template <int J>
+__device__ __forceinline__ void fma_rowbcast(float &a, float x, float q) {
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(a) : "v"(q), "v"(x), "n"(J));
+}
+template <int J>
+__device__ __forceinline__ void chunk_fmas(float (&A)[kRNE], const f32x4_t (&xv)[4], const f32x4_t &q) {
+#pragma unroll
+    for (int i = 0; i < kRNE; ++i) fma_rowbcast<J>(A[i], xv[J >> 2][J & 3], q[i]);
+    if constexpr (J + 1 < 16) chunk_fmas<J + 1>(A, xv, q);
+}
+
 __global__ __launch_bounds__(256) void k_router_tok(const uint16_t *__restrict__ x, int T, int d, int E,
                                                     const float *__restrict__ tab, const float *__restrict__ xsum,
                                                     const float *__restrict__ logit_bias, float *__restrict__ logits) {
+    __shared__ __align__(16) float xs[2][64][kXPitch];
     const int G = d / 64;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int eb = blockIdx.y * 4 + wave;
-    const int e0 = eb * kRNE;
-    if (e0 >= E) return;   // wave-uniform; the kernel has no barriers
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int eb = min(blockIdx.y * 4 + wave, cdiv(E, kRNE) - 1);   // waves past E compute a valid block, store nothing
+    const int e0 = (blockIdx.y * 4 + wave) * kRNE;
     const int t = blockIdx.x * 64 + lane;
-    const int tc = t < T ? t : T - 1;
-    const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(x + (size_t)tc * d);
-    const float *xs = xsum + (size_t)tc * G;
+    const float *xsr = xsum + (size_t)(t < T ? t : T - 1) * G;
+    // staging: thread -> token tid/4, inputs 16 (tid%4) .. +15 of the group
+    const int st = tid >> 2, sq = tid & 3;
+    const int stok = min((int)blockIdx.x * 64 + st, T - 1);
+    const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(x + (size_t)stok * d + 16 * sq);
     const float *blk = tab + (size_t)eb * G * kRBlk;
+    auto stage = [&](int buf, const u32x4_t (&v)[2]) {
+        f32x4_t f[4];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                f[2 * c + (w >> 1)][2 * (w & 1)] = bf16_to_f32(v[c][w] & 0xFFFFu);
+                f[2 * c + (w >> 1)][2 * (w & 1) + 1] = __uint_as_float(v[c][w] & 0xFFFF0000u);
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4_t *>(&xs[buf][st][16 * sq + 4 * i]) = f[i];
+    };
+    auto load_q = [&](int g, f32x4_t (&q)[4]) {
+#pragma unroll
+        for (int jc = 0; jc < 4; ++jc)
+            q[jc] = *reinterpret_cast<const f32x4_t *>(blk + (size_t)g * kRBlk + (16 * jc + (lane & 15)) * kRNE);
+    };
     float L[kRNE];
 #pragma unroll
     for (int i = 0; i < kRNE; ++i) L[i] = 0.0f;
-    u32x4_t nxt[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) nxt[c] = xr[c];
-    float Xn = xs[0];
-    for (int g = 0; g < G; ++g, blk += kRBlk) {
-        float xf[64];
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                xf[8 * c + 2 * w] = bf16_to_f32(nxt[c][w] & 0xFFFFu);
-                xf[8 * c + 2 * w + 1] = __uint_as_float(nxt[c][w] & 0xFFFF0000u);
-            }
+    u32x4_t nv[2] = {xr[0], xr[1]};
+    f32x4_t qa[4], qb[4];   // codes of the even and odd groups (loaded straight into place)
+    load_q(0, qa);
+    stage(0, nv);
+    float Xn = xsr[0];
+    __syncthreads();
+    auto group = [&](int g, const f32x4_t (&q)[4], f32x4_t (&qnext)[4]) {
+        const int buf = g & 1;
         const float X = Xn;
-        {   // next group's inputs in flight during this group's chains (the last group re-reads itself)
+        {   // next group's loads in flight during this group's chains (the last group re-reads itself)
             const int gn = g + 1 < G ? g + 1 : g;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) nxt[c] = xr[8 * gn + c];
-            Xn = xs[gn];
+            nv[0] = xr[8 * gn];
+            nv[1] = xr[8 * gn + 1];
+            load_q(gn, qnext);
+            Xn = xsr[gn];
         }
         float A[kRNE];
 #pragma unroll
         for (int i = 0; i < kRNE; ++i) A[i] = 0.0f;
 #pragma unroll
         for (int jc = 0; jc < 4; ++jc) {
-            // keeps each chunk's code loads next to their use (scalar register pressure)
-            asm volatile("" ::: "memory");
-            float q[kRNE][16];
+            f32x4_t xv[4];
 #pragma unroll
-            for (int i = 0; i < kRNE; ++i)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) q[i][j] = blk[(jc * kRNE + i) * 16 + j];
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-#pragma unroll
-                for (int i = 0; i < kRNE; ++i) A[i] = __builtin_fmaf(xf[16 * jc + j], q[i][j], A[i]);
+            for (int c = 0; c < 4; ++c) xv[c] = *reinterpret_cast<const f32x4_t *>(&xs[buf][lane][16 * jc + 4 * c]);
+            chunk_fmas<0>(A, xv, q[jc]);
         }
+        const float *sb = blk + (size_t)g * kRBlk + 64 * kRNE;
 #pragma unroll
         for (int i = 0; i < kRNE; ++i) {
-            const float sc = blk[64 * kRNE + i], bi = blk[65 * kRNE + i];
+            const float sc = sb[i], bi = sb[kRNE + i];
             const float bX = bi * X;
             L[i] = L[i] + __builtin_fmaf(sc, A[i], bX);
         }
+        // the other buffer was last read in group g - 1, which every wave has finished
+        if (g + 1 < G) stage(buf ^ 1, nv);
+        __syncthreads();
+    };
+    for (int g = 0; g < G; g += 2) {
+        group(g, qa, qb);
+        if (g + 1 < G) group(g + 1, qb, qa);
     }
     if (t >= T) return;
 #pragma unroll
@@ -143,7 +176,7 @@ __global__ __launch_bounds__(256) void k_router_tok(const uint16_t *__restrict__
     }
 }
 
-// The router table k_router_tok reads (codes, scales and biases as exact fp32).
+// The router table k_router_tok reads (codes, scales and biases as exact fp32; layout above).
 // grid ceil(n / 256) with n = ceil(E / kRNE) * G * kRBlk; block 256
 __global__ __launch_bounds__(256) void k_router_table(const uint8_t *__restrict__ q, const uint32_t *__restrict__ sb,
                                                       int E, int d, float *__restrict__ out) {
@@ -156,7 +189,7 @@ __global__ __launch_bounds__(256) void k_router_table(const uint8_t *__restrict_
     const int g = (int)(bg % G), eb = (int)(bg / G);
     float v = 0.0f;
     if (r < 64 * kRNE) {
-        const int jc = r / (16 * kRNE), ii = (r / 16) % kRNE, j = r % 16;
+        const int jc = r / (16 * kRNE), j = (r / kRNE) % 16, ii = r % kRNE;
         const int e = eb * kRNE + ii;
         if (e < E) v = (float)q[(size_t)e * d + 64 * g + 16 * jc + j];
     } else {

@@ -26,14 +26,18 @@ constexpr int kPreWG = 256;
 
 // LDS rings of the K loop (one 64-input group per step). A ring: kAStages stages of the A
 // tile (128 rows x 64 inputs, 16-bit, rows of 128 B with the 16-byte chunks XOR-swizzled),
-// loaded kAStages - 1 steps ahead by all four waves together. B ring: kBStages stages of the
-// four 1 KiB code tiles and their scale/bias words (64 per wave, rows duplicated), each wave
-// loading its own tile kBStages - 1 steps ahead. Everything arrives by direct global->LDS
-// loads, so no staging registers are needed. Sized for three workgroups per compute unit.
+// loaded one step ahead by all four waves together. B ring: kBStages stages of the four 1 KiB
+// code tiles and their scale/bias words (64 per wave, rows duplicated), each wave loading its
+// own tile two steps ahead. Everything arrives by direct global->LDS loads, so no staging
+// registers are needed. The K loop is unrolled by kUnroll steps, a multiple of both ring
+// lengths, so every stage offset is a constant. Sized for three workgroups per compute unit.
 constexpr int kAStages = 2;
-constexpr int kBStages = 3;
-constexpr int kADist = kAStages - 1;   // steps the A loads run ahead
-constexpr int kBDist = kBStages - 1;   // steps the B loads run ahead
+constexpr int kBStages = 4;
+constexpr int kUnroll = 4;
+constexpr int kADist = 1;   // steps the A loads run ahead
+constexpr int kBDist = 2;   // steps the B loads run ahead
+static_assert(kADist < kAStages && kBDist < kBStages, "a stage is refilled only after its step");
+static_assert(kUnroll % kAStages == 0 && kUnroll % kBStages == 0, "constant stages per unrolled step");
 static_assert(kBDist >= kADist, "weights are requested no later than the A rows of a step");
 constexpr int kAStageBytes = kMT * 128;
 constexpr int kBStageBytes = 4 * 1024;
@@ -48,15 +52,17 @@ constexpr int kDmaPerStep = 6;   // per thread: 4 A chunks, 1 code chunk, 1 scal
 constexpr int kWaitA = 2 + kDmaPerStep * (kADist - 1);
 constexpr int kWaitB = kDmaPerStep * (kBDist - 1);
 constexpr int kWaitB0 = 2 * (kBDist - 1) + 4 * kADist;   // after the scale/bias word of step 0
-// gate/up epilogue tile (reusing the rings): u in fp32, then h in fp16 in the same space
-constexpr int kUPitch = 72;
-constexpr int kHPitch = 72;
-static_assert(kMT * kUPitch * 4 <= kSmemBytes && kMT * kHPitch * 2 <= kSmemBytes, "epilogue tile exceeds the LDS rings");
+// Gate/up epilogue tiles (reusing the rings once every wave has left the K loop): four 64-row x
+// 32-column fp32 tiles, one per wave. Rows are 160 B apart (16-byte aligned; the two rows one 32-bit store
+// instruction writes, four apart, start 32 banks apart).
+constexpr int kXPitch = 40;
+constexpr int kXTile = 64 * kXPitch * 4;
+static_assert(4 * kXTile <= kSmemBytes, "epilogue tiles exceed the LDS rings");
 // down epilogue: 64 rows x 128 fp32 per half (row pitch 136: the two rows one store instruction
 // writes start 32 banks apart)
 constexpr int kOPitch = 136;
 static_assert(64 * kOPitch * 4 <= kSmemBytes, "down epilogue tile exceeds the LDS rings");
-static_assert(3 * (kSmemBytes + 2 * kMT * 4) <= 160 * 1024, "three workgroups per compute unit");
+static_assert(kSmemBytes <= 53248, "at most 53,248 bytes of LDS per workgroup leave room for three per compute unit");
 
 // Physical 16-byte chunk of logical chunk c in A-tile row r is c ^ swz(r). 16 consecutive
 // rows read at one logical chunk then hit 16 distinct 16-byte bank groups (and any 8
@@ -130,6 +136,47 @@ __device__ __forceinline__ void dma16x4(const void *sbase, const uint32_t voff[4
         : "memory", "scc");
 }
 
+// All direct loads of one ring step with one save and restore of M0: the four A chunks
+// (sbase_a + voff_a[i] -> lds_a + 4096 i + 16 lane), then the wave's code tile (16 bytes per
+// lane) and its scale/bias words (4 bytes per lane). Issue order is the one the counted waits
+// assume.
+__device__ __forceinline__ void dma_step(const void *sbase_a, const uint32_t voff_a[4], const uint8_t *lds_a,
+                                         const void *sbase_b, uint32_t voff_b, const uint8_t *lds_b,
+                                         const void *sbase_s, uint32_t voff_s, const uint8_t *lds_s) {
+    const uint32_t ma = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_a);
+    const uint32_t mb = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_b);
+    const uint32_t ms = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_s);
+    const void *sa = uniform_ptr(sbase_a);
+    const void *sb = uniform_ptr(sbase_b);
+    const void *ss = uniform_ptr(sbase_s);
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %7\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %10\n\t"
+        "s_add_u32 m0, m0, 0x1000\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %10\n\t"
+        "s_add_u32 m0, m0, 0x1000\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %10\n\t"
+        "s_add_u32 m0, m0, 0x1000\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, %10\n\t"
+        "s_mov_b32 m0, %8\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %5, %11\n\t"
+        "s_mov_b32 m0, %9\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %6, %12\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "v"(voff_a[0]), "v"(voff_a[1]), "v"(voff_a[2]), "v"(voff_a[3]), "v"(voff_b), "v"(voff_s), "s"(ma), "s"(mb),
+          "s"(ms), "s"(sa), "s"(sb), "s"(ss)
+        : "memory", "scc");
+}
+
 // Ring barrier of step g: step g's A tile has landed for this wave (direct loads retire in
 // issue order and are counted by vmcnt) and for every wave (the barrier), which also frees
 // the A stage about to be refilled; lgkmcnt(0): this wave's LDS reads of the stages about to
@@ -169,8 +216,6 @@ __device__ __forceinline__ f16x8_t dequant_frag(uint32_t w, f16x2_t s2, f16x2_t 
 template <int MODE>  // 0: gate/up + GeGLU, 1: down
 __global__ __launch_bounds__(kPreWG, 3) void k_pre_gemm(PreArgs a) {
     __shared__ __align__(16) uint8_t smem[kSmemBytes];
-    __shared__ int32_t srow[kMT];   // A source row (-1: padding)
-    __shared__ int32_t drow[kMT];   // destination row
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -218,22 +263,21 @@ __global__ __launch_bounds__(kPreWG, 3) void k_pre_gemm(PreArgs a) {
     const int G = K / 64;   // ring steps: one 64-input group each
     const uint16_t *Asrc = MODE == 0 ? a.x16 : (shared_item ? a.h_s : a.h_r);
 
+    // A source row of each tile row (-1: padding), staged at the start of the rings until every
+    // wave has its load offsets
+    int32_t *srow = reinterpret_cast<int32_t *>(smem);
     if (tid < kMT) {
         const int r = mt * kMT + tid;
-        int src = -1, dst = -1;
-        if (r < count) {
-            if (shared_item) {
-                src = r;
-                dst = r;
-            } else {
-                dst = rowbase + r;
-                src = MODE == 0 ? a.perm[dst] / a.k : dst;
-            }
-        }
+        int src = -1;
+        if (r < count) src = shared_item ? r : (MODE == 0 ? a.perm[rowbase + r] / a.k : rowbase + r);
         srow[tid] = src;
-        drow[tid] = dst;
     }
     __syncthreads();
+    // destination row of tile row r (-1: padding)
+    auto drow = [&](int r) {
+        const int rr = mt * kMT + r;
+        return rr < count ? (shared_item ? 0 : rowbase) + rr : -1;
+    };
 
     // Wave w owns one 32-row weight tile for all 128 token rows: gate/up -> gate blocks
     // 2nt, 2nt+1 (waves 0, 1) and up blocks 2nt, 2nt+1 (waves 2, 3); down -> block 4nt + w.
@@ -263,6 +307,7 @@ __global__ __launch_bounds__(kPreWG, 3) void k_pre_gemm(PreArgs a) {
         if (src < 0) src = srow[0];
         aro[i] = ((uint32_t)src * K + 8 * c) * 2;
     }
+    __syncthreads();   // srow is read; the ring loads may overwrite it
 
     // loads of one ring step: the A chunks of step ga (into A stage sa) and the wave's code
     // tile and scale/bias words of step gb (into B stage sbi)
@@ -305,16 +350,22 @@ __global__ __launch_bounds__(kPreWG, 3) void k_pre_gemm(PreArgs a) {
     // the fragments dequantized during step g - 1 and dequantizes those of step g + 1.
     auto kloop = [&](auto lms_c) {
         constexpr int LMS = decltype(lms_c)::value;
-        int sa = 0, sbi = 0;   // A and B stages of the current step
-        auto step = [&](int g, const f16x8_t (&bc)[4], f16x8_t (&bn)[4]) {
+        // step g (J = g mod kUnroll) multiplies with the fragments dequantized during step g - 1
+        // and dequantizes those of step g + 1
+        auto step = [&](auto j_c, int g, const f16x8_t (&bc)[4], f16x8_t (&bn)[4]) {
+            constexpr int J = decltype(j_c)::value;
+            constexpr int SA = J % kAStages, SAN = (J + kADist) % kAStages;
+            constexpr int SB1 = (J + 1) % kBStages, SBN = (J + kBDist) % kBStages;
             ring_sync();
-            // stages of steps g + kADist and g + kBDist
-            const int san = sa + kADist >= kAStages ? sa + kADist - kAStages : sa + kADist;
-            const int sbn = sbi + kBDist >= kBStages ? sbi + kBDist - kBStages : sbi + kBDist;
-            issue_a(min(g + kADist, G - 1), san);
-            issue_b(min(g + kBDist, G - 1), sbn);
-            const uint8_t *sA = smem + sa * kAStageBytes;
-            // A fragments of step s + 1 are read while step s multiplies
+            {
+                const int ga = min(g + kADist, G - 1), gb = min(g + kBDist, G - 1);
+                dma_step(reinterpret_cast<const uint8_t *>(Asrc) + 128 * ga, aro,
+                         smem + SAN * kAStageBytes + wave * 1024, Bt + (size_t)gb * 1024, boff,
+                         smem + kBRingOff + SBN * kBStageBytes + wave * 1024, St + gb * 128, soff,
+                         smem + kSRingOff + SBN * kSStageBytes + wave * 256);
+            }
+            const uint8_t *sA = smem + SA * kAStageBytes;
+            // A fragments of K-step s + 1 are read while K-step s multiplies
             u32x4_t af[2][LMS];
 #pragma unroll
             for (int ms = 0; ms < LMS; ++ms) af[0][ms] = ld16(sA + aoff[0] + 4096 * ms);
@@ -329,27 +380,37 @@ __global__ __launch_bounds__(kPreWG, 3) void k_pre_gemm(PreArgs a) {
                     acc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, af[s & 1][ms]), bc[s],
                                                                      acc[ms], 0, 0, 0);
             }
+            // keep the A-fragment reads one K-step ahead of the products that use them
+            __builtin_amdgcn_sched_group_barrier(0x100, LMS, 0);
+#pragma unroll
+            for (int s = 0; s < 3; ++s) {
+                __builtin_amdgcn_sched_group_barrier(0x100, LMS, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, LMS, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, LMS, 0);
             // step g + 1 (a past-the-end step reads a valid clamped stage)
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitB) : "memory");
-            load_b(sbi + 1 == kBStages ? 0 : sbi + 1, bn);
-            sa = sa + 1 == kAStages ? 0 : sa + 1;
-            sbi = sbi + 1 == kBStages ? 0 : sbi + 1;
+            load_b(SB1, bn);
         };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        using I3 = std::integral_constant<int, 3>;
+        static_assert(kUnroll == 4, "the loop below is written out for four steps");
         f16x8_t bx[4], by[4];
         // B of step 0: issued first in the prologue
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitB0) : "memory");
+        load_b(0, bx);
         int g = 0;
-        if (G & 1) {
-            load_b(0, by);
-            step(0, by, bx);
-            g = 1;
-        } else {
-            load_b(0, bx);
+        for (; g + kUnroll <= G; g += kUnroll) {
+            step(I0{}, g, bx, by);
+            step(I1{}, g + 1, by, bx);
+            step(I2{}, g + 2, bx, by);
+            step(I3{}, g + 3, by, bx);
         }
-        for (; g < G; g += 2) {
-            step(g, bx, by);
-            step(g + 1, by, bx);
-        }
+        if (g < G) step(I0{}, g, bx, by);
+        if (g + 1 < G) step(I1{}, g + 1, by, bx);
+        if (g + 2 < G) step(I2{}, g + 2, bx, by);
     };
     switch (live_ms) {
         case 1: kloop(std::integral_constant<int, 1>{}); break;
@@ -363,51 +424,55 @@ __global__ __launch_bounds__(kPreWG, 3) void k_pre_gemm(PreArgs a) {
     // ---- epilogue. Accumulator element v of lane l in subtile ms: row 32 ms + 8 (v/4) +
     // 4 (l/32) + v%4, column l%32 of the wave's weight tile.
     if (MODE == 0) {
-        // h = fp16(gelu(g) * u): the up waves hand u over through LDS, the gate waves form
-        // h into an fp16 tile, then each row leaves as 16-byte stores
+        // h = fp16(gelu(g) * u). Gate wave p and up wave p + 2 hold the same 32 hidden columns;
+        // the gate wave finishes token rows 0..63 and the up wave rows 64..127, each handing the
+        // other half of its values to its partner through one tile.
         const int J = shared_item ? a.Is : a.I;
         uint16_t *hout = shared_item ? a.h_s : a.h_r;
-        float *U = reinterpret_cast<float *>(smem);
-        uint16_t *Hs = reinterpret_cast<uint16_t *>(smem);   // written after every u is read
-        if (wave >= 2) {
+        const int p = wave & 1;
+        const bool gate_w = wave < 2;
+        float *send = reinterpret_cast<float *>(smem + (gate_w ? p : 2 + p) * kXTile);
+        float *recv = reinterpret_cast<float *>(smem + (gate_w ? 2 + p : p) * kXTile);
+        const int mk = gate_w ? 0 : 2;   // subtiles this wave finishes
+        const int mg = gate_w ? 2 : 0;   // subtiles it hands over
 #pragma unroll
-            for (int ms = 0; ms < 4; ++ms)
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = 32 * ms + 8 * (v >> 2) + 4 * half + (v & 3);
-                    U[row * kUPitch + (wave - 2) * 32 + n] = acc[ms][v];
-                }
-        }
+            for (int v = 0; v < 16; ++v) {
+                const int row = 32 * m + 8 * (v >> 2) + 4 * half + (v & 3);
+                send[row * kXPitch + n] = acc[mg + m][v];
+            }
         __syncthreads();
-        uint32_t hb[4][16];
-        if (wave < 2) {
+        uint32_t hb[2][16];
 #pragma unroll
-            for (int ms = 0; ms < 4; ++ms)
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = 32 * ms + 8 * (v >> 2) + 4 * half + (v & 3);
-                    const float u = U[row * kUPitch + wave * 32 + n];
-                    hb[ms][v] = f32_to_f16_sat(gelu_tanh_f32(acc[ms][v]) * u);
-                }
-        }
-        __syncthreads();
-        if (wave < 2) {
+            for (int v = 0; v < 16; ++v) {
+                const int row = 32 * m + 8 * (v >> 2) + 4 * half + (v & 3);
+                const float o = recv[row * kXPitch + n];
+                const float g = gate_w ? acc[mk + m][v] : o;
+                const float u = gate_w ? o : acc[mk + m][v];
+                hb[m][v] = f32_to_f16_sat(gelu_tanh_f32(g) * u);
+            }
+        // only this wave reads recv: it becomes the wave's fp16 staging tile of 64 rows x 32 columns
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        uint16_t *Hw = reinterpret_cast<uint16_t *>(recv);
 #pragma unroll
-            for (int ms = 0; ms < 4; ++ms)
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = 32 * ms + 8 * (v >> 2) + 4 * half + (v & 3);
-                    Hs[row * kHPitch + wave * 32 + n] = (uint16_t)hb[ms][v];
-                }
-        }
-        __syncthreads();
-        const int row = tid >> 1, hh = tid & 1;
-        const int dst = drow[row];
-        if (dst >= 0) {
-            const u32x4_t *src = reinterpret_cast<const u32x4_t *>(Hs + row * kHPitch + hh * 32);
-            u32x4_t *o = reinterpret_cast<u32x4_t *>(hout + (size_t)dst * J + nt * 64 + hh * 32);
+            for (int v = 0; v < 16; ++v) {
+                const int row = 32 * m + 8 * (v >> 2) + 4 * half + (v & 3);
+                Hw[row * (2 * kXPitch) + n] = (uint16_t)hb[m][v];
+            }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // each 64-byte row leaves as four 16-byte stores (lane -> row lane / 4 + 16 i, chunk lane % 4)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = src[i];
+        for (int i = 0; i < 4; ++i) {
+            const int row = (lane >> 2) + 16 * i;
+            const int dst = drow((gate_w ? 0 : 64) + row);
+            if (dst >= 0)
+                *reinterpret_cast<u32x4_t *>(hout + (size_t)dst * J + nt * 64 + p * 32 + 8 * (lane & 3)) =
+                    *reinterpret_cast<const u32x4_t *>(Hw + row * (2 * kXPitch) + 8 * (lane & 3));
         }
     } else {
         // the 128 x 128 fp32 output tile leaves through LDS in two halves of 64 rows, each
@@ -430,7 +495,7 @@ __global__ __launch_bounds__(kPreWG, 3) void k_pre_gemm(PreArgs a) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int row = (tid >> 5) + 8 * i;
-                    const int dst = drow[64 * part + row];
+                    const int dst = drow(64 * part + row);
                     if (dst >= 0)
                         *reinterpret_cast<f32x4_t *>(out + (size_t)dst * a.d + nt * 128 + 4 * c) =
                             *reinterpret_cast<const f32x4_t *>(O + row * kOPitch + 4 * c);

@@ -24,13 +24,19 @@ namespace {
 
 constexpr int kPreWG = 256;
 
+// Workgroup tile: 128 token rows x 256 weight rows (down: output columns). Wave w owns 64
+// weight rows as two 32-row code tiles for all 128 token rows: gate/up -> the gate and the up
+// tile of hidden block 4 nt + w (32 hidden units), so GeGLU needs no exchange between waves;
+// down -> row blocks 2 (4 nt + w) and 2 (4 nt + w) + 1 of the down matrix. acc is 4 x 2
+// tiles of 32 x 32 fp32; two workgroups per compute unit.
+//
 // LDS rings of the K loop (one 64-input group per step). A ring: kAStages stages of the A
 // tile (128 rows x 64 inputs, 16-bit, rows of 128 B with the 16-byte chunks XOR-swizzled),
-// loaded one step ahead by all four waves together. B ring: kBStages stages of the four 1 KiB
-// code tiles and their scale/bias words (64 per wave, rows duplicated), each wave loading its
-// own tile two steps ahead. Everything arrives by direct global->LDS loads, so no staging
-// registers are needed. The K loop is unrolled by kUnroll steps, a multiple of both ring
-// lengths, so every stage offset is a constant. Sized for three workgroups per compute unit.
+// loaded one step ahead by all four waves together. B ring: kBStages stages of the eight
+// 1 KiB code tiles and their scale/bias words (64 per tile, rows duplicated), each wave
+// loading its own two tiles two steps ahead. Everything arrives by direct global->LDS loads,
+// so no staging registers are needed. The K loop is unrolled by kUnroll steps, a multiple of
+// both ring lengths, so every stage offset is a constant.
 constexpr int kAStages = 2;
 constexpr int kBStages = 4;
 constexpr int kUnroll = 4;
@@ -38,31 +44,29 @@ constexpr int kADist = 1;   // steps the A loads run ahead
 constexpr int kBDist = 2;   // steps the B loads run ahead
 static_assert(kADist < kAStages && kBDist < kBStages, "a stage is refilled only after its step");
 static_assert(kUnroll % kAStages == 0 && kUnroll % kBStages == 0, "constant stages per unrolled step");
-static_assert(kBDist >= kADist, "weights are requested no later than the A rows of a step");
 constexpr int kAStageBytes = kMT * 128;
-constexpr int kBStageBytes = 4 * 1024;
-constexpr int kSStageBytes = 4 * 256;
+constexpr int kBStageBytes = 4 * 2 * 1024;
+constexpr int kSStageBytes = 4 * 2 * 256;
 constexpr int kBRingOff = kAStages * kAStageBytes;
 constexpr int kSRingOff = kBRingOff + kBStages * kBStageBytes;
 constexpr int kSmemBytes = kSRingOff + kBStages * kSStageBytes;
-constexpr int kDmaPerStep = 6;   // per thread: 4 A chunks, 1 code chunk, 1 scale/bias word
+static_assert(2 * kSmemBytes <= 147456, "two workgroups per compute unit");
+constexpr int kDmaPerStep = 8;   // per thread: 4 A chunks, 2 code chunks, 2 scale/bias words
 // Direct loads issued after the A chunks of step g up to the barrier of step g, and after the
-// scale/bias word of step g + 1 up to its dequantization at the end of step g (every step
-// issues the same six loads, the prologue the same pattern).
-constexpr int kWaitA = 2 + kDmaPerStep * (kADist - 1);
+// scale/bias words of step g + 1 up to their use at the end of step g (every step issues the
+// same eight loads, the prologue the same pattern).
+constexpr int kWaitA = 4 + kDmaPerStep * (kADist - 1);
 constexpr int kWaitB = kDmaPerStep * (kBDist - 1);
-constexpr int kWaitB0 = 2 * (kBDist - 1) + 4 * kADist;   // after the scale/bias word of step 0
-// Gate/up epilogue tiles (reusing the rings once every wave has left the K loop): four 64-row x
-// 32-column fp32 tiles, one per wave. Rows are 160 B apart (16-byte aligned; the two rows one 32-bit store
-// instruction writes, four apart, start 32 banks apart).
-constexpr int kXPitch = 40;
-constexpr int kXTile = 64 * kXPitch * 4;
-static_assert(4 * kXTile <= kSmemBytes, "epilogue tiles exceed the LDS rings");
-// down epilogue: 64 rows x 128 fp32 per half (row pitch 136: the two rows one store instruction
-// writes start 32 banks apart)
-constexpr int kOPitch = 136;
+constexpr int kWaitB0 = 4 * (kBDist - 1) + 4 * kADist;   // after the scale/bias words of step 0
+// gate/up epilogue: each wave's h tile, 128 rows x 32 fp16 (rows 96 B apart: the two rows one
+// 16-bit store instruction writes start 32 banks apart)
+constexpr int kHPitch = 48;
+constexpr int kHTile = kMT * kHPitch * 2;
+static_assert(4 * kHTile <= kSmemBytes, "h tiles exceed the LDS rings");
+// down epilogue: 64 rows x 256 fp32 per half (row pitch 264: the two rows one store
+// instruction writes start 32 banks apart)
+constexpr int kOPitch = 264;
 static_assert(64 * kOPitch * 4 <= kSmemBytes, "down epilogue tile exceeds the LDS rings");
-static_assert(kSmemBytes <= 53248, "at most 53,248 bytes of LDS per workgroup leave room for three per compute unit");
 
 // Physical 16-byte chunk of logical chunk c in A-tile row r is c ^ swz(r). 16 consecutive
 // rows read at one logical chunk then hit 16 distinct 16-byte bank groups (and any 8
@@ -82,33 +86,6 @@ __device__ __forceinline__ const void *uniform_ptr(const void *p) {
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
     return (const void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
-__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, const uint8_t *lds_base) {
-    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
-    const void *sb = uniform_ptr(sbase);
-    uint32_t save;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "global_load_lds_dwordx4 %1, %2\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(save)
-        : "v"(voff), "s"(sb), "s"(m)
-        : "memory");
-}
-__device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, const uint8_t *lds_base) {
-    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
-    const void *sb = uniform_ptr(sbase);
-    uint32_t save;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "global_load_lds_dword %1, %2\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(save)
-        : "v"(voff), "s"(sb), "s"(m)
-        : "memory");
-}
-
 // Four direct loads of 16 bytes per lane from sbase + voff[i] to lds_base + 4096 i + 16 lane
 // (the four 8-row A chunks of one wave), with one save and restore of M0. Each M0 write is
 // followed by one wait state before the load that reads it.
@@ -136,19 +113,45 @@ __device__ __forceinline__ void dma16x4(const void *sbase, const uint32_t voff[4
         : "memory", "scc");
 }
 
+// The wave's two code tiles (16 bytes per lane each, to lds_b and lds_b + 1024) and their
+// scale/bias words (4 bytes per lane, to lds_s and lds_s + 256), one save and restore of M0.
+__device__ __forceinline__ void dma_b(const void *sb0, const void *sb1, uint32_t voff_b, const uint8_t *lds_b,
+                                      const void *ss0, const void *ss1, uint32_t voff_s, const uint8_t *lds_s) {
+    const uint32_t mb = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_b);
+    const uint32_t ms = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_s);
+    const void *b0 = uniform_ptr(sb0), *b1 = uniform_ptr(sb1), *s0 = uniform_ptr(ss0), *s1 = uniform_ptr(ss1);
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %5\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %6\n\t"
+        "s_mov_b32 m0, %4\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %2, %7\n\t"
+        "s_add_u32 m0, m0, 0x100\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %2, %8\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "v"(voff_b), "v"(voff_s), "s"(mb), "s"(ms), "s"(b0), "s"(b1), "s"(s0), "s"(s1)
+        : "memory", "scc");
+}
+
 // All direct loads of one ring step with one save and restore of M0: the four A chunks
-// (sbase_a + voff_a[i] -> lds_a + 4096 i + 16 lane), then the wave's code tile (16 bytes per
-// lane) and its scale/bias words (4 bytes per lane). Issue order is the one the counted waits
-// assume.
+// (sbase_a + voff_a[i] -> lds_a + 4096 i + 16 lane), then the wave's two code tiles and
+// their scale/bias words as in dma_b. Issue order is the one the counted waits assume.
 __device__ __forceinline__ void dma_step(const void *sbase_a, const uint32_t voff_a[4], const uint8_t *lds_a,
-                                         const void *sbase_b, uint32_t voff_b, const uint8_t *lds_b,
-                                         const void *sbase_s, uint32_t voff_s, const uint8_t *lds_s) {
+                                         const void *sb0, const void *sb1, uint32_t voff_b, const uint8_t *lds_b,
+                                         const void *ss0, const void *ss1, uint32_t voff_s, const uint8_t *lds_s) {
     const uint32_t ma = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_a);
     const uint32_t mb = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_b);
     const uint32_t ms = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_s);
     const void *sa = uniform_ptr(sbase_a);
-    const void *sb = uniform_ptr(sbase_b);
-    const void *ss = uniform_ptr(sbase_s);
+    const void *b0 = uniform_ptr(sb0), *b1 = uniform_ptr(sb1), *s0 = uniform_ptr(ss0), *s1 = uniform_ptr(ss1);
     uint32_t save;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
@@ -167,13 +170,19 @@ __device__ __forceinline__ void dma_step(const void *sbase_a, const uint32_t vof
         "s_mov_b32 m0, %8\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %5, %11\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %5, %12\n\t"
         "s_mov_b32 m0, %9\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dword %6, %12\n\t"
+        "global_load_lds_dword %6, %13\n\t"
+        "s_add_u32 m0, m0, 0x100\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %6, %14\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(save)
         : "v"(voff_a[0]), "v"(voff_a[1]), "v"(voff_a[2]), "v"(voff_a[3]), "v"(voff_b), "v"(voff_s), "s"(ma), "s"(mb),
-          "s"(ms), "s"(sa), "s"(sb), "s"(ss)
+          "s"(ms), "s"(sa), "s"(b0), "s"(b1), "s"(s0), "s"(s1)
         : "memory", "scc");
 }
 
@@ -214,7 +223,7 @@ __device__ __forceinline__ f16x8_t dequant_frag(uint32_t w, f16x2_t s2, f16x2_t 
 }
 
 template <int MODE>  // 0: gate/up + GeGLU, 1: down
-__global__ __launch_bounds__(kPreWG, 3) void k_pre_gemm(PreArgs a) {
+__global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
     __shared__ __align__(16) uint8_t smem[kSmemBytes];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -234,8 +243,8 @@ __global__ __launch_bounds__(kPreWG, 3) void k_pre_gemm(PreArgs a) {
     // of a row tile runs on the same XCD, so the row tile is fetched into one L2 only. The
     // routed part is sized for the worst case; workgroups past the real tiles exit at once.
     const int Ms = cdiv(a.T, kMT), Ms8 = roundup(Ms, 8);
-    const int NTs = MODE == 0 ? a.Is / 64 : a.d / 128;
-    const int NTr = MODE == 0 ? a.I / 64 : a.d / 128;
+    const int NTs = MODE == 0 ? cdiv(a.Is / 32, 4) : cdiv(a.d / 64, 4);
+    const int NTr = MODE == 0 ? cdiv(a.I / 32, 4) : cdiv(a.d / 64, 4);
     const int bid = blockIdx.x, Gs = Ms8 * NTs;
     bool shared_item;
     int e = 0, mt, nt, count, rowbase;
@@ -279,20 +288,29 @@ __global__ __launch_bounds__(kPreWG, 3) void k_pre_gemm(PreArgs a) {
         return rr < count ? (shared_item ? 0 : rowbase) + rr : -1;
     };
 
-    // Wave w owns one 32-row weight tile for all 128 token rows: gate/up -> gate blocks
-    // 2nt, 2nt+1 (waves 0, 1) and up blocks 2nt, 2nt+1 (waves 2, 3); down -> block 4nt + w.
-    const uint8_t *Bt;        // code tile of step 0 (wave-uniform); lane adds 16 lane
-    const uint8_t *St;        // scale/bias words of step 0 (wave-uniform); lane adds 4 n
+    // The wave's block (gate/up: 32 hidden units; down: 64 output columns) and its two code
+    // tiles. A wave past the end of the matrix (the last tile of a width that is not a multiple
+    // of the tile) loads block 4 nt's tiles to keep the ring's load pattern and computes nothing.
+    const int blk = 4 * nt + wave;
+    const int J = MODE == 0 ? (shared_item ? a.Is : a.I) : a.d;   // rows of the weight matrices
+    const bool live_w = MODE == 0 ? blk * 32 < J : blk * 64 < J;
+    const uint8_t *Bt0, *Bt1;   // code tiles of step 0 (wave-uniform); lane adds 16 lane
+    const uint8_t *St0, *St1;   // scale/bias words of step 0 (wave-uniform); lane adds 4 n
     {
-        const moe_qmat *m = MODE == 0 ? (wave < 2 ? (shared_item ? &a.sh_gate : &a.gate)
-                                                  : (shared_item ? &a.sh_up : &a.up))
-                                      : (shared_item ? &a.sh_down : &a.down);
-        const int rows = MODE == 0 ? (shared_item ? a.Is : a.I) : a.d;
-        const int rb = MODE == 0 ? 2 * nt + (wave & 1) : 4 * nt + wave;
-        Bt = static_cast<const uint8_t *>(m->codes) + (size_t)e * rows * K / 2 + (size_t)rb * G * 1024;
-        St = reinterpret_cast<const uint8_t *>(m->sb + (size_t)e * rows * G + (size_t)rb * G * 32);
-        Bt = static_cast<const uint8_t *>(uniform_ptr(Bt));
-        St = static_cast<const uint8_t *>(uniform_ptr(St));
+        const int bl = live_w ? blk : 4 * nt;
+        const moe_qmat *m0 = MODE == 0 ? (shared_item ? &a.sh_gate : &a.gate) : (shared_item ? &a.sh_down : &a.down);
+        const moe_qmat *m1 = MODE == 0 ? (shared_item ? &a.sh_up : &a.up) : m0;
+        const int rb0 = MODE == 0 ? bl : 2 * bl;
+        const int rb1 = MODE == 0 ? bl : 2 * bl + 1;
+        const size_t mat_bytes = (size_t)J * K / 2, mat_words = (size_t)J * G;
+        Bt0 = static_cast<const uint8_t *>(m0->codes) + e * mat_bytes + (size_t)rb0 * G * 1024;
+        Bt1 = static_cast<const uint8_t *>(m1->codes) + e * mat_bytes + (size_t)rb1 * G * 1024;
+        St0 = reinterpret_cast<const uint8_t *>(m0->sb + e * mat_words + (size_t)rb0 * G * 32);
+        St1 = reinterpret_cast<const uint8_t *>(m1->sb + e * mat_words + (size_t)rb1 * G * 32);
+        Bt0 = static_cast<const uint8_t *>(uniform_ptr(Bt0));
+        Bt1 = static_cast<const uint8_t *>(uniform_ptr(Bt1));
+        St0 = static_cast<const uint8_t *>(uniform_ptr(St0));
+        St1 = static_cast<const uint8_t *>(uniform_ptr(St1));
     }
     const uint32_t boff = lane * 16, soff = n * 4;
     // A rows this thread moves: chunk i covers rows 8 (4 i + wave) .. +7, lane -> row
@@ -309,31 +327,35 @@ __global__ __launch_bounds__(kPreWG, 3) void k_pre_gemm(PreArgs a) {
     }
     __syncthreads();   // srow is read; the ring loads may overwrite it
 
-    // loads of one ring step: the A chunks of step ga (into A stage sa) and the wave's code
-    // tile and scale/bias words of step gb (into B stage sbi)
+    // loads of the prologue: A chunks of step ga into A stage sa; the wave's code tiles and
+    // scale/bias words of step gb into B stage sbi
     auto issue_a = [&](int ga, int sa) {
         dma16x4(reinterpret_cast<const uint8_t *>(Asrc) + 128 * ga, aro, smem + sa * kAStageBytes + wave * 1024);
     };
     auto issue_b = [&](int gb, int sbi) {
-        dma16(Bt + (size_t)gb * 1024, boff, smem + kBRingOff + sbi * kBStageBytes + wave * 1024);
-        dma4(St + gb * 128, soff, smem + kSRingOff + sbi * kSStageBytes + wave * 256);
+        dma_b(Bt0 + (size_t)gb * 1024, Bt1 + (size_t)gb * 1024, boff, smem + kBRingOff + sbi * kBStageBytes + wave * 2048,
+              St0 + gb * 128, St1 + gb * 128, soff, smem + kSRingOff + sbi * kSStageBytes + wave * 512);
     };
-    // dequantized B fragments of the step whose code tile sits in B stage sbi
-    auto load_b = [&](int sbi, f16x8_t (&b)[4]) {
-        const u32x4_t bw = ld16(smem + kBRingOff + sbi * kBStageBytes + wave * 1024 + lane * 16);
-        const uint32_t sbw = *reinterpret_cast<const uint32_t *>(smem + kSRingOff + sbi * kSStageBytes + wave * 256 + lane * 4);
-        const float sc = bf16_to_f32(sbw & 0xFFFFu), bi = bf16_to_f32(sbw >> 16);
-        const f16x2_t s2 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(sc, sc));
-        const f16x2_t b2 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(bi, bi));
+    // raw code words and fp16 scale/bias pairs of the step whose tiles sit in B stage sbi
+    auto load_w = [&](int sbi, u32x4_t (&bw)[2], f16x2_t (&s2)[2], f16x2_t (&b2)[2]) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) b[s] = dequant_frag(bw[s], s2, b2);
+        for (int t = 0; t < 2; ++t) {
+            bw[t] = ld16(smem + kBRingOff + sbi * kBStageBytes + wave * 2048 + t * 1024 + lane * 16);
+            const uint32_t sbw =
+                *reinterpret_cast<const uint32_t *>(smem + kSRingOff + sbi * kSStageBytes + wave * 512 + t * 256 + lane * 4);
+            const float sc = bf16_to_f32(sbw & 0xFFFFu), bi = bf16_to_f32(sbw >> 16);
+            s2[t] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(sc, sc));
+            b2[t] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(bi, bi));
+        }
     };
 
-    f32x16_t acc[4];
+    f32x16_t acc[4][2];
 #pragma unroll
     for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[ms][v] = 0.0f;
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[ms][t][v] = 0.0f;
     // 32-row subtiles holding at least one real row (uniform)
     const int live = count - mt * kMT;
     const int live_ms = live >= kMT ? 4 : (live + 31) >> 5;
@@ -346,71 +368,71 @@ __global__ __launch_bounds__(kPreWG, 3) void k_pre_gemm(PreArgs a) {
     }
 
     // The K loop, instantiated per number of live 32-row subtiles (1..4) so that padding
-    // subtiles cost nothing and the MFMA sequence stays branch-free. Step g multiplies with
-    // the fragments dequantized during step g - 1 and dequantizes those of step g + 1.
+    // subtiles cost nothing and the MFMA sequence stays branch-free. Within a step, K-step s
+    // multiplies while the A fragments and the dequantized weights of K-step s + 1 are formed;
+    // the code words of step g + 1 are read at the end of step g.
     auto kloop = [&](auto lms_c) {
         constexpr int LMS = decltype(lms_c)::value;
-        // step g (J = g mod kUnroll) multiplies with the fragments dequantized during step g - 1
-        // and dequantizes those of step g + 1
-        auto step = [&](auto j_c, int g, const f16x8_t (&bc)[4], f16x8_t (&bn)[4]) {
-            constexpr int J = decltype(j_c)::value;
-            constexpr int SA = J % kAStages, SAN = (J + kADist) % kAStages;
-            constexpr int SB1 = (J + 1) % kBStages, SBN = (J + kBDist) % kBStages;
+        u32x4_t bw[2];
+        f16x2_t s2[2], b2[2];
+        auto step = [&](auto j_c, int g) {
+            constexpr int Ju = decltype(j_c)::value;
+            constexpr int SA = Ju % kAStages, SAN = (Ju + kADist) % kAStages;
+            constexpr int SB1 = (Ju + 1) % kBStages, SBN = (Ju + kBDist) % kBStages;
             ring_sync();
             {
                 const int ga = min(g + kADist, G - 1), gb = min(g + kBDist, G - 1);
-                dma_step(reinterpret_cast<const uint8_t *>(Asrc) + 128 * ga, aro,
-                         smem + SAN * kAStageBytes + wave * 1024, Bt + (size_t)gb * 1024, boff,
-                         smem + kBRingOff + SBN * kBStageBytes + wave * 1024, St + gb * 128, soff,
-                         smem + kSRingOff + SBN * kSStageBytes + wave * 256);
+                dma_step(reinterpret_cast<const uint8_t *>(Asrc) + 128 * ga, aro, smem + SAN * kAStageBytes + wave * 1024,
+                         Bt0 + (size_t)gb * 1024, Bt1 + (size_t)gb * 1024, boff,
+                         smem + kBRingOff + SBN * kBStageBytes + wave * 2048, St0 + gb * 128, St1 + gb * 128, soff,
+                         smem + kSRingOff + SBN * kSStageBytes + wave * 512);
             }
-            const uint8_t *sA = smem + SA * kAStageBytes;
-            // A fragments of K-step s + 1 are read while K-step s multiplies
-            u32x4_t af[2][LMS];
+            if (live_w) {
+                const uint8_t *sA = smem + SA * kAStageBytes;
+                u32x4_t af[2][LMS];
+                f16x8_t bf[2][2];
 #pragma unroll
-            for (int ms = 0; ms < LMS; ++ms) af[0][ms] = ld16(sA + aoff[0] + 4096 * ms);
+                for (int ms = 0; ms < LMS; ++ms) af[0][ms] = ld16(sA + aoff[0] + 4096 * ms);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                if (s < 3) {
+                for (int t = 0; t < 2; ++t) bf[0][t] = dequant_frag(bw[t][0], s2[t], b2[t]);
 #pragma unroll
-                    for (int ms = 0; ms < LMS; ++ms) af[(s + 1) & 1][ms] = ld16(sA + aoff[s + 1] + 4096 * ms);
+                for (int s = 0; s < 4; ++s) {
+                    if (s < 3) {
+#pragma unroll
+                        for (int ms = 0; ms < LMS; ++ms) af[(s + 1) & 1][ms] = ld16(sA + aoff[s + 1] + 4096 * ms);
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) bf[(s + 1) & 1][t] = dequant_frag(bw[t][s + 1], s2[t], b2[t]);
+                    }
+#pragma unroll
+                    for (int ms = 0; ms < LMS; ++ms)
+#pragma unroll
+                        for (int t = 0; t < 2; ++t)
+                            acc[ms][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                __builtin_bit_cast(f16x8_t, af[s & 1][ms]), bf[s & 1][t], acc[ms][t], 0, 0, 0);
                 }
-#pragma unroll
-                for (int ms = 0; ms < LMS; ++ms)
-                    acc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, af[s & 1][ms]), bc[s],
-                                                                     acc[ms], 0, 0, 0);
             }
-            // keep the A-fragment reads one K-step ahead of the products that use them
-            __builtin_amdgcn_sched_group_barrier(0x100, LMS, 0);
-#pragma unroll
-            for (int s = 0; s < 3; ++s) {
-                __builtin_amdgcn_sched_group_barrier(0x100, LMS, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, LMS, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, LMS, 0);
-            // step g + 1 (a past-the-end step reads a valid clamped stage)
+            // code words of step g + 1 (a past-the-end step reads a valid clamped stage)
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitB) : "memory");
-            load_b(SB1, bn);
+            if (live_w) load_w(SB1, bw, s2, b2);
         };
         using I0 = std::integral_constant<int, 0>;
         using I1 = std::integral_constant<int, 1>;
         using I2 = std::integral_constant<int, 2>;
         using I3 = std::integral_constant<int, 3>;
         static_assert(kUnroll == 4, "the loop below is written out for four steps");
-        f16x8_t bx[4], by[4];
         // B of step 0: issued first in the prologue
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitB0) : "memory");
-        load_b(0, bx);
+        if (live_w) load_w(0, bw, s2, b2);
         int g = 0;
         for (; g + kUnroll <= G; g += kUnroll) {
-            step(I0{}, g, bx, by);
-            step(I1{}, g + 1, by, bx);
-            step(I2{}, g + 2, bx, by);
-            step(I3{}, g + 3, by, bx);
+            step(I0{}, g);
+            step(I1{}, g + 1);
+            step(I2{}, g + 2);
+            step(I3{}, g + 3);
         }
-        if (g < G) step(I0{}, g, bx, by);
-        if (g + 1 < G) step(I1{}, g + 1, by, bx);
-        if (g + 2 < G) step(I2{}, g + 2, bx, by);
+        if (g < G) step(I0{}, g);
+        if (g + 1 < G) step(I1{}, g + 1);
+        if (g + 2 < G) step(I2{}, g + 2);
     };
     switch (live_ms) {
         case 1: kloop(std::integral_constant<int, 1>{}); break;
@@ -421,83 +443,64 @@ __global__ __launch_bounds__(kPreWG, 3) void k_pre_gemm(PreArgs a) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the clamped tail loads still land in the rings
     __syncthreads();   // every wave is done with the rings (no loads are outstanding)
 
-    // ---- epilogue. Accumulator element v of lane l in subtile ms: row 32 ms + 8 (v/4) +
-    // 4 (l/32) + v%4, column l%32 of the wave's weight tile.
+    // ---- epilogue. Accumulator element v of lane l in tile (ms, t): token row 32 ms + 8 (v/4)
+    // + 4 (l/32) + v%4, weight row l%32 of the wave's code tile t.
     if (MODE == 0) {
-        // h = fp16(gelu(g) * u). Gate wave p and up wave p + 2 hold the same 32 hidden columns;
-        // the gate wave finishes token rows 0..63 and the up wave rows 64..127, each handing the
-        // other half of its values to its partner through one tile.
-        const int J = shared_item ? a.Is : a.I;
-        uint16_t *hout = shared_item ? a.h_s : a.h_r;
-        const int p = wave & 1;
-        const bool gate_w = wave < 2;
-        float *send = reinterpret_cast<float *>(smem + (gate_w ? p : 2 + p) * kXTile);
-        float *recv = reinterpret_cast<float *>(smem + (gate_w ? 2 + p : p) * kXTile);
-        const int mk = gate_w ? 0 : 2;   // subtiles this wave finishes
-        const int mg = gate_w ? 2 : 0;   // subtiles it hands over
+        // h = fp16(gelu(g) * u) in registers (tile 0: gate, tile 1: up, same hidden unit per
+        // lane), staged through the wave's own LDS tile and written as 64-byte row pieces
+        if (live_w) {
+            uint16_t *hout = shared_item ? a.h_s : a.h_r;
+            uint16_t *Hw = reinterpret_cast<uint16_t *>(smem + wave * kHTile);
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+            for (int ms = 0; ms < 4; ++ms) {
+                if (ms < live_ms) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = 32 * m + 8 * (v >> 2) + 4 * half + (v & 3);
-                send[row * kXPitch + n] = acc[mg + m][v];
+                    for (int v = 0; v < 16; ++v) {
+                        const int row = 32 * ms + 8 * (v >> 2) + 4 * half + (v & 3);
+                        Hw[row * kHPitch + n] = (uint16_t)f32_to_f16_sat(gelu_tanh_f32(acc[ms][0][v]) * acc[ms][1][v]);
+                    }
+                }
             }
-        __syncthreads();
-        uint32_t hb[2][16];
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            // lane -> row lane / 4 + 16 i, 16-byte chunk lane % 4
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = 32 * m + 8 * (v >> 2) + 4 * half + (v & 3);
-                const float o = recv[row * kXPitch + n];
-                const float g = gate_w ? acc[mk + m][v] : o;
-                const float u = gate_w ? o : acc[mk + m][v];
-                hb[m][v] = f32_to_f16_sat(gelu_tanh_f32(g) * u);
+            for (int i = 0; i < 8; ++i) {
+                const int row = (lane >> 2) + 16 * i;
+                const int dst = drow(row);
+                if (row < 32 * live_ms && dst >= 0)
+                    *reinterpret_cast<u32x4_t *>(hout + (size_t)dst * J + blk * 32 + 8 * (lane & 3)) =
+                        *reinterpret_cast<const u32x4_t *>(Hw + row * kHPitch + 8 * (lane & 3));
             }
-        // only this wave reads recv: it becomes the wave's fp16 staging tile of 64 rows x 32 columns
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        uint16_t *Hw = reinterpret_cast<uint16_t *>(recv);
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = 32 * m + 8 * (v >> 2) + 4 * half + (v & 3);
-                Hw[row * (2 * kXPitch) + n] = (uint16_t)hb[m][v];
-            }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        // each 64-byte row leaves as four 16-byte stores (lane -> row lane / 4 + 16 i, chunk lane % 4)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = (lane >> 2) + 16 * i;
-            const int dst = drow((gate_w ? 0 : 64) + row);
-            if (dst >= 0)
-                *reinterpret_cast<u32x4_t *>(hout + (size_t)dst * J + nt * 64 + p * 32 + 8 * (lane & 3)) =
-                    *reinterpret_cast<const u32x4_t *>(Hw + row * (2 * kXPitch) + 8 * (lane & 3));
         }
     } else {
-        // the 128 x 128 fp32 output tile leaves through LDS in two halves of 64 rows, each
-        // row as one 512-byte run of 16-byte stores
+        // the 128 x 256 fp32 output tile leaves through LDS in two halves of 64 rows, each row
+        // as one run of up to 1 KiB of 16-byte stores
         float *out = shared_item ? a.sh : a.r;
         float *O = reinterpret_cast<float *>(smem);
+        const int c = tid & 63;   // 16-byte chunk of a row
+        const bool col_ok = nt * 256 + 4 * c < a.d;
 #pragma unroll
         for (int part = 0; part < 2; ++part) {
             if (2 * part < live_ms) {
                 if (part) __syncthreads();   // the first half has left
+                if (live_w) {
 #pragma unroll
-                for (int mh = 0; mh < 2; ++mh)
+                    for (int mh = 0; mh < 2; ++mh)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int row = 32 * mh + 8 * (v >> 2) + 4 * half + (v & 3);
-                        O[row * kOPitch + wave * 32 + n] = acc[2 * part + mh][v];
-                    }
+                        for (int t = 0; t < 2; ++t)
+#pragma unroll
+                            for (int v = 0; v < 16; ++v) {
+                                const int row = 32 * mh + 8 * (v >> 2) + 4 * half + (v & 3);
+                                O[row * kOPitch + wave * 64 + t * 32 + n] = acc[2 * part + mh][t][v];
+                            }
+                }
                 __syncthreads();
-                const int c = tid & 31;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int row = (tid >> 5) + 8 * i;
+                for (int i = 0; i < 16; ++i) {
+                    const int row = (tid >> 6) + 4 * i;
                     const int dst = drow(64 * part + row);
-                    if (dst >= 0)
-                        *reinterpret_cast<f32x4_t *>(out + (size_t)dst * a.d + nt * 128 + 4 * c) =
+                    if (col_ok && dst >= 0)
+                        *reinterpret_cast<f32x4_t *>(out + (size_t)dst * a.d + nt * 256 + 4 * c) =
                             *reinterpret_cast<const f32x4_t *>(O + row * kOPitch + 4 * c);
                 }
             }
@@ -552,8 +555,8 @@ PreArgs make_args(const moe_layer *L, int T) {
 // plus the routed part sized for the worst case, cdiv(T k, 128) + min(E, T k) row tiles.
 int pre_grid(const moe_layer *L, int T, int mode) {
     const moe_dims &D = L->dims;
-    const int NTs = mode == 0 ? D.d_shared / 64 : D.d_model / 128;
-    const int NTr = mode == 0 ? D.d_expert / 64 : D.d_model / 128;
+    const int NTs = mode == 0 ? cdiv(D.d_shared / 32, 4) : cdiv(D.d_model / 64, 4);
+    const int NTr = mode == 0 ? cdiv(D.d_expert / 32, 4) : cdiv(D.d_model / 64, 4);
     const int Mr = max_routed_tiles(T, D.top_k, D.n_experts);
     return roundup(cdiv(T, kMT), 8) * NTs + roundup(Mr, 8) * NTr;
 }

@@ -1,7 +1,8 @@
 """GPU parity on layer shapes away from the 2816-wide workload, through the C ABI: the
 widest model dimension the kernels take (8192: router lanes loop over 128 groups), many
 experts with the largest top-k (256 experts, top-16: four logits per lane in the top-k,
-every down-projection wave shared), and top-1 (a single routing weight of exactly 1).
+every down-projection wave shared), top-1 (a single routing weight of exactly 1), and widths
+whose last prefill tile is only partly filled.
 Same bar as the other parity tests: top-k index sets and grouping bit-exact, outputs within
 max |err| <= 2e-3 * rms of the oracle.
 """
@@ -21,6 +22,9 @@ SHAPES = {
     "wide_d8192": (synth.Dims(d_model=8192, n_experts=16, top_k=4, d_expert=128, d_shared=128), 2, 130),
     "e256_top16": (synth.Dims(d_model=1024, n_experts=256, top_k=16, d_expert=256, d_shared=512), 3, 200),
     "top1": (synth.Dims(d_model=256, n_experts=4, top_k=1, d_expert=64, d_shared=64), 5, 70),
+    # widths that leave the last prefill tile part-empty: 10 column blocks of 64 for the down
+    # projection (tiles of 4), 6 and 10 hidden blocks of 32 for gate/up
+    "ragged_tiles": (synth.Dims(d_model=640, n_experts=8, top_k=2, d_expert=192, d_shared=320), 3, 150),
 }
 
 

@@ -290,62 +290,124 @@ __global__ __launch_bounds__(256) void k_bucket_rank(const int32_t *__restrict__
         chunk_cnt[(size_t)blockIdx.x * E + i] = wcnt[0][i] + wcnt[1][i] + wcnt[2][i] + wcnt[3][i];
 }
 
-// Counts, offsets, per-chunk bases, GEMM tile offsets and the GEMM's routed work items
-// (expert, row tile, first pair row, pairs of the expert), one per row tile in expert order.
-// grid 1; block 1024
+// Exclusive prefix sums of NV values per thread over threads 0 .. 64 nw - 1 of the block (v is
+// replaced by its prefix; tot receives the totals; threads past them must hold zeros). ws: LDS
+// of 16 x NV.
+template <int NV>
+__device__ __forceinline__ void block_scan(int (&v)[NV], int (&tot)[NV], int32_t (*ws)[NV], int nw) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int inc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) inc[i] = v[i];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int t = __shfl_up(inc[i], o);
+            if (lane >= o) inc[i] += t;
+        }
+    if (lane == 63)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) ws[wave][i] = inc[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        int base = 0, total = 0;
+        for (int w = 0; w < nw; ++w) {
+            const int x = ws[w][i];
+            if (w < wave) base += x;
+            total += x;
+        }
+        v[i] = base + inc[i] - v[i];
+        tot[i] = total;
+    }
+    __syncthreads();
+}
+
+constexpr int kScanPiece = 16384;   // chunk counts per LDS piece of the scan
+
+// Counts, offsets, per-chunk bases and the GEMM's routed work items. grid 1; block 1024
+// (thread e: expert e).
+//  * chunk_base[c][e] becomes the number of pairs of expert e in chunks before c (the expert's
+//    own start is added by the scatter), in pieces of whole chunks staged in LDS with coalesced
+//    loads and stores.
+//  * counts[e], offsets[e] (exclusive prefix; offsets[E] = all pairs), tile_off[e] (prefix of
+//    ceil(counts / mt) in expert order; tile_off[E] = all routed row tiles).
+//  * items: one (expert, row tile, first pair row, pairs of the expert) per row tile, in expert
+//    order (a part-filled last tile after the expert's full ones).
 __global__ __launch_bounds__(1024) void k_bucket_scan(int nchunks, int E, int32_t *__restrict__ chunk_base,
                                                       int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                                                       int32_t *__restrict__ tile_off, int mt, int4 *__restrict__ items) {
-    __shared__ int32_t sc[MOE_MAX_EXPERTS];
-    __shared__ int32_t st[MOE_MAX_EXPERTS];
-    const int e = threadIdx.x;
-    int run = 0;
-    if (e < E) {
-        for (int c0 = 0; c0 < nchunks; c0 += 16) {   // loads of a batch are independent
-            int v[16];
+    __shared__ int32_t piece[kScanPiece];
+    __shared__ int32_t ws[16][2];
+    __shared__ int32_t seg[8][MOE_MAX_EXPERTS];
+    __shared__ int32_t carry[MOE_MAX_EXPERTS];   // pairs of each expert in the pieces so far
+    const int tid = threadIdx.x, e = tid;
+    const int pc = kScanPiece / E;   // chunks per piece (E <= 1024)
+    if (e < E) carry[e] = 0;
+    for (int c0 = 0; c0 < nchunks; c0 += pc) {
+        const int nc = min(pc, nchunks - c0), n = nc * E;
+        int32_t *blk = chunk_base + (size_t)c0 * E;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) v[i] = (c0 + i < nchunks) ? chunk_base[(size_t)(c0 + i) * E + e] : 0;
+        for (int k0 = 0; k0 < kScanPiece / 1024; k0 += 8) {   // eight independent loads at a time
+            int v[8];
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (c0 + i < nchunks) {
-                    chunk_base[(size_t)(c0 + i) * E + e] = run;
-                    run += v[i];
+            for (int k = 0; k < 8; ++k) {
+                const int i = tid + 1024 * (k0 + k);
+                v[k] = i < n ? blk[i] : 0;
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = tid + 1024 * (k0 + k);
+                if (i < n) piece[i] = v[k];
+            }
+        }
+        __syncthreads();
+        // thread (segment sg, expert ee) scans its segment of L consecutive chunks of the piece
+        // for expert ee, starting from the totals of the expert's earlier segments and pieces
+        {
+            const int nseg = min(8, 1024 / E), L = (nc + nseg - 1) / nseg;
+            const int sg = tid / E, ee = tid % E;
+            const int c_lo = sg * L, c_hi = min(nc, c_lo + L);
+            int tsum = 0;
+            if (sg < nseg)
+                for (int c = c_lo; c < c_hi; ++c) tsum += piece[c * E + ee];
+            if (sg < nseg) seg[sg][ee] = tsum;
+            __syncthreads();
+            if (sg < nseg) {
+                int r = carry[ee];
+                for (int q = 0; q < sg; ++q) r += seg[q][ee];
+                for (int c = c_lo; c < c_hi; ++c) {
+                    const int x = piece[c * E + ee];
+                    piece[c * E + ee] = r;
+                    r += x;
                 }
+            }
+            __syncthreads();
+            if (e < E)
+                for (int q = 0; q < nseg; ++q) carry[e] += seg[q][e];
         }
-        counts[e] = run;
-        sc[e] = run;
-        st[e] = (run + mt - 1) / mt;
-    }
-    __syncthreads();
-    if (e == 0) {
-        int a = 0, b = 0;
-        for (int i = 0; i < E; ++i) {
-            offsets[i] = a;
-            tile_off[i] = b;
-            const int ca = sc[i], cb = st[i];
-            sc[i] = a;
-            st[i] = b;
-            a += ca;
-            b += cb;
-        }
-        offsets[E] = a;
-        tile_off[E] = b;
-    }
-    __syncthreads();
-    if (e < E) {
-        const int ntile = (run + mt - 1) / mt;
-        for (int j = 0; j < ntile; ++j) items[st[e] + j] = make_int4(e, j, sc[e], run);
-    }
-    if (e < E) {
-        const int base = sc[e];
-        for (int c0 = 0; c0 < nchunks; c0 += 16) {
-            int v[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) v[i] = (c0 + i < nchunks) ? chunk_base[(size_t)(c0 + i) * E + e] : 0;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (c0 + i < nchunks) chunk_base[(size_t)(c0 + i) * E + e] = v[i] + base;
+        for (int k = 0; k < kScanPiece / 1024; ++k) {
+            const int i = tid + 1024 * k;
+            if (i < n) blk[i] = piece[i];
         }
+        __syncthreads();   // the piece is refilled
+    }
+    const bool ok = e < E;
+    const int cnt = ok ? carry[e] : 0, ntile = (cnt + mt - 1) / mt;
+    int v[2] = {cnt, ntile};
+    int tot[2];
+    block_scan<2>(v, tot, ws, min(16, (E + 63) / 64));
+    if (ok) {
+        counts[e] = cnt;
+        offsets[e] = v[0];
+        tile_off[e] = v[1];
+        for (int j = 0; j < ntile; ++j) items[v[1] + j] = make_int4(e, j, v[0], cnt);
+    }
+    if (tid == 0) {
+        offsets[E] = tot[0];
+        tile_off[E] = tot[1];
     }
 }
 
@@ -353,12 +415,13 @@ __global__ __launch_bounds__(1024) void k_bucket_scan(int nchunks, int E, int32_
 __global__ __launch_bounds__(256) void k_bucket_scatter(const int32_t *__restrict__ idx, int P, int E,
                                                         const int32_t *__restrict__ rank,
                                                         const int32_t *__restrict__ chunk_base,
+                                                        const int32_t *__restrict__ offsets,
                                                         int32_t *__restrict__ perm, int32_t *__restrict__ pos,
                                                         int32_t *__restrict__ perm_out) {
     const int p = blockIdx.x * kChunk + threadIdx.x;
     if (p >= P) return;
     const int e = idx[p];
-    const int q = chunk_base[(size_t)blockIdx.x * E + e] + rank[p];
+    const int q = offsets[e] + chunk_base[(size_t)blockIdx.x * E + e] + rank[p];
     perm[q] = p;
     pos[p] = q;
     if (perm_out) perm_out[q] = p;
@@ -409,7 +472,7 @@ hipError_t launch_bucket_scan(const moe_layer *L, int T, hipStream_t s) {
 hipError_t launch_bucket_scatter(const moe_layer *L, int T, const int32_t *idx, int32_t *perm_out, hipStream_t s) {
     const int P = T * L->dims.top_k;
     launch(k_bucket_scatter, dim3(cdiv(P, kChunk)), dim3(kChunk), 0, s, idx, P, L->dims.n_experts,
-                       L->ws.rank, L->ws.chunk_base, L->ws.perm, L->ws.pos, perm_out);
+                       L->ws.rank, L->ws.chunk_base, L->ws.offsets, L->ws.perm, L->ws.pos, perm_out);
     return hipGetLastError();
 }
 

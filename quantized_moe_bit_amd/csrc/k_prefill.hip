@@ -222,7 +222,32 @@ __device__ __forceinline__ f16x8_t dequant_frag(uint32_t w, f16x2_t s2, f16x2_t 
     return __builtin_bit_cast(f16x8_t, r);
 }
 
-template <int MODE>  // 0: gate/up + GeGLU, 1: down
+// The same eight weights when every scale s of the matrix satisfies 2^-34 <= |s| < 2^-4 (or
+// s = 0): the nibbles of pair p, moved to bits 4..7 of each 16-bit half, are the fp16
+// subnormals q 2^-20 (exact), and one packed fma with the fp16 scale 2^20 s (exact: a normal
+// fp16 value in that range) gives fp16(s q + b), rounded once -- the same value as
+// dequant_frag with two fewer instructions per word.
+__device__ __forceinline__ f16x8_t dequant_frag_sub(uint32_t w, f16x2_t s2, f16x2_t b2) {
+    const uint32_t m = 0x00F000F0u;
+    const uint32_t t[4] = {(w << 4) & m, w & m, (w >> 4) & m, (w >> 8) & m};
+    u32x4_t r;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        r[p] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, t[p]), s2, b2));
+    return __builtin_bit_cast(f16x8_t, r);
+}
+
+// Scale-range check for dequant_frag_sub: *bad |= 1 if any scale/bias word of the matrix has
+// a nonzero scale outside [2^-34, 2^-4) (bf16 magnitude bits outside [0x2E80, 0x3D80); NaN and
+// infinity included). grid ceil(n / 256); block 256
+__global__ __launch_bounds__(256) void k_scale_range(const uint32_t *__restrict__ sb, size_t n, int32_t *__restrict__ bad) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const uint32_t m = sb[i] & 0x7FFFu;
+    if (m != 0 && (m < 0x2E80u || m >= 0x3D80u)) atomicOr(bad, 1);
+}
+
+template <int MODE, bool SUB>  // MODE 0: gate/up + GeGLU, 1: down; SUB: dequant_frag_sub
 __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
     __shared__ __align__(16) uint8_t smem[kSmemBytes];
 
@@ -343,7 +368,7 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
             bw[t] = ld16(smem + kBRingOff + sbi * kBStageBytes + wave * 2048 + t * 1024 + lane * 16);
             const uint32_t sbw =
                 *reinterpret_cast<const uint32_t *>(smem + kSRingOff + sbi * kSStageBytes + wave * 512 + t * 256 + lane * 4);
-            const float sc = bf16_to_f32(sbw & 0xFFFFu), bi = bf16_to_f32(sbw >> 16);
+            const float sc = bf16_to_f32(sbw & 0xFFFFu) * (SUB ? 1048576.0f : 1.0f), bi = bf16_to_f32(sbw >> 16);
             s2[t] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(sc, sc));
             b2[t] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(bi, bi));
         }
@@ -394,14 +419,16 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
 #pragma unroll
                 for (int ms = 0; ms < LMS; ++ms) af[0][ms] = ld16(sA + aoff[0] + 4096 * ms);
 #pragma unroll
-                for (int t = 0; t < 2; ++t) bf[0][t] = dequant_frag(bw[t][0], s2[t], b2[t]);
+                for (int t = 0; t < 2; ++t) bf[0][t] = SUB ? dequant_frag_sub(bw[t][0], s2[t], b2[t]) : dequant_frag(bw[t][0], s2[t], b2[t]);
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     if (s < 3) {
 #pragma unroll
                         for (int ms = 0; ms < LMS; ++ms) af[(s + 1) & 1][ms] = ld16(sA + aoff[s + 1] + 4096 * ms);
 #pragma unroll
-                        for (int t = 0; t < 2; ++t) bf[(s + 1) & 1][t] = dequant_frag(bw[t][s + 1], s2[t], b2[t]);
+                        for (int t = 0; t < 2; ++t)
+                            bf[(s + 1) & 1][t] = SUB ? dequant_frag_sub(bw[t][s + 1], s2[t], b2[t])
+                                                     : dequant_frag(bw[t][s + 1], s2[t], b2[t]);
                     }
 #pragma unroll
                     for (int ms = 0; ms < LMS; ++ms)
@@ -563,14 +590,33 @@ int pre_grid(const moe_layer *L, int T, int mode) {
 
 }  // namespace
 
+hipError_t launch_scale_check(const moe_layer *L, int32_t *flag, hipStream_t s) {
+    const moe_dims &D = L->dims;
+    const size_t E = D.n_experts, d = D.d_model, I = D.d_expert, Is = D.d_shared;
+    hipError_t err = hipMemsetAsync(flag, 0, sizeof(int32_t), s);
+    if (err != hipSuccess) return err;
+    const struct { const uint32_t *sb; size_t n; } mats[6] = {
+        {L->w.gate.sb, E * I * (d / 64)},     {L->w.up.sb, E * I * (d / 64)},  {L->w.down.sb, E * d * (I / 64)},
+        {L->w.sh_gate.sb, Is * (d / 64)},     {L->w.sh_up.sb, Is * (d / 64)},  {L->w.sh_down.sb, d * (Is / 64)}};
+    for (const auto &m : mats)
+        launch(k_scale_range, dim3((unsigned)((m.n + 255) / 256)), dim3(256), 0, s, m.sb, m.n, flag);
+    return hipGetLastError();
+}
+
 hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s) {
     (void)x;   // the GEMM reads the fp16 copy of x the router's prologue wrote
-    launch(k_pre_gemm<0>, dim3(pre_grid(L, T, 0)), dim3(kPreWG), 0, s, make_args(L, T));
+    if (L->pre_sub)
+        launch(k_pre_gemm<0, true>, dim3(pre_grid(L, T, 0)), dim3(kPreWG), 0, s, make_args(L, T));
+    else
+        launch(k_pre_gemm<0, false>, dim3(pre_grid(L, T, 0)), dim3(kPreWG), 0, s, make_args(L, T));
     return hipGetLastError();
 }
 
 hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s) {
-    launch(k_pre_gemm<1>, dim3(pre_grid(L, T, 1)), dim3(kPreWG), 0, s, make_args(L, T));
+    if (L->pre_sub)
+        launch(k_pre_gemm<1, true>, dim3(pre_grid(L, T, 1)), dim3(kPreWG), 0, s, make_args(L, T));
+    else
+        launch(k_pre_gemm<1, false>, dim3(pre_grid(L, T, 1)), dim3(kPreWG), 0, s, make_args(L, T));
     return hipGetLastError();
 }
 

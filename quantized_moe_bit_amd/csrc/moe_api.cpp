@@ -243,6 +243,7 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.r, P * d);
     plan.take(&ws.sh, Tm * d);
     plan.take(&ws.rqf, router_table_floats(D));
+    plan.take(&ws.flag, 1);
     plan.take(&ws.dxg, dec_workspace_floats(D, L->max_dec, 0));
     plan.take(&ws.dh_r, 2 * dec_workspace_floats(D, L->max_dec, 1));
     plan.take(&ws.dh_s, 2 * dec_workspace_floats(D, L->max_dec, 2));
@@ -282,6 +283,7 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     rebase(ws.r, base);
     rebase(ws.sh, base);
     rebase(ws.rqf, base);
+    rebase(ws.flag, base);
     rebase(ws.dxg, base);
     rebase(ws.dh_r, base);
     rebase(ws.dh_s, base);
@@ -291,6 +293,11 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     err = hipMemset(L->ws_base, 0, L->ws_bytes);
     // derived bias-term tables of the prefill GEMMs (read from the borrowed scale/bias words)
     if (err == hipSuccess) err = launch_router_table(L, nullptr);
+    // the prefill GEMMs take the subnormal-code dequantization when every expert scale allows it
+    if (err == hipSuccess) err = launch_scale_check(L, ws.flag, nullptr);
+    int32_t bad = 1;
+    if (err == hipSuccess) err = hipMemcpy(&bad, ws.flag, sizeof(bad), hipMemcpyDeviceToHost);
+    L->pre_sub = err == hipSuccess && bad == 0;
     if (err == hipSuccess) err = hipDeviceSynchronize();
     if (err != hipSuccess) {
         (void)hipFree(L->ws_base);

@@ -71,6 +71,7 @@ struct Workspace {
     float *r;             // [maxT*k, d]        routed expert outputs (bucket order)
     float *sh;            // [maxT, d]          shared expert outputs
     float *rqf;           // router codes, scales and biases as fp32 (prefill router table)
+    int32_t *flag;        // [1]                layer-creation checks
     // decode path (D = decode capacity, KSd/KSs = input pieces of d / of I_s)
     float *dxg;           // [D, d/64]          decode: group sums of x
     uint16_t *dh_r;       // [D*k, I]           decode: routed hidden activations, fp16 bits
@@ -92,6 +93,7 @@ struct moe_layer {
     int device;
     int G_d, G_I, G_Is;        // groups along d, I, I_s
     int max_dec;               // decode capacity = min(max_tokens, MOE_MAX_DECODE_TOKENS)
+    bool pre_sub;              // prefill dequantization through fp16 subnormal codes (expert scales in range)
     void *ws_base;
     size_t ws_bytes;
     qmoe::Workspace ws;
@@ -142,6 +144,7 @@ hipError_t launch_dec_down(const moe_layer *L, int T, float *y, hipStream_t s);
 size_t dec_gateup_lds(const moe_dims &D);
 size_t dec_down_lds(const moe_dims &D);
 size_t dec_workspace_floats(const moe_dims &D, int max_dec, int which);
+hipError_t launch_scale_check(const moe_layer *L, int32_t *flag, hipStream_t s);
 hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s);
 hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s);
 hipError_t launch_combine(const moe_layer *L, int T, float *y, hipStream_t s);

@@ -2,7 +2,7 @@
 widest model dimension the kernels take (8192: router lanes loop over 128 groups), many
 experts with the largest top-k (256 experts, top-16: four logits per lane in the top-k,
 every down-projection wave shared), top-1 (a single routing weight of exactly 1), and widths
-whose last prefill tile is only partly filled.
+whose last prefill tile is only partly filled, and expert scales above 2^-4.
 Same bar as the other parity tests: top-k index sets and grouping bit-exact, outputs within
 max |err| <= 2e-3 * rms of the oracle.
 """
@@ -25,7 +25,16 @@ SHAPES = {
     # widths that leave the last prefill tile part-empty: 10 column blocks of 64 for the down
     # projection (tiles of 4), 6 and 10 hidden blocks of 32 for gate/up
     "ragged_tiles": (synth.Dims(d_model=640, n_experts=8, top_k=2, d_expert=192, d_shared=320), 3, 150),
+    # expert scales and biases 8x the usual (scales up to 0.16): the prefill GEMMs must take the
+    # dequantization that does not rely on scales below 2^-4
+    "large_scales": (synth.Dims(d_model=512, n_experts=8, top_k=2, d_expert=128, d_shared=192), 2, 140),
 }
+
+
+def times8(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns multiplied by 8 (exponent + 3; zeros stay zero)."""
+    b = bits.astype(np.uint32)
+    return np.where((b & 0x7FFF) != 0, b + (3 << 7), b).astype(np.uint16)
 
 
 def check_close(y_gpu, y_ref, what):
@@ -41,6 +50,11 @@ def check_close(y_gpu, y_ref, what):
 def test_shape(name):
     dims, t_dec, t_pre = SHAPES[name]
     lay = synth.gen_layer(dims, 11)
+    if name == "large_scales":
+        for m in (lay.gate, lay.up, lay.down, lay.sh_gate, lay.sh_up, lay.sh_down):
+            m.scales[...] = times8(m.scales)
+            m.biases[...] = times8(m.biases)
+        assert max(synth.bf16_bits_to_f32(m.scales).max() for m in (lay.gate, lay.down)) > 0.0625
     x, _, _ = synth.gen_tokens(dims, t_pre, 12)
     dl = DeviceLayer(lay, max_tokens=t_pre)
     xd = tokens_to_device(x)

@@ -113,16 +113,16 @@ void orc_dequant_row(int bits, int K, const uint8_t *codes, const uint16_t *scal
 /* ------------------------------------------------------------------ router */
 /*
  * Router logits in the canonical fp32 order, for tokens t < T and experts e < E.
- * With x_j the token's bf16 activations (exact in fp32) and q_j the 8-bit codes:
+ * With x_j the token's bf16 activations (exact in fp32), q_j the 8-bit codes and s_g, b_g
+ * the group's scale and bias:
  *
- *   X_g  = ((0 + x_{64g}) + x_{64g+1}) + ... + x_{64g+63}           fp32 adds, ascending j
- *   A_g  = fma(x_{64g+63}, q, ... fma(x_{64g}, q_{64g}, 0))          fp32 fma chain, ascending j
- *   P_g  = fma(s_g, A_g, fl(b_g * X_g))                               the group's affine term
- *   L    = ((0 + P_0) + P_1) + ... + P_{G-1}                           fp32 adds, ascending g
+ *   w_j  = fma(s_g, q_j, b_g)                                         the dequantized weight, fp32
+ *   A_g  = fma(x_{64g+63}, w_{64g+63}, ... fma(x_{64g}, w_{64g}, 0))   fp32 fma chain, ascending j
+ *   L    = ((0 + A_0) + A_1) + ... + A_{G-1}                           fp32 adds, ascending g
  *   logit = L + bias_e   (only when a logit bias is given)
  *
- * Since w = s*q + b, the exact value of P_g is sum_j x_j * w_j over the group; the order
- * above only fixes the rounding, identically on both sides.
+ * This is the router projection W_r x of the affine-dequantized matrix with one fixed
+ * rounding order, so that both sides reach the same fp32 logits and hence the same top-k.
  */
 void orc_router_logits(int T, int d, int E, const uint16_t *x, const uint8_t *rq,
                        const uint16_t *rs, const uint16_t *rb, const float *logit_bias,
@@ -131,27 +131,19 @@ void orc_router_logits(int T, int d, int E, const uint16_t *x, const uint8_t *rq
 #pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
         float *xf = (float *)malloc(sizeof(float) * (size_t)d);
-        float *X = (float *)malloc(sizeof(float) * (size_t)G);
         for (int i = 0; i < d; ++i) xf[i] = bf16_f32(x[(size_t)t * d + i]);
-        for (int g = 0; g < G; ++g) {
-            float s = 0.0f;
-            for (int j = 0; j < 64; ++j) s = s + xf[64 * g + j];
-            X[g] = s;
-        }
         for (int e = 0; e < E; ++e) {
             const uint8_t *q = rq + (size_t)e * d;
             float L = 0.0f;
             for (int g = 0; g < G; ++g) {
+                const float sg = bf16_f32(rs[(size_t)e * G + g]), bg = bf16_f32(rb[(size_t)e * G + g]);
                 float A = 0.0f;
-                for (int j = 0; j < 64; ++j) A = fmaf(xf[64 * g + j], (float)q[64 * g + j], A);
-                float bX = bf16_f32(rb[(size_t)e * G + g]) * X[g];
-                float P = fmaf(bf16_f32(rs[(size_t)e * G + g]), A, bX);
-                L = L + P;
+                for (int j = 0; j < 64; ++j) A = fmaf(xf[64 * g + j], fmaf(sg, (float)q[64 * g + j], bg), A);
+                L = L + A;
             }
             logits[(size_t)t * E + e] = logit_bias ? L + logit_bias[e] : L;
         }
         free(xf);
-        free(X);
     }
 }
 

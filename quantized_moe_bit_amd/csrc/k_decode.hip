@@ -46,9 +46,10 @@ constexpr size_t kGlueLdsMax = 32768;   // bf16 bytes of x the fused residual st
 
 // ----------------------------------------------------------------------------- router
 // The wave's expert e; lane g handles input group g (and g + 64, ... for d > 4096).
-// P[t][g] into Ps, then lanes t < T sum over g in ascending order (the group sums X also go
-// to xg_out when it is given). Fixed fp32 order:
-//   X = ((0 + x_0) + x_1) + ...; A = fma chain; P = fma(s, A, fl(b * X)); L = ((0 + P_0) + ...)
+// A[t][g] into Ps, then lanes t < T sum over g in ascending order. Fixed fp32 order:
+//   w_j = fma(s, q_j, b); A = fma chain of x_j w_j, ascending j; L = ((0 + A_0) + A_1) + ...
+// The group sums X = ((0 + x_0) + x_1) + ... go to xg_out when it is given (the gate/up
+// units' bias terms use them; they are not part of the logits).
 __device__ __forceinline__ void router_wave(const uint16_t *__restrict__ x, int T, int d, int e, const uint8_t *__restrict__ rq,
                             const uint32_t *__restrict__ rsb, float *Ps, float *xg_out) {
 #pragma clang fp contract(off)
@@ -75,11 +76,10 @@ __device__ __forceinline__ void router_wave(const uint16_t *__restrict__ x, int 
                 const float qa = (float)((c >> sh) & 0xFFu), qb = (float)((c >> (sh + 8)) & 0xFFu);
                 X = X + xa;
                 X = X + xb;
-                A = __builtin_fmaf(xa, qa, A);
-                A = __builtin_fmaf(xb, qb, A);
+                A = __builtin_fmaf(xa, __builtin_fmaf(sc, qa, bi), A);
+                A = __builtin_fmaf(xb, __builtin_fmaf(sc, qb, bi), A);
             }
-            const float bX = bi * X;
-            Ps[t * G + g] = __builtin_fmaf(sc, A, bX);
+            Ps[t * G + g] = A;
             if (xg_out) xg_out[t * G + g] = X;
         }
     }

@@ -8,7 +8,7 @@
 // with one packed fp16 fma per two weights (a single rounding of the exact value; exact
 // whenever the value fits fp16's 11 significant bits, as it does for bf16 scales and biases
 // of like magnitude). The activations are fp16 too (x converted exactly from bf16 by the
-// router's prologue; the hidden activation h = gelu(g) * u is carried in fp16), and
+// router; the hidden activation h = gelu(g) * u is carried in fp16), and
 // v_mfma_f32_32x32x16_f16 accumulates in fp32 across all groups.
 //
 // Work items: (expert or shared, 128-row tile, output tile), one per workgroup; all output
@@ -604,7 +604,7 @@ hipError_t launch_scale_check(const moe_layer *L, int32_t *flag, hipStream_t s) 
 }
 
 hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s) {
-    (void)x;   // the GEMM reads the fp16 copy of x the router's prologue wrote
+    (void)x;   // the GEMM reads the fp16 copy of x the router wrote
     if (L->pre_sub)
         launch(k_pre_gemm<0, true>, dim3(pre_grid(L, T, 0)), dim3(kPreWG), 0, s, make_args(L, T));
     else

@@ -6,10 +6,9 @@
 // shape"; "Decode", router listing), plus an optional per-expert logit bias. The
 // logits decide an integer result (the top-k set), so they are computed in one fixed
 // fp32 order, the same one the CPU oracle writes out:
-//   X_g = x_{64g} + ... + x_{64g+63}               (fp32 adds, ascending)
-//   A_g = fma chain of x_j * q_j, ascending j         (fp32, starting from 0)
-//   P_g = fma(scale_g, A_g, fl(bias_g * X_g))
-//   logit = (P_0 + P_1 + ... + P_{G-1}) [+ logit_bias]   (fp32 adds, ascending g)
+//   w_j = fma(scale_g, q_j, bias_g)                   (the dequantized weight, fp32)
+//   A_g = fma chain of x_j * w_j, ascending j         (fp32, starting from 0)
+//   logit = (A_0 + A_1 + ... + A_{G-1}) [+ logit_bias]   (fp32 adds, ascending g)
 // Contraction is disabled in this file so the compiler cannot fuse or reorder these.
 //
 // Top-k: the k largest logits, largest first, equal values ordered by lower expert
@@ -30,50 +29,22 @@ namespace {
 
 
 constexpr int kRNE = 4;                  // experts per wave of the prefill router
-constexpr int kRBlk = 64 * kRNE + 2 * kRNE;   // router table floats per (expert block, group)
-
-// Group sums X_g = ((0 + x_0) + x_1) + ... + x_63 of each token (fp32, ascending), and the
-// fp16 copy of x the prefill gate/up GEMM reads (exact for |x| in fp16's normal range).
-// grid: ceil(T * G / 256); block 256
-__global__ __launch_bounds__(256) void k_xsum(const uint16_t *__restrict__ x, int T, int d,
-                                              float *__restrict__ xsum, uint16_t *__restrict__ x16) {
-    const int G = d / 64;
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= T * G) return;
-    const int t = i / G, g = i % G;
-    const u32x4_t *xp = reinterpret_cast<const u32x4_t *>(x + (size_t)t * d + 64 * g);
-    u32x4_t *op = reinterpret_cast<u32x4_t *>(x16 + (size_t)t * d + 64 * g);
-    u32x4_t v[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = xp[q];
-    float X = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        u32x4_t h;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float lo = bf16_to_f32(v[q][w] & 0xFFFFu), hi = bf16_to_f32(v[q][w] >> 16);
-            X = X + lo;
-            X = X + hi;
-            h[w] = f32_to_f16_sat(lo) | (f32_to_f16_sat(hi) << 16);
-        }
-        op[q] = h;
-    }
-    xsum[i] = X;
-}
+constexpr int kRBlk = 64 * kRNE;   // router table floats per (expert block, group)
 
 // Prefill router: lane = token, wave = kRNE = 4 consecutive experts, workgroup = 4 waves (64
 // tokens x 16 experts). Per 64-input group the workgroup stages its tokens' inputs into LDS as
 // fp32, converted once for all waves and double-buffered (the next group's loads are in
-// flight during this group's chains). The codes come as fp32 from a table built at layer
-// creation: one 16-byte load per lane and 16-input chunk puts input j of the chunk for the
-// wave's four experts into lane j of every 16-lane row, and each fma takes its code from
-// there by a row broadcast (DPP row_newbcast), so no instruction is spent on moving codes.
-// Per (token, expert) the arithmetic is the fixed order stated at the top of this file.
+// flight during this group's chains); the workgroups of the first expert block also store
+// the fp16 copy of x the prefill gate/up GEMM reads (exact for |x| in fp16's normal range).
+// The weights come dequantized to fp32 from a table built at layer creation: one 16-byte load
+// per lane and 16-input chunk puts input j of the chunk for the wave's four experts into lane
+// j of every 16-lane row, and each fma takes its weight from there by a row broadcast (DPP
+// row_newbcast), so no instruction is spent on moving weights. Per (token, expert) the
+// arithmetic is the fixed order stated at the top of this file.
 //
-// Table layout, per block of kRNE experts eb and group g (kRBlk floats): codes [4 jc][16 j][kRNE]
-// (input 16 jc + j of expert kRNE eb + i at [jc][j][i]), then kRNE scales, then kRNE biases.
-// Experts past E are zero.
+// Table layout, per block of kRNE experts eb and group g (kRBlk floats): weights
+// [4 jc][16 j][kRNE] (input 16 jc + j of expert kRNE eb + i at [jc][j][i]). Experts past E are
+// zero.
 // grid: (ceil(T / 64), ceil(E / (4 kRNE))); block 256
 constexpr int kXPitch = 68;   // fp32 per staged token row: 16 lanes of one ds_read_b128 pass hit 64 distinct banks
 static_assert(kRNE == 4, "one 16-byte load per lane holds the four experts' codes of an input");
@@ -92,8 +63,8 @@ __device__ __forceinline__ void chunk_fmas(float (&A)[kRNE], const f32x4_t (&xv)
 }
 
 __global__ __launch_bounds__(256) void k_router_tok(const uint16_t *__restrict__ x, int T, int d, int E,
-                                                    const float *__restrict__ tab, const float *__restrict__ xsum,
-                                                    const float *__restrict__ logit_bias, float *__restrict__ logits) {
+                                                    const float *__restrict__ tab, const float *__restrict__ logit_bias,
+                                                    float *__restrict__ logits, uint16_t *__restrict__ x16) {
     __shared__ __align__(16) float xs[2][64][kXPitch];
     const int G = d / 64;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -101,13 +72,24 @@ __global__ __launch_bounds__(256) void k_router_tok(const uint16_t *__restrict__
     const int eb = min(blockIdx.y * 4 + wave, cdiv(E, kRNE) - 1);   // waves past E compute a valid block, store nothing
     const int e0 = (blockIdx.y * 4 + wave) * kRNE;
     const int t = blockIdx.x * 64 + lane;
-    const float *xsr = xsum + (size_t)(t < T ? t : T - 1) * G;
     // staging: thread -> token tid/4, inputs 16 (tid%4) .. +15 of the group
     const int st = tid >> 2, sq = tid & 3;
     const int stok = min((int)blockIdx.x * 64 + st, T - 1);
+    const bool st_x16 = blockIdx.y == 0 && (int)blockIdx.x * 64 + st < T;   // this thread stores x16
     const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(x + (size_t)stok * d + 16 * sq);
+    u32x4_t *xo = reinterpret_cast<u32x4_t *>(x16 + (size_t)stok * d + 16 * sq);
     const float *blk = tab + (size_t)eb * G * kRBlk;
-    auto stage = [&](int buf, const u32x4_t (&v)[2]) {
+    auto stage = [&](int buf, int g, const u32x4_t (&v)[2]) {
+        if (st_x16) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                u32x4_t h;
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    h[w] = f32_to_f16_sat(bf16_to_f32(v[c][w] & 0xFFFFu)) | (f32_to_f16_sat(bf16_to_f32(v[c][w] >> 16)) << 16);
+                xo[8 * g + c] = h;
+            }
+        }
         f32x4_t f[4];
 #pragma unroll
         for (int c = 0; c < 2; ++c)
@@ -130,18 +112,15 @@ __global__ __launch_bounds__(256) void k_router_tok(const uint16_t *__restrict__
     u32x4_t nv[2] = {xr[0], xr[1]};
     f32x4_t qa[4], qb[4];   // codes of the even and odd groups (loaded straight into place)
     load_q(0, qa);
-    stage(0, nv);
-    float Xn = xsr[0];
+    stage(0, 0, nv);
     __syncthreads();
     auto group = [&](int g, const f32x4_t (&q)[4], f32x4_t (&qnext)[4]) {
         const int buf = g & 1;
-        const float X = Xn;
         {   // next group's loads in flight during this group's chains (the last group re-reads itself)
             const int gn = g + 1 < G ? g + 1 : g;
             nv[0] = xr[8 * gn];
             nv[1] = xr[8 * gn + 1];
             load_q(gn, qnext);
-            Xn = xsr[gn];
         }
         float A[kRNE];
 #pragma unroll
@@ -153,15 +132,10 @@ __global__ __launch_bounds__(256) void k_router_tok(const uint16_t *__restrict__
             for (int c = 0; c < 4; ++c) xv[c] = *reinterpret_cast<const f32x4_t *>(&xs[buf][lane][16 * jc + 4 * c]);
             chunk_fmas<0>(A, xv, q[jc]);
         }
-        const float *sb = blk + (size_t)g * kRBlk + 64 * kRNE;
 #pragma unroll
-        for (int i = 0; i < kRNE; ++i) {
-            const float sc = sb[i], bi = sb[kRNE + i];
-            const float bX = bi * X;
-            L[i] = L[i] + __builtin_fmaf(sc, A[i], bX);
-        }
+        for (int i = 0; i < kRNE; ++i) L[i] = L[i] + A[i];
         // the other buffer was last read in group g - 1, which every wave has finished
-        if (g + 1 < G) stage(buf ^ 1, nv);
+        if (g + 1 < G) stage(buf ^ 1, g + 1, nv);
         __syncthreads();
     };
     for (int g = 0; g < G; g += 2) {
@@ -176,7 +150,7 @@ __global__ __launch_bounds__(256) void k_router_tok(const uint16_t *__restrict__
     }
 }
 
-// The router table k_router_tok reads (codes, scales and biases as exact fp32; layout above).
+// The router table k_router_tok reads (weights fma(scale, q, bias) in fp32; layout above).
 // grid ceil(n / 256) with n = ceil(E / kRNE) * G * kRBlk; block 256
 __global__ __launch_bounds__(256) void k_router_table(const uint8_t *__restrict__ q, const uint32_t *__restrict__ sb,
                                                       int E, int d, float *__restrict__ out) {
@@ -187,18 +161,12 @@ __global__ __launch_bounds__(256) void k_router_table(const uint8_t *__restrict_
     const int r = (int)(i % kRBlk);
     const size_t bg = i / kRBlk;
     const int g = (int)(bg % G), eb = (int)(bg / G);
+    const int jc = r / (16 * kRNE), j = (r / kRNE) % 16, ii = r % kRNE;
+    const int e = eb * kRNE + ii;
     float v = 0.0f;
-    if (r < 64 * kRNE) {
-        const int jc = r / (16 * kRNE), j = (r / kRNE) % 16, ii = r % kRNE;
-        const int e = eb * kRNE + ii;
-        if (e < E) v = (float)q[(size_t)e * d + 64 * g + 16 * jc + j];
-    } else {
-        const int ii = (r - 64 * kRNE) % kRNE, part = (r - 64 * kRNE) / kRNE;   // 0: scale, 1: bias
-        const int e = eb * kRNE + ii;
-        if (e < E) {
-            const uint32_t w = sb[(size_t)e * G + g];
-            v = bf16_to_f32(part == 0 ? (w & 0xFFFFu) : (w >> 16));
-        }
+    if (e < E) {
+        const uint32_t w = sb[(size_t)e * G + g];
+        v = __builtin_fmaf(bf16_to_f32(w & 0xFFFFu), (float)q[(size_t)e * d + 64 * g + 16 * jc + j], bf16_to_f32(w >> 16));
     }
     out[i] = v;
 }
@@ -430,10 +398,9 @@ __global__ __launch_bounds__(256) void k_bucket_scatter(const int32_t *__restric
 }  // namespace
 
 hipError_t launch_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s) {
-    const int d = L->dims.d_model, E = L->dims.n_experts, G = d / 64;
-    launch(k_xsum, dim3(cdiv(T * G, 256)), dim3(256), 0, s, x, T, d, L->ws.xsum, L->ws.x16);
-    launch(k_router_tok, dim3(cdiv(T, 64), cdiv(E, 4 * kRNE)), dim3(256), 0, s, x, T, d, E, L->ws.rqf, L->ws.xsum,
-           L->w.logit_bias, logits);
+    const int d = L->dims.d_model, E = L->dims.n_experts;
+    launch(k_router_tok, dim3(cdiv(T, 64), cdiv(E, 4 * kRNE)), dim3(256), 0, s, x, T, d, E, L->ws.rqf,
+           L->w.logit_bias, logits, L->ws.x16);
     return hipGetLastError();
 }
 

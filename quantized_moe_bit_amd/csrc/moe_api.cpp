@@ -228,7 +228,6 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.logits, Tm * E);
     plan.take(&ws.idx, P);
     plan.take(&ws.wts, P);
-    plan.take(&ws.xsum, Tm * L->G_d);
     plan.take(&ws.x16, Tm * d);
     plan.take(&ws.counts, E);
     plan.take(&ws.offsets, E + 1);
@@ -268,7 +267,6 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     rebase(ws.logits, base);
     rebase(ws.idx, base);
     rebase(ws.wts, base);
-    rebase(ws.xsum, base);
     rebase(ws.x16, base);
     rebase(ws.counts, base);
     rebase(ws.offsets, base);

@@ -56,8 +56,7 @@ struct Workspace {
     float *logits;        // [maxT, E]
     int32_t *idx;         // [maxT, k]
     float *wts;           // [maxT, k]
-    float *xsum;          // [maxT, G]          router-order group sums of x
-    uint16_t *x16;        // [maxT, d]          fp16 copy of x (prefill gate/up operand)
+    uint16_t *x16;        // [maxT, d]          fp16 copy of x (prefill gate/up operand, written by the router)
     int32_t *counts;      // [E]
     int32_t *offsets;     // [E+1]
     int32_t *tile_off;    // [E+1]              prefix sum of ceil(count/kMT)
@@ -70,7 +69,7 @@ struct Workspace {
     uint16_t *h_s;        // [maxT, I_s]        shared hidden activations, fp16 bits
     float *r;             // [maxT*k, d]        routed expert outputs (bucket order)
     float *sh;            // [maxT, d]          shared expert outputs
-    float *rqf;           // router codes, scales and biases as fp32 (prefill router table)
+    float *rqf;           // router weights fma(scale, q, bias) as fp32 (prefill router table)
     int32_t *flag;        // [1]                layer-creation checks
     // decode path (D = decode capacity, KSd/KSs = input pieces of d / of I_s)
     float *dxg;           // [D, d/64]          decode: group sums of x

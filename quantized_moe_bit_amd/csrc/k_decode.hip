@@ -50,16 +50,32 @@ constexpr size_t kGlueLdsMax = 32768;   // bf16 bytes of x the fused residual st
 //   w_j = fma(s, q_j, b); A = fma chain of x_j w_j, ascending j; L = ((0 + A_0) + A_1) + ...
 // The group sums X = ((0 + x_0) + x_1) + ... go to xg_out when it is given (the gate/up
 // units' bias terms use them; they are not part of the logits).
+// The 64 codes and the scale/bias word of expert e's input group g.
+struct RouterCodes {
+    u32x4_t c[4];
+    uint32_t sbw;
+};
+__device__ __forceinline__ RouterCodes router_codes(const uint8_t *__restrict__ rq, const uint32_t *__restrict__ rsb,
+                                                    int d, int e, int g) {
+    RouterCodes r;
+    const u32x4_t *cp = reinterpret_cast<const u32x4_t *>(rq + (size_t)e * d + 64 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.c[i] = cp[i];
+    r.sbw = rsb[(size_t)e * (d / 64) + g];
+    return r;
+}
+
+// pre: the codes of group `lane` when the caller loaded them ahead (or null)
 __device__ __forceinline__ void router_wave(const uint16_t *__restrict__ x, int T, int d, int e, const uint8_t *__restrict__ rq,
-                            const uint32_t *__restrict__ rsb, float *Ps, float *xg_out) {
+                            const uint32_t *__restrict__ rsb, float *Ps, float *xg_out, const RouterCodes *pre) {
 #pragma clang fp contract(off)
     const int G = d / 64, lane = threadIdx.x & 63;
     for (int g = lane; g < G; g += 64) {
-        const u32x4_t *cp = reinterpret_cast<const u32x4_t *>(rq + (size_t)e * d + 64 * g);
-        const u32x4_t c0 = cp[0], c1 = cp[1], c2 = cp[2], c3 = cp[3];
+        const RouterCodes rc = (pre && g == lane) ? *pre : router_codes(rq, rsb, d, e, g);
+        const u32x4_t c0 = rc.c[0], c1 = rc.c[1], c2 = rc.c[2], c3 = rc.c[3];
         const uint32_t cw[16] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3],
                                  c2[0], c2[1], c2[2], c2[3], c3[0], c3[1], c3[2], c3[3]};
-        const uint32_t sbw = rsb[(size_t)e * G + g];
+        const uint32_t sbw = rc.sbw;
         const float sc = bf16_to_f32(sbw & 0xFFFFu), bi = bf16_to_f32(sbw >> 16);
         for (int t = 0; t < T; ++t) {
             const u32x4_t *xp = reinterpret_cast<const u32x4_t *>(x + (size_t)t * d + 64 * g);
@@ -350,6 +366,11 @@ __global__ __launch_bounds__(64 * kRW) void k_dec_router(DecArgs a) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     float *Ps = reinterpret_cast<float *>(smem);     // [kRW][T][G]
     const uint16_t *x = a.x;
+    const int e = blockIdx.x * kRW + wave;
+    // with the residual step in front, the codes of the wave's first group are requested
+    // before it, so their latency overlaps the step's own loads
+    RouterCodes pre;
+    if (GLUE && e < a.E) pre = router_codes(a.rq, a.rsb, a.d, e, min(lane, G - 1));
     if (GLUE) {
         uint16_t *xs = reinterpret_cast<uint16_t *>(smem + sizeof(float) * kRW * a.T * G);
         double *red = reinterpret_cast<double *>(xs + (size_t)a.T * a.d);
@@ -362,9 +383,8 @@ __global__ __launch_bounds__(64 * kRW) void k_dec_router(DecArgs a) {
                 *reinterpret_cast<u32x4_t *>(a.x_out + 8 * i) = *reinterpret_cast<const u32x4_t *>(xs + 8 * i);
         x = xs;
     }
-    const int e = blockIdx.x * kRW + wave;
     float *P = Ps + (size_t)wave * a.T * G;
-    if (e < a.E) router_wave(x, a.T, a.d, e, a.rq, a.rsb, P, e == 0 ? a.xg : nullptr);
+    if (e < a.E) router_wave(x, a.T, a.d, e, a.rq, a.rsb, P, e == 0 ? a.xg : nullptr, GLUE ? &pre : nullptr);
     __syncthreads();
     if (e < a.E && lane < a.T) {
 #pragma clang fp contract(off)

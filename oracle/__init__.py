@@ -55,7 +55,8 @@ def lib():
         L.orc_gelu_tanh.restype = C.c_double
         L.orc_dequant_row.argtypes = [i32, i32, vp, vp, vp, vp]
         L.orc_router_logits.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp]
-        L.orc_topk.argtypes = [i32, i32, i32, vp, vp, vp]
+        L.orc_topk.argtypes = [i32, i32, i32, vp, vp, vp, vp]
+        L.orc_router_prologue.argtypes = [i32, i32, vp, vp, C.c_double, vp]
         L.orc_bucket.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
         L.orc_ffn.argtypes = [i32, i32, vp, C.POINTER(_QMat), C.POINTER(_QMat), C.POINTER(_QMat), vp]
         L.orc_layer_tokens.argtypes = [i32, i32, i32, i32, i32, vp, i32, vp, vp, vp] + \
@@ -107,14 +108,25 @@ def router_logits(x, rq, rs, rb, logit_bias=None) -> np.ndarray:
     return out
 
 
-def topk(logits, k: int):
-    """-> (idx int32 [T,k], w float64 [T,k])"""
+def topk(logits, k: int, per_expert_scale=None):
+    """-> (idx int32 [T,k], w float64 [T,k]); per_expert_scale: optional bf16 bits [E]"""
     logits = _c(logits, np.float32)
     T, E = logits.shape
+    pes = None if per_expert_scale is None else _c(per_expert_scale, np.uint16)
     idx = np.empty((T, k), np.int32)
     w = np.empty((T, k), np.float64)
-    lib().orc_topk(T, E, k, _p(logits), _p(idx), _p(w))
+    lib().orc_topk(T, E, k, _p(logits), _p(pes), _p(idx), _p(w))
     return idx, w
+
+
+def router_prologue(x, router_scale, eps: float = STACK_EPS):
+    """x: bf16 bits [T,d]; router_scale: bf16 bits [d] -> router input u, bf16 bits [T,d]"""
+    x = _c(x, np.uint16)
+    rs = _c(router_scale, np.uint16)
+    T, d = x.shape
+    u = np.empty_like(x)
+    lib().orc_router_prologue(T, d, _p(x), _p(rs), float(eps), _p(u))
+    return u
 
 
 def bucket(idx, E: int):
@@ -175,10 +187,12 @@ def layer_tokens(layer, x, idx, w, tokens: Optional[Sequence[int]] = None, want_
 
 
 def route(layer, x):
-    """Router logits, top-k and weights, and expert grouping for all tokens of x."""
-    logits = router_logits(x, layer.router.codes, layer.router.scales, layer.router.biases,
+    """Router logits, top-k and weights, and expert grouping for all tokens of x (with the
+    router prologue and per-expert scale when the layer has them)."""
+    u = x if layer.router_scale is None else router_prologue(x, layer.router_scale)
+    logits = router_logits(u, layer.router.codes, layer.router.scales, layer.router.biases,
                            layer.logit_bias)
-    idx, w = topk(logits, layer.dims.top_k)
+    idx, w = topk(logits, layer.dims.top_k, layer.per_expert_scale)
     counts, offsets, perm, pos = bucket(idx, layer.dims.n_experts)
     return dict(logits=logits, idx=idx, w=w, counts=counts, offsets=offsets, perm=perm, pos=pos)
 

@@ -150,9 +150,11 @@ void orc_router_logits(int T, int d, int E, const uint16_t *x, const uint8_t *rq
 /*
  * Top-k of each row of logits: the k largest values, listed largest first; among equal
  * values the lower expert index comes first (and is the one kept at the k boundary).
- * Routing weights: softmax over the k selected logits, in float64.
+ * Routing weights: softmax over the k selected logits, in float64, each multiplied by the
+ * selected expert's per_expert_scale when one is given (Mference "Decode", router listing).
  */
-void orc_topk(int T, int E, int k, const float *logits, int32_t *idx, double *w) {
+void orc_topk(int T, int E, int k, const float *logits, const uint16_t *per_expert_scale, int32_t *idx,
+              double *w) {
 #pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
         const float *l = logits + (size_t)t * E;
@@ -170,7 +172,11 @@ void orc_topk(int T, int E, int k, const float *logits, int32_t *idx, double *w)
         double m = (double)l[sel[0]];
         double z = 0.0;
         for (int s = 0; s < k; ++s) z += exp((double)l[sel[s]] - m);
-        for (int s = 0; s < k; ++s) w[(size_t)t * k + s] = exp((double)l[sel[s]] - m) / z;
+        for (int s = 0; s < k; ++s) {
+            double v = exp((double)l[sel[s]] - m) / z;
+            if (per_expert_scale) v *= bf16_f64(per_expert_scale[sel[s]]);   /* router epilogue */
+            w[(size_t)t * k + s] = v;
+        }
         free(taken);
     }
 }
@@ -290,6 +296,30 @@ void orc_layer_tokens(int d, int E, int k, int I, int Is, const uint16_t *x, int
         free(xd);
         free(sh);
         free(r);
+    }
+}
+
+/* ------------------------------------------------------------------ router prologue */
+/*
+ * Router input from the layer input (Mference "Decode", router listing): the input is
+ * normalized without a learned scale, multiplied by the router scale and by 1/sqrt(d):
+ *   v = x / sqrt(mean(x^2) + eps)          (sum of squares ascending, float64)
+ *   u = bf16(((v * router_scale) / sqrt(d)))   (float64, rounded once)
+ * x, u: bf16 bits [T, d]; router_scale: bf16 bits [d].
+ */
+void orc_router_prologue(int T, int d, const uint16_t *x, const uint16_t *router_scale, double eps,
+                         uint16_t *u) {
+    for (int t = 0; t < T; ++t) {
+        const uint16_t *xt = x + (size_t)t * d;
+        double ss = 0.0;
+        for (int i = 0; i < d; ++i) {
+            const double v = bf16_f64(xt[i]);
+            ss += v * v;
+        }
+        const double inv = 1.0 / sqrt(ss / d + eps);
+        const double sd = sqrt((double)d);
+        for (int i = 0; i < d; ++i)
+            u[(size_t)t * d + i] = orc_f64_to_bf16(((bf16_f64(xt[i]) * inv) * bf16_f64(router_scale[i])) / sd);
     }
 }
 

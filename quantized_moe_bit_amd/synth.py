@@ -150,6 +150,8 @@ class Layer:
     logit_bias: Optional[np.ndarray] = None       # float32 [E]
     tie_groups: Optional[np.ndarray] = None       # int32 [n_groups, 9], ascending within a group
     meta: dict = field(default_factory=dict)
+    router_scale: Optional[np.ndarray] = None     # bf16 bits [d]: router prologue scale
+    per_expert_scale: Optional[np.ndarray] = None  # bf16 bits [E]: routing-weight scale
 
     def nbytes(self) -> int:
         tot = 0

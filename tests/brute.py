@@ -76,6 +76,15 @@ def ffn_dense(x: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray) -> 
     return rowdot(Wd, h)
 
 
+def router_prologue(x: np.ndarray, rs: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """Router input: x / rms(x) (no learned scale) * router_scale / sqrt(d), each value rounded
+    exactly to bf16 (x, rs float64 [T, d] / [d] -> float64 values of the bf16 results)."""
+    d = x.shape[-1]
+    inv = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    v = x * inv * rs[None, :] / math.sqrt(d)
+    return np.vectorize(rne_bf16_exact, otypes=[np.float64])(v)
+
+
 def layer(lay, x_bits: np.ndarray):
     """-> dict(logits64, order, idx, w, y) computed densely for every token and expert."""
     dims = lay.dims
@@ -85,7 +94,8 @@ def layer(lay, x_bits: np.ndarray):
     Wr = dense(lay.router)
     Wg, Wu, Wd = dense(lay.gate), dense(lay.up), dense(lay.down)
     Sg, Su, Sd = dense(lay.sh_gate), dense(lay.sh_up), dense(lay.sh_down)
-    logits = np.stack([rowdot(Wr, x[t]) for t in range(T)])
+    xr = x if lay.router_scale is None else router_prologue(x, bf16_value(lay.router_scale))
+    logits = np.stack([rowdot(Wr, xr[t]) for t in range(T)])
     if lay.logit_bias is not None:
         logits = logits + lay.logit_bias.astype(np.float64)[None, :]
     y = np.zeros((T, dims.d_model))
@@ -96,6 +106,8 @@ def layer(lay, x_bits: np.ndarray):
         sel = order[:k]
         z = np.exp(logits[t, sel] - logits[t, sel].max())
         wsel = z / z.sum()
+        if lay.per_expert_scale is not None:
+            wsel = wsel * bf16_value(lay.per_expert_scale)[sel]
         mask = np.zeros(E)
         mask[sel] = wsel
         outs = np.stack([ffn_dense(x[t], Wg[e], Wu[e], Wd[e]) for e in range(E)])  # every expert

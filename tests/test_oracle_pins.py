@@ -152,6 +152,53 @@ def test_router_matches_brute_force_selection():
     np.testing.assert_array_equal(r["idx"][:6], b["idx"])
 
 
+# ----------------------------------------------------------------------------- router prologue / epilogue
+def test_router_prologue_closed_form():
+    # constant inputs: x / rms(x) = 1 up to eps, so u = bf16(router_scale / sqrt(d))
+    d = 256
+    one = synth.f32_to_bf16_bits(np.ones((2, d), np.float32))
+    u = oracle.router_prologue(one, synth.f32_to_bf16_bits(np.ones(d, np.float32)))
+    assert np.all(u == 0x3D80)                                   # 1/16 exactly
+    three = synth.f32_to_bf16_bits(np.full((1, d), -3.0, np.float32))
+    u = oracle.router_prologue(three, synth.f32_to_bf16_bits(np.full(d, 2.0, np.float32)))
+    assert np.all(u == 0xBE00)                                   # -2/16 = -0.125
+    # router_scale entering per channel
+    rs = synth.f32_to_bf16_bits(np.where(np.arange(d) % 2 == 0, 1.0, 4.0).astype(np.float32))
+    u = oracle.router_prologue(one, rs)
+    assert np.all(u[:, 0::2] == 0x3D80) and np.all(u[:, 1::2] == 0x3E80)   # 1/16 and 4/16
+    # inputs small enough that eps = 1e-6 matters: x = 2^-10, mean(x^2) = 2^-20
+    tiny = synth.f32_to_bf16_bits(np.full((1, d), 2.0 ** -10, np.float32))
+    u = oracle.router_prologue(tiny, synth.f32_to_bf16_bits(np.ones(d, np.float32)))
+    want = brute.rne_bf16_exact(2.0 ** -10 / math.sqrt(2.0 ** -20 + 1e-6) / 16.0)
+    assert np.all(brute.bf16_value(u) == want) and abs(want - 2.0 ** -10 * 1024 / 16) > 0.01
+
+
+def test_router_prologue_matches_exact_rounding():
+    rng = np.random.default_rng(12)
+    T, d = 3, 192
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32) * 3)
+    rs = synth.f32_to_bf16_bits(rng.uniform(0.25, 2.0, d).astype(np.float32))
+    u = oracle.router_prologue(x, rs)
+    ref = brute.router_prologue(brute.bf16_value(x), brute.bf16_value(rs))
+    np.testing.assert_array_equal(brute.bf16_value(u), ref)
+
+
+def test_per_expert_scale_multiplies_routing_weights():
+    rng = np.random.default_rng(13)
+    logits = rng.standard_normal((40, 32)).astype(np.float32)
+    idx0, w0 = oracle.topk(logits, 4)
+    idx1, w1 = oracle.topk(logits, 4, np.full(32, 0x3F80, np.uint16))     # scale 1: unchanged
+    np.testing.assert_array_equal(idx1, idx0)
+    np.testing.assert_array_equal(w1, w0)
+    idx2, w2 = oracle.topk(logits, 4, np.full(32, 0x4000, np.uint16))     # scale 2: doubled exactly
+    np.testing.assert_array_equal(idx2, idx0)
+    np.testing.assert_array_equal(w2, 2.0 * w0)
+    pes = synth.f32_to_bf16_bits(rng.uniform(0.5, 2.0, 32).astype(np.float32))
+    idx3, w3 = oracle.topk(logits, 4, pes)
+    np.testing.assert_array_equal(idx3, idx0)                           # selection is unaffected
+    np.testing.assert_allclose(w3, w0 * brute.bf16_value(pes)[idx0], rtol=1e-15)
+
+
 # ----------------------------------------------------------------------------- top-k
 def test_topk_equals_full_sort_with_ties():
     rng = np.random.default_rng(7)
@@ -216,11 +263,13 @@ def _cmp_layer(lay, x, ntok):
     # routing weights: softmax of fp32 logits vs fp64 logits. Each logit is within the router's
     # error bound B (the bound of test_router_fp32_within_error_bound_of_fp64), so each weight
     # is within a relative exp(2 max B) - 1 of the fp64 one.
-    xv = brute.bf16_value(x[:ntok])
+    xv = brute.bf16_value(x[:ntok] if lay.router_scale is None else oracle.router_prologue(x[:ntok], lay.router_scale))
     mag = np.abs(xv) @ np.abs(brute.dense(lay.router)).T + np.abs(xv) @ np.abs(
         brute.bf16_value(np.repeat(lay.router.biases, 64, axis=1))).T
     bound = 2 * (64 + lay.dims.G + 4) * 2.0 ** -24 * mag
     bmax = np.take_along_axis(bound, r["idx"], axis=1).max(axis=1, keepdims=True)
+    if lay.per_expert_scale is not None:   # the logit bound is relative to the softmax weights
+        bmax = bmax * (1.0 + 2.0 ** -40)
     assert np.all(np.abs(r["w"] - b["w"]) <= b["w"] * np.expm1(2 * bmax) + 1e-15)
     assert np.max(bmax) < 1e-2   # under 2 % relative: a wrong weight or a dropped logit term shows
     scale = np.sqrt(np.mean(b["y"] ** 2))
@@ -240,6 +289,16 @@ def test_layer_matches_dense_brute_force_odd_shapes():
     lay = synth.gen_layer(dims, 21, router="normal", zipf_s=1.0)
     x, _, _ = synth.gen_tokens(dims, 3, 21)
     _cmp_layer(lay, x, 3)
+
+
+def test_layer_matches_dense_brute_force_with_router_prologue_and_expert_scale():
+    dims = synth.Dims(d_model=256, n_experts=8, top_k=3, d_expert=64, d_shared=128)
+    lay = synth.gen_layer(dims, 23, router="normal")
+    rng = np.random.default_rng(23)
+    lay.router_scale = synth.f32_to_bf16_bits(rng.uniform(0.5, 1.5, dims.d_model).astype(np.float32))
+    lay.per_expert_scale = synth.f32_to_bf16_bits(rng.uniform(0.5, 2.0, dims.n_experts).astype(np.float32))
+    x, _, _ = synth.gen_tokens(dims, 4, 23)
+    _cmp_layer(lay, x, 4)
 
 
 def test_identical_experts_make_output_independent_of_routing():

@@ -75,6 +75,7 @@ def main():
     ap.add_argument("--no-stack", action="store_true", help="skip the 30-layer decode stack workload")
     ap.add_argument("--stack-layers", type=int, default=0, help="layers of the stack workload (0: its 30)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prologue", action="store_true", help="skip the router prologue measurement")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -247,6 +248,44 @@ def main():
                                         unit="TFLOP/s", frac=round(tf / MFMA_PEAK_TFLOPS, 4))
         result["prefill"] = pre
         P.close()
+        if not args.no_prologue:
+            # widened row: the same layer and tokens with the router prologue and per-expert scale
+            rng = np.random.default_rng(7)
+            lp.router_scale = synth.f32_to_bf16_bits(rng.uniform(0.5, 1.5, d).astype(np.float32))
+            lp.per_expert_scale = synth.f32_to_bf16_bits(rng.uniform(0.5, 2.0, lp.dims.n_experts).astype(np.float32))
+            PP = DeviceLayer(lp, max_tokens=T, device=dev)
+            for _ in range(2):
+                B.moe_forward_prefill(PP.handle, xpd, T, yp)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(args.prefill_steps):
+                B.moe_forward_prefill(PP.handle, xpd, T, yp)
+            e1.record()
+            torch.cuda.synchronize()
+            ms_pro = e0.elapsed_time(e1) / args.prefill_steps
+            kid = B.kernel_id("router_prologue")
+            B.moe_profile_reset(PP.handle)
+            B.moe_profile_enable(PP.handle, True)
+            for _ in range(args.prefill_steps):
+                B.moe_forward_prefill(PP.handle, xpd, T, yp)
+            torch.cuda.synchronize()
+            ms_kp, n_kp = B.moe_profile_read(PP.handle, kid)
+            B.moe_profile_reset(PP.handle)
+            for _ in range(20):
+                B.moe_forward_decode(PP.handle, xpd[:1], 1, yp[:1])
+            torch.cuda.synchronize()
+            ms_kd, n_kd = B.moe_profile_read(PP.handle, kid)
+            B.moe_profile_enable(PP.handle, False)
+            us_p = 1000.0 * ms_kp / max(n_kp, 1)
+            pro_bytes = 3 * 2 * T * d   # x read, u and the fp16 copy of x written (router_scale stays cached)
+            result["next_rows"] = {"router_prologue": {
+                "workload": "4096-token prefill chunk and 1-token decode through the 2816-wide layer with the "
+                            "router prologue (rmsnorm without scale, router_scale / sqrt(d)) and per-expert scale",
+                "prefill_ms_per_step": round(ms_pro, 4), "prefill_ms_without": round(ms_pre, 4),
+                "prologue_us_prefill": round(us_p, 2), "prologue_bytes_prefill": pro_bytes,
+                "prologue_gbs_prefill": round(pro_bytes / (us_p * 1e-6) / 1e9, 1),
+                "prologue_us_decode": round(1000.0 * ms_kd / max(n_kd, 1), 2)}}
+            PP.close()
 
     # ------------------------------------------------------------------ 30-layer decode stack
     if not args.no_stack:

@@ -95,6 +95,17 @@ typedef struct {
     moe_qmat sh_gate, sh_up;  /* [I_s, d] 4-bit */
     moe_qmat sh_down;         /* [d, I_s] 4-bit */
     const float *logit_bias;  /* optional fp32 [E] added to every token's router logits (routing skew); may be NULL */
+    /*
+     * Optional router prologue and epilogue (Mference system design, "Decode", router listing);
+     * NULL leaves the router as above.
+     *   router_scale: bf16 [d], 16-byte aligned. The router reads
+     *       u = bf16(((x / sqrt(mean(x^2) + 1e-6)) * router_scale) / sqrt(d))
+     *     (float64, rounded once) instead of x; the experts still read x.
+     *   per_expert_scale: bf16 [E]. Each routing weight is multiplied by the scale of its expert
+     *     (the weights then no longer sum to 1).
+     */
+    const uint16_t *router_scale;
+    const uint16_t *per_expert_scale;
 } moe_weights;
 
 /*
@@ -111,12 +122,12 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
 void moe_layer_destroy(moe_layer *layer);
 
 /*
- * Router and grouping only (Mference, "Decode": the router listing, without the
- * norm prologue and per-expert scale; "Prefill": token/expert pairs grouped by
+ * Router and grouping only (Mference, "Decode": the router listing, with its prologue
+ * and per-expert scale when the layer has them; "Prefill": token/expert pairs grouped by
  * expert). For T tokens x (bf16 [T, d]):
  *   logits     fp32 [T, E]   optional (NULL to skip): router logits (+ logit_bias)
  *   topk_idx   int32 [T, k]  the k selected experts, largest logit first, ties to lower index
- *   topk_w     fp32 [T, k]   softmax of the selected logits
+ *   topk_w     fp32 [T, k]   softmax of the selected logits (times per_expert_scale if given)
  *   expert_offsets int32 [E+1] optional: offsets[e] = number of pairs routed to experts < e
  *   pair_perm  int32 [T*k]   optional: pair ids p = t*k + slot ordered by (expert, token)
  * expert_offsets and pair_perm must be both given or both NULL.

@@ -40,7 +40,7 @@ class moe_qmat(C.Structure):
 
 class moe_weights(C.Structure):
     _fields_ = [(n, moe_qmat) for n in ("router", "gate", "up", "down", "sh_gate", "sh_up", "sh_down")] + \
-               [("logit_bias", C.c_void_p)]
+               [("logit_bias", C.c_void_p), ("router_scale", C.c_void_p), ("per_expert_scale", C.c_void_p)]
 
 
 class moe_host_qmat(C.Structure):

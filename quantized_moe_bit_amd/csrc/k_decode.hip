@@ -335,6 +335,7 @@ struct DecArgs {
     const uint8_t *rq;
     const uint32_t *rsb;
     const float *logit_bias;
+    const uint16_t *pes;    // [E]              optional per-expert scale of the routing weights (bf16)
     float *logits;
     int32_t *idx;
     float *wts;
@@ -436,7 +437,7 @@ __global__ __launch_bounds__(64 * kBW) void k_dec_gateup(DecArgs a) {
         const int e = __builtin_amdgcn_readfirstlane(wave_topk<kPer>(a.logits + (size_t)t * a.E, a.E, a.k, slot, record, wsel));
         if (record && lane == 0) {
             a.idx[pr] = e;
-            a.wts[pr] = wsel;
+            a.wts[pr] = a.pes ? wsel * bf16_to_f32(a.pes[e]) : wsel;   // router epilogue
         }
         mg = &a.gate;
         mu = &a.up;
@@ -600,6 +601,7 @@ DecArgs dec_args(const moe_layer *L, const uint16_t *x, int T, float *y) {
     a.rq = static_cast<const uint8_t *>(L->w.router.codes);
     a.rsb = L->w.router.sb;
     a.logit_bias = L->w.logit_bias;
+    a.pes = L->w.per_expert_scale;
     a.logits = L->ws.logits;
     a.idx = L->ws.idx;
     a.wts = L->ws.wts;
@@ -641,10 +643,12 @@ size_t dec_workspace_floats(const moe_dims &D, int max_dec, int which) {
     }
 }
 
-hipError_t launch_dec_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s) {
+hipError_t launch_dec_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s,
+                             bool write_aux) {
     const moe_dims &D = L->dims;
     DecArgs a = dec_args(L, x, T, nullptr);
     a.logits = logits;
+    if (!write_aux) a.xg = nullptr;   // the group sums of x come from the router prologue
     const size_t lds = sizeof(float) * kRW * T * (D.d_model / 64);
     launch(k_dec_router<false>, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
     return hipGetLastError();

@@ -31,6 +31,68 @@ namespace {
 constexpr int kRNE = 4;                  // experts per wave of the prefill router
 constexpr int kRBlk = 64 * kRNE;   // router table floats per (expert block, group)
 
+// Router prologue (Mference system design, "Decode", router listing): the router reads
+//   u = bf16(((x / sqrt(mean(x^2) + 1e-6)) * router_scale) / sqrt(d))
+// computed in float64 in that order and rounded once, the same expression the oracle writes
+// out (its sum of squares runs in another order; the bf16 rounding absorbs the difference).
+// Also writes the fp16 copy of x (x16, prefill) or the fixed-order group sums of x (xg,
+// decode), which the router would otherwise derive from its own input.
+// grid: T; block 256 (d <= 8192: at most four 16-byte chunks per thread)
+constexpr int kProChunks = 4;
+__global__ __launch_bounds__(256) void k_router_prologue(const uint16_t *__restrict__ x, int d,
+                                                         const uint16_t *__restrict__ rs, uint16_t *__restrict__ u,
+                                                         uint16_t *__restrict__ x16, float *__restrict__ xg) {
+    __shared__ double red[4];
+    const int t = blockIdx.x, tid = threadIdx.x, nc = d / 8;
+    const uint16_t *xt = x + (size_t)t * d;
+    u32x4_t xv[kProChunks], rv[kProChunks];
+    double ss = 0.0;
+#pragma unroll
+    for (int c = 0; c < kProChunks; ++c) {
+        const int i = tid + 256 * c;
+        if (i < nc) {
+            xv[c] = ld16(xt + 8 * i);
+            rv[c] = ld16(rs + 8 * i);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const double v = bf16_to_f64((xv[c][j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+                ss = fma(v, v, ss);
+            }
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    const double tot = (red[0] + red[1]) + (red[2] + red[3]);
+    const double inv = 1.0 / sqrt(tot / (double)d + 1e-6), sd = sqrt((double)d);
+#pragma unroll
+    for (int c = 0; c < kProChunks; ++c) {
+        const int i = tid + 256 * c;
+        if (i < nc) {
+            u32x4_t uo, ho;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                uint32_t ub[2], hb[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t xb = (xv[c][w] >> (16 * h)) & 0xFFFFu, rb = (rv[c][w] >> (16 * h)) & 0xFFFFu;
+                    ub[h] = f64_to_bf16(((bf16_to_f64(xb) * inv) * bf16_to_f64(rb)) / sd);
+                    hb[h] = f32_to_f16_sat(bf16_to_f32(xb));
+                }
+                uo[w] = ub[0] | (ub[1] << 16);
+                ho[w] = hb[0] | (hb[1] << 16);
+            }
+            *reinterpret_cast<u32x4_t *>(u + (size_t)t * d + 8 * i) = uo;
+            if (x16) *reinterpret_cast<u32x4_t *>(x16 + (size_t)t * d + 8 * i) = ho;
+        }
+    }
+    if (xg && tid < d / 64) {   // X_g = ((0 + x_0) + x_1) + ... + x_63, fp32
+        float X = 0.0f;
+        for (int j = 0; j < 64; ++j) X = X + bf16_to_f32(xt[64 * tid + j]);
+        xg[(size_t)t * (d / 64) + tid] = X;
+    }
+}
+
 // Prefill router: lane = token, wave = kRNE = 4 consecutive experts, workgroup = 4 waves (64
 // tokens x 16 experts). Per 64-input group the workgroup stages its tokens' inputs into LDS as
 // fp32, converted once for all waves and double-buffered (the next group's loads are in
@@ -75,9 +137,9 @@ __global__ __launch_bounds__(256) void k_router_tok(const uint16_t *__restrict__
     // staging: thread -> token tid/4, inputs 16 (tid%4) .. +15 of the group
     const int st = tid >> 2, sq = tid & 3;
     const int stok = min((int)blockIdx.x * 64 + st, T - 1);
-    const bool st_x16 = blockIdx.y == 0 && (int)blockIdx.x * 64 + st < T;   // this thread stores x16
+    const bool st_x16 = x16 && blockIdx.y == 0 && (int)blockIdx.x * 64 + st < T;   // this thread stores x16
     const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(x + (size_t)stok * d + 16 * sq);
-    u32x4_t *xo = reinterpret_cast<u32x4_t *>(x16 + (size_t)stok * d + 16 * sq);
+    u32x4_t *xo = reinterpret_cast<u32x4_t *>(x16 ? x16 + (size_t)stok * d + 16 * sq : nullptr);
     const float *blk = tab + (size_t)eb * G * kRBlk;
     auto stage = [&](int buf, int g, const u32x4_t (&v)[2]) {
         if (st_x16) {
@@ -179,7 +241,8 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
 // grid: ceil(T / 4); block 256 -- one wave per token; kPer logits per lane (E <= 64 kPer)
 template <int kPer>
 __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, int T, int E, int k,
-                                              int32_t *__restrict__ idx, float *__restrict__ wout) {
+                                              const uint16_t *__restrict__ pes, int32_t *__restrict__ idx,
+                                              float *__restrict__ wout) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
@@ -224,8 +287,10 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
         }
     }
     if (lane < k) {
-        idx[(size_t)t * k + lane] = min(max(my_i, 0), E - 1);
-        wout[(size_t)t * k + lane] = __expf(my_v - m) / z;
+        const int e = min(max(my_i, 0), E - 1);
+        idx[(size_t)t * k + lane] = e;
+        const float w = __expf(my_v - m) / z;
+        wout[(size_t)t * k + lane] = pes ? w * bf16_to_f32(pes[e]) : w;   // router epilogue
     }
 }
 
@@ -397,10 +462,11 @@ __global__ __launch_bounds__(256) void k_bucket_scatter(const int32_t *__restric
 
 }  // namespace
 
-hipError_t launch_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s) {
+hipError_t launch_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s,
+                         bool write_aux) {
     const int d = L->dims.d_model, E = L->dims.n_experts;
     launch(k_router_tok, dim3(cdiv(T, 64), cdiv(E, 4 * kRNE)), dim3(256), 0, s, x, T, d, E, L->ws.rqf,
-           L->w.logit_bias, logits, L->ws.x16);
+           L->w.logit_bias, logits, write_aux ? L->ws.x16 : nullptr);
     return hipGetLastError();
 }
 
@@ -416,9 +482,10 @@ hipError_t launch_router_table(const moe_layer *L, hipStream_t s) {
 
 hipError_t launch_topk(const moe_layer *L, int T, const float *logits, int32_t *idx, float *w, hipStream_t s) {
     const int E = L->dims.n_experts, k = L->dims.top_k;
-    if (E <= 128) launch(k_topk<2>, dim3(cdiv(T, 4)), dim3(256), 0, s, logits, T, E, k, idx, w);
-    else if (E <= 256) launch(k_topk<4>, dim3(cdiv(T, 4)), dim3(256), 0, s, logits, T, E, k, idx, w);
-    else launch(k_topk<MOE_MAX_EXPERTS / 64>, dim3(cdiv(T, 4)), dim3(256), 0, s, logits, T, E, k, idx, w);
+    const uint16_t *pes = L->w.per_expert_scale;
+    if (E <= 128) launch(k_topk<2>, dim3(cdiv(T, 4)), dim3(256), 0, s, logits, T, E, k, pes, idx, w);
+    else if (E <= 256) launch(k_topk<4>, dim3(cdiv(T, 4)), dim3(256), 0, s, logits, T, E, k, pes, idx, w);
+    else launch(k_topk<MOE_MAX_EXPERTS / 64>, dim3(cdiv(T, 4)), dim3(256), 0, s, logits, T, E, k, pes, idx, w);
     return hipGetLastError();
 }
 
@@ -440,6 +507,12 @@ hipError_t launch_bucket_scatter(const moe_layer *L, int T, const int32_t *idx, 
     const int P = T * L->dims.top_k;
     launch(k_bucket_scatter, dim3(cdiv(P, kChunk)), dim3(kChunk), 0, s, idx, P, L->dims.n_experts,
                        L->ws.rank, L->ws.chunk_base, L->ws.offsets, L->ws.perm, L->ws.pos, perm_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_prologue(const moe_layer *L, const uint16_t *x, int T, bool for_prefill, hipStream_t s) {
+    launch(k_router_prologue, dim3(T), dim3(256), 0, s, x, L->dims.d_model, L->w.router_scale, L->ws.u,
+           for_prefill ? L->ws.x16 : nullptr, for_prefill ? nullptr : L->ws.dxg);
     return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@ namespace {
 
 const char *kKernelNames[K_COUNT] = {"router",     "topk",       "bucket_rank", "bucket_scan", "bucket_scatter",
                                      "dec_router", "dec_gateup", "dec_down", "pre_gateup",  "pre_down",
-                                     "combine",    "glue"};
+                                     "combine",    "glue",       "router_prologue"};
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -81,6 +81,7 @@ moe_status check_weights(const moe_weights *w) {
     if ((s = check_qmat(w->sh_up, "sh_up")) != MOE_OK) return s;
     if ((s = check_qmat(w->sh_down, "sh_down")) != MOE_OK) return s;
     if (w->logit_bias && !aligned16(w->logit_bias)) return fail(MOE_E_ALIGN, "logit_bias not 16-byte aligned");
+    if (w->router_scale && !aligned16(w->router_scale)) return fail(MOE_E_ALIGN, "router_scale not 16-byte aligned");
     return MOE_OK;
 }
 
@@ -159,10 +160,24 @@ moe_status run(moe_layer *L, int id, hipStream_t s, F &&f) {
         if (_st != MOE_OK) return _st;                             \
     } while (0)
 
+// The router's input: x itself, or the router prologue's output (which also writes what the
+// router would have derived from x: the fp16 copy for prefill, the group sums for decode).
+moe_status router_input(moe_layer *L, const uint16_t *x, int T, bool for_prefill, hipStream_t s, const uint16_t **u) {
+    *u = x;
+    if (!L->w.router_scale) return MOE_OK;
+    RUN(K_ROUTER_PROLOGUE, launch_router_prologue(L, x, T, for_prefill, s));
+    *u = L->ws.u;
+    return MOE_OK;
+}
+
 moe_status route_impl(moe_layer *L, const uint16_t *x, int T, hipStream_t s, float *logits, int32_t *idx,
                       float *w, bool bucket, int32_t *perm_out, bool prefill) {
-    if (!prefill && T <= L->max_dec) RUN(K_ROUTER, launch_dec_router(L, x, T, logits, s));
-    else RUN(K_ROUTER, launch_router(L, x, T, logits, s));
+    const bool dec = !prefill && T <= L->max_dec;
+    const uint16_t *u = x;
+    moe_status st = router_input(L, x, T, !dec, s, &u);
+    if (st != MOE_OK) return st;
+    if (dec) RUN(K_ROUTER, launch_dec_router(L, u, T, logits, s, u == x));
+    else RUN(K_ROUTER, launch_router(L, u, T, logits, s, u == x));
     RUN(K_TOPK, launch_topk(L, T, logits, idx, w, s));
     if (bucket) {
         RUN(K_BUCKET_RANK, launch_bucket_rank(L, T, idx, s));
@@ -229,6 +244,7 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.idx, P);
     plan.take(&ws.wts, P);
     plan.take(&ws.x16, Tm * d);
+    plan.take(&ws.u, w->router_scale ? Tm * d : 0);
     plan.take(&ws.counts, E);
     plan.take(&ws.offsets, E + 1);
     plan.take(&ws.tile_off, E + 1);
@@ -268,6 +284,7 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     rebase(ws.idx, base);
     rebase(ws.wts, base);
     rebase(ws.x16, base);
+    rebase(ws.u, base);
     rebase(ws.counts, base);
     rebase(ws.offsets, base);
     rebase(ws.tile_off, base);
@@ -353,7 +370,9 @@ moe_status moe_forward_decode(moe_layer *L, const uint16_t *x, int32_t T, float 
     if (T > L->max_dec)
         return fail(MOE_E_CAPACITY, "moe_forward_decode: T = %d exceeds the decode capacity %d", T, L->max_dec);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    RUN(K_DEC_ROUTER, launch_dec_router(L, x, T, L->ws.logits, s));
+    const uint16_t *u = x;
+    if ((st = router_input(L, x, T, false, s, &u)) != MOE_OK) return st;
+    RUN(K_DEC_ROUTER, launch_dec_router(L, u, T, L->ws.logits, s, u == x));
     RUN(K_DEC_GATEUP, launch_dec_gateup(L, x, T, s));
     RUN(K_DEC_DOWN, launch_dec_down(L, T, y, s));
     return MOE_OK;
@@ -414,11 +433,14 @@ moe_status moe_stack_forward_decode(moe_layer *const *layers, int32_t n_layers, 
         moe_layer *L = layers[l];
         uint16_t *src = (l & 1) ? h_buf : h, *dst = (l & 1) ? h : h_buf;
         const float *yp = l ? y_buf : nullptr;
-        if (dec_router_glue_fits(L->dims, T)) {
+        if (dec_router_glue_fits(L->dims, T) && !L->w.router_scale) {
             RUN(K_DEC_ROUTER, launch_dec_router_glue(L, src, yp, dst, x_buf, T, s));
         } else {
             RUN(K_GLUE, launch_glue(src, yp, dst, x_buf, T, d, s));
-            RUN(K_DEC_ROUTER, launch_dec_router(L, x_buf, T, L->ws.logits, s));
+            const uint16_t *u = x_buf;
+            moe_status st = router_input(L, x_buf, T, false, s, &u);
+            if (st != MOE_OK) return st;
+            RUN(K_DEC_ROUTER, launch_dec_router(L, u, T, L->ws.logits, s, u == x_buf));
         }
         RUN(K_DEC_GATEUP, launch_dec_gateup(L, x_buf, T, s));
         RUN(K_DEC_DOWN, launch_dec_down(L, T, y_buf, s));

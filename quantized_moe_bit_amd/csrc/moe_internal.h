@@ -48,6 +48,7 @@ enum KernelId {
     K_PRE_DOWN,
     K_COMBINE,
     K_GLUE,
+    K_ROUTER_PROLOGUE,
     K_COUNT
 };
 
@@ -57,6 +58,7 @@ struct Workspace {
     int32_t *idx;         // [maxT, k]
     float *wts;           // [maxT, k]
     uint16_t *x16;        // [maxT, d]          fp16 copy of x (prefill gate/up operand, written by the router)
+    uint16_t *u;          // [maxT, d]          router input after the router prologue (bf16), if the layer has one
     int32_t *counts;      // [E]
     int32_t *offsets;     // [E+1]
     int32_t *tile_off;    // [E+1]              prefix sum of ceil(count/kMT)
@@ -127,8 +129,15 @@ inline void launch(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, A
 }
 
 // Kernel launchers (each enqueues on stream, returns hipGetLastError()).
-hipError_t launch_dec_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s);
-hipError_t launch_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s);
+hipError_t launch_dec_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s,
+                             bool write_aux = true);
+// write_aux: the prefill router also writes the fp16 copy of x from its input, the decode router
+// the group sums of x; both are off when the router reads the prologue's output instead of x.
+hipError_t launch_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s,
+                         bool write_aux = true);
+// Router prologue: u = bf16(((x / rms(x)) * router_scale) / sqrt(d)) into ws.u, plus the fp16
+// copy of x (for_prefill) or the decode group sums of x (otherwise).
+hipError_t launch_router_prologue(const moe_layer *L, const uint16_t *x, int T, bool for_prefill, hipStream_t s);
 bool dec_router_glue_fits(const moe_dims &D, int T);
 hipError_t launch_dec_router_glue(const moe_layer *L, const uint16_t *h_in, const float *y_in, uint16_t *h_out,
                                   uint16_t *x_out, int T, hipStream_t s);

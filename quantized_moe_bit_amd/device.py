@@ -39,11 +39,13 @@ class DeviceLayer:
             tc, ts = _dev(c, self.device), _dev(s.view(np.int32), self.device)
             self._keep[name] = (tc, ts)
             q[name] = B.moe_qmat(tc.data_ptr(), ts.data_ptr())
-        lb = None
-        if layer.logit_bias is not None:
-            lb = _dev(layer.logit_bias.astype(np.float32), self.device)
-            self._keep["logit_bias"] = lb
-        w = B.moe_weights(**q, logit_bias=None if lb is None else lb.data_ptr())
+        vecs = {"logit_bias": None if layer.logit_bias is None else layer.logit_bias.astype(np.float32),
+                "router_scale": None if layer.router_scale is None else layer.router_scale.view(np.int16),
+                "per_expert_scale": None if layer.per_expert_scale is None else layer.per_expert_scale.view(np.int16)}
+        for name, v in vecs.items():
+            if v is not None:
+                self._keep[name] = _dev(v, self.device)
+        w = self._weights(q)
         self.dims = B.moe_dims(D.d_model, D.n_experts, D.top_k, D.d_expert, D.d_shared, D.group, D.router_bits,
                                D.expert_bits, max_tokens)
         self.max_tokens = max_tokens
@@ -58,17 +60,22 @@ class DeviceLayer:
         other._keep = {}
         q = {}
         for name, v in self._keep.items():
-            if name == "logit_bias":
+            if name in self._VECS:
                 other._keep[name] = v.clone()
             else:
                 tc, ts = v[0].clone(), v[1].clone()
                 other._keep[name] = (tc, ts)
                 q[name] = B.moe_qmat(tc.data_ptr(), ts.data_ptr())
-        lb = other._keep.get("logit_bias")
-        w = B.moe_weights(**q, logit_bias=None if lb is None else lb.data_ptr())
+        w = other._weights(q)
         other.dims = B.moe_dims(*[getattr(self.dims, f) for f, _ in B.moe_dims._fields_])
         other.handle = B.moe_layer_create(other.dims, w, 0)
         return other
+
+    _VECS = ("logit_bias", "router_scale", "per_expert_scale")
+
+    def _weights(self, q) -> "B.moe_weights":
+        vec = {n: (self._keep[n].data_ptr() if n in self._keep else None) for n in self._VECS}
+        return B.moe_weights(**q, **vec)
 
     def weight_bytes(self) -> int:
         tot = 0

@@ -185,4 +185,45 @@ __device__ __forceinline__ void glue_token(const uint16_t *h, const float *y, ui
     }
 }
 
+// Router prologue of one token held in LDS (bf16 [d], d a multiple of 8), in place, by one
+// full workgroup of kGlueWG threads: x -> bf16(((x / sqrt(mean(x^2) + 1e-6)) * rs) / sqrt(d)),
+// float64 in that order and rounded once (Mference system design, "Decode", router listing).
+// rs: bf16 [d] in global memory, 16-byte aligned. red: kGlueWG / 64 doubles of LDS.
+__device__ __forceinline__ void prologue_token(uint16_t *xs, const uint16_t *rs, int d, double *red) {
+    const int tid = threadIdx.x;
+    const int nc = d / 8;
+    double ss = 0.0;
+    for (int i = tid; i < nc; i += kGlueWG) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(xs + 8 * i);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const double f = bf16_to_f64((v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+            ss = fma(f, f, ss);
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    double tot = 0.0;
+#pragma unroll
+    for (int w = 0; w < kGlueWG / 64; ++w) tot += red[w];
+    __syncthreads();   // red may be reused by the caller
+    const double inv = 1.0 / sqrt(tot / (double)d + 1e-6), sd = sqrt((double)d);
+    for (int i = tid; i < nc; i += kGlueWG) {   // each thread rewrites the chunks it alone reads
+        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(xs + 8 * i);
+        const u32x4_t r = *reinterpret_cast<const u32x4_t *>(rs + 8 * i);
+        u32x4_t o;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            uint32_t ub[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                ub[h] = f64_to_bf16(((bf16_to_f64((v[w] >> (16 * h)) & 0xFFFFu) * inv) *
+                                     bf16_to_f64((r[w] >> (16 * h)) & 0xFFFFu)) / sd);
+            o[w] = ub[0] | (ub[1] << 16);
+        }
+        *reinterpret_cast<u32x4_t *>(xs + 8 * i) = o;
+    }
+}
+
 }  // namespace qmoe

@@ -352,14 +352,18 @@ struct DecArgs {
     const uint16_t *h_in;
     const float *y_in;
     uint16_t *h_out, *x_out;
+    // router prologue fused into the router launch: router_scale (bf16 [d])
+    const uint16_t *router_scale;
 };
 
 // ----------------------------------------------------------------------------- launch A
-// grid: ceil(E / kRW); block 64 * kRW; LDS kRW * T * (d/64) floats, plus (GLUE) T * d bf16
-// and 4 doubles. With GLUE every workgroup first forms x = norm(bf16(h_in + y_in)) for its
+// grid: ceil(E / kRW); block 64 * kRW; LDS kRW * T * (d/64) floats, plus (GLUE or PRO) T * d
+// bf16 and 4 doubles. With GLUE every workgroup first forms x = norm(bf16(h_in + y_in)) for its
 // own use (the same fp64 residual step as the stack glue kernel; workgroup 0 also stores h_out
-// and x_out for the later launches), so the stack needs no separate residual launch.
-template <bool GLUE>
+// and x_out for the later launches), so the stack needs no separate residual launch. With PRO
+// every workgroup applies the router prologue to its copy of x (workgroup 0 first stores the
+// group sums of x itself for the gate/up launch), so the router reads the prologue's output.
+template <bool GLUE, bool PRO>
 __global__ __launch_bounds__(64 * kRW) void k_dec_router(DecArgs a) {
     static_assert(64 * kRW == kGlueWG, "the residual step runs on one full workgroup");
     extern __shared__ __align__(16) unsigned char smem[];
@@ -370,22 +374,43 @@ __global__ __launch_bounds__(64 * kRW) void k_dec_router(DecArgs a) {
     const int e = blockIdx.x * kRW + wave;
     // with the residual step in front, the codes of the wave's first group are requested
     // before it, so their latency overlaps the step's own loads
+    constexpr bool LDSX = GLUE || PRO;   // x (then u) kept in LDS
     RouterCodes pre;
-    if (GLUE && e < a.E) pre = router_codes(a.rq, a.rsb, a.d, e, min(lane, G - 1));
-    if (GLUE) {
+    if (LDSX && e < a.E) pre = router_codes(a.rq, a.rsb, a.d, e, min(lane, G - 1));
+    if (LDSX) {
         uint16_t *xs = reinterpret_cast<uint16_t *>(smem + sizeof(float) * kRW * a.T * G);
         double *red = reinterpret_cast<double *>(xs + (size_t)a.T * a.d);
-        for (int t = 0; t < a.T; ++t)
-            glue_token(a.h_in + (size_t)t * a.d, a.y_in ? a.y_in + (size_t)t * a.d : nullptr,
-                       blockIdx.x == 0 ? a.h_out + (size_t)t * a.d : nullptr, xs + (size_t)t * a.d, a.d, red);
-        __syncthreads();
-        if (blockIdx.x == 0)
+        if (GLUE) {
+            for (int t = 0; t < a.T; ++t)
+                glue_token(a.h_in + (size_t)t * a.d, a.y_in ? a.y_in + (size_t)t * a.d : nullptr,
+                           blockIdx.x == 0 ? a.h_out + (size_t)t * a.d : nullptr, xs + (size_t)t * a.d, a.d, red);
+            __syncthreads();
+            if (blockIdx.x == 0)
+                for (int i = tid; i < a.T * a.d / 8; i += 64 * kRW)
+                    *reinterpret_cast<u32x4_t *>(a.x_out + 8 * i) = *reinterpret_cast<const u32x4_t *>(xs + 8 * i);
+        } else {
             for (int i = tid; i < a.T * a.d / 8; i += 64 * kRW)
-                *reinterpret_cast<u32x4_t *>(a.x_out + 8 * i) = *reinterpret_cast<const u32x4_t *>(xs + 8 * i);
+                *reinterpret_cast<u32x4_t *>(xs + 8 * i) = ld16(a.x + 8 * i);
+        }
+        if (PRO) {
+            __syncthreads();
+            if (blockIdx.x == 0 && tid < G) {   // X_g = ((0 + x_0) + x_1) + ... + x_63, fp32
+#pragma clang fp contract(off)
+                for (int t = 0; t < a.T; ++t) {
+                    float X = 0.0f;
+                    for (int j = 0; j < 64; ++j) X = X + bf16_to_f32(xs[(size_t)t * a.d + 64 * tid + j]);
+                    a.xg[(size_t)t * G + tid] = X;
+                }
+            }
+            __syncthreads();   // x_out and the group sums are read from xs before it is rewritten
+            for (int t = 0; t < a.T; ++t) prologue_token(xs + (size_t)t * a.d, a.router_scale, a.d, red);
+        }
+        __syncthreads();
         x = xs;
     }
     float *P = Ps + (size_t)wave * a.T * G;
-    if (e < a.E) router_wave(x, a.T, a.d, e, a.rq, a.rsb, P, e == 0 ? a.xg : nullptr, GLUE ? &pre : nullptr);
+    if (e < a.E)
+        router_wave(x, a.T, a.d, e, a.rq, a.rsb, P, (!PRO && e == 0) ? a.xg : nullptr, LDSX ? &pre : nullptr);
     __syncthreads();
     if (e < a.E && lane < a.T) {
 #pragma clang fp contract(off)
@@ -650,7 +675,18 @@ hipError_t launch_dec_router(const moe_layer *L, const uint16_t *x, int T, float
     a.logits = logits;
     if (!write_aux) a.xg = nullptr;   // the group sums of x come from the router prologue
     const size_t lds = sizeof(float) * kRW * T * (D.d_model / 64);
-    launch(k_dec_router<false>, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
+    launch(k_dec_router<false, false>, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dec_router_pro(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s) {
+    const moe_dims &D = L->dims;
+    DecArgs a = dec_args(L, x, T, nullptr);
+    a.logits = logits;
+    a.router_scale = L->w.router_scale;
+    const size_t lds = sizeof(float) * kRW * T * (D.d_model / 64) + sizeof(uint16_t) * T * D.d_model +
+                       sizeof(double) * (kGlueWG / 64);
+    launch(k_dec_router<false, true>, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
     return hipGetLastError();
 }
 
@@ -666,7 +702,11 @@ hipError_t launch_dec_router_glue(const moe_layer *L, const uint16_t *h_in, cons
     a.x_out = x_out;
     const size_t lds = sizeof(float) * kRW * T * (D.d_model / 64) + sizeof(uint16_t) * T * D.d_model +
                        sizeof(double) * (kGlueWG / 64);
-    launch(k_dec_router<true>, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
+    a.router_scale = L->w.router_scale;
+    if (a.router_scale)
+        launch(k_dec_router<true, true>, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
+    else
+        launch(k_dec_router<true, false>, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
     return hipGetLastError();
 }
 

@@ -173,11 +173,15 @@ moe_status router_input(moe_layer *L, const uint16_t *x, int T, bool for_prefill
 moe_status route_impl(moe_layer *L, const uint16_t *x, int T, hipStream_t s, float *logits, int32_t *idx,
                       float *w, bool bucket, int32_t *perm_out, bool prefill) {
     const bool dec = !prefill && T <= L->max_dec;
-    const uint16_t *u = x;
-    moe_status st = router_input(L, x, T, !dec, s, &u);
-    if (st != MOE_OK) return st;
-    if (dec) RUN(K_ROUTER, launch_dec_router(L, u, T, logits, s, u == x));
-    else RUN(K_ROUTER, launch_router(L, u, T, logits, s, u == x));
+    if (dec && L->w.router_scale && dec_router_glue_fits(L->dims, T)) {
+        RUN(K_ROUTER, launch_dec_router_pro(L, x, T, logits, s));
+    } else {
+        const uint16_t *u = x;
+        moe_status st = router_input(L, x, T, !dec, s, &u);
+        if (st != MOE_OK) return st;
+        if (dec) RUN(K_ROUTER, launch_dec_router(L, u, T, logits, s, u == x));
+        else RUN(K_ROUTER, launch_router(L, u, T, logits, s, u == x));
+    }
     RUN(K_TOPK, launch_topk(L, T, logits, idx, w, s));
     if (bucket) {
         RUN(K_BUCKET_RANK, launch_bucket_rank(L, T, idx, s));
@@ -370,9 +374,13 @@ moe_status moe_forward_decode(moe_layer *L, const uint16_t *x, int32_t T, float 
     if (T > L->max_dec)
         return fail(MOE_E_CAPACITY, "moe_forward_decode: T = %d exceeds the decode capacity %d", T, L->max_dec);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    const uint16_t *u = x;
-    if ((st = router_input(L, x, T, false, s, &u)) != MOE_OK) return st;
-    RUN(K_DEC_ROUTER, launch_dec_router(L, u, T, L->ws.logits, s, u == x));
+    if (L->w.router_scale && dec_router_glue_fits(L->dims, T)) {
+        RUN(K_DEC_ROUTER, launch_dec_router_pro(L, x, T, L->ws.logits, s));
+    } else {
+        const uint16_t *u = x;
+        if ((st = router_input(L, x, T, false, s, &u)) != MOE_OK) return st;
+        RUN(K_DEC_ROUTER, launch_dec_router(L, u, T, L->ws.logits, s, u == x));
+    }
     RUN(K_DEC_GATEUP, launch_dec_gateup(L, x, T, s));
     RUN(K_DEC_DOWN, launch_dec_down(L, T, y, s));
     return MOE_OK;
@@ -433,7 +441,7 @@ moe_status moe_stack_forward_decode(moe_layer *const *layers, int32_t n_layers, 
         moe_layer *L = layers[l];
         uint16_t *src = (l & 1) ? h_buf : h, *dst = (l & 1) ? h : h_buf;
         const float *yp = l ? y_buf : nullptr;
-        if (dec_router_glue_fits(L->dims, T) && !L->w.router_scale) {
+        if (dec_router_glue_fits(L->dims, T)) {
             RUN(K_DEC_ROUTER, launch_dec_router_glue(L, src, yp, dst, x_buf, T, s));
         } else {
             RUN(K_GLUE, launch_glue(src, yp, dst, x_buf, T, d, s));

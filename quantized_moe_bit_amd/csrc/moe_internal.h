@@ -139,6 +139,9 @@ hipError_t launch_router(const moe_layer *L, const uint16_t *x, int T, float *lo
 // copy of x (for_prefill) or the decode group sums of x (otherwise).
 hipError_t launch_router_prologue(const moe_layer *L, const uint16_t *x, int T, bool for_prefill, hipStream_t s);
 bool dec_router_glue_fits(const moe_dims &D, int T);
+// decode router with the router prologue fused (every workgroup forms the router input in LDS;
+// needs dec_router_glue_fits); writes the group sums of x itself
+hipError_t launch_dec_router_pro(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s);
 hipError_t launch_dec_router_glue(const moe_layer *L, const uint16_t *h_in, const float *y_in, uint16_t *h_out,
                                   uint16_t *x_out, int T, hipStream_t s);
 hipError_t launch_router_table(const moe_layer *L, hipStream_t s);

@@ -77,6 +77,12 @@ def test_layer_with_router_prologue(name):
     y = dl.decode(xd[:3])
     torch.cuda.synchronize()
     check_close(y.cpu().numpy(), y_ref[:3], f"{name} decode T=3")
+    # 16 tokens: the decode router input no longer fits the router launch's LDS, so the
+    # prologue runs as a launch of its own
+    check_route(dl, lay, x[:16], f"{name} route T=16")
+    y = dl.decode(xd[:16])
+    torch.cuda.synchronize()
+    check_close(y.cpu().numpy(), y_ref[:16], f"{name} decode T=16")
     dl.close()
 
 

@@ -61,7 +61,7 @@ def lib():
         L.orc_ffn.argtypes = [i32, i32, vp, C.POINTER(_QMat), C.POINTER(_QMat), C.POINTER(_QMat), vp]
         L.orc_layer_tokens.argtypes = [i32, i32, i32, i32, i32, vp, i32, vp, vp, vp] + \
             [C.POINTER(_QMat)] * 6 + [vp, vp, vp]
-        L.orc_stack_glue.argtypes = [i32, i32, vp, vp, C.c_double, vp, vp]
+        L.orc_stack_glue.argtypes = [i32, i32, vp, vp, vp, C.c_double, C.c_double, vp, vp]
         _lib = L
     return _lib
 
@@ -204,12 +204,14 @@ def layer_forward(layer, x, tokens: Optional[Sequence[int]] = None):
     return y, r
 
 
-def stack_glue(h, y, eps: float = STACK_EPS):
-    """-> (h_next, x_next) bf16 bits [T,d]; y float64 [T,d] or None (first layer's norm only)."""
+def stack_glue(h, y, eps: float = STACK_EPS, post=None, scalar: float = 1.0):
+    """-> (h_next, x_next) bf16 bits [T,d]; y float64 [T,d] or None (first layer's norm only);
+    post: optional bf16 bits [d] (post-FFN norm weight), scalar: layer scalar (with y)."""
     h = _c(h, np.uint16)
     T, d = h.shape
     yy = None if y is None else _c(y, np.float64)
+    pp = None if post is None else _c(post, np.uint16)
     hn = np.empty_like(h)
     xn = np.empty_like(h)
-    lib().orc_stack_glue(T, d, _p(h), _p(yy), float(eps), _p(hn), _p(xn))
+    lib().orc_stack_glue(T, d, _p(h), _p(yy), _p(pp), float(scalar), float(eps), _p(hn), _p(xn))
     return hn, xn

@@ -325,20 +325,35 @@ void orc_router_prologue(int T, int d, const uint16_t *x, const uint16_t *router
 
 /* ------------------------------------------------------------------ layer stack glue */
 /*
- * Residual stream between layers of the decode stack:
- *   h_next = bf16(h + y)
- *   x_next = bf16(h_next / sqrt(mean(h_next^2) + eps))      (norm without a learned scale)
- * h, h_next, x_next: bf16 bits [T, d]; y: float64 [T, d].
+ * Residual stream between layers of the decode stack, with the layer tail (Mference system
+ * design, "Decode", cb2: post-FFN norm, residual, layer scalar):
+ *   z      = y / sqrt(mean(y^2) + eps) * post          (only when post is given; else z = y)
+ *   h_next = bf16((h + z) * scalar)
+ *   x_next = bf16(h_next / sqrt(mean(h_next^2) + eps))  (norm without a learned scale)
+ * float64 throughout, sums of squares ascending. h, h_next, x_next: bf16 bits [T, d];
+ * y: float64 [T, d] (NULL: no layer output yet, h_next = h); post: bf16 bits [d] or NULL.
  */
-void orc_stack_glue(int T, int d, const uint16_t *h, const double *y, double eps,
-                    uint16_t *h_next, uint16_t *x_next) {
+void orc_stack_glue(int T, int d, const uint16_t *h, const double *y, const uint16_t *post, double scalar,
+                    double eps, uint16_t *h_next, uint16_t *x_next) {
     for (int t = 0; t < T; ++t) {
+        const double *yt = y ? y + (size_t)t * d : NULL;
+        double inv_y = 1.0;
+        if (yt && post) {
+            double sy = 0.0;
+            for (int i = 0; i < d; ++i) sy += yt[i] * yt[i];
+            inv_y = 1.0 / sqrt(sy / d + eps);
+        }
         double ss = 0.0;
         for (int i = 0; i < d; ++i) {
             size_t o = (size_t)t * d + i;
-            h_next[o] = orc_f64_to_bf16(bf16_f64(h[o]) + (y ? y[o] : 0.0));
-            double v = bf16_f64(h_next[o]);
-            ss += v * v;
+            double v = bf16_f64(h[o]);
+            if (yt) {
+                const double z = post ? (yt[i] * inv_y) * bf16_f64(post[i]) : yt[i];
+                v = (v + z) * scalar;
+            }
+            h_next[o] = orc_f64_to_bf16(v);
+            const double r = bf16_f64(h_next[o]);
+            ss += r * r;
         }
         double inv = 1.0 / sqrt(ss / d + eps);
         for (int i = 0; i < d; ++i) {

@@ -391,3 +391,33 @@ def test_stack_glue_closed_forms():
             assert float(brute.bf16_value(hn[t, i])) == brute.rne_bf16_exact(float(ref_h[t, i]))
     xv = brute.bf16_value(xn)
     np.testing.assert_allclose(np.sqrt(np.mean(xv ** 2, axis=1)), 1.0, rtol=4e-3)
+
+
+def test_stack_glue_layer_tail():
+    # post-FFN norm, residual add and layer scalar (Mference "Decode", cb2)
+    d = 128
+    rng = np.random.default_rng(72)
+    post = synth.f32_to_bf16_bits(rng.uniform(0.5, 2.0, d).astype(np.float32))
+    zero = np.zeros((1, d), np.uint16)
+    # a constant layer output normalizes to 1: h_next = post (h = 0, scalar 1)
+    hn, _ = oracle.stack_glue(zero, np.full((1, d), -7.0), post=post)
+    np.testing.assert_array_equal(brute.bf16_value(hn)[0], -brute.bf16_value(post))
+    # the scalar multiplies the whole stream after the add: 2 doubles it exactly
+    h = synth.f32_to_bf16_bits(rng.standard_normal((3, d)).astype(np.float32) * 4)
+    y = rng.standard_normal((3, d)) * 3
+    h1, _ = oracle.stack_glue(h, y, post=post, scalar=1.0)
+    h2, _ = oracle.stack_glue(h, y, post=post, scalar=2.0)
+    np.testing.assert_array_equal(brute.bf16_value(h2), 2.0 * brute.bf16_value(h1))
+    # against an independent float64 computation rounded exactly
+    s = 0.75
+    hn, xn = oracle.stack_glue(h, y, post=post, scalar=s)
+    z = y / np.sqrt(np.mean(y * y, axis=1, keepdims=True) + 1e-6) * brute.bf16_value(post)[None, :]
+    ref = (brute.bf16_value(h) + z) * s
+    for t in range(3):
+        for i in range(0, d, 7):
+            assert float(brute.bf16_value(hn[t, i])) == brute.rne_bf16_exact(float(ref[t, i]))
+    # no post weight and scalar 1: the plain residual step
+    hp, xp = oracle.stack_glue(h, y)
+    hq, xq = oracle.stack_glue(h, y, post=None, scalar=1.0)
+    np.testing.assert_array_equal(hp, hq)
+    np.testing.assert_array_equal(xp, xq)

@@ -106,6 +106,16 @@ typedef struct {
      */
     const uint16_t *router_scale;
     const uint16_t *per_expert_scale;
+    /*
+     * Optional layer tail (Mference system design, "Decode", cb2: post-FFN norm, residual add,
+     * layer scalar), applied to this layer's output y by the residual step that follows it in
+     * a stack (moe_stack_forward_decode); moe_forward_* return y without it. NULL leaves the
+     * step out.
+     *   post_ffn_norm: bf16 [d], 16-byte aligned: y -> (y / sqrt(mean(y^2) + 1e-6)) * post_ffn_norm
+     *   layer_scalar: one bf16 in device memory: h_next = bf16((h + y) * layer_scalar)
+     */
+    const uint16_t *post_ffn_norm;
+    const uint16_t *layer_scalar;
 } moe_weights;
 
 /*
@@ -153,27 +163,33 @@ moe_status moe_forward_prefill(moe_layer *layer, const uint16_t *x, int32_t T, f
                                void *hip_stream);
 
 /*
- * Residual stream between stacked layers (device, bf16 bit patterns):
- *   h_next = bf16(h + y)                                  (y may be NULL: h_next = h)
+ * Residual stream between stacked layers (device, bf16 bit patterns), with the tail of the
+ * layer that produced y (Mference system design, "Decode", cb2):
+ *   z      = post ? (y / sqrt(mean(y^2) + 1e-6)) * post : y
+ *   h_next = bf16((h + z) * scalar)                       (y may be NULL: h_next = h)
  *   x_next = bf16(h_next / sqrt(mean(h_next^2) + 1e-6))   (norm without a learned scale)
- * h, h_next, x_next: [T, d] bf16; y: [T, d] fp32. h_next may alias h. d must be a
- * multiple of 8 in [8, 8192] (MOE_E_SHAPE). Both results are computed in fp64 and rounded
- * once to bf16 (round to nearest even).
+ * h, h_next, x_next: [T, d] bf16; y: [T, d] fp32; post: bf16 [d] or NULL (no post-FFN norm);
+ * scalar: one bf16 or NULL (1); all device memory. h_next may alias h. d must be a multiple
+ * of 8 in [8, 8192] (MOE_E_SHAPE); h, y, h_next, x_next and post 16-byte aligned (MOE_E_ALIGN).
+ * Both results are computed in fp64 in that order and rounded once to bf16 (round to nearest
+ * even).
  */
-moe_status moe_stack_glue(const uint16_t *h, const float *y, uint16_t *h_next, uint16_t *x_next,
-                          int32_t T, int32_t d, void *hip_stream);
+moe_status moe_stack_glue(const uint16_t *h, const float *y, const uint16_t *post, const uint16_t *scalar,
+                          uint16_t *h_next, uint16_t *x_next, int32_t T, int32_t d, void *hip_stream);
 
 /*
  * A stack of decode layers with the residual stream between them, for
  * 1 <= T <= every layer's decode capacity. h (bf16 [T, d]) is the residual stream on entry
  * and is updated in place; for l = 0 .. n_layers-1 in order:
- *   x = bf16(h / sqrt(mean(h^2) + 1e-6));  y = layer_l(x);  h = bf16(h + y)
- * (moe_stack_glue's two steps around moe_forward_decode; the residual step before a layer
- * runs inside that layer's router launch when T * d_model <= 16384). x_buf, h_buf (bf16
- * [T, d]) and y_buf (fp32 [T, d]) are caller-owned scratch; x_buf and y_buf hold the last
- * layer's x and y on return. All layers must have the same d_model (MOE_E_SHAPE); every layer
- * handle is used on this stream. MOE_E_INVALID for NULL arguments or n_layers < 1,
- * MOE_E_CAPACITY for T above a layer's decode capacity; T = 0 is a no-op.
+ *   x = bf16(h / sqrt(mean(h^2) + 1e-6));  y = layer_l(x);
+ *   h = bf16((h + post_l(y)) * scalar_l)
+ * with post_l, scalar_l the layer's optional post_ffn_norm and layer_scalar (moe_stack_glue's
+ * steps around moe_forward_decode; the residual step before a layer runs inside that layer's
+ * router launch when T * d_model <= 16384). x_buf, h_buf (bf16 [T, d]) and y_buf (fp32
+ * [T, d]) are caller-owned scratch; on return x_buf holds the norm of the final stream (what
+ * a next layer would read) and y_buf the last layer's y. All layers must have the same d_model (MOE_E_SHAPE); every layer handle is used on this
+ * stream. MOE_E_INVALID for NULL arguments or n_layers < 1, MOE_E_CAPACITY for T above a
+ * layer's decode capacity; T = 0 is a no-op.
  */
 moe_status moe_stack_forward_decode(moe_layer *const *layers, int32_t n_layers, uint16_t *h, int32_t T,
                                     uint16_t *x_buf, float *y_buf, uint16_t *h_buf, void *hip_stream);

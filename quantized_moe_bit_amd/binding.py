@@ -40,7 +40,8 @@ class moe_qmat(C.Structure):
 
 class moe_weights(C.Structure):
     _fields_ = [(n, moe_qmat) for n in ("router", "gate", "up", "down", "sh_gate", "sh_up", "sh_down")] + \
-               [("logit_bias", C.c_void_p), ("router_scale", C.c_void_p), ("per_expert_scale", C.c_void_p)]
+               [(n, C.c_void_p) for n in ("logit_bias", "router_scale", "per_expert_scale", "post_ffn_norm",
+                                           "layer_scalar")]
 
 
 class moe_host_qmat(C.Structure):
@@ -60,7 +61,7 @@ def lib() -> C.CDLL:
             "moe_route": (st, [vp, vp, i32, vp, vp, vp, vp, vp, vp]),
             "moe_forward_decode": (st, [vp, vp, i32, vp, vp]),
             "moe_forward_prefill": (st, [vp, vp, i32, vp, vp]),
-            "moe_stack_glue": (st, [vp, vp, vp, vp, i32, i32, vp]),
+            "moe_stack_glue": (st, [vp, vp, vp, vp, vp, vp, i32, i32, vp]),
             "moe_stack_forward_decode": (st, [C.POINTER(vp), i32, vp, i32, vp, vp, vp, vp]),
             "moe_packed_bytes": (C.c_size_t, [i32, i32, i32, i32, i32]),
             "moe_repack": (st, [i32, i32, i32, i32, C.POINTER(moe_host_qmat), vp, vp]),
@@ -144,9 +145,9 @@ def moe_forward_prefill(handle, x, T, y, stream=None):
     _check(lib().moe_forward_prefill(handle, _ptr(x), T, _ptr(y), _stream(stream)), "moe_forward_prefill")
 
 
-def moe_stack_glue(h, y, h_next, x_next, T, d, stream=None):
-    _check(lib().moe_stack_glue(_ptr(h), _ptr(y), _ptr(h_next), _ptr(x_next), T, d, _stream(stream)),
-           "moe_stack_glue")
+def moe_stack_glue(h, y, h_next, x_next, T, d, stream=None, post=None, scalar=None):
+    _check(lib().moe_stack_glue(_ptr(h), _ptr(y), _ptr(post), _ptr(scalar), _ptr(h_next), _ptr(x_next), T, d,
+                                _stream(stream)), "moe_stack_glue")
 
 
 def moe_stack_forward_decode(handles, h, T, x_buf, y_buf, h_buf, stream=None):

@@ -119,21 +119,41 @@ __device__ __forceinline__ uint32_t f64_to_bf16(double v) {
 __device__ __forceinline__ double bf16_to_f64(uint32_t bits16) { return (double)bf16_to_f32(bits16); }
 
 
-// Residual step between stacked layers for one token, by one workgroup of kGlueWG threads:
-//   h' = bf16(h + y)      x = bf16(h' / sqrt(mean(h'^2) + 1e-6))
-// in fp64, each rounded once to bf16 (y may be null: h' = h). Thread i owns the 8-element
-// chunks i, i + kGlueWG, ... and issues all of its loads before any arithmetic; the fp64 sum
-// of squares is reduced in a fixed order. d % 8 == 0, d <= 8 kGlueWG kGlueChunks. h' goes to
-// h_next unless it is null (h_next may alias h); x goes to x_next (global or LDS). red: LDS
-// for kGlueWG / 64 doubles. Every thread of the workgroup must call it.
+// Residual step between stacked layers for one token, by one workgroup of kGlueWG threads,
+// with the tail of the layer that produced y (Mference system design, "Decode", cb2: post-FFN
+// norm, residual add, layer scalar):
+//   z  = post ? (y / sqrt(mean(y^2) + 1e-6)) * post : y
+//   h' = bf16((h + z) * scalar)      x = bf16(h' / sqrt(mean(h'^2) + 1e-6))
+// in fp64 in that order, each rounded once to bf16 (y may be null: h' = h). post: bf16 [d] or
+// null; scalar: one bf16 or null (1). Thread i owns the 8-element chunks i, i + kGlueWG, ...
+// and issues all of its loads before any arithmetic; the fp64 sums of squares are reduced in
+// a fixed order. d % 8 == 0, d <= 8 kGlueWG kGlueChunks. h' goes to h_next unless it is null
+// (h_next may alias h); x goes to x_next (global or LDS). red: LDS for kGlueWG / 64 doubles.
+// Every thread of the workgroup must call it.
 constexpr int kGlueWG = 256;
 constexpr int kGlueChunks = 4;
-__device__ __forceinline__ void glue_token(const uint16_t *h, const float *y, uint16_t *h_next, uint16_t *x_next,
-                                           int d, double *red) {
+
+// fixed-order fp64 sum over the workgroup (every thread gets the total; red reusable after)
+__device__ __forceinline__ double glue_block_sum(double v, double *red) {
+    const int tid = threadIdx.x;
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+    double tot = 0.0;
+#pragma unroll
+    for (int w = 0; w < kGlueWG / 64; ++w) tot += red[w];
+    __syncthreads();
+    return tot;
+}
+
+__device__ __forceinline__ void glue_token(const uint16_t *h, const float *y, const uint16_t *post,
+                                           const uint16_t *scalar, uint16_t *h_next, uint16_t *x_next, int d,
+                                           double *red) {
     const int tid = threadIdx.x;
     const int nc = d / 8;
-    u32x4_t hv[kGlueChunks];
+    u32x4_t hv[kGlueChunks], pv[kGlueChunks];
     f32x4_t yv[kGlueChunks][2];
+    const bool tail = y && post;
 #pragma unroll
     for (int c = 0; c < kGlueChunks; ++c) {
         const int i = tid + kGlueWG * c;
@@ -143,7 +163,23 @@ __device__ __forceinline__ void glue_token(const uint16_t *h, const float *y, ui
                 yv[c][0] = *reinterpret_cast<const f32x4_t *>(y + 8 * i);
                 yv[c][1] = *reinterpret_cast<const f32x4_t *>(y + 8 * i + 4);
             }
+            if (tail) pv[c] = ld16(post + 8 * i);
         }
+    }
+    const double sc = (y && scalar) ? bf16_to_f64(*scalar) : 1.0;
+    double inv_y = 1.0;
+    if (tail) {
+        double sy = 0.0;
+#pragma unroll
+        for (int c = 0; c < kGlueChunks; ++c)
+            if (tid + kGlueWG * c < nc) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const double f = (double)yv[c][j >> 2][j & 3];
+                    sy = fma(f, f, sy);
+                }
+            }
+        inv_y = 1.0 / sqrt(glue_block_sum(sy, red) / (double)d + 1e-6);
     }
     uint32_t hb[kGlueChunks][8];
     double ss = 0.0;
@@ -153,21 +189,18 @@ __device__ __forceinline__ void glue_token(const uint16_t *h, const float *y, ui
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 double v = bf16_to_f64((hv[c][j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-                if (y) v += (double)yv[c][j >> 2][j & 3];
+                if (y) {
+                    double z = (double)yv[c][j >> 2][j & 3];
+                    if (tail) z = (z * inv_y) * bf16_to_f64((pv[c][j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+                    v = (v + z) * sc;
+                }
                 hb[c][j] = f64_to_bf16(v);
                 const double r = bf16_to_f64(hb[c][j]);
                 ss = fma(r, r, ss);
             }
         }
     }
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-    if ((tid & 63) == 0) red[tid >> 6] = ss;
-    __syncthreads();
-    double tot = 0.0;
-#pragma unroll
-    for (int w = 0; w < kGlueWG / 64; ++w) tot += red[w];
-    __syncthreads();   // red may be reused by the caller
-    const double inv = 1.0 / sqrt(tot / (double)d + 1e-6);
+    const double inv = 1.0 / sqrt(glue_block_sum(ss, red) / (double)d + 1e-6);
 #pragma unroll
     for (int c = 0; c < kGlueChunks; ++c) {
         const int i = tid + kGlueWG * c;

@@ -347,10 +347,12 @@ struct DecArgs {
     float *hs_s;            // [T][I_s/16]      sums of 16 consecutive shared h values
     float *y;
     // fused residual step of a layer stack (router launch only): h_in, y_in (null before the
-    // first layer) -> h_out (written by workgroup 0) and x (written by workgroup 0 to x_out,
-    // and kept in LDS by every workgroup for its own router waves)
+    // first layer) with the previous layer's tail post_in, scalar_in (optional) -> h_out
+    // (written by workgroup 0) and x (written by workgroup 0 to x_out, and kept in LDS by
+    // every workgroup for its own router waves)
     const uint16_t *h_in;
     const float *y_in;
+    const uint16_t *post_in, *scalar_in;
     uint16_t *h_out, *x_out;
     // router prologue fused into the router launch: router_scale (bf16 [d])
     const uint16_t *router_scale;
@@ -382,8 +384,8 @@ __global__ __launch_bounds__(64 * kRW) void k_dec_router(DecArgs a) {
         double *red = reinterpret_cast<double *>(xs + (size_t)a.T * a.d);
         if (GLUE) {
             for (int t = 0; t < a.T; ++t)
-                glue_token(a.h_in + (size_t)t * a.d, a.y_in ? a.y_in + (size_t)t * a.d : nullptr,
-                           blockIdx.x == 0 ? a.h_out + (size_t)t * a.d : nullptr, xs + (size_t)t * a.d, a.d, red);
+                glue_token(a.h_in + (size_t)t * a.d, a.y_in ? a.y_in + (size_t)t * a.d : nullptr, a.post_in,
+                           a.scalar_in, blockIdx.x == 0 ? a.h_out + (size_t)t * a.d : nullptr, xs + (size_t)t * a.d, a.d, red);
             __syncthreads();
             if (blockIdx.x == 0)
                 for (int i = tid; i < a.T * a.d / 8; i += 64 * kRW)
@@ -692,12 +694,15 @@ hipError_t launch_dec_router_pro(const moe_layer *L, const uint16_t *x, int T, f
 
 bool dec_router_glue_fits(const moe_dims &D, int T) { return (size_t)T * D.d_model * 2 <= kGlueLdsMax; }
 
-hipError_t launch_dec_router_glue(const moe_layer *L, const uint16_t *h_in, const float *y_in, uint16_t *h_out,
+hipError_t launch_dec_router_glue(const moe_layer *L, const uint16_t *h_in, const float *y_in,
+                                  const uint16_t *post_in, const uint16_t *scalar_in, uint16_t *h_out,
                                   uint16_t *x_out, int T, hipStream_t s) {
     const moe_dims &D = L->dims;
     DecArgs a = dec_args(L, x_out, T, nullptr);
     a.h_in = h_in;
     a.y_in = y_in;
+    a.post_in = post_in;
+    a.scalar_in = scalar_in;
     a.h_out = h_out;
     a.x_out = x_out;
     const size_t lds = sizeof(float) * kRW * T * (D.d_model / 64) + sizeof(uint16_t) * T * D.d_model +

@@ -82,6 +82,7 @@ moe_status check_weights(const moe_weights *w) {
     if ((s = check_qmat(w->sh_down, "sh_down")) != MOE_OK) return s;
     if (w->logit_bias && !aligned16(w->logit_bias)) return fail(MOE_E_ALIGN, "logit_bias not 16-byte aligned");
     if (w->router_scale && !aligned16(w->router_scale)) return fail(MOE_E_ALIGN, "router_scale not 16-byte aligned");
+    if (w->post_ffn_norm && !aligned16(w->post_ffn_norm)) return fail(MOE_E_ALIGN, "post_ffn_norm not 16-byte aligned");
     return MOE_OK;
 }
 
@@ -399,17 +400,18 @@ moe_status moe_forward_prefill(moe_layer *L, const uint16_t *x, int32_t T, float
     return MOE_OK;
 }
 
-moe_status moe_stack_glue(const uint16_t *h, const float *y, uint16_t *h_next, uint16_t *x_next, int32_t T,
-                          int32_t d, void *hip_stream) {
+moe_status moe_stack_glue(const uint16_t *h, const float *y, const uint16_t *post, const uint16_t *scalar,
+                          uint16_t *h_next, uint16_t *x_next, int32_t T, int32_t d, void *hip_stream) {
     clear_error();
     if (T < 0) return fail(MOE_E_SHAPE, "moe_stack_glue: T = %d is negative", T);
     if (d < 8 || d % 8 || d > 8192)
         return fail(MOE_E_SHAPE, "moe_stack_glue: d = %d must be a multiple of 8 in [8, 8192]", d);
     if (T == 0) return MOE_OK;
     if (!h || !h_next || !x_next) return fail(MOE_E_INVALID, "moe_stack_glue: NULL pointer");
-    if (!aligned16(h) || !aligned16(h_next) || !aligned16(x_next) || (y && !aligned16(y)))
+    if (!aligned16(h) || !aligned16(h_next) || !aligned16(x_next) || (y && !aligned16(y)) ||
+        (post && !aligned16(post)))
         return fail(MOE_E_ALIGN, "moe_stack_glue: pointer not 16-byte aligned");
-    hipError_t err = launch_glue(h, y, h_next, x_next, T, d, static_cast<hipStream_t>(hip_stream));
+    hipError_t err = launch_glue(h, y, post, scalar, h_next, x_next, T, d, static_cast<hipStream_t>(hip_stream));
     if (err != hipSuccess) return fail(MOE_E_DEVICE, "kernel glue: %s", hipGetErrorString(err));
     return MOE_OK;
 }
@@ -441,10 +443,13 @@ moe_status moe_stack_forward_decode(moe_layer *const *layers, int32_t n_layers, 
         moe_layer *L = layers[l];
         uint16_t *src = (l & 1) ? h_buf : h, *dst = (l & 1) ? h : h_buf;
         const float *yp = l ? y_buf : nullptr;
+        // the previous layer's tail goes with its output y into this layer's residual step
+        const uint16_t *post = l ? layers[l - 1]->w.post_ffn_norm : nullptr;
+        const uint16_t *scalar = l ? layers[l - 1]->w.layer_scalar : nullptr;
         if (dec_router_glue_fits(L->dims, T)) {
-            RUN(K_DEC_ROUTER, launch_dec_router_glue(L, src, yp, dst, x_buf, T, s));
+            RUN(K_DEC_ROUTER, launch_dec_router_glue(L, src, yp, post, scalar, dst, x_buf, T, s));
         } else {
-            RUN(K_GLUE, launch_glue(src, yp, dst, x_buf, T, d, s));
+            RUN(K_GLUE, launch_glue(src, yp, post, scalar, dst, x_buf, T, d, s));
             const uint16_t *u = x_buf;
             moe_status st = router_input(L, x_buf, T, false, s, &u);
             if (st != MOE_OK) return st;
@@ -456,7 +461,7 @@ moe_status moe_stack_forward_decode(moe_layer *const *layers, int32_t n_layers, 
     {   // the last layer's residual add, into h
         moe_layer *L = layers[n_layers - 1];
         uint16_t *src = ((n_layers - 1) & 1) ? h : h_buf;
-        RUN(K_GLUE, launch_glue(src, y_buf, h, x_buf, T, d, s));
+        RUN(K_GLUE, launch_glue(src, y_buf, L->w.post_ffn_norm, L->w.layer_scalar, h, x_buf, T, d, s));
     }
     return MOE_OK;
 }

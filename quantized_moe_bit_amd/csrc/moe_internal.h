@@ -142,7 +142,8 @@ bool dec_router_glue_fits(const moe_dims &D, int T);
 // decode router with the router prologue fused (every workgroup forms the router input in LDS;
 // needs dec_router_glue_fits); writes the group sums of x itself
 hipError_t launch_dec_router_pro(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s);
-hipError_t launch_dec_router_glue(const moe_layer *L, const uint16_t *h_in, const float *y_in, uint16_t *h_out,
+hipError_t launch_dec_router_glue(const moe_layer *L, const uint16_t *h_in, const float *y_in,
+                                  const uint16_t *post_in, const uint16_t *scalar_in, uint16_t *h_out,
                                   uint16_t *x_out, int T, hipStream_t s);
 hipError_t launch_router_table(const moe_layer *L, hipStream_t s);
 size_t router_table_floats(const moe_dims &D);
@@ -159,7 +160,8 @@ hipError_t launch_scale_check(const moe_layer *L, int32_t *flag, hipStream_t s);
 hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s);
 hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s);
 hipError_t launch_combine(const moe_layer *L, int T, float *y, hipStream_t s);
-hipError_t launch_glue(const uint16_t *h, const float *y, uint16_t *h_next, uint16_t *x_next, int T, int d,
+hipError_t launch_glue(const uint16_t *h, const float *y, const uint16_t *post, const uint16_t *scalar,
+                       uint16_t *h_next, uint16_t *x_next, int T, int d,
                        hipStream_t s);
 
 }  // namespace qmoe

@@ -41,7 +41,10 @@ class DeviceLayer:
             q[name] = B.moe_qmat(tc.data_ptr(), ts.data_ptr())
         vecs = {"logit_bias": None if layer.logit_bias is None else layer.logit_bias.astype(np.float32),
                 "router_scale": None if layer.router_scale is None else layer.router_scale.view(np.int16),
-                "per_expert_scale": None if layer.per_expert_scale is None else layer.per_expert_scale.view(np.int16)}
+                "per_expert_scale": None if layer.per_expert_scale is None else layer.per_expert_scale.view(np.int16),
+                "post_ffn_norm": None if layer.post_ffn_norm is None else layer.post_ffn_norm.view(np.int16),
+                "layer_scalar": None if layer.layer_scalar is None else
+                np.asarray(layer.layer_scalar, np.uint16).reshape(1).view(np.int16)}
         for name, v in vecs.items():
             if v is not None:
                 self._keep[name] = _dev(v, self.device)
@@ -71,11 +74,15 @@ class DeviceLayer:
         other.handle = B.moe_layer_create(other.dims, w, 0)
         return other
 
-    _VECS = ("logit_bias", "router_scale", "per_expert_scale")
+    _VECS = ("logit_bias", "router_scale", "per_expert_scale", "post_ffn_norm", "layer_scalar")
 
     def _weights(self, q) -> "B.moe_weights":
         vec = {n: (self._keep[n].data_ptr() if n in self._keep else None) for n in self._VECS}
         return B.moe_weights(**q, **vec)
+
+    def tail(self):
+        """Device tensors of the layer tail (post-FFN norm weight, layer scalar); None where absent."""
+        return self._keep.get("post_ffn_norm"), self._keep.get("layer_scalar")
 
     def weight_bytes(self) -> int:
         tot = 0

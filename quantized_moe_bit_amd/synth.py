@@ -152,6 +152,8 @@ class Layer:
     meta: dict = field(default_factory=dict)
     router_scale: Optional[np.ndarray] = None     # bf16 bits [d]: router prologue scale
     per_expert_scale: Optional[np.ndarray] = None  # bf16 bits [E]: routing-weight scale
+    post_ffn_norm: Optional[np.ndarray] = None    # bf16 bits [d]: post-FFN norm weight (stack layer tail)
+    layer_scalar: Optional[int] = None            # bf16 bits: layer scalar (stack layer tail)
 
     def nbytes(self) -> int:
         tot = 0

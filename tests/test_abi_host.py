@@ -153,11 +153,11 @@ def test_calls_reject_null_layer_and_bad_sizes():
     assert L.moe_forward_decode(None, None, 1, None, None) == B.MOE_E_INVALID
     assert L.moe_forward_prefill(None, None, 1, None, None) == B.MOE_E_INVALID
     assert L.moe_route(None, None, 1, None, None, None, None, None, None) == B.MOE_E_INVALID
-    assert L.moe_stack_glue(None, None, None, None, -1, 16, None) == B.MOE_E_SHAPE
-    assert L.moe_stack_glue(None, None, None, None, 0, 16, None) == B.MOE_OK      # T = 0 is a no-op
-    assert L.moe_stack_glue(None, None, None, None, 2, 16, None) == B.MOE_E_INVALID
-    assert L.moe_stack_glue(None, None, None, None, 2, 12, None) == B.MOE_E_SHAPE     # d % 8
-    assert L.moe_stack_glue(None, None, None, None, 2, 8200, None) == B.MOE_E_SHAPE   # d > 8192
+    assert L.moe_stack_glue(None, None, None, None, None, None, -1, 16, None) == B.MOE_E_SHAPE
+    assert L.moe_stack_glue(None, None, None, None, None, None, 0, 16, None) == B.MOE_OK      # T = 0 is a no-op
+    assert L.moe_stack_glue(None, None, None, None, None, None, 2, 16, None) == B.MOE_E_INVALID
+    assert L.moe_stack_glue(None, None, None, None, None, None, 2, 12, None) == B.MOE_E_SHAPE     # d % 8
+    assert L.moe_stack_glue(None, None, None, None, None, None, 2, 8200, None) == B.MOE_E_SHAPE   # d > 8192
     assert L.moe_profile_enable(None, 1) == B.MOE_E_INVALID
     one_null = (C.c_void_p * 1)(None)
     assert L.moe_stack_forward_decode(None, 1, None, 1, None, None, None, None) == B.MOE_E_INVALID

@@ -75,6 +75,28 @@ __device__ __forceinline__ f16x8_t nib_frag_f16(uint32_t w) {
     return __builtin_bit_cast(f16x8_t, v);
 }
 
+// The four fp16 pairs of one device-layout word as subnormals: pair p holds nibbles p and
+// 4 + p (elements 2p, 2p + 1). Masked in place, nibble n sits in mantissa bits 0..3 of its
+// half (value q 2^-24) for n = 0, 4 and bits 4..7 (value 16 q 2^-24) for n = 1, 5; the word
+// shifted down by 8 gives nibbles 2, 6 and 3, 7 the same way. Pairs 0 and 2 therefore carry
+// q 2^-24 and pairs 1 and 3 carry 16 q 2^-24, all exact. One shift and four ands.
+__device__ __forceinline__ u32x4_t nib_sub(uint32_t w) {
+    const uint32_t w8 = w >> 8;
+    return u32x4_t{w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u};
+}
+
+// Eight bf16 values -> eight fp16 values (exact for |v| in fp16's normal range; larger values
+// saturate, smaller ones lose low bits as fp16 subnormals).
+__device__ __forceinline__ u32x4_t bf16x8_to_f16x8(u32x4_t v) {
+    u32x4_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v[i] << 16), __uint_as_float(v[i] & 0xFFFF0000u));
+        r[i] = __builtin_bit_cast(uint32_t, h);
+    }
+    return r;
+}
+
 __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
 }

@@ -7,12 +7,15 @@
 // and BF16 scale/bias directly, and the routed kernels fuse the affine decode, GeGLU and the
 // weighted reduction).
 //
-// Exact affine split per group (x the 64 inputs of the group):
-//   sum_j x_j (s q_j + b) = 16 s * sum_j x_j (1 + q_j/16) + (b - 16 s) * sum_j x_j.
-// 1 + q/16 comes from the nibbles with one shift and one and-or; v_dot2_f32_bf16 (gate/up,
-// x is bf16) and v_dot2_f32_f16 (down, h is fp16) accumulate in fp32. The group sums of the
-// inputs are formed once (x: by the router, in its fixed order; h: from 16-value sums the
-// gate/up units write) and enter once per (row, group).
+// Affine split per group (x the 64 inputs of the group):
+//   sum_j x_j (s q_j + b) = (2^24 s) * sum_j x_j (q_j 2^-24) + b * sum_j x_j.
+// q 2^-24 is the fp16 subnormal whose mantissa is q, so masking a device-layout word gives
+// two of them at once (exact; see nib_sub), and v_dot2_f32_f16 forms x_j q_j 2^-24 with fp32
+// accumulation. The inputs enter as fp16: h is fp16; x is converted when it is staged, which
+// is exact for |x| in fp16's normal range (a layer input normalized to unit rms has
+// |x| <= sqrt(d)). The group sums of the inputs are formed once (x: by the router, from the
+// bf16 x in its fixed order; h: from 16-value sums the gate/up units write) and enter once
+// per (row, group).
 //
 // A decode launch moves a few MB of weights; one compute unit streams only some tens of
 // GB/s, so the work of every launch is cut into units of 16 weight rows (half of a 1 KiB
@@ -206,7 +209,7 @@ __device__ __forceinline__ float row_sum16(float v) {
 // Gate and up sums of 16 rows over the group pairs p = p0, p0 + PS, ... (< cdiv(G, 2)), MP
 // pairs per batch. load(i0) issues one batch (unconditionally: pairs past the input re-read
 // a valid group and are masked later), so a caller can put the first batch in flight before
-// it stages the input; compute(i0) consumes it with x (bf16) and its group sums Xs in LDS.
+// it stages the input; compute(i0) consumes it with x (fp16) and its group sums Xs in LDS.
 template <int MP>
 struct GateUp16 {
     const uint8_t *Wg, *Wu;
@@ -248,24 +251,28 @@ struct GateUp16 {
         for (int i = 0; i < MP; ++i) {
             const int g = 2 * (p0 + PS * (i0 + i)) + gsel;
             const int gc = min(g, G - 1);
-            float ag = 0.0f, au = 0.0f;
+            // pairs 0 and 2 of a word carry q 2^-24, pairs 1 and 3 carry 16 q 2^-24
+            float ag0 = 0.0f, ag1 = 0.0f, au0 = 0.0f, au1 = 0.0f;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xs + 64 * gc + 16 * s + 8 * khalf);
-                ag = dot2_bf16(xv[0], nib_pair<0>(wg[i][s]), ag);
-                ag = dot2_bf16(xv[1], nib_pair<1>(wg[i][s]), ag);
-                ag = dot2_bf16(xv[2], nib_pair<2>(wg[i][s]), ag);
-                ag = dot2_bf16(xv[3], nib_pair<3>(wg[i][s]), ag);
-                au = dot2_bf16(xv[0], nib_pair<0>(wu[i][s]), au);
-                au = dot2_bf16(xv[1], nib_pair<1>(wu[i][s]), au);
-                au = dot2_bf16(xv[2], nib_pair<2>(wu[i][s]), au);
-                au = dot2_bf16(xv[3], nib_pair<3>(wu[i][s]), au);
+                const u32x4_t pg = nib_sub(wg[i][s]), pu = nib_sub(wu[i][s]);
+                ag0 = dot2_f16(xv[0], pg[0], ag0);
+                ag1 = dot2_f16(xv[1], pg[1], ag1);
+                au0 = dot2_f16(xv[0], pu[0], au0);
+                au1 = dot2_f16(xv[1], pu[1], au1);
+                ag0 = dot2_f16(xv[2], pg[2], ag0);
+                ag1 = dot2_f16(xv[3], pg[3], ag1);
+                au0 = dot2_f16(xv[2], pu[2], au0);
+                au1 = dot2_f16(xv[3], pu[3], au1);
             }
+            const float ag = fmaf(ag1, 0.0625f, ag0), au = fmaf(au1, 0.0625f, au0);
             const float on = g < G ? 1.0f : 0.0f;
             const float X = Xs[gc] * (khalf == 0 ? 1.0f : 0.0f);   // the X_g term once per (row, group)
-            const float s16g = 16.0f * bf16_to_f32(sg[i] & 0xFFFFu), s16u = 16.0f * bf16_to_f32(su[i] & 0xFFFFu);
-            accg = fmaf(on, fmaf(s16g, ag, (bf16_to_f32(sg[i] >> 16) - s16g) * X), accg);
-            accu = fmaf(on, fmaf(s16u, au, (bf16_to_f32(su[i] >> 16) - s16u) * X), accu);
+            const float s24g = 16777216.0f * bf16_to_f32(sg[i] & 0xFFFFu);
+            const float s24u = 16777216.0f * bf16_to_f32(su[i] & 0xFFFFu);
+            accg = fmaf(on, fmaf(s24g, ag, bf16_to_f32(sg[i] >> 16) * X), accg);
+            accu = fmaf(on, fmaf(s24u, au, bf16_to_f32(su[i] >> 16) * X), accu);
         }
     }
 };
@@ -311,19 +318,20 @@ struct Down16 {
             asm volatile("" ::: "memory");
             const int g = 2 * (p0 + PS * (i0 + i)) + gsel;
             const int gc = min(g, G - 1);
-            float a = 0.0f;
+            float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const u32x4_t hv = *reinterpret_cast<const u32x4_t *>(hl + 64 * gc + 16 * s + 8 * khalf);
-                a = dot2_f16(hv[0], nib_pair_f16<0>(w[i][s]), a);
-                a = dot2_f16(hv[1], nib_pair_f16<1>(w[i][s]), a);
-                a = dot2_f16(hv[2], nib_pair_f16<2>(w[i][s]), a);
-                a = dot2_f16(hv[3], nib_pair_f16<3>(w[i][s]), a);
+                const u32x4_t p = nib_sub(w[i][s]);
+                a0 = dot2_f16(hv[0], p[0], a0);
+                a1 = dot2_f16(hv[1], p[1], a1);
+                a0 = dot2_f16(hv[2], p[2], a0);
+                a1 = dot2_f16(hv[3], p[3], a1);
             }
             const float on = g < G ? 1.0f : 0.0f;
             const float H = Hs[gc] * (khalf == 0 ? 1.0f : 0.0f);
-            const float s16 = 16.0f * bf16_to_f32(sb[i] & 0xFFFFu);
-            acc = fmaf(on, fmaf(s16, a, (bf16_to_f32(sb[i] >> 16) - s16) * H), acc);
+            const float s24 = 16777216.0f * bf16_to_f32(sb[i] & 0xFFFFu);
+            acc = fmaf(on, fmaf(s24, fmaf(a1, 0.0625f, a0), bf16_to_f32(sb[i] >> 16) * H), acc);
         }
         return acc;
     }
@@ -425,7 +433,7 @@ __global__ __launch_bounds__(64 * kRW) void k_dec_router(DecArgs a) {
 
 // ----------------------------------------------------------------------------- launch B
 // grid: T * k * (I / 16) routed units, then T * (I_s / 16) shared units; block 64 * kBW.
-// LDS: x [d bf16] | Xs [d/64 floats] | red [kBW][2][16]
+// LDS: x [d fp16] | Xs [d/64 floats] | red [kBW][2][16]
 template <int kPer>
 __global__ __launch_bounds__(64 * kBW) void k_dec_gateup(DecArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -478,7 +486,7 @@ __global__ __launch_bounds__(64 * kBW) void k_dec_gateup(DecArgs a) {
 #pragma unroll
     for (int c = 0; c < kXC; ++c) {
         const int i = tid + 64 * kBW * c;
-        if (i < a.d / 8) *reinterpret_cast<u32x4_t *>(xs + 8 * i) = xv[c];
+        if (i < a.d / 8) *reinterpret_cast<u32x4_t *>(xs + 8 * i) = bf16x8_to_f16x8(xv[c]);
     }
     if (tid < G) Xs[tid] = xgv;
     __syncthreads();

@@ -60,7 +60,7 @@ def lib():
         L.orc_bucket.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
         L.orc_ffn.argtypes = [i32, i32, vp, C.POINTER(_QMat), C.POINTER(_QMat), C.POINTER(_QMat), vp]
         L.orc_layer_tokens.argtypes = [i32, i32, i32, i32, i32, vp, i32, vp, vp, vp] + \
-            [C.POINTER(_QMat)] * 6 + [vp, vp, vp]
+            [C.POINTER(_QMat)] * 6 + [vp, vp, vp, vp, vp]
         L.orc_stack_glue.argtypes = [i32, i32, vp, vp, vp, C.c_double, C.c_double, vp, vp]
         _lib = L
     return _lib
@@ -166,7 +166,9 @@ def ffn(x_f64, gate, up, down) -> np.ndarray:
 
 
 def layer_tokens(layer, x, idx, w, tokens: Optional[Sequence[int]] = None, want_parts=False):
-    """Layer output (float64) for the listed tokens of x (bf16 bits [T,d]) under routing idx/w."""
+    """Layer output (float64) for the listed tokens of x (bf16 bits [T,d]) under routing idx/w.
+    want_parts: also the ungated shared output, the per-slot outputs and the shared-expert
+    gate values (1 without a gate)."""
     dims = layer.dims
     x = _c(x, np.uint16)
     T, d = x.shape
@@ -178,11 +180,15 @@ def layer_tokens(layer, x, idx, w, tokens: Optional[Sequence[int]] = None, want_
     y = np.empty((n, d), np.float64)
     sh = np.empty((n, d), np.float64) if want_parts else None
     r = np.empty((n, dims.top_k, d), np.float64) if want_parts else None
+    a = np.empty(n, np.float64) if want_parts else None
+    sg = getattr(layer, "shared_gate", None)
+    sg = None if sg is None else _c(sg, np.uint16)
     qs = [keep.qmat(m) for m in (layer.gate, layer.up, layer.down, layer.sh_gate, layer.sh_up, layer.sh_down)]
     lib().orc_layer_tokens(d, dims.n_experts, dims.top_k, dims.d_expert, dims.d_shared, _p(x), n,
-                           _p(toks), _p(idx), _p(w), *[C.byref(q) for q in qs], _p(y), _p(sh), _p(r))
+                           _p(toks), _p(idx), _p(w), *[C.byref(q) for q in qs], _p(sg), _p(y), _p(sh), _p(r),
+                           _p(a))
     if want_parts:
-        return y, sh, r
+        return y, sh, r, a
     return y
 
 

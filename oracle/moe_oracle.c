@@ -21,7 +21,10 @@
  *    the synthetic layer's GELU-gated FFN), gate and up projections, tanh-form
  *    GELU on the gate, product, down projection.
  *  - Shared expert: a dense branch on the same input, added without a routing
- *    weight (Mference, "Why the runtime has this shape").
+ *    weight (Mference, "Why the runtime has this shape"). Optionally gated per token
+ *    (Mference system design, "Scope and limitations": the Qwen 3.6 layers have a gated
+ *    shared expert): the branch is multiplied by sigmoid(g . x) for a learned bf16 vector
+ *    g over the model dimension.
  *  - Combine: routed outputs reduced with the router weights and added to the
  *    shared branch (Mference, "Decode", the cb2 phase), in the fixed slot order
  *    (TinyTitan architecture, "Invariants": fp32-or-better accumulation in a fixed
@@ -261,15 +264,17 @@ static orc_qmat expert_view(const orc_qmat *stack, int e, int out_dim, int in_di
 
 /*
  * Layer outputs for the listed tokens, given their routing:
- *   y_t = shared(x_t) + sum_{s=0..k-1} w[t,s] * expert_{idx[t,s]}(x_t)
- * accumulated in float64 in that order. Also returns the shared and per-slot outputs
- * when the pointers are non-null (sh: [n_tok, d], r: [n_tok, k, d]).
+ *   y_t = a_t * shared(x_t) + sum_{s=0..k-1} w[t,s] * expert_{idx[t,s]}(x_t)
+ * accumulated in float64 in that order, with a_t = 1 / (1 + exp(-(g . x_t))) when the
+ * shared-expert gate g (bf16 [d]) is given and a_t = 1 otherwise. Also returns the
+ * (ungated) shared output, the per-slot outputs and a_t when the pointers are non-null
+ * (sh: [n_tok, d], r: [n_tok, k, d], a: [n_tok]).
  */
 void orc_layer_tokens(int d, int E, int k, int I, int Is, const uint16_t *x, int n_tok,
                       const int32_t *tokens, const int32_t *idx, const double *w,
                       const orc_qmat *gate, const orc_qmat *up, const orc_qmat *down,
                       const orc_qmat *sh_gate, const orc_qmat *sh_up, const orc_qmat *sh_down,
-                      double *y, double *sh_out, double *r_out) {
+                      const uint16_t *shared_gate, double *y, double *sh_out, double *r_out, double *a_out) {
     (void)E;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int n = 0; n < n_tok; ++n) {
@@ -279,8 +284,15 @@ void orc_layer_tokens(int d, int E, int k, int I, int Is, const uint16_t *x, int
         double *r = (double *)malloc(sizeof(double) * (size_t)d);
         for (int i = 0; i < d; ++i) xd[i] = bf16_f64(x[(size_t)t * d + i]);
         orc_ffn(d, Is, xd, sh_gate, sh_up, sh_down, sh);
+        double a = 1.0;
+        if (shared_gate) {
+            double z = 0.0;
+            for (int i = 0; i < d; ++i) z += xd[i] * bf16_f64(shared_gate[i]);
+            a = 1.0 / (1.0 + exp(-z));
+        }
+        if (a_out) a_out[n] = a;
         double *yt = y + (size_t)n * d;
-        for (int i = 0; i < d; ++i) yt[i] = sh[i];
+        for (int i = 0; i < d; ++i) yt[i] = a * sh[i];
         if (sh_out)
             for (int i = 0; i < d; ++i) sh_out[(size_t)n * d + i] = sh[i];
         for (int s = 0; s < k; ++s) {

@@ -154,6 +154,7 @@ class Layer:
     per_expert_scale: Optional[np.ndarray] = None  # bf16 bits [E]: routing-weight scale
     post_ffn_norm: Optional[np.ndarray] = None    # bf16 bits [d]: post-FFN norm weight (stack layer tail)
     layer_scalar: Optional[int] = None            # bf16 bits: layer scalar (stack layer tail)
+    shared_gate: Optional[np.ndarray] = None      # bf16 bits [d]: shared-expert gate vector
 
     def nbytes(self) -> int:
         tot = 0

@@ -111,7 +111,11 @@ def layer(lay, x_bits: np.ndarray):
         mask = np.zeros(E)
         mask[sel] = wsel
         outs = np.stack([ffn_dense(x[t], Wg[e], Wu[e], Wd[e]) for e in range(E)])  # every expert
-        y[t] = ffn_dense(x[t], Sg, Su, Sd) + (mask[:, None] * outs).sum(axis=0)
+        sh = ffn_dense(x[t], Sg, Su, Sd)
+        if getattr(lay, "shared_gate", None) is not None:     # gated shared expert: sigmoid(g . x)
+            z = float(np.dot(x[t], bf16_value(lay.shared_gate)))
+            sh = sh / (1.0 + math.exp(-z))
+        y[t] = sh + (mask[:, None] * outs).sum(axis=0)
         idx[t] = sel
         wts[t] = wsel
     return dict(logits64=logits, idx=idx, w=wts, y=y)

@@ -301,6 +301,59 @@ def test_layer_matches_dense_brute_force_with_router_prologue_and_expert_scale()
     _cmp_layer(lay, x, 4)
 
 
+def test_layer_matches_dense_brute_force_with_gated_shared_expert():
+    """Gated shared expert (Mference system design, "Scope and limitations": the Qwen 3.6
+    layers have one), read as the shared branch times sigmoid(g . x): against the brute force,
+    which evaluates the gate with its own dot product and exp."""
+    dims = synth.Dims(d_model=256, n_experts=16, top_k=4, d_expert=64, d_shared=64)
+    lay = synth.gen_layer(dims, 25, router="normal")
+    lay.shared_gate = synth.f32_to_bf16_bits(
+        np.random.default_rng(25).normal(0, 1 / np.sqrt(dims.d_model), dims.d_model).astype(np.float32))
+    x, _, _ = synth.gen_tokens(dims, 4, 25)
+    _cmp_layer(lay, x, 4)
+
+
+def test_shared_gate_closed_forms():
+    """g = 0 gives a gate of exactly 1/2; g and -g give gates summing to 1 (so the two outputs
+    sum to twice the g = 0 output); a gate driven to +-40 turns the shared branch fully on or
+    off to float64 precision."""
+    dims = synth.Dims(d_model=128, n_experts=8, top_k=2, d_expert=64, d_shared=128)
+    lay = synth.gen_layer(dims, 61, router="normal")
+    x, _, _ = synth.gen_tokens(dims, 4, 61)
+    r = oracle.route(lay, x)
+    y1, sh, _, a1 = oracle.layer_tokens(lay, x, r["idx"], r["w"], want_parts=True)
+    routed = y1 - sh
+    scale = np.abs(y1).max()
+
+    def run(g):
+        lay.shared_gate = g
+        y, sh_g, _, a = oracle.layer_tokens(lay, x, r["idx"], r["w"], want_parts=True)
+        np.testing.assert_array_equal(sh_g, sh)   # the ungated branch does not depend on g
+        return y, a
+
+    yz, az = run(np.zeros(dims.d_model, np.uint16))
+    assert np.all(az == 0.5)
+    np.testing.assert_allclose(yz, routed + 0.5 * sh, rtol=0, atol=1e-13 * scale)
+    g = synth.f32_to_bf16_bits(np.random.default_rng(5).normal(0, 0.2, dims.d_model).astype(np.float32))
+    yp, ap = run(g)
+    yn, an = run(g ^ np.uint16(0x8000))
+    assert np.all(np.abs(ap - 0.5) > 1e-3)
+    np.testing.assert_allclose(ap + an, 1.0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(yp + yn, 2 * yz, rtol=0, atol=1e-12 * scale)
+    # against the library sigmoid of an independently formed dot product
+    z = brute.bf16_value(x) @ brute.bf16_value(g)
+    np.testing.assert_allclose(ap, torch.sigmoid(torch.from_numpy(z)).numpy(), rtol=1e-14, atol=0)
+    # saturation on token 0: z = +-40 (up to the bf16 rounding of g)
+    x0 = brute.bf16_value(x[0])
+    gs = synth.f32_to_bf16_bits((40.0 * x0 / np.dot(x0, x0)).astype(np.float32))
+    yon, aon = run(gs)
+    yoff, aoff = run(gs ^ np.uint16(0x8000))
+    assert aon[0] > 1 - 1e-16 and aoff[0] < 1e-16
+    np.testing.assert_allclose(yon[0], y1[0], rtol=0, atol=1e-14 * scale)
+    np.testing.assert_allclose(yoff[0], routed[0], rtol=0, atol=1e-14 * scale)
+    lay.shared_gate = None
+
+
 def test_identical_experts_make_output_independent_of_routing():
     dims = synth.Dims(d_model=128, n_experts=6, top_k=2, d_expert=64, d_shared=64)
     lay = synth.gen_layer(dims, 31, router="uniform")
@@ -321,8 +374,9 @@ def test_shared_branch_added_without_weight():
     dims = synth.Dims(d_model=128, n_experts=4, top_k=2, d_expert=64, d_shared=128)
     lay = synth.gen_layer(dims, 41, router="uniform")
     x, _, _ = synth.gen_tokens(dims, 3, 41)
-    y_full, sh, r = oracle.layer_tokens(lay, x, *oracle.topk(oracle.route(lay, x)["logits"], 2),
-                                        want_parts=True)
+    y_full, sh, r, a = oracle.layer_tokens(lay, x, *oracle.topk(oracle.route(lay, x)["logits"], 2),
+                                           want_parts=True)
+    assert np.all(a == 1.0)   # no shared-expert gate
     # shared part equals the dense brute force of the shared expert alone, unscaled
     for t in range(3):
         ref = brute.ffn_dense(brute.bf16_value(x[t]), brute.dense(lay.sh_gate), brute.dense(lay.sh_up),

@@ -116,6 +116,13 @@ typedef struct {
      */
     const uint16_t *post_ffn_norm;
     const uint16_t *layer_scalar;
+    /*
+     * Optional shared-expert gate (Mference system design, "Scope and limitations": the Qwen
+     * 3.6 layers carry a gated shared expert): bf16 [d], 16-byte aligned. The shared branch
+     * is multiplied by a = 1 / (1 + exp(-(g . x))) per token, the dot product in fp32 over the
+     * fp16 copy of x; NULL leaves the branch ungated.
+     */
+    const uint16_t *shared_gate;
 } moe_weights;
 
 /*

@@ -41,7 +41,7 @@ class moe_qmat(C.Structure):
 class moe_weights(C.Structure):
     _fields_ = [(n, moe_qmat) for n in ("router", "gate", "up", "down", "sh_gate", "sh_up", "sh_down")] + \
                [(n, C.c_void_p) for n in ("logit_bias", "router_scale", "per_expert_scale", "post_ffn_norm",
-                                           "layer_scalar")]
+                                           "layer_scalar", "shared_gate")]
 
 
 class moe_host_qmat(C.Structure):

@@ -240,6 +240,34 @@ __device__ __forceinline__ void glue_token(const uint16_t *h, const float *y, co
     }
 }
 
+// Shared-expert gate of one token, by one full workgroup of kGlueWG threads (Mference system
+// design, "Scope and limitations": a gated shared expert): a = 1 / (1 + exp(-z)) with
+// z = sum_i x_i g_i, x fp16 (global or LDS), g bf16 in global memory, d a multiple of 8.
+// Thread i accumulates inputs 8 (i + kGlueWG c) + j in fp32, c then j ascending; the
+// partial sums are added by a fixed butterfly within each wave and then wave by wave, so
+// every caller gets the same bits for the same x. red: kGlueWG / 64 floats of LDS.
+__device__ __forceinline__ float shared_gate_token(const uint16_t *x, const uint16_t *g, int d, float *red) {
+    const int tid = threadIdx.x;
+    float z = 0.0f;
+    for (int i = tid; i < d / 8; i += kGlueWG) {
+        const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(x + 8 * i);
+        const u32x4_t gv = ld16(g + 8 * i);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float xf = f16_to_f32((xv[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+            z = fmaf(xf, bf16_to_f32((gv[j >> 1] >> (16 * (j & 1))) & 0xFFFFu), z);
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
+    if ((tid & 63) == 0) red[tid >> 6] = z;
+    __syncthreads();
+    float tot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kGlueWG / 64; ++w) tot += red[w];
+    __syncthreads();
+    return 1.0f / (1.0f + __expf(-tot));
+}
+
 // Router prologue of one token held in LDS (bf16 [d], d a multiple of 8), in place, by one
 // full workgroup of kGlueWG threads: x -> bf16(((x / sqrt(mean(x^2) + 1e-6)) * rs) / sqrt(d)),
 // float64 in that order and rounded once (Mference system design, "Decode", router listing).

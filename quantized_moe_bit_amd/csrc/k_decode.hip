@@ -364,6 +364,9 @@ struct DecArgs {
     uint16_t *h_out, *x_out;
     // router prologue fused into the router launch: router_scale (bf16 [d])
     const uint16_t *router_scale;
+    // shared-expert gate: g (bf16 [d]) and the per-token gate values (gate/up -> down)
+    const uint16_t *shared_gate;
+    float *sgate;
 };
 
 // ----------------------------------------------------------------------------- launch A
@@ -496,6 +499,12 @@ __global__ __launch_bounds__(64 * kBW) void k_dec_gateup(DecArgs a) {
         gu.load(i0);
         gu.compute(i0, xs, Xs, accg, accu);
     }
+    if (!routed && jb == 0 && a.shared_gate) {   // one unit per token forms its shared-expert gate
+        __shared__ float gred[kBW];
+        static_assert(64 * kBW == kGlueWG, "the gate runs on one full workgroup");
+        const float gv = shared_gate_token(xs, a.shared_gate, a.d, gred);
+        if (tid == 0) a.sgate[t] = gv;
+    }
     accg = row_sum16(accg);
     accu = row_sum16(accu);
     if (lane < 16) {
@@ -565,6 +574,7 @@ __global__ __launch_bounds__(MAXT) void k_dec_down(DecArgs a) {
     const float qr0 = qr[0], qr1 = qr[1], qr2 = qr[2], qr3 = qr[3];
     const float qs0 = qs[0], qs1 = qs[1], qs2 = qs[2], qs3 = qs[3];
     const float wv = a.wts[(size_t)t * a.k + min(tid, a.k - 1)];
+    const float sgv = a.shared_gate ? a.sgate[t] : 1.0f;
     Down16<kMPC> dr(static_cast<const uint8_t *>(a.down.codes) + (size_t)e * a.d * a.I / 2,
                     a.down.sb + (size_t)e * a.d * GI, db >> 1, db & 1, GI, 0, 1);
     Down16<kMPC> ds(static_cast<const uint8_t *>(a.sh_down.codes), a.sh_down.sb, db >> 1, db & 1, GS, sw, SN);
@@ -618,6 +628,7 @@ __global__ __launch_bounds__(MAXT) void k_dec_down(DecArgs a) {
     if (tid < 16) {
         float out = 0.0f;
         for (int w = s0; w < NW; ++w) out += part_s[w * 16 + tid];
+        out *= sgv;   // gated shared expert (1 without a gate)
         for (int s = 0; s < a.k; ++s) out = fmaf(Ws[s], part_r[s * 16 + tid], out);
         a.y[(size_t)t * a.d + 16 * db + tid] = out;
     }
@@ -652,6 +663,8 @@ DecArgs dec_args(const moe_layer *L, const uint16_t *x, int T, float *y) {
     a.hs_r = L->ws.dhs_r;
     a.hs_s = L->ws.dhs_s;
     a.y = y;
+    a.shared_gate = L->w.shared_gate;
+    a.sgate = L->ws.sgate;
     return a;
 }
 

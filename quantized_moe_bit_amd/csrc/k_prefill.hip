@@ -535,14 +535,20 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
     }
 }
 
-// y[t] = sh[t] + sum_s w[t,s] * r[pos[t*k+s]] in slot order. grid (cdiv(d,1024), T); block 256
-__global__ __launch_bounds__(256) void k_combine(int d, int k, const float *__restrict__ sh,
-                                                 const float *__restrict__ r, const int32_t *__restrict__ pos,
-                                                 const float *__restrict__ wts, float *__restrict__ y) {
+// y[t] = a_t sh[t] + sum_s w[t,s] * r[pos[t*k+s]] in slot order, a_t the shared-expert gate
+// of token t from the fp16 copy of x (1 without a gate). grid (cdiv(d,1024), T); block 256
+__global__ __launch_bounds__(kGlueWG) void k_combine(int d, int k, const float *__restrict__ sh,
+                                                     const float *__restrict__ r, const int32_t *__restrict__ pos,
+                                                     const float *__restrict__ wts, const uint16_t *__restrict__ x16,
+                                                     const uint16_t *__restrict__ gvec, float *__restrict__ y) {
+    __shared__ float gred[kGlueWG / 64];
     const int t = blockIdx.y;
-    const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+    const int c = (blockIdx.x * kGlueWG + threadIdx.x) * 4;
+    const float a = gvec ? shared_gate_token(x16 + (size_t)t * d, gvec, d, gred) : 1.0f;
     if (c >= d) return;
     f32x4_t acc = *reinterpret_cast<const f32x4_t *>(sh + (size_t)t * d + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] *= a;
     for (int s = 0; s < k; ++s) {
         const float w = wts[(size_t)t * k + s];
         const f32x4_t rv = *reinterpret_cast<const f32x4_t *>(r + (size_t)pos[(size_t)t * k + s] * d + c);
@@ -622,8 +628,8 @@ hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s) {
 
 hipError_t launch_combine(const moe_layer *L, int T, float *y, hipStream_t s) {
     const int d = L->dims.d_model;
-    launch(k_combine, dim3(cdiv(d, 1024), T), dim3(256), 0, s, d, L->dims.top_k, L->ws.sh, L->ws.r,
-                       L->ws.pos, L->ws.wts, y);
+    launch(k_combine, dim3(cdiv(d, 4 * kGlueWG), T), dim3(kGlueWG), 0, s, d, L->dims.top_k, L->ws.sh, L->ws.r,
+                       L->ws.pos, L->ws.wts, L->ws.x16, L->w.shared_gate, y);
     return hipGetLastError();
 }
 

@@ -6,6 +6,8 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
+#include <utility>
+#include <vector>
 
 #include "moe_internal.h"
 
@@ -83,6 +85,7 @@ moe_status check_weights(const moe_weights *w) {
     if (w->logit_bias && !aligned16(w->logit_bias)) return fail(MOE_E_ALIGN, "logit_bias not 16-byte aligned");
     if (w->router_scale && !aligned16(w->router_scale)) return fail(MOE_E_ALIGN, "router_scale not 16-byte aligned");
     if (w->post_ffn_norm && !aligned16(w->post_ffn_norm)) return fail(MOE_E_ALIGN, "post_ffn_norm not 16-byte aligned");
+    if (w->shared_gate && !aligned16(w->shared_gate)) return fail(MOE_E_ALIGN, "shared_gate not 16-byte aligned");
     return MOE_OK;
 }
 
@@ -97,23 +100,26 @@ moe_status check_call(moe_layer *L, const void *x, int32_t T, const void *out, c
     return MOE_OK;
 }
 
-// Bump allocator over one device allocation; every region 256-byte aligned.
+// Bump allocator over one device allocation; every region 256-byte aligned. take() records
+// where each region's pointer lives, and rebase() turns every recorded offset into an address
+// inside the allocation, so no region can be left holding a bare offset.
 struct Plan {
     size_t off = 0;
+    std::vector<std::pair<void *, size_t>> slots;   // (address of the pointer, byte offset)
     template <class T>
-    size_t take(T **p, size_t count) {
+    void take(T **p, size_t count) {
         off = (off + 255) & ~size_t(255);
-        const size_t at = off;
+        slots.emplace_back(static_cast<void *>(p), off);
+        *p = nullptr;
         off += sizeof(T) * (count ? count : 1);
-        *p = reinterpret_cast<T *>(at);  // offset for now; rebased after allocation
-        return at;
+    }
+    void rebase(char *base) const {
+        for (const auto &sl : slots) {
+            char *addr = base + sl.second;
+            std::memcpy(sl.first, &addr, sizeof(addr));   // every object pointer has one representation
+        }
     }
 };
-
-template <class T>
-void rebase(T *&p, char *base) {
-    p = reinterpret_cast<T *>(base + reinterpret_cast<uintptr_t>(p));
-}
 
 hipError_t prof_begin(moe_layer *L, int id, hipStream_t s, hipEvent_t *a, hipEvent_t *b) {
     (void)id;
@@ -262,6 +268,7 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.h_s, Tm * Is);
     plan.take(&ws.r, P * d);
     plan.take(&ws.sh, Tm * d);
+    plan.take(&ws.sgate, w->shared_gate ? Tm : 0);
     plan.take(&ws.rqf, router_table_floats(D));
     plan.take(&ws.flag, 1);
     plan.take(&ws.dxg, dec_workspace_floats(D, L->max_dec, 0));
@@ -284,31 +291,7 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
         delete L;
         return fail(MOE_E_NOMEM, "workspace of %zu bytes: %s", plan.off, hipGetErrorString(err));
     }
-    char *base = static_cast<char *>(L->ws_base);
-    rebase(ws.logits, base);
-    rebase(ws.idx, base);
-    rebase(ws.wts, base);
-    rebase(ws.x16, base);
-    rebase(ws.u, base);
-    rebase(ws.counts, base);
-    rebase(ws.offsets, base);
-    rebase(ws.tile_off, base);
-    rebase(ws.items, base);
-    rebase(ws.chunk_base, base);
-    rebase(ws.rank, base);
-    rebase(ws.perm, base);
-    rebase(ws.pos, base);
-    rebase(ws.h_r, base);
-    rebase(ws.h_s, base);
-    rebase(ws.r, base);
-    rebase(ws.sh, base);
-    rebase(ws.rqf, base);
-    rebase(ws.flag, base);
-    rebase(ws.dxg, base);
-    rebase(ws.dh_r, base);
-    rebase(ws.dh_s, base);
-    rebase(ws.dhs_r, base);
-    rebase(ws.dhs_s, base);
+    plan.rebase(static_cast<char *>(L->ws_base));
     // zero once: padding columns of the split sums rely on it
     err = hipMemset(L->ws_base, 0, L->ws_bytes);
     // derived bias-term tables of the prefill GEMMs (read from the borrowed scale/bias words)

@@ -71,6 +71,7 @@ struct Workspace {
     uint16_t *h_s;        // [maxT, I_s]        shared hidden activations, fp16 bits
     float *r;             // [maxT*k, d]        routed expert outputs (bucket order)
     float *sh;            // [maxT, d]          shared expert outputs
+    float *sgate;         // [maxT]             decode: shared-expert gate values (layers with a gate)
     float *rqf;           // router weights fma(scale, q, bias) as fp32 (prefill router table)
     int32_t *flag;        // [1]                layer-creation checks
     // decode path (D = decode capacity, KSd/KSs = input pieces of d / of I_s)

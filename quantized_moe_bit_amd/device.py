@@ -44,7 +44,8 @@ class DeviceLayer:
                 "per_expert_scale": None if layer.per_expert_scale is None else layer.per_expert_scale.view(np.int16),
                 "post_ffn_norm": None if layer.post_ffn_norm is None else layer.post_ffn_norm.view(np.int16),
                 "layer_scalar": None if layer.layer_scalar is None else
-                np.asarray(layer.layer_scalar, np.uint16).reshape(1).view(np.int16)}
+                np.asarray(layer.layer_scalar, np.uint16).reshape(1).view(np.int16),
+                "shared_gate": None if getattr(layer, "shared_gate", None) is None else layer.shared_gate.view(np.int16)}
         for name, v in vecs.items():
             if v is not None:
                 self._keep[name] = _dev(v, self.device)
@@ -74,7 +75,7 @@ class DeviceLayer:
         other.handle = B.moe_layer_create(other.dims, w, 0)
         return other
 
-    _VECS = ("logit_bias", "router_scale", "per_expert_scale", "post_ffn_norm", "layer_scalar")
+    _VECS = ("logit_bias", "router_scale", "per_expert_scale", "post_ffn_norm", "layer_scalar", "shared_gate")
 
     def _weights(self, q) -> "B.moe_weights":
         vec = {n: (self._keep[n].data_ptr() if n in self._keep else None) for n in self._VECS}

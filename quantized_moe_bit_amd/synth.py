@@ -61,10 +61,14 @@ class Workload:
     zipf_s: Optional[float] = None  # per-expert logit bias -s*ln(rank)
     tie_frac: float = 0.0           # fraction of tokens with exactly tied top-8/top-9 logits
     layers: int = 1
+    shared_gate: bool = False       # gated shared expert (gate vector N(0, 1/d) in bf16)
 
 
 TINY = Dims(d_model=256, n_experts=8, top_k=2, d_expert=128, d_shared=256)
 GEMMA = Dims(d_model=2816, n_experts=128, top_k=8, d_expert=704, d_shared=2112)
+# Qwen 3.6 style layer: 256 routed experts, top-8, a gated shared expert, experts about half
+# the size of the 2816-wide layer's (3 x 512 x 2048 against 3 x 704 x 2816 weights)
+QWEN = Dims(d_model=2048, n_experts=256, top_k=8, d_expert=512, d_shared=512)
 
 WORKLOADS: Dict[str, Workload] = {
     "tiny": Workload("tiny", TINY, tokens=4, seed=0, router="uniform"),
@@ -72,6 +76,9 @@ WORKLOADS: Dict[str, Workload] = {
     "stack": Workload("stack", GEMMA, tokens=256, seed=2, layers=30),
     "prefill512": Workload("prefill512", GEMMA, tokens=512, seed=3, zipf_s=1.1),
     "prefill4096": Workload("prefill4096", GEMMA, tokens=4096, seed=4, zipf_s=1.3, tie_frac=0.02),
+    "qwen_decode": Workload("qwen_decode", QWEN, tokens=1, seed=5, shared_gate=True),
+    "qwen_prefill4096": Workload("qwen_prefill4096", QWEN, tokens=4096, seed=6, zipf_s=1.3, tie_frac=0.02,
+                                 shared_gate=True),
 }
 
 TIE_GROUP_SIZE = 9      # experts whose logits are made equal: ranks 8 and 9 tie
@@ -164,7 +171,7 @@ class Layer:
 
 
 def gen_layer(dims: Dims, seed: int, *, router: str = "normal", zipf_s: Optional[float] = None,
-              tie_groups: bool = False, layer_index: int = 0) -> Layer:
+              tie_groups: bool = False, layer_index: int = 0, shared_gate: bool = False) -> Layer:
     d, E, I, Is = dims.d_model, dims.n_experts, dims.d_expert, dims.d_shared
     key = (layer_index,)
     if router == "normal":
@@ -199,8 +206,12 @@ def gen_layer(dims: Dims, seed: int, *, router: str = "normal", zipf_s: Optional
                 rq.biases[e, :half_groups] = rq.biases[lead, :half_groups]
                 if bias is not None:
                     bias[e] = bias[lead]
-    return Layer(dims, rq, gate, up, down, sh_gate, sh_up, sh_down, bias, groups,
-                 meta=dict(seed=seed, router=router, zipf_s=zipf_s, layer_index=layer_index))
+    lay = Layer(dims, rq, gate, up, down, sh_gate, sh_up, sh_down, bias, groups,
+                meta=dict(seed=seed, router=router, zipf_s=zipf_s, layer_index=layer_index))
+    if shared_gate:   # g . x ~ N(0, 1) for unit-rms x
+        g = _rng(seed, *key, 10).normal(0.0, 1.0 / np.sqrt(d), d).astype(np.float32)
+        lay.shared_gate = f32_to_bf16_bits(g)
+    return lay
 
 
 def gen_tokens(dims: Dims, T: int, seed: int, *, layer: Optional[Layer] = None,
@@ -246,7 +257,7 @@ def gen_stack_tokens(dims: Dims, T: int, seed: int) -> np.ndarray:
 
 def workload_layer(w: Workload, layer_index: int = 0) -> Layer:
     return gen_layer(w.dims, w.seed, router=w.router, zipf_s=w.zipf_s,
-                     tie_groups=w.tie_frac > 0, layer_index=layer_index)
+                     tie_groups=w.tie_frac > 0, layer_index=layer_index, shared_gate=w.shared_gate)
 
 
 def workload_tokens(w: Workload, layer: Optional[Layer] = None, T: Optional[int] = None):

@@ -63,6 +63,109 @@ def qmat_bytes(out_dim, in_dim, bits):
     return out_dim * in_dim * bits // 8 + out_dim * (in_dim // 64) * 4
 
 
+def decode_layer_bytes(D):
+    """Weights one decode token streams once: router, k routed and the shared gate/up, down."""
+    d, I, Is, E, k = D.d_model, D.d_expert, D.d_shared, D.n_experts, D.top_k
+    return {"dec_router": qmat_bytes(E, d, 8),
+            "dec_gateup": k * 2 * qmat_bytes(I, d, 4) + 2 * qmat_bytes(Is, d, 4),
+            "dec_down": k * qmat_bytes(d, I, 4) + qmat_bytes(d, Is, 4)}
+
+
+def qwen_section(args, dev, K, W):
+    """Decode (1 token, layer copies rotated) and 4096-token prefill of the 2048-wide,
+    256-expert layer with a gated shared expert."""
+    import torch
+    from quantized_moe_bit_amd import binding as B
+    from quantized_moe_bit_amd import synth
+    from quantized_moe_bit_amd.device import DeviceLayer, tokens_to_device
+    out = {}
+    wd = synth.WORKLOADS["qwen_decode"]
+    D = wd.dims
+    log("generating the 2048-wide 256-expert layer with a gated shared expert")
+    lay = synth.workload_layer(wd)
+    base = DeviceLayer(lay, max_tokens=1, device=dev)
+    copies = [base] + [base.replicate() for _ in range(args.layers - 1)]
+    xt, _, _ = synth.gen_tokens(D, 256, wd.seed + 1000)
+    xs = tokens_to_device(xt, dev)
+    y = torch.empty((1, D.d_model), dtype=torch.float32, device=dev)
+
+    def step(i):
+        B.moe_forward_decode(copies[i % len(copies)].handle, xs[i % 256: i % 256 + 1], 1, y)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(K):
+        step(W + i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    for L in copies:
+        B.moe_profile_reset(L.handle)
+        B.moe_profile_enable(L.handle, True)
+    for i in range(K):
+        step(W + i)
+    torch.cuda.synchronize()
+    stage = decode_layer_bytes(D)
+    kus = {}
+    for name in stage:
+        tot, n = 0.0, 0
+        for L in copies:
+            m, c = B.moe_profile_read(L.handle, B.kernel_id(name))
+            tot += m
+            n += c
+        kus[name] = 1000.0 * tot / max(n, 1)
+    for L in copies:
+        L.close()
+    btok = sum(stage.values())
+    out["workload"] = ("layer d_model 2048, 256 experts, top-8, expert width 512, shared width 512 with a "
+                       "sigmoid(g . x) gate, 8-bit g64 router, 4-bit g64 experts")
+    out["decode"] = {"tokens_per_s": round(1000.0 / ms, 1), "us_per_token": round(1000.0 * ms, 3),
+                     "bytes_per_token": btok, "hbm_gbs": round(btok / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(btok / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "kernels_us": {n: round(v, 3) for n, v in kus.items()},
+                     "kernels_gbs": {n: round(stage[n] / (kus[n] * 1e-6) / 1e9, 1) for n in stage}}
+    if not args.no_prefill:
+        torch.cuda.empty_cache()
+        wp = synth.WORKLOADS["qwen_prefill4096"]
+        lp = synth.workload_layer(wp)
+        xp, _, _ = synth.workload_tokens(wp, lp)
+        T = wp.tokens
+        P = DeviceLayer(lp, max_tokens=T, device=dev)
+        xpd = tokens_to_device(xp, dev)
+        yp = torch.empty((T, D.d_model), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            B.moe_forward_prefill(P.handle, xpd, T, yp)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.prefill_steps):
+            B.moe_forward_prefill(P.handle, xpd, T, yp)
+        e1.record()
+        torch.cuda.synchronize()
+        msp = e0.elapsed_time(e1) / args.prefill_steps
+        B.moe_profile_reset(P.handle)
+        B.moe_profile_enable(P.handle, True)
+        for _ in range(args.prefill_steps):
+            B.moe_forward_prefill(P.handle, xpd, T, yp)
+        torch.cuda.synchronize()
+        pk = {}
+        for kid, name in enumerate(B.KERNEL_NAMES):
+            m, c = B.moe_profile_read(P.handle, kid)
+            if c:
+                pk[name] = round(1000.0 * m / c, 2)
+        P.close()
+        d, I, Is, k = D.d_model, D.d_expert, D.d_shared, D.top_k
+        flops = 2.0 * (T * k * 2 * I * d + T * 2 * Is * d) + 2.0 * (T * k * d * I + T * d * Is)
+        out["prefill"] = {"tokens": T, "routing": "Zipf(1.3) logit skew, 2% tied tokens",
+                          "ms_per_step": round(msp, 4), "tokens_per_s": round(T / (msp * 1e-3), 1),
+                          "mfma_tflops": round(flops / (msp * 1e-3) / 1e12, 2),
+                          "mfma_frac": round(flops / (msp * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+                          "kernels_us": pk}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -76,6 +179,7 @@ def main():
     ap.add_argument("--stack-layers", type=int, default=0, help="layers of the stack workload (0: its 30)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prologue", action="store_true", help="skip the router prologue measurement")
+    ap.add_argument("--no-qwen", action="store_true", help="skip the gated-shared-expert (Qwen 3.6 style) layer")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -195,12 +299,15 @@ def main():
                                    for n, v in kern.items() if n in stage_bytes}},
     }
 
-    # ------------------------------------------------------------------ 4096-token prefill
-    if not args.no_prefill:
+    def release_decode_copies():
         for L in layers:
             L.close()
-        del layers, base
+        layers.clear()
         torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------ 4096-token prefill
+    if not args.no_prefill:
+        release_decode_copies()
         wp = synth.WORKLOADS["prefill4096"]
         log("generating the 4096-token Zipf prefill workload")
         lp = synth.workload_layer(wp)
@@ -278,22 +385,23 @@ def main():
             B.moe_profile_enable(PP.handle, False)
             us_p = 1000.0 * ms_kp / max(n_kp, 1)
             pro_bytes = 3 * 2 * T * d   # x read, u and the fp16 copy of x written (router_scale stays cached)
-            result["next_rows"] = {"router_prologue": {
+            result.setdefault("next_rows", {})["router_prologue"] = {
                 "workload": "4096-token prefill chunk and 1-token decode through the 2816-wide layer with the "
                             "router prologue (rmsnorm without scale, router_scale / sqrt(d)) and per-expert scale",
                 "prefill_ms_per_step": round(ms_pro, 4), "prefill_ms_without": round(ms_pre, 4),
                 "prologue_us_prefill": round(us_p, 2), "prologue_bytes_prefill": pro_bytes,
                 "prologue_gbs_prefill": round(pro_bytes / (us_p * 1e-6) / 1e9, 1),
-                "decode_router_with_prologue_us": round(1000.0 * ms_kd / max(n_kd, 1), 2)}}
+                "decode_router_with_prologue_us": round(1000.0 * ms_kd / max(n_kd, 1), 2)}
             PP.close()
+
+    # ------------------------------------------------------------------ widened row: gated shared expert
+    if not args.no_qwen:
+        release_decode_copies()
+        result.setdefault("next_rows", {})["qwen_gated_shared"] = qwen_section(args, dev, K, W)
 
     # ------------------------------------------------------------------ 30-layer decode stack
     if not args.no_stack:
-        if args.no_prefill:         # the prefill section already released the decode copies
-            for L in layers:
-                L.close()
-            del layers, base
-        torch.cuda.empty_cache()
+        release_decode_copies()
         ws = synth.WORKLOADS["stack"]
         NL = args.stack_layers or ws.layers
         log(f"generating the {NL}-layer decode stack")

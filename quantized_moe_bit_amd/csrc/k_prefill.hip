@@ -551,7 +551,10 @@ __global__ __launch_bounds__(kGlueWG) void k_combine(int d, int k, const float *
     for (int i = 0; i < 4; ++i) acc[i] *= a;
     for (int s = 0; s < k; ++s) {
         const float w = wts[(size_t)t * k + s];
-        const f32x4_t rv = *reinterpret_cast<const f32x4_t *>(r + (size_t)pos[(size_t)t * k + s] * d + c);
+        // each routed output is read exactly once: non-temporal, so the stream does not evict
+        // what the caches still hold for the other slots' rows
+        const f32x4_t rv =
+            __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(r + (size_t)pos[(size_t)t * k + s] * d + c));
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, rv[i], acc[i]);
     }

@@ -117,6 +117,11 @@ __device__ __forceinline__ float gelu_tanh_f32(float v) {
 }
 
 __device__ __forceinline__ u32x4_t ld16(const void *p) { return *reinterpret_cast<const u32x4_t *>(p); }
+// 16-byte load of data read once per call (decode weight streams): non-temporal, so it does
+// not displace what the caches hold for the rest of the call
+__device__ __forceinline__ u32x4_t ld16_nt(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+}
 
 // 16-byte store with the non-temporal hint (streamed past the caches), for a large output no
 // later kernel of the call reads.

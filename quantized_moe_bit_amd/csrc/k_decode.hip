@@ -240,8 +240,8 @@ struct GateUp16 {
 #pragma unroll
         for (int i = 0; i < MP; ++i) {
             const int g = min(2 * (p0 + PS * (i0 + i)) + gsel, G - 1);
-            wg[i] = ld16(Wg + ((uint32_t)g * 1024 + co));
-            wu[i] = ld16(Wu + ((uint32_t)g * 1024 + co));
+            wg[i] = ld16_nt(Wg + ((uint32_t)g * 1024 + co));
+            wu[i] = ld16_nt(Wu + ((uint32_t)g * 1024 + co));
             sg[i] = Sg[(uint32_t)g * 32 + so];
             su[i] = Su[(uint32_t)g * 32 + so];
         }
@@ -306,7 +306,7 @@ struct Down16 {
 #pragma unroll
         for (int i = 0; i < MP; ++i) {
             const int g = min(2 * (p0 + PS * (i0 + i)) + gsel, G - 1);
-            w[i] = ld16(W + ((uint32_t)g * 1024 + co));
+            w[i] = ld16_nt(W + ((uint32_t)g * 1024 + co));
             sb[i] = S[(uint32_t)g * 32 + so];
         }
     }

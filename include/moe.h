@@ -123,6 +123,21 @@ typedef struct {
      * fp16 copy of x; NULL leaves the branch ungated.
      */
     const uint16_t *shared_gate;
+    /*
+     * Optional expert slots (Mference system design, "Load and ownership": each layer keeps
+     * its routed experts in a slab of slots and a GPU-visible expert-to-slot table, -1 for an
+     * absent expert). When expert_slot is non-NULL (device int32 [E]), the routed gate, up and
+     * down arrays hold n_slots experts (slot n at n times the per-expert size) and routed
+     * expert e is read from slot expert_slot[e]. The caller fills slots and updates the table
+     * between calls (moe_slot_cache_* plan which expert goes where); every expert a call
+     * selects must be resident when its routed kernels run. A kernel that meets an absent or
+     * out-of-range slot reads slot 0 instead, so nothing outside the slab is touched, and
+     * records the fault: moe_slot_faults returns the count, and the call's output must then
+     * be discarded. The prefill GEMMs use the general fp16 dequantization with slots (the
+     * scale range of experts filled later is not known at creation).
+     */
+    const int32_t *expert_slot;
+    int32_t n_slots;
 } moe_weights;
 
 /*
@@ -248,6 +263,42 @@ const char *moe_last_error(void);
  * the recorded events and returns the summed milliseconds and launch count of
  * kernel id since the last reset. moe_kernel_name(id) is NULL past the last id.
  */
+/* ---------------------------------------------------------------- expert slot cache */
+/*
+ * GPU slot lookup (Mference system design, "Decode": the slot map resolves the router's
+ * top-k IDs against the layer's expert-to-slot table on the GPU). topk_idx: device int32
+ * [T, k] (as moe_route writes it); missing: device int32 [1 + E]: missing[0] = the number of
+ * distinct selected experts without a slot, then those experts in ascending order. Needs a
+ * layer created with expert_slot (MOE_E_INVALID otherwise); T = 0 writes a count of 0.
+ */
+moe_status moe_slot_lookup(moe_layer *layer, const int32_t *topk_idx, int32_t T, int32_t *missing,
+                           void *hip_stream);
+
+/* Number of absent or out-of-range slots the layer's kernels have met since creation (or
+ * the last reset); synchronizes the layer's stream. */
+moe_status moe_slot_faults(moe_layer *layer, int32_t reset, int32_t *count, void *hip_stream);
+
+/*
+ * Host-side slot planner (Mference system design, "Load and ownership": least-frequently
+ * used eviction with recency as the tie-breaker; a hit reuses its slot, a miss takes an
+ * evictable slot). Each slot counts the uses of its expert since it was filled and the
+ * request of its last use. moe_slot_cache_plan takes one request (the experts one call
+ * needs, in any order, duplicates allowed): every listed resident expert is a hit (count + 1,
+ * last use = this request); the missing ones, in ascending expert order, take free slots in
+ * ascending slot order, then evict, among the residents this request does not list, the one
+ * with the lowest count, then the oldest last use, then the lowest slot. A request with more
+ * distinct experts than slots is MOE_E_CAPACITY and changes nothing. slot_of (host [n]) gets
+ * each listed expert's slot; fill_expert / fill_slot (host, room for n) get the fills the
+ * caller must perform before the call runs, n_fill their number.
+ */
+typedef struct moe_slot_cache moe_slot_cache;
+moe_status moe_slot_cache_create(int32_t n_experts, int32_t n_slots, moe_slot_cache **out);
+void moe_slot_cache_destroy(moe_slot_cache *cache);
+moe_status moe_slot_cache_plan(moe_slot_cache *cache, const int32_t *experts, int32_t n, int32_t *slot_of,
+                               int32_t *fill_expert, int32_t *fill_slot, int32_t *n_fill);
+/* The current expert-to-slot table (host int32 [n_experts], -1 for absent experts). */
+moe_status moe_slot_cache_table(const moe_slot_cache *cache, int32_t *expert_slot);
+
 moe_status moe_profile_enable(moe_layer *layer, int32_t on);
 moe_status moe_profile_read(moe_layer *layer, int32_t kernel_id, double *total_ms, int64_t *launches);
 moe_status moe_profile_reset(moe_layer *layer);

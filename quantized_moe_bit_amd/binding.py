@@ -41,7 +41,8 @@ class moe_qmat(C.Structure):
 class moe_weights(C.Structure):
     _fields_ = [(n, moe_qmat) for n in ("router", "gate", "up", "down", "sh_gate", "sh_up", "sh_down")] + \
                [(n, C.c_void_p) for n in ("logit_bias", "router_scale", "per_expert_scale", "post_ffn_norm",
-                                           "layer_scalar", "shared_gate")]
+                                           "layer_scalar", "shared_gate", "expert_slot")] + \
+               [("n_slots", C.c_int32)]
 
 
 class moe_host_qmat(C.Structure):
@@ -72,6 +73,12 @@ def lib() -> C.CDLL:
             "moe_profile_read": (st, [vp, i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
             "moe_profile_reset": (st, [vp]),
             "moe_kernel_name": (C.c_char_p, [i32]),
+            "moe_slot_lookup": (st, [vp, vp, i32, vp, vp]),
+            "moe_slot_faults": (st, [vp, i32, C.POINTER(C.c_int32), vp]),
+            "moe_slot_cache_create": (st, [i32, i32, C.POINTER(vp)]),
+            "moe_slot_cache_destroy": (None, [vp]),
+            "moe_slot_cache_plan": (st, [vp, vp, i32, vp, vp, vp, C.POINTER(C.c_int32)]),
+            "moe_slot_cache_table": (st, [vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -204,3 +211,50 @@ def moe_profile_reset(handle):
 def kernel_id(name: str) -> int:
     lib()
     return KERNEL_NAMES.index(name)
+
+
+def moe_slot_lookup(handle, idx, T, missing, stream=None):
+    _check(lib().moe_slot_lookup(handle, _ptr(idx), T, _ptr(missing), _stream(stream)), "moe_slot_lookup")
+
+
+def moe_slot_faults(handle, reset=False, stream=None) -> int:
+    n = C.c_int32()
+    _check(lib().moe_slot_faults(handle, int(bool(reset)), C.byref(n), _stream(stream)), "moe_slot_faults")
+    return n.value
+
+
+class SlotCache:
+    """The library's host-side slot planner (least-frequently used, recency as the tie-breaker)."""
+
+    def __init__(self, n_experts: int, n_slots: int):
+        h = C.c_void_p()
+        _check(lib().moe_slot_cache_create(n_experts, n_slots, C.byref(h)), "moe_slot_cache_create")
+        self.handle, self.n_experts, self.n_slots = h.value, n_experts, n_slots
+
+    def plan(self, experts):
+        """-> (slot of each listed expert, [(expert, slot) fills])"""
+        e = np.ascontiguousarray(np.asarray(experts, np.int32).ravel())
+        n = e.shape[0]
+        slot_of = np.empty(max(n, 1), np.int32)
+        fe = np.empty(max(n, 1), np.int32)
+        fs = np.empty(max(n, 1), np.int32)
+        nf = C.c_int32()
+        _check(lib().moe_slot_cache_plan(self.handle, e.ctypes.data, n, slot_of.ctypes.data, fe.ctypes.data,
+                                         fs.ctypes.data, C.byref(nf)), "moe_slot_cache_plan")
+        return slot_of[:n].tolist(), list(zip(fe[:nf.value].tolist(), fs[:nf.value].tolist()))
+
+    def table(self) -> np.ndarray:
+        t = np.empty(self.n_experts, np.int32)
+        _check(lib().moe_slot_cache_table(self.handle, t.ctypes.data), "moe_slot_cache_table")
+        return t
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().moe_slot_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

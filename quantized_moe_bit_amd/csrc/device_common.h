@@ -245,6 +245,21 @@ __device__ __forceinline__ void glue_token(const uint16_t *h, const float *y, co
     }
 }
 
+// Slot of routed expert e when the layer keeps its experts in slots (eslot non-null): an absent
+// or out-of-range slot is replaced by slot 0, so no access leaves the slab, and counted in
+// *faults by the callers that pass count (one per workgroup or wave); the caller's output is
+// then void. Without slots the expert's own index.
+__device__ __forceinline__ int expert_slot_of(const int32_t *eslot, int n_slots, int32_t *faults, int e,
+                                              bool count) {
+    if (!eslot) return e;
+    int s = eslot[e];
+    if (s < 0 || s >= n_slots) {
+        if (count) atomicAdd(faults, 1);
+        s = 0;
+    }
+    return s;
+}
+
 // Shared-expert gate of one token, by one full workgroup of kGlueWG threads (Mference system
 // design, "Scope and limitations": a gated shared expert): a = 1 / (1 + exp(-z)) with
 // z = sum_i x_i g_i, x fp16 (global or LDS), g bf16 in global memory, d a multiple of 8.

@@ -367,6 +367,10 @@ struct DecArgs {
     // shared-expert gate: g (bf16 [d]) and the per-token gate values (gate/up -> down)
     const uint16_t *shared_gate;
     float *sgate;
+    // expert slots (null: routed expert e is matrix e of the routed arrays)
+    const int32_t *eslot;
+    int n_slots;
+    int32_t *slot_faults;
 };
 
 // ----------------------------------------------------------------------------- launch A
@@ -479,8 +483,10 @@ __global__ __launch_bounds__(64 * kBW) void k_dec_gateup(DecArgs a) {
         }
         mg = &a.gate;
         mu = &a.up;
-        cbase = (size_t)e * a.I * a.d / 2;
-        sbase = (size_t)e * a.I * G;
+        const int es = __builtin_amdgcn_readfirstlane(
+            expert_slot_of(a.eslot, a.n_slots, a.slot_faults, e, record && lane == 0));
+        cbase = (size_t)es * a.I * a.d / 2;
+        sbase = (size_t)es * a.I * G;
     }
     // the first batch of weights goes out before x is staged
     GateUp16<kMPB> gu(static_cast<const uint8_t *>(mg->codes) + cbase, static_cast<const uint8_t *>(mu->codes) + cbase,
@@ -562,7 +568,10 @@ __global__ __launch_bounds__(MAXT) void k_dec_down(DecArgs a) {
     // weights; loads retire in order, so the staging stores below wait only for the former
     const int sw = wave >= s0 ? wave - s0 : 0;
     int e = 0;
-    if (wave < a.k) e = __builtin_amdgcn_readfirstlane(a.idx[(size_t)t * a.k + wave]);
+    if (wave < a.k) {
+        e = __builtin_amdgcn_readfirstlane(a.idx[(size_t)t * a.k + wave]);
+        e = __builtin_amdgcn_readfirstlane(expert_slot_of(a.eslot, a.n_slots, a.slot_faults, e, false));
+    }
     constexpr int kHC = 2;   // 16-byte chunks of the slot h per thread: k I / 8 <= kHC * 64 * NW
     u32x4_t hrv[kHC];
 #pragma unroll
@@ -665,6 +674,9 @@ DecArgs dec_args(const moe_layer *L, const uint16_t *x, int T, float *y) {
     a.y = y;
     a.shared_gate = L->w.shared_gate;
     a.sgate = L->ws.sgate;
+    a.eslot = L->w.expert_slot;
+    a.n_slots = L->w.n_slots;
+    a.slot_faults = L->ws.slot_faults;
     return a;
 }
 

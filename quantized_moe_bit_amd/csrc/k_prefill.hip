@@ -204,6 +204,9 @@ struct PreArgs {
     moe_qmat gate, up, sh_gate, sh_up, down, sh_down;
     uint16_t *h_r, *h_s;        // hidden activations (fp16): [T k, I] bucket order, [T, I_s]
     float *r, *sh;
+    const int32_t *eslot;       // expert slots (null: expert e is matrix e of the routed arrays)
+    int n_slots;
+    int32_t *slot_faults;
 };
 
 // Eight fp16 weights scale * q + bias from one device-layout word (elements j = 0..7 of a
@@ -288,7 +291,7 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
         nt = j % NTr;
         const int4 it = a.items[mg];   // in bounds: the table holds the worst-case tile count
         if (mg >= a.tile_off[E]) return;
-        e = it.x;
+        e = expert_slot_of(a.eslot, a.n_slots, a.slot_faults, it.x, MODE == 0 && nt == 0 && threadIdx.x == 0);
         mt = it.y;
         rowbase = it.z;
         count = it.w;
@@ -584,6 +587,9 @@ PreArgs make_args(const moe_layer *L, int T) {
     a.h_s = L->ws.h_s;
     a.r = L->ws.r;
     a.sh = L->ws.sh;
+    a.eslot = L->w.expert_slot;
+    a.n_slots = L->w.n_slots;
+    a.slot_faults = L->ws.slot_faults;
     return a;
 }
 

@@ -30,7 +30,7 @@ namespace {
 
 const char *kKernelNames[K_COUNT] = {"router",     "topk",       "bucket_rank", "bucket_scan", "bucket_scatter",
                                      "dec_router", "dec_gateup", "dec_down", "pre_gateup",  "pre_down",
-                                     "combine",    "glue",       "router_prologue"};
+                                     "combine",    "glue",       "router_prologue", "slot_lookup"};
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -86,6 +86,11 @@ moe_status check_weights(const moe_weights *w) {
     if (w->router_scale && !aligned16(w->router_scale)) return fail(MOE_E_ALIGN, "router_scale not 16-byte aligned");
     if (w->post_ffn_norm && !aligned16(w->post_ffn_norm)) return fail(MOE_E_ALIGN, "post_ffn_norm not 16-byte aligned");
     if (w->shared_gate && !aligned16(w->shared_gate)) return fail(MOE_E_ALIGN, "shared_gate not 16-byte aligned");
+    if (w->expert_slot) {
+        if (reinterpret_cast<uintptr_t>(w->expert_slot) & 3u) return fail(MOE_E_ALIGN, "expert_slot not 4-byte aligned");
+        if (w->n_slots < 1 || w->n_slots > MOE_MAX_EXPERTS)
+            return fail(MOE_E_SHAPE, "n_slots %d out of range [1, %d]", w->n_slots, MOE_MAX_EXPERTS);
+    }
     return MOE_OK;
 }
 
@@ -269,6 +274,7 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.r, P * d);
     plan.take(&ws.sh, Tm * d);
     plan.take(&ws.sgate, w->shared_gate ? Tm : 0);
+    plan.take(&ws.slot_faults, 1);
     plan.take(&ws.rqf, router_table_floats(D));
     plan.take(&ws.flag, 1);
     plan.take(&ws.dxg, dec_workspace_floats(D, L->max_dec, 0));
@@ -297,9 +303,12 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     // derived bias-term tables of the prefill GEMMs (read from the borrowed scale/bias words)
     if (err == hipSuccess) err = launch_router_table(L, nullptr);
     // the prefill GEMMs take the subnormal-code dequantization when every expert scale allows it
-    if (err == hipSuccess) err = launch_scale_check(L, ws.flag, nullptr);
+    // (not with expert slots: the routed arrays then hold n_slots experts, filled later)
     int32_t bad = 1;
-    if (err == hipSuccess) err = hipMemcpy(&bad, ws.flag, sizeof(bad), hipMemcpyDeviceToHost);
+    if (!w->expert_slot) {
+        if (err == hipSuccess) err = launch_scale_check(L, ws.flag, nullptr);
+        if (err == hipSuccess) err = hipMemcpy(&bad, ws.flag, sizeof(bad), hipMemcpyDeviceToHost);
+    }
     L->pre_sub = err == hipSuccess && bad == 0;
     if (err == hipSuccess) err = hipDeviceSynchronize();
     if (err != hipSuccess) {
@@ -446,6 +455,30 @@ moe_status moe_stack_forward_decode(moe_layer *const *layers, int32_t n_layers, 
         uint16_t *src = ((n_layers - 1) & 1) ? h : h_buf;
         RUN(K_GLUE, launch_glue(src, y_buf, L->w.post_ffn_norm, L->w.layer_scalar, h, x_buf, T, d, s));
     }
+    return MOE_OK;
+}
+
+moe_status moe_slot_lookup(moe_layer *L, const int32_t *topk_idx, int32_t T, int32_t *missing, void *hip_stream) {
+    clear_error();
+    if (!L) return fail(MOE_E_INVALID, "moe_slot_lookup: layer is NULL");
+    if (!L->w.expert_slot) return fail(MOE_E_INVALID, "moe_slot_lookup: the layer has no expert slots");
+    if (T < 0) return fail(MOE_E_SHAPE, "moe_slot_lookup: T = %d is negative", T);
+    if (!missing || (T > 0 && !topk_idx)) return fail(MOE_E_INVALID, "moe_slot_lookup: NULL pointer");
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    RUN(K_SLOT_LOOKUP, launch_slot_lookup(L, topk_idx, T, missing, s));
+    return MOE_OK;
+}
+
+moe_status moe_slot_faults(moe_layer *L, int32_t reset, int32_t *count, void *hip_stream) {
+    clear_error();
+    if (!L || !count) return fail(MOE_E_INVALID, "moe_slot_faults: NULL argument");
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    int32_t v = 0;
+    hipError_t err = hipMemcpyAsync(&v, L->ws.slot_faults, sizeof(v), hipMemcpyDeviceToHost, s);
+    if (err == hipSuccess) err = hipStreamSynchronize(s);
+    if (err == hipSuccess && reset) err = hipMemsetAsync(L->ws.slot_faults, 0, sizeof(int32_t), s);
+    if (err != hipSuccess) return fail(MOE_E_DEVICE, "moe_slot_faults: %s", hipGetErrorString(err));
+    *count = v;
     return MOE_OK;
 }
 

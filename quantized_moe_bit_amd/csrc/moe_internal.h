@@ -49,6 +49,7 @@ enum KernelId {
     K_COMBINE,
     K_GLUE,
     K_ROUTER_PROLOGUE,
+    K_SLOT_LOOKUP,
     K_COUNT
 };
 
@@ -72,6 +73,7 @@ struct Workspace {
     float *r;             // [maxT*k, d]        routed expert outputs (bucket order)
     float *sh;            // [maxT, d]          shared expert outputs
     float *sgate;         // [maxT]             decode: shared-expert gate values (layers with a gate)
+    int32_t *slot_faults; // [1]                absent expert slots the kernels met (layers with slots)
     float *rqf;           // router weights fma(scale, q, bias) as fp32 (prefill router table)
     int32_t *flag;        // [1]                layer-creation checks
     // decode path (D = decode capacity, KSd/KSs = input pieces of d / of I_s)
@@ -161,6 +163,8 @@ hipError_t launch_scale_check(const moe_layer *L, int32_t *flag, hipStream_t s);
 hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s);
 hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s);
 hipError_t launch_combine(const moe_layer *L, int T, float *y, hipStream_t s);
+// GPU slot lookup of the top-k experts (layers with expert slots)
+hipError_t launch_slot_lookup(const moe_layer *L, const int32_t *idx, int T, int32_t *missing, hipStream_t s);
 hipError_t launch_glue(const uint16_t *h, const float *y, const uint16_t *post, const uint16_t *scalar,
                        uint16_t *h_next, uint16_t *x_next, int T, int d,
                        hipStream_t s);

@@ -19,11 +19,15 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
 class DeviceLayer:
     """One MoE layer resident on a GPU. `layer` is a canonical-layout synth.Layer."""
 
-    def __init__(self, layer, max_tokens: int, device="cuda:0"):
+    def __init__(self, layer, max_tokens: int, device="cuda:0", n_slots: Optional[int] = None):
+        """n_slots: keep the routed experts in that many slots (expert slot cache): every
+        expert's device-layout bytes stay in pinned host memory and `ensure` fills slots."""
         self.dims_py = layer.dims
         self.device = torch.device(device)
         D = layer.dims
         self._keep = {}
+        self.n_slots = n_slots
+        self._slot_src = {}
         q = {}
         specs = {
             "router": (layer.router, 8, 1, D.n_experts, D.d_model),
@@ -36,7 +40,16 @@ class DeviceLayer:
         }
         for name, (m, bits, n, o, i) in specs.items():
             c, s = B.moe_repack(bits, n, o, i, m.codes, m.scales, m.biases)
-            tc, ts = _dev(c, self.device), _dev(s.view(np.int32), self.device)
+            if n_slots is not None and name in ("gate", "up", "down"):
+                # slab of n_slots experts; each expert's bytes stay on the host
+                pc, ps = c.size // n, s.size // n
+                hc = torch.from_numpy(c).pin_memory()
+                hs = torch.from_numpy(s.view(np.int32)).pin_memory()
+                tc = torch.zeros(n_slots * pc, dtype=torch.uint8, device=self.device)
+                ts = torch.zeros(n_slots * ps, dtype=torch.int32, device=self.device)
+                self._slot_src[name] = (hc, hs, pc, ps)
+            else:
+                tc, ts = _dev(c, self.device), _dev(s.view(np.int32), self.device)
             self._keep[name] = (tc, ts)
             q[name] = B.moe_qmat(tc.data_ptr(), ts.data_ptr())
         vecs = {"logit_bias": None if layer.logit_bias is None else layer.logit_bias.astype(np.float32),
@@ -49,6 +62,10 @@ class DeviceLayer:
         for name, v in vecs.items():
             if v is not None:
                 self._keep[name] = _dev(v, self.device)
+        if n_slots is not None:
+            self.slot_cache = B.SlotCache(D.n_experts, n_slots)
+            self._table_host = torch.full((D.n_experts,), -1, dtype=torch.int32).pin_memory()
+            self._table = self._table_host.to(self.device)
         w = self._weights(q)
         self.dims = B.moe_dims(D.d_model, D.n_experts, D.top_k, D.d_expert, D.d_shared, D.group, D.router_bits,
                                D.expert_bits, max_tokens)
@@ -57,9 +74,13 @@ class DeviceLayer:
 
     def replicate(self) -> "DeviceLayer":
         """A copy of this layer in fresh device memory (same values, new addresses, new handle)."""
+        if self.n_slots is not None:
+            raise NotImplementedError("replicate() of a layer with expert slots")
         other = DeviceLayer.__new__(DeviceLayer)
         other.dims_py = self.dims_py
         other.device = self.device
+        other.n_slots = None
+        other._slot_src = {}
         other.max_tokens = self.max_tokens
         other._keep = {}
         q = {}
@@ -79,7 +100,39 @@ class DeviceLayer:
 
     def _weights(self, q) -> "B.moe_weights":
         vec = {n: (self._keep[n].data_ptr() if n in self._keep else None) for n in self._VECS}
+        if self.n_slots is not None:
+            vec["expert_slot"] = self._table.data_ptr()
+            vec["n_slots"] = self.n_slots
         return B.moe_weights(**q, **vec)
+
+    # -------------------------------------------------------------- expert slots
+    def ensure(self, experts, stream=None) -> int:
+        """Make the listed experts resident: plan with the library's slot planner, copy the
+        fills from pinned host memory into their slots and upload the slot table, all on the
+        current stream (so later calls on it see them). Returns the number of fills."""
+        _, fills = self.slot_cache.plan(experts)
+        for e, sl in fills:
+            for name, (hc, hs, pc, ps) in self._slot_src.items():
+                tc, ts = self._keep[name]
+                tc[sl * pc:(sl + 1) * pc].copy_(hc[e * pc:(e + 1) * pc], non_blocking=True)
+                ts[sl * ps:(sl + 1) * ps].copy_(hs[e * ps:(e + 1) * ps], non_blocking=True)
+        if fills:
+            # a fresh pinned staging copy per update: an earlier upload may still be in flight
+            tab = torch.from_numpy(self.slot_cache.table()).pin_memory()
+            self._table.copy_(tab, non_blocking=True)
+            self._staged = tab
+        return len(fills)
+
+    def set_slot_table(self, table: np.ndarray):
+        """Upload an expert-to-slot table as is (synchronously; tests of absent slots)."""
+        self._table.copy_(torch.from_numpy(np.ascontiguousarray(table, np.int32)))
+
+    def missing(self, idx: torch.Tensor) -> np.ndarray:
+        """Distinct selected experts without a slot, from the GPU slot lookup (synchronizes)."""
+        out = torch.empty(1 + self.dims_py.n_experts, dtype=torch.int32, device=self.device)
+        B.moe_slot_lookup(self.handle, idx, idx.shape[0], out)
+        o = out.cpu().numpy()
+        return o[1:1 + o[0]]
 
     def tail(self):
         """Device tensors of the layer tail (post-FFN norm weight, layer scalar); None where absent."""

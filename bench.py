@@ -23,6 +23,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -166,6 +168,72 @@ def qwen_section(args, dev, K, W):
     return out
 
 
+def slot_section(dev, ntok=256):
+    """Expert slot cache on the 2816-wide layer with Zipf(1.3) routing, one token per call:
+    (a) every expert resident through a permuted slot table against the plain resident layer
+    (the cost of the indirection); (b) 16 slots streamed from pinned host memory: per token
+    route, GPU lookup of the missing experts (read back), plan, fills, forward."""
+    import torch
+    from quantized_moe_bit_amd import binding as B
+    from quantized_moe_bit_amd import synth
+    from quantized_moe_bit_amd.device import DeviceLayer, tokens_to_device
+    wl = synth.WORKLOADS["prefill4096"]
+    D = wl.dims
+    log("generating the Zipf-routed 2816-wide layer for the slot cache")
+    lay = synth.workload_layer(wl)
+    x, _, _ = synth.workload_tokens(wl, lay, T=ntok)
+    xd = tokens_to_device(x, dev)
+    y = torch.empty((1, D.d_model), dtype=torch.float32, device=dev)
+    out = {"workload": f"{ntok} Zipf(1.3)-routed tokens, one per call, through one 2816-wide layer "
+                       "(128 experts, top-8)"}
+    res = DeviceLayer(lay, max_tokens=1, device=dev)
+    perm = DeviceLayer(lay, max_tokens=1, device=dev, n_slots=D.n_experts)
+    for e in reversed(range(D.n_experts)):
+        perm.ensure([e])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    us = {}
+    for name, L in (("resident", res), ("all_in_slots", perm)):
+        for i in range(20):
+            B.moe_forward_decode(L.handle, xd[i:i + 1], 1, y)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(ntok):
+            B.moe_forward_decode(L.handle, xd[i:i + 1], 1, y)
+        e1.record()
+        torch.cuda.synchronize()
+        us[name] = 1000.0 * e0.elapsed_time(e1) / ntok
+    out["decode_us_resident"] = round(us["resident"], 3)
+    out["decode_us_all_in_slots"] = round(us["all_in_slots"], 3)
+    res.close()
+    perm.close()
+    ss = DeviceLayer(lay, max_tokens=1, device=dev, n_slots=16)
+    expert_bytes = 3 * qmat_bytes(D.d_expert, D.d_model, 4)
+    fills = hits = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(ntok):
+        r = ss.route(xd[i:i + 1], with_logits=False, with_grouping=False)
+        miss = ss.missing(r["idx"])                   # GPU lookup, read back
+        sel = r["idx"].cpu().numpy().ravel()
+        n = ss.ensure(sel)
+        assert n == len(miss)
+        fills += n
+        hits += len(np.unique(sel)) - n
+        B.moe_forward_decode(ss.handle, xd[i:i + 1], 1, y)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert B.moe_slot_faults(ss.handle) == 0
+    ss.close()
+    out["streaming_16_slots"] = {
+        "tokens_per_s_host_inclusive": round(ntok / wall, 1), "hit_rate": round(hits / max(hits + fills, 1), 4),
+        "fills_per_token": round(fills / ntok, 3), "expert_bytes": expert_bytes,
+        "fill_gbs_host_to_device": round(fills * expert_bytes / wall / 1e9, 2),
+        "note": "wall clock per token includes the host readback of the missing list, planning and "
+                "pinned-host-to-HBM fills"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +248,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prologue", action="store_true", help="skip the router prologue measurement")
     ap.add_argument("--no-qwen", action="store_true", help="skip the gated-shared-expert (Qwen 3.6 style) layer")
+    ap.add_argument("--no-slots", action="store_true", help="skip the expert slot cache measurement")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -398,6 +467,11 @@ def main():
     if not args.no_qwen:
         release_decode_copies()
         result.setdefault("next_rows", {})["qwen_gated_shared"] = qwen_section(args, dev, K, W)
+
+    # ------------------------------------------------------------------ widened row: expert slot cache
+    if not args.no_slots:
+        release_decode_copies()
+        result.setdefault("next_rows", {})["expert_slots"] = slot_section(dev)
 
     # ------------------------------------------------------------------ 30-layer decode stack
     if not args.no_stack:

@@ -274,6 +274,25 @@ const char *moe_last_error(void);
 moe_status moe_slot_lookup(moe_layer *layer, const int32_t *topk_idx, int32_t T, int32_t *missing,
                            void *hip_stream);
 
+/*
+ * Prefill in expert tiles (Mference system design, "Prefill": a chunk's routed experts are
+ * streamed through the slot cache in tiles; each tile's work runs while its experts occupy
+ * slots), for layers with expert slots. Three stream-ordered steps on one chunk of T tokens
+ * (the layer's workspace holds it between them; no other call on the layer in between):
+ *   moe_prefill_route: routing and grouping of the chunk, as moe_forward_prefill starts;
+ *     expert_counts (device int32 [E], may be NULL) gets each expert's number of pairs.
+ *   moe_prefill_tile: the gate/up and down projections of the routed pairs whose expert has
+ *     a slot in the table at that point of the stream (pairs of absent experts are skipped,
+ *     not faults), and with tile = 0 also the shared expert. The caller maps each expert of
+ *     the chunk in exactly one tile's table.
+ *   moe_prefill_combine: y (fp32 [T, d]) from the shared and routed outputs.
+ * moe_prefill_tile on a layer without slots is MOE_E_INVALID.
+ */
+moe_status moe_prefill_route(moe_layer *layer, const uint16_t *x, int32_t T, int32_t *expert_counts,
+                             void *hip_stream);
+moe_status moe_prefill_tile(moe_layer *layer, int32_t T, int32_t tile, void *hip_stream);
+moe_status moe_prefill_combine(moe_layer *layer, int32_t T, float *y, void *hip_stream);
+
 /* Number of absent or out-of-range slots the layer's kernels have met since creation (or
  * the last reset); synchronizes the layer's stream. */
 moe_status moe_slot_faults(moe_layer *layer, int32_t reset, int32_t *count, void *hip_stream);

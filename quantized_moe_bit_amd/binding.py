@@ -74,6 +74,9 @@ def lib() -> C.CDLL:
             "moe_profile_reset": (st, [vp]),
             "moe_kernel_name": (C.c_char_p, [i32]),
             "moe_slot_lookup": (st, [vp, vp, i32, vp, vp]),
+            "moe_prefill_route": (st, [vp, vp, i32, vp, vp]),
+            "moe_prefill_tile": (st, [vp, i32, i32, vp]),
+            "moe_prefill_combine": (st, [vp, i32, vp, vp]),
             "moe_slot_faults": (st, [vp, i32, C.POINTER(C.c_int32), vp]),
             "moe_slot_cache_create": (st, [i32, i32, C.POINTER(vp)]),
             "moe_slot_cache_destroy": (None, [vp]),
@@ -258,3 +261,15 @@ class SlotCache:
             self.close()
         except Exception:
             pass
+
+
+def moe_prefill_route(handle, x, T, expert_counts=None, stream=None):
+    _check(lib().moe_prefill_route(handle, _ptr(x), T, _ptr(expert_counts), _stream(stream)), "moe_prefill_route")
+
+
+def moe_prefill_tile(handle, T, tile, stream=None):
+    _check(lib().moe_prefill_tile(handle, T, tile, _stream(stream)), "moe_prefill_tile")
+
+
+def moe_prefill_combine(handle, T, y, stream=None):
+    _check(lib().moe_prefill_combine(handle, T, _ptr(y), _stream(stream)), "moe_prefill_combine")

@@ -207,6 +207,9 @@ struct PreArgs {
     const int32_t *eslot;       // expert slots (null: expert e is matrix e of the routed arrays)
     int n_slots;
     int32_t *slot_faults;
+    // expert tiles: routed items whose expert has no slot are skipped (not faults), and the
+    // shared items run only with shared set
+    int tile_mode, shared;
 };
 
 // Eight fp16 weights scale * q + bias from one device-layout word (elements j = 0..7 of a
@@ -281,7 +284,7 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
         shared_item = true;
         mt = 8 * (j / NTs) + (bid & 7);
         nt = j % NTs;
-        if (mt >= Ms) return;
+        if (mt >= Ms || !a.shared) return;
         count = a.T;
         rowbase = 0;
     } else {
@@ -291,6 +294,10 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
         nt = j % NTr;
         const int4 it = a.items[mg];   // in bounds: the table holds the worst-case tile count
         if (mg >= a.tile_off[E]) return;
+        if (a.tile_mode) {   // another tile's expert: its rows are computed by that tile's launch
+            const int sl = a.eslot[it.x];
+            if (sl < 0 || sl >= a.n_slots) return;
+        }
         e = expert_slot_of(a.eslot, a.n_slots, a.slot_faults, it.x, MODE == 0 && nt == 0 && threadIdx.x == 0);
         mt = it.y;
         rowbase = it.z;
@@ -590,6 +597,8 @@ PreArgs make_args(const moe_layer *L, int T) {
     a.eslot = L->w.expert_slot;
     a.n_slots = L->w.n_slots;
     a.slot_faults = L->ws.slot_faults;
+    a.tile_mode = 0;
+    a.shared = 1;
     return a;
 }
 
@@ -618,20 +627,26 @@ hipError_t launch_scale_check(const moe_layer *L, int32_t *flag, hipStream_t s) 
     return hipGetLastError();
 }
 
-hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s) {
+hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s, int tile) {
     (void)x;   // the GEMM reads the fp16 copy of x the router wrote
+    PreArgs a = make_args(L, T);
+    a.tile_mode = tile >= 0;
+    a.shared = tile <= 0;
     if (L->pre_sub)
-        launch(k_pre_gemm<0, true>, dim3(pre_grid(L, T, 0)), dim3(kPreWG), 0, s, make_args(L, T));
+        launch(k_pre_gemm<0, true>, dim3(pre_grid(L, T, 0)), dim3(kPreWG), 0, s, a);
     else
-        launch(k_pre_gemm<0, false>, dim3(pre_grid(L, T, 0)), dim3(kPreWG), 0, s, make_args(L, T));
+        launch(k_pre_gemm<0, false>, dim3(pre_grid(L, T, 0)), dim3(kPreWG), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s) {
+hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s, int tile) {
+    PreArgs a = make_args(L, T);
+    a.tile_mode = tile >= 0;
+    a.shared = tile <= 0;
     if (L->pre_sub)
-        launch(k_pre_gemm<1, true>, dim3(pre_grid(L, T, 1)), dim3(kPreWG), 0, s, make_args(L, T));
+        launch(k_pre_gemm<1, true>, dim3(pre_grid(L, T, 1)), dim3(kPreWG), 0, s, a);
     else
-        launch(k_pre_gemm<1, false>, dim3(pre_grid(L, T, 1)), dim3(kPreWG), 0, s, make_args(L, T));
+        launch(k_pre_gemm<1, false>, dim3(pre_grid(L, T, 1)), dim3(kPreWG), 0, s, a);
     return hipGetLastError();
 }
 

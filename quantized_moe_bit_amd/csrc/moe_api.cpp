@@ -458,6 +458,47 @@ moe_status moe_stack_forward_decode(moe_layer *const *layers, int32_t n_layers, 
     return MOE_OK;
 }
 
+moe_status moe_prefill_route(moe_layer *L, const uint16_t *x, int32_t T, int32_t *expert_counts, void *hip_stream) {
+    clear_error();
+    const int32_t dummy_out[4] = {0, 0, 0, 0};
+    moe_status st = check_call(L, x, T, dummy_out, "moe_prefill_route");
+    if (st != MOE_OK || T == 0) return st;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    st = route_impl(L, x, T, s, L->ws.logits, L->ws.idx, L->ws.wts, true, nullptr, true);
+    if (st != MOE_OK) return st;
+    if (expert_counts) {
+        hipError_t err = hipMemcpyAsync(expert_counts, L->ws.counts, sizeof(int32_t) * L->dims.n_experts,
+                                        hipMemcpyDeviceToDevice, s);
+        if (err != hipSuccess) return fail(MOE_E_DEVICE, "moe_prefill_route: %s", hipGetErrorString(err));
+    }
+    return MOE_OK;
+}
+
+moe_status moe_prefill_tile(moe_layer *L, int32_t T, int32_t tile, void *hip_stream) {
+    clear_error();
+    if (!L) return fail(MOE_E_INVALID, "moe_prefill_tile: layer is NULL");
+    if (!L->w.expert_slot) return fail(MOE_E_INVALID, "moe_prefill_tile: the layer has no expert slots");
+    if (T < 0 || T > L->dims.max_tokens)
+        return fail(T < 0 ? MOE_E_SHAPE : MOE_E_CAPACITY, "moe_prefill_tile: T = %d out of [0, %d]", T,
+                    L->dims.max_tokens);
+    if (tile < 0) return fail(MOE_E_INVALID, "moe_prefill_tile: tile = %d is negative", tile);
+    if (T == 0) return MOE_OK;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    RUN(K_PRE_GATEUP, launch_pre_gateup(L, nullptr, T, s, tile));
+    RUN(K_PRE_DOWN, launch_pre_down(L, T, s, tile));
+    return MOE_OK;
+}
+
+moe_status moe_prefill_combine(moe_layer *L, int32_t T, float *y, void *hip_stream) {
+    clear_error();
+    const int32_t dummy_in[4] = {0, 0, 0, 0};
+    moe_status st = check_call(L, dummy_in, T, y, "moe_prefill_combine");
+    if (st != MOE_OK || T == 0) return st;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    RUN(K_COMBINE, launch_combine(L, T, y, s));
+    return MOE_OK;
+}
+
 moe_status moe_slot_lookup(moe_layer *L, const int32_t *topk_idx, int32_t T, int32_t *missing, void *hip_stream) {
     clear_error();
     if (!L) return fail(MOE_E_INVALID, "moe_slot_lookup: layer is NULL");

@@ -160,8 +160,10 @@ size_t dec_gateup_lds(const moe_dims &D);
 size_t dec_down_lds(const moe_dims &D);
 size_t dec_workspace_floats(const moe_dims &D, int max_dec, int which);
 hipError_t launch_scale_check(const moe_layer *L, int32_t *flag, hipStream_t s);
-hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s);
-hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s);
+// tile: -1 for a whole chunk; otherwise the index of an expert tile of a chunk (routed items
+// whose expert has no slot are skipped; the shared expert runs with tile 0 only)
+hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s, int tile = -1);
+hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s, int tile = -1);
 hipError_t launch_combine(const moe_layer *L, int T, float *y, hipStream_t s);
 // GPU slot lookup of the top-k experts (layers with expert slots)
 hipError_t launch_slot_lookup(const moe_layer *L, const int32_t *idx, int T, int32_t *missing, hipStream_t s);

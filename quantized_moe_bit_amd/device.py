@@ -123,6 +123,39 @@ class DeviceLayer:
             self._staged = tab
         return len(fills)
 
+    def prefill_tiled(self, x: torch.Tensor, y: Optional[torch.Tensor] = None):
+        """Prefill one chunk through the slot cache in expert tiles of at most n_slots experts
+        (experts already resident first): route once, then per tile make its experts resident
+        and run its projections with a table that maps only them, then combine.
+        Returns (y, tiles, fills)."""
+        T = x.shape[0]
+        D = self.dims_py
+        if y is None:
+            y = torch.empty((T, D.d_model), dtype=torch.float32, device=self.device)
+        counts = torch.empty(D.n_experts, dtype=torch.int32, device=self.device)
+        B.moe_prefill_route(self.handle, x, T, counts)
+        used = np.nonzero(counts.cpu().numpy())[0]
+        table = self.slot_cache.table()
+        order = [int(e) for e in used if table[e] >= 0] + [int(e) for e in used if table[e] < 0]
+        tiles = [order[i:i + self.n_slots] for i in range(0, len(order), self.n_slots)] or [[]]
+        fills = 0
+        staged = []
+        for ti, tile in enumerate(tiles):
+            fills += self.ensure(tile)
+            active = np.full(D.n_experts, -1, np.int32)
+            full = self.slot_cache.table()
+            active[tile] = full[tile]
+            tab = torch.from_numpy(active).pin_memory()
+            self._table.copy_(tab, non_blocking=True)
+            staged.append(tab)
+            B.moe_prefill_tile(self.handle, T, ti)
+        tab = torch.from_numpy(self.slot_cache.table()).pin_memory()
+        self._table.copy_(tab, non_blocking=True)
+        staged.append(tab)
+        self._staged_tiles = staged
+        B.moe_prefill_combine(self.handle, T, y)
+        return y, len(tiles), fills
+
     def set_slot_table(self, table: np.ndarray):
         """Upload an expert-to-slot table as is (synchronously; tests of absent slots)."""
         self._table.copy_(torch.from_numpy(np.ascontiguousarray(table, np.int32)))

@@ -8,7 +8,9 @@ their addresses differ. Decode runs a token sequence one token at a time with fe
 than experts (hits, misses and evictions through the library's planner); the GPU lookup must
 report exactly the selected experts without a slot. Prefill runs with a permuted slot
 assignment (its GEMMs then take the general fp16 dequantization, which rounds to the same
-fp16 weights). An absent slot must be counted and must not be read outside the slab.
+fp16 weights), and in expert tiles when the chunk selects more experts than there are slots
+(Mference "Prefill": experts streamed in tiles through the slot cache). An absent slot must
+be counted and must not be read outside the slab.
 """
 import numpy as np
 import pytest
@@ -107,5 +109,29 @@ def test_absent_slot_is_counted_and_contained():
     np.testing.assert_array_equal(bits(y), bits(ref.decode(xd[:1])))
     assert B.moe_slot_faults(sl.handle) == 0
     say("absent slot: counted by decode and prefill, nothing read outside the slab; table restored")
+    sl.close()
+    ref.close()
+
+
+def test_prefill_in_expert_tiles():
+    """More experts in the chunk than slots: tiles of at most n_slots experts."""
+    lay = synth.gen_layer(DIMS, 94, router="normal", zipf_s=0.5)
+    x, _, _ = synth.gen_tokens(DIMS, 150, 94)
+    ref = DeviceLayer(lay, max_tokens=150)
+    sl = DeviceLayer(lay, max_tokens=150, n_slots=8)
+    xd = tokens_to_device(x)
+    y_ref = ref.prefill(xd)
+    y, tiles, fills = sl.prefill_tiled(xd)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(y), bits(y_ref))
+    assert tiles >= 3 and fills >= 8 * (tiles - 1)
+    y2, tiles2, fills2 = sl.prefill_tiled(xd)   # the residents of the last tile are reused first
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(y2), bits(y_ref))
+    assert fills2 < fills
+    assert B.moe_slot_faults(sl.handle) == 0
+    say(f"prefill: 150 tokens through 8 slots in {tiles} expert tiles ({fills} fills, then {fills2}), bit-identical")
+    with pytest.raises(B.MoeError):
+        B.moe_prefill_tile(ref.handle, 150, 0)   # a layer without slots
     sl.close()
     ref.close()

@@ -94,12 +94,17 @@ moe_status check_weights(const moe_weights *w) {
     return MOE_OK;
 }
 
-moe_status check_call(moe_layer *L, const void *x, int32_t T, const void *out, const char *what) {
+moe_status check_tokens(moe_layer *L, int32_t T, const char *what) {
     if (!L) return fail(MOE_E_INVALID, "%s: layer is NULL", what);
     if (T < 0) return fail(MOE_E_SHAPE, "%s: T = %d is negative", what, T);
     if (T > L->dims.max_tokens)
         return fail(MOE_E_CAPACITY, "%s: T = %d exceeds max_tokens %d", what, T, L->dims.max_tokens);
-    if (T == 0) return MOE_OK;
+    return MOE_OK;
+}
+
+moe_status check_call(moe_layer *L, const void *x, int32_t T, const void *out, const char *what) {
+    moe_status st = check_tokens(L, T, what);
+    if (st != MOE_OK || T == 0) return st;
     if (!x || !out) return fail(MOE_E_INVALID, "%s: NULL input or output", what);
     if (!aligned16(x) || !aligned16(out)) return fail(MOE_E_ALIGN, "%s: input/output not 16-byte aligned", what);
     return MOE_OK;
@@ -460,9 +465,10 @@ moe_status moe_stack_forward_decode(moe_layer *const *layers, int32_t n_layers, 
 
 moe_status moe_prefill_route(moe_layer *L, const uint16_t *x, int32_t T, int32_t *expert_counts, void *hip_stream) {
     clear_error();
-    const int32_t dummy_out[4] = {0, 0, 0, 0};
-    moe_status st = check_call(L, x, T, dummy_out, "moe_prefill_route");
+    moe_status st = check_tokens(L, T, "moe_prefill_route");
     if (st != MOE_OK || T == 0) return st;
+    if (!x) return fail(MOE_E_INVALID, "moe_prefill_route: x is NULL");
+    if (!aligned16(x)) return fail(MOE_E_ALIGN, "moe_prefill_route: x not 16-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     st = route_impl(L, x, T, s, L->ws.logits, L->ws.idx, L->ws.wts, true, nullptr, true);
     if (st != MOE_OK) return st;
@@ -476,11 +482,9 @@ moe_status moe_prefill_route(moe_layer *L, const uint16_t *x, int32_t T, int32_t
 
 moe_status moe_prefill_tile(moe_layer *L, int32_t T, int32_t tile, void *hip_stream) {
     clear_error();
-    if (!L) return fail(MOE_E_INVALID, "moe_prefill_tile: layer is NULL");
+    moe_status st = check_tokens(L, T, "moe_prefill_tile");
+    if (st != MOE_OK) return st;
     if (!L->w.expert_slot) return fail(MOE_E_INVALID, "moe_prefill_tile: the layer has no expert slots");
-    if (T < 0 || T > L->dims.max_tokens)
-        return fail(T < 0 ? MOE_E_SHAPE : MOE_E_CAPACITY, "moe_prefill_tile: T = %d out of [0, %d]", T,
-                    L->dims.max_tokens);
     if (tile < 0) return fail(MOE_E_INVALID, "moe_prefill_tile: tile = %d is negative", tile);
     if (T == 0) return MOE_OK;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
@@ -491,9 +495,10 @@ moe_status moe_prefill_tile(moe_layer *L, int32_t T, int32_t tile, void *hip_str
 
 moe_status moe_prefill_combine(moe_layer *L, int32_t T, float *y, void *hip_stream) {
     clear_error();
-    const int32_t dummy_in[4] = {0, 0, 0, 0};
-    moe_status st = check_call(L, dummy_in, T, y, "moe_prefill_combine");
+    moe_status st = check_tokens(L, T, "moe_prefill_combine");
     if (st != MOE_OK || T == 0) return st;
+    if (!y) return fail(MOE_E_INVALID, "moe_prefill_combine: y is NULL");
+    if (!aligned16(y)) return fail(MOE_E_ALIGN, "moe_prefill_combine: y not 16-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     RUN(K_COMBINE, launch_combine(L, T, y, s));
     return MOE_OK;

@@ -163,6 +163,17 @@ def test_calls_reject_null_layer_and_bad_sizes():
     assert L.moe_stack_forward_decode(None, 1, None, 1, None, None, None, None) == B.MOE_E_INVALID
     assert L.moe_stack_forward_decode(one_null, 0, None, 1, None, None, None, None) == B.MOE_E_INVALID
     assert L.moe_stack_forward_decode(one_null, 1, None, 1, None, None, None, None) == B.MOE_E_INVALID
+    # expert slots and tiled prefill: argument checks happen before anything touches a device
+    assert L.moe_slot_lookup(None, None, 1, None, None) == B.MOE_E_INVALID
+    assert L.moe_slot_faults(None, 0, None, None) == B.MOE_E_INVALID
+    assert L.moe_prefill_route(None, None, 1, None, None) == B.MOE_E_INVALID
+    assert L.moe_prefill_tile(None, 1, 0, None) == B.MOE_E_INVALID
+    assert L.moe_prefill_combine(None, 1, None, None) == B.MOE_E_INVALID
+    out = C.c_void_p()
+    assert L.moe_slot_cache_create(8, 0, C.byref(out)) == B.MOE_E_SHAPE
+    assert L.moe_slot_cache_create(0, 1, C.byref(out)) == B.MOE_E_SHAPE
+    assert L.moe_slot_cache_create(8, 2, None) == B.MOE_E_INVALID
+    assert L.moe_slot_cache_table(None, None) == B.MOE_E_INVALID
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -171,7 +171,10 @@ moe_status moe_route(moe_layer *layer, const uint16_t *x, int32_t T, int32_t *to
 
 /*
  * Full layer, decode path (wavefront GEMV kernels), for 1 <= T <= MOE_MAX_DECODE_TOKENS:
- *   y[t] = shared(x[t]) + sum_{s<k} w[t,s] * expert_{idx[t,s]}(x[t])      fp32 [T, d]
+ *   y[t] = a[t] * shared(x[t]) + sum_{s<k} w[t,s] * expert_{idx[t,s]}(x[t])      fp32 [T, d]
+ * with a[t] the shared-expert gate (1 without shared_gate) and the routing of moe_route
+ * (including the router prologue and per-expert scale when the weights carry them). With
+ * expert slots every selected expert must be resident (see expert_slot).
  * T = 0 is a no-op; T above MOE_MAX_DECODE_TOKENS or max_tokens is MOE_E_CAPACITY.
  */
 moe_status moe_forward_decode(moe_layer *layer, const uint16_t *x, int32_t T, float *y,

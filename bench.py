@@ -296,7 +296,7 @@ def main():
     D = wl.dims
     log("generating the 2816-wide layer")
     lay = synth.workload_layer(wl)
-    base = DeviceLayer(lay, max_tokens=1, device=dev)
+    base = DeviceLayer(lay, max_tokens=16, device=dev)   # 1-token steps; 16-token calls for the batch line
     layers = [base] + [base.replicate() for _ in range(args.layers - 1)]
     xt, _, _ = synth.gen_tokens(D, 256, wl.seed + 1000)
     xs = tokens_to_device(xt, dev)
@@ -319,6 +319,24 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = ev0.elapsed_time(ev1) / K
+
+    # the same layer copies with 16-token decode calls (batched decode, distinct tokens per call)
+    xs16 = tokens_to_device(synth.gen_tokens(D, 16 * 16, wl.seed + 2000)[0], dev)
+    y16 = torch.empty((16, D.d_model), dtype=torch.float32, device=dev)
+
+    def step16(i):
+        j = i % 16
+        B.moe_forward_decode(layers[i % len(layers)].handle, xs16[16 * j:16 * j + 16], 16, y16)
+
+    for i in range(W):
+        step16(i)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(K):
+        step16(W + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_step16 = ev0.elapsed_time(ev1) / K
 
     # per-kernel durations (HIP events around each launch, same stream), second pass
     for L in layers:
@@ -380,6 +398,8 @@ def main():
                    "tokens_per_step": 1, "layer_copies_rotated": len(layers), "distinct_tokens": ntok,
                    "parallelism": "single GPU"},
         "roofline": roofline,
+        "decode_batch16": {"workload": "16 tokens per decode call through the same layer copies",
+                           "tokens_per_s": round(16 * 1000.0 / ms_step16, 1), "us_per_call": round(1000.0 * ms_step16, 3)},
         "decode": {"bytes_per_token": b_token, "layer_hbm_gbs": round(layer_gbs, 1),
                    "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4), "host_wall_s": round(wall, 4),
                    "kernels_us": {n: round(v["avg_us"], 3) for n, v in kern.items()},

@@ -1,7 +1,7 @@
 """GPU parity on layer shapes away from the 2816-wide workload, through the C ABI: the
 widest model dimension the kernels take (8192: router lanes loop over 128 groups), many
 experts with the largest top-k (256 experts, top-16: four logits per lane in the top-k,
-every down-projection wave shared), top-1 (a single routing weight of exactly 1), and widths
+every down-projection wave shared), the largest expert count (1024, top-8), top-1 (a single routing weight of exactly 1), and widths
 whose last prefill tile is only partly filled, and expert scales above 2^-4.
 Same bar as the other parity tests: top-k index sets and grouping bit-exact, outputs within
 max |err| <= 2e-3 * rms of the oracle.
@@ -28,6 +28,8 @@ SHAPES = {
     # expert scales and biases 8x the usual (scales up to 0.16): the prefill GEMMs must take the
     # dequantization that does not rely on scales below 2^-4
     "large_scales": (synth.Dims(d_model=512, n_experts=8, top_k=2, d_expert=128, d_shared=192), 2, 140),
+    # the largest expert count the library takes (sixteen logits per lane in the top-k)
+    "e1024_top8": (synth.Dims(d_model=512, n_experts=1024, top_k=8, d_expert=64, d_shared=128), 4, 260),
 }
 
 

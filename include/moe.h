@@ -19,7 +19,10 @@
  * All compute runs in gfx950 HIP kernels on the stream the caller passes. Every
  * entry point validates its arguments on the host before enqueuing anything; on
  * error nothing is enqueued, nothing is written, and the handle stays usable.
- * No entry point reads device memory back to the host.
+ * Calls enqueue work and return without waiting for it, with these exceptions, which
+ * read device memory back to the host: moe_layer_create (it checks the quantization
+ * metadata once and waits for that check), moe_slot_faults, moe_profile_read, and every
+ * call on a layer created with MOE_FLAG_CHECK_FINITE (see there).
  *
  * Memory ownership:
  *   - weights are caller-owned device buffers in the device layout moe_repack
@@ -50,13 +53,33 @@ typedef struct moe_layer moe_layer; /* opaque handle */
 typedef enum {
     MOE_OK = 0,
     MOE_E_INVALID = 1,  /* null required pointer, unknown flag, bad enum value */
-    MOE_E_SHAPE = 2,    /* dimension not a multiple of 64 / 32, top_k out of range, T < 0 */
-    MOE_E_QUANT = 3,    /* group != 64, router bits != 8, expert bits != 4 */
+    MOE_E_SHAPE = 2,    /* dimension not a multiple of 64, top_k out of range, T < 0 */
+    MOE_E_QUANT = 3,    /* group != 64, router bits != 8, expert bits != 4, expert scales or
+                           biases the prefill path cannot stage (see moe_layer_create) */
     MOE_E_ALIGN = 4,    /* a device pointer is not 16-byte aligned */
     MOE_E_CAPACITY = 5, /* T above max_tokens (or above MOE_MAX_DECODE_TOKENS for decode) */
-    MOE_E_NOMEM = 6,    /* workspace allocation failed */
-    MOE_E_DEVICE = 7    /* a HIP call or kernel launch reported an error */
+    MOE_E_NOMEM = 6,    /* workspace allocation failed, or the workspace exceeds the budget in the flags */
+    MOE_E_DEVICE = 7,   /* a HIP call or kernel launch reported an error */
+    MOE_E_NONFINITE = 8 /* MOE_FLAG_CHECK_FINITE only: an input or output holds a NaN or infinity */
 } moe_status;
+
+/*
+ * Flags of moe_layer_create (Mference system design, "Correctness and safety invariants": a
+ * step refuses rather than emitting corrupt output).
+ *   MOE_FLAG_CHECK_FINITE: debug mode. moe_route, moe_forward_decode, moe_forward_prefill,
+ *     moe_prefill_route and moe_stack_forward_decode first count the NaN and infinite values
+ *     of their input on the stream and wait for the count; a non-zero count returns
+ *     MOE_E_NONFINITE with nothing else enqueued and no output written. The forward calls
+ *     (and moe_prefill_combine) then count those of their output y (the stack: of the final
+ *     residual stream) and return MOE_E_NONFINITE if there are any; y has then been written.
+ *     Without the flag, inputs are assumed finite and nothing is checked or waited for.
+ *   MOE_FLAG_WS_BUDGET_MIB(n): the workspace may take at most n MiB (1 <= n < 2^24); a layer
+ *     whose workspace would be larger is refused with MOE_E_NOMEM before anything is
+ *     allocated. n = 0 (the default) sets no budget.
+ * Other bits are MOE_E_INVALID.
+ */
+#define MOE_FLAG_CHECK_FINITE 0x1u
+#define MOE_FLAG_WS_BUDGET_MIB(n) (((uint32_t)(n) & 0xFFFFFFu) << 8)
 
 /* Largest token count moe_forward_decode accepts; larger chunks use moe_forward_prefill. */
 #define MOE_MAX_DECODE_TOKENS 16
@@ -66,7 +89,7 @@ typedef enum {
 #define MOE_MAX_EXPERTS 1024
 
 typedef struct {
-    int32_t d_model;     /* model width d; multiple of 64, at most 8192 */
+    int32_t d_model;     /* model width d; multiple of 64 in [64, 8192] */
     int32_t n_experts;   /* routed experts E, 1..MOE_MAX_EXPERTS */
     int32_t top_k;       /* experts per token k, 1..min(E, MOE_MAX_TOP_K) */
     int32_t d_expert;    /* routed expert width I; multiple of 64 */
@@ -133,18 +156,31 @@ typedef struct {
      * selects must be resident when its routed kernels run. A kernel that meets an absent or
      * out-of-range slot reads slot 0 instead, so nothing outside the slab is touched, and
      * records the fault: moe_slot_faults returns the count, and the call's output must then
-     * be discarded. The prefill GEMMs use the general fp16 dequantization with slots (the
-     * scale range of experts filled later is not known at creation).
+     * be discarded. The prefill calls check the scale/bias words of the experts in slots (the
+     * checks moe_layer_create makes for resident layers) and count an expert they cannot
+     * stage as a fault too.
      */
     const int32_t *expert_slot;
     int32_t n_slots;
 } moe_weights;
 
 /*
- * Create a layer handle. Validates dims (MOE_E_QUANT, MOE_E_SHAPE), the weight
- * pointers (MOE_E_INVALID if any required pointer is NULL, MOE_E_ALIGN if not
- * 16-byte aligned) and flags (must be 0, else MOE_E_INVALID), then allocates the
- * workspace for dims->max_tokens tokens on the current HIP device (MOE_E_NOMEM).
+ * Create a layer handle for one MoE FFN layer (Mference system design, "Why the runtime has
+ * this shape": 8-bit group-64 affine router, 4-bit group-64 affine experts with BF16 scale and
+ * bias; ".gturbo directory": weights are bound in place, incompatible quantization metadata is
+ * rejected). Validates dims (MOE_E_QUANT, MOE_E_SHAPE), the weight pointers (MOE_E_INVALID if
+ * any required pointer is NULL, MOE_E_ALIGN if not 16-byte aligned) and flags (MOE_FLAG_*,
+ * else MOE_E_INVALID), then allocates the workspace for dims->max_tokens tokens on the current
+ * HIP device (MOE_E_NOMEM, also when it exceeds the flags' budget).
+ *
+ * The prefill GEMMs stage each dequantized expert weight as one fp16 value, fp16(2^m (s q + b)),
+ * with a power-of-two exponent m per matrix chosen from the matrix's largest |scale| (the
+ * accumulated products are scaled back by 2^-m in fp32, exactly), so the staging keeps 11
+ * significant bits for scales of any magnitude. At creation the library reads every expert
+ * matrix's scale/bias words once and waits for the result: a NaN or infinite scale or bias, a
+ * largest |scale| outside [2^-69, 2^59), or a bias with floor(log2 |bias|) >=
+ * floor(log2 max |scale|) + 20 in its matrix is MOE_E_QUANT. Layers with expert slots check the routed experts' words in
+ * every prefill call instead (see expert_slot), since the slots are filled later.
  * *out is written only on MOE_OK.
  */
 moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t flags,
@@ -170,7 +206,10 @@ moe_status moe_route(moe_layer *layer, const uint16_t *x, int32_t T, int32_t *to
                      void *hip_stream);
 
 /*
- * Full layer, decode path (wavefront GEMV kernels), for 1 <= T <= MOE_MAX_DECODE_TOKENS:
+ * Full layer, decode path (wavefront GEMV kernels; Mference system design, "Decode": router,
+ * top-8 IDs and weights, shared branch, routed experts, weighted reduction (cb2); "Metal
+ * execution": custom affine INT4/INT8 GEMV kernels for single-token decode), for
+ * 1 <= T <= MOE_MAX_DECODE_TOKENS:
  *   y[t] = a[t] * shared(x[t]) + sum_{s<k} w[t,s] * expert_{idx[t,s]}(x[t])      fp32 [T, d]
  * with a[t] the shared-expert gate (1 without shared_gate) and the routing of moe_route
  * (including the router prologue and per-expert scale when the weights carry them). With
@@ -181,11 +220,25 @@ moe_status moe_forward_decode(moe_layer *layer, const uint16_t *x, int32_t T, fl
                               void *hip_stream);
 
 /*
- * Full layer, prefill path (grouped MFMA GEMM over expert-bucketed rows), for
- * 1 <= T <= max_tokens. Same result definition as moe_forward_decode.
+ * Full layer, prefill path (Mference system design, "Prefill": token/expert pairs grouped by
+ * expert and each expert's rows run as one dense product against its dequantized tiles;
+ * "Metal execution": matrix units for multi-row prefill): grouped MFMA GEMMs over
+ * expert-bucketed rows, for 1 <= T <= max_tokens. Same result definition as
+ * moe_forward_decode.
  */
 moe_status moe_forward_prefill(moe_layer *layer, const uint16_t *x, int32_t T, float *y,
                                void *hip_stream);
+
+/*
+ * Routing of the last moe_forward_decode or moe_forward_prefill (or moe_prefill_route) on
+ * this layer, as that call's own kernels selected it: copies, in stream order, the top-k
+ * expert ids (int32 [T, k]) and routing weights (fp32 [T, k]) of its first T tokens to the
+ * device buffers idx and w (Mference system design, "Decode": the router hands eight IDs and
+ * eight weights to the expert stage). T must be at most that call's T; MOE_E_INVALID if no
+ * such call has run or T is larger. An inspection aid for tests; the forward calls need it
+ * not.
+ */
+moe_status moe_last_routing(moe_layer *layer, int32_t T, int32_t *idx, float *w, void *hip_stream);
 
 /*
  * Residual stream between stacked layers (device, bf16 bit patterns), with the tail of the
@@ -260,12 +313,10 @@ const char *moe_status_str(moe_status s);
 /* Message of the last failed call on this thread ("" if none). */
 const char *moe_last_error(void);
 
-/*
- * Per-kernel timing with HIP events recorded around each kernel on the caller's
- * stream. Off by default; it never changes results. moe_profile_read synchronizes
- * the recorded events and returns the summed milliseconds and launch count of
- * kernel id since the last reset. moe_kernel_name(id) is NULL past the last id.
- */
+/* Build identity of the library: a hash over the sources it was compiled from (a binding can
+ * refuse a library older than its sources). */
+const char *moe_build_id(void);
+
 /* ---------------------------------------------------------------- expert slot cache */
 /*
  * GPU slot lookup (Mference system design, "Decode": the slot map resolves the router's
@@ -289,7 +340,11 @@ moe_status moe_slot_lookup(moe_layer *layer, const int32_t *topk_idx, int32_t T,
  *     not faults), and with tile = 0 also the shared expert. The caller maps each expert of
  *     the chunk in exactly one tile's table.
  *   moe_prefill_combine: y (fp32 [T, d]) from the shared and routed outputs.
- * moe_prefill_tile on a layer without slots is MOE_E_INVALID.
+ * moe_prefill_tile on a layer without slots is MOE_E_INVALID, and so are moe_prefill_tile and
+ * moe_prefill_combine when no chunk has been routed on the layer or T differs from the routed
+ * chunk's T. moe_prefill_tile first checks the scale/bias words of the experts its slot table
+ * maps (as moe_layer_create does for resident layers); an expert the prefill GEMMs cannot
+ * stage counts as a slot fault.
  */
 moe_status moe_prefill_route(moe_layer *layer, const uint16_t *x, int32_t T, int32_t *expert_counts,
                              void *hip_stream);
@@ -321,6 +376,13 @@ moe_status moe_slot_cache_plan(moe_slot_cache *cache, const int32_t *experts, in
 /* The current expert-to-slot table (host int32 [n_experts], -1 for absent experts). */
 moe_status moe_slot_cache_table(const moe_slot_cache *cache, int32_t *expert_slot);
 
+/*
+ * Per-kernel timing with HIP events attached to each kernel dispatch on the caller's stream
+ * (Gem native architecture, "Ownership boundaries": a profiled run must give the same results
+ * as the ordinary one). Off by default; it never changes results. moe_profile_read
+ * synchronizes the recorded events and returns the summed milliseconds and launch count of
+ * kernel id since the last reset. moe_kernel_name(id) is NULL past the last id.
+ */
 moe_status moe_profile_enable(moe_layer *layer, int32_t on);
 moe_status moe_profile_read(moe_layer *layer, int32_t kernel_id, double *total_ms, int64_t *launches);
 moe_status moe_profile_reset(moe_layer *layer);

@@ -18,8 +18,16 @@ from . import build as _build
 LIB_PATH = _build.LIB
 _lib = None
 
-MOE_OK, MOE_E_INVALID, MOE_E_SHAPE, MOE_E_QUANT, MOE_E_ALIGN, MOE_E_CAPACITY, MOE_E_NOMEM, MOE_E_DEVICE = range(8)
+(MOE_OK, MOE_E_INVALID, MOE_E_SHAPE, MOE_E_QUANT, MOE_E_ALIGN, MOE_E_CAPACITY, MOE_E_NOMEM, MOE_E_DEVICE,
+ MOE_E_NONFINITE) = range(9)
 MOE_MAX_DECODE_TOKENS = 16
+MOE_FLAG_CHECK_FINITE = 0x1
+
+
+def MOE_FLAG_WS_BUDGET_MIB(n: int) -> int:
+    return (int(n) & 0xFFFFFF) << 8
+
+
 KERNEL_NAMES = []
 
 
@@ -55,6 +63,12 @@ def lib() -> C.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m quantized_moe_bit_amd.build`")
         L = C.CDLL(LIB_PATH)
+        L.moe_build_id.restype = C.c_char_p
+        L.moe_build_id.argtypes = []
+        built, want = L.moe_build_id().decode(), _build.source_hash()
+        if built != want:
+            raise RuntimeError(f"{LIB_PATH} was built from other sources (build id {built[:16]}, sources "
+                               f"{want[:16]}): rebuild it with `python -m quantized_moe_bit_amd.build`")
         vp, i32, st = C.c_void_p, C.c_int32, C.c_int
         sig = {
             "moe_layer_create": (st, [C.POINTER(moe_dims), C.POINTER(moe_weights), C.c_uint32, C.POINTER(vp)]),
@@ -62,6 +76,7 @@ def lib() -> C.CDLL:
             "moe_route": (st, [vp, vp, i32, vp, vp, vp, vp, vp, vp]),
             "moe_forward_decode": (st, [vp, vp, i32, vp, vp]),
             "moe_forward_prefill": (st, [vp, vp, i32, vp, vp]),
+            "moe_last_routing": (st, [vp, i32, vp, vp, vp]),
             "moe_stack_glue": (st, [vp, vp, vp, vp, vp, vp, i32, i32, vp]),
             "moe_stack_forward_decode": (st, [C.POINTER(vp), i32, vp, i32, vp, vp, vp, vp]),
             "moe_packed_bytes": (C.c_size_t, [i32, i32, i32, i32, i32]),
@@ -153,6 +168,14 @@ def moe_forward_decode(handle, x, T, y, stream=None):
 
 def moe_forward_prefill(handle, x, T, y, stream=None):
     _check(lib().moe_forward_prefill(handle, _ptr(x), T, _ptr(y), _stream(stream)), "moe_forward_prefill")
+
+
+def moe_last_routing(handle, T, idx, w, stream=None):
+    _check(lib().moe_last_routing(handle, T, _ptr(idx), _ptr(w), _stream(stream)), "moe_last_routing")
+
+
+def moe_build_id() -> str:
+    return lib().moe_build_id().decode()
 
 
 def moe_stack_glue(h, y, h_next, x_next, T, d, stream=None, post=None, scalar=None):

@@ -4,12 +4,14 @@
 // "Prefill"); each expert's rows then form one dense GEMM against its 4-bit
 // group-64 affine weights. The Mference design unpacks an affine tile into bounded
 // FP16 staging and hands it to a matrix unit ("Prefill"; "Metal execution"); here each
-// wave turns its codes into fp16 MFMA operands in registers, w = fp16(scale * q + bias)
-// with one packed fp16 fma per two weights (a single rounding of the exact value; exact
-// whenever the value fits fp16's 11 significant bits, as it does for bf16 scales and biases
-// of like magnitude). The activations are fp16 too (x converted exactly from bf16 by the
-// router; the hidden activation h = gelu(g) * u is carried in fp16), and
-// v_mfma_f32_32x32x16_f16 accumulates in fp32 across all groups.
+// wave turns its codes into fp16 MFMA operands in registers: with a power-of-two
+// exponent m per matrix (chosen from the matrix's largest |scale|, see k_stage_shift), the
+// staged weight is fp16(2^m (scale * q + bias)), formed by one packed fp16 fma per two
+// weights (a single rounding of the exact value, 11 significant bits for scales of any
+// magnitude), and the fp32 accumulators are scaled back by 2^-m (exact). The activations
+// are fp16 too (x converted exactly from bf16 by the router; the hidden activation
+// h = gelu(g) * u is carried in fp16), and v_mfma_f32_32x32x16_f16 accumulates in fp32
+// across all groups.
 //
 // Work items: (expert or shared, 128-row tile, output tile), one per workgroup; all output
 // tiles of a row tile run on the same XCD (workgroup i runs on XCD i % 8), so the row tile
@@ -210,30 +212,18 @@ struct PreArgs {
     // expert tiles: routed items whose expert has no slot are skipped (not faults), and the
     // shared items run only with shared set
     int tile_mode, shared;
+    const int32_t *shift;       // fp16 staging exponents: [kind * n_mats + matrix], shared at [3 n_mats + kind]
+    int n_mats;
 };
 
-// Eight fp16 weights scale * q + bias from one device-layout word (elements j = 0..7 of a
-// K-step; element j in nibble j even ? j/2 : 4 + j/2). Pair p (elements 2p, 2p + 1) is
-// nibbles p and 4 + p: (w >> 4p) & 0x000F000F | 0x6400 gives fp16 1024 + q (exact), minus
-// 1024 gives q, and one packed fma gives fp16(s q + b), rounded once.
+// Eight staged weights fp16(2^m (s q + b)) from one device-layout word (elements j = 0..7 of
+// a K-step; element j in nibble j even ? j/2 : 4 + j/2), given s2 = fp16(2^(20+m) s) and
+// b2 = fp16(2^m b) in both halves: the nibbles of pair p (elements 2p, 2p + 1 are nibbles p and
+// 4 + p), moved to bits 4..7 of each 16-bit half, are the fp16 subnormals q 2^-20 (exact), and
+// one packed fma gives fp16(q 2^-20 s2 + b2), rounded once. k_stage_shift chooses m so that
+// 2^(20+m) |s| < 2^16 for every scale of the matrix (s2 is then the exact scale, or for a scale
+// below 2^-29 of the largest an fp16 subnormal within 2^-24 of it).
 __device__ __forceinline__ f16x8_t dequant_frag(uint32_t w, f16x2_t s2, f16x2_t b2) {
-    const f16x2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-    u32x4_t r;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t t = and_or(p == 0 ? w : w >> (4 * p), 0x000F000Fu, 0x64006400u);
-        const f16x2_t q = __builtin_bit_cast(f16x2_t, t) - k1024;
-        r[p] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
-    }
-    return __builtin_bit_cast(f16x8_t, r);
-}
-
-// The same eight weights when every scale s of the matrix satisfies 2^-34 <= |s| < 2^-4 (or
-// s = 0): the nibbles of pair p, moved to bits 4..7 of each 16-bit half, are the fp16
-// subnormals q 2^-20 (exact), and one packed fma with the fp16 scale 2^20 s (exact: a normal
-// fp16 value in that range) gives fp16(s q + b), rounded once -- the same value as
-// dequant_frag with two fewer instructions per word.
-__device__ __forceinline__ f16x8_t dequant_frag_sub(uint32_t w, f16x2_t s2, f16x2_t b2) {
     const uint32_t m = 0x00F000F0u;
     const uint32_t t[4] = {(w << 4) & m, w & m, (w >> 4) & m, (w >> 8) & m};
     u32x4_t r;
@@ -243,17 +233,61 @@ __device__ __forceinline__ f16x8_t dequant_frag_sub(uint32_t w, f16x2_t s2, f16x
     return __builtin_bit_cast(f16x8_t, r);
 }
 
-// Scale-range check for dequant_frag_sub: *bad |= 1 if any scale/bias word of the matrix has
-// a nonzero scale outside [2^-34, 2^-4) (bf16 magnitude bits outside [0x2E80, 0x3D80); NaN and
-// infinity included). grid ceil(n / 256); block 256
-__global__ __launch_bounds__(256) void k_scale_range(const uint32_t *__restrict__ sb, size_t n, int32_t *__restrict__ bad) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
-    const uint32_t m = sb[i] & 0x7FFFu;
-    if (m != 0 && (m < 0x2E80u || m >= 0x3D80u)) atomicOr(bad, 1);
+// fp16 staging exponent of one matrix. grid (n_mats + 1, 3): x = routed matrix (expert or
+// slot, when routed is set; x = n_mats: the shared expert, when shared is set), y = kind
+// (gate, up, down);
+// block 256. With e the bf16 exponent field of the matrix's largest |scale| (its value lies in
+// [2^(e-127), 2^(e-126))), m = 122 - e puts that scale times 2^m in [2^-5, 2^-4): every scale
+// times 2^(20+m) is then below 2^16 (an fp16 value), and every staged weight below
+// 1 + 2^m |bias|. A matrix whose scales are all zero takes m from its largest |bias|, placed in
+// [2^14, 2^15). The matrix cannot be staged (m = 0, *faults += 1) if a scale or bias is NaN or
+// infinite, m lies outside [-64, 64], or 2^m |bias| can reach 2^15.
+struct StageArgs {
+    const uint32_t *sb[3];      // routed gate, up, down scale/bias words (n_mats matrices each)
+    const uint32_t *sb_sh[3];   // shared gate, up, down
+    int words[3], words_sh[3];  // words per matrix
+    int n_mats, routed, shared;
+    int32_t *shift, *faults;
+};
+__global__ __launch_bounds__(256) void k_stage_shift(StageArgs a) {
+    const int kind = blockIdx.y, mat = blockIdx.x;
+    const bool sh = mat == a.n_mats;
+    if (sh ? !a.shared : !a.routed) return;
+    const int n = sh ? a.words_sh[kind] : a.words[kind];
+    const uint32_t *w = sh ? a.sb_sh[kind] : a.sb[kind] + (size_t)mat * n;
+    uint32_t smax = 0, bmax = 0;
+    for (int i = threadIdx.x; i < n / 4; i += 256) {
+        const u32x4_t v = ld16(w + 4 * i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            smax = max(smax, v[j] & 0x7FFFu);
+            bmax = max(bmax, (v[j] >> 16) & 0x7FFFu);
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        smax = max(smax, (uint32_t)__shfl_xor((int)smax, off));
+        bmax = max(bmax, (uint32_t)__shfl_xor((int)bmax, off));
+    }
+    __shared__ uint32_t red[2][4];
+    if ((threadIdx.x & 63) == 0) {
+        red[0][threadIdx.x >> 6] = smax;
+        red[1][threadIdx.x >> 6] = bmax;
+    }
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    smax = max(max(red[0][0], red[0][1]), max(red[0][2], red[0][3]));
+    bmax = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3]));
+    const int es = (int)(smax >> 7), eb = (int)(bmax >> 7);
+    int m = smax ? 122 - es : (bmax ? 141 - eb : 0);
+    const bool bad = smax >= 0x7F80u || bmax >= 0x7F80u || m < -64 || m > 64 || (bmax && eb + m > 141);
+    if (bad) {
+        atomicAdd(a.faults, 1);
+        m = 0;
+    }
+    a.shift[sh ? 3 * a.n_mats + kind : kind * a.n_mats + mat] = m;
 }
 
-template <int MODE, bool SUB>  // MODE 0: gate/up + GeGLU, 1: down; SUB: dequant_frag_sub
+template <int MODE>  // MODE 0: gate/up + GeGLU, 1: down
 __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
     __shared__ __align__(16) uint8_t smem[kSmemBytes];
 
@@ -347,6 +381,18 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
         St0 = static_cast<const uint8_t *>(uniform_ptr(St0));
         St1 = static_cast<const uint8_t *>(uniform_ptr(St1));
     }
+    // fp16 staging exponents of the wave's two code tiles (gate/up: gate and up; down: down twice):
+    // scale and bias words are multiplied by 2^(20+m) and 2^m before the fp16 conversion, the
+    // accumulators by 2^-m after the K loop
+    float fS[2], fB[2], fR[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int kind = MODE == 0 ? t : 2;
+        const int m = a.shift[shared_item ? 3 * a.n_mats + kind : kind * a.n_mats + e];
+        fS[t] = __builtin_ldexpf(1.0f, 20 + m);
+        fB[t] = __builtin_ldexpf(1.0f, m);
+        fR[t] = __builtin_ldexpf(1.0f, -m);
+    }
     const uint32_t boff = lane * 16, soff = n * 4;
     // A rows this thread moves: chunk i covers rows 8 (4 i + wave) .. +7, lane -> row
     // + lane/8 at physical chunk lane%8 (byte offsets from the buffer start). Padding rows
@@ -378,7 +424,7 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
             bw[t] = ld16(smem + kBRingOff + sbi * kBStageBytes + wave * 2048 + t * 1024 + lane * 16);
             const uint32_t sbw =
                 *reinterpret_cast<const uint32_t *>(smem + kSRingOff + sbi * kSStageBytes + wave * 512 + t * 256 + lane * 4);
-            const float sc = bf16_to_f32(sbw & 0xFFFFu) * (SUB ? 1048576.0f : 1.0f), bi = bf16_to_f32(sbw >> 16);
+            const float sc = bf16_to_f32(sbw & 0xFFFFu) * fS[t], bi = bf16_to_f32(sbw >> 16) * fB[t];
             s2[t] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(sc, sc));
             b2[t] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(bi, bi));
         }
@@ -429,7 +475,7 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
 #pragma unroll
                 for (int ms = 0; ms < LMS; ++ms) af[0][ms] = ld16(sA + aoff[0] + 4096 * ms);
 #pragma unroll
-                for (int t = 0; t < 2; ++t) bf[0][t] = SUB ? dequant_frag_sub(bw[t][0], s2[t], b2[t]) : dequant_frag(bw[t][0], s2[t], b2[t]);
+                for (int t = 0; t < 2; ++t) bf[0][t] = dequant_frag(bw[t][0], s2[t], b2[t]);
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     if (s < 3) {
@@ -437,8 +483,7 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
                         for (int ms = 0; ms < LMS; ++ms) af[(s + 1) & 1][ms] = ld16(sA + aoff[s + 1] + 4096 * ms);
 #pragma unroll
                         for (int t = 0; t < 2; ++t)
-                            bf[(s + 1) & 1][t] = SUB ? dequant_frag_sub(bw[t][s + 1], s2[t], b2[t])
-                                                     : dequant_frag(bw[t][s + 1], s2[t], b2[t]);
+                            bf[(s + 1) & 1][t] = dequant_frag(bw[t][s + 1], s2[t], b2[t]);
                     }
 #pragma unroll
                     for (int ms = 0; ms < LMS; ++ms)
@@ -494,7 +539,8 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int row = 32 * ms + 8 * (v >> 2) + 4 * half + (v & 3);
-                        Hw[row * kHPitch + n] = (uint16_t)f32_to_f16_sat(gelu_tanh_f32(acc[ms][0][v]) * acc[ms][1][v]);
+                        Hw[row * kHPitch + n] =
+                            (uint16_t)f32_to_f16_sat(gelu_tanh_f32(acc[ms][0][v] * fR[0]) * (acc[ms][1][v] * fR[1]));
                     }
                 }
             }
@@ -528,7 +574,7 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
 #pragma unroll
                             for (int v = 0; v < 16; ++v) {
                                 const int row = 32 * mh + 8 * (v >> 2) + 4 * half + (v & 3);
-                                O[row * kOPitch + wave * 64 + t * 32 + n] = acc[2 * part + mh][t][v];
+                                O[row * kOPitch + wave * 64 + t * 32 + n] = acc[2 * part + mh][t][v] * fR[t];
                             }
                 }
                 __syncthreads();
@@ -599,6 +645,8 @@ PreArgs make_args(const moe_layer *L, int T) {
     a.slot_faults = L->ws.slot_faults;
     a.tile_mode = 0;
     a.shared = 1;
+    a.shift = L->ws.shift;
+    a.n_mats = L->n_mats;
     return a;
 }
 
@@ -614,16 +662,26 @@ int pre_grid(const moe_layer *L, int T, int mode) {
 
 }  // namespace
 
-hipError_t launch_scale_check(const moe_layer *L, int32_t *flag, hipStream_t s) {
+hipError_t launch_stage_shift(const moe_layer *L, bool routed, bool shared, int32_t *faults, hipStream_t s) {
     const moe_dims &D = L->dims;
-    const size_t E = D.n_experts, d = D.d_model, I = D.d_expert, Is = D.d_shared;
-    hipError_t err = hipMemsetAsync(flag, 0, sizeof(int32_t), s);
-    if (err != hipSuccess) return err;
-    const struct { const uint32_t *sb; size_t n; } mats[6] = {
-        {L->w.gate.sb, E * I * (d / 64)},     {L->w.up.sb, E * I * (d / 64)},  {L->w.down.sb, E * d * (I / 64)},
-        {L->w.sh_gate.sb, Is * (d / 64)},     {L->w.sh_up.sb, Is * (d / 64)},  {L->w.sh_down.sb, d * (Is / 64)}};
-    for (const auto &m : mats)
-        launch(k_scale_range, dim3((unsigned)((m.n + 255) / 256)), dim3(256), 0, s, m.sb, m.n, flag);
+    const int d = D.d_model, I = D.d_expert, Is = D.d_shared;
+    StageArgs a{};
+    a.sb[0] = L->w.gate.sb;
+    a.sb[1] = L->w.up.sb;
+    a.sb[2] = L->w.down.sb;
+    a.sb_sh[0] = L->w.sh_gate.sb;
+    a.sb_sh[1] = L->w.sh_up.sb;
+    a.sb_sh[2] = L->w.sh_down.sb;
+    a.words[0] = a.words[1] = I * (d / 64);
+    a.words[2] = d * (I / 64);
+    a.words_sh[0] = a.words_sh[1] = Is * (d / 64);
+    a.words_sh[2] = d * (Is / 64);
+    a.n_mats = L->n_mats;
+    a.routed = routed;
+    a.shared = shared;
+    a.shift = L->ws.shift;
+    a.faults = faults;
+    launch(k_stage_shift, dim3(L->n_mats + 1, 3), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -632,10 +690,7 @@ hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipSt
     PreArgs a = make_args(L, T);
     a.tile_mode = tile >= 0;
     a.shared = tile <= 0;
-    if (L->pre_sub)
-        launch(k_pre_gemm<0, true>, dim3(pre_grid(L, T, 0)), dim3(kPreWG), 0, s, a);
-    else
-        launch(k_pre_gemm<0, false>, dim3(pre_grid(L, T, 0)), dim3(kPreWG), 0, s, a);
+    launch(k_pre_gemm<0>, dim3(pre_grid(L, T, 0)), dim3(kPreWG), 0, s, a);
     return hipGetLastError();
 }
 
@@ -643,10 +698,7 @@ hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s, int tile) {
     PreArgs a = make_args(L, T);
     a.tile_mode = tile >= 0;
     a.shared = tile <= 0;
-    if (L->pre_sub)
-        launch(k_pre_gemm<1, true>, dim3(pre_grid(L, T, 1)), dim3(kPreWG), 0, s, a);
-    else
-        launch(k_pre_gemm<1, false>, dim3(pre_grid(L, T, 1)), dim3(kPreWG), 0, s, a);
+    launch(k_pre_gemm<1>, dim3(pre_grid(L, T, 1)), dim3(kPreWG), 0, s, a);
     return hipGetLastError();
 }
 

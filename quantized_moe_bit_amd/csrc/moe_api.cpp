@@ -39,8 +39,8 @@ moe_status check_dims(const moe_dims *D) {
     if (D->group != 64) return fail(MOE_E_QUANT, "group must be 64, got %d", D->group);
     if (D->router_bits != 8) return fail(MOE_E_QUANT, "router_bits must be 8, got %d", D->router_bits);
     if (D->expert_bits != 4) return fail(MOE_E_QUANT, "expert_bits must be 4, got %d", D->expert_bits);
-    if (D->d_model < 64 || D->d_model % 128 || D->d_model > 8192)
-        return fail(MOE_E_SHAPE, "d_model %d must be a multiple of 128 in [128, 8192]", D->d_model);
+    if (D->d_model < 64 || D->d_model % 64 || D->d_model > 8192)
+        return fail(MOE_E_SHAPE, "d_model %d must be a multiple of 64 in [64, 8192]", D->d_model);
     if (D->d_expert < 64 || D->d_expert % 64)
         return fail(MOE_E_SHAPE, "d_expert %d must be a positive multiple of 64", D->d_expert);
     if (D->d_shared < 64 || D->d_shared % 64)
@@ -177,6 +177,37 @@ moe_status run(moe_layer *L, int id, hipStream_t s, F &&f) {
         if (_st != MOE_OK) return _st;                             \
     } while (0)
 
+// MOE_FLAG_CHECK_FINITE: the number of NaN / infinite values among n values at p (bf16, or fp32
+// with f32), counted on the stream and read back (the stream is synchronized). MOE_E_NONFINITE
+// when there are any.
+moe_status check_finite(moe_layer *L, const void *p, size_t n, bool f32, hipStream_t s, const char *what) {
+    int32_t cnt = 0;
+    hipError_t err = hipMemsetAsync(L->ws.flag, 0, sizeof(int32_t), s);
+    if (err == hipSuccess) err = launch_count_nonfinite(p, n, f32, L->ws.flag, s);
+    if (err == hipSuccess) err = hipMemcpyAsync(&cnt, L->ws.flag, sizeof(cnt), hipMemcpyDeviceToHost, s);
+    if (err == hipSuccess) err = hipStreamSynchronize(s);
+    if (err != hipSuccess) return fail(MOE_E_DEVICE, "%s: finite check: %s", what, hipGetErrorString(err));
+    if (cnt) return fail(MOE_E_NONFINITE, "%s: %d NaN or infinite %s values", what, cnt, f32 ? "output" : "input");
+    return MOE_OK;
+}
+
+#define CHECK_FINITE(p, n, f32, what)                                               \
+    do {                                                                            \
+        if (L->flags & MOE_FLAG_CHECK_FINITE) {                                     \
+            moe_status _st = check_finite(L, (p), (size_t)(n), (f32), s, (what));   \
+            if (_st != MOE_OK) return _st;                                          \
+        }                                                                           \
+    } while (0)
+
+// Routed experts of a layer with expert slots: the fp16 staging exponents of the matrices now in
+// the slots (they are filled after creation), with unstageable ones counted as slot faults.
+moe_status slot_stage_shift(moe_layer *L, hipStream_t s) {
+    if (!L->w.expert_slot) return MOE_OK;
+    hipError_t err = launch_stage_shift(L, true, false, L->ws.slot_faults, s);
+    if (err != hipSuccess) return fail(MOE_E_DEVICE, "kernel stage_shift: %s", hipGetErrorString(err));
+    return MOE_OK;
+}
+
 // The router's input: x itself, or the router prologue's output (which also writes what the
 // router would have derived from x: the fp16 copy for prefill, the group sums for decode).
 moe_status router_input(moe_layer *L, const uint16_t *x, int T, bool for_prefill, hipStream_t s, const uint16_t **u) {
@@ -225,11 +256,17 @@ const char *moe_status_str(moe_status s) {
         case MOE_E_CAPACITY: return "MOE_E_CAPACITY";
         case MOE_E_NOMEM: return "MOE_E_NOMEM";
         case MOE_E_DEVICE: return "MOE_E_DEVICE";
+        case MOE_E_NONFINITE: return "MOE_E_NONFINITE";
     }
     return "MOE_E_UNKNOWN";
 }
 
 const char *moe_last_error(void) { return g_err; }
+
+#ifndef QMOE_SOURCE_HASH
+#define QMOE_SOURCE_HASH "unknown"
+#endif
+const char *moe_build_id(void) { return QMOE_SOURCE_HASH; }
 
 const char *moe_kernel_name(int32_t id) { return (id >= 0 && id < K_COUNT) ? kKernelNames[id] : nullptr; }
 
@@ -239,12 +276,17 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     moe_status st = check_dims(dims);
     if (st != MOE_OK) return st;
     if ((st = check_weights(w)) != MOE_OK) return st;
-    if (flags != 0) return fail(MOE_E_INVALID, "unknown flags 0x%x", flags);
+    if (flags & ~(MOE_FLAG_CHECK_FINITE | MOE_FLAG_WS_BUDGET_MIB(0xFFFFFFu)))
+        return fail(MOE_E_INVALID, "unknown flags 0x%x", flags);
 
     moe_layer *L = new (std::nothrow) moe_layer();
     if (!L) return fail(MOE_E_NOMEM, "host allocation failed");
     L->dims = *dims;
     L->w = *w;
+    L->flags = flags;
+    L->routed_T = -1;
+    L->last_T = -1;
+    L->n_mats = w->expert_slot ? w->n_slots : dims->n_experts;
     L->prof_on = false;
     for (int i = 0; i < K_COUNT; ++i) {
         L->prof_ms[i] = 0.0;
@@ -282,12 +324,20 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.slot_faults, 1);
     plan.take(&ws.rqf, router_table_floats(D));
     plan.take(&ws.flag, 1);
+    plan.take(&ws.shift, 3 * (size_t)L->n_mats + 3);
     plan.take(&ws.dxg, dec_workspace_floats(D, L->max_dec, 0));
     plan.take(&ws.dh_r, 2 * dec_workspace_floats(D, L->max_dec, 1));
     plan.take(&ws.dh_s, 2 * dec_workspace_floats(D, L->max_dec, 2));
     plan.take(&ws.dhs_r, dec_workspace_floats(D, L->max_dec, 3));
     plan.take(&ws.dhs_s, dec_workspace_floats(D, L->max_dec, 4));
     L->ws_bytes = (plan.off + 255) & ~size_t(255);
+    const uint64_t budget_mib = flags >> 8;
+    if (budget_mib && L->ws_bytes > (budget_mib << 20)) {
+        const size_t need = L->ws_bytes;
+        delete L;
+        return fail(MOE_E_NOMEM, "workspace of %zu bytes exceeds the budget of %llu MiB", need,
+                    (unsigned long long)budget_mib);
+    }
 
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
@@ -307,19 +357,24 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     err = hipMemset(L->ws_base, 0, L->ws_bytes);
     // derived bias-term tables of the prefill GEMMs (read from the borrowed scale/bias words)
     if (err == hipSuccess) err = launch_router_table(L, nullptr);
-    // the prefill GEMMs take the subnormal-code dequantization when every expert scale allows it
-    // (not with expert slots: the routed arrays then hold n_slots experts, filled later)
-    int32_t bad = 1;
-    if (!w->expert_slot) {
-        if (err == hipSuccess) err = launch_scale_check(L, ws.flag, nullptr);
-        if (err == hipSuccess) err = hipMemcpy(&bad, ws.flag, sizeof(bad), hipMemcpyDeviceToHost);
-    }
-    L->pre_sub = err == hipSuccess && bad == 0;
+    // fp16 staging exponents of the prefill GEMMs, and the check that every expert matrix can be
+    // staged (routed ones of a layer with slots: at each prefill call, once the slots are filled)
+    int32_t bad = 0;
+    if (err == hipSuccess) err = launch_stage_shift(L, !w->expert_slot, true, ws.flag, nullptr);
+    if (err == hipSuccess) err = hipMemcpy(&bad, ws.flag, sizeof(bad), hipMemcpyDeviceToHost);
     if (err == hipSuccess) err = hipDeviceSynchronize();
     if (err != hipSuccess) {
         (void)hipFree(L->ws_base);
         delete L;
         return fail(MOE_E_DEVICE, "workspace init: %s", hipGetErrorString(err));
+    }
+    if (bad) {
+        (void)hipFree(L->ws_base);
+        delete L;
+        return fail(MOE_E_QUANT,
+                    "%d expert matrices have scales or biases the fp16 staging cannot carry (NaN or infinite, "
+                    "largest |scale| outside [2^-69, 2^59), or floor(log2 |bias|) >= floor(log2 max |scale|) + 20)",
+                    bad);
     }
     *out = L;
     return MOE_OK;
@@ -354,7 +409,9 @@ moe_status moe_route(moe_layer *L, const uint16_t *x, int32_t T, int32_t *topk_i
     if (expert_offsets && (!aligned16(expert_offsets) || !aligned16(pair_perm)))
         return fail(MOE_E_ALIGN, "moe_route: grouping outputs not 16-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    CHECK_FINITE(x, (size_t)T * L->dims.d_model, false, "moe_route");
     float *lg = logits ? logits : L->ws.logits;
+    L->routed_T = -1;   // the router and grouping kernels reuse the workspace of a routed chunk
     st = route_impl(L, x, T, s, lg, topk_idx, topk_w, expert_offsets != nullptr, pair_perm, false);
     if (st != MOE_OK) return st;
     if (expert_offsets) {
@@ -372,6 +429,9 @@ moe_status moe_forward_decode(moe_layer *L, const uint16_t *x, int32_t T, float 
     if (T > L->max_dec)
         return fail(MOE_E_CAPACITY, "moe_forward_decode: T = %d exceeds the decode capacity %d", T, L->max_dec);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    CHECK_FINITE(x, (size_t)T * L->dims.d_model, false, "moe_forward_decode");
+    L->routed_T = -1;
+    L->last_T = T;
     if (L->w.router_scale && dec_router_glue_fits(L->dims, T)) {
         RUN(K_DEC_ROUTER, launch_dec_router_pro(L, x, T, L->ws.logits, s));
     } else {
@@ -381,6 +441,7 @@ moe_status moe_forward_decode(moe_layer *L, const uint16_t *x, int32_t T, float 
     }
     RUN(K_DEC_GATEUP, launch_dec_gateup(L, x, T, s));
     RUN(K_DEC_DOWN, launch_dec_down(L, T, y, s));
+    CHECK_FINITE(y, (size_t)T * L->dims.d_model, true, "moe_forward_decode");
     return MOE_OK;
 }
 
@@ -389,11 +450,34 @@ moe_status moe_forward_prefill(moe_layer *L, const uint16_t *x, int32_t T, float
     moe_status st = check_call(L, x, T, y, "moe_forward_prefill");
     if (st != MOE_OK || T == 0) return st;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    CHECK_FINITE(x, (size_t)T * L->dims.d_model, false, "moe_forward_prefill");
+    L->routed_T = T;
+    L->last_T = T;
     st = route_impl(L, x, T, s, L->ws.logits, L->ws.idx, L->ws.wts, true, nullptr, true);
     if (st != MOE_OK) return st;
+    if ((st = slot_stage_shift(L, s)) != MOE_OK) return st;
     RUN(K_PRE_GATEUP, launch_pre_gateup(L, x, T, s));
     RUN(K_PRE_DOWN, launch_pre_down(L, T, s));
     RUN(K_COMBINE, launch_combine(L, T, y, s));
+    CHECK_FINITE(y, (size_t)T * L->dims.d_model, true, "moe_forward_prefill");
+    return MOE_OK;
+}
+
+moe_status moe_last_routing(moe_layer *L, int32_t T, int32_t *idx, float *w, void *hip_stream) {
+    clear_error();
+    if (!L) return fail(MOE_E_INVALID, "moe_last_routing: layer is NULL");
+    if (T < 0) return fail(MOE_E_SHAPE, "moe_last_routing: T = %d is negative", T);
+    if (L->last_T < 0) return fail(MOE_E_INVALID, "moe_last_routing: no forward call has run on the layer");
+    if (T > L->last_T)
+        return fail(MOE_E_INVALID, "moe_last_routing: T = %d exceeds the last call's %d tokens", T, L->last_T);
+    if (T == 0) return MOE_OK;
+    if (!idx || !w) return fail(MOE_E_INVALID, "moe_last_routing: NULL output");
+    if (!aligned16(idx) || !aligned16(w)) return fail(MOE_E_ALIGN, "moe_last_routing: output not 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const size_t n = (size_t)T * L->dims.top_k;
+    hipError_t err = hipMemcpyAsync(idx, L->ws.idx, n * sizeof(int32_t), hipMemcpyDeviceToDevice, s);
+    if (err == hipSuccess) err = hipMemcpyAsync(w, L->ws.wts, n * sizeof(float), hipMemcpyDeviceToDevice, s);
+    if (err != hipSuccess) return fail(MOE_E_DEVICE, "moe_last_routing: %s", hipGetErrorString(err));
     return MOE_OK;
 }
 
@@ -434,10 +518,19 @@ moe_status moe_stack_forward_decode(moe_layer *const *layers, int32_t n_layers, 
         return fail(MOE_E_ALIGN, "moe_stack_forward_decode: buffer not 16-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const int d = layers[0]->dims.d_model;
+    moe_layer *check = nullptr;   // a layer created with MOE_FLAG_CHECK_FINITE: its flag workspace counts
+    for (int l = 0; l < n_layers; ++l)
+        if (layers[l]->flags & MOE_FLAG_CHECK_FINITE) check = layers[l];
+    if (check) {
+        moe_status st = check_finite(check, h, (size_t)T * d, false, s, "moe_stack_forward_decode");
+        if (st != MOE_OK) return st;
+    }
     // the residual stream alternates between h and h_buf: layer l reads the stream before it
     // from one and leaves the stream after the previous layer's residual add in the other
     for (int l = 0; l < n_layers; ++l) {
         moe_layer *L = layers[l];
+        L->routed_T = -1;
+        L->last_T = T;
         uint16_t *src = (l & 1) ? h_buf : h, *dst = (l & 1) ? h : h_buf;
         const float *yp = l ? y_buf : nullptr;
         // the previous layer's tail goes with its output y into this layer's residual step
@@ -460,6 +553,10 @@ moe_status moe_stack_forward_decode(moe_layer *const *layers, int32_t n_layers, 
         uint16_t *src = ((n_layers - 1) & 1) ? h : h_buf;
         RUN(K_GLUE, launch_glue(src, y_buf, L->w.post_ffn_norm, L->w.layer_scalar, h, x_buf, T, d, s));
     }
+    if (check) {
+        moe_status st = check_finite(check, h, (size_t)T * d, false, s, "moe_stack_forward_decode");
+        if (st != MOE_OK) return st;
+    }
     return MOE_OK;
 }
 
@@ -469,7 +566,12 @@ moe_status moe_prefill_route(moe_layer *L, const uint16_t *x, int32_t T, int32_t
     if (st != MOE_OK || T == 0) return st;
     if (!x) return fail(MOE_E_INVALID, "moe_prefill_route: x is NULL");
     if (!aligned16(x)) return fail(MOE_E_ALIGN, "moe_prefill_route: x not 16-byte aligned");
+    if (expert_counts && !aligned16(expert_counts))
+        return fail(MOE_E_ALIGN, "moe_prefill_route: expert_counts not 16-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    CHECK_FINITE(x, (size_t)T * L->dims.d_model, false, "moe_prefill_route");
+    L->routed_T = T;
+    L->last_T = T;
     st = route_impl(L, x, T, s, L->ws.logits, L->ws.idx, L->ws.wts, true, nullptr, true);
     if (st != MOE_OK) return st;
     if (expert_counts) {
@@ -487,7 +589,10 @@ moe_status moe_prefill_tile(moe_layer *L, int32_t T, int32_t tile, void *hip_str
     if (!L->w.expert_slot) return fail(MOE_E_INVALID, "moe_prefill_tile: the layer has no expert slots");
     if (tile < 0) return fail(MOE_E_INVALID, "moe_prefill_tile: tile = %d is negative", tile);
     if (T == 0) return MOE_OK;
+    if (L->routed_T != T)
+        return fail(MOE_E_INVALID, "moe_prefill_tile: T = %d is not the routed chunk's (%d; -1: none)", T, L->routed_T);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    if ((st = slot_stage_shift(L, s)) != MOE_OK) return st;
     RUN(K_PRE_GATEUP, launch_pre_gateup(L, nullptr, T, s, tile));
     RUN(K_PRE_DOWN, launch_pre_down(L, T, s, tile));
     return MOE_OK;
@@ -499,8 +604,12 @@ moe_status moe_prefill_combine(moe_layer *L, int32_t T, float *y, void *hip_stre
     if (st != MOE_OK || T == 0) return st;
     if (!y) return fail(MOE_E_INVALID, "moe_prefill_combine: y is NULL");
     if (!aligned16(y)) return fail(MOE_E_ALIGN, "moe_prefill_combine: y not 16-byte aligned");
+    if (L->routed_T != T)
+        return fail(MOE_E_INVALID, "moe_prefill_combine: T = %d is not the routed chunk's (%d; -1: none)", T,
+                    L->routed_T);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     RUN(K_COMBINE, launch_combine(L, T, y, s));
+    CHECK_FINITE(y, (size_t)T * L->dims.d_model, true, "moe_prefill_combine");
     return MOE_OK;
 }
 

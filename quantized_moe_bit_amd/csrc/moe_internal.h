@@ -75,7 +75,9 @@ struct Workspace {
     float *sgate;         // [maxT]             decode: shared-expert gate values (layers with a gate)
     int32_t *slot_faults; // [1]                absent expert slots the kernels met (layers with slots)
     float *rqf;           // router weights fma(scale, q, bias) as fp32 (prefill router table)
-    int32_t *flag;        // [1]                layer-creation checks
+    int32_t *flag;        // [1]                layer-creation checks, non-finite counts
+    int32_t *shift;       // [3 n_mats + 3]     fp16 staging exponents of the prefill GEMMs: routed
+                          //                    gate, up, down (kind * n_mats + matrix), then shared
     // decode path (D = decode capacity, KSd/KSs = input pieces of d / of I_s)
     float *dxg;           // [D, d/64]          decode: group sums of x
     uint16_t *dh_r;       // [D*k, I]           decode: routed hidden activations, fp16 bits
@@ -97,7 +99,10 @@ struct moe_layer {
     int device;
     int G_d, G_I, G_Is;        // groups along d, I, I_s
     int max_dec;               // decode capacity = min(max_tokens, MOE_MAX_DECODE_TOKENS)
-    bool pre_sub;              // prefill dequantization through fp16 subnormal codes (expert scales in range)
+    int n_mats;                // routed matrices per kind in the weight arrays (experts, or slots)
+    uint32_t flags;            // MOE_FLAG_* of the creation
+    int routed_T;              // tokens of the chunk whose routing and grouping the workspace holds (-1: none)
+    int last_T;                // tokens of the last call whose top-k ws.idx / ws.wts hold (-1: none)
     void *ws_base;
     size_t ws_bytes;
     qmoe::Workspace ws;
@@ -159,7 +164,12 @@ hipError_t launch_dec_down(const moe_layer *L, int T, float *y, hipStream_t s);
 size_t dec_gateup_lds(const moe_dims &D);
 size_t dec_down_lds(const moe_dims &D);
 size_t dec_workspace_floats(const moe_dims &D, int max_dec, int which);
-hipError_t launch_scale_check(const moe_layer *L, int32_t *flag, hipStream_t s);
+// fp16 staging exponents of the prefill GEMMs (ws.shift) from the scale/bias words of the
+// routed matrices (routed) and of the shared expert (shared). Matrices that cannot be staged
+// add to *faults.
+hipError_t launch_stage_shift(const moe_layer *L, bool routed, bool shared, int32_t *faults, hipStream_t s);
+// *count += the number of NaN / infinite values among n bf16 (f32: fp32) values at p
+hipError_t launch_count_nonfinite(const void *p, size_t n, bool f32, int32_t *count, hipStream_t s);
 // tile: -1 for a whole chunk; otherwise the index of an expert tile of a chunk (routed items
 // whose expert has no slot are skipped; the shared expert runs with tile 0 only)
 hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s, int tile = -1);

@@ -19,9 +19,10 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
 class DeviceLayer:
     """One MoE layer resident on a GPU. `layer` is a canonical-layout synth.Layer."""
 
-    def __init__(self, layer, max_tokens: int, device="cuda:0", n_slots: Optional[int] = None):
+    def __init__(self, layer, max_tokens: int, device="cuda:0", n_slots: Optional[int] = None, flags: int = 0):
         """n_slots: keep the routed experts in that many slots (expert slot cache): every
-        expert's device-layout bytes stay in pinned host memory and `ensure` fills slots."""
+        expert's device-layout bytes stay in pinned host memory and `ensure` fills slots.
+        flags: MOE_FLAG_* of moe_layer_create."""
         self.dims_py = layer.dims
         self.device = torch.device(device)
         D = layer.dims
@@ -70,7 +71,7 @@ class DeviceLayer:
         self.dims = B.moe_dims(D.d_model, D.n_experts, D.top_k, D.d_expert, D.d_shared, D.group, D.router_bits,
                                D.expert_bits, max_tokens)
         self.max_tokens = max_tokens
-        self.handle = B.moe_layer_create(self.dims, w, 0)
+        self.handle = B.moe_layer_create(self.dims, w, flags)
 
     def replicate(self) -> "DeviceLayer":
         """A copy of this layer in fresh device memory (same values, new addresses, new handle)."""

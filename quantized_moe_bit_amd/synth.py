@@ -72,6 +72,8 @@ QWEN = Dims(d_model=2048, n_experts=256, top_k=8, d_expert=512, d_shared=512)
 
 WORKLOADS: Dict[str, Workload] = {
     "tiny": Workload("tiny", TINY, tokens=4, seed=0, router="uniform"),
+    # the same layer with the stated bias recipe (-8 * scale) applied to the 8-bit router as written
+    "tiny_literal": Workload("tiny_literal", TINY, tokens=4, seed=0, router="uniform_mid8"),
     "decode": Workload("decode", GEMMA, tokens=1, seed=1),
     "stack": Workload("stack", GEMMA, tokens=256, seed=2, layers=30),
     "prefill512": Workload("prefill512", GEMMA, tokens=512, seed=3, zipf_s=1.1),
@@ -114,18 +116,21 @@ def _rng(seed: int, *key: int) -> np.random.Generator:
     return np.random.default_rng(np.random.SeedSequence([seed, *key]))
 
 
-def uniform_qmat(rng: np.random.Generator, lead: tuple, out_dim: int, in_dim: int, bits: int) -> QMat:
-    """Uniform codes, scale ~ U(0.002, 0.02), bias = -mid*scale + N(0, 1e-3), mid = 2^(bits-1)."""
+def uniform_qmat(rng: np.random.Generator, lead: tuple, out_dim: int, in_dim: int, bits: int,
+                 mid: Optional[int] = None, scale_range=(0.002, 0.02)) -> QMat:
+    """Uniform codes, scale ~ U(scale_range), bias = -mid*scale + N(0, 1e-3) (noise scaled with the
+    scale range), mid = 2^(bits-1) unless given."""
     G = in_dim // GROUP
     nbytes = in_dim * bits // 8
     shape = lead + (out_dim, nbytes)
     n = int(np.prod(shape))
     # uniform bytes drawn as 64-bit words (an order of magnitude faster than per-byte draws)
     codes = rng.integers(0, 1 << 64, size=(n + 7) // 8, dtype=np.uint64).view(np.uint8)[:n].reshape(shape)
-    s = rng.random(size=lead + (out_dim, G), dtype=np.float32) * np.float32(0.018) + np.float32(0.002)
+    lo, hi = scale_range
+    s = rng.random(size=lead + (out_dim, G), dtype=np.float32) * np.float32(hi - lo) + np.float32(lo)
     s_bits = f32_to_bf16_bits(s)
-    mid = np.float32(1 << (bits - 1))
-    noise = rng.standard_normal(size=lead + (out_dim, G), dtype=np.float32) * np.float32(1e-3)
+    mid = np.float32(1 << (bits - 1) if mid is None else mid)
+    noise = rng.standard_normal(size=lead + (out_dim, G), dtype=np.float32) * np.float32(1e-3 * hi / 0.02)
     b = -mid * bf16_bits_to_f32(s_bits) + noise
     return QMat(codes, s_bits, f32_to_bf16_bits(b), bits, out_dim, in_dim)
 
@@ -178,6 +183,8 @@ def gen_layer(dims: Dims, seed: int, *, router: str = "normal", zipf_s: Optional
         rq = normal_router_qmat(_rng(seed, *key, 1), E, d)
     elif router == "uniform":
         rq = uniform_qmat(_rng(seed, *key, 1), (), E, d, dims.router_bits)
+    elif router == "uniform_mid8":
+        rq = uniform_qmat(_rng(seed, *key, 1), (), E, d, dims.router_bits, mid=8)
     else:
         raise ValueError(router)
     gate = uniform_qmat(_rng(seed, *key, 2), (E,), I, d, dims.expert_bits)

@@ -142,10 +142,34 @@ def test_create_rejects_null_misaligned_and_flags():
     L = B.lib()
     assert L.moe_layer_create(C.byref(_dims()), C.byref(_weights(null="down")), 0, C.byref(h)) == B.MOE_E_INVALID
     assert L.moe_layer_create(C.byref(_dims()), C.byref(_weights(align=4)), 0, C.byref(h)) == B.MOE_E_ALIGN
-    assert L.moe_layer_create(C.byref(_dims()), C.byref(_weights()), 1, C.byref(h)) == B.MOE_E_INVALID
+    for bad_flags in (0x2, 0x80, 0x4):   # bits other than MOE_FLAG_CHECK_FINITE and the budget field
+        assert L.moe_layer_create(C.byref(_dims()), C.byref(_weights()), bad_flags, C.byref(h)) == B.MOE_E_INVALID
     assert L.moe_layer_create(C.byref(_dims()), None, 0, C.byref(h)) == B.MOE_E_INVALID
     assert L.moe_layer_create(None, C.byref(_weights()), 0, C.byref(h)) == B.MOE_E_INVALID
     assert h.value is None
+
+
+@pytest.mark.parametrize("d_model", [192, 256])
+def test_workspace_budget_flag_refuses_before_allocating(d_model):
+    """A workspace above the flags' budget is MOE_E_NOMEM, decided on the host before any
+    allocation (no GPU here); d_model = 192 (a multiple of 64, not of 128) passes validation."""
+    h = C.c_void_p(0)
+    L = B.lib()
+    dims = _dims(d_model=d_model, max_tokens=4096)
+    for flags in (B.MOE_FLAG_WS_BUDGET_MIB(1), B.MOE_FLAG_WS_BUDGET_MIB(1) | B.MOE_FLAG_CHECK_FINITE):
+        assert L.moe_layer_create(C.byref(dims), C.byref(_weights()), flags, C.byref(h)) == B.MOE_E_NOMEM
+        assert "budget" in B.moe_last_error()
+    assert h.value is None
+
+
+def test_binding_refuses_a_library_built_from_other_sources(monkeypatch):
+    """The library carries a hash of the sources it was built from; a loader refuses a stale one."""
+    from quantized_moe_bit_amd import build as hb
+    assert B.moe_build_id() == hb.source_hash()
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(hb, "source_hash", lambda: "0" * 64)
+    with pytest.raises(RuntimeError, match="other sources"):
+        B.lib()
 
 
 def test_calls_reject_null_layer_and_bad_sizes():
@@ -169,6 +193,8 @@ def test_calls_reject_null_layer_and_bad_sizes():
     assert L.moe_prefill_route(None, None, 1, None, None) == B.MOE_E_INVALID
     assert L.moe_prefill_tile(None, 1, 0, None) == B.MOE_E_INVALID
     assert L.moe_prefill_combine(None, 1, None, None) == B.MOE_E_INVALID
+    assert L.moe_last_routing(None, 1, None, None, None) == B.MOE_E_INVALID
+    assert B.status_str(B.MOE_E_NONFINITE) == "MOE_E_NONFINITE"
     out = C.c_void_p()
     assert L.moe_slot_cache_create(8, 0, C.byref(out)) == B.MOE_E_SHAPE
     assert L.moe_slot_cache_create(0, 1, C.byref(out)) == B.MOE_E_SHAPE

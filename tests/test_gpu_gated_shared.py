@@ -1,13 +1,12 @@
 """GPU parity of the gated shared expert on a Qwen 3.6 style layer (Mference system design,
-"Scope and limitations": 256 routed experts per layer and a gated shared expert), through
-the C ABI.
+"Scope and limitations": Qwen 3.6 layers have 256 experts and a shared branch behind a
+gate), through the C ABI.
 
 Layer: d_model 2048, 256 experts, top-8, expert width 512, shared width 512, 8-bit g64
 router, 4-bit g64 experts, and a bf16 gate vector g: the shared branch is multiplied by
 sigmoid(g . x) per token. Same bar as the other parity tests: logits bit-identical, top-k
-and grouping bit-exact, outputs within max |err| <= 2e-3 * rms of the oracle. At the
-4096-token prefill size the routing is compared for every token and the outputs on a
-sample of tokens the oracle computes one by one.
+and grouping bit-exact, outputs within max |err| <= 2e-3 * rms of the oracle, on every
+token, including the 4096-token prefill chunk.
 """
 import numpy as np
 import pytest
@@ -77,7 +76,7 @@ def test_qwen_layer_prefill_and_decode():
     dl.close()
 
 
-def test_qwen_prefill_4096_sampled():
+def test_qwen_prefill_4096_all_tokens():
     wl = synth.WORKLOADS["qwen_prefill4096"]
     lay = synth.workload_layer(wl)
     x, tied, _ = synth.workload_tokens(wl, lay)
@@ -89,10 +88,14 @@ def test_qwen_prefill_4096_sampled():
     torch.cuda.synchronize()
     ref = oracle.route(lay, x)
     check_route(r, ref, "qwen T=4096")
-    rng = np.random.default_rng(4096)
-    sample = np.unique(np.concatenate([[0, T - 1], tied[:4], rng.choice(T, 10, replace=False)])).astype(np.int32)
-    y_ref = oracle.layer_tokens(lay, x, ref["idx"], ref["w"], sample)
-    check_close(y.cpu().numpy()[sample], y_ref, f"qwen prefill T=4096 ({len(sample)} sampled tokens)",
+    y_ref = np.empty((T, wl.dims.d_model), np.float64)
+    for c in range(0, T, 1024):   # the oracle on every token, in chunks (progress lines)
+        toks = np.arange(c, min(c + 1024, T), dtype=np.int32)
+        y_ref[toks] = oracle.layer_tokens(lay, x, ref["idx"], ref["w"], toks)
+        say(f"qwen T=4096 oracle tokens {c}..{toks[-1]}")
+    sample = np.unique(np.concatenate([[0, T - 1], tied[:4], np.arange(0, T, 97)])).astype(np.int32)
+    check_close(y.cpu().numpy(), y_ref, f"qwen prefill T=4096 (all tokens)")
+    check_close(y.cpu().numpy()[sample], y_ref[sample], f"qwen prefill T=4096 gate in effect ({len(sample)} tokens)",
                 ungated(lay, x, ref["idx"], ref["w"], sample))
     dl.close()
 

@@ -1,13 +1,14 @@
 """GPU parity of the 30-layer decode stack (2816-wide layers, distinct seeded weights per
 layer, 256 consecutive tokens, residual stream between layers), through the C ABI.
 
-Each layer is checked against the CPU oracle on the GPU's own input to that layer
-(teacher forcing) for a sample of the tokens: router top-k sets bit-exact, layer output
-within max |err| <= 2e-3 * rms, and the residual step (h + y, then the norm) bit-exact,
-both sides rounding the fp64 value once to bf16. The whole stack then runs one token at a
-time through moe_stack_forward_decode, and its final residual stream must equal, bit for
-bit, the layer-by-layer run on the sampled tokens (decode results do not depend on how
-many tokens share a call).
+Every layer is checked against the CPU oracle on the GPU's own input to that layer (teacher
+forcing) for all 256 tokens, run as 16-token decode calls: router top-k sets bit-exact (the
+decode launch's own selection, read back through moe_last_routing), layer output within
+max |err| <= 2e-3 * rms, and the residual step (h + y, then the norm) bit-exact, both sides
+rounding the fp64 value once to bf16. The whole stack then runs one token at a time through
+moe_stack_forward_decode, and its final residual stream must equal, bit for bit, the
+layer-by-layer run on every token (decode results do not depend on how many tokens share a
+call).
 """
 import numpy as np
 import pytest
@@ -21,6 +22,7 @@ from quantized_moe_bit_amd.device import DeviceLayer, tokens_to_device
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
+CALL = 16   # tokens per decode call (the decode path's capacity)
 
 
 def say(msg):
@@ -34,19 +36,18 @@ def bits(t: torch.Tensor) -> np.ndarray:
 def test_stack_30_layers_256_tokens():
     w = synth.WORKLOADS["stack"]
     D = w.dims
-    T, NL = w.tokens, w.layers
+    T, NL, k = w.tokens, w.layers, w.dims.top_k
     h0 = synth.gen_stack_tokens(D, T, w.seed)
-    rng = np.random.default_rng(2030)
-    sample = np.unique(np.concatenate([[0, 1, T - 1], rng.choice(T, 5, replace=False)])).astype(np.int64)
-    S = len(sample)
     dev = torch.device("cuda:0")
 
-    hs = tokens_to_device(h0[sample], dev)
+    hs = tokens_to_device(h0, dev)
     xs = torch.empty_like(hs)
-    ys = torch.empty((S, D.d_model), dtype=torch.float32, device=dev)
-    B.moe_stack_glue(hs, None, hs, xs, S, D.d_model)
+    ys = torch.empty((T, D.d_model), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    B.moe_stack_glue(hs, None, hs, xs, T, D.d_model)
     torch.cuda.synchronize()
-    hn_ref, xn_ref = oracle.stack_glue(h0[sample], None)
+    hn_ref, xn_ref = oracle.stack_glue(h0, None)
     np.testing.assert_array_equal(bits(hs), hn_ref)
     np.testing.assert_array_equal(bits(xs), xn_ref)
 
@@ -54,16 +55,19 @@ def test_stack_30_layers_256_tokens():
     worst = 0.0
     for l in range(NL):
         lay = synth.workload_layer(w, l)
-        dl = DeviceLayer(lay, max_tokens=16, device=dev)
+        dl = DeviceLayer(lay, max_tokens=CALL, device=dev)
         layers.append(dl)
         x_l = bits(xs)
-        r = dl.route(xs)
-        dl.decode(xs, ys)
+        for c in range(0, T, CALL):
+            dl.decode(xs[c:c + CALL], ys[c:c + CALL])
+            B.moe_last_routing(dl.handle, CALL, idx[c:c + CALL], wts[c:c + CALL])
         h_prev = bits(hs)
-        B.moe_stack_glue(hs, ys, hs, xs, S, D.d_model)
+        B.moe_stack_glue(hs, ys, hs, xs, T, D.d_model)
         torch.cuda.synchronize()
         ref_r = oracle.route(lay, x_l)
-        np.testing.assert_array_equal(r["idx"].cpu().numpy(), ref_r["idx"], err_msg=f"layer {l} top-k")
+        np.testing.assert_array_equal(idx.cpu().numpy(), ref_r["idx"], err_msg=f"layer {l} decode top-k")
+        np.testing.assert_allclose(wts.cpu().numpy(), ref_r["w"], rtol=2e-6, atol=1e-7,
+                                   err_msg=f"layer {l} decode routing weights")
         y_ref = oracle.layer_tokens(lay, x_l, ref_r["idx"], ref_r["w"])
         y_gpu = ys.cpu().numpy().astype(np.float64)
         rms = np.sqrt(np.mean(y_ref ** 2))
@@ -73,7 +77,7 @@ def test_stack_30_layers_256_tokens():
         hn_ref, xn_ref = oracle.stack_glue(h_prev, y_gpu)
         np.testing.assert_array_equal(bits(hs), hn_ref, err_msg=f"layer {l} residual")
         np.testing.assert_array_equal(bits(xs), xn_ref, err_msg=f"layer {l} norm")
-        say(f"layer {l}: top-k exact, max|err| {err:.2e} rms, residual and norm bit-exact")
+        say(f"layer {l}: {T} tokens, top-k exact, max|err| {err:.2e} rms, residual and norm bit-exact")
         del lay
     say(f"worst layer error {worst:.2e} rms")
 
@@ -86,19 +90,18 @@ def test_stack_30_layers_256_tokens():
     for t in range(T):
         B.moe_stack_forward_decode(handles, h[t:t + 1], 1, xb, yb, hb)
     torch.cuda.synchronize()
-    hf = bits(h)
-    np.testing.assert_array_equal(hf[sample], bits(hs))
-    assert np.all(np.isfinite(synth.bf16_bits_to_f32(hf)))
-    say(f"stack entry point: {T} tokens x {NL} layers, sampled rows identical to the layer-by-layer run")
-    # the sampled tokens in one call: the residual step runs in its own launch (T d above the
-    # router's LDS budget) and gives the same bits
-    hS = tokens_to_device(h0[sample], dev)
+    np.testing.assert_array_equal(bits(h), bits(hs))
+    say(f"stack entry point: {T} tokens x {NL} layers one at a time, every row identical to the "
+        f"layer-by-layer run")
+    # 16 tokens per call: the residual step runs in its own launch (T d above the router's LDS
+    # budget) and gives the same bits
+    hS = tokens_to_device(h0[:CALL], dev)
     xS, hbS = torch.empty_like(hS), torch.empty_like(hS)
-    yS = torch.empty((S, D.d_model), dtype=torch.float32, device=dev)
-    B.moe_stack_forward_decode(handles, hS, S, xS, yS, hbS)
+    yS = torch.empty((CALL, D.d_model), dtype=torch.float32, device=dev)
+    B.moe_stack_forward_decode(handles, hS, CALL, xS, yS, hbS)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(bits(hS), bits(hs))
-    say(f"stack entry point with {S} tokens per call: identical")
+    np.testing.assert_array_equal(bits(hS), bits(hs)[:CALL])
+    say(f"stack entry point with {CALL} tokens per call: identical")
     for L in layers:
         L.close()
 

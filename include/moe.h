@@ -230,6 +230,24 @@ moe_status moe_forward_prefill(moe_layer *layer, const uint16_t *x, int32_t T, f
                                void *hip_stream);
 
 /*
+ * moe_forward_decode for callers that cannot allocate (code under HIP stream capture, tight
+ * serving loops, harnesses that forbid allocation): the same computation and the same results,
+ * without a layer handle. dims and w are as for moe_layer_create (validated the same way;
+ * expert slots and flags are not available here); x, T and y as for moe_forward_decode, with
+ * 1 <= T <= min(dims->max_tokens, MOE_MAX_DECODE_TOKENS). The call's scratch (logits, top-k,
+ * hidden activations and their sums, about 0.4 MiB for 16 tokens of the 2816-wide layer) lives
+ * in one static device array of 1 MiB per device that the library holds until the process
+ * ends: a call whose scratch would not fit (the widest layers at 16 tokens) returns
+ * MOE_E_CAPACITY before enqueuing anything.
+ * The entry point allocates nothing (no hipMalloc, hipFree or allocating library routine); on
+ * its first call on a device it looks up that device's array (hipGetSymbolAddress). Every
+ * call on one device shares that device's array: calls that overlap on one device (on
+ * different streams, or from several threads) race and must be serialized by the caller.
+ */
+moe_status moe_forward_decode_noalloc(const moe_dims *dims, const moe_weights *w, const uint16_t *x, int32_t T,
+                                      float *y, void *hip_stream);
+
+/*
  * Routing of the last moe_forward_decode or moe_forward_prefill (or moe_prefill_route) on
  * this layer, as that call's own kernels selected it: copies, in stream order, the top-k
  * expert ids (int32 [T, k]) and routing weights (fp32 [T, k]) of its first T tokens to the

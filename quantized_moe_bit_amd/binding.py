@@ -77,6 +77,7 @@ def lib() -> C.CDLL:
             "moe_forward_decode": (st, [vp, vp, i32, vp, vp]),
             "moe_forward_prefill": (st, [vp, vp, i32, vp, vp]),
             "moe_last_routing": (st, [vp, i32, vp, vp, vp]),
+            "moe_forward_decode_noalloc": (st, [C.POINTER(moe_dims), C.POINTER(moe_weights), vp, i32, vp, vp]),
             "moe_stack_glue": (st, [vp, vp, vp, vp, vp, vp, i32, i32, vp]),
             "moe_stack_forward_decode": (st, [C.POINTER(vp), i32, vp, i32, vp, vp, vp, vp]),
             "moe_packed_bytes": (C.c_size_t, [i32, i32, i32, i32, i32]),
@@ -168,6 +169,11 @@ def moe_forward_decode(handle, x, T, y, stream=None):
 
 def moe_forward_prefill(handle, x, T, y, stream=None):
     _check(lib().moe_forward_prefill(handle, _ptr(x), T, _ptr(y), _stream(stream)), "moe_forward_prefill")
+
+
+def moe_forward_decode_noalloc(dims: moe_dims, weights: moe_weights, x, T, y, stream=None):
+    _check(lib().moe_forward_decode_noalloc(C.byref(dims), C.byref(weights), _ptr(x), T, _ptr(y), _stream(stream)),
+           "moe_forward_decode_noalloc")
 
 
 def moe_last_routing(handle, T, idx, w, stream=None):

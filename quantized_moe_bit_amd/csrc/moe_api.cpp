@@ -94,6 +94,15 @@ moe_status check_weights(const moe_weights *w) {
     return MOE_OK;
 }
 
+}  // namespace
+
+moe_status check_layer_args(const moe_dims *D, const moe_weights *w) {
+    moe_status st = check_dims(D);
+    return st != MOE_OK ? st : check_weights(w);
+}
+
+namespace {
+
 moe_status check_tokens(moe_layer *L, int32_t T, const char *what) {
     if (!L) return fail(MOE_E_INVALID, "%s: layer is NULL", what);
     if (T < 0) return fail(MOE_E_SHAPE, "%s: T = %d is negative", what, T);

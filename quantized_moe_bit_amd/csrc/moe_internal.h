@@ -16,6 +16,8 @@ namespace qmoe {
 // ----------------------------------------------------------------------------- errors
 moe_status fail(moe_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
+// dims and weight pointers of moe_layer_create (validation only)
+moe_status check_layer_args(const moe_dims *D, const moe_weights *w);
 
 // ----------------------------------------------------------------------------- tiling constants
 constexpr int kGroup = 64;          // quantization group (inputs per scale/bias)

@@ -71,6 +71,7 @@ class DeviceLayer:
         self.dims = B.moe_dims(D.d_model, D.n_experts, D.top_k, D.d_expert, D.d_shared, D.group, D.router_bits,
                                D.expert_bits, max_tokens)
         self.max_tokens = max_tokens
+        self.weights = w   # the moe_weights the handle was created with
         self.handle = B.moe_layer_create(self.dims, w, flags)
 
     def replicate(self) -> "DeviceLayer":

@@ -172,6 +172,22 @@ def test_binding_refuses_a_library_built_from_other_sources(monkeypatch):
         B.lib()
 
 
+def test_noalloc_decode_refuses_scratch_beyond_its_static_array():
+    """The handle-free decode's scratch lives in a 1 MiB static device array: the widest layer at
+    16 tokens needs more and is refused on the host, before any device call (no GPU here)."""
+    L = B.lib()
+    fake = (C.c_uint8 * 64)()
+    p = (C.addressof(fake) + 15) // 16 * 16
+    dims = _dims(d_model=8192, n_experts=1024, top_k=16, d_expert=1536, d_shared=4096, max_tokens=16)
+    w = _weights()
+    assert L.moe_forward_decode_noalloc(C.byref(dims), C.byref(w), p, 16, p, None) == B.MOE_E_CAPACITY
+    assert "scratch" in B.moe_last_error()
+    assert L.moe_forward_decode_noalloc(C.byref(dims), C.byref(w), p, 17, p, None) == B.MOE_E_CAPACITY
+    assert L.moe_forward_decode_noalloc(C.byref(_dims(d_model=200)), C.byref(w), p, 1, p, None) == B.MOE_E_SHAPE
+    assert L.moe_forward_decode_noalloc(None, C.byref(w), p, 1, p, None) == B.MOE_E_INVALID
+    assert L.moe_forward_decode_noalloc(C.byref(_dims()), C.byref(w), p, 0, p, None) == B.MOE_OK   # no-op
+
+
 def test_calls_reject_null_layer_and_bad_sizes():
     L = B.lib()
     assert L.moe_forward_decode(None, None, 1, None, None) == B.MOE_E_INVALID

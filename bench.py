@@ -253,6 +253,64 @@ def slot_section(dev, ntok=256):
     return out
 
 
+def prefill_section(args, dev, name, label):
+    """One prefill chunk of a workload through one layer: chunk time over --prefill-steps calls after
+    two warm-up calls, MFMA rate of the whole step and of each GEMM, and per-kernel durations from a
+    second pass with the library's dispatch-attached events. Returns (layer, x on device, T, dict)."""
+    import torch
+    from quantized_moe_bit_amd import binding as B
+    from quantized_moe_bit_amd import synth
+    from quantized_moe_bit_amd.device import DeviceLayer, tokens_to_device
+    wp = synth.WORKLOADS[name]
+    D = wp.dims
+    lp = synth.workload_layer(wp)
+    xp, _, _ = synth.workload_tokens(wp, lp)
+    T = wp.tokens
+    P = DeviceLayer(lp, max_tokens=T, device=dev)
+    xpd = tokens_to_device(xp, dev)
+    yp = torch.empty((T, D.d_model), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        B.moe_forward_prefill(P.handle, xpd, T, yp)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.prefill_steps):
+        B.moe_forward_prefill(P.handle, xpd, T, yp)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_pre = e0.elapsed_time(e1) / args.prefill_steps
+    B.moe_profile_reset(P.handle)
+    B.moe_profile_enable(P.handle, True)
+    for _ in range(args.prefill_steps):
+        B.moe_forward_prefill(P.handle, xpd, T, yp)
+    torch.cuda.synchronize()
+    pk = {}
+    for kid, kname in enumerate(B.KERNEL_NAMES):
+        ms, c = B.moe_profile_read(P.handle, kid)
+        if c:
+            pk[kname] = 1000.0 * ms / c
+    B.moe_profile_enable(P.handle, False)
+    P.close()
+    d, I, Is, k = D.d_model, D.d_expert, D.d_shared, D.top_k
+    fl_gateup = 2.0 * (T * k * 2 * I * d + T * 2 * Is * d)
+    fl_down = 2.0 * (T * k * d * I + T * d * Is)
+    flops = fl_gateup + fl_down
+    pre = {"workload": label,
+           "tokens_per_s": round(T / (ms_pre * 1e-3), 1), "ms_per_step": round(ms_pre, 4),
+           "mfma_flops_per_step": flops,
+           "mfma_tflops": round(flops / (ms_pre * 1e-3) / 1e12, 2),
+           "mfma_frac": round(flops / (ms_pre * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+           "kernels_us": {n: round(v, 2) for n, v in pk.items()},
+           "kernels_sum_us": round(sum(pk.values()), 2)}
+    for kname, fl in (("pre_gateup", fl_gateup), ("pre_down", fl_down)):
+        if kname in pk:
+            tf = fl / (pk[kname] * 1e-6) / 1e12
+            pre["roofline_" + kname[4:]] = dict(bound="mfma", achieved=round(tf, 1), peak=MFMA_PEAK_TFLOPS,
+                                                 unit="TFLOP/s", frac=round(tf / MFMA_PEAK_TFLOPS, 4),
+                                                 flops=fl, avg_us=round(pk[kname], 2))
+    return lp, xpd, T, pre
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -391,7 +449,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp16",
         "data": "synthetic",
         "config": {"workload": "decode: 1 token through one layer, d_model 2816, 128 experts, top-8, "
                                "expert width 704, shared width 2112, 8-bit g64 router, 4-bit g64 experts",
@@ -413,56 +471,19 @@ def main():
         layers.clear()
         torch.cuda.empty_cache()
 
-    # ------------------------------------------------------------------ 4096-token prefill
+    # ------------------------------------------------------------------ prefill chunks (4096 and 512 tokens)
     if not args.no_prefill:
         release_decode_copies()
-        wp = synth.WORKLOADS["prefill4096"]
         log("generating the 4096-token Zipf prefill workload")
-        lp = synth.workload_layer(wp)
-        xp, _, _ = synth.workload_tokens(wp, lp)
-        P = DeviceLayer(lp, max_tokens=wp.tokens, device=dev)
-        xpd = tokens_to_device(xp, dev)
-        yp = torch.empty((wp.tokens, d), dtype=torch.float32, device=dev)
-        T = wp.tokens
-        for _ in range(2):
-            B.moe_forward_prefill(P.handle, xpd, T, yp)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.prefill_steps):
-            B.moe_forward_prefill(P.handle, xpd, T, yp)
-        e1.record()
-        torch.cuda.synchronize()
-        ms_pre = e0.elapsed_time(e1) / args.prefill_steps
-        B.moe_profile_reset(P.handle)
-        B.moe_profile_enable(P.handle, True)
-        for _ in range(args.prefill_steps):
-            B.moe_forward_prefill(P.handle, xpd, T, yp)
-        torch.cuda.synchronize()
-        pk = {}
-        for kid, name in enumerate(B.KERNEL_NAMES):
-            ms, c = B.moe_profile_read(P.handle, kid)
-            if c:
-                pk[name] = 1000.0 * ms / c
-        fl_gateup = 2.0 * (T * k * 2 * I * d + T * 2 * Is * d)
-        fl_down = 2.0 * (T * k * d * I + T * d * Is)
-        flops = fl_gateup + fl_down
-        pre = {"workload": "prefill: 4096 tokens, one 2816-wide layer, Zipf(1.3) logit skew, 2% tied tokens",
-               "tokens_per_s": round(T / (ms_pre * 1e-3), 1), "ms_per_step": round(ms_pre, 4),
-               "mfma_flops_per_step": flops,
-               "mfma_tflops": round(flops / (ms_pre * 1e-3) / 1e12, 2),
-               "mfma_frac": round(flops / (ms_pre * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
-               "kernels_us": {n: round(v, 2) for n, v in pk.items()}}
-        if "pre_gateup" in pk:
-            tf = fl_gateup / (pk["pre_gateup"] * 1e-6) / 1e12
-            pre["roofline_gateup"] = dict(bound="mfma", achieved=round(tf, 1), peak=MFMA_PEAK_TFLOPS,
-                                          unit="TFLOP/s", frac=round(tf / MFMA_PEAK_TFLOPS, 4))
-        if "pre_down" in pk:
-            tf = fl_down / (pk["pre_down"] * 1e-6) / 1e12
-            pre["roofline_down"] = dict(bound="mfma", achieved=round(tf, 1), peak=MFMA_PEAK_TFLOPS,
-                                        unit="TFLOP/s", frac=round(tf / MFMA_PEAK_TFLOPS, 4))
+        lp, xpd, T, pre = prefill_section(args, dev, "prefill4096",
+                                          "prefill: 4096 tokens, one 2816-wide layer, Zipf(1.3) logit skew, 2% tied tokens")
         result["prefill"] = pre
-        P.close()
+        ms_pre = pre["ms_per_step"]
+        yp = torch.empty((T, d), dtype=torch.float32, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        log("generating the 512-token Zipf prefill workload")
+        result["prefill512"] = prefill_section(args, dev, "prefill512",
+                                               "prefill: 512 tokens, one 2816-wide layer, Zipf(1.1) logit skew")[3]
         if not args.no_prologue:
             # widened row: the same layer and tokens with the router prologue and per-expert scale
             rng = np.random.default_rng(7)

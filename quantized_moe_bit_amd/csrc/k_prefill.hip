@@ -468,6 +468,11 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
                          smem + kBRingOff + SBN * kBStageBytes + wave * 2048, St0 + gb * 128, St1 + gb * 128, soff,
                          smem + kSRingOff + SBN * kSStageBytes + wave * 512);
             }
+            // Scheduling: the LDS reads of K-step s + 1 (A fragments; in K-step 3 the next ring
+            // step's code words and scale/bias words) are issued before the MFMAs of K-step s, so a
+            // whole K-step of MFMAs covers their latency; the sched barriers keep the compiler from
+            // sinking them next to their use. The dequantization VALU of K-step s + 1 interleaves
+            // with the MFMAs of K-step s.
             if (live_w) {
                 const uint8_t *sA = smem + SA * kAStageBytes;
                 u32x4_t af[2][LMS];
@@ -481,6 +486,14 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
                     if (s < 3) {
 #pragma unroll
                         for (int ms = 0; ms < LMS; ++ms) af[(s + 1) & 1][ms] = ld16(sA + aoff[s + 1] + 4096 * ms);
+                    } else {
+                        // code words of step g + 1 (a past-the-end step reads a valid clamped stage);
+                        // this K-step's fragments are already in registers
+                        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitB) : "memory");
+                        load_w(SB1, bw, s2, b2);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (s < 3) {
 #pragma unroll
                         for (int t = 0; t < 2; ++t)
                             bf[(s + 1) & 1][t] = dequant_frag(bw[t][s + 1], s2[t], b2[t]);
@@ -491,11 +504,11 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
                         for (int t = 0; t < 2; ++t)
                             acc[ms][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                                 __builtin_bit_cast(f16x8_t, af[s & 1][ms]), bf[s & 1][t], acc[ms][t], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
+            } else {
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitB) : "memory");
             }
-            // code words of step g + 1 (a past-the-end step reads a valid clamped stage)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitB) : "memory");
-            if (live_w) load_w(SB1, bw, s2, b2);
         };
         using I0 = std::integral_constant<int, 0>;
         using I1 = std::integral_constant<int, 1>;

@@ -178,8 +178,8 @@ typedef struct {
  * accumulated products are scaled back by 2^-m in fp32, exactly), so the staging keeps 11
  * significant bits for scales of any magnitude. At creation the library reads every expert
  * matrix's scale/bias words once and waits for the result: a NaN or infinite scale or bias, a
- * largest |scale| outside [2^-69, 2^59), or a bias with floor(log2 |bias|) >=
- * floor(log2 max |scale|) + 20 in its matrix is MOE_E_QUANT. Layers with expert slots check the routed experts' words in
+ * largest |scale| outside [2^-73, 2^56), or a bias with floor(log2 |bias|) >=
+ * floor(log2 max |scale|) + 24 in its matrix is MOE_E_QUANT. Layers with expert slots check the routed experts' words in
  * every prefill call instead (see expert_slot), since the slots are filled later.
  * *out is written only on MOE_OK.
  */

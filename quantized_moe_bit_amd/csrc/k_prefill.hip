@@ -44,6 +44,7 @@ constexpr int kBStages = 4;
 constexpr int kUnroll = 4;
 constexpr int kADist = 1;   // steps the A loads run ahead
 constexpr int kBDist = 2;   // steps the B loads run ahead
+static_assert(kADist <= kBDist, "the prologue issues A no earlier than B");
 static_assert(kADist < kAStages && kBDist < kBStages, "a stage is refilled only after its step");
 static_assert(kUnroll % kAStages == 0 && kUnroll % kBStages == 0, "constant stages per unrolled step");
 constexpr int kAStageBytes = kMT * 128;
@@ -52,14 +53,21 @@ constexpr int kSStageBytes = 4 * 2 * 256;
 constexpr int kBRingOff = kAStages * kAStageBytes;
 constexpr int kSRingOff = kBRingOff + kBStages * kBStageBytes;
 constexpr int kSmemBytes = kSRingOff + kBStages * kSStageBytes;
-static_assert(2 * kSmemBytes <= 147456, "two workgroups per compute unit");
+static_assert(2 * kSmemBytes <= 159744, "two workgroups per compute unit");
 constexpr int kDmaPerStep = 8;   // per thread: 4 A chunks, 2 code chunks, 2 scale/bias words
 // Direct loads issued after the A chunks of step g up to the barrier of step g, and after the
 // scale/bias words of step g + 1 up to their use at the end of step g (every step issues the
 // same eight loads, the prologue the same pattern).
 constexpr int kWaitA = 4 + kDmaPerStep * (kADist - 1);
 constexpr int kWaitB = kDmaPerStep * (kBDist - 1);
-constexpr int kWaitB0 = 4 * (kBDist - 1) + 4 * kADist;   // after the scale/bias words of step 0
+// loads the prologue issues after the scale/bias words of step 0 (steps -kBDist + 1 .. -1: A when
+// it has started, then B)
+constexpr int prologue_after_b0() {
+    int n = 0;
+    for (int j = -kBDist + 1; j < 0; ++j) n += (j + kADist >= 0 ? 4 : 0) + 4;
+    return n;
+}
+constexpr int kWaitB0 = prologue_after_b0();
 // gate/up epilogue: each wave's h tile, 128 rows x 32 fp16 (rows 96 B apart: the two rows one
 // 16-bit store instruction writes start 32 banks apart)
 constexpr int kHPitch = 48;
@@ -198,6 +206,15 @@ __device__ __forceinline__ void ring_sync() {
     asm volatile("" ::: "memory");
 }
 
+// f(integral_constant<J>) for J = J0 .. N - 1, in order (the K loop's constant stage offsets)
+template <int J0, int N, class F>
+__device__ __forceinline__ void unroll_steps(F &&f) {
+    if constexpr (J0 < N) {
+        f(std::integral_constant<int, J0>{});
+        unroll_steps<J0 + 1, N>(f);
+    }
+}
+
 struct PreArgs {
     int T, d, k, I, Is, E;
     const uint16_t *x16;        // gate/up A rows [T, d], fp16
@@ -217,19 +234,23 @@ struct PreArgs {
 };
 
 // Eight staged weights fp16(2^m (s q + b)) from one device-layout word (elements j = 0..7 of
-// a K-step; element j in nibble j even ? j/2 : 4 + j/2), given s2 = fp16(2^(20+m) s) and
-// b2 = fp16(2^m b) in both halves: the nibbles of pair p (elements 2p, 2p + 1 are nibbles p and
-// 4 + p), moved to bits 4..7 of each 16-bit half, are the fp16 subnormals q 2^-20 (exact), and
-// one packed fma gives fp16(q 2^-20 s2 + b2), rounded once. k_stage_shift chooses m so that
-// 2^(20+m) |s| < 2^16 for every scale of the matrix (s2 is then the exact scale, or for a scale
-// below 2^-29 of the largest an fp16 subnormal within 2^-24 of it).
-__device__ __forceinline__ f16x8_t dequant_frag(uint32_t w, f16x2_t s2, f16x2_t b2) {
-    const uint32_t m = 0x00F000F0u;
-    const uint32_t t[4] = {(w << 4) & m, w & m, (w >> 4) & m, (w >> 8) & m};
+// a K-step; element j in nibble j even ? j/2 : 4 + j/2, so pair p = elements 2p, 2p + 1 is
+// nibbles p and 4 + p), given sc = {fp16(2^(24+m) s), fp16(2^(20+m) s)} and b2 = fp16(2^m b)
+// in both halves. Each pair is masked out in place, as a pair of fp16 subnormals: pairs 0 and 1
+// from the word, pairs 2 and 3 from the word shifted right by 8; nibbles at bits 0..3 / 16..19
+// are q 2^-24 and take the 2^24 scale, nibbles at bits 4..7 / 20..23 are q 2^-20 and take the
+// 2^20 scale (both exact), and one packed fma gives fp16(q s + b) times 2^m, rounded once: one
+// shift, four ands and four fmas per eight weights. k_stage_shift chooses m so that
+// 2^(24+m) |s| < 2^16 for every scale of the matrix (both fp16 scales are then exact, or for a
+// scale below 2^-25 of the largest within 2^-24 of it).
+__device__ __forceinline__ f16x8_t dequant_frag(uint32_t w, f16x2_t sc, f16x2_t b2) {
+    const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u, w8 = w >> 8;
+    const f16x2_t s24 = {sc[0], sc[0]}, s20 = {sc[1], sc[1]};
     u32x4_t r;
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-        r[p] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, t[p]), s2, b2));
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, w & lo), s24, b2));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, w & hi), s20, b2));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, w8 & lo), s24, b2));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, w8 & hi), s20, b2));
     return __builtin_bit_cast(f16x8_t, r);
 }
 
@@ -237,11 +258,11 @@ __device__ __forceinline__ f16x8_t dequant_frag(uint32_t w, f16x2_t s2, f16x2_t 
 // slot, when routed is set; x = n_mats: the shared expert, when shared is set), y = kind
 // (gate, up, down);
 // block 256. With e the bf16 exponent field of the matrix's largest |scale| (its value lies in
-// [2^(e-127), 2^(e-126))), m = 122 - e puts that scale times 2^m in [2^-5, 2^-4): every scale
-// times 2^(20+m) is then below 2^16 (an fp16 value), and every staged weight below
-// 1 + 2^m |bias|. A matrix whose scales are all zero takes m from its largest |bias|, placed in
-// [2^14, 2^15). The matrix cannot be staged (m = 0, *faults += 1) if a scale or bias is NaN or
-// infinite, m lies outside [-64, 64], or 2^m |bias| can reach 2^15.
+// [2^(e-127), 2^(e-126))), m = 118 - e puts that scale times 2^m in [2^-9, 2^-8): every scale
+// times 2^(24+m) is then below 2^16 (an fp16 value), and every staged weight below
+// 2^-4 + 2^m |bias|. A matrix whose scales are all zero takes m from its largest |bias|, placed
+// in [2^14, 2^15). The matrix cannot be staged (m = 0, *faults += 1) if a scale or bias is NaN
+// or infinite, m lies outside [-64, 64], or 2^m |bias| can reach 2^15.
 struct StageArgs {
     const uint32_t *sb[3];      // routed gate, up, down scale/bias words (n_mats matrices each)
     const uint32_t *sb_sh[3];   // shared gate, up, down
@@ -278,7 +299,7 @@ __global__ __launch_bounds__(256) void k_stage_shift(StageArgs a) {
     smax = max(max(red[0][0], red[0][1]), max(red[0][2], red[0][3]));
     bmax = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3]));
     const int es = (int)(smax >> 7), eb = (int)(bmax >> 7);
-    int m = smax ? 122 - es : (bmax ? 141 - eb : 0);
+    int m = smax ? 118 - es : (bmax ? 141 - eb : 0);
     const bool bad = smax >= 0x7F80u || bmax >= 0x7F80u || m < -64 || m > 64 || (bmax && eb + m > 141);
     if (bad) {
         atomicAdd(a.faults, 1);
@@ -382,14 +403,14 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
         St1 = static_cast<const uint8_t *>(uniform_ptr(St1));
     }
     // fp16 staging exponents of the wave's two code tiles (gate/up: gate and up; down: down twice):
-    // scale and bias words are multiplied by 2^(20+m) and 2^m before the fp16 conversion, the
-    // accumulators by 2^-m after the K loop
+    // scales are multiplied by 2^(24+m) and 2^(20+m), biases by 2^m before the fp16 conversion,
+    // the accumulators by 2^-m after the K loop
     float fS[2], fB[2], fR[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const int kind = MODE == 0 ? t : 2;
         const int m = a.shift[shared_item ? 3 * a.n_mats + kind : kind * a.n_mats + e];
-        fS[t] = __builtin_ldexpf(1.0f, 20 + m);
+        fS[t] = __builtin_ldexpf(1.0f, 24 + m);
         fB[t] = __builtin_ldexpf(1.0f, m);
         fR[t] = __builtin_ldexpf(1.0f, -m);
     }
@@ -425,7 +446,7 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
             const uint32_t sbw =
                 *reinterpret_cast<const uint32_t *>(smem + kSRingOff + sbi * kSStageBytes + wave * 512 + t * 256 + lane * 4);
             const float sc = bf16_to_f32(sbw & 0xFFFFu) * fS[t], bi = bf16_to_f32(sbw >> 16) * fB[t];
-            s2[t] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(sc, sc));
+            s2[t] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(sc, sc * 0.0625f));
             b2[t] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(bi, bi));
         }
     };
@@ -451,11 +472,13 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
     // The K loop, instantiated per number of live 32-row subtiles (1..4) so that padding
     // subtiles cost nothing and the MFMA sequence stays branch-free. Within a step, K-step s
     // multiplies while the A fragments and the dequantized weights of K-step s + 1 are formed;
-    // the code words of step g + 1 are read at the end of step g.
+    // the code words of step g + 1 are read, and its K-step 0 dequantized, during K-step 3 of
+    // step g.
     auto kloop = [&](auto lms_c) {
         constexpr int LMS = decltype(lms_c)::value;
         u32x4_t bw[2];
         f16x2_t s2[2], b2[2];
+        f16x8_t bf0[2];   // K-step 0 of the next ring step, dequantized during K-step 3 of this one
         auto step = [&](auto j_c, int g) {
             constexpr int Ju = decltype(j_c)::value;
             constexpr int SA = Ju % kAStages, SAN = (Ju + kADist) % kAStages;
@@ -480,7 +503,7 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
 #pragma unroll
                 for (int ms = 0; ms < LMS; ++ms) af[0][ms] = ld16(sA + aoff[0] + 4096 * ms);
 #pragma unroll
-                for (int t = 0; t < 2; ++t) bf[0][t] = dequant_frag(bw[t][0], s2[t], b2[t]);
+                for (int t = 0; t < 2; ++t) bf[0][t] = bf0[t];
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     if (s < 3) {
@@ -504,30 +527,29 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
                         for (int t = 0; t < 2; ++t)
                             acc[ms][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                                 __builtin_bit_cast(f16x8_t, af[s & 1][ms]), bf[s & 1][t], acc[ms][t], 0, 0, 0);
+                    if (s == 3) {
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) bf0[t] = dequant_frag(bw[t][0], s2[t], b2[t]);
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             } else {
                 asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitB) : "memory");
             }
         };
-        using I0 = std::integral_constant<int, 0>;
-        using I1 = std::integral_constant<int, 1>;
-        using I2 = std::integral_constant<int, 2>;
-        using I3 = std::integral_constant<int, 3>;
-        static_assert(kUnroll == 4, "the loop below is written out for four steps");
         // B of step 0: issued first in the prologue
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitB0) : "memory");
-        if (live_w) load_w(0, bw, s2, b2);
-        int g = 0;
-        for (; g + kUnroll <= G; g += kUnroll) {
-            step(I0{}, g);
-            step(I1{}, g + 1);
-            step(I2{}, g + 2);
-            step(I3{}, g + 3);
+        if (live_w) {
+            load_w(0, bw, s2, b2);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) bf0[t] = dequant_frag(bw[t][0], s2[t], b2[t]);
         }
-        if (g < G) step(I0{}, g);
-        if (g + 1 < G) step(I1{}, g + 1);
-        if (g + 2 < G) step(I2{}, g + 2);
+        int g = 0;
+        for (; g + kUnroll <= G; g += kUnroll)
+            unroll_steps<0, kUnroll>([&](auto j_c) { step(j_c, g + decltype(j_c)::value); });
+        unroll_steps<0, kUnroll - 1>([&](auto j_c) {
+            if (g + decltype(j_c)::value < G) step(j_c, g + decltype(j_c)::value);
+        });
     };
     switch (live_ms) {
         case 1: kloop(std::integral_constant<int, 1>{}); break;

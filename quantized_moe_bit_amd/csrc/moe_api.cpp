@@ -382,7 +382,7 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
         delete L;
         return fail(MOE_E_QUANT,
                     "%d expert matrices have scales or biases the fp16 staging cannot carry (NaN or infinite, "
-                    "largest |scale| outside [2^-69, 2^59), or floor(log2 |bias|) >= floor(log2 max |scale|) + 20)",
+                    "largest |scale| outside [2^-73, 2^56), or floor(log2 |bias|) >= floor(log2 max |scale|) + 24)",
                     bad);
     }
     *out = L;

@@ -5,7 +5,7 @@
 * Expert scales far from the stated U(0.002, 0.02): around 1e-5 (below fp16's normal range)
   and above 2^-4, within one layer. The prefill GEMMs stage weights in fp16 with a per-matrix
   power-of-two exponent, so both paths stay within the output tolerance; metadata that cannot
-  be staged (NaN scales, biases 2^20 times the largest scale) is refused at creation
+  be staged (NaN scales, biases 2^24 times the largest scale) is refused at creation
   (Mference system design, ".gturbo directory": incompatible quantization metadata is
   rejected).
 * MOE_FLAG_CHECK_FINITE: non-finite inputs are refused before anything is enqueued, a
@@ -113,8 +113,8 @@ def test_create_refuses_unstageable_metadata(bad):
         s[3, 7, 1] = 0x7FC0
     elif bad == "inf_bias":
         b[5, 0, 0] = 0xFF80
-    else:   # |bias| 2^20 times the largest scale's power of two
-        b[2, 9, 1] = synth.f32_to_bf16_bits(np.array([0.03 * 2 ** 21], np.float32))[0]
+    else:   # |bias| 2^24 times the largest scale's power of two
+        b[2, 9, 1] = synth.f32_to_bf16_bits(np.array([0.03 * 2 ** 25], np.float32))[0]
     lay.down = synth.QMat(m.codes, s, b, m.bits, m.out_dim, m.in_dim)
     with pytest.raises(B.MoeError) as ei:
         DeviceLayer(lay, 16)

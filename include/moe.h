@@ -391,6 +391,17 @@ moe_status moe_slot_cache_create(int32_t n_experts, int32_t n_slots, moe_slot_ca
 void moe_slot_cache_destroy(moe_slot_cache *cache);
 moe_status moe_slot_cache_plan(moe_slot_cache *cache, const int32_t *experts, int32_t n, int32_t *slot_of,
                                int32_t *fill_expert, int32_t *fill_slot, int32_t *n_fill);
+/*
+ * moe_slot_cache_plan with protected experts (host int32 [n_protect]): those that are resident
+ * and not in the request keep their slots (this request evicts none of them) and count no use,
+ * so a caller can plan the next tile of a chunk while the current tile's experts still serve
+ * queued work (Mference system design, "Prefill"; "Correctness and safety invariants"). The
+ * request's distinct experts plus the kept protected ones must fit the slots (MOE_E_CAPACITY
+ * otherwise, nothing changed). moe_slot_cache_plan is this call with no protected experts.
+ */
+moe_status moe_slot_cache_plan_protected(moe_slot_cache *cache, const int32_t *experts, int32_t n,
+                                         const int32_t *protect, int32_t n_protect, int32_t *slot_of,
+                                         int32_t *fill_expert, int32_t *fill_slot, int32_t *n_fill);
 /* The current expert-to-slot table (host int32 [n_experts], -1 for absent experts). */
 moe_status moe_slot_cache_table(const moe_slot_cache *cache, int32_t *expert_slot);
 

@@ -97,6 +97,7 @@ def lib() -> C.CDLL:
             "moe_slot_cache_create": (st, [i32, i32, C.POINTER(vp)]),
             "moe_slot_cache_destroy": (None, [vp]),
             "moe_slot_cache_plan": (st, [vp, vp, i32, vp, vp, vp, C.POINTER(C.c_int32)]),
+            "moe_slot_cache_plan_protected": (st, [vp, vp, i32, vp, i32, vp, vp, vp, C.POINTER(C.c_int32)]),
             "moe_slot_cache_table": (st, [vp, vp]),
         }
         for name, (res, args) in sig.items():
@@ -263,16 +264,18 @@ class SlotCache:
         _check(lib().moe_slot_cache_create(n_experts, n_slots, C.byref(h)), "moe_slot_cache_create")
         self.handle, self.n_experts, self.n_slots = h.value, n_experts, n_slots
 
-    def plan(self, experts):
-        """-> (slot of each listed expert, [(expert, slot) fills])"""
+    def plan(self, experts, protect=()):
+        """-> (slot of each listed expert, [(expert, slot) fills]); protected experts keep their slots"""
         e = np.ascontiguousarray(np.asarray(experts, np.int32).ravel())
+        p = np.ascontiguousarray(np.asarray(list(protect), np.int32).ravel())
         n = e.shape[0]
         slot_of = np.empty(max(n, 1), np.int32)
         fe = np.empty(max(n, 1), np.int32)
         fs = np.empty(max(n, 1), np.int32)
         nf = C.c_int32()
-        _check(lib().moe_slot_cache_plan(self.handle, e.ctypes.data, n, slot_of.ctypes.data, fe.ctypes.data,
-                                         fs.ctypes.data, C.byref(nf)), "moe_slot_cache_plan")
+        _check(lib().moe_slot_cache_plan_protected(self.handle, e.ctypes.data, n, p.ctypes.data if p.size else None,
+                                                   p.shape[0], slot_of.ctypes.data, fe.ctypes.data, fs.ctypes.data,
+                                                   C.byref(nf)), "moe_slot_cache_plan")
         return slot_of[:n].tolist(), list(zip(fe[:nf.value].tolist(), fs[:nf.value].tolist()))
 
     def table(self) -> np.ndarray:

@@ -255,8 +255,8 @@ __device__ __forceinline__ f16x8_t dequant_frag(uint32_t w, f16x2_t sc, f16x2_t 
 }
 
 // fp16 staging exponent of one matrix. grid (n_mats + 1, 3): x = routed matrix (expert or
-// slot, when routed is set; x = n_mats: the shared expert, when shared is set), y = kind
-// (gate, up, down);
+// slot, when routed is set, and for a layer with slots only a slot its table maps; x = n_mats:
+// the shared expert, when shared is set), y = kind (gate, up, down);
 // block 256. With e the bf16 exponent field of the matrix's largest |scale| (its value lies in
 // [2^(e-127), 2^(e-126))), m = 118 - e puts that scale times 2^m in [2^-9, 2^-8): every scale
 // times 2^(24+m) is then below 2^16 (an fp16 value), and every staged weight below
@@ -269,11 +269,22 @@ struct StageArgs {
     int words[3], words_sh[3];  // words per matrix
     int n_mats, routed, shared;
     int32_t *shift, *faults;
+    const int32_t *table;       // expert-to-slot table (layers with slots): only the slots it maps
+    int E;                      // are read (others may be being filled)
 };
 __global__ __launch_bounds__(256) void k_stage_shift(StageArgs a) {
     const int kind = blockIdx.y, mat = blockIdx.x;
     const bool sh = mat == a.n_mats;
     if (sh ? !a.shared : !a.routed) return;
+    if (!sh && a.table) {   // a slot the table does not map: no kernel of this call reads it
+        __shared__ int mapped;
+        if (threadIdx.x == 0) mapped = 0;
+        __syncthreads();
+        for (int e = threadIdx.x; e < a.E; e += 256)
+            if (a.table[e] == mat) mapped = 1;
+        __syncthreads();
+        if (!mapped) return;
+    }
     const int n = sh ? a.words_sh[kind] : a.words[kind];
     const uint32_t *w = sh ? a.sb_sh[kind] : a.sb[kind] + (size_t)mat * n;
     uint32_t smax = 0, bmax = 0;
@@ -716,6 +727,8 @@ hipError_t launch_stage_shift(const moe_layer *L, bool routed, bool shared, int3
     a.shared = shared;
     a.shift = L->ws.shift;
     a.faults = faults;
+    a.table = L->w.expert_slot;
+    a.E = D.n_experts;
     launch(k_stage_shift, dim3(L->n_mats + 1, 3), dim3(256), 0, s, a);
     return hipGetLastError();
 }

@@ -10,7 +10,12 @@
 //
 // Deterministic order: hits first (all of them, in one step), then the missing experts in
 // ascending expert order, each taking the lowest free slot, else the evictable slot with the
-// lowest use count, then the oldest last use, then the lowest slot index.
+// lowest use count, then the oldest last use, then the lowest slot index. A request may also name
+// protected experts: resident ones keep their slots (not evictable by this request) without
+// counting a use, which lets a caller plan the next tile of a chunk while the current tile's
+// experts still serve queued work (Mference system design, "Prefill": the next tile is fetched
+// while the current one is queued; "Correctness and safety invariants": a slot is not reused
+// while queued work owns it).
 #include <algorithm>
 #include <cstdint>
 #include <new>
@@ -56,23 +61,44 @@ void moe_slot_cache_destroy(moe_slot_cache *cache) { delete cache; }
 
 moe_status moe_slot_cache_plan(moe_slot_cache *c, const int32_t *experts, int32_t n, int32_t *slot_of,
                                int32_t *fill_expert, int32_t *fill_slot, int32_t *n_fill) {
+    return moe_slot_cache_plan_protected(c, experts, n, nullptr, 0, slot_of, fill_expert, fill_slot, n_fill);
+}
+
+moe_status moe_slot_cache_plan_protected(moe_slot_cache *c, const int32_t *experts, int32_t n,
+                                         const int32_t *protect, int32_t n_protect, int32_t *slot_of,
+                                         int32_t *fill_expert, int32_t *fill_slot, int32_t *n_fill) {
     qmoe::clear_error();
-    if (!c || !n_fill || (n > 0 && (!experts || !slot_of || !fill_expert || !fill_slot)))
+    if (!c || !n_fill || (n > 0 && (!experts || !slot_of || !fill_expert || !fill_slot)) ||
+        (n_protect > 0 && !protect))
         return fail(MOE_E_INVALID, "moe_slot_cache_plan: NULL argument");
-    if (n < 0) return fail(MOE_E_SHAPE, "moe_slot_cache_plan: n = %d is negative", n);
+    if (n < 0 || n_protect < 0) return fail(MOE_E_SHAPE, "moe_slot_cache_plan: n = %d or n_protect = %d is negative", n, n_protect);
     *n_fill = 0;
     // the request's distinct experts, ascending
     std::vector<int32_t> want(experts, experts + n);
     for (int32_t e : want)
         if (e < 0 || e >= c->n_experts)
             return fail(MOE_E_INVALID, "moe_slot_cache_plan: expert %d out of range [0, %d)", e, c->n_experts);
+    for (int32_t i = 0; i < n_protect; ++i)
+        if (protect[i] < 0 || protect[i] >= c->n_experts)
+            return fail(MOE_E_INVALID, "moe_slot_cache_plan: protected expert %d out of range [0, %d)", protect[i],
+                        c->n_experts);
     std::sort(want.begin(), want.end());
     want.erase(std::unique(want.begin(), want.end()), want.end());
-    if ((int32_t)want.size() > c->n_slots)
-        return fail(MOE_E_CAPACITY, "moe_slot_cache_plan: %zu distinct experts need more than the %d slots",
-                    want.size(), c->n_slots);
-    const int64_t req = c->request++;
+    // slots the request may not evict: those of its own experts (marked below) and of the
+    // resident protected experts it does not list
     std::vector<char> in_request(c->n_slots, 0);
+    int32_t n_kept = 0;
+    for (int32_t i = 0; i < n_protect; ++i) {
+        const int32_t s = c->slot_of[protect[i]];
+        if (s >= 0 && !in_request[s] && !std::binary_search(want.begin(), want.end(), protect[i])) {
+            in_request[s] = 1;
+            ++n_kept;
+        }
+    }
+    if ((int32_t)want.size() + n_kept > c->n_slots)
+        return fail(MOE_E_CAPACITY, "moe_slot_cache_plan: %zu distinct experts (and %d protected) need more than the %d slots",
+                    want.size(), n_kept, c->n_slots);
+    const int64_t req = c->request++;
     std::vector<int32_t> misses;
     for (int32_t e : want) {
         const int32_t s = c->slot_of[e];

@@ -113,11 +113,7 @@ class DeviceLayer:
         fills from pinned host memory into their slots and upload the slot table, all on the
         current stream (so later calls on it see them). Returns the number of fills."""
         _, fills = self.slot_cache.plan(experts)
-        for e, sl in fills:
-            for name, (hc, hs, pc, ps) in self._slot_src.items():
-                tc, ts = self._keep[name]
-                tc[sl * pc:(sl + 1) * pc].copy_(hc[e * pc:(e + 1) * pc], non_blocking=True)
-                ts[sl * ps:(sl + 1) * ps].copy_(hs[e * ps:(e + 1) * ps], non_blocking=True)
+        self._fill(fills)
         if fills:
             # a fresh pinned staging copy per update: an earlier upload may still be in flight
             tab = torch.from_numpy(self.slot_cache.table()).pin_memory()
@@ -125,13 +121,35 @@ class DeviceLayer:
             self._staged = tab
         return len(fills)
 
-    def prefill_tiled(self, x: torch.Tensor, y: Optional[torch.Tensor] = None):
-        """Prefill one chunk through the slot cache in expert tiles of at most n_slots experts
-        (experts already resident first): route once, then per tile make its experts resident
-        and run its projections with a table that maps only them, then combine.
+    def _fill(self, fills):
+        """Copy the planned fills [(expert, slot)] from pinned host memory into their slots (on
+        the current stream)."""
+        for e, sl in fills:
+            for name, (hc, hs, pc, ps) in self._slot_src.items():
+                tc, ts = self._keep[name]
+                tc[sl * pc:(sl + 1) * pc].copy_(hc[e * pc:(e + 1) * pc], non_blocking=True)
+                ts[sl * ps:(sl + 1) * ps].copy_(hs[e * ps:(e + 1) * ps], non_blocking=True)
+
+    def _upload_table(self, table: np.ndarray, keep: list):
+        tab = torch.from_numpy(np.ascontiguousarray(table, np.int32)).pin_memory()
+        self._table.copy_(tab, non_blocking=True)
+        keep.append(tab)
+
+    def prefill_tiled(self, x: torch.Tensor, y: Optional[torch.Tensor] = None, overlap: bool = False,
+                      tile_experts: Optional[int] = None):
+        """Prefill one chunk through the slot cache in expert tiles (Mference system design,
+        "Prefill"): route once, then per tile make its experts resident and run its projections
+        with a table that maps only them, then combine.
+
+        overlap: tiles of at most half the slots (tile_experts overrides), and the fills of tile
+        i + 1 run on a copy stream while tile i's kernels run: tile i + 1 is planned with tile i's
+        experts protected (they keep their slots), every fill waits for the last queued kernel
+        that read its slot, and a tile's kernels wait for its own fills. Without overlap, tiles of
+        up to n_slots experts and fills in line on the compute stream.
         Returns (y, tiles, fills)."""
         T = x.shape[0]
         D = self.dims_py
+        comp = torch.cuda.current_stream(self.device)
         if y is None:
             y = torch.empty((T, D.d_model), dtype=torch.float32, device=self.device)
         counts = torch.empty(D.n_experts, dtype=torch.int32, device=self.device)
@@ -139,21 +157,45 @@ class DeviceLayer:
         used = np.nonzero(counts.cpu().numpy())[0]
         table = self.slot_cache.table()
         order = [int(e) for e in used if table[e] >= 0] + [int(e) for e in used if table[e] < 0]
-        tiles = [order[i:i + self.n_slots] for i in range(0, len(order), self.n_slots)] or [[]]
-        fills = 0
-        staged = []
+        cap = tile_experts or (max(1, self.n_slots // 2) if overlap else self.n_slots)
+        tiles = [order[i:i + cap] for i in range(0, len(order), cap)] or [[]]
+        fills, staged, prev = 0, [], []
+        if overlap:
+            if getattr(self, "_copy_stream", None) is None:
+                self._copy_stream = torch.cuda.Stream(self.device)
+            copy = self._copy_stream
+            # fills may only start after everything queued before this chunk (earlier calls read
+            # the slots too)
+            start = torch.cuda.Event()
+            start.record(comp)
+            copy.wait_event(start)
+            reader = {}   # slot -> event after the last queued tile kernels that read it
         for ti, tile in enumerate(tiles):
-            fills += self.ensure(tile)
+            slot_of, plan_fills = self.slot_cache.plan(tile, protect=prev if overlap else ())
+            if plan_fills:
+                if overlap:
+                    with torch.cuda.stream(copy):
+                        for _, sl in plan_fills:
+                            if sl in reader:
+                                copy.wait_event(reader[sl])
+                        self._fill(plan_fills)
+                        done = torch.cuda.Event()
+                        done.record(copy)
+                    comp.wait_event(done)
+                else:
+                    self._fill(plan_fills)
+            fills += len(plan_fills)
             active = np.full(D.n_experts, -1, np.int32)
-            full = self.slot_cache.table()
-            active[tile] = full[tile]
-            tab = torch.from_numpy(active).pin_memory()
-            self._table.copy_(tab, non_blocking=True)
-            staged.append(tab)
+            active[tile] = slot_of
+            self._upload_table(active, staged)
             B.moe_prefill_tile(self.handle, T, ti)
-        tab = torch.from_numpy(self.slot_cache.table()).pin_memory()
-        self._table.copy_(tab, non_blocking=True)
-        staged.append(tab)
+            if overlap:
+                ev = torch.cuda.Event()
+                ev.record(comp)
+                for sl in slot_of:
+                    reader[sl] = ev
+            prev = tile
+        self._upload_table(self.slot_cache.table(), staged)
         self._staged_tiles = staged
         B.moe_prefill_combine(self.handle, T, y)
         return y, len(tiles), fills

@@ -128,26 +128,38 @@ def test_absent_slot_is_counted_and_contained():
     ref.close()
 
 
-def test_prefill_in_expert_tiles():
-    """More experts in the chunk than slots: tiles of at most n_slots experts."""
+@pytest.mark.parametrize("overlap", [False, True])
+def test_prefill_in_expert_tiles(overlap):
+    """More experts in the chunk than slots: tiles of at most n_slots experts filled in line, or
+    (overlap) tiles of at most half the slots whose fills run on a copy stream while the previous
+    tile's kernels run (Mference system design, "Prefill")."""
     lay = synth.gen_layer(DIMS, 94, router="normal", zipf_s=0.5)
     x, _, _ = synth.gen_tokens(DIMS, 150, 94)
     ref = DeviceLayer(lay, max_tokens=150)
     sl = DeviceLayer(lay, max_tokens=150, n_slots=8)
     xd = tokens_to_device(x)
     y_ref = ref.prefill(xd)
-    y, tiles, fills = sl.prefill_tiled(xd)
+    y, tiles, fills = sl.prefill_tiled(xd, overlap=overlap)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bits(y), bits(y_ref))
     err = check_oracle(y, lay, x, "tiled prefill")
-    assert tiles >= 3 and fills >= 8 * (tiles - 1)
-    y2, tiles2, fills2 = sl.prefill_tiled(xd)   # the residents of the last tile are reused first
+    per = 4 if overlap else 8
+    assert tiles >= 3 and fills >= per * (tiles - 1)
+    y2, tiles2, fills2 = sl.prefill_tiled(xd, overlap=overlap)   # residents of the last tile are reused first
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bits(y2), bits(y_ref))
     assert fills2 < fills
     assert B.moe_slot_faults(sl.handle) == 0
-    say(f"prefill: 150 tokens through 8 slots in {tiles} expert tiles ({fills} fills, then {fills2}), "
-        f"bit-identical, oracle max|err| {err:.2e} rms")
+    # a decode between chunks, then another chunk: fills wait for everything queued before them
+    sl.ensure(sl.route(xd[:1])["idx"].cpu().numpy().ravel())
+    y_d = sl.decode(xd[:1])
+    y3, _, _ = sl.prefill_tiled(xd, overlap=overlap)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(y3), bits(y_ref))
+    np.testing.assert_array_equal(bits(y_d), bits(ref.decode(xd[:1])))
+    assert B.moe_slot_faults(sl.handle) == 0
+    say(f"prefill (overlap {overlap}): 150 tokens through 8 slots in {tiles} expert tiles ({fills} fills, "
+        f"then {fills2}), bit-identical, oracle max|err| {err:.2e} rms")
     with pytest.raises(B.MoeError):
         B.moe_prefill_tile(ref.handle, 150, 0)   # a layer without slots
     # tiles and the combine belong to the chunk the layer routed last

@@ -25,13 +25,14 @@ class ModelLFU:
     def where(self, e):
         return self.expert.index(e) if e in self.expert else -1
 
-    def plan(self, experts):
+    def plan(self, experts, protect=()):
         want = sorted(set(int(e) for e in experts))
-        if len(want) > self.S:
+        kept = {self.where(int(e)) for e in protect if int(e) not in want and self.where(int(e)) >= 0}
+        if len(want) + len(kept) > self.S:
             return None
         r = self.req
         self.req += 1
-        used_now = set()
+        used_now = set(kept)   # protected residents are not evictable by this request
         misses = []
         for e in want:
             s = self.where(e)
@@ -106,6 +107,46 @@ def test_capacity_refused_without_change():
     c.close()
     with pytest.raises(B.MoeError):
         B.SlotCache(8, 9)   # more slots than experts
+
+
+def test_protected_experts_keep_their_slots():
+    """Planning the next tile while the current one is queued: the current tile's experts are
+    protected (not evicted, no use counted), so the next tile's misses take other slots."""
+    c = B.SlotCache(16, 4)
+    assert c.plan([0, 1]) == ([0, 1], [(0, 0), (1, 1)])
+    assert c.plan([2, 3], protect=[0, 1]) == ([2, 3], [(2, 2), (3, 3)])
+    # tile {4, 5} while {2, 3} is queued: 0 and 1 (one use each) are evicted, 2 and 3 kept
+    assert c.plan([4, 5], protect=[2, 3]) == ([0, 1], [(4, 0), (5, 1)])
+    # protection counts no use: 2 and 3 still have one use each, like 4 and 5; the oldest go
+    assert c.plan([6, 7], protect=[4, 5]) == ([2, 3], [(6, 2), (7, 3)])
+    # a protected expert that the request itself lists is an ordinary hit
+    assert c.plan([6, 8], protect=[6, 7]) == ([2, 0], [(8, 0)])
+    # the request plus the kept protected experts must fit
+    before = c.table().copy()
+    with pytest.raises(B.MoeError) as ei:
+        c.plan([9, 10, 11], protect=[6, 8])
+    assert ei.value.status == B.MOE_E_CAPACITY
+    np.testing.assert_array_equal(c.table(), before)
+    c.close()
+
+
+@pytest.mark.parametrize("E,S,k,seed", [(32, 8, 4, 3), (128, 16, 8, 4)])
+def test_random_tiles_with_protection_match_model(E, S, k, seed):
+    """Tiles of at most half the slots, each planned while the previous tile is protected."""
+    rng = np.random.default_rng(seed)
+    c = B.SlotCache(E, S)
+    m = ModelLFU(E, S)
+    prev = []
+    for _ in range(300):
+        tile = rng.choice(E, size=int(rng.integers(1, S // 2 + 1)), replace=False).astype(np.int32)
+        got = c.plan(tile, protect=prev)
+        want = m.plan(tile, protect=prev)
+        assert list(got[0]) == want[0] and got[1] == want[1]
+        t = c.table()
+        np.testing.assert_array_equal(t, m.table())
+        assert np.all(t[tile] >= 0) and np.all(t[np.array(prev, np.int32)] >= 0) if len(prev) else True
+        prev = tile.tolist()
+    c.close()
 
 
 @pytest.mark.parametrize("E,S,k,seed", [(32, 8, 4, 0), (128, 16, 8, 1), (64, 64, 8, 2)])

@@ -37,7 +37,7 @@ def build() -> str:
 
 
 class _QMat(C.Structure):
-    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("biases", C.c_void_p)]
+    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("biases", C.c_void_p), ("q4_0", C.c_int)]
 
 
 def lib():
@@ -54,6 +54,9 @@ def lib():
         L.orc_gelu_tanh.argtypes = [C.c_double]
         L.orc_gelu_tanh.restype = C.c_double
         L.orc_dequant_row.argtypes = [i32, i32, vp, vp, vp, vp]
+        L.orc_dequant_q4_0_row.argtypes = [i32, vp, vp]
+        L.orc_f16_to_f64.argtypes = [C.c_uint16]
+        L.orc_f16_to_f64.restype = C.c_double
         L.orc_router_logits.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp]
         L.orc_topk.argtypes = [i32, i32, i32, vp, vp, vp, vp]
         L.orc_router_prologue.argtypes = [i32, i32, vp, vp, C.c_double, vp]
@@ -94,6 +97,18 @@ def dequant_row(bits: int, codes, scales, biases, K: int) -> np.ndarray:
     out = np.empty(K, np.float64)
     codes, scales, biases = _c(codes, np.uint8), _c(scales, np.uint16), _c(biases, np.uint16)
     lib().orc_dequant_row(bits, K, _p(codes), _p(scales), _p(biases), _p(out))
+    return out
+
+
+def f16_to_f64(bits: int) -> float:
+    return float(lib().orc_f16_to_f64(int(bits)))
+
+
+def dequant_q4_0_row(blocks, K: int) -> np.ndarray:
+    """One row of K elements from K/32 Q4_0 blocks (uint8, 18 bytes each)."""
+    out = np.empty(K, np.float64)
+    blocks = _c(blocks, np.uint8)
+    lib().orc_dequant_q4_0_row(K, _p(blocks), _p(out))
     return out
 
 
@@ -148,9 +163,13 @@ class _Keep:
         self.refs = []
 
     def qmat(self, m) -> _QMat:
+        if getattr(m, "fmt", "affine") == "q4_0":
+            c = _c(m.codes, np.uint8)
+            self.refs.append(c)
+            return _QMat(_p(c), None, None, 1)
         c, s, b = _c(m.codes, np.uint8), _c(m.scales, np.uint16), _c(m.biases, np.uint16)
         self.refs += [c, s, b]
-        return _QMat(_p(c), _p(s), _p(b))
+        return _QMat(_p(c), _p(s), _p(b), 0)
 
 
 def ffn(x_f64, gate, up, down) -> np.ndarray:

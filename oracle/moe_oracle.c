@@ -10,6 +10,11 @@
  *  - Affine group-64 dequantization: weight = scale * code + bias, BF16 scale and
  *    BF16 bias per 64 consecutive input elements, 8-bit router codes, 4-bit expert
  *    codes (Mference system design, "Why the runtime has this shape").
+ *  - Q4_0 expert matrices, the alternative expert format: blocks of 32 elements in 18 bytes
+ *    (Gem native architecture, "M4 Max operating assumptions"; "Ownership boundaries": the GGUF
+ *    loader accepts Q4_0 matrices), read here as an fp16 scale d followed by 16 bytes of 4-bit
+ *    codes, element j < 16 in the low nibble of byte j and element j + 16 in its high nibble,
+ *    weight = d * (code - 8).
  *  - Router: one logit per expert from the 8-bit projection of the token, no
  *    softcap, top-8 by value, softmax over the selected logits (Mference,
  *    "Decode", the router listing; "Why the runtime has this shape" for the
@@ -113,6 +118,30 @@ void orc_dequant_row(int bits, int K, const uint8_t *codes, const uint16_t *scal
         out[i] = bf16_f64(scales[i / 64]) * (double)code_at(codes, i, bits) + bf16_f64(biases[i / 64]);
 }
 
+/* IEEE binary16 bits to float64, exactly (subnormals, infinities and NaN included). */
+double orc_f16_to_f64(uint16_t h) {
+    const int sign = h >> 15, e = (h >> 10) & 0x1F, m = h & 0x3FF;
+    double v;
+    if (e == 0) v = ldexp((double)m, -24);                      /* zero and subnormals: m 2^-24 */
+    else if (e == 31) v = m ? NAN : INFINITY;
+    else v = ldexp(1024.0 + (double)m, e - 25);                 /* (1 + m/1024) 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* Dequantize one row of K elements stored as K/32 Q4_0 blocks (18 bytes each: fp16 scale d,
+ * little-endian, then 16 code bytes): element 32b + j is d_b * (q - 8) with q the low nibble of
+ * code byte j (j < 16) or the high nibble of code byte j - 16 (j >= 16). */
+void orc_dequant_q4_0_row(int K, const uint8_t *blocks, double *out) {
+    for (int b = 0; b < K / 32; ++b) {
+        const uint8_t *blk = blocks + (size_t)b * 18;
+        const double d = orc_f16_to_f64((uint16_t)(blk[0] | (blk[1] << 8)));
+        for (int j = 0; j < 32; ++j) {
+            const int q = j < 16 ? (blk[2 + j] & 0xF) : (blk[2 + j - 16] >> 4);
+            out[32 * b + j] = d * (double)(q - 8);
+        }
+    }
+}
+
 /* ------------------------------------------------------------------ router */
 /*
  * Router logits in the canonical fp32 order, for tokens t < T and experts e < E.
@@ -213,19 +242,27 @@ double orc_gelu_tanh(double v) {
 }
 
 typedef struct {
-    const uint8_t *codes;    /* [out, in*bits/8] */
-    const uint16_t *scales;  /* [out, in/64] */
-    const uint16_t *biases;  /* [out, in/64] */
+    const uint8_t *codes;    /* affine: [out, in*bits/8]; Q4_0: blocks [out, in/32, 18 bytes] */
+    const uint16_t *scales;  /* affine: [out, in/64]; Q4_0: unused */
+    const uint16_t *biases;  /* affine: [out, in/64]; Q4_0: unused */
+    int q4_0;                /* 1: Q4_0 blocks */
 } orc_qmat;
+
+static size_t qmat_row_bytes(const orc_qmat *W, int bits, int in_dim) {
+    return W->q4_0 ? (size_t)in_dim / 32 * 18 : (size_t)in_dim * bits / 8;
+}
 
 /* y[out] = W x, W dequantized to float64 one row at a time. */
 static void qmatvec(int bits, int out_dim, int in_dim, const orc_qmat *W, const double *x,
                     double *y, double *rowbuf) {
-    const size_t row_bytes = (size_t)in_dim * bits / 8;
+    const size_t row_bytes = qmat_row_bytes(W, bits, in_dim);
     const int G = in_dim / 64;
     for (int o = 0; o < out_dim; ++o) {
-        orc_dequant_row(bits, in_dim, W->codes + (size_t)o * row_bytes, W->scales + (size_t)o * G,
-                        W->biases + (size_t)o * G, rowbuf);
+        if (W->q4_0)
+            orc_dequant_q4_0_row(in_dim, W->codes + (size_t)o * row_bytes, rowbuf);
+        else
+            orc_dequant_row(bits, in_dim, W->codes + (size_t)o * row_bytes, W->scales + (size_t)o * G,
+                            W->biases + (size_t)o * G, rowbuf);
         double acc = 0.0;
         for (int i = 0; i < in_dim; ++i) acc += rowbuf[i] * x[i];
         y[o] = acc;
@@ -254,11 +291,13 @@ void orc_ffn(int d, int I, const double *x, const orc_qmat *gate, const orc_qmat
 
 /* Expert e of a stack [E, out, ...] */
 static orc_qmat expert_view(const orc_qmat *stack, int e, int out_dim, int in_dim) {
-    orc_qmat m;
-    size_t row_bytes = (size_t)in_dim / 2, G = (size_t)in_dim / 64;
+    orc_qmat m = *stack;
+    size_t row_bytes = qmat_row_bytes(stack, 4, in_dim), G = (size_t)in_dim / 64;
     m.codes = stack->codes + (size_t)e * out_dim * row_bytes;
-    m.scales = stack->scales + (size_t)e * out_dim * G;
-    m.biases = stack->biases + (size_t)e * out_dim * G;
+    if (!stack->q4_0) {
+        m.scales = stack->scales + (size_t)e * out_dim * G;
+        m.biases = stack->biases + (size_t)e * out_dim * G;
+    }
     return m;
 }
 

@@ -18,6 +18,13 @@ design describes ("Why the runtime has this shape"): a weight is
 ``scale * code + bias`` with a BF16 scale and a BF16 bias per group of 64,
 8-bit codes for the router and 4-bit codes for the shared and routed experts.
 
+Expert matrices may instead be Q4_0 (Gem native architecture, "M4 Max operating
+assumptions": 32 elements in an 18-byte block). A Q4_0 matrix ``[out, in]`` is
+``uint8[..., out, in/32, 18]``: per block an fp16 scale d (little-endian), then 16
+bytes whose byte j holds element j in its low nibble and element j + 16 in its
+high nibble; the element's value is d * (code - 8). Its ``scales`` and
+``biases`` arrays are empty.
+
 Value distributions follow the five workloads the layer is measured on:
 uniform codes, BF16 scale ~ U(0.002, 0.02), bias = -(code midpoint) * scale
 + N(0, 1e-3); router weights N(0, 0.02) quantized per group by min-max for the
@@ -45,6 +52,7 @@ class Dims:
     group: int = GROUP
     router_bits: int = 8
     expert_bits: int = 4
+    expert_format: str = "affine"   # "affine" (group-64 scale/bias) or "q4_0" (32-element blocks)
 
     @property
     def G(self) -> int:
@@ -66,6 +74,7 @@ class Workload:
 
 TINY = Dims(d_model=256, n_experts=8, top_k=2, d_expert=128, d_shared=256)
 GEMMA = Dims(d_model=2816, n_experts=128, top_k=8, d_expert=704, d_shared=2112)
+GEMMA_Q4_0 = Dims(d_model=2816, n_experts=128, top_k=8, d_expert=704, d_shared=2112, expert_format="q4_0")
 # Qwen 3.6 style layer: 256 routed experts, top-8, a gated shared expert, experts about half
 # the size of the 2816-wide layer's (3 x 512 x 2048 against 3 x 704 x 2816 weights)
 QWEN = Dims(d_model=2048, n_experts=256, top_k=8, d_expert=512, d_shared=512)
@@ -78,6 +87,9 @@ WORKLOADS: Dict[str, Workload] = {
     "stack": Workload("stack", GEMMA, tokens=256, seed=2, layers=30),
     "prefill512": Workload("prefill512", GEMMA, tokens=512, seed=3, zipf_s=1.1),
     "prefill4096": Workload("prefill4096", GEMMA, tokens=4096, seed=4, zipf_s=1.3, tie_frac=0.02),
+    # the 2816-wide layer with Q4_0 experts
+    "q4_0_decode": Workload("q4_0_decode", GEMMA_Q4_0, tokens=1, seed=7),
+    "q4_0_prefill512": Workload("q4_0_prefill512", GEMMA_Q4_0, tokens=512, seed=8, zipf_s=1.1),
     "qwen_decode": Workload("qwen_decode", QWEN, tokens=1, seed=5, shared_gate=True),
     "qwen_prefill4096": Workload("qwen_prefill4096", QWEN, tokens=4096, seed=6, zipf_s=1.3, tie_frac=0.02,
                                  shared_gate=True),
@@ -103,13 +115,14 @@ def bf16_bits_to_f32(b) -> np.ndarray:
 # ----------------------------------------------------------------------------- quantized matrices
 @dataclass
 class QMat:
-    """One (or a stack of) affine-quantized matrices in the canonical layout."""
-    codes: np.ndarray   # uint8 [..., out, in*bits/8]
-    scales: np.ndarray  # uint16 [..., out, in/64]
-    biases: np.ndarray  # uint16 [..., out, in/64]
+    """One (or a stack of) quantized matrices in the canonical layout."""
+    codes: np.ndarray   # uint8 [..., out, in*bits/8]; Q4_0: [..., out, in/32 * 18] blocks
+    scales: np.ndarray  # uint16 [..., out, in/64]; Q4_0: [..., out, 0]
+    biases: np.ndarray  # uint16 [..., out, in/64]; Q4_0: [..., out, 0]
     bits: int
     out_dim: int
     in_dim: int
+    fmt: str = "affine"
 
 
 def _rng(seed: int, *key: int) -> np.random.Generator:
@@ -133,6 +146,31 @@ def uniform_qmat(rng: np.random.Generator, lead: tuple, out_dim: int, in_dim: in
     noise = rng.standard_normal(size=lead + (out_dim, G), dtype=np.float32) * np.float32(1e-3 * hi / 0.02)
     b = -mid * bf16_bits_to_f32(s_bits) + noise
     return QMat(codes, s_bits, f32_to_bf16_bits(b), bits, out_dim, in_dim)
+
+
+def q4_0_qmat(rng: np.random.Generator, lead: tuple, out_dim: int, in_dim: int,
+              scale_range=(0.002, 0.02)) -> QMat:
+    """Q4_0 blocks: uniform 4-bit codes, d = +-U(scale_range) (random sign) rounded to fp16."""
+    nb = in_dim // 32
+    shape = lead + (out_dim, nb)
+    n = int(np.prod(shape)) * 16
+    packed = rng.integers(0, 1 << 64, size=(n + 7) // 8, dtype=np.uint64).view(np.uint8)[:n]
+    lo, hi = scale_range
+    d = rng.random(size=shape, dtype=np.float32) * np.float32(hi - lo) + np.float32(lo)
+    d = np.where(rng.random(size=shape) < 0.5, -d, d).astype(np.float16)
+    blocks = np.empty(shape + (18,), np.uint8)
+    blocks[..., :2] = d.reshape(shape + (1,)).view(np.uint8)   # little-endian fp16
+    blocks[..., 2:] = packed.reshape(shape + (16,))
+    empty = np.zeros(lead + (out_dim, 0), np.uint16)
+    return QMat(blocks.reshape(lead + (out_dim, nb * 18)), empty, empty.copy(), 4, out_dim, in_dim, "q4_0")
+
+
+def expert_qmat(dims: Dims, rng: np.random.Generator, lead: tuple, out_dim: int, in_dim: int) -> QMat:
+    if dims.expert_format == "q4_0":
+        return q4_0_qmat(rng, lead, out_dim, in_dim)
+    if dims.expert_format != "affine":
+        raise ValueError(dims.expert_format)
+    return uniform_qmat(rng, lead, out_dim, in_dim, dims.expert_bits)
 
 
 def normal_router_qmat(rng: np.random.Generator, E: int, d: int, std: float = 0.02) -> QMat:
@@ -187,12 +225,12 @@ def gen_layer(dims: Dims, seed: int, *, router: str = "normal", zipf_s: Optional
         rq = uniform_qmat(_rng(seed, *key, 1), (), E, d, dims.router_bits, mid=8)
     else:
         raise ValueError(router)
-    gate = uniform_qmat(_rng(seed, *key, 2), (E,), I, d, dims.expert_bits)
-    up = uniform_qmat(_rng(seed, *key, 3), (E,), I, d, dims.expert_bits)
-    down = uniform_qmat(_rng(seed, *key, 4), (E,), d, I, dims.expert_bits)
-    sh_gate = uniform_qmat(_rng(seed, *key, 5), (), Is, d, dims.expert_bits)
-    sh_up = uniform_qmat(_rng(seed, *key, 6), (), Is, d, dims.expert_bits)
-    sh_down = uniform_qmat(_rng(seed, *key, 7), (), d, Is, dims.expert_bits)
+    gate = expert_qmat(dims, _rng(seed, *key, 2), (E,), I, d)
+    up = expert_qmat(dims, _rng(seed, *key, 3), (E,), I, d)
+    down = expert_qmat(dims, _rng(seed, *key, 4), (E,), d, I)
+    sh_gate = expert_qmat(dims, _rng(seed, *key, 5), (), Is, d)
+    sh_up = expert_qmat(dims, _rng(seed, *key, 6), (), Is, d)
+    sh_down = expert_qmat(dims, _rng(seed, *key, 7), (), d, Is)
     bias = None
     if zipf_s is not None:
         ranks = _rng(seed, *key, 8).permutation(E) + 1

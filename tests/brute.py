@@ -54,6 +54,12 @@ def unpack_codes(codes: np.ndarray, bits: int, K: int) -> np.ndarray:
 
 def dense(m) -> np.ndarray:
     """Dequantize a QMat (possibly stacked) to float64 [..., out, in]."""
+    if getattr(m, "fmt", "affine") == "q4_0":
+        blk = np.asarray(m.codes, np.uint8).reshape(m.codes.shape[:-1] + (m.in_dim // 32, 18))
+        d = np.ascontiguousarray(blk[..., :2]).view(np.float16)[..., 0].astype(np.float64)
+        body = blk[..., 2:]
+        q = np.concatenate([body & 0x0F, body >> 4], axis=-1).astype(np.int64)   # elements 0-15, 16-31
+        return (d[..., None] * (q - 8)).reshape(m.codes.shape[:-1] + (m.in_dim,))
     q = unpack_codes(m.codes, m.bits, m.in_dim)
     s = np.repeat(bf16_value(m.scales), 64, axis=-1)
     b = np.repeat(bf16_value(m.biases), 64, axis=-1)

@@ -97,6 +97,119 @@ def test_expert_blob_byte_accounting():
     assert blob * kv["n_experts"] * kv["n_layers"] == kv["total_bytes"]
 
 
+# ----------------------------------------------------------------------------- Q4_0 codec
+def _golden_q4_0():
+    def val(tok):
+        if "*2^" in tok:
+            a, e = tok.split("*2^")
+            return float(a) * 2.0 ** int(e)
+        return float(tok)
+    blocks = {}
+    for line in open(os.path.join(GOLD, "q4_0_blocks.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        name, key, *vals = line.split()
+        b = blocks.setdefault(name, {})
+        if key == "d":
+            b[key] = int(vals[0], 16)
+        elif key == "bytes":
+            b[key] = [int(v, 16) for v in vals]
+        else:
+            b[key] = np.array([val(v) for v in vals])
+    out = {}
+    for name, b in blocks.items():
+        raw = np.array([b["d"] & 0xFF, b["d"] >> 8] + b["bytes"], np.uint8)
+        assert raw.shape == (18,) and b["weights"].shape == (32,)
+        out[name] = (raw, b["weights"])
+    return out
+
+
+@pytest.mark.parametrize("name", ["P", "Q", "R", "S", "U"])
+def test_q4_0_hand_built_blocks(name):
+    raw, weights = _golden_q4_0()[name]
+    np.testing.assert_array_equal(oracle.dequant_q4_0_row(raw, 32), weights)
+
+
+def test_q4_0_blocks_follow_in_order():
+    """A row of several blocks: block b covers elements 32 b .. 32 b + 31, each with its own d."""
+    g = _golden_q4_0()
+    names = ["Q", "P", "S", "R", "U", "P"]
+    raw = np.concatenate([g[n][0] for n in names])
+    np.testing.assert_array_equal(oracle.dequant_q4_0_row(raw, 32 * len(names)),
+                                  np.concatenate([g[n][1] for n in names]))
+
+
+def test_fp16_decoding_matches_library_for_every_pattern():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_to_f64(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_q4_0_round_trip_of_a_block_quantizer():
+    """Blocks made by the usual Q4_0 quantizer (d = the block's largest-magnitude value / -8,
+    code = round(x / d) + 8 clamped to 0..15) dequantize to within |d| of every input."""
+    rng = np.random.default_rng(5)
+    K = 32 * 40
+    x = rng.standard_normal(K) * np.exp(rng.uniform(-6, 3, K // 32)).repeat(32)
+    raw = np.zeros((K // 32, 18), np.uint8)
+    dd = np.zeros(K // 32)
+    for b in range(K // 32):
+        xb = x[32 * b: 32 * b + 32]
+        amax = xb[np.argmax(np.abs(xb))]
+        d16 = np.float16(amax / -8.0)
+        dd[b] = float(d16)
+        q = np.clip(np.rint(xb / dd[b]) + 8, 0, 15).astype(np.uint8)
+        raw[b, :2] = np.array([d16]).view(np.uint8)
+        raw[b, 2:] = q[:16] | (q[16:] << 4)
+    w = oracle.dequant_q4_0_row(raw.reshape(-1), K)
+    assert np.all(np.abs(w - x) <= np.abs(dd).repeat(32) * (1 + 2.0 ** -9))
+    # the pin has teeth: the nibble halves swapped would miss by far more
+    swapped = raw.copy()
+    swapped[:, 2:] = (raw[:, 2:] >> 4) | (raw[:, 2:] << 4)
+    w2 = oracle.dequant_q4_0_row(swapped.reshape(-1), K)
+    assert np.max(np.abs(w2 - x) / np.abs(dd).repeat(32)) > 4
+
+
+def test_q4_0_layer_matches_dense_brute_force():
+    dims = synth.Dims(d_model=256, n_experts=8, top_k=3, d_expert=128, d_shared=192, expert_format="q4_0")
+    lay = synth.gen_layer(dims, 31, router="normal", zipf_s=0.8)
+    x, _, _ = synth.gen_tokens(dims, 4, 31)
+    _cmp_layer(lay, x, 4)
+
+
+def test_q4_0_layer_equals_affine_layer_with_the_same_weights():
+    """Q4_0 blocks whose two halves of a 64-group share d are the affine format with scale d,
+    bias -8 d (exact in bf16 when d has at most 8 significant bits): identical oracle outputs."""
+    dims = synth.Dims(d_model=256, n_experts=6, top_k=2, d_expert=64, d_shared=128)
+    lay = synth.gen_layer(dims, 33, router="normal")
+    qdims = synth.Dims(d_model=256, n_experts=6, top_k=2, d_expert=64, d_shared=128, expert_format="q4_0")
+    qlay = synth.gen_layer(qdims, 33, router="normal")
+    for name in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down"):
+        m = getattr(lay, name)
+        sval = synth.bf16_bits_to_f32(m.scales)
+        # biases -8 * scale exactly (bf16 keeps the scale's 8 significant bits)
+        m.biases = synth.f32_to_bf16_bits(np.float32(-8.0) * sval)
+        # the same weights as Q4_0: element 32 h + i of group g from the canonical nibbles
+        q = np.stack([m.codes & 0x0F, m.codes >> 4], axis=-1).reshape(m.codes.shape[:-1] + (m.in_dim,))
+        qb = q.reshape(q.shape[:-1] + (m.in_dim // 32, 32))
+        d16 = sval.astype(np.float16).repeat(2, axis=-1)      # bf16 values are exact in fp16 here
+        assert np.array_equal(d16.astype(np.float32), sval.repeat(2, axis=-1))
+        blk = np.empty(qb.shape[:-1] + (18,), np.uint8)
+        blk[..., :2] = d16[..., None].view(np.uint8)
+        blk[..., 2:] = (qb[..., :16] | (qb[..., 16:] << 4)).astype(np.uint8)
+        qm = getattr(qlay, name)
+        qm.codes = blk.reshape(qm.codes.shape)
+    x, _, _ = synth.gen_tokens(dims, 5, 33)
+    ya, ra = oracle.layer_forward(lay, x)
+    yq, rq = oracle.layer_forward(qlay, x)
+    np.testing.assert_array_equal(ra["idx"], rq["idx"])
+    np.testing.assert_array_equal(ya, yq)
+
+
 # ----------------------------------------------------------------------------- router
 def _dyadic_router_case(rng, T=3, E=5, d=128):
     """Inputs on which every fp32 operation of the router is exact."""

@@ -88,6 +88,19 @@ typedef enum {
 /* Largest number of routed experts the kernels support. */
 #define MOE_MAX_EXPERTS 1024
 
+/*
+ * Formats of the expert matrices (routed and shared; the router is always 8-bit affine):
+ *   MOE_FORMAT_AFFINE_G64: weight = scale * code + bias, 4-bit codes, one BF16 scale and one
+ *     BF16 bias per 64 consecutive inputs (Mference system design, "Why the runtime has this
+ *     shape").
+ *   MOE_FORMAT_Q4_0: weight = d * (code - 8), 4-bit codes, one fp16 scale d per 32 consecutive
+ *     inputs (Gem native architecture, "M4 Max operating assumptions": 32 weights in an 18-byte
+ *     block; "Ownership boundaries": the GGUF loader accepts Q4_0 matrices). Host blocks are
+ *     converted with moe_repack_q4_0.
+ */
+#define MOE_FORMAT_AFFINE_G64 0
+#define MOE_FORMAT_Q4_0 1
+
 typedef struct {
     int32_t d_model;     /* model width d; multiple of 64 in [64, 8192] */
     int32_t n_experts;   /* routed experts E, 1..MOE_MAX_EXPERTS */
@@ -98,13 +111,17 @@ typedef struct {
     int32_t router_bits; /* must be 8 */
     int32_t expert_bits; /* must be 4 */
     int32_t max_tokens;  /* workspace capacity in tokens per call, >= 1 */
+    int32_t expert_format; /* MOE_FORMAT_AFFINE_G64 (0) or MOE_FORMAT_Q4_0 (1); other values are
+                              MOE_E_QUANT */
 } moe_dims;
 
 /*
  * One quantized matrix (or a stack of E of them) in the device layout:
  *   codes: device bytes, layout per moe_repack;
- *   sb:    device uint32 words, each (bf16 scale) | (bf16 bias << 16), one per
- *          (row, group of 64 inputs), layout per moe_repack.
+ *   sb:    device uint32 words, one per (row, group of 64 inputs), layout per moe_repack:
+ *          affine: (bf16 scale) | (bf16 bias << 16);
+ *          Q4_0 expert matrices: (fp16 d of inputs 0..31 of the group) | (fp16 d of inputs
+ *          32..63 << 16).
  */
 typedef struct {
     const void *codes;
@@ -179,8 +196,10 @@ typedef struct {
  * significant bits for scales of any magnitude. At creation the library reads every expert
  * matrix's scale/bias words once and waits for the result: a NaN or infinite scale or bias, a
  * largest |scale| outside [2^-73, 2^56), or a bias with floor(log2 |bias|) >=
- * floor(log2 max |scale|) + 24 in its matrix is MOE_E_QUANT. Layers with expert slots check the routed experts' words in
- * every prefill call instead (see expert_slot), since the slots are filled later.
+ * floor(log2 max |scale|) + 24 in its matrix is MOE_E_QUANT. For Q4_0 experts (weight
+ * d (q - 8)) the staged value is fp16(2^m (d q - 8 d)) and only a NaN or infinite d is refused
+ * (every finite fp16 d can be staged). Layers with expert slots check the routed experts'
+ * words in every prefill call instead (see expert_slot), since the slots are filled later.
  * *out is written only on MOE_OK.
  */
 moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t flags,
@@ -324,6 +343,28 @@ moe_status moe_repack(int32_t bits, int32_t n_mats, int32_t out_dim, int32_t in_
 moe_status moe_unrepack(int32_t bits, int32_t n_mats, int32_t out_dim, int32_t in_dim,
                         const void *codes_in, const uint32_t *sb_in, uint8_t *codes,
                         uint16_t *scales, uint16_t *biases);
+
+/*
+ * Host-to-host lossless repack of Q4_0 expert matrices (MOE_FORMAT_Q4_0) into the device
+ * layout (Mference, "Source weights and bounded repack": a packed sidecar derived
+ * reproducibly, codes moved and never re-quantized).
+ *   blocks: [n_mats, out, in/32] blocks of 18 bytes: fp16 d (little-endian), then 16 bytes,
+ *           byte j holding the code of element j in its low nibble and of element j + 16 in
+ *           its high nibble; weight = d * (code - 8).
+ *   codes_out: the 4-bit tile layout of moe_repack (moe_packed_bytes(4, ..., 0) bytes), codes
+ *           unchanged (0..15); sb_out: one word per (row, group of 64 inputs) in moe_repack's
+ *           order, d of the group's first block in the low half, of its second block in the
+ *           high half.
+ * out must be a multiple of 32 and in a multiple of 64 (MOE_E_SHAPE); NULL pointers are
+ * MOE_E_INVALID. Nothing is written on error. Scales are copied as bit patterns; NaN or
+ * infinite scales are refused later by moe_layer_create (MOE_E_QUANT).
+ */
+moe_status moe_repack_q4_0(int32_t n_mats, int32_t out_dim, int32_t in_dim, const uint8_t *blocks,
+                           void *codes_out, uint32_t *sb_out);
+
+/* Exact inverse of moe_repack_q4_0 (host to host): device layout back to the 18-byte blocks. */
+moe_status moe_unrepack_q4_0(int32_t n_mats, int32_t out_dim, int32_t in_dim, const void *codes_in,
+                             const uint32_t *sb_in, uint8_t *blocks);
 
 /* ---------------------------------------------------------------- diagnostics */
 

@@ -39,7 +39,12 @@ class MoeError(RuntimeError):
 
 class moe_dims(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("d_model", "n_experts", "top_k", "d_expert", "d_shared", "group",
-                                         "router_bits", "expert_bits", "max_tokens")]
+                                         "router_bits", "expert_bits", "max_tokens", "expert_format")]
+
+
+MOE_FORMAT_AFFINE_G64 = 0
+MOE_FORMAT_Q4_0 = 1
+FORMATS = {"affine": MOE_FORMAT_AFFINE_G64, "q4_0": MOE_FORMAT_Q4_0}
 
 
 class moe_qmat(C.Structure):
@@ -83,6 +88,8 @@ def lib() -> C.CDLL:
             "moe_packed_bytes": (C.c_size_t, [i32, i32, i32, i32, i32]),
             "moe_repack": (st, [i32, i32, i32, i32, C.POINTER(moe_host_qmat), vp, vp]),
             "moe_unrepack": (st, [i32, i32, i32, i32, vp, vp, vp, vp, vp]),
+            "moe_repack_q4_0": (st, [i32, i32, i32, vp, vp, vp]),
+            "moe_unrepack_q4_0": (st, [i32, i32, i32, vp, vp, vp]),
             "moe_status_str": (C.c_char_p, [st]),
             "moe_last_error": (C.c_char_p, []),
             "moe_profile_enable": (st, [vp, i32]),
@@ -225,6 +232,27 @@ def moe_unrepack(bits, n_mats, out_dim, in_dim, codes_dev, sb_dev):
     _check(lib().moe_unrepack(bits, n_mats, out_dim, in_dim, codes_dev.ctypes.data, sb_dev.ctypes.data,
                               codes.ctypes.data, scales.ctypes.data, biases.ctypes.data), "moe_unrepack")
     return codes, scales, biases
+
+
+def moe_repack_q4_0(n_mats, out_dim, in_dim, blocks):
+    """Q4_0 host blocks (uint8, 18 bytes per 32 inputs) -> (device-layout codes uint8, sb uint32)."""
+    blocks = np.ascontiguousarray(blocks, np.uint8)
+    nc = moe_packed_bytes(4, n_mats, out_dim, in_dim, 0)
+    ns = moe_packed_bytes(4, n_mats, out_dim, in_dim, 1)
+    out_c = np.empty(max(nc, 1), np.uint8)
+    out_s = np.empty(max(ns // 4, 1), np.uint32)
+    _check(lib().moe_repack_q4_0(n_mats, out_dim, in_dim, blocks.ctypes.data, out_c.ctypes.data, out_s.ctypes.data),
+           "moe_repack_q4_0")
+    return out_c, out_s
+
+
+def moe_unrepack_q4_0(n_mats, out_dim, in_dim, codes_dev, sb_dev):
+    blocks = np.empty((n_mats, out_dim, in_dim // 32 * 18), np.uint8)
+    codes_dev = np.ascontiguousarray(codes_dev, np.uint8)
+    sb_dev = np.ascontiguousarray(sb_dev, np.uint32)
+    _check(lib().moe_unrepack_q4_0(n_mats, out_dim, in_dim, codes_dev.ctypes.data, sb_dev.ctypes.data,
+                                   blocks.ctypes.data), "moe_unrepack_q4_0")
+    return blocks
 
 
 def moe_profile_enable(handle, on: bool):

@@ -9,6 +9,9 @@
 //
 // Affine split per group (x the 64 inputs of the group):
 //   sum_j x_j (s q_j + b) = (2^24 s) * sum_j x_j (q_j 2^-24) + b * sum_j x_j.
+// Q4_0 expert matrices (weight d (q - 8), one fp16 d per 32 inputs) split per block the same
+// way, with scale d and bias -8 d: the two halves of a group keep their own dot products and
+// input sums (the router and the 16-value h sums provide half-group sums instead).
 // q 2^-24 is the fp16 subnormal whose mantissa is q, so masking a device-layout word gives
 // two of them at once (exact; see nib_sub), and v_dot2_f32_f16 forms x_j q_j 2^-24 with fp32
 // accumulation. The inputs enter as fp16: h is fp16; x is converted when it is staged, which
@@ -52,7 +55,8 @@ constexpr size_t kGlueLdsMax = 32768;   // bf16 bytes of x the fused residual st
 // A[t][g] into Ps, then lanes t < T sum over g in ascending order. Fixed fp32 order:
 //   w_j = fma(s, q_j, b); A = fma chain of x_j w_j, ascending j; L = ((0 + A_0) + A_1) + ...
 // The group sums X = ((0 + x_0) + x_1) + ... go to xg_out when it is given (the gate/up
-// units' bias terms use them; they are not part of the logits).
+// units' bias terms use them; they are not part of the logits); with halves = 2 (Q4_0
+// experts) the sums of the group's two halves of 32, each in the same order.
 // The 64 codes and the scale/bias word of expert e's input group g.
 struct RouterCodes {
     u32x4_t c[4];
@@ -70,7 +74,8 @@ __device__ __forceinline__ RouterCodes router_codes(const uint8_t *__restrict__ 
 
 // pre: the codes of group `lane` when the caller loaded them ahead (or null)
 __device__ __forceinline__ void router_wave(const uint16_t *__restrict__ x, int T, int d, int e, const uint8_t *__restrict__ rq,
-                            const uint32_t *__restrict__ rsb, float *Ps, float *xg_out, const RouterCodes *pre) {
+                            const uint32_t *__restrict__ rsb, float *Ps, float *xg_out, const RouterCodes *pre,
+                            int halves) {
 #pragma clang fp contract(off)
     const int G = d / 64, lane = threadIdx.x & 63;
     for (int g = lane; g < G; g += 64) {
@@ -85,9 +90,13 @@ __device__ __forceinline__ void router_wave(const uint16_t *__restrict__ x, int 
             u32x4_t xv[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) xv[i] = xp[i];
-            float X = 0.0f, A = 0.0f;
+            float X = 0.0f, X0 = 0.0f, A = 0.0f;
 #pragma unroll
             for (int j2 = 0; j2 < 32; ++j2) {          // element pair (2 j2, 2 j2 + 1)
+                if (j2 == 16 && halves == 2) {   // the first half's sum is complete
+                    X0 = X;
+                    X = 0.0f;
+                }
                 const uint32_t xw = xv[j2 >> 2][j2 & 3];
                 const float xa = bf16_to_f32(xw & 0xFFFFu), xb = bf16_to_f32(xw >> 16);
                 const uint32_t c = cw[j2 >> 1];
@@ -99,7 +108,12 @@ __device__ __forceinline__ void router_wave(const uint16_t *__restrict__ x, int 
                 A = __builtin_fmaf(xb, __builtin_fmaf(sc, qb, bi), A);
             }
             Ps[t * G + g] = A;
-            if (xg_out) xg_out[t * G + g] = X;
+            if (xg_out && halves == 2) {
+                xg_out[(size_t)t * 2 * G + 2 * g] = X0;
+                xg_out[(size_t)t * 2 * G + 2 * g + 1] = X;
+            } else if (xg_out) {
+                xg_out[t * G + g] = X;
+            }
         }
     }
 }
@@ -210,7 +224,7 @@ __device__ __forceinline__ float row_sum16(float v) {
 // pairs per batch. load(i0) issues one batch (unconditionally: pairs past the input re-read
 // a valid group and are masked later), so a caller can put the first batch in flight before
 // it stages the input; compute(i0) consumes it with x (fp16) and its group sums Xs in LDS.
-template <int MP>
+template <int MP, bool Q4>
 struct GateUp16 {
     const uint8_t *Wg, *Wu;
     const uint32_t *Sg, *Su;
@@ -246,40 +260,55 @@ struct GateUp16 {
             su[i] = Su[(uint32_t)g * 32 + so];
         }
     }
+    // Xs: the group sums of x (Q4_0: half-group sums, two per group)
     __device__ __forceinline__ void compute(int i0, const uint16_t *xs, const float *Xs, float &accg, float &accu) const {
 #pragma unroll
         for (int i = 0; i < MP; ++i) {
             const int g = 2 * (p0 + PS * (i0 + i)) + gsel;
             const int gc = min(g, G - 1);
-            // pairs 0 and 2 of a word carry q 2^-24, pairs 1 and 3 carry 16 q 2^-24
-            float ag0 = 0.0f, ag1 = 0.0f, au0 = 0.0f, au1 = 0.0f;
+            // pairs 0 and 2 of a word carry q 2^-24, pairs 1 and 3 carry 16 q 2^-24; [h]: K-steps
+            // 2 h, 2 h + 1 (inputs 32 h .. 32 h + 31 of the group)
+            float ag0[2] = {0.0f, 0.0f}, ag1[2] = {0.0f, 0.0f}, au0[2] = {0.0f, 0.0f}, au1[2] = {0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
+                const int h = Q4 ? s >> 1 : 0;
                 const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xs + 64 * gc + 16 * s + 8 * khalf);
                 const u32x4_t pg = nib_sub(wg[i][s]), pu = nib_sub(wu[i][s]);
-                ag0 = dot2_f16(xv[0], pg[0], ag0);
-                ag1 = dot2_f16(xv[1], pg[1], ag1);
-                au0 = dot2_f16(xv[0], pu[0], au0);
-                au1 = dot2_f16(xv[1], pu[1], au1);
-                ag0 = dot2_f16(xv[2], pg[2], ag0);
-                ag1 = dot2_f16(xv[3], pg[3], ag1);
-                au0 = dot2_f16(xv[2], pu[2], au0);
-                au1 = dot2_f16(xv[3], pu[3], au1);
+                ag0[h] = dot2_f16(xv[0], pg[0], ag0[h]);
+                ag1[h] = dot2_f16(xv[1], pg[1], ag1[h]);
+                au0[h] = dot2_f16(xv[0], pu[0], au0[h]);
+                au1[h] = dot2_f16(xv[1], pu[1], au1[h]);
+                ag0[h] = dot2_f16(xv[2], pg[2], ag0[h]);
+                ag1[h] = dot2_f16(xv[3], pg[3], ag1[h]);
+                au0[h] = dot2_f16(xv[2], pu[2], au0[h]);
+                au1[h] = dot2_f16(xv[3], pu[3], au1[h]);
             }
-            const float ag = fmaf(ag1, 0.0625f, ag0), au = fmaf(au1, 0.0625f, au0);
             const float on = g < G ? 1.0f : 0.0f;
-            const float X = Xs[gc] * (khalf == 0 ? 1.0f : 0.0f);   // the X_g term once per (row, group)
-            const float s24g = 16777216.0f * bf16_to_f32(sg[i] & 0xFFFFu);
-            const float s24u = 16777216.0f * bf16_to_f32(su[i] & 0xFFFFu);
-            accg = fmaf(on, fmaf(s24g, ag, bf16_to_f32(sg[i] >> 16) * X), accg);
-            accu = fmaf(on, fmaf(s24u, au, bf16_to_f32(su[i] >> 16) * X), accu);
+            const float first = khalf == 0 ? 1.0f : 0.0f;   // the input-sum terms once per (row, group)
+            if constexpr (Q4) {
+                // d (2^24 A - 8 X) per block, A = sum x q 2^-24 over the block, X its input sum
+                const float X0 = Xs[2 * gc] * first, X1 = Xs[2 * gc + 1] * first;
+                const float g0 = fmaf(16777216.0f, fmaf(ag1[0], 0.0625f, ag0[0]), -8.0f * X0);
+                const float g1 = fmaf(16777216.0f, fmaf(ag1[1], 0.0625f, ag0[1]), -8.0f * X1);
+                const float u0 = fmaf(16777216.0f, fmaf(au1[0], 0.0625f, au0[0]), -8.0f * X0);
+                const float u1 = fmaf(16777216.0f, fmaf(au1[1], 0.0625f, au0[1]), -8.0f * X1);
+                accg = fmaf(on, fmaf(f16_to_f32(sg[i] & 0xFFFFu), g0, f16_to_f32(sg[i] >> 16) * g1), accg);
+                accu = fmaf(on, fmaf(f16_to_f32(su[i] & 0xFFFFu), u0, f16_to_f32(su[i] >> 16) * u1), accu);
+            } else {
+                const float ag = fmaf(ag1[0], 0.0625f, ag0[0]), au = fmaf(au1[0], 0.0625f, au0[0]);
+                const float X = Xs[gc] * first;
+                const float s24g = 16777216.0f * bf16_to_f32(sg[i] & 0xFFFFu);
+                const float s24u = 16777216.0f * bf16_to_f32(su[i] & 0xFFFFu);
+                accg = fmaf(on, fmaf(s24g, ag, bf16_to_f32(sg[i] >> 16) * X), accg);
+                accu = fmaf(on, fmaf(s24u, au, bf16_to_f32(su[i] >> 16) * X), accu);
+            }
         }
     }
 };
 
 // Down sum of 16 rows over group pairs p = p0, p0 + PS, ... of an fp16 input h (LDS, with its
 // group sums Hs), MP pairs per batch; load / compute as in GateUp16.
-template <int MP>
+template <int MP, bool Q4>
 struct Down16 {
     const uint8_t *W;
     const uint32_t *S;
@@ -318,20 +347,28 @@ struct Down16 {
             asm volatile("" ::: "memory");
             const int g = 2 * (p0 + PS * (i0 + i)) + gsel;
             const int gc = min(g, G - 1);
-            float a0 = 0.0f, a1 = 0.0f;
+            float a0[2] = {0.0f, 0.0f}, a1[2] = {0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
+                const int h = Q4 ? s >> 1 : 0;
                 const u32x4_t hv = *reinterpret_cast<const u32x4_t *>(hl + 64 * gc + 16 * s + 8 * khalf);
                 const u32x4_t p = nib_sub(w[i][s]);
-                a0 = dot2_f16(hv[0], p[0], a0);
-                a1 = dot2_f16(hv[1], p[1], a1);
-                a0 = dot2_f16(hv[2], p[2], a0);
-                a1 = dot2_f16(hv[3], p[3], a1);
+                a0[h] = dot2_f16(hv[0], p[0], a0[h]);
+                a1[h] = dot2_f16(hv[1], p[1], a1[h]);
+                a0[h] = dot2_f16(hv[2], p[2], a0[h]);
+                a1[h] = dot2_f16(hv[3], p[3], a1[h]);
             }
             const float on = g < G ? 1.0f : 0.0f;
-            const float H = Hs[gc] * (khalf == 0 ? 1.0f : 0.0f);
-            const float s24 = 16777216.0f * bf16_to_f32(sb[i] & 0xFFFFu);
-            acc = fmaf(on, fmaf(s24, fmaf(a1, 0.0625f, a0), bf16_to_f32(sb[i] >> 16) * H), acc);
+            const float first = khalf == 0 ? 1.0f : 0.0f;
+            if constexpr (Q4) {   // Hs: half-group sums of h
+                const float r0 = fmaf(16777216.0f, fmaf(a1[0], 0.0625f, a0[0]), -8.0f * (Hs[2 * gc] * first));
+                const float r1 = fmaf(16777216.0f, fmaf(a1[1], 0.0625f, a0[1]), -8.0f * (Hs[2 * gc + 1] * first));
+                acc = fmaf(on, fmaf(f16_to_f32(sb[i] & 0xFFFFu), r0, f16_to_f32(sb[i] >> 16) * r1), acc);
+            } else {
+                const float H = Hs[gc] * first;
+                const float s24 = 16777216.0f * bf16_to_f32(sb[i] & 0xFFFFu);
+                acc = fmaf(on, fmaf(s24, fmaf(a1[0], 0.0625f, a0[0]), bf16_to_f32(sb[i] >> 16) * H), acc);
+            }
         }
         return acc;
     }
@@ -348,7 +385,8 @@ struct DecArgs {
     int32_t *idx;
     float *wts;
     moe_qmat gate, up, down, sh_gate, sh_up, sh_down;
-    float *xg;              // [T][d/64]        group sums of x (router, fixed order)
+    float *xg;              // [T][d/64]        group sums of x (router, fixed order); Q4_0: [T][d/32] half sums
+    int q4_0;               // expert matrices in Q4_0 (1) or affine (0)
     uint16_t *h_r;          // [T*k][I]         routed hidden activations (fp16 bits)
     uint16_t *h_s;          // [T][I_s]         shared hidden activations (fp16 bits)
     float *hs_r;            // [T*k][I/16]      sums of 16 consecutive routed h values
@@ -411,12 +449,13 @@ __global__ __launch_bounds__(64 * kRW) void k_dec_router(DecArgs a) {
         }
         if (PRO) {
             __syncthreads();
-            if (blockIdx.x == 0 && tid < G) {   // X_g = ((0 + x_0) + x_1) + ... + x_63, fp32
+            const int NX = a.q4_0 ? 2 * G : G, NL = 64 * G / NX;   // sums per token, inputs per sum
+            if (blockIdx.x == 0 && tid < NX) {   // X = ((0 + x_0) + x_1) + ... over NL inputs, fp32
 #pragma clang fp contract(off)
                 for (int t = 0; t < a.T; ++t) {
                     float X = 0.0f;
-                    for (int j = 0; j < 64; ++j) X = X + bf16_to_f32(xs[(size_t)t * a.d + 64 * tid + j]);
-                    a.xg[(size_t)t * G + tid] = X;
+                    for (int j = 0; j < NL; ++j) X = X + bf16_to_f32(xs[(size_t)t * a.d + NL * tid + j]);
+                    a.xg[(size_t)t * NX + tid] = X;
                 }
             }
             __syncthreads();   // x_out and the group sums are read from xs before it is rewritten
@@ -427,7 +466,8 @@ __global__ __launch_bounds__(64 * kRW) void k_dec_router(DecArgs a) {
     }
     float *P = Ps + (size_t)wave * a.T * G;
     if (e < a.E)
-        router_wave(x, a.T, a.d, e, a.rq, a.rsb, P, (!PRO && e == 0) ? a.xg : nullptr, LDSX ? &pre : nullptr);
+        router_wave(x, a.T, a.d, e, a.rq, a.rsb, P, (!PRO && e == 0) ? a.xg : nullptr, LDSX ? &pre : nullptr,
+                    a.q4_0 ? 2 : 1);
     __syncthreads();
     if (e < a.E && lane < a.T) {
 #pragma clang fp contract(off)
@@ -440,15 +480,15 @@ __global__ __launch_bounds__(64 * kRW) void k_dec_router(DecArgs a) {
 
 // ----------------------------------------------------------------------------- launch B
 // grid: T * k * (I / 16) routed units, then T * (I_s / 16) shared units; block 64 * kBW.
-// LDS: x [d fp16] | Xs [d/64 floats] | red [kBW][2][16]
-template <int kPer>
+// LDS: x [d fp16] | Xs [NX floats] | red [kBW][2][16], NX = d/64 group sums (Q4_0: d/32 half sums)
+template <int kPer, bool Q4>
 __global__ __launch_bounds__(64 * kBW) void k_dec_gateup(DecArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int G = a.d / 64;
+    const int G = a.d / 64, NX = Q4 ? 2 * G : G;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
     float *Xs = reinterpret_cast<float *>(smem + sizeof(uint16_t) * a.d);
-    float(*red)[2][16] = reinterpret_cast<float(*)[2][16]>(smem + sizeof(uint16_t) * a.d + sizeof(float) * G);
+    float(*red)[2][16] = reinterpret_cast<float(*)[2][16]>(smem + sizeof(uint16_t) * a.d + sizeof(float) * NX);
     const int JBr = a.I / 16, JBs = a.Is / 16;
     const int nR = a.T * a.k * JBr;
     const bool routed = (int)blockIdx.x < nR;
@@ -467,7 +507,7 @@ __global__ __launch_bounds__(64 * kBW) void k_dec_gateup(DecArgs a) {
     u32x4_t xv[kXC];
 #pragma unroll
     for (int c = 0; c < kXC; ++c) xv[c] = ld16(xrow + 8 * min(tid + 64 * kBW * c, a.d / 8 - 1));
-    const float xgv = a.xg[(size_t)t * G + min(tid, G - 1)];
+    const float xgv = a.xg[(size_t)t * NX + min(tid, NX - 1)];   // NX <= 256 threads
 
     const moe_qmat *mg = &a.sh_gate, *mu = &a.sh_up;
     size_t cbase = 0, sbase = 0;
@@ -489,7 +529,7 @@ __global__ __launch_bounds__(64 * kBW) void k_dec_gateup(DecArgs a) {
         sbase = (size_t)es * a.I * G;
     }
     // the first batch of weights goes out before x is staged
-    GateUp16<kMPB> gu(static_cast<const uint8_t *>(mg->codes) + cbase, static_cast<const uint8_t *>(mu->codes) + cbase,
+    GateUp16<kMPB, Q4> gu(static_cast<const uint8_t *>(mg->codes) + cbase, static_cast<const uint8_t *>(mu->codes) + cbase,
                       mg->sb + sbase, mu->sb + sbase, jb >> 1, jb & 1, G, wave, kBW);
     gu.load(0);
 #pragma unroll
@@ -497,7 +537,7 @@ __global__ __launch_bounds__(64 * kBW) void k_dec_gateup(DecArgs a) {
         const int i = tid + 64 * kBW * c;
         if (i < a.d / 8) *reinterpret_cast<u32x4_t *>(xs + 8 * i) = bf16x8_to_f16x8(xv[c]);
     }
-    if (tid < G) Xs[tid] = xgv;
+    if (tid < NX) Xs[tid] = xgv;
     __syncthreads();
     float accg = 0.0f, accu = 0.0f;
     gu.compute(0, xs, Xs, accg, accu);
@@ -548,8 +588,8 @@ __global__ __launch_bounds__(64 * kBW) void k_dec_gateup(DecArgs a) {
 // shared down projection's group pairs go round-robin to waves k..NW-1 (to all waves when
 // k == 16).
 // LDS: h_r of the k slots [k][I] | h_s [I_s] | Hr [k][I/64] | Hsh [I_s/64] | Ws [k] |
-//      part_r [k][16] | part_s [NW][16]
-template <int MAXT>
+//      part_r [k][16] | part_s [NW][16]; Q4_0: Hr [k][I/32] and Hsh [I_s/32] half-group sums
+template <int MAXT, bool Q4>
 __global__ __launch_bounds__(MAXT) void k_dec_down(DecArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int RB = a.d / 16, GI = a.I / 64, GS = a.Is / 64;
@@ -560,8 +600,9 @@ __global__ __launch_bounds__(MAXT) void k_dec_down(DecArgs a) {
     uint16_t *hr = reinterpret_cast<uint16_t *>(smem);
     uint16_t *hsh = hr + (size_t)a.k * a.I;
     float *Hr = reinterpret_cast<float *>(hsh + a.Is);
-    float *Hsh = Hr + a.k * GI;
-    float *Ws = Hsh + GS;
+    constexpr int NH = Q4 ? 2 : 1;   // input sums per group
+    float *Hsh = Hr + a.k * GI * NH;
+    float *Ws = Hsh + GS * NH;
     float *part_r = Ws + a.k;
     float *part_s = part_r + a.k * 16;
     // the expert indices, then the (small) staging reads, then this wave's first batch of
@@ -584,9 +625,9 @@ __global__ __launch_bounds__(MAXT) void k_dec_down(DecArgs a) {
     const float qs0 = qs[0], qs1 = qs[1], qs2 = qs[2], qs3 = qs[3];
     const float wv = a.wts[(size_t)t * a.k + min(tid, a.k - 1)];
     const float sgv = a.shared_gate ? a.sgate[t] : 1.0f;
-    Down16<kMPC> dr(static_cast<const uint8_t *>(a.down.codes) + (size_t)e * a.d * a.I / 2,
+    Down16<kMPC, Q4> dr(static_cast<const uint8_t *>(a.down.codes) + (size_t)e * a.d * a.I / 2,
                     a.down.sb + (size_t)e * a.d * GI, db >> 1, db & 1, GI, 0, 1);
-    Down16<kMPC> ds(static_cast<const uint8_t *>(a.sh_down.codes), a.sh_down.sb, db >> 1, db & 1, GS, sw, SN);
+    Down16<kMPC, Q4> ds(static_cast<const uint8_t *>(a.sh_down.codes), a.sh_down.sb, db >> 1, db & 1, GS, sw, SN);
     if (wave < a.k) dr.load(0);
     if (wave >= s0) ds.load(0);
     if (a.k * a.I / 8 <= kHC * nth) {
@@ -603,23 +644,32 @@ __global__ __launch_bounds__(MAXT) void k_dec_down(DecArgs a) {
         for (int i = tid; i < a.Is / 8; i += nth)
             *reinterpret_cast<u32x4_t *>(hsh + 8 * i) = ld16(a.h_s + (size_t)t * a.Is + 8 * i);
     }
-    if (tid < a.k * GI) Hr[tid] = (qr0 + qr1) + (qr2 + qr3);
+    // group sums of h from its 16-value sums (Q4_0: the two half-group sums)
+    auto put = [&](float *dst, int i, float q0, float q1, float q2, float q3) {
+        if (Q4) {
+            dst[2 * i] = q0 + q1;
+            dst[2 * i + 1] = q2 + q3;
+        } else {
+            dst[i] = (q0 + q1) + (q2 + q3);
+        }
+    };
+    if (tid < a.k * GI) put(Hr, tid, qr0, qr1, qr2, qr3);
     for (int i = tid + nth; i < a.k * GI; i += nth) {
         const float *q = a.hs_r + (size_t)t * a.k * (a.I / 16) + 4 * i;
-        Hr[i] = (q[0] + q[1]) + (q[2] + q[3]);
+        put(Hr, i, q[0], q[1], q[2], q[3]);
     }
-    if (tid < GS) Hsh[tid] = (qs0 + qs1) + (qs2 + qs3);
+    if (tid < GS) put(Hsh, tid, qs0, qs1, qs2, qs3);
     for (int i = tid + nth; i < GS; i += nth) {
         const float *q = a.hs_s + (size_t)t * (a.Is / 16) + 4 * i;
-        Hsh[i] = (q[0] + q[1]) + (q[2] + q[3]);
+        put(Hsh, i, q[0], q[1], q[2], q[3]);
     }
     if (tid < a.k) Ws[tid] = wv;
     __syncthreads();
     if (wave < a.k) {
-        float r = dr.compute(0, hr + (size_t)wave * a.I, Hr + wave * GI);
+        float r = dr.compute(0, hr + (size_t)wave * a.I, Hr + wave * GI * NH);
         for (int i0 = kMPC; dr.more(i0); i0 += kMPC) {
             dr.load(i0);
-            r += dr.compute(i0, hr + (size_t)wave * a.I, Hr + wave * GI);
+            r += dr.compute(i0, hr + (size_t)wave * a.I, Hr + wave * GI * NH);
         }
         r = row_sum16(r);
         if (lane < 16) part_r[wave * 16 + lane] = r;
@@ -667,6 +717,7 @@ DecArgs dec_args(const moe_layer *L, const uint16_t *x, int T, float *y) {
     a.sh_up = L->w.sh_up;
     a.sh_down = L->w.sh_down;
     a.xg = L->ws.dxg;
+    a.q4_0 = D.expert_format == MOE_FORMAT_Q4_0;
     a.h_r = L->ws.dh_r;
     a.h_s = L->ws.dh_s;
     a.hs_r = L->ws.dhs_r;
@@ -684,18 +735,22 @@ DecArgs dec_args(const moe_layer *L, const uint16_t *x, int T, float *y) {
 
 int dec_down_waves(const moe_dims &D) { return D.top_k + 4 < 16 ? D.top_k + 4 : 16; }
 
+// input sums per 64-input group the decode kernels use (Q4_0: one per 32-input block)
+static size_t sums_per_group(const moe_dims &D) { return D.expert_format == MOE_FORMAT_Q4_0 ? 2 : 1; }
+
 size_t dec_down_lds(const moe_dims &D) {
-    const size_t k = D.top_k, I = D.d_expert, Is = D.d_shared;
-    return sizeof(uint16_t) * (k * I + Is) + sizeof(float) * (k * I / 64 + Is / 64 + k + 16 * k + 16 * dec_down_waves(D));
+    const size_t k = D.top_k, I = D.d_expert, Is = D.d_shared, nh = sums_per_group(D);
+    return sizeof(uint16_t) * (k * I + Is) +
+           sizeof(float) * (nh * (k * I / 64 + Is / 64) + k + 16 * k + 16 * dec_down_waves(D));
 }
 
 size_t dec_gateup_lds(const moe_dims &D) {
-    return sizeof(uint16_t) * D.d_model + sizeof(float) * (D.d_model / 64 + kBW * 2 * 16);
+    return sizeof(uint16_t) * D.d_model + sizeof(float) * (sums_per_group(D) * (D.d_model / 64) + kBW * 2 * 16);
 }
 
 size_t dec_workspace_floats(const moe_dims &D, int max_dec, int which) {
     switch (which) {
-        case 0: return (size_t)max_dec * (D.d_model / 64);                      // x group sums
+        case 0: return (size_t)max_dec * (D.d_model / 64) * sums_per_group(D);  // x group (Q4_0: half) sums
         case 1: return (size_t)max_dec * D.top_k * D.d_expert / 2;              // routed h (fp16)
         case 2: return (size_t)max_dec * D.d_shared / 2;                        // shared h (fp16)
         case 3: return (size_t)max_dec * D.top_k * (D.d_expert / 16);           // routed 16-value h sums
@@ -753,9 +808,15 @@ hipError_t launch_dec_gateup(const moe_layer *L, const uint16_t *x, int T, hipSt
     const DecArgs a = dec_args(L, x, T, nullptr);
     const int grid = T * D.top_k * (D.d_expert / 16) + T * (D.d_shared / 16);
     const size_t lds = dec_gateup_lds(D);
-    if (D.n_experts <= 128) launch(k_dec_gateup<2>, dim3(grid), dim3(64 * kBW), lds, s, a);
-    else if (D.n_experts <= 256) launch(k_dec_gateup<4>, dim3(grid), dim3(64 * kBW), lds, s, a);
-    else launch(k_dec_gateup<MOE_MAX_EXPERTS / 64>, dim3(grid), dim3(64 * kBW), lds, s, a);
+    if (a.q4_0) {
+        if (D.n_experts <= 128) launch(k_dec_gateup<2, true>, dim3(grid), dim3(64 * kBW), lds, s, a);
+        else if (D.n_experts <= 256) launch(k_dec_gateup<4, true>, dim3(grid), dim3(64 * kBW), lds, s, a);
+        else launch(k_dec_gateup<MOE_MAX_EXPERTS / 64, true>, dim3(grid), dim3(64 * kBW), lds, s, a);
+    } else {
+        if (D.n_experts <= 128) launch(k_dec_gateup<2, false>, dim3(grid), dim3(64 * kBW), lds, s, a);
+        else if (D.n_experts <= 256) launch(k_dec_gateup<4, false>, dim3(grid), dim3(64 * kBW), lds, s, a);
+        else launch(k_dec_gateup<MOE_MAX_EXPERTS / 64, false>, dim3(grid), dim3(64 * kBW), lds, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -763,10 +824,14 @@ hipError_t launch_dec_down(const moe_layer *L, int T, float *y, hipStream_t s) {
     const moe_dims &D = L->dims;
     const DecArgs a = dec_args(L, nullptr, T, y);
     const int nw = dec_down_waves(D);
-    if (nw <= 12)
-        launch(k_dec_down<768>, dim3(T * (D.d_model / 16)), dim3(64 * nw), dec_down_lds(D), s, a);
-    else
-        launch(k_dec_down<1024>, dim3(T * (D.d_model / 16)), dim3(64 * nw), dec_down_lds(D), s, a);
+    const dim3 grid(T * (D.d_model / 16)), block(64 * nw);
+    if (a.q4_0) {
+        if (nw <= 12) launch(k_dec_down<768, true>, grid, block, dec_down_lds(D), s, a);
+        else launch(k_dec_down<1024, true>, grid, block, dec_down_lds(D), s, a);
+    } else {
+        if (nw <= 12) launch(k_dec_down<768, false>, grid, block, dec_down_lds(D), s, a);
+        else launch(k_dec_down<1024, false>, grid, block, dec_down_lds(D), s, a);
+    }
     return hipGetLastError();
 }
 

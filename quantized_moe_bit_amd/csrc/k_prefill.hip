@@ -11,7 +11,13 @@
 // magnitude), and the fp32 accumulators are scaled back by 2^-m (exact). The activations
 // are fp16 too (x converted exactly from bf16 by the router; the hidden activation
 // h = gelu(g) * u is carried in fp16), and v_mfma_f32_32x32x16_f16 accumulates in fp32
-// across all groups.
+// across all groups. Q4_0 expert matrices (weight d (q - 8), one fp16 d per 32 inputs) take the
+// same path with scale d and bias -8 d, the K-steps of a group's first 32 inputs using its
+// first block's d and the last two K-steps its second block's. An 11-bit d times a 4-bit code
+// does not fit fp16's 11 significant bits, so d is split into d_hi (its leading 8 bits) and
+// d_lo = d - d_hi (at most 3 bits): both products are exact in fp16 (d_lo's down to the fp16
+// subnormal quantum 2^-24 of the staged scale), and each K-step runs one MFMA per part into the
+// same accumulator.
 //
 // Work items: (expert or shared, 128-row tile, output tile), one per workgroup; all output
 // tiles of a row tile run on the same XCD (workgroup i runs on XCD i % 8), so the row tile
@@ -233,6 +239,8 @@ struct PreArgs {
     int n_mats;
 };
 
+enum { kFmtAffine = 0, kFmtQ4_0 = 1 };
+
 // Eight staged weights fp16(2^m (s q + b)) from one device-layout word (elements j = 0..7 of
 // a K-step; element j in nibble j even ? j/2 : 4 + j/2, so pair p = elements 2p, 2p + 1 is
 // nibbles p and 4 + p), given sc = {fp16(2^(24+m) s), fp16(2^(20+m) s)} and b2 = fp16(2^m b)
@@ -263,6 +271,9 @@ __device__ __forceinline__ f16x8_t dequant_frag(uint32_t w, f16x2_t sc, f16x2_t 
 // 2^-4 + 2^m |bias|. A matrix whose scales are all zero takes m from its largest |bias|, placed
 // in [2^14, 2^15). The matrix cannot be staged (m = 0, *faults += 1) if a scale or bias is NaN
 // or infinite, m lies outside [-64, 64], or 2^m |bias| can reach 2^15.
+// Q4_0 matrices (words d0 | d1 << 16, fp16): the same rule with the largest |d| as the
+// largest scale; the biases -8 d then stay below 2^-5 after scaling, every finite fp16 d gives
+// m in [-24, 15], and only a NaN or infinite d cannot be staged.
 struct StageArgs {
     const uint32_t *sb[3];      // routed gate, up, down scale/bias words (n_mats matrices each)
     const uint32_t *sb_sh[3];   // shared gate, up, down
@@ -271,6 +282,7 @@ struct StageArgs {
     int32_t *shift, *faults;
     const int32_t *table;       // expert-to-slot table (layers with slots): only the slots it maps
     int E;                      // are read (others may be being filled)
+    int q4_0;                   // Q4_0 expert matrices
 };
 __global__ __launch_bounds__(256) void k_stage_shift(StageArgs a) {
     const int kind = blockIdx.y, mat = blockIdx.x;
@@ -292,8 +304,12 @@ __global__ __launch_bounds__(256) void k_stage_shift(StageArgs a) {
         const u32x4_t v = ld16(w + 4 * i);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            smax = max(smax, v[j] & 0x7FFFu);
-            bmax = max(bmax, (v[j] >> 16) & 0x7FFFu);
+            if (a.q4_0) {   // two fp16 scales; no biases
+                smax = max(smax, max(v[j] & 0x7FFFu, (v[j] >> 16) & 0x7FFFu));
+            } else {
+                smax = max(smax, v[j] & 0x7FFFu);
+                bmax = max(bmax, (v[j] >> 16) & 0x7FFFu);
+            }
         }
     }
     for (int off = 32; off > 0; off >>= 1) {
@@ -309,9 +325,17 @@ __global__ __launch_bounds__(256) void k_stage_shift(StageArgs a) {
     if (threadIdx.x != 0) return;
     smax = max(max(red[0][0], red[0][1]), max(red[0][2], red[0][3]));
     bmax = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3]));
-    const int es = (int)(smax >> 7), eb = (int)(bmax >> 7);
-    int m = smax ? 118 - es : (bmax ? 141 - eb : 0);
-    const bool bad = smax >= 0x7F80u || bmax >= 0x7F80u || m < -64 || m > 64 || (bmax && eb + m > 141);
+    int m;
+    bool bad;
+    if (a.q4_0) {   // the fp32 exponent field of the largest |d| plays the bf16 one's part
+        const int es = (int)((__builtin_bit_cast(uint32_t, f16_to_f32(smax)) >> 23) & 0xFF);
+        m = smax ? 118 - es : 0;
+        bad = smax >= 0x7C00u;
+    } else {
+        const int es = (int)(smax >> 7), eb = (int)(bmax >> 7);
+        m = smax ? 118 - es : (bmax ? 141 - eb : 0);
+        bad = smax >= 0x7F80u || bmax >= 0x7F80u || m < -64 || m > 64 || (bmax && eb + m > 141);
+    }
     if (bad) {
         atomicAdd(a.faults, 1);
         m = 0;
@@ -319,7 +343,7 @@ __global__ __launch_bounds__(256) void k_stage_shift(StageArgs a) {
     a.shift[sh ? 3 * a.n_mats + kind : kind * a.n_mats + mat] = m;
 }
 
-template <int MODE>  // MODE 0: gate/up + GeGLU, 1: down
+template <int MODE, int FMT>  // MODE 0: gate/up + GeGLU, 1: down; FMT: kFmtAffine / kFmtQ4_0
 __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
     __shared__ __align__(16) uint8_t smem[kSmemBytes];
 
@@ -449,16 +473,33 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
         dma_b(Bt0 + (size_t)gb * 1024, Bt1 + (size_t)gb * 1024, boff, smem + kBRingOff + sbi * kBStageBytes + wave * 2048,
               St0 + gb * 128, St1 + gb * 128, soff, smem + kSRingOff + sbi * kSStageBytes + wave * 512);
     };
-    // raw code words and fp16 scale/bias pairs of the step whose tiles sit in B stage sbi
-    auto load_w = [&](int sbi, u32x4_t (&bw)[2], f16x2_t (&s2)[2], f16x2_t (&b2)[2]) {
+    // raw code words and fp16 scale/bias pairs of the step whose tiles sit in B stage sbi:
+    // [t][h] serves K-steps 2 h and 2 h + 1 (the same pair for both halves of an affine group;
+    // Q4_0: block h of the group, scale d_h and bias -8 d_h, split into the parts hi, lo)
+    auto load_w = [&](int sbi, u32x4_t (&bw)[2], f16x2_t (&s2)[2][2], f16x2_t (&b2)[2][2], f16x2_t (&s2l)[2][2],
+                      f16x2_t (&b2l)[2][2]) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             bw[t] = ld16(smem + kBRingOff + sbi * kBStageBytes + wave * 2048 + t * 1024 + lane * 16);
             const uint32_t sbw =
                 *reinterpret_cast<const uint32_t *>(smem + kSRingOff + sbi * kSStageBytes + wave * 512 + t * 256 + lane * 4);
-            const float sc = bf16_to_f32(sbw & 0xFFFFu) * fS[t], bi = bf16_to_f32(sbw >> 16) * fB[t];
-            s2[t] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(sc, sc * 0.0625f));
-            b2[t] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(bi, bi));
+            if constexpr (FMT == kFmtAffine) {
+                const float sc = bf16_to_f32(sbw & 0xFFFFu) * fS[t], bi = bf16_to_f32(sbw >> 16) * fB[t];
+                s2[t][0] = s2[t][1] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(sc, sc * 0.0625f));
+                b2[t][0] = b2[t][1] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(bi, bi));
+            } else {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float dh = f16_to_f32((sbw >> (16 * h)) & 0xFFFFu);
+                    const float hi = __uint_as_float(__float_as_uint(dh) & 0xFFFF0000u), lo = dh - hi;   // exact
+                    const float sc = hi * fS[t], bi = hi * (-8.0f * fB[t]);
+                    const float scl = lo * fS[t], bil = lo * (-8.0f * fB[t]);
+                    s2[t][h] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(sc, sc * 0.0625f));
+                    b2[t][h] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(bi, bi));
+                    s2l[t][h] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(scl, scl * 0.0625f));
+                    b2l[t][h] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(bil, bil));
+                }
+            }
         }
     };
 
@@ -487,9 +528,10 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
     // step g.
     auto kloop = [&](auto lms_c) {
         constexpr int LMS = decltype(lms_c)::value;
+        constexpr bool Q4 = FMT == kFmtQ4_0;
         u32x4_t bw[2];
-        f16x2_t s2[2], b2[2];
-        f16x8_t bf0[2];   // K-step 0 of the next ring step, dequantized during K-step 3 of this one
+        f16x2_t s2[2][2], b2[2][2], s2l[2][2], b2l[2][2];   // s2l, b2l: the d_lo part (Q4_0)
+        f16x8_t bf0[2], bl0[2];   // K-step 0 of the next ring step, dequantized during K-step 3 of this one
         auto step = [&](auto j_c, int g) {
             constexpr int Ju = decltype(j_c)::value;
             constexpr int SA = Ju % kAStages, SAN = (Ju + kADist) % kAStages;
@@ -510,11 +552,14 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
             if (live_w) {
                 const uint8_t *sA = smem + SA * kAStageBytes;
                 u32x4_t af[2][LMS];
-                f16x8_t bf[2][2];
+                f16x8_t bf[2][2], bl[2][2];
 #pragma unroll
                 for (int ms = 0; ms < LMS; ++ms) af[0][ms] = ld16(sA + aoff[0] + 4096 * ms);
 #pragma unroll
-                for (int t = 0; t < 2; ++t) bf[0][t] = bf0[t];
+                for (int t = 0; t < 2; ++t) {
+                    bf[0][t] = bf0[t];
+                    if constexpr (Q4) bl[0][t] = bl0[t];
+                }
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     if (s < 3) {
@@ -524,23 +569,33 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
                         // code words of step g + 1 (a past-the-end step reads a valid clamped stage);
                         // this K-step's fragments are already in registers
                         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitB) : "memory");
-                        load_w(SB1, bw, s2, b2);
+                        load_w(SB1, bw, s2, b2, s2l, b2l);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                     if (s < 3) {
 #pragma unroll
-                        for (int t = 0; t < 2; ++t)
-                            bf[(s + 1) & 1][t] = dequant_frag(bw[t][s + 1], s2[t], b2[t]);
+                        for (int t = 0; t < 2; ++t) {
+                            const int hs = (s + 1) >> 1;
+                            bf[(s + 1) & 1][t] = dequant_frag(bw[t][s + 1], s2[t][hs], b2[t][hs]);
+                            if constexpr (Q4) bl[(s + 1) & 1][t] = dequant_frag(bw[t][s + 1], s2l[t][hs], b2l[t][hs]);
+                        }
                     }
 #pragma unroll
                     for (int ms = 0; ms < LMS; ++ms)
 #pragma unroll
-                        for (int t = 0; t < 2; ++t)
+                        for (int t = 0; t < 2; ++t) {
                             acc[ms][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                                 __builtin_bit_cast(f16x8_t, af[s & 1][ms]), bf[s & 1][t], acc[ms][t], 0, 0, 0);
+                            if constexpr (Q4)
+                                acc[ms][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                    __builtin_bit_cast(f16x8_t, af[s & 1][ms]), bl[s & 1][t], acc[ms][t], 0, 0, 0);
+                        }
                     if (s == 3) {
 #pragma unroll
-                        for (int t = 0; t < 2; ++t) bf0[t] = dequant_frag(bw[t][0], s2[t], b2[t]);
+                        for (int t = 0; t < 2; ++t) {
+                            bf0[t] = dequant_frag(bw[t][0], s2[t][0], b2[t][0]);
+                            if constexpr (Q4) bl0[t] = dequant_frag(bw[t][0], s2l[t][0], b2l[t][0]);
+                        }
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -551,9 +606,12 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
         // B of step 0: issued first in the prologue
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitB0) : "memory");
         if (live_w) {
-            load_w(0, bw, s2, b2);
+            load_w(0, bw, s2, b2, s2l, b2l);
 #pragma unroll
-            for (int t = 0; t < 2; ++t) bf0[t] = dequant_frag(bw[t][0], s2[t], b2[t]);
+            for (int t = 0; t < 2; ++t) {
+                bf0[t] = dequant_frag(bw[t][0], s2[t][0], b2[t][0]);
+                if constexpr (Q4) bl0[t] = dequant_frag(bw[t][0], s2l[t][0], b2l[t][0]);
+            }
         }
         int g = 0;
         for (; g + kUnroll <= G; g += kUnroll)
@@ -729,6 +787,7 @@ hipError_t launch_stage_shift(const moe_layer *L, bool routed, bool shared, int3
     a.faults = faults;
     a.table = L->w.expert_slot;
     a.E = D.n_experts;
+    a.q4_0 = D.expert_format == MOE_FORMAT_Q4_0;
     launch(k_stage_shift, dim3(L->n_mats + 1, 3), dim3(256), 0, s, a);
     return hipGetLastError();
 }
@@ -738,7 +797,10 @@ hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipSt
     PreArgs a = make_args(L, T);
     a.tile_mode = tile >= 0;
     a.shared = tile <= 0;
-    launch(k_pre_gemm<0>, dim3(pre_grid(L, T, 0)), dim3(kPreWG), 0, s, a);
+    if (L->dims.expert_format == MOE_FORMAT_Q4_0)
+        launch(k_pre_gemm<0, kFmtQ4_0>, dim3(pre_grid(L, T, 0)), dim3(kPreWG), 0, s, a);
+    else
+        launch(k_pre_gemm<0, kFmtAffine>, dim3(pre_grid(L, T, 0)), dim3(kPreWG), 0, s, a);
     return hipGetLastError();
 }
 
@@ -746,7 +808,10 @@ hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s, int tile) {
     PreArgs a = make_args(L, T);
     a.tile_mode = tile >= 0;
     a.shared = tile <= 0;
-    launch(k_pre_gemm<1>, dim3(pre_grid(L, T, 1)), dim3(kPreWG), 0, s, a);
+    if (L->dims.expert_format == MOE_FORMAT_Q4_0)
+        launch(k_pre_gemm<1, kFmtQ4_0>, dim3(pre_grid(L, T, 1)), dim3(kPreWG), 0, s, a);
+    else
+        launch(k_pre_gemm<1, kFmtAffine>, dim3(pre_grid(L, T, 1)), dim3(kPreWG), 0, s, a);
     return hipGetLastError();
 }
 

@@ -36,12 +36,13 @@ constexpr int kRBlk = 64 * kRNE;   // router table floats per (expert block, gro
 // computed in float64 in that order and rounded once, the same expression the oracle writes
 // out (its sum of squares runs in another order; the bf16 rounding absorbs the difference).
 // Also writes the fp16 copy of x (x16, prefill) or the fixed-order group sums of x (xg,
-// decode), which the router would otherwise derive from its own input.
+// decode; nl = 32 for Q4_0 experts: sums of 32 inputs), which the router would otherwise
+// derive from its own input.
 // grid: T; block 256 (d <= 8192: at most four 16-byte chunks per thread)
 constexpr int kProChunks = 4;
 __global__ __launch_bounds__(256) void k_router_prologue(const uint16_t *__restrict__ x, int d,
                                                          const uint16_t *__restrict__ rs, uint16_t *__restrict__ u,
-                                                         uint16_t *__restrict__ x16, float *__restrict__ xg) {
+                                                         uint16_t *__restrict__ x16, float *__restrict__ xg, int nl) {
     __shared__ double red[4];
     const int t = blockIdx.x, tid = threadIdx.x, nc = d / 8;
     const uint16_t *xt = x + (size_t)t * d;
@@ -86,10 +87,10 @@ __global__ __launch_bounds__(256) void k_router_prologue(const uint16_t *__restr
             if (x16) *reinterpret_cast<u32x4_t *>(x16 + (size_t)t * d + 8 * i) = ho;
         }
     }
-    if (xg && tid < d / 64) {   // X_g = ((0 + x_0) + x_1) + ... + x_63, fp32
+    if (xg && tid < d / nl) {   // X = ((0 + x_0) + x_1) + ... over nl inputs, fp32
         float X = 0.0f;
-        for (int j = 0; j < 64; ++j) X = X + bf16_to_f32(xt[64 * tid + j]);
-        xg[(size_t)t * (d / 64) + tid] = X;
+        for (int j = 0; j < nl; ++j) X = X + bf16_to_f32(xt[nl * tid + j]);
+        xg[(size_t)t * (d / nl) + tid] = X;
     }
 }
 
@@ -512,7 +513,8 @@ hipError_t launch_bucket_scatter(const moe_layer *L, int T, const int32_t *idx, 
 
 hipError_t launch_router_prologue(const moe_layer *L, const uint16_t *x, int T, bool for_prefill, hipStream_t s) {
     launch(k_router_prologue, dim3(T), dim3(256), 0, s, x, L->dims.d_model, L->w.router_scale, L->ws.u,
-           for_prefill ? L->ws.x16 : nullptr, for_prefill ? nullptr : L->ws.dxg);
+           for_prefill ? L->ws.x16 : nullptr, for_prefill ? nullptr : L->ws.dxg,
+           L->dims.expert_format == MOE_FORMAT_Q4_0 ? 32 : 64);
     return hipGetLastError();
 }
 

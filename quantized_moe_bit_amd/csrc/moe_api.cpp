@@ -39,6 +39,9 @@ moe_status check_dims(const moe_dims *D) {
     if (D->group != 64) return fail(MOE_E_QUANT, "group must be 64, got %d", D->group);
     if (D->router_bits != 8) return fail(MOE_E_QUANT, "router_bits must be 8, got %d", D->router_bits);
     if (D->expert_bits != 4) return fail(MOE_E_QUANT, "expert_bits must be 4, got %d", D->expert_bits);
+    if (D->expert_format != MOE_FORMAT_AFFINE_G64 && D->expert_format != MOE_FORMAT_Q4_0)
+        return fail(MOE_E_QUANT, "expert_format %d is neither MOE_FORMAT_AFFINE_G64 nor MOE_FORMAT_Q4_0",
+                    D->expert_format);
     if (D->d_model < 64 || D->d_model % 64 || D->d_model > 8192)
         return fail(MOE_E_SHAPE, "d_model %d must be a multiple of 64 in [64, 8192]", D->d_model);
     if (D->d_expert < 64 || D->d_expert % 64)
@@ -382,7 +385,8 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
         delete L;
         return fail(MOE_E_QUANT,
                     "%d expert matrices have scales or biases the fp16 staging cannot carry (NaN or infinite, "
-                    "largest |scale| outside [2^-73, 2^56), or floor(log2 |bias|) >= floor(log2 max |scale|) + 24)",
+                    "largest |scale| outside [2^-73, 2^56), or floor(log2 |bias|) >= floor(log2 max |scale|) + 24; "
+                    "Q4_0: a NaN or infinite d)",
                     bad);
     }
     *out = L;

@@ -81,7 +81,7 @@ struct Workspace {
     int32_t *shift;       // [3 n_mats + 3]     fp16 staging exponents of the prefill GEMMs: routed
                           //                    gate, up, down (kind * n_mats + matrix), then shared
     // decode path (D = decode capacity, KSd/KSs = input pieces of d / of I_s)
-    float *dxg;           // [D, d/64]          decode: group sums of x
+    float *dxg;           // [D, d/64]          decode: group sums of x (Q4_0 experts: [D, d/32] half sums)
     uint16_t *dh_r;       // [D*k, I]           decode: routed hidden activations, fp16 bits
     uint16_t *dh_s;       // [D, I_s]           decode: shared hidden activations, fp16 bits
     float *dhs_r;         // [D*k, I/16]        decode: sums of 16 consecutive routed h values

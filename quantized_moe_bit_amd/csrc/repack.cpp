@@ -15,6 +15,11 @@
 //
 // Device layout of an 8-bit matrix [out, in]: codes unchanged (row-major bytes),
 // scale/bias words ordered (row, group).
+//
+// Q4_0 expert matrices (32 weights per 18-byte block: fp16 d, then byte j holding element j
+// in its low and element j + 16 in its high nibble; Gem native architecture, "M4 Max operating
+// assumptions") take the same code tiles, their codes unchanged, and one word per (row, group
+// of 64) holding the d of the group's two blocks: d0 | d1 << 16.
 #include <cstdint>
 #include <cstring>
 
@@ -151,6 +156,107 @@ extern "C" moe_status moe_unrepack(int32_t bits, int32_t n_mats, int32_t out_dim
                     const size_t si = (size_t)(rb * 32 + r) * G + g;
                     scm[si] = (uint16_t)(v & 0xFFFFu);
                     bcm[si] = (uint16_t)(v >> 16);
+                }
+            }
+    }
+    return MOE_OK;
+}
+
+namespace {
+
+moe_status check_q4_0(int32_t n_mats, int32_t out_dim, int32_t in_dim) {
+    if (n_mats < 1 || out_dim < 1 || in_dim < 64)
+        return qmoe::fail(MOE_E_SHAPE, "repack_q4_0: bad sizes n_mats=%d out=%d in=%d", n_mats, out_dim, in_dim);
+    if (in_dim % 64) return qmoe::fail(MOE_E_SHAPE, "repack_q4_0: in_dim %d not a multiple of 64", in_dim);
+    if (out_dim % 32) return qmoe::fail(MOE_E_SHAPE, "repack_q4_0: out_dim %d not a multiple of 32", out_dim);
+    return MOE_OK;
+}
+
+// Block element i (0..31) sits in byte 2 + (i % 16) of its block, in the low nibble for
+// i < 16 and the high nibble otherwise.
+inline int q4_0_code(const uint8_t *blk, int i) { return (blk[2 + (i & 15)] >> (4 * (i >> 4))) & 0xF; }
+
+}  // namespace
+
+extern "C" moe_status moe_repack_q4_0(int32_t n_mats, int32_t out_dim, int32_t in_dim, const uint8_t *blocks,
+                                      void *codes_out, uint32_t *sb_out) {
+    qmoe::clear_error();
+    moe_status st = check_q4_0(n_mats, out_dim, in_dim);
+    if (st != MOE_OK) return st;
+    if (!blocks || !codes_out || !sb_out) return qmoe::fail(MOE_E_INVALID, "repack_q4_0: null pointer");
+    const int G = in_dim / 64, RB = out_dim / 32;
+    const size_t row_blocks = (size_t)in_dim / 32;
+    uint8_t *dst = static_cast<uint8_t *>(codes_out);
+    for (int m = 0; m < n_mats; ++m) {
+        const uint8_t *bm = blocks + (size_t)m * out_dim * row_blocks * 18;
+        uint8_t *dm = dst + (size_t)m * out_dim * (in_dim / 2);
+        uint32_t *wm = sb_out + (size_t)m * out_dim * G;
+        for (int rb = 0; rb < RB; ++rb)
+            for (int g = 0; g < G; ++g) {
+                uint8_t *tile = dm + ((size_t)rb * G + g) * 1024;
+                for (int l = 0; l < 64; ++l) {
+                    const int row = rb * 32 + (l & 31), half = l >> 5;
+                    const uint8_t *brow = bm + (size_t)row * row_blocks * 18;
+                    for (int s = 0; s < 4; ++s) {
+                        // elements 64 g + 16 s + 8 half + (0..7) as one canonical word (element j in nibble j)
+                        uint32_t c = 0;
+                        for (int j = 0; j < 8; ++j) {
+                            const int e = 64 * g + 16 * s + 8 * half + j;
+                            c |= (uint32_t)q4_0_code(brow + (size_t)(e / 32) * 18, e % 32) << (4 * j);
+                        }
+                        const uint32_t word = to_device_word(c);
+                        std::memcpy(tile + l * 16 + s * 4, &word, 4);
+                    }
+                }
+                for (int r = 0; r < 32; ++r) {
+                    const uint8_t *b0 = bm + ((size_t)(rb * 32 + r) * row_blocks + 2 * g) * 18, *b1 = b0 + 18;
+                    const uint32_t d0 = (uint32_t)b0[0] | ((uint32_t)b0[1] << 8);
+                    const uint32_t d1 = (uint32_t)b1[0] | ((uint32_t)b1[1] << 8);
+                    wm[((size_t)rb * G + g) * 32 + r] = d0 | (d1 << 16);
+                }
+            }
+    }
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_unrepack_q4_0(int32_t n_mats, int32_t out_dim, int32_t in_dim, const void *codes_in,
+                                        const uint32_t *sb_in, uint8_t *blocks) {
+    qmoe::clear_error();
+    moe_status st = check_q4_0(n_mats, out_dim, in_dim);
+    if (st != MOE_OK) return st;
+    if (!codes_in || !sb_in || !blocks) return qmoe::fail(MOE_E_INVALID, "unrepack_q4_0: null pointer");
+    const int G = in_dim / 64, RB = out_dim / 32;
+    const size_t row_blocks = (size_t)in_dim / 32;
+    const uint8_t *src = static_cast<const uint8_t *>(codes_in);
+    for (int m = 0; m < n_mats; ++m) {
+        const uint8_t *sm_ = src + (size_t)m * out_dim * (in_dim / 2);
+        const uint32_t *wm = sb_in + (size_t)m * out_dim * G;
+        uint8_t *bm = blocks + (size_t)m * out_dim * row_blocks * 18;
+        for (int rb = 0; rb < RB; ++rb)
+            for (int g = 0; g < G; ++g) {
+                const uint8_t *tile = sm_ + ((size_t)rb * G + g) * 1024;
+                for (int r = 0; r < 32; ++r) {
+                    const uint32_t v = wm[((size_t)rb * G + g) * 32 + r];
+                    uint8_t *b0 = bm + ((size_t)(rb * 32 + r) * row_blocks + 2 * g) * 18, *b1 = b0 + 18;
+                    b0[0] = (uint8_t)(v & 0xFF);
+                    b0[1] = (uint8_t)((v >> 8) & 0xFF);
+                    b1[0] = (uint8_t)((v >> 16) & 0xFF);
+                    b1[1] = (uint8_t)(v >> 24);
+                    std::memset(b0 + 2, 0, 16);
+                    std::memset(b1 + 2, 0, 16);
+                }
+                for (int l = 0; l < 64; ++l) {
+                    const int row = rb * 32 + (l & 31), half = l >> 5;
+                    uint8_t *brow = bm + (size_t)row * row_blocks * 18;
+                    for (int s = 0; s < 4; ++s) {
+                        uint32_t word;
+                        std::memcpy(&word, tile + l * 16 + s * 4, 4);
+                        const uint32_t c = to_canonical_word(word);
+                        for (int j = 0; j < 8; ++j) {
+                            const int e = 64 * g + 16 * s + 8 * half + j, i = e % 32;
+                            brow[(size_t)(e / 32) * 18 + 2 + (i & 15)] |= (uint8_t)(((c >> (4 * j)) & 0xF) << (4 * (i >> 4)));
+                        }
+                    }
                 }
             }
     }

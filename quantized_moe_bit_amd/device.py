@@ -40,7 +40,10 @@ class DeviceLayer:
             "sh_down": (layer.sh_down, 4, 1, D.d_model, D.d_shared),
         }
         for name, (m, bits, n, o, i) in specs.items():
-            c, s = B.moe_repack(bits, n, o, i, m.codes, m.scales, m.biases)
+            if getattr(m, "fmt", "affine") == "q4_0":
+                c, s = B.moe_repack_q4_0(n, o, i, m.codes)
+            else:
+                c, s = B.moe_repack(bits, n, o, i, m.codes, m.scales, m.biases)
             if n_slots is not None and name in ("gate", "up", "down"):
                 # slab of n_slots experts; each expert's bytes stay on the host
                 pc, ps = c.size // n, s.size // n
@@ -69,7 +72,7 @@ class DeviceLayer:
             self._table = self._table_host.to(self.device)
         w = self._weights(q)
         self.dims = B.moe_dims(D.d_model, D.n_experts, D.top_k, D.d_expert, D.d_shared, D.group, D.router_bits,
-                               D.expert_bits, max_tokens)
+                               D.expert_bits, max_tokens, B.FORMATS[getattr(D, "expert_format", "affine")])
         self.max_tokens = max_tokens
         self.weights = w   # the moe_weights the handle was created with
         self.handle = B.moe_layer_create(self.dims, w, flags)

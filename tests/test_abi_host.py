@@ -76,6 +76,49 @@ def test_repack_layout_matches_documentation():
                 assert w & 0xFFFF == scales[m, row, g] and w >> 16 == biases[m, row, g]
 
 
+@pytest.mark.parametrize("n,o,i", [(3, 64, 128), (2, 96, 192), (1, 32, 64)])
+def test_q4_0_repack_round_trip_is_bit_exact(n, o, i):
+    """Any block bytes (scales included: NaN and infinite patterns are copied as bits)."""
+    rng = np.random.default_rng(n * 1000 + o)
+    blocks = rng.integers(0, 256, size=(n, o, i // 32 * 18), dtype=np.uint8)
+    dc, ds = B.moe_repack_q4_0(n, o, i, blocks)
+    assert dc.nbytes == B.moe_packed_bytes(4, n, o, i, 0) and ds.nbytes == B.moe_packed_bytes(4, n, o, i, 1)
+    np.testing.assert_array_equal(B.moe_unrepack_q4_0(n, o, i, dc, ds), blocks)
+
+
+def test_q4_0_repack_matches_the_affine_tile_layout():
+    """Q4_0 codes land in the same tiles as the affine codes of the same elements (the affine
+    layout is pinned element by element above), and each group's word holds its two blocks' d."""
+    n, o, i = 2, 64, 192
+    rng = np.random.default_rng(9)
+    blocks = rng.integers(0, 256, size=(n, o, i // 32, 18), dtype=np.uint8)
+    body = blocks[..., 2:]
+    q = np.concatenate([body & 0x0F, body >> 4], axis=-1).reshape(n, o, i)   # element order
+    canon = (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8)             # affine canonical packing
+    G = i // 64
+    zero = np.zeros((n, o, G), np.uint16)
+    ac, _ = B.moe_repack(4, n, o, i, canon, zero, zero)
+    dc, ds = B.moe_repack_q4_0(n, o, i, blocks.reshape(n, o, -1))
+    np.testing.assert_array_equal(dc, ac)
+    d = blocks[..., 0].astype(np.uint32) | (blocks[..., 1].astype(np.uint32) << 8)   # [n, o, i/32]
+    for m in range(n):
+        for row in range(o):
+            for g in range(G):
+                w = ds[m * o * G + ((row // 32) * G + g) * 32 + row % 32]
+                assert w & 0xFFFF == d[m, row, 2 * g] and w >> 16 == d[m, row, 2 * g + 1]
+
+
+def test_q4_0_repack_rejects_bad_arguments():
+    z = np.zeros(8192, np.uint8)
+    L = B.lib()
+    for o, i, st in [(30, 64, B.MOE_E_SHAPE), (32, 96, B.MOE_E_SHAPE), (32, 32, B.MOE_E_SHAPE), (0, 64, B.MOE_E_SHAPE)]:
+        out = np.zeros(4096, np.uint8)
+        assert L.moe_repack_q4_0(1, o, i, z.ctypes.data, out.ctypes.data, out.ctypes.data) == st
+        assert np.all(out == 0)
+    assert L.moe_repack_q4_0(1, 32, 64, None, z.ctypes.data, z.ctypes.data) == B.MOE_E_INVALID
+    assert L.moe_unrepack_q4_0(1, 32, 64, z.ctypes.data, None, z.ctypes.data) == B.MOE_E_INVALID
+
+
 def test_packed_bytes_matches_canonical_sizes():
     d, I = 2816, 704
     per_proj = B.moe_packed_bytes(4, 1, I, d, 0) + B.moe_packed_bytes(4, 1, I, d, 1)
@@ -121,6 +164,8 @@ def _weights(align=16, null=None):
     (dict(group=32), B.MOE_E_QUANT),
     (dict(router_bits=4), B.MOE_E_QUANT),
     (dict(expert_bits=8), B.MOE_E_QUANT),
+    (dict(expert_format=2), B.MOE_E_QUANT),
+    (dict(expert_format=-1), B.MOE_E_QUANT),
     (dict(d_model=200), B.MOE_E_SHAPE),
     (dict(d_expert=100), B.MOE_E_SHAPE),
     (dict(d_shared=0), B.MOE_E_SHAPE),

@@ -73,17 +73,15 @@ def decode_layer_bytes(D):
             "dec_down": k * qmat_bytes(d, I, 4) + qmat_bytes(d, Is, 4)}
 
 
-def qwen_section(args, dev, K, W):
-    """Decode (1 token, layer copies rotated) and 4096-token prefill of the 2048-wide,
-    256-expert layer with a gated shared expert."""
+def decode_rotated(args, dev, name, K, W):
+    """Decode of one token per call through --layers copies of a workload's layer (rotated, so the
+    weights come from HBM), timed with events, then a second pass with per-kernel events."""
     import torch
     from quantized_moe_bit_amd import binding as B
     from quantized_moe_bit_amd import synth
     from quantized_moe_bit_amd.device import DeviceLayer, tokens_to_device
-    out = {}
-    wd = synth.WORKLOADS["qwen_decode"]
+    wd = synth.WORKLOADS[name]
     D = wd.dims
-    log("generating the 2048-wide 256-expert layer with a gated shared expert")
     lay = synth.workload_layer(wd)
     base = DeviceLayer(lay, max_tokens=1, device=dev)
     copies = [base] + [base.replicate() for _ in range(args.layers - 1)]
@@ -112,23 +110,52 @@ def qwen_section(args, dev, K, W):
     torch.cuda.synchronize()
     stage = decode_layer_bytes(D)
     kus = {}
-    for name in stage:
+    for kname in stage:
         tot, n = 0.0, 0
         for L in copies:
-            m, c = B.moe_profile_read(L.handle, B.kernel_id(name))
+            m, c = B.moe_profile_read(L.handle, B.kernel_id(kname))
             tot += m
             n += c
-        kus[name] = 1000.0 * tot / max(n, 1)
+        kus[kname] = 1000.0 * tot / max(n, 1)
     for L in copies:
         L.close()
+    torch.cuda.empty_cache()
     btok = sum(stage.values())
+    return {"tokens_per_s": round(1000.0 / ms, 1), "us_per_token": round(1000.0 * ms, 3),
+            "bytes_per_token": btok, "hbm_gbs": round(btok / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(btok / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernels_us": {n: round(v, 3) for n, v in kus.items()},
+            "kernels_gbs": {n: round(stage[n] / (kus[n] * 1e-6) / 1e9, 1) for n in stage}}
+
+
+def q4_0_section(args, dev, K, W):
+    """The 2816-wide layer with Q4_0 experts: 1-token decode (rotated copies) and a 4096-token
+    prefill chunk. A Q4_0 block (18 bytes per 32 weights) streams the same 36 bytes per 64 weights
+    as an affine group, so the decode byte counts are the affine ones."""
+    log("Q4_0 experts: decode and 4096-token prefill")
+    out = {"workload": "the 2816-wide layer (128 experts, top-8, widths 704 / 2112) with Q4_0 expert "
+                       "matrices (fp16 d per 32 weights), 8-bit g64 router",
+           "decode": decode_rotated(args, dev, "q4_0_decode", K, W)}
+    if not args.no_prefill:
+        out["prefill"] = prefill_section(args, dev, "q4_0_prefill4096",
+                                         "prefill: 4096 tokens, Q4_0 experts, Zipf(1.3) logit skew, 2% tied tokens")[3]
+    return out
+
+
+def qwen_section(args, dev, K, W):
+    """Decode (1 token, layer copies rotated) and 4096-token prefill of the 2048-wide,
+    256-expert layer with a gated shared expert."""
+    import torch
+    from quantized_moe_bit_amd import binding as B
+    from quantized_moe_bit_amd import synth
+    from quantized_moe_bit_amd.device import DeviceLayer, tokens_to_device
+    out = {}
+    log("generating the 2048-wide 256-expert layer with a gated shared expert")
+    D = synth.WORKLOADS["qwen_decode"].dims
     out["workload"] = ("layer d_model 2048, 256 experts, top-8, expert width 512, shared width 512 with a "
                        "sigmoid(g . x) gate, 8-bit g64 router, 4-bit g64 experts")
-    out["decode"] = {"tokens_per_s": round(1000.0 / ms, 1), "us_per_token": round(1000.0 * ms, 3),
-                     "bytes_per_token": btok, "hbm_gbs": round(btok / (ms * 1e-3) / 1e9, 1),
-                     "hbm_frac": round(btok / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "kernels_us": {n: round(v, 3) for n, v in kus.items()},
-                     "kernels_gbs": {n: round(stage[n] / (kus[n] * 1e-6) / 1e9, 1) for n in stage}}
+    out["decode"] = decode_rotated(args, dev, "qwen_decode", K, W)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if not args.no_prefill:
         torch.cuda.empty_cache()
         wp = synth.WORKLOADS["qwen_prefill4096"]
@@ -361,6 +388,7 @@ def main():
     ap.add_argument("--no-prologue", action="store_true", help="skip the router prologue measurement")
     ap.add_argument("--no-qwen", action="store_true", help="skip the gated-shared-expert (Qwen 3.6 style) layer")
     ap.add_argument("--no-slots", action="store_true", help="skip the expert slot cache measurement")
+    ap.add_argument("--no-q4-0", dest="no_q4_0", action="store_true", help="skip the Q4_0-expert layer")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -569,6 +597,11 @@ def main():
     if not args.no_qwen:
         release_decode_copies()
         result.setdefault("next_rows", {})["qwen_gated_shared"] = qwen_section(args, dev, K, W)
+
+    # ------------------------------------------------------------------ widened row: Q4_0 experts
+    if not args.no_q4_0:
+        release_decode_copies()
+        result.setdefault("next_rows", {})["q4_0_experts"] = q4_0_section(args, dev, K, W)
 
     # ------------------------------------------------------------------ widened row: expert slot cache
     if not args.no_slots:

@@ -21,7 +21,8 @@
 //
 // Work items: (expert or shared, 128-row tile, output tile), one per workgroup; all output
 // tiles of a row tile run on the same XCD (workgroup i runs on XCD i % 8), so the row tile
-// is fetched into one L2.
+// is fetched into one L2. Routed tiles with at most 32 live rows take a narrow workgroup tile
+// (32 token rows x 512 weight rows) in the same launch.
 #include <type_traits>
 
 #include "device_common.h"
@@ -237,9 +238,12 @@ struct PreArgs {
     int tile_mode, shared;
     const int32_t *shift;       // fp16 staging exponents: [kind * n_mats + matrix], shared at [3 n_mats + kind]
     int n_mats;
+    int n_wide;                 // workgroups of the 128-row items; the narrow items follow
 };
 
 enum { kFmtAffine = 0, kFmtQ4_0 = 1 };
+
+constexpr int kNMRows = 32;   // routed tiles with at most this many live rows run in the narrow-tile kernel
 
 // Eight staged weights fp16(2^m (s q + b)) from one device-layout word (elements j = 0..7 of
 // a K-step; element j in nibble j even ? j/2 : 4 + j/2, so pair p = elements 2p, 2p + 1 is
@@ -343,10 +347,9 @@ __global__ __launch_bounds__(256) void k_stage_shift(StageArgs a) {
     a.shift[sh ? 3 * a.n_mats + kind : kind * a.n_mats + mat] = m;
 }
 
+// The 128-row work items of one GEMM launch (workgroup index bid < a.n_wide).
 template <int MODE, int FMT>  // MODE 0: gate/up + GeGLU, 1: down; FMT: kFmtAffine / kFmtQ4_0
-__global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
-    __shared__ __align__(16) uint8_t smem[kSmemBytes];
-
+__device__ __forceinline__ void pre_gemm_wide(const PreArgs &a, uint8_t *smem, const int bid) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, half = lane >> 5;
@@ -366,7 +369,7 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
     const int Ms = cdiv(a.T, kMT), Ms8 = roundup(Ms, 8);
     const int NTs = MODE == 0 ? cdiv(a.Is / 32, 4) : cdiv(a.d / 64, 4);
     const int NTr = MODE == 0 ? cdiv(a.I / 32, 4) : cdiv(a.d / 64, 4);
-    const int bid = blockIdx.x, Gs = Ms8 * NTs;
+    const int Gs = Ms8 * NTs;
     bool shared_item;
     int e = 0, mt, nt, count, rowbase;
     if (bid < Gs) {
@@ -388,6 +391,7 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
             const int sl = a.eslot[it.x];
             if (sl < 0 || sl >= a.n_slots) return;
         }
+        if (it.w - it.y * kMT <= kNMRows) return;   // at most 32 live rows: the narrow-tile launch
         e = expert_slot_of(a.eslot, a.n_slots, a.slot_faults, it.x, MODE == 0 && nt == 0 && threadIdx.x == 0);
         mt = it.y;
         rowbase = it.z;
@@ -695,6 +699,350 @@ __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
     }
 }
 
+// ----------------------------------------------------------------------------- narrow tiles
+// Routed row tiles with at most 32 live rows (experts with few pairs, and the last tile of
+// an expert whose pairs end just past a multiple of 128) run in a launch of their own with a
+// narrow workgroup tile: 32 token rows x 512 weight rows. In the 128-row kernel such a tile
+// streams the weights of 256 weight rows and a 128-row A ring for a quarter of the MFMA work;
+// here each weight is still dequantized once per tile, but the tile moves twice the weights
+// per step behind one barrier, its A ring is a quarter of the size, and the weight ring runs
+// two steps ahead with 16 KiB per wave in flight. Wave w owns four 32-row code tiles for the
+// 32 token rows: gate/up -> gate and up of hidden blocks 8 nt + 2 w and 8 nt + 2 w + 1
+// (tiles gate, up, gate, up); down -> row blocks 16 nt + 4 w .. 16 nt + 4 w + 3.
+constexpr int kNM = kNMRows;                    // token rows per narrow tile
+constexpr int kNStages = 3;                     // A and B ring stages (one step each)
+constexpr int kNDist = 2;                       // steps the A and B loads run ahead
+constexpr int kNUnroll = 3;
+static_assert(kNDist < kNStages && kNUnroll % kNStages == 0, "narrow ring layout");
+constexpr int kNAStageBytes = kNM * 128;        // 32 rows x 64 inputs, fp16, swizzled chunks
+constexpr int kNBStageBytes = 4 * 4 * 1024;     // four waves x four code tiles
+constexpr int kNSStageBytes = 4 * 4 * 256;      // their scale/bias words, rows duplicated
+constexpr int kNBRingOff = kNStages * kNAStageBytes;
+constexpr int kNSRingOff = kNBRingOff + kNStages * kNBStageBytes;
+constexpr int kNSmemBytes = kNSRingOff + kNStages * kNSStageBytes;
+static_assert(2 * kNSmemBytes <= 159744, "two narrow workgroups per compute unit");
+constexpr int kNDmaPerStep = 9;                 // per thread: 1 A chunk, 4 code chunks, 4 scale/bias words
+constexpr int kNWaitA = (kNDmaPerStep - 1) + kNDmaPerStep * (kNDist - 1);   // loads after step g's A chunk
+constexpr int kNWaitB = kNDmaPerStep * (kNDist - 1);                        // loads after step g+1's words
+constexpr int kNWaitB0 = 1 + 8;                 // prologue: A and B of step 1 follow step 0's words
+constexpr int kNHPitch = 72;                    // gate/up epilogue: 32 rows x 64 fp16 per wave
+constexpr int kNOPitch = 520;                   // down epilogue: 32 rows x 512 fp32
+static_assert(4 * kNM * kNHPitch * 2 <= kNSmemBytes && kNM * kNOPitch * 4 <= kNSmemBytes, "narrow epilogue tiles");
+
+// One ring step of a narrow tile with one save and restore of M0: the thread's A chunk
+// (sbase_a + voff_a -> lds_a + 16 lane), the wave's four code tiles (b[t] + voff_b ->
+// lds_b + 1024 t + 16 lane) and their scale/bias words (s[t] + voff_s -> lds_s + 256 t + 4 lane).
+// With a_on false the A chunk is left out (the prologue issues B first).
+__device__ __forceinline__ void dma_narrow(const void *sbase_a, uint32_t voff_a, const uint8_t *lds_a,
+                                           const void *const b[4], uint32_t voff_b, const uint8_t *lds_b,
+                                           const void *const sw[4], uint32_t voff_s, const uint8_t *lds_s) {
+    const uint32_t ma = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_a);
+    const uint32_t mb = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_b);
+    const uint32_t ms = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_s);
+    const void *sa = uniform_ptr(sbase_a);
+    const void *b0 = uniform_ptr(b[0]), *b1 = uniform_ptr(b[1]), *b2 = uniform_ptr(b[2]), *b3 = uniform_ptr(b[3]);
+    const void *s0 = uniform_ptr(sw[0]), *s1 = uniform_ptr(sw[1]), *s2 = uniform_ptr(sw[2]), *s3 = uniform_ptr(sw[3]);
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %4\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %7\n\t"
+        "s_mov_b32 m0, %5\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %8\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %9\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %10\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %11\n\t"
+        "s_mov_b32 m0, %6\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %3, %12\n\t"
+        "s_add_u32 m0, m0, 0x100\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %3, %13\n\t"
+        "s_add_u32 m0, m0, 0x100\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %3, %14\n\t"
+        "s_add_u32 m0, m0, 0x100\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %3, %15\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "v"(voff_a), "v"(voff_b), "v"(voff_s), "s"(ma), "s"(mb), "s"(ms), "s"(sa), "s"(b0), "s"(b1), "s"(b2), "s"(b3),
+          "s"(s0), "s"(s1), "s"(s2), "s"(s3)
+        : "memory", "scc");
+}
+
+__device__ __forceinline__ void ring_sync_narrow() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kNWaitA) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// The narrow work items of one GEMM launch (workgroup index i = bid - a.n_wide): routed
+// items (the worst-case count, dealt to the XCDs as the 128-row items are) x output tiles of
+// 512 weight rows; items with more than 32 live rows, or past the real tiles, exit.
+template <int MODE, int FMT>
+__device__ __forceinline__ void pre_gemm_narrow(const PreArgs &a, uint8_t *smem, const int i) {
+    constexpr bool Q4 = FMT == kFmtQ4_0;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, half = lane >> 5;
+    const int E = a.E;
+
+    const int NT = MODE == 0 ? cdiv(a.I / 32, 8) : cdiv(a.d / 32, 16);
+    const int j = i >> 3;
+    const int mg = 8 * (j / NT) + (i & 7), nt = j % NT;
+    const int4 it = a.items[mg];   // in bounds: the table holds the worst-case tile count
+    if (mg >= a.tile_off[E]) return;
+    const int mt = it.y, rowbase = it.z, count = it.w;
+    const int live = count - mt * kMT;
+    if (live > kNM) return;   // a tile of the 128-row kernel
+    if (a.tile_mode) {
+        const int sl = a.eslot[it.x];
+        if (sl < 0 || sl >= a.n_slots) return;
+    }
+    const int e = expert_slot_of(a.eslot, a.n_slots, a.slot_faults, it.x, MODE == 0 && nt == 0 && threadIdx.x == 0);
+    const int K = MODE == 0 ? a.d : a.I;
+    const int G = K / 64;
+    const int J = MODE == 0 ? a.I : a.d;
+    const uint16_t *Asrc = MODE == 0 ? a.x16 : a.h_r;
+
+    // A row of this thread's chunk: tile row r = 8 wave + lane / 8 (padding rows read row 0)
+    uint32_t aro;
+    {
+        const int r = 8 * wave + (lane >> 3);
+        const int rr = r < live ? r : 0;
+        const int src = MODE == 0 ? a.perm[rowbase + mt * kMT + rr] / a.k : rowbase + mt * kMT + rr;
+        const int c = (lane & 7) ^ swz(r);
+        aro = ((uint32_t)src * K + 8 * c) * 2;
+    }
+    int aoff[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) aoff[s] = n * 128 + 16 * ((2 * s + half) ^ swz(n));
+
+    // the wave's four code tiles (a tile past the matrix reads tile 0 and is not stored)
+    const void *Bt[4], *St[4];
+    bool live_t[4];
+    float fS[4], fB[4], fR[4];
+    {
+        const size_t mat_bytes = (size_t)J * K / 2, mat_words = (size_t)J * G;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const moe_qmat *m = MODE == 0 ? ((t & 1) ? &a.up : &a.gate) : &a.down;
+            const int rb = MODE == 0 ? 8 * nt + 2 * wave + (t >> 1) : 16 * nt + 4 * wave + t;
+            live_t[t] = rb * 32 < J;
+            const int rbc = live_t[t] ? rb : 0;
+            Bt[t] = uniform_ptr(static_cast<const uint8_t *>(m->codes) + e * mat_bytes + (size_t)rbc * G * 1024);
+            St[t] = uniform_ptr(m->sb + e * mat_words + (size_t)rbc * G * 32);
+            const int kind = MODE == 0 ? (t & 1) : 2;
+            const int sh = a.shift[kind * a.n_mats + e];
+            fS[t] = __builtin_ldexpf(1.0f, 24 + sh);
+            fB[t] = __builtin_ldexpf(1.0f, sh);
+            fR[t] = __builtin_ldexpf(1.0f, -sh);
+        }
+    }
+    const bool live_w = live_t[0] || live_t[1] || live_t[2] || live_t[3];
+    const uint32_t boff = lane * 16, soff = n * 4;
+    auto issue = [&](int ga, int gb, int sa, int sbi) {
+        const void *bs[4], *ss[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            bs[t] = static_cast<const uint8_t *>(Bt[t]) + (size_t)gb * 1024;
+            ss[t] = static_cast<const uint8_t *>(St[t]) + gb * 128;
+        }
+        dma_narrow(reinterpret_cast<const uint8_t *>(Asrc) + 128 * ga, aro, smem + sa * kNAStageBytes + wave * 1024, bs,
+                   boff, smem + kNBRingOff + sbi * kNBStageBytes + wave * 4096, ss, soff,
+                   smem + kNSRingOff + sbi * kNSStageBytes + wave * 1024);
+    };
+    // raw code words and fp16 scale/bias pairs of the step in B stage sbi ([t][h] as in k_pre_gemm)
+    auto load_w = [&](int sbi, u32x4_t (&bw)[4], f16x2_t (&s2)[4][2], f16x2_t (&b2)[4][2], f16x2_t (&s2l)[4][2],
+                      f16x2_t (&b2l)[4][2]) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            bw[t] = ld16(smem + kNBRingOff + sbi * kNBStageBytes + wave * 4096 + t * 1024 + lane * 16);
+            const uint32_t sbw =
+                *reinterpret_cast<const uint32_t *>(smem + kNSRingOff + sbi * kNSStageBytes + wave * 1024 + t * 256 + lane * 4);
+            if constexpr (!Q4) {
+                const float sc = bf16_to_f32(sbw & 0xFFFFu) * fS[t], bi = bf16_to_f32(sbw >> 16) * fB[t];
+                s2[t][0] = s2[t][1] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(sc, sc * 0.0625f));
+                b2[t][0] = b2[t][1] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(bi, bi));
+            } else {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float dh = f16_to_f32((sbw >> (16 * h)) & 0xFFFFu);
+                    const float hi = __uint_as_float(__float_as_uint(dh) & 0xFFFF0000u), lo = dh - hi;
+                    const float sc = hi * fS[t], bi = hi * (-8.0f * fB[t]);
+                    const float scl = lo * fS[t], bil = lo * (-8.0f * fB[t]);
+                    s2[t][h] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(sc, sc * 0.0625f));
+                    b2[t][h] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(bi, bi));
+                    s2l[t][h] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(scl, scl * 0.0625f));
+                    b2l[t][h] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(bil, bil));
+                }
+            }
+        }
+    };
+
+    f32x16_t acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[t][v] = 0.0f;
+
+    // prologue: steps 0 .. kNDist - 1 into stages 0 .. kNDist - 1
+#pragma unroll
+    for (int p = 0; p < kNDist; ++p) issue(min(p, G - 1), min(p, G - 1), p, p);
+
+    auto kloop = [&]() {
+        u32x4_t bw[4];
+        f16x2_t s2[4][2], b2[4][2], s2l[4][2], b2l[4][2];
+        f16x8_t bf0[4], bl0[4];
+        auto step = [&](auto j_c, int g) {
+            constexpr int Ju = decltype(j_c)::value;
+            constexpr int SA = Ju % kNStages, SN = (Ju + kNDist) % kNStages, SB1 = (Ju + 1) % kNStages;
+            ring_sync_narrow();
+            {
+                const int gn = min(g + kNDist, G - 1);
+                issue(gn, gn, SN, SN);
+            }
+            if (live_w) {
+                const uint8_t *sA = smem + SA * kNAStageBytes;
+                u32x4_t af[2];
+                f16x8_t bf[2][4], bl[2][4];
+                af[0] = ld16(sA + aoff[0]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    bf[0][t] = bf0[t];
+                    if constexpr (Q4) bl[0][t] = bl0[t];
+                }
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    if (s < 3) {
+                        af[(s + 1) & 1] = ld16(sA + aoff[s + 1]);
+                    } else {
+                        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kNWaitB) : "memory");
+                        load_w(SB1, bw, s2, b2, s2l, b2l);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (s < 3) {
+                        const int hs = (s + 1) >> 1;
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            bf[(s + 1) & 1][t] = dequant_frag(bw[t][s + 1], s2[t][hs], b2[t][hs]);
+                            if constexpr (Q4) bl[(s + 1) & 1][t] = dequant_frag(bw[t][s + 1], s2l[t][hs], b2l[t][hs]);
+                        }
+                    }
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, af[s & 1]), bf[s & 1][t],
+                                                                       acc[t], 0, 0, 0);
+                        if constexpr (Q4)
+                            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, af[s & 1]),
+                                                                           bl[s & 1][t], acc[t], 0, 0, 0);
+                    }
+                    if (s == 3) {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            bf0[t] = dequant_frag(bw[t][0], s2[t][0], b2[t][0]);
+                            if constexpr (Q4) bl0[t] = dequant_frag(bw[t][0], s2l[t][0], b2l[t][0]);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kNWaitB) : "memory");
+            }
+        };
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kNWaitB0) : "memory");   // step 0's words
+        if (live_w) {
+            load_w(0, bw, s2, b2, s2l, b2l);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                bf0[t] = dequant_frag(bw[t][0], s2[t][0], b2[t][0]);
+                if constexpr (Q4) bl0[t] = dequant_frag(bw[t][0], s2l[t][0], b2l[t][0]);
+            }
+        }
+        int g = 0;
+        for (; g + kNUnroll <= G; g += kNUnroll)
+            unroll_steps<0, kNUnroll>([&](auto j_c) { step(j_c, g + decltype(j_c)::value); });
+        unroll_steps<0, kNUnroll - 1>([&](auto j_c) {
+            if (g + decltype(j_c)::value < G) step(j_c, g + decltype(j_c)::value);
+        });
+    };
+    kloop();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    // ---- epilogue. Accumulator element v of lane l in tile t: token row 8 (v/4) + 4 (l/32) +
+    // v%4, weight row l%32 of code tile t.
+    auto drow = [&](int r) { return r < live ? rowbase + mt * kMT + r : -1; };
+    if (MODE == 0) {
+        // h = fp16(gelu(g) * u) of the wave's two hidden blocks, through its own LDS tile
+        if (live_w) {
+            uint16_t *Hw = reinterpret_cast<uint16_t *>(smem + wave * kNM * kNHPitch * 2);
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = 8 * (v >> 2) + 4 * half + (v & 3);
+                    Hw[row * kNHPitch + 32 * hb + n] = (uint16_t)f32_to_f16_sat(
+                        gelu_tanh_f32(acc[2 * hb][v] * fR[2 * hb]) * (acc[2 * hb + 1][v] * fR[2 * hb + 1]));
+                }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            const int hb0 = 8 * nt + 2 * wave;
+            // lane -> row lane / 8 + 8 i, 16-byte chunk lane % 8 of the 64 hidden units
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = (lane >> 3) + 8 * i, c = lane & 7;
+                const int dst = drow(row);
+                if (dst >= 0 && live_t[2 * (c >> 2)])
+                    *reinterpret_cast<u32x4_t *>(a.h_r + (size_t)dst * J + 32 * hb0 + 8 * c) =
+                        *reinterpret_cast<const u32x4_t *>(Hw + row * kNHPitch + 8 * c);
+            }
+        }
+    } else {
+        // the 32 x 512 fp32 output tile leaves through LDS, each row as one run of 16-byte stores
+        float *O = reinterpret_cast<float *>(smem);
+        if (live_w) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = 8 * (v >> 2) + 4 * half + (v & 3);
+                    O[row * kNOPitch + wave * 128 + t * 32 + n] = acc[t][v] * fR[t];
+                }
+        }
+        __syncthreads();
+        const int c = tid & 127;   // 16-byte chunk of a row
+        const bool col_ok = nt * 512 + 4 * c < a.d;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = (tid >> 7) + 2 * i;
+            const int dst = drow(row);
+            if (col_ok && dst >= 0)
+                *reinterpret_cast<f32x4_t *>(a.r + (size_t)dst * a.d + nt * 512 + 4 * c) =
+                    *reinterpret_cast<const f32x4_t *>(O + row * kNOPitch + 4 * c);
+        }
+    }
+}
+
+// One prefill GEMM launch: workgroups [0, n_wide) take the shared-expert and 128-row routed
+// items, the rest the narrow items, so both kinds run side by side in one launch.
+template <int MODE, int FMT>
+__global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
+    static_assert(kNSmemBytes <= kSmemBytes, "one LDS buffer serves both tile kinds");
+    __shared__ __align__(16) uint8_t smem[kSmemBytes];
+    const int bid = blockIdx.x;
+    if (bid < a.n_wide) pre_gemm_wide<MODE, FMT>(a, smem, bid);
+    else pre_gemm_narrow<MODE, FMT>(a, smem, bid - a.n_wide);
+}
+
 // y[t] = a_t sh[t] + sum_s w[t,s] * r[pos[t*k+s]] in slot order, a_t the shared-expert gate
 // of token t from the fp16 copy of x (1 without a gate). grid (cdiv(d,1024), T); block 256
 __global__ __launch_bounds__(kGlueWG) void k_combine(int d, int k, const float *__restrict__ sh,
@@ -764,6 +1112,14 @@ int pre_grid(const moe_layer *L, int T, int mode) {
     return roundup(cdiv(T, kMT), 8) * NTs + roundup(Mr, 8) * NTr;
 }
 
+// Workgroups of one narrow-tile launch: the worst-case routed tile count (padded to a multiple
+// of 8) times the output tiles of 512 weight rows.
+int pre_grid_narrow(const moe_layer *L, int T, int mode) {
+    const moe_dims &D = L->dims;
+    const int NT = mode == 0 ? cdiv(D.d_expert / 32, 8) : cdiv(D.d_model / 32, 16);
+    return roundup(max_routed_tiles(T, D.top_k, D.n_experts), 8) * NT;
+}
+
 }  // namespace
 
 hipError_t launch_stage_shift(const moe_layer *L, bool routed, bool shared, int32_t *faults, hipStream_t s) {
@@ -797,10 +1153,12 @@ hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipSt
     PreArgs a = make_args(L, T);
     a.tile_mode = tile >= 0;
     a.shared = tile <= 0;
+    a.n_wide = pre_grid(L, T, 0);
+    const dim3 grid(a.n_wide + pre_grid_narrow(L, T, 0));
     if (L->dims.expert_format == MOE_FORMAT_Q4_0)
-        launch(k_pre_gemm<0, kFmtQ4_0>, dim3(pre_grid(L, T, 0)), dim3(kPreWG), 0, s, a);
+        launch(k_pre_gemm<0, kFmtQ4_0>, grid, dim3(kPreWG), 0, s, a);
     else
-        launch(k_pre_gemm<0, kFmtAffine>, dim3(pre_grid(L, T, 0)), dim3(kPreWG), 0, s, a);
+        launch(k_pre_gemm<0, kFmtAffine>, grid, dim3(kPreWG), 0, s, a);
     return hipGetLastError();
 }
 
@@ -808,10 +1166,12 @@ hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s, int tile) {
     PreArgs a = make_args(L, T);
     a.tile_mode = tile >= 0;
     a.shared = tile <= 0;
+    a.n_wide = pre_grid(L, T, 1);
+    const dim3 grid(a.n_wide + pre_grid_narrow(L, T, 1));
     if (L->dims.expert_format == MOE_FORMAT_Q4_0)
-        launch(k_pre_gemm<1, kFmtQ4_0>, dim3(pre_grid(L, T, 1)), dim3(kPreWG), 0, s, a);
+        launch(k_pre_gemm<1, kFmtQ4_0>, grid, dim3(kPreWG), 0, s, a);
     else
-        launch(k_pre_gemm<1, kFmtAffine>, dim3(pre_grid(L, T, 1)), dim3(kPreWG), 0, s, a);
+        launch(k_pre_gemm<1, kFmtAffine>, grid, dim3(kPreWG), 0, s, a);
     return hipGetLastError();
 }
 

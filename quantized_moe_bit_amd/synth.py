@@ -90,6 +90,7 @@ WORKLOADS: Dict[str, Workload] = {
     # the 2816-wide layer with Q4_0 experts
     "q4_0_decode": Workload("q4_0_decode", GEMMA_Q4_0, tokens=1, seed=7),
     "q4_0_prefill512": Workload("q4_0_prefill512", GEMMA_Q4_0, tokens=512, seed=8, zipf_s=1.1),
+    "q4_0_prefill4096": Workload("q4_0_prefill4096", GEMMA_Q4_0, tokens=4096, seed=9, zipf_s=1.3, tie_frac=0.02),
     "qwen_decode": Workload("qwen_decode", QWEN, tokens=1, seed=5, shared_gate=True),
     "qwen_prefill4096": Workload("qwen_prefill4096", QWEN, tokens=4096, seed=6, zipf_s=1.3, tie_frac=0.02,
                                  shared_gate=True),

@@ -234,6 +234,12 @@ moe_status moe_route(moe_layer *layer, const uint16_t *x, int32_t T, int32_t *to
  * (including the router prologue and per-expert scale when the weights carry them). With
  * expert slots every selected expert must be resident (see expert_slot).
  * T = 0 is a no-op; T above MOE_MAX_DECODE_TOKENS or max_tokens is MOE_E_CAPACITY.
+ * Range: the experts read x and the hidden activation h = gelu(gate x) * (up x) in fp16 (as
+ * moe_forward_prefill does). Values that round above 65504 in magnitude become infinite and a
+ * NaN stays NaN, so the output is then non-finite (MOE_FLAG_CHECK_FINITE reports it) rather
+ * than silently wrong; magnitudes below 2^-14 are fp16 subnormals and keep fewer significant
+ * bits (a layer input normalized to unit rms, and the hidden activations of weights with
+ * scales near the usual 2^-9 .. 2^-5, lie well inside the normal range).
  */
 moe_status moe_forward_decode(moe_layer *layer, const uint16_t *x, int32_t T, float *y,
                               void *hip_stream);

@@ -49,11 +49,10 @@ __device__ __forceinline__ bf16x8_t nib_frag(uint32_t w) {
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// float -> fp16 bits, round to nearest even, saturating at +-65504 (the expert hidden activation).
-__device__ __forceinline__ uint32_t f32_to_f16_sat(float f) {
-    f = fminf(fmaxf(f, -65504.0f), 65504.0f);
-    return __builtin_bit_cast(uint16_t, (_Float16)f);
-}
+// float -> fp16 bits, round to nearest even; magnitudes that round above 65504 become +-inf and
+// NaN stays NaN, so a value outside fp16's range makes the layer output non-finite (reported
+// under MOE_FLAG_CHECK_FINITE) instead of silently changing it.
+__device__ __forceinline__ uint32_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
 __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);

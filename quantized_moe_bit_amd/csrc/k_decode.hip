@@ -567,7 +567,7 @@ __global__ __launch_bounds__(64 * kBW) void k_dec_gateup(DecArgs a) {
                 gv += red[w][0][lane];
                 uv += red[w][1][lane];
             }
-            const uint32_t hb = f32_to_f16_sat(gelu_tanh_f32(gv) * uv);
+            const uint32_t hb = f32_to_f16(gelu_tanh_f32(gv) * uv);
             if (routed) a.h_r[(size_t)pr * a.I + 16 * jb + lane] = (uint16_t)hb;
             else a.h_s[(size_t)t * a.Is + 16 * jb + lane] = (uint16_t)hb;
             hv = f16_to_f32(hb);

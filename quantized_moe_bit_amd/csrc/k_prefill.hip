@@ -648,7 +648,7 @@ __device__ __forceinline__ void pre_gemm_wide(const PreArgs &a, uint8_t *smem, c
                     for (int v = 0; v < 16; ++v) {
                         const int row = 32 * ms + 8 * (v >> 2) + 4 * half + (v & 3);
                         Hw[row * kHPitch + n] =
-                            (uint16_t)f32_to_f16_sat(gelu_tanh_f32(acc[ms][0][v] * fR[0]) * (acc[ms][1][v] * fR[1]));
+                            (uint16_t)f32_to_f16(gelu_tanh_f32(acc[ms][0][v] * fR[0]) * (acc[ms][1][v] * fR[1]));
                     }
                 }
             }
@@ -991,7 +991,7 @@ __device__ __forceinline__ void pre_gemm_narrow(const PreArgs &a, uint8_t *smem,
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int row = 8 * (v >> 2) + 4 * half + (v & 3);
-                    Hw[row * kNHPitch + 32 * hb + n] = (uint16_t)f32_to_f16_sat(
+                    Hw[row * kNHPitch + 32 * hb + n] = (uint16_t)f32_to_f16(
                         gelu_tanh_f32(acc[2 * hb][v] * fR[2 * hb]) * (acc[2 * hb + 1][v] * fR[2 * hb + 1]));
                 }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void k_router_prologue(const uint16_t *__restr
                 for (int h = 0; h < 2; ++h) {
                     const uint32_t xb = (xv[c][w] >> (16 * h)) & 0xFFFFu, rb = (rv[c][w] >> (16 * h)) & 0xFFFFu;
                     ub[h] = f64_to_bf16(((bf16_to_f64(xb) * inv) * bf16_to_f64(rb)) / sd);
-                    hb[h] = f32_to_f16_sat(bf16_to_f32(xb));
+                    hb[h] = f32_to_f16(bf16_to_f32(xb));
                 }
                 uo[w] = ub[0] | (ub[1] << 16);
                 ho[w] = hb[0] | (hb[1] << 16);
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void k_router_tok(const uint16_t *__restrict__
                 u32x4_t h;
 #pragma unroll
                 for (int w = 0; w < 4; ++w)
-                    h[w] = f32_to_f16_sat(bf16_to_f32(v[c][w] & 0xFFFFu)) | (f32_to_f16_sat(bf16_to_f32(v[c][w] >> 16)) << 16);
+                    h[w] = f32_to_f16(bf16_to_f32(v[c][w] & 0xFFFFu)) | (f32_to_f16(bf16_to_f32(v[c][w] >> 16)) << 16);
                 xo[8 * g + c] = h;
             }
         }

@@ -11,6 +11,8 @@
 * MOE_FLAG_CHECK_FINITE: non-finite inputs are refused before anything is enqueued, a
   non-finite output is reported, finite calls give the same bits as without the flag
   (Mference, "Correctness and safety invariants": refuse rather than emit corrupt output).
+  Inputs or hidden activations beyond fp16's range (the experts' operand type) make the
+  output non-finite instead of clipping it, so the flag catches them too.
 * Profiling on and off give bit-identical outputs (Gem native architecture, "Ownership
   boundaries": the profiled route must match the ordinary one).
 """
@@ -166,6 +168,41 @@ def test_check_finite_flag():
     plain.close()
     chk.close()
     say("check-finite flag: identical when finite, refuses NaN/inf inputs, reports non-finite outputs")
+
+
+def test_values_beyond_fp16_range_make_the_output_nonfinite():
+    """The experts read x and the hidden activation in fp16: a finite bf16 input above 65504, or
+    a hidden activation above it (gate/up scales of 8), gives a non-finite output instead of a
+    silently clipped one, and MOE_FLAG_CHECK_FINITE reports it for decode and prefill."""
+    D = synth.Dims(d_model=256, n_experts=8, top_k=2, d_expert=128, d_shared=256)
+    lay = synth.gen_layer(D, 14, router="uniform")
+    x, _, _ = synth.gen_tokens(D, 24, 14)
+    big_x = x.copy()
+    big_x[5, 40] = synth.f32_to_bf16_bits(np.array([1.0e5], np.float32))[0]
+    big_h = synth.gen_layer(D, 14, router="uniform")
+    for name in ("gate", "up", "sh_gate", "sh_up"):
+        setattr(big_h, name, _rescale(getattr(big_h, name), np.random.default_rng(15), 8.0, 8.0))
+    for what, L, xx, row in (("x above 65504", lay, big_x, 5), ("hidden activation above 65504", big_h, x, None)):
+        plain = DeviceLayer(L, 32)
+        chk = DeviceLayer(L, 32, flags=B.MOE_FLAG_CHECK_FINITE)
+        xd = tokens_to_device(xx)
+        for path, T in (("prefill", 24), ("decode", 16)):
+            y = plain.prefill(xd[:T]) if path == "prefill" else plain.decode(xd[:T])
+            torch.cuda.synchronize()
+            yn = y.cpu().numpy()
+            if row is not None:
+                assert not np.all(np.isfinite(yn[row])), f"{what} {path}"
+                ok = np.ones(T, bool)
+                ok[row] = False
+                assert np.all(np.isfinite(yn[ok])), f"{what} {path}: other tokens stay finite"
+            else:
+                assert not np.all(np.isfinite(yn)), f"{what} {path}"
+            with pytest.raises(B.MoeError) as ei:
+                chk.prefill(xd[:T]) if path == "prefill" else chk.decode(xd[:T])
+            assert ei.value.status == B.MOE_E_NONFINITE and "output" in str(ei.value)
+        plain.close()
+        chk.close()
+        say(f"{what}: non-finite output, reported under the check-finite flag (decode and prefill)")
 
 
 def test_profiling_does_not_change_results():

@@ -29,6 +29,7 @@ namespace {
 
 
 constexpr int kRNE = 4;                  // experts per wave of the prefill router
+constexpr long kRouterKsplitMaxWG = 1280;   // see router_ksplit
 constexpr int kRBlk = 64 * kRNE;   // router table floats per (expert block, group)
 
 // Router prologue (Mference system design, "Decode", router listing): the router reads
@@ -211,6 +212,116 @@ __global__ __launch_bounds__(256) void k_router_tok(const uint16_t *__restrict__
         const int e = e0 + i;
         if (e < E) logits[(size_t)t * E + e] = logit_bias ? L[i] + logit_bias[e] : L[i];
     }
+}
+
+// Prefill router with the groups split across the waves of a workgroup: lane = token, the
+// workgroup = 64 tokens x kRNE experts, wave w computes the group sums A_g of groups
+// [w gw, (w + 1) gw) (gw = ceil(G / kKW)) with the same chains as k_router_tok and stores them
+// in LDS; after one barrier, wave i < kRNE folds expert i's sums in group order,
+// L = ((0 + A_0) + A_1) + ... + A_{G-1}, so the logits are bit-identical to k_router_tok's.
+// A wave brings its groups' inputs in with coalesced loads (eight lanes per token row) into a
+// staging tile of its own in LDS and reads them back one token row per lane, so it waits on no
+// other wave until the fold. A workgroup carries a quarter of k_router_tok's experts and an
+// eighth of each wave's chain, which fills the chip when the chunk has few tokens (512 tokens:
+// 256 workgroups of 8 waves against 64 of 4). LDS: G x kRNE x 64 fp32 of group sums (d <= 4096)
+// and 8 staging tiles of 64 x 64 bf16.
+// grid: (ceil(T / 64), ceil(E / kRNE)); block 64 kKW
+constexpr int kKW = 8;
+constexpr int kKSplitMaxG = 64;
+constexpr int kKXP = 72;   // bf16 per staged token row (144 B: row t's 16-byte chunks spread over the banks)
+__global__ __launch_bounds__(64 * kKW) void k_router_ksplit(const uint16_t *__restrict__ x, int T, int d, int E,
+                                                           const float *__restrict__ tab,
+                                                           const float *__restrict__ logit_bias,
+                                                           float *__restrict__ logits, uint16_t *__restrict__ x16) {
+    __shared__ float As[kKSplitMaxG][kRNE][64];
+    __shared__ __align__(16) uint16_t xsw[kKW][64][kKXP];
+    const int G = d / 64;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int eb = blockIdx.y, e0 = eb * kRNE;
+    const int t = blockIdx.x * 64 + lane;
+    const int gw = cdiv(G, kKW), g0 = wave * gw, g1 = min(G, g0 + gw);
+    // coalesced loads: this lane moves chunk lc = lane % 8 (inputs 8 lc .. 8 lc + 7 of the group)
+    // of token rows lane / 8 + 8 i, i = 0..7
+    const int lc = lane & 7, lr = lane >> 3;
+    uint16_t (*xw)[kKXP] = xsw[wave];
+    const float *blk = tab + (size_t)eb * G * kRBlk;
+    auto load_q = [&](int g, f32x4_t (&q)[4]) {
+#pragma unroll
+        for (int jc = 0; jc < 4; ++jc)
+            q[jc] = *reinterpret_cast<const f32x4_t *>(blk + (size_t)g * kRBlk + (16 * jc + (lane & 15)) * kRNE);
+    };
+    auto load_x = [&](int g, u32x4_t (&v)[8]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = min((int)blockIdx.x * 64 + lr + 8 * i, T - 1);
+            v[i] = ld16(x + (size_t)r * d + 64 * g + 8 * lc);
+        }
+    };
+    // loaded chunks into the staging tile (and, for the first expert block, the fp16 copy of x)
+    auto put_x = [&](int g, const u32x4_t (&v)[8]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int rl = lr + 8 * i;
+            *reinterpret_cast<u32x4_t *>(&xw[rl][8 * lc]) = v[i];
+            const int r = (int)blockIdx.x * 64 + rl;
+            if (x16 && eb == 0 && r < T) {
+                u32x4_t h;
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    h[w] = f32_to_f16(bf16_to_f32(v[i][w] & 0xFFFFu)) | (f32_to_f16(bf16_to_f32(v[i][w] >> 16)) << 16);
+                *reinterpret_cast<u32x4_t *>(x16 + (size_t)r * d + 64 * g + 8 * lc) = h;
+            }
+        }
+    };
+    if (g0 < g1) {
+        u32x4_t nv[8];
+        f32x4_t qa[4], qb[4];
+        load_x(g0, nv);
+        load_q(g0, qa);
+        put_x(g0, nv);
+        // one group: the next group's loads go out first; its inputs replace this group's in the
+        // staging tile after this group's reads (LDS operations of a wave complete in order)
+        auto group = [&](int g, const f32x4_t (&q)[4], f32x4_t (&qn)[4]) {
+            const bool more = g + 1 < g1;
+            if (more) {
+                load_x(g + 1, nv);
+                load_q(g + 1, qn);
+            }
+            float A[kRNE];
+#pragma unroll
+            for (int i = 0; i < kRNE; ++i) A[i] = 0.0f;
+#pragma unroll
+            for (int jc = 0; jc < 4; ++jc) {
+                // inputs 16 jc .. 16 jc + 15 of this lane's token as fp32 (bf16 -> fp32 is exact)
+                const u32x4_t c0 = *reinterpret_cast<const u32x4_t *>(&xw[lane][16 * jc]);
+                const u32x4_t c1 = *reinterpret_cast<const u32x4_t *>(&xw[lane][16 * jc + 8]);
+                f32x4_t xf[4];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    xf[w >> 1][2 * (w & 1)] = __uint_as_float(c0[w] << 16);
+                    xf[w >> 1][2 * (w & 1) + 1] = __uint_as_float(c0[w] & 0xFFFF0000u);
+                    xf[2 + (w >> 1)][2 * (w & 1)] = __uint_as_float(c1[w] << 16);
+                    xf[2 + (w >> 1)][2 * (w & 1) + 1] = __uint_as_float(c1[w] & 0xFFFF0000u);
+                }
+                chunk_fmas<0>(A, xf, q[jc]);
+            }
+#pragma unroll
+            for (int i = 0; i < kRNE; ++i) As[g][i][lane] = A[i];
+            if (more) put_x(g + 1, nv);
+        };
+        for (int g = g0; g < g1; g += 2) {
+            group(g, qa, qb);
+            if (g + 1 < g1) group(g + 1, qb, qa);
+        }
+    }
+    __syncthreads();
+    if (wave >= kRNE || t >= T) return;
+    const int e = e0 + wave;
+    if (e >= E) return;
+    float L = 0.0f;   // contraction is off for this file: the fold is L = L + A_g, in group order
+    for (int g = 0; g < G; ++g) L = L + As[g][wave][lane];
+    logits[(size_t)t * E + e] = logit_bias ? L + logit_bias[e] : L;
 }
 
 // The router table k_router_tok reads (weights fma(scale, q, bias) in fp32; layout above).
@@ -463,11 +574,21 @@ __global__ __launch_bounds__(256) void k_bucket_scatter(const int32_t *__restric
 
 }  // namespace
 
+// k_router_ksplit while its launch has at most kRouterKsplitMaxWG workgroups (five per compute
+// unit); both kernels give the same bits. Measured on the 2816-wide, 128-expert layer (router
+// kernel, ksplit against k_router_tok): 256 tokens 17.0 / 62.1 us, 512: 18.8 / 64.2, 1024:
+// 30.6 / 64.6, 2048: 52.3 / 65.0, 3072: 73.8 / 67.6.
+static bool router_ksplit(int T, int E) { return (long)cdiv(T, 64) * cdiv(E, kRNE) <= kRouterKsplitMaxWG; }
+
 hipError_t launch_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s,
                          bool write_aux) {
     const int d = L->dims.d_model, E = L->dims.n_experts;
-    launch(k_router_tok, dim3(cdiv(T, 64), cdiv(E, 4 * kRNE)), dim3(256), 0, s, x, T, d, E, L->ws.rqf,
-           L->w.logit_bias, logits, write_aux ? L->ws.x16 : nullptr);
+    if (d / 64 <= kKSplitMaxG && router_ksplit(T, E))
+        launch(k_router_ksplit, dim3(cdiv(T, 64), cdiv(E, kRNE)), dim3(64 * kKW), 0, s, x, T, d, E, L->ws.rqf,
+               L->w.logit_bias, logits, write_aux ? L->ws.x16 : nullptr);
+    else
+        launch(k_router_tok, dim3(cdiv(T, 64), cdiv(E, 4 * kRNE)), dim3(256), 0, s, x, T, d, E, L->ws.rqf,
+               L->w.logit_bias, logits, write_aux ? L->ws.x16 : nullptr);
     return hipGetLastError();
 }
 

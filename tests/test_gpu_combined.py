@@ -1,12 +1,16 @@
 """GPU parity with every optional layer feature at once, through the C ABI: a decode stack of
 2048-wide layers with 256 experts (the gated-shared-expert workload's shape) whose layers carry
 the router prologue and per-expert scale (Mference system design, "Decode", router listing),
-the gated shared expert ("Scope and limitations") and the layer tail ("Decode", cb2).
+the gated shared expert ("Scope and limitations") and the layer tail ("Decode", cb2), with
+affine group-64 experts and with Q4_0 experts (Gem native architecture, "M4 Max operating
+assumptions").
 
 Layer by layer on the GPU's own stream (teacher forcing): logits bit-identical, top-k exact,
 layer output within max |err| <= 2e-3 * rms of the oracle, residual step with the tail
 bit-exact; then the stack entry point reproduces the layer-by-layer stream bit for bit.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -35,8 +39,9 @@ def full_layer(dims, seed):
     return lay
 
 
-def test_stack_with_every_layer_feature():
-    dims = synth.WORKLOADS["qwen_decode"].dims
+@pytest.mark.parametrize("fmt", ["affine", "q4_0"])
+def test_stack_with_every_layer_feature(fmt):
+    dims = dataclasses.replace(synth.WORKLOADS["qwen_decode"].dims, expert_format=fmt)
     NL, T = 3, 4
     layers = [full_layer(dims, 120 + l) for l in range(NL)]
     dls = [DeviceLayer(l, max_tokens=16) for l in layers]
@@ -68,7 +73,7 @@ def test_stack_with_every_layer_feature():
         hn_ref, xn_ref = oracle.stack_glue(h_prev, y_gpu, post=lay.post_ffn_norm, scalar=scal)
         np.testing.assert_array_equal(bits(hs), hn_ref, err_msg=f"layer {l} residual")
         np.testing.assert_array_equal(bits(xs), xn_ref, err_msg=f"layer {l} norm")
-        print(f"[combined] layer {l}: logits and top-k exact, max|err| {err:.2e} rms, residual bit-exact",
+        print(f"[combined] {fmt} layer {l}: logits and top-k exact, max|err| {err:.2e} rms, residual bit-exact",
               flush=True)
     h = tokens_to_device(h0, dev)
     xb = torch.empty((1, dims.d_model), dtype=torch.int16, device=dev)
@@ -78,6 +83,6 @@ def test_stack_with_every_layer_feature():
         B.moe_stack_forward_decode([d.handle for d in dls], h[t:t + 1], 1, xb, yb, hb)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bits(h), bits(hs))
-    print(f"[combined] stack entry point: {T} tokens x {NL} layers identical", flush=True)
+    print(f"[combined] {fmt} stack entry point: {T} tokens x {NL} layers identical", flush=True)
     for d in dls:
         d.close()

@@ -3,9 +3,12 @@ widest model dimension the kernels take (8192: router lanes loop over 128 groups
 experts with the largest top-k (256 experts, top-16: four logits per lane in the top-k,
 every down-projection wave shared), the largest expert count (1024, top-8), top-1 (a single routing weight of exactly 1), and widths
 whose last prefill tile is only partly filled, and expert scales above 2^-4.
-Same bar as the other parity tests: top-k index sets and grouping bit-exact, outputs within
-max |err| <= 2e-3 * rms of the oracle.
+Each shape runs with affine group-64 experts and (except the rescaled-scale case, which is about
+affine metadata) with Q4_0 experts. Same bar as the other parity tests: top-k index sets and
+grouping bit-exact, outputs within max |err| <= 2e-3 * rms of the oracle.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -48,11 +51,17 @@ def check_close(y_gpu, y_ref, what):
     print(f"[shapes] {what}: max|err| {err / rms:.2e} rms", flush=True)
 
 
-@pytest.mark.parametrize("name", list(SHAPES))
-def test_shape(name):
+# every shape with affine experts; the ones that do not rescale affine metadata with Q4_0 experts too
+CASES = [(n, "affine") for n in SHAPES] + [(n, "q4_0") for n in SHAPES if n != "large_scales"]
+
+
+@pytest.mark.parametrize("name,fmt", CASES)
+def test_shape(name, fmt):
     dims, t_dec, t_pre = SHAPES[name]
+    dims = dataclasses.replace(dims, expert_format=fmt)
+    name = name if fmt == "affine" else f"{name} q4_0"
     lay = synth.gen_layer(dims, 11)
-    if name == "large_scales":
+    if name == "large_scales":   # affine only
         for m in (lay.gate, lay.up, lay.down, lay.sh_gate, lay.sh_up, lay.sh_down):
             m.scales[...] = times8(m.scales)
             m.biases[...] = times8(m.biases)

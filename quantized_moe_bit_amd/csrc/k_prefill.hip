@@ -701,8 +701,8 @@ __device__ __forceinline__ void pre_gemm_wide(const PreArgs &a, uint8_t *smem, c
 
 // ----------------------------------------------------------------------------- narrow tiles
 // Routed row tiles with at most 32 live rows (experts with few pairs, and the last tile of
-// an expert whose pairs end just past a multiple of 128) run in a launch of their own with a
-// narrow workgroup tile: 32 token rows x 512 weight rows. In the 128-row kernel such a tile
+// an expert whose pairs end just past a multiple of 128) run as narrow work items, after the
+// 128-row ones in the same launch: 32 token rows x 512 weight rows per workgroup. In the 128-row kernel such a tile
 // streams the weights of 256 weight rows and a 128-row A ring for a quarter of the MFMA work;
 // here each weight is still dequantized once per tile, but the tile moves twice the weights
 // per step behind one barrier, its A ring is a quarter of the size, and the weight ring runs
@@ -731,8 +731,8 @@ static_assert(4 * kNM * kNHPitch * 2 <= kNSmemBytes && kNM * kNOPitch * 4 <= kNS
 
 // One ring step of a narrow tile with one save and restore of M0: the thread's A chunk
 // (sbase_a + voff_a -> lds_a + 16 lane), the wave's four code tiles (b[t] + voff_b ->
-// lds_b + 1024 t + 16 lane) and their scale/bias words (s[t] + voff_s -> lds_s + 256 t + 4 lane).
-// With a_on false the A chunk is left out (the prologue issues B first).
+// lds_b + 1024 t + 16 lane) and their scale/bias words (s[t] + voff_s -> lds_s + 256 t + 4 lane),
+// in that order (the counted waits assume it).
 __device__ __forceinline__ void dma_narrow(const void *sbase_a, uint32_t voff_a, const uint8_t *lds_a,
                                            const void *const b[4], uint32_t voff_b, const uint8_t *lds_b,
                                            const void *const sw[4], uint32_t voff_s, const uint8_t *lds_s) {

@@ -10,6 +10,10 @@
 //   A_g = fma chain of x_j * w_j, ascending j         (fp32, starting from 0)
 //   logit = (A_0 + A_1 + ... + A_{G-1}) [+ logit_bias]   (fp32 adds, ascending g)
 // Contraction is disabled in this file so the compiler cannot fuse or reorder these.
+// Two kernels compute it: k_router_tok (one token per lane, all groups in one wave) for
+// large chunks, and k_router_ksplit (the groups of a token spread over eight waves, each
+// A_g kept in LDS and folded in ascending g by one wave) for chunks too small to fill the
+// chip that way; both give the same bits.
 //
 // Top-k: the k largest logits, largest first, equal values ordered by lower expert
 // index (TinyTitan architecture, "Invariants": top-k index sets must match exactly),
@@ -25,8 +29,6 @@
 
 namespace qmoe {
 namespace {
-
-
 
 constexpr int kRNE = 4;                  // experts per wave of the prefill router
 constexpr long kRouterKsplitMaxWG = 1280;   // see router_ksplit

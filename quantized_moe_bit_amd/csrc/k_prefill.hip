@@ -19,9 +19,11 @@
 // subnormal quantum 2^-24 of the staged scale), and each K-step runs one MFMA per part into the
 // same accumulator.
 //
-// Work items: (expert or shared, 128-row tile, output tile), one per workgroup; all output
-// tiles of a row tile run on the same XCD (workgroup i runs on XCD i % 8), so the row tile
-// is fetched into one L2. Routed tiles with at most 32 live rows take a narrow workgroup tile
+// Work items: (expert or shared, 128-row tile, output tile), one per workgroup, taken from the
+// work list of the workgroup's XCD (workgroup b runs on XCD b % 8 and takes item b / 8 of its
+// list; the lists are built with the grouping so that the XCDs get about the same work, the
+// longest items first, and all output tiles of a routed row tile on one XCD, so its rows are
+// fetched into one L2). Routed tiles with at most 32 live rows take a narrow workgroup tile
 // (32 token rows x 512 weight rows) in the same launch.
 #include <type_traits>
 
@@ -225,8 +227,10 @@ __device__ __forceinline__ void unroll_steps(F &&f) {
 struct PreArgs {
     int T, d, k, I, Is, E;
     const uint16_t *x16;        // gate/up A rows [T, d], fp16
-    const int32_t *perm, *tile_off;
-    const int4 *items;          // routed work items (expert, row tile, first pair row, pairs)
+    const int32_t *perm;
+    const int4 *list;           // [kXcds][cap] work items of this launch (Workspace::list)
+    const int32_t *list_n;      // [kXcds] items in each XCD's list
+    int cap;
     moe_qmat gate, up, sh_gate, sh_up, down, sh_down;
     uint16_t *h_r, *h_s;        // hidden activations (fp16): [T k, I] bucket order, [T, I_s]
     float *r, *sh;
@@ -238,7 +242,6 @@ struct PreArgs {
     int tile_mode, shared;
     const int32_t *shift;       // fp16 staging exponents: [kind * n_mats + matrix], shared at [3 n_mats + kind]
     int n_mats;
-    int n_wide;                 // workgroups of the 128-row items; the narrow items follow
 };
 
 enum { kFmtAffine = 0, kFmtQ4_0 = 1 };
@@ -347,13 +350,12 @@ __global__ __launch_bounds__(256) void k_stage_shift(StageArgs a) {
     a.shift[sh ? 3 * a.n_mats + kind : kind * a.n_mats + mat] = m;
 }
 
-// The 128-row work items of one GEMM launch (workgroup index bid < a.n_wide).
+// A 128-row work item of one GEMM launch (kind kItemShared or kItemWide; Workspace::list).
 template <int MODE, int FMT>  // MODE 0: gate/up + GeGLU, 1: down; FMT: kFmtAffine / kFmtQ4_0
-__device__ __forceinline__ void pre_gemm_wide(const PreArgs &a, uint8_t *smem, const int bid) {
+__device__ __forceinline__ void pre_gemm_wide(const PreArgs &a, uint8_t *smem, const int4 it) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, half = lane >> 5;
-    const int E = a.E;
 
     // A-fragment byte offsets within a stage: row 32 ms + n, logical chunk 2 s + half sits
     // at aoff[s] + 4096 ms.
@@ -361,39 +363,22 @@ __device__ __forceinline__ void pre_gemm_wide(const PreArgs &a, uint8_t *smem, c
 #pragma unroll
     for (int s = 0; s < 4; ++s) aoff[s] = n * 128 + 16 * ((2 * s + half) ^ swz(n));
 
-    // Work item of this workgroup (one per workgroup). Shared-expert items come first, then
-    // routed ones; within each part, 128-row tiles are dealt to the eight XCDs round-robin
-    // (workgroup b runs on XCD b % 8, parts start at multiples of 8) and every output tile
-    // of a row tile runs on the same XCD, so the row tile is fetched into one L2 only. The
-    // routed part is sized for the worst case; workgroups past the real tiles exit at once.
-    const int Ms = cdiv(a.T, kMT), Ms8 = roundup(Ms, 8);
-    const int NTs = MODE == 0 ? cdiv(a.Is / 32, 4) : cdiv(a.d / 64, 4);
-    const int NTr = MODE == 0 ? cdiv(a.I / 32, 4) : cdiv(a.d / 64, 4);
-    const int Gs = Ms8 * NTs;
-    bool shared_item;
-    int e = 0, mt, nt, count, rowbase;
-    if (bid < Gs) {
-        const int j = bid >> 3;
-        shared_item = true;
-        mt = 8 * (j / NTs) + (bid & 7);
-        nt = j % NTs;
-        if (mt >= Ms || !a.shared) return;
+    // The work item: a row tile of the shared expert or of a routed expert with more than 32 live
+    // rows, and its output tile nt
+    const bool shared_item = (it.y >> 28) == kItemShared;
+    const int nt = it.x >> 16, mt = it.y & 0xFFFFFFF;
+    int e = 0, count, rowbase;
+    if (shared_item) {
+        if (!a.shared) return;
         count = a.T;
         rowbase = 0;
     } else {
-        const int i = bid - Gs, j = i >> 3;
-        shared_item = false;
-        const int mg = 8 * (j / NTr) + (i & 7);
-        nt = j % NTr;
-        const int4 it = a.items[mg];   // in bounds: the table holds the worst-case tile count
-        if (mg >= a.tile_off[E]) return;
+        const int ex = it.x & 0xFFFF;
         if (a.tile_mode) {   // another tile's expert: its rows are computed by that tile's launch
-            const int sl = a.eslot[it.x];
+            const int sl = a.eslot[ex];
             if (sl < 0 || sl >= a.n_slots) return;
         }
-        if (it.w - it.y * kMT <= kNMRows) return;   // at most 32 live rows: the narrow-tile launch
-        e = expert_slot_of(a.eslot, a.n_slots, a.slot_faults, it.x, MODE == 0 && nt == 0 && threadIdx.x == 0);
-        mt = it.y;
+        e = expert_slot_of(a.eslot, a.n_slots, a.slot_faults, ex, MODE == 0 && nt == 0 && threadIdx.x == 0);
         rowbase = it.z;
         count = it.w;
     }
@@ -785,30 +770,23 @@ __device__ __forceinline__ void ring_sync_narrow() {
     asm volatile("" ::: "memory");
 }
 
-// The narrow work items of one GEMM launch (workgroup index i = bid - a.n_wide): routed
-// items (the worst-case count, dealt to the XCDs as the 128-row items are) x output tiles of
-// 512 weight rows; items with more than 32 live rows, or past the real tiles, exit.
+// A narrow work item of one GEMM launch (kind kItemNarrow): a routed row tile with at most 32
+// live rows and its output tile nt of 512 weight rows.
 template <int MODE, int FMT>
-__device__ __forceinline__ void pre_gemm_narrow(const PreArgs &a, uint8_t *smem, const int i) {
+__device__ __forceinline__ void pre_gemm_narrow(const PreArgs &a, uint8_t *smem, const int4 it) {
     constexpr bool Q4 = FMT == kFmtQ4_0;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, half = lane >> 5;
-    const int E = a.E;
 
-    const int NT = MODE == 0 ? cdiv(a.I / 32, 8) : cdiv(a.d / 32, 16);
-    const int j = i >> 3;
-    const int mg = 8 * (j / NT) + (i & 7), nt = j % NT;
-    const int4 it = a.items[mg];   // in bounds: the table holds the worst-case tile count
-    if (mg >= a.tile_off[E]) return;
-    const int mt = it.y, rowbase = it.z, count = it.w;
-    const int live = count - mt * kMT;
-    if (live > kNM) return;   // a tile of the 128-row kernel
+    const int ex = it.x & 0xFFFF, nt = it.x >> 16;
+    const int mt = it.y & 0xFFFFFFF, rowbase = it.z, count = it.w;
+    const int live = count - mt * kMT;   // 1 .. kNM (the list's class of the tile)
     if (a.tile_mode) {
-        const int sl = a.eslot[it.x];
+        const int sl = a.eslot[ex];
         if (sl < 0 || sl >= a.n_slots) return;
     }
-    const int e = expert_slot_of(a.eslot, a.n_slots, a.slot_faults, it.x, MODE == 0 && nt == 0 && threadIdx.x == 0);
+    const int e = expert_slot_of(a.eslot, a.n_slots, a.slot_faults, ex, MODE == 0 && nt == 0 && threadIdx.x == 0);
     const int K = MODE == 0 ? a.d : a.I;
     const int G = K / 64;
     const int J = MODE == 0 ? a.I : a.d;
@@ -1032,15 +1010,18 @@ __device__ __forceinline__ void pre_gemm_narrow(const PreArgs &a, uint8_t *smem,
     }
 }
 
-// One prefill GEMM launch: workgroups [0, n_wide) take the shared-expert and 128-row routed
-// items, the rest the narrow items, so both kinds run side by side in one launch.
+// One prefill GEMM launch: workgroup b takes item b / kXcds of XCD b % kXcds's list (past the
+// list's items it exits), 128-row and narrow items side by side.
 template <int MODE, int FMT>
 __global__ __launch_bounds__(kPreWG, 2) void k_pre_gemm(PreArgs a) {
     static_assert(kNSmemBytes <= kSmemBytes, "one LDS buffer serves both tile kinds");
     __shared__ __align__(16) uint8_t smem[kSmemBytes];
-    const int bid = blockIdx.x;
-    if (bid < a.n_wide) pre_gemm_wide<MODE, FMT>(a, smem, bid);
-    else pre_gemm_narrow<MODE, FMT>(a, smem, bid - a.n_wide);
+    const int x = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
+    const int n = a.list_n[x];
+    const int4 it = a.list[x * a.cap + q];   // in bounds: the grid is kXcds cap workgroups
+    if (q >= n) return;
+    if ((it.y >> 28) == kItemNarrow) pre_gemm_narrow<MODE, FMT>(a, smem, it);
+    else pre_gemm_wide<MODE, FMT>(a, smem, it);
 }
 
 // y[t] = a_t sh[t] + sum_s w[t,s] * r[pos[t*k+s]] in slot order, a_t the shared-expert gate
@@ -1080,8 +1061,6 @@ PreArgs make_args(const moe_layer *L, int T) {
     a.E = D.n_experts;
     a.x16 = L->ws.x16;
     a.perm = L->ws.perm;
-    a.tile_off = L->ws.tile_off;
-    a.items = L->ws.items;
     a.gate = L->w.gate;
     a.up = L->w.up;
     a.sh_gate = L->w.sh_gate;
@@ -1102,23 +1081,8 @@ PreArgs make_args(const moe_layer *L, int T) {
     return a;
 }
 
-// Workgroups of one prefill GEMM launch: shared part (row tiles padded to a multiple of 8)
-// plus the routed part sized for the worst case, cdiv(T k, 128) + min(E, T k) row tiles.
-int pre_grid(const moe_layer *L, int T, int mode) {
-    const moe_dims &D = L->dims;
-    const int NTs = mode == 0 ? cdiv(D.d_shared / 32, 4) : cdiv(D.d_model / 64, 4);
-    const int NTr = mode == 0 ? cdiv(D.d_expert / 32, 4) : cdiv(D.d_model / 64, 4);
-    const int Mr = max_routed_tiles(T, D.top_k, D.n_experts);
-    return roundup(cdiv(T, kMT), 8) * NTs + roundup(Mr, 8) * NTr;
-}
-
-// Workgroups of one narrow-tile launch: the worst-case routed tile count (padded to a multiple
-// of 8) times the output tiles of 512 weight rows.
-int pre_grid_narrow(const moe_layer *L, int T, int mode) {
-    const moe_dims &D = L->dims;
-    const int NT = mode == 0 ? cdiv(D.d_expert / 32, 8) : cdiv(D.d_model / 32, 16);
-    return roundup(max_routed_tiles(T, D.top_k, D.n_experts), 8) * NT;
-}
+// Workgroups of one prefill GEMM launch: kXcds lists of gemm_list_cap items.
+int pre_grid(const moe_layer *L, int T, int mode) { return kXcds * gemm_list_cap(L->dims, T, mode); }
 
 }  // namespace
 
@@ -1153,8 +1117,10 @@ hipError_t launch_pre_gateup(const moe_layer *L, const uint16_t *x, int T, hipSt
     PreArgs a = make_args(L, T);
     a.tile_mode = tile >= 0;
     a.shared = tile <= 0;
-    a.n_wide = pre_grid(L, T, 0);
-    const dim3 grid(a.n_wide + pre_grid_narrow(L, T, 0));
+    a.list = L->ws.list[0];
+    a.list_n = L->ws.list_n;
+    a.cap = gemm_list_cap(L->dims, T, 0);
+    const dim3 grid(pre_grid(L, T, 0));
     if (L->dims.expert_format == MOE_FORMAT_Q4_0)
         launch(k_pre_gemm<0, kFmtQ4_0>, grid, dim3(kPreWG), 0, s, a);
     else
@@ -1166,8 +1132,10 @@ hipError_t launch_pre_down(const moe_layer *L, int T, hipStream_t s, int tile) {
     PreArgs a = make_args(L, T);
     a.tile_mode = tile >= 0;
     a.shared = tile <= 0;
-    a.n_wide = pre_grid(L, T, 1);
-    const dim3 grid(a.n_wide + pre_grid_narrow(L, T, 1));
+    a.list = L->ws.list[1];
+    a.list_n = L->ws.list_n + kXcds;
+    a.cap = gemm_list_cap(L->dims, T, 1);
+    const dim3 grid(pre_grid(L, T, 1));
     if (L->dims.expert_format == MOE_FORMAT_Q4_0)
         launch(k_pre_gemm<1, kFmtQ4_0>, grid, dim3(kPreWG), 0, s, a);
     else

@@ -473,21 +473,44 @@ __device__ __forceinline__ void block_scan(int (&v)[NV], int (&tot)[NV], int32_t
 
 constexpr int kScanPiece = 16384;   // chunk counts per LDS piece of the scan
 
-// Counts, offsets, per-chunk bases and the GEMM's routed work items. grid 1; block 1024
-// (thread e: expert e).
+// Class dealt o-th in launch m's lists: the classes by live rows of the tile (0: 97-128, 1: 65-96,
+// 2: 33-64, 3: at most 32, narrow) in the order of their measured item durations, longest
+// first (gate/up: 0, 1, 3, 2; down: 0, 1, 2, 3)
+__device__ __forceinline__ int list_class(int m, int o) { return (m == 0 && o >= 2) ? 5 - o : o; }
+
+// Arguments of the GEMM work-list build (gemm_list_cap has the list bound)
+struct ListArgs {
+    int T;                           // tokens of the chunk: cdiv(T, kMT) shared row tiles
+    int nts[2], ntr[2], ntn[2];      // output tiles per row tile (shared, routed 128-row, narrow), per launch
+    int cap[2];                      // list capacity per XCD, per launch
+    int4 *list[2];                   // [kXcds][cap]: gate/up, down
+    int32_t *list_n;                 // [2][kXcds]
+};
+
+// Counts, offsets, per-chunk bases and the work lists of the two GEMM launches. grid 1;
+// block 1024 (thread e: expert e).
 //  * chunk_base[c][e] becomes the number of pairs of expert e in chunks before c (the expert's
 //    own start is added by the scatter), in pieces of whole chunks staged in LDS with coalesced
 //    loads and stores.
-//  * counts[e], offsets[e] (exclusive prefix; offsets[E] = all pairs), tile_off[e] (prefix of
-//    ceil(counts / mt) in expert order; tile_off[E] = all routed row tiles).
-//  * items: one (expert, row tile, first pair row, pairs of the expert) per row tile, in expert
-//    order (a part-filled last tile after the expert's full ones).
+//  * counts[e], offsets[e] (exclusive prefix; offsets[E] = all pairs).
+//  * Work lists (one per launch and XCD; gemm_list_cap). Routed row tiles fall in four classes by
+//    their live rows (97-128, 65-96, 33-64: 128-row items; at most 32: narrow items), dealt in
+//    the order list_class gives (longest items first). A list holds, in this order, its share
+//    of the shared-expert items (item i of S = cdiv(T, kMT) nts to XCD i % 8, in order) and,
+//    per class, whole routed tiles (all their output tiles, so a tile's rows are fetched into
+//    one L2): rank r of class c (expert order) goes to the XCD in position r % 8 of that
+//    class's order, the XCDs sorted by the items they hold before the class (ties to the lower
+//    XCD). The workgroups of an XCD start in list order, so the longest items start first and
+//    the XCDs end together.
 __global__ __launch_bounds__(1024) void k_bucket_scan(int nchunks, int E, int32_t *__restrict__ chunk_base,
                                                       int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-                                                      int32_t *__restrict__ tile_off, int mt, int4 *__restrict__ items) {
+                                                      ListArgs la) {
+    static_assert(kTileTabMax <= kScanPiece, "the tile table reuses the scan's piece buffer");
     __shared__ int32_t piece[kScanPiece];
-    __shared__ int32_t ws[16][2];
+    __shared__ int32_t ws[16][5];
     __shared__ int32_t seg[8][MOE_MAX_EXPERTS];
+    __shared__ int32_t plan_sh[2][kXcds], plan_n[2][kXcds];
+    __shared__ int32_t plan_start[2][4][kXcds], plan_pos[2][4][kXcds], plan_unit[2][4][kXcds];
     __shared__ int32_t carry[MOE_MAX_EXPERTS];   // pairs of each expert in the pieces so far
     const int tid = threadIdx.x, e = tid;
     const int pc = kScanPiece / E;   // chunks per piece (E <= 1024)
@@ -542,19 +565,103 @@ __global__ __launch_bounds__(1024) void k_bucket_scan(int nchunks, int E, int32_
         __syncthreads();   // the piece is refilled
     }
     const bool ok = e < E;
-    const int cnt = ok ? carry[e] : 0, ntile = (cnt + mt - 1) / mt;
-    int v[2] = {cnt, ntile};
-    int tot[2];
-    block_scan<2>(v, tot, ws, min(16, (E + 63) / 64));
+    const int cnt = ok ? carry[e] : 0;
+    // the expert's full row tiles and the class of its last one (-1: none past the full ones)
+    const int nfull = cnt / kMT, rem = cnt - nfull * kMT;
+    const int lastc = rem == 0 ? -1 : rem > 3 * kMT / 4 ? 0 : rem > kMT / 2 ? 1 : rem > kMT / 4 ? 2 : 3;
+    int v[5] = {cnt, nfull + (lastc == 0 ? 1 : 0), lastc == 1 ? 1 : 0, lastc == 2 ? 1 : 0, lastc == 3 ? 1 : 0};
+    int tot[5];
+    block_scan<5>(v, tot, ws, min(16, (E + 63) / 64));
     if (ok) {
         counts[e] = cnt;
         offsets[e] = v[0];
-        tile_off[e] = v[1];
-        for (int j = 0; j < ntile; ++j) items[v[1] + j] = make_int4(e, j, v[0], cnt);
     }
-    if (tid == 0) {
-        offsets[E] = tot[0];
-        tile_off[E] = tot[1];
+    if (tid == 0) offsets[E] = tot[0];
+
+    // routed row tiles by class in LDS (the scan's piece buffer is free): class c from 0, cb1,
+    // cb2, cb3, in expert order, each as expert << 20 | tile; the expert's first pair row and
+    // pairs in seg
+    const int cb1 = tot[1], cb2 = cb1 + tot[2], cb3 = cb2 + tot[3];
+    if (ok) {
+        seg[0][e] = v[0];
+        seg[1][e] = cnt;
+        const int n0 = nfull + (lastc == 0 ? 1 : 0);   // class-0 tiles: the full ones and a last one of 97+ rows
+        for (int j = 0; j < n0; ++j)
+            if (v[1] + j < kTileTabMax) piece[v[1] + j] = (e << 20) | j;
+        if (lastc > 0) {
+            const int i = (lastc == 1 ? cb1 : lastc == 2 ? cb2 : cb3) + v[1 + lastc];
+            if (i < kTileTabMax) piece[i] = (e << 20) | nfull;
+        }
+    }
+
+    // The plan of each launch (wave 0: gate/up, wave 1: down; lane x < 8: XCD x). Units of an
+    // XCD's list, in order: its shared items (one item each), then per class in the launch's
+    // order its routed tiles (n items each). Per XCD and class: the first unit, the first item
+    // and the XCD's position in the class's dealing order.
+    if (tid < 128 && (tid & 63) < kXcds) {
+        const int m = tid >> 6, x = tid & 63;
+        const int S = cdiv(la.T, kMT) * la.nts[m];
+        int load = S > x ? (S - 1 - x) / kXcds + 1 : 0, units = load;
+        plan_sh[m][x] = load;
+#pragma unroll
+        for (int o = 0; o < 4; ++o) {
+            const int c = list_class(m, o);
+            const int n = c < 3 ? la.ntr[m] : la.ntn[m];
+            const int mc = c == 0 ? tot[1] : c == 1 ? tot[2] : c == 2 ? tot[3] : tot[4];
+            int pos = 0;   // XCDs holding fewer items (ties: lower XCDs) come first
+#pragma unroll
+            for (int y = 0; y < kXcds; ++y) {
+                const int ly = __builtin_amdgcn_readlane(load, y);
+                pos += (ly < load || (ly == load && y < x)) ? 1 : 0;
+            }
+            const int tiles = mc > pos ? (mc - 1 - pos) / kXcds + 1 : 0;
+            plan_pos[m][o][x] = pos;
+            plan_start[m][o][x] = load;
+            plan_unit[m][o][x] = units;
+            load += tiles * n;
+            units += tiles;
+        }
+        plan_n[m][x] = units;
+        la.list_n[m * kXcds + x] = min(load, la.cap[m]);   // load <= cap (gemm_list_cap)
+    }
+    __syncthreads();
+
+    // The lists (threads [0, 512): gate/up, [512, 1024): down): thread tid takes units u, u + 64,
+    // ... (u = tid % 512 / 8) of XCD tid % 8 and writes their items (item q of XCD x at x cap + q)
+    {
+        const int m = tid >> 9, x = tid & (kXcds - 1);
+        const int cap = la.cap[m], nts = la.nts[m], nsh = plan_sh[m][x], nu = plan_n[m][x];
+        int u0[4], q0[4], p0[4];
+#pragma unroll
+        for (int o = 0; o < 4; ++o) {
+            u0[o] = plan_unit[m][o][x];
+            q0[o] = plan_start[m][o][x];
+            p0[o] = plan_pos[m][o][x];
+        }
+        int4 *list = la.list[m] + (size_t)x * cap;
+        for (int u = (tid & 511) >> 3; u < nu; u += 512 / kXcds) {
+            if (u < nsh) {   // shared item i = 8 u + x: row tile i / nts, output tile i % nts
+                const int i = kXcds * u + x;
+                if (u < cap) list[u] = make_int4((i % nts) << 16, (i / nts) | (kItemShared << 28), 0, la.T);
+                continue;
+            }
+            int o = 0;
+#pragma unroll
+            for (int oo = 1; oo < 4; ++oo)
+                if (u0[oo] <= u) o = oo;
+            const int c = list_class(m, o);
+            const int n = c < 3 ? la.ntr[m] : la.ntn[m];
+            const int k = u - (o == 0 ? u0[0] : o == 1 ? u0[1] : o == 2 ? u0[2] : u0[3]);
+            const int po = o == 0 ? p0[0] : o == 1 ? p0[1] : o == 2 ? p0[2] : p0[3];
+            const int qs = (o == 0 ? q0[0] : o == 1 ? q0[1] : o == 2 ? q0[2] : q0[3]) + k * n;
+            const int r = (c == 0 ? 0 : c == 1 ? cb1 : c == 2 ? cb2 : cb3) + po + kXcds * k;
+            const int tv = piece[min(r, kTileTabMax - 1)];
+            const int ex = min(tv >> 20, E - 1), j = tv & 0xFFFFF;
+            const int kind = c < 3 ? kItemWide : kItemNarrow;
+            const int oe = seg[0][ex], ce = seg[1][ex];
+            for (int nt = 0; nt < n && qs + nt < cap; ++nt)
+                list[qs + nt] = make_int4(ex | (nt << 16), j | (kind << 28), oe, ce);
+        }
     }
 }
 
@@ -622,8 +729,19 @@ hipError_t launch_bucket_rank(const moe_layer *L, int T, const int32_t *idx, hip
 
 hipError_t launch_bucket_scan(const moe_layer *L, int T, hipStream_t s) {
     const int P = T * L->dims.top_k;
-    launch(k_bucket_scan, dim3(1), dim3(1024), 0, s, cdiv(P, kChunk), L->dims.n_experts,
-                       L->ws.chunk_base, L->ws.counts, L->ws.offsets, L->ws.tile_off, kMT, L->ws.items);
+    ListArgs la{};
+    la.T = T;
+    for (int m = 0; m < 2; ++m) {
+        const GemmTiles g = gemm_tiles(L->dims, m);
+        la.nts[m] = g.nts;
+        la.ntr[m] = g.ntr;
+        la.ntn[m] = g.ntn;
+        la.cap[m] = gemm_list_cap(L->dims, T, m);
+        la.list[m] = L->ws.list[m];
+    }
+    la.list_n = L->ws.list_n;
+    launch(k_bucket_scan, dim3(1), dim3(1024), 0, s, cdiv(P, kChunk), L->dims.n_experts, L->ws.chunk_base,
+           L->ws.counts, L->ws.offsets, la);
     return hipGetLastError();
 }
 

@@ -63,6 +63,9 @@ moe_status check_dims(const moe_dims *D) {
         if (P * wmax * 2 >= (1ull << 32) || (uint64_t)D->max_tokens * D->d_shared * 2 >= (1ull << 32))
             return fail(MOE_E_SHAPE, "max_tokens %d too large: activation buffers exceed 4 GiB", D->max_tokens);
     }
+    if (max_routed_tiles(D->max_tokens, D->top_k, D->n_experts) > kTileTabMax)
+        return fail(MOE_E_SHAPE, "max_tokens %d too large: a chunk could hold more than %d routed row tiles "
+                    "(ceil(max_tokens top_k / 128) + min(n_experts, max_tokens top_k))", D->max_tokens, kTileTabMax);
     if (dec_down_lds(*D) > 65536)
         return fail(MOE_E_SHAPE, "top_k * d_expert + d_shared = %d too large for the decode down projection (LDS)",
                     D->top_k * D->d_expert + D->d_shared);
@@ -322,8 +325,9 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.u, w->router_scale ? Tm * d : 0);
     plan.take(&ws.counts, E);
     plan.take(&ws.offsets, E + 1);
-    plan.take(&ws.tile_off, E + 1);
-    plan.take(&ws.items, (size_t)roundup(max_routed_tiles((int)Tm, k, E), 8));   // the GEMM grid rounds to 8
+    plan.take(&ws.list[0], (size_t)kXcds * gemm_list_cap(D, (int)Tm, 0));
+    plan.take(&ws.list[1], (size_t)kXcds * gemm_list_cap(D, (int)Tm, 1));
+    plan.take(&ws.list_n, 2 * kXcds);
     plan.take(&ws.chunk_base, nchunks * E);
     plan.take(&ws.rank, P);
     plan.take(&ws.perm, P);

@@ -36,6 +36,32 @@ __host__ __device__ inline int roundup(int a, int b) { return (a + b - 1) / b * 
 constexpr int cdiv_c(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Work lists of the prefill GEMM launches. A launch has kXcds * cap workgroups; workgroup b runs
+// on XCD b % kXcds and takes item b / kXcds of that XCD's list (the lists are built with the
+// grouping, so each XCD gets about the same work: every shared-expert item is dealt on its own,
+// routed row tiles whole, class by class from the longest). Output tiles per row tile:
+//   shared 128-row tile nts, routed 128-row tile ntr, routed tile of at most 32 rows ntn.
+constexpr int kXcds = 8;
+constexpr int kTileTabMax = 16384;   // routed row tiles per chunk the list builder holds
+struct GemmTiles {
+    int nts, ntr, ntn;
+};
+inline GemmTiles gemm_tiles(const moe_dims &D, int mode) {   // mode 0: gate/up, 1: down
+    if (mode == 0) return GemmTiles{cdiv(D.d_shared / 32, 4), cdiv(D.d_expert / 32, 4), cdiv(D.d_expert / 32, 8)};
+    return GemmTiles{cdiv(D.d_model / 64, 4), cdiv(D.d_model / 64, 4), cdiv(D.d_model / 32, 16)};
+}
+// Items per XCD list for a chunk of T tokens. The shared items are dealt one by one (at most
+// ceil(S / 8) per XCD) and each of the four routed classes by whole tiles (at most
+// ceil(m_c / 8) tiles of n_c items), so a list holds at most worst / 8 + 1 + sum n_c items,
+// worst = S + (routed row tiles) ntr >= every chunk's item count (ntn <= ntr).
+inline int gemm_list_cap(const moe_dims &D, int T, int mode) {
+    const GemmTiles g = gemm_tiles(D, mode);
+    const int worst = cdiv(T, kMT) * g.nts + max_routed_tiles(T, D.top_k, D.n_experts) * g.ntr;
+    return cdiv(worst, kXcds) + 1 + 3 * g.ntr + g.ntn;
+}
+// Kind of a work-list item (bits 28.. of its .y)
+enum { kItemShared = 0, kItemWide = 1, kItemNarrow = 2 };
+
 // Kernel ids for per-kernel timing.
 enum KernelId {
     K_ROUTER = 0,
@@ -64,8 +90,11 @@ struct Workspace {
     uint16_t *u;          // [maxT, d]          router input after the router prologue (bf16), if the layer has one
     int32_t *counts;      // [E]
     int32_t *offsets;     // [E+1]
-    int32_t *tile_off;    // [E+1]              prefix sum of ceil(count/kMT)
-    int4 *items;          // [max routed tiles]  (expert, row tile, first pair row, pairs of the expert)
+    int4 *list[2];        // [kXcds, cap]        GEMM work lists (gate/up, down): item q of XCD x at
+                          //                    x cap + q: (expert | nt << 16, row tile | kind << 28,
+                          //                    first pair row, pairs of the expert); shared: (nt << 16,
+                          //                    row tile, 0, T)
+    int32_t *list_n;      // [2, kXcds]          items in each XCD's list
     int32_t *chunk_base;  // [nchunks, E]
     int32_t *rank;        // [maxT*k]
     int32_t *perm;        // [maxT*k]

@@ -182,6 +182,21 @@ def test_create_rejects_bad_dims_before_device_work(kw, status):
     assert B.moe_last_error()
 
 
+def test_create_rejects_chunks_with_more_routed_tiles_than_the_list_builder_holds():
+    """A chunk of max_tokens tokens may hold ceil(T k / 128) + min(E, T k) routed row tiles; the
+    GEMM work-list builder holds 16384 of them, so a layer whose bound exceeds that is refused
+    (MOE_E_SHAPE) before any device work, while one just inside passes validation."""
+    h = C.c_void_p(0)
+    L = B.lib()
+    big = dict(d_model=64, d_expert=64, d_shared=64, max_tokens=1 << 20)
+    assert L.moe_layer_create(C.byref(_dims(top_k=2, **big)), C.byref(_weights()), 0, C.byref(h)) == B.MOE_E_SHAPE
+    assert "routed row tiles" in B.moe_last_error()
+    # top-1: 8192 + 8 tiles, within the bound; refused only by the tiny workspace budget
+    assert L.moe_layer_create(C.byref(_dims(top_k=1, **big)), C.byref(_weights()), B.MOE_FLAG_WS_BUDGET_MIB(1),
+                              C.byref(h)) == B.MOE_E_NOMEM
+    assert h.value is None
+
+
 def test_create_rejects_null_misaligned_and_flags():
     h = C.c_void_p(0)
     L = B.lib()

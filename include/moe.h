@@ -110,7 +110,11 @@ typedef struct {
     int32_t group;       /* quantization group; must be 64 */
     int32_t router_bits; /* must be 8 */
     int32_t expert_bits; /* must be 4 */
-    int32_t max_tokens;  /* workspace capacity in tokens per call, >= 1 */
+    int32_t max_tokens;  /* workspace capacity in tokens per call, in [1, 2^20], with the fp16
+                            activation buffers (max_tokens top_k max(d, I) and max_tokens I_s
+                            values) below 4 GiB and at most 16384 routed row tiles per chunk
+                            (ceil(max_tokens top_k / 128) + min(E, max_tokens top_k), the
+                            prefill GEMMs' work-list bound); else MOE_E_SHAPE */
     int32_t expert_format; /* MOE_FORMAT_AFFINE_G64 (0) or MOE_FORMAT_Q4_0 (1); other values are
                               MOE_E_QUANT */
 } moe_dims;

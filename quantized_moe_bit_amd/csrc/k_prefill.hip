@@ -537,7 +537,9 @@ __device__ __forceinline__ void pre_gemm_wide(const PreArgs &a, uint8_t *smem, c
             // step's code words and scale/bias words) are issued before the MFMAs of K-step s, so a
             // whole K-step of MFMAs covers their latency; the sched barriers keep the compiler from
             // sinking them next to their use. The dequantization VALU of K-step s + 1 interleaves
-            // with the MFMAs of K-step s.
+            // with the MFMAs of K-step s. K-loop note: the MFMA/dequantization phase of a K-step
+            // runs at wave priority 1 (s_setprio), the LDS reads and ring barrier at 0, so of the two
+            // waves sharing a SIMD (two workgroups per CU) the one with MFMAs ready issues first.
             if (live_w) {
                 const uint8_t *sA = smem + SA * kAStageBytes;
                 u32x4_t af[2][LMS];
@@ -561,6 +563,7 @@ __device__ __forceinline__ void pre_gemm_wide(const PreArgs &a, uint8_t *smem, c
                         load_w(SB1, bw, s2, b2, s2l, b2l);
                     }
                     __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_s_setprio(1);   // MFMA phase first (see the K-loop note)
                     if (s < 3) {
 #pragma unroll
                         for (int t = 0; t < 2; ++t) {
@@ -586,6 +589,7 @@ __device__ __forceinline__ void pre_gemm_wide(const PreArgs &a, uint8_t *smem, c
                             if constexpr (Q4) bl0[t] = dequant_frag(bw[t][0], s2l[t][0], b2l[t][0]);
                         }
                     }
+                    __builtin_amdgcn_s_setprio(0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             } else {
@@ -908,6 +912,7 @@ __device__ __forceinline__ void pre_gemm_narrow(const PreArgs &a, uint8_t *smem,
                         load_w(SB1, bw, s2, b2, s2l, b2l);
                     }
                     __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_s_setprio(1);   // MFMA phase first (see the K-loop note)
                     if (s < 3) {
                         const int hs = (s + 1) >> 1;
 #pragma unroll
@@ -931,6 +936,7 @@ __device__ __forceinline__ void pre_gemm_narrow(const PreArgs &a, uint8_t *smem,
                             if constexpr (Q4) bl0[t] = dequant_frag(bw[t][0], s2l[t][0], b2l[t][0]);
                         }
                     }
+                    __builtin_amdgcn_s_setprio(0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             } else {

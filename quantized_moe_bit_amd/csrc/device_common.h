@@ -84,15 +84,14 @@ __device__ __forceinline__ u32x4_t nib_sub(uint32_t w) {
     return u32x4_t{w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u};
 }
 
-// Eight bf16 values -> eight fp16 values (exact for |v| in fp16's normal range; larger values
-// saturate, smaller ones lose low bits as fp16 subnormals).
+// Eight bf16 values -> eight fp16 values, each rounded to nearest even as f32_to_f16 does (exact
+// for |v| in fp16's normal range; values that round above 65504 become infinite and smaller
+// ones fp16 subnormals, the same conversion the prefill path applies to x).
 __device__ __forceinline__ u32x4_t bf16x8_to_f16x8(u32x4_t v) {
     u32x4_t r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v[i] << 16), __uint_as_float(v[i] & 0xFFFF0000u));
-        r[i] = __builtin_bit_cast(uint32_t, h);
-    }
+    for (int i = 0; i < 4; ++i)
+        r[i] = f32_to_f16(__uint_as_float(v[i] << 16)) | (f32_to_f16(__uint_as_float(v[i] & 0xFFFF0000u)) << 16);
     return r;
 }
 

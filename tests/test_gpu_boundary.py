@@ -205,6 +205,33 @@ def test_values_beyond_fp16_range_make_the_output_nonfinite():
         say(f"{what}: non-finite output, reported under the check-finite flag (decode and prefill)")
 
 
+def test_x_beyond_fp16_range_is_infinite_on_both_paths():
+    """Both paths convert x to fp16 rounding to nearest: with the gate/up weights of x's first
+    input group made tiny (so x clipped to 65504 would still give finite hidden activations), an
+    input of 1e5 in that group makes its token's output non-finite in decode as in prefill, while
+    6e4 (below 65504) keeps every output finite."""
+    D = synth.Dims(d_model=256, n_experts=8, top_k=2, d_expert=128, d_shared=256)
+    lay = synth.gen_layer(D, 16, router="uniform")
+    for name in ("gate", "up", "sh_gate", "sh_up"):
+        m = getattr(lay, name)
+        sc, bi = m.scales.copy(), m.biases.copy()
+        sc[..., 0] = synth.f32_to_bf16_bits(np.full(sc[..., 0].shape, 1e-7, np.float32))
+        bi[..., 0] = synth.f32_to_bf16_bits(np.full(bi[..., 0].shape, -4e-7, np.float32))
+        setattr(lay, name, synth.QMat(m.codes, sc, bi, m.bits, m.out_dim, m.in_dim))
+    x, _, _ = synth.gen_tokens(D, 16, 16)
+    dl = DeviceLayer(lay, 16)
+    for v, finite in ((1.0e5, False), (6.0e4, True)):
+        xx = x.copy()
+        xx[5, 40] = synth.f32_to_bf16_bits(np.array([v], np.float32))[0]
+        xd = tokens_to_device(xx)
+        for path in ("prefill", "decode"):
+            y = (dl.prefill(xd) if path == "prefill" else dl.decode(xd)).cpu().numpy()
+            assert np.all(np.isfinite(np.delete(y, 5, axis=0))), f"x = {v:g} {path}: other tokens"
+            assert bool(np.all(np.isfinite(y[5]))) == finite, f"x = {v:g} {path}"
+    dl.close()
+    say("x = 1e5 (tiny weights on its group): non-finite output in decode and prefill; x = 6e4: finite")
+
+
 def test_profiling_does_not_change_results():
     wd = synth.WORKLOADS["prefill512"]
     lay = synth.workload_layer(wd)

@@ -309,8 +309,9 @@ moe_status moe_stack_glue(const uint16_t *h, const float *y, const uint16_t *pos
  *   x = bf16(h / sqrt(mean(h^2) + 1e-6));  y = layer_l(x);
  *   h = bf16((h + post_l(y)) * scalar_l)
  * with post_l, scalar_l the layer's optional post_ffn_norm and layer_scalar (moe_stack_glue's
- * steps around moe_forward_decode; the residual step before a layer runs inside that layer's
- * router launch when T * d_model <= 16384). x_buf, h_buf (bf16 [T, d]) and y_buf (fp32
+ * steps around moe_forward_decode; when T * d_model <= 16384 the residual step after a layer
+ * without a post-FFN norm runs in that layer's down launch, and after one with it in the next
+ * layer's router launch). x_buf, h_buf (bf16 [T, d]) and y_buf (fp32
  * [T, d]) are caller-owned scratch; on return x_buf holds the norm of the final stream (what
  * a next layer would read) and y_buf the last layer's y. All layers must have the same d_model (MOE_E_SHAPE); every layer handle is used on this
  * stream. MOE_E_INVALID for NULL arguments or n_layers < 1, MOE_E_CAPACITY for T above a

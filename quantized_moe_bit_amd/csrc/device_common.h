@@ -158,10 +158,39 @@ __device__ __forceinline__ double bf16_to_f64(uint32_t bits16) { return (double)
 constexpr int kGlueWG = 256;
 constexpr int kGlueChunks = 4;
 
+// Inclusive fp64 sum within each 16-lane row of the wave (every lane of the row active): lane
+// 15 of the row gets the row's total, added in a fixed tree (DPP row shifts by 1, 2, 4, 8;
+// lanes shifted in from outside the row add 0).
+template <int SH>
+__device__ __forceinline__ double row_shr_f64(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, 0x110 + SH, 0xF, 0xF, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), 0x110 + SH, 0xF, 0xF, true);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double row_scan16_f64(double v) {
+    v += row_shr_f64<1>(v);
+    v += row_shr_f64<2>(v);
+    v += row_shr_f64<4>(v);
+    v += row_shr_f64<8>(v);
+    return v;
+}
+__device__ __forceinline__ double lane_f64(double v, int lane) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// fp64 sum over a full wave in a fixed order (the same value in every lane)
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v = row_scan16_f64(v);
+    return (lane_f64(v, 15) + lane_f64(v, 31)) + (lane_f64(v, 47) + lane_f64(v, 63));
+}
+
 // fixed-order fp64 sum over the workgroup (every thread gets the total; red reusable after)
 __device__ __forceinline__ double glue_block_sum(double v, double *red) {
     const int tid = threadIdx.x;
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    v = wave_sum_f64(v);
     if ((tid & 63) == 0) red[tid >> 6] = v;
     __syncthreads();
     double tot = 0.0;
@@ -302,7 +331,7 @@ __device__ __forceinline__ void prologue_token(uint16_t *xs, const uint16_t *rs,
             ss = fma(f, f, ss);
         }
     }
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    ss = wave_sum_f64(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
     double tot = 0.0;

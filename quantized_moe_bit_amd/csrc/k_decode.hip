@@ -400,6 +400,13 @@ struct DecArgs {
     const float *y_in;
     const uint16_t *post_in, *scalar_in;
     uint16_t *h_out, *x_out;
+    const double *ss_in;    // [T][d/16] router launch with the stream formed by the previous down launch:
+                            // fp64 sums of squares of its 16-row pieces (h_in is that stream)
+    // the next layer's residual step in the down launch: res_out = bf16((res_h + y) * res_scalar)
+    // (res_scalar optional) and the fp64 sums of squares of its 16-row pieces into res_ss
+    const uint16_t *res_h, *res_scalar;
+    uint16_t *res_out;
+    double *res_ss;
     // router prologue fused into the router launch: router_scale (bf16 [d])
     const uint16_t *router_scale;
     // shared-expert gate: g (bf16 [d]) and the per-token gate values (gate/up -> down)
@@ -411,14 +418,45 @@ struct DecArgs {
     int32_t *slot_faults;
 };
 
+// x = bf16(h / sqrt(mean(h^2) + 1e-6)) of one token (one full workgroup), h the stream a down
+// launch formed together with the fp64 sums of squares of its 16-row pieces (ssp, d / 16 of
+// them): the sums are added per thread and then over the workgroup in a fixed order, and
+// inv and x follow glue_token's expressions.
+__device__ __forceinline__ void norm_token(const uint16_t *h, const double *ssp, uint16_t *x_next, int d, double *red) {
+    const int tid = threadIdx.x, nc = d / 8, np = d / 16;
+    u32x4_t hv[kGlueChunks];
+#pragma unroll
+    for (int c = 0; c < kGlueChunks; ++c) {
+        const int i = tid + kGlueWG * c;
+        if (i < nc) hv[c] = ld16(h + 8 * i);
+    }
+    double ss = 0.0;
+    for (int i = tid; i < np; i += kGlueWG) ss += ssp[i];
+    const double inv = 1.0 / sqrt(glue_block_sum(ss, red) / (double)d + 1e-6);
+#pragma unroll
+    for (int c = 0; c < kGlueChunks; ++c) {
+        const int i = tid + kGlueWG * c;
+        if (i < nc) {
+            u32x4_t xo;
+#pragma unroll
+            for (int j2 = 0; j2 < 4; ++j2)
+                xo[j2] = f64_to_bf16(bf16_to_f64(hv[c][j2] & 0xFFFFu) * inv) |
+                         (f64_to_bf16(bf16_to_f64(hv[c][j2] >> 16) * inv) << 16);
+            *reinterpret_cast<u32x4_t *>(x_next + 8 * i) = xo;
+        }
+    }
+}
+
 // ----------------------------------------------------------------------------- launch A
 // grid: ceil(E / kRW); block 64 * kRW; LDS kRW * T * (d/64) floats, plus (GLUE or PRO) T * d
-// bf16 and 4 doubles. With GLUE every workgroup first forms x = norm(bf16(h_in + y_in)) for its
+// bf16 and 4 doubles. With GLUE == 2 every workgroup forms x = norm(h_in) from the stream the
+// previous layer's down launch formed, with that launch's sums of squares (ss_in; workgroup 0
+// stores x_out). With GLUE == 1 every workgroup first forms x = norm(bf16(h_in + y_in)) for its
 // own use (the same fp64 residual step as the stack glue kernel; workgroup 0 also stores h_out
 // and x_out for the later launches), so the stack needs no separate residual launch. With PRO
 // every workgroup applies the router prologue to its copy of x (workgroup 0 first stores the
 // group sums of x itself for the gate/up launch), so the router reads the prologue's output.
-template <bool GLUE, bool PRO>
+template <int GLUE, bool PRO>
 __global__ __launch_bounds__(64 * kRW) void k_dec_router(DecArgs a) {
     static_assert(64 * kRW == kGlueWG, "the residual step runs on one full workgroup");
     extern __shared__ __align__(16) unsigned char smem[];
@@ -429,13 +467,20 @@ __global__ __launch_bounds__(64 * kRW) void k_dec_router(DecArgs a) {
     const int e = blockIdx.x * kRW + wave;
     // with the residual step in front, the codes of the wave's first group are requested
     // before it, so their latency overlaps the step's own loads
-    constexpr bool LDSX = GLUE || PRO;   // x (then u) kept in LDS
+    constexpr bool LDSX = GLUE != 0 || PRO;   // x (then u) kept in LDS
     RouterCodes pre;
     if (LDSX && e < a.E) pre = router_codes(a.rq, a.rsb, a.d, e, min(lane, G - 1));
     if (LDSX) {
         uint16_t *xs = reinterpret_cast<uint16_t *>(smem + sizeof(float) * kRW * a.T * G);
         double *red = reinterpret_cast<double *>(xs + (size_t)a.T * a.d);
-        if (GLUE) {
+        if (GLUE == 2) {
+            for (int t = 0; t < a.T; ++t)
+                norm_token(a.h_in + (size_t)t * a.d, a.ss_in + (size_t)t * (a.d / 16), xs + (size_t)t * a.d, a.d, red);
+            __syncthreads();
+            if (blockIdx.x == 0)
+                for (int i = tid; i < a.T * a.d / 8; i += 64 * kRW)
+                    *reinterpret_cast<u32x4_t *>(a.x_out + 8 * i) = *reinterpret_cast<const u32x4_t *>(xs + 8 * i);
+        } else if (GLUE == 1) {
             for (int t = 0; t < a.T; ++t)
                 glue_token(a.h_in + (size_t)t * a.d, a.y_in ? a.y_in + (size_t)t * a.d : nullptr, a.post_in,
                            a.scalar_in, blockIdx.x == 0 ? a.h_out + (size_t)t * a.d : nullptr, xs + (size_t)t * a.d, a.d, red);
@@ -625,6 +670,7 @@ __global__ __launch_bounds__(MAXT) void k_dec_down(DecArgs a) {
     const float qs0 = qs[0], qs1 = qs[1], qs2 = qs[2], qs3 = qs[3];
     const float wv = a.wts[(size_t)t * a.k + min(tid, a.k - 1)];
     const float sgv = a.shared_gate ? a.sgate[t] : 1.0f;
+    const uint32_t hres = (a.res_out && tid < 16) ? a.res_h[(size_t)t * a.d + 16 * db + tid] : 0u;
     Down16<kMPC, Q4> dr(static_cast<const uint8_t *>(a.down.codes) + (size_t)e * a.d * a.I / 2,
                     a.down.sb + (size_t)e * a.d * GI, db >> 1, db & 1, GI, 0, 1);
     Down16<kMPC, Q4> ds(static_cast<const uint8_t *>(a.sh_down.codes), a.sh_down.sb, db >> 1, db & 1, GS, sw, SN);
@@ -690,6 +736,14 @@ __global__ __launch_bounds__(MAXT) void k_dec_down(DecArgs a) {
         out *= sgv;   // gated shared expert (1 without a gate)
         for (int s = 0; s < a.k; ++s) out = fmaf(Ws[s], part_r[s * 16 + tid], out);
         a.y[(size_t)t * a.d + 16 * db + tid] = out;
+        if (a.res_out) {   // the next layer's residual step (glue_token's expression, no post-FFN norm)
+            const double sc = a.res_scalar ? bf16_to_f64(*a.res_scalar) : 1.0;
+            const uint32_t hb = f64_to_bf16((bf16_to_f64(hres) + (double)out) * sc);
+            a.res_out[(size_t)t * a.d + 16 * db + tid] = (uint16_t)hb;
+            const double r = bf16_to_f64(hb);
+            const double ss = row_scan16_f64(r * r);   // lanes 0-15: row 0 of wave 0
+            if (tid == 15) a.res_ss[(size_t)t * (a.d / 16) + db] = ss;
+        }
     }
 }
 
@@ -765,7 +819,7 @@ hipError_t launch_dec_router(const moe_layer *L, const uint16_t *x, int T, float
     a.logits = logits;
     if (!write_aux) a.xg = nullptr;   // the group sums of x come from the router prologue
     const size_t lds = sizeof(float) * kRW * T * (D.d_model / 64);
-    launch(k_dec_router<false, false>, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
+    launch(k_dec_router<0, false>, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
     return hipGetLastError();
 }
 
@@ -776,7 +830,7 @@ hipError_t launch_dec_router_pro(const moe_layer *L, const uint16_t *x, int T, f
     a.router_scale = L->w.router_scale;
     const size_t lds = sizeof(float) * kRW * T * (D.d_model / 64) + sizeof(uint16_t) * T * D.d_model +
                        sizeof(double) * (kGlueWG / 64);
-    launch(k_dec_router<false, true>, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
+    launch(k_dec_router<0, true>, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
     return hipGetLastError();
 }
 
@@ -797,9 +851,26 @@ hipError_t launch_dec_router_glue(const moe_layer *L, const uint16_t *h_in, cons
                        sizeof(double) * (kGlueWG / 64);
     a.router_scale = L->w.router_scale;
     if (a.router_scale)
-        launch(k_dec_router<true, true>, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
+        launch(k_dec_router<1, true>, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
     else
-        launch(k_dec_router<true, false>, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
+        launch(k_dec_router<1, false>, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dec_router_norm(const moe_layer *L, const uint16_t *h_in, const double *ss_in, uint16_t *x_out,
+                                  int T, hipStream_t s) {
+    const moe_dims &D = L->dims;
+    DecArgs a = dec_args(L, x_out, T, nullptr);
+    a.h_in = h_in;
+    a.ss_in = ss_in;
+    a.x_out = x_out;
+    const size_t lds = sizeof(float) * kRW * T * (D.d_model / 64) + sizeof(uint16_t) * T * D.d_model +
+                       sizeof(double) * (kGlueWG / 64);
+    a.router_scale = L->w.router_scale;
+    if (a.router_scale)
+        launch(k_dec_router<2, true>, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
+    else
+        launch(k_dec_router<2, false>, dim3(cdiv(D.n_experts, kRW)), dim3(64 * kRW), lds, s, a);
     return hipGetLastError();
 }
 
@@ -820,9 +891,16 @@ hipError_t launch_dec_gateup(const moe_layer *L, const uint16_t *x, int T, hipSt
     return hipGetLastError();
 }
 
-hipError_t launch_dec_down(const moe_layer *L, int T, float *y, hipStream_t s) {
+hipError_t launch_dec_down(const moe_layer *L, int T, float *y, hipStream_t s, const uint16_t *res_h,
+                           uint16_t *res_out) {
     const moe_dims &D = L->dims;
-    const DecArgs a = dec_args(L, nullptr, T, y);
+    DecArgs a = dec_args(L, nullptr, T, y);
+    if (res_out) {
+        a.res_h = res_h;
+        a.res_out = res_out;
+        a.res_scalar = L->w.layer_scalar;
+        a.res_ss = L->ws.dss;
+    }
     const int nw = dec_down_waves(D);
     const dim3 grid(T * (D.d_model / 16)), block(64 * nw);
     if (a.q4_0) {

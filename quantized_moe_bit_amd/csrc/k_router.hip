@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void k_router_prologue(const uint16_t *__restr
             }
         }
     }
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    ss = wave_sum_f64(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
     const double tot = (red[0] + red[1]) + (red[2] + red[3]);

@@ -346,6 +346,7 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.dh_s, 2 * dec_workspace_floats(D, L->max_dec, 2));
     plan.take(&ws.dhs_r, dec_workspace_floats(D, L->max_dec, 3));
     plan.take(&ws.dhs_s, dec_workspace_floats(D, L->max_dec, 4));
+    plan.take(&ws.dss, (size_t)L->max_dec * (d / 16));
     L->ws_bytes = (plan.off + 255) & ~size_t(255);
     const uint64_t budget_mib = flags >> 8;
     if (budget_mib && L->ws_bytes > (budget_mib << 20)) {
@@ -542,8 +543,13 @@ moe_status moe_stack_forward_decode(moe_layer *const *layers, int32_t n_layers, 
         moe_status st = check_finite(check, h, (size_t)T * d, false, s, "moe_stack_forward_decode");
         if (st != MOE_OK) return st;
     }
-    // the residual stream alternates between h and h_buf: layer l reads the stream before it
-    // from one and leaves the stream after the previous layer's residual add in the other
+    // The residual stream alternates between h and h_buf: layer l's stream (after the previous
+    // layer's residual add) goes to dst_l = (l odd ? h : h_buf). The residual step before layer
+    // l >= 1 runs either inside layer l's router launch (with layer l-1's post-FFN norm, from
+    // dst_{l-1} and y) or, for a layer l-1 without one, already in layer l-1's down launch, which
+    // writes dst_l and the sums of squares that layer l's router then reads.
+    const bool fused = dec_router_glue_fits(layers[0]->dims, T);
+    bool formed = false;   // dst_l was formed by the previous down launch
     for (int l = 0; l < n_layers; ++l) {
         moe_layer *L = layers[l];
         L->routed_T = -1;
@@ -553,7 +559,9 @@ moe_status moe_stack_forward_decode(moe_layer *const *layers, int32_t n_layers, 
         // the previous layer's tail goes with its output y into this layer's residual step
         const uint16_t *post = l ? layers[l - 1]->w.post_ffn_norm : nullptr;
         const uint16_t *scalar = l ? layers[l - 1]->w.layer_scalar : nullptr;
-        if (dec_router_glue_fits(L->dims, T)) {
+        if (formed) {
+            RUN(K_DEC_ROUTER, launch_dec_router_norm(L, dst, layers[l - 1]->ws.dss, x_buf, T, s));
+        } else if (fused) {
             RUN(K_DEC_ROUTER, launch_dec_router_glue(L, src, yp, post, scalar, dst, x_buf, T, s));
         } else {
             RUN(K_GLUE, launch_glue(src, yp, post, scalar, dst, x_buf, T, d, s));
@@ -563,10 +571,17 @@ moe_status moe_stack_forward_decode(moe_layer *const *layers, int32_t n_layers, 
             RUN(K_DEC_ROUTER, launch_dec_router(L, u, T, L->ws.logits, s, u == x_buf));
         }
         RUN(K_DEC_GATEUP, launch_dec_gateup(L, x_buf, T, s));
-        RUN(K_DEC_DOWN, launch_dec_down(L, T, y_buf, s));
+        // this layer's residual step in its down launch when it has no post-FFN norm and the
+        // next step takes a formed stream (the next router holds x in LDS, or the final step)
+        const bool last = l == n_layers - 1;
+        formed = fused && !L->w.post_ffn_norm;
+        uint16_t *next = last ? h : (((l + 1) & 1) ? h : h_buf);
+        RUN(K_DEC_DOWN, launch_dec_down(L, T, y_buf, s, formed ? dst : nullptr, formed ? next : nullptr));
     }
-    {   // the last layer's residual add, into h
-        moe_layer *L = layers[n_layers - 1];
+    moe_layer *L = layers[n_layers - 1];
+    if (formed) {   // the final stream is in h already: x_buf = its norm
+        RUN(K_GLUE, launch_glue(h, nullptr, nullptr, nullptr, h, x_buf, T, d, s));
+    } else {   // the last layer's residual add, into h
         uint16_t *src = ((n_layers - 1) & 1) ? h : h_buf;
         RUN(K_GLUE, launch_glue(src, y_buf, L->w.post_ffn_norm, L->w.layer_scalar, h, x_buf, T, d, s));
     }

@@ -115,6 +115,8 @@ struct Workspace {
     uint16_t *dh_s;       // [D, I_s]           decode: shared hidden activations, fp16 bits
     float *dhs_r;         // [D*k, I/16]        decode: sums of 16 consecutive routed h values
     float *dhs_s;         // [D, I_s/16]        decode: sums of 16 consecutive shared h values
+    double *dss;          // [D, d/16]          decode stack: fp64 sums of squares of 16-row pieces of the
+                          //                    stream this layer's down launch formed
 };
 
 struct ProfEvent {
@@ -191,7 +193,15 @@ hipError_t launch_bucket_rank(const moe_layer *L, int T, const int32_t *idx, hip
 hipError_t launch_bucket_scan(const moe_layer *L, int T, hipStream_t s);
 hipError_t launch_bucket_scatter(const moe_layer *L, int T, const int32_t *idx, int32_t *perm, hipStream_t s);
 hipError_t launch_dec_gateup(const moe_layer *L, const uint16_t *x, int T, hipStream_t s);
-hipError_t launch_dec_down(const moe_layer *L, int T, float *y, hipStream_t s);
+// res_out: also the next layer's residual step of a stack, res_out = bf16((res_h + y) * layer_scalar)
+// (a layer without a post-FFN norm), and the fp64 sums of squares of its 16-row pieces into ws.dss
+hipError_t launch_dec_down(const moe_layer *L, int T, float *y, hipStream_t s, const uint16_t *res_h = nullptr,
+                           uint16_t *res_out = nullptr);
+// decode router whose input is x = norm(h_in), h_in formed by the previous layer's down launch
+// with its sums of squares ss_in (that layer's ws.dss); workgroup 0 stores x_out. Needs
+// dec_router_glue_fits.
+hipError_t launch_dec_router_norm(const moe_layer *L, const uint16_t *h_in, const double *ss_in, uint16_t *x_out,
+                                  int T, hipStream_t s);
 size_t dec_gateup_lds(const moe_dims &D);
 size_t dec_down_lds(const moe_dims &D);
 size_t dec_workspace_floats(const moe_dims &D, int max_dec, int which);

@@ -158,6 +158,26 @@ __device__ __forceinline__ double bf16_to_f64(uint32_t bits16) { return (double)
 constexpr int kGlueWG = 256;
 constexpr int kGlueChunks = 4;
 
+// Largest float of the wave: DPP within rows of 16 (swap pairs, swap halves of quads,
+// half-row mirror, row mirror), then the four row results through scalar registers.
+template <int CTRL>
+__device__ __forceinline__ float max_dpp(float x) {
+    const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+    return fmaxf(x, y);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+    x = max_dpp<0xB1>(x);    // quad_perm [1,0,3,2]
+    x = max_dpp<0x4E>(x);    // quad_perm [2,3,0,1]
+    x = max_dpp<0x141>(x);   // row_half_mirror
+    x = max_dpp<0x140>(x);   // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // Inclusive fp64 sum within each 16-lane row of the wave (every lane of the row active): lane
 // 15 of the row gets the row's total, added in a fixed tree (DPP row shifts by 1, 2, 4, 8;
 // lanes shifted in from outside the row add 0).

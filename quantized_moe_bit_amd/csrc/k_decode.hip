@@ -119,26 +119,6 @@ __device__ __forceinline__ void router_wave(const uint16_t *__restrict__ x, int 
 }
 
 // ----------------------------------------------------------------------------- top-k
-// Largest float of the wave: DPP within rows of 16 (swap pairs, swap halves of quads,
-// half-row mirror, row mirror), then the four row results through scalar registers.
-template <int CTRL>
-__device__ __forceinline__ float max_dpp(float x) {
-    const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
-    return fmaxf(x, y);
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-    x = max_dpp<0xB1>(x);    // quad_perm [1,0,3,2]
-    x = max_dpp<0x4E>(x);    // quad_perm [2,3,0,1]
-    x = max_dpp<0x141>(x);   // row_half_mirror
-    x = max_dpp<0x140>(x);   // row_mirror
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
-    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-}
-
 // Slot `slot` of a token's top-k, derived by one wave from its logits row (identical on
 // every lane and every wave): each round takes the largest remaining logit, ties to the
 // lowest expert index (the lowest lane of the lowest 64-expert block holding the maximum).

@@ -348,11 +348,10 @@ __global__ __launch_bounds__(256) void k_router_table(const uint8_t *__restrict_
 }
 
 // (value desc, index asc) ordering
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
-}
-
-// grid: ceil(T / 4); block 256 -- one wave per token; kPer logits per lane (E <= 64 kPer)
+// grid: ceil(T / 4); block 256 -- one wave per token; kPer logits per lane (E <= 64 kPer).
+// Round s takes the largest remaining logit (wave_max over DPP), ties to the lowest expert
+// (the lowest set bit of a ballot); if every remaining logit is NaN, the lowest remaining
+// expert, so the index stays valid.
 template <int kPer>
 __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, int T, int E, int k,
                                               const uint16_t *__restrict__ pes, int32_t *__restrict__ idx,
@@ -362,42 +361,47 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
     if (t >= T) return;
     const float *l = logits + (size_t)t * E;
     float v[kPer];
-    const int nper = (E + 63) / 64;
+    bool live[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int e = lane + 64 * i;
-        v[i] = (i < nper && e < E) ? l[e] : -__builtin_inff();
+        live[i] = e < E;
+        v[i] = live[i] ? l[e] : -__builtin_inff();
     }
-    uint32_t taken = 0;   // bit i: element lane + 64 i already selected
     float my_v = 0.0f, m = 0.0f, z = 0.0f;   // lane s keeps slot s
     int my_i = 0;
     for (int s = 0; s < k; ++s) {
-        float bv = -__builtin_inff();
-        int bi = 0x7FFFFFFF;
+        float lb = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            if (live[i]) lb = fmaxf(lb, v[i]);
+        const float mx = wave_max(lb);
+        int e = -1;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-            const int e = lane + 64 * i;
-            // an unset best (bi == INT_MAX) takes any candidate, so the index stays valid even for NaN
-            if (i < nper && e < E && !((taken >> i) & 1u) && (bi == 0x7FFFFFFF || better(v[i], e, bv, bi))) {
-                bv = v[i];
-                bi = e;
-            }
+            const uint64_t bal = __ballot(live[i] && v[i] == mx);
+            if (e < 0 && bal) e = 64 * i + __ffsll((long long)bal) - 1;
         }
+        if (e < 0) {   // only NaN left
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            if (oi != 0x7FFFFFFF && (bi == 0x7FFFFFFF || better(ov, oi, bv, bi))) {
-                bv = ov;
-                bi = oi;
+            for (int i = 0; i < kPer; ++i) {
+                const uint64_t bal = __ballot(live[i]);
+                if (e < 0 && bal) e = 64 * i + __ffsll((long long)bal) - 1;
             }
         }
-        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-        if (s == 0) m = bv;
-        z += __expf(bv - m);
+        e = max(e, 0);
+        float val = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            if ((e >> 6) == i) {
+                val = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), e & 63));
+                if (lane == (e & 63)) live[i] = false;
+            }
+        if (s == 0) m = val;
+        z += __expf(val - m);
         if (lane == s) {
-            my_v = bv;
-            my_i = bi;
+            my_v = val;
+            my_i = e;
         }
     }
     if (lane < k) {

@@ -37,6 +37,10 @@
 //   (down projection of that slot's h) and a few waves for the shared down projection, then
 //   y = shared + w_0 r_0 + ... + w_{k-1} r_{k-1} in slot order (Mference "Decode", cb2;
 //   TinyTitan architecture "Invariants": fixed reduction order).
+// In a layer stack the residual step between layers (Mference "Decode", cb2) runs in launch A
+// of the next layer (from h and y), or, after a layer without a post-FFN norm, already in
+// launch C: each workgroup forms its 16 rows of the next stream, bf16((h + y) * scalar), and
+// their fp64 sum of squares, and the next layer's launch A normalizes that stream.
 #include "device_common.h"
 #include "moe_internal.h"
 

@@ -10,10 +10,11 @@
 //   A_g = fma chain of x_j * w_j, ascending j         (fp32, starting from 0)
 //   logit = (A_0 + A_1 + ... + A_{G-1}) [+ logit_bias]   (fp32 adds, ascending g)
 // Contraction is disabled in this file so the compiler cannot fuse or reorder these.
-// Two kernels compute it: k_router_tok (one token per lane, all groups in one wave) for
-// large chunks, and k_router_ksplit (the groups of a token spread over eight waves, each
-// A_g kept in LDS and folded in ascending g by one wave) for chunks too small to fill the
-// chip that way; both give the same bits.
+// Two kernels compute it: k_router_ksplit (lane = token, the groups of a token spread over
+// eight waves, fma chains with row-broadcast weights, each A_g kept in LDS and folded in
+// ascending g by one wave) for chunks up to about a thousand tokens, and k_router_mfma (the
+// chains on the matrix cores, whose fp32 multiply-add is an ordered fma) for larger ones;
+// both give the same bits.
 //
 // Top-k: the k largest logits, largest first, equal values ordered by lower expert
 // index (TinyTitan architecture, "Invariants": top-k index sets must match exactly),
@@ -31,7 +32,7 @@ namespace qmoe {
 namespace {
 
 constexpr int kRNE = 4;                  // experts per wave of the prefill router
-constexpr long kRouterKsplitMaxWG = 1280;   // see router_ksplit
+constexpr long kRouterKsplitMaxWG = 512;    // see router_ksplit
 constexpr int kRBlk = 64 * kRNE;   // router table floats per (expert block, group)
 
 // Router prologue (Mference system design, "Decode", router listing): the router reads
@@ -97,22 +98,9 @@ __global__ __launch_bounds__(256) void k_router_prologue(const uint16_t *__restr
     }
 }
 
-// Prefill router: lane = token, wave = kRNE = 4 consecutive experts, workgroup = 4 waves (64
-// tokens x 16 experts). Per 64-input group the workgroup stages its tokens' inputs into LDS as
-// fp32, converted once for all waves and double-buffered (the next group's loads are in
-// flight during this group's chains); the workgroups of the first expert block also store
-// the fp16 copy of x the prefill gate/up GEMM reads (exact for |x| in fp16's normal range).
-// The weights come dequantized to fp32 from a table built at layer creation: one 16-byte load
-// per lane and 16-input chunk puts input j of the chunk for the wave's four experts into lane
-// j of every 16-lane row, and each fma takes its weight from there by a row broadcast (DPP
-// row_newbcast), so no instruction is spent on moving weights. Per (token, expert) the
-// arithmetic is the fixed order stated at the top of this file.
-//
-// Table layout, per block of kRNE experts eb and group g (kRBlk floats): weights
-// [4 jc][16 j][kRNE] (input 16 jc + j of expert kRNE eb + i at [jc][j][i]). Experts past E are
-// zero.
-// grid: (ceil(T / 64), ceil(E / (4 kRNE))); block 256
-constexpr int kXPitch = 68;   // fp32 per staged token row: 16 lanes of one ds_read_b128 pass hit 64 distinct banks
+// Router weight table (built at layer creation, k_router_table): the weights dequantized to
+// fp32, per block of kRNE experts eb and group g kRBlk floats [4 jc][16 j][kRNE] (input
+// 16 jc + j of expert kRNE eb + i at [jc][j][i]); experts past E are zero.
 static_assert(kRNE == 4, "one 16-byte load per lane holds the four experts' codes of an input");
 
 // a += x * (lane J of q's 16-lane row), one instruction (the DPP source is a loaded register,
@@ -128,105 +116,18 @@ __device__ __forceinline__ void chunk_fmas(float (&A)[kRNE], const f32x4_t (&xv)
     if constexpr (J + 1 < 16) chunk_fmas<J + 1>(A, xv, q);
 }
 
-__global__ __launch_bounds__(256) void k_router_tok(const uint16_t *__restrict__ x, int T, int d, int E,
-                                                    const float *__restrict__ tab, const float *__restrict__ logit_bias,
-                                                    float *__restrict__ logits, uint16_t *__restrict__ x16) {
-    __shared__ __align__(16) float xs[2][64][kXPitch];
-    const int G = d / 64;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int eb = min(blockIdx.y * 4 + wave, cdiv(E, kRNE) - 1);   // waves past E compute a valid block, store nothing
-    const int e0 = (blockIdx.y * 4 + wave) * kRNE;
-    const int t = blockIdx.x * 64 + lane;
-    // staging: thread -> token tid/4, inputs 16 (tid%4) .. +15 of the group
-    const int st = tid >> 2, sq = tid & 3;
-    const int stok = min((int)blockIdx.x * 64 + st, T - 1);
-    const bool st_x16 = x16 && blockIdx.y == 0 && (int)blockIdx.x * 64 + st < T;   // this thread stores x16
-    const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(x + (size_t)stok * d + 16 * sq);
-    u32x4_t *xo = reinterpret_cast<u32x4_t *>(x16 ? x16 + (size_t)stok * d + 16 * sq : nullptr);
-    const float *blk = tab + (size_t)eb * G * kRBlk;
-    auto stage = [&](int buf, int g, const u32x4_t (&v)[2]) {
-        if (st_x16) {
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                u32x4_t h;
-#pragma unroll
-                for (int w = 0; w < 4; ++w)
-                    h[w] = f32_to_f16(bf16_to_f32(v[c][w] & 0xFFFFu)) | (f32_to_f16(bf16_to_f32(v[c][w] >> 16)) << 16);
-                xo[8 * g + c] = h;
-            }
-        }
-        f32x4_t f[4];
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                f[2 * c + (w >> 1)][2 * (w & 1)] = bf16_to_f32(v[c][w] & 0xFFFFu);
-                f[2 * c + (w >> 1)][2 * (w & 1) + 1] = __uint_as_float(v[c][w] & 0xFFFF0000u);
-            }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4_t *>(&xs[buf][st][16 * sq + 4 * i]) = f[i];
-    };
-    auto load_q = [&](int g, f32x4_t (&q)[4]) {
-#pragma unroll
-        for (int jc = 0; jc < 4; ++jc)
-            q[jc] = *reinterpret_cast<const f32x4_t *>(blk + (size_t)g * kRBlk + (16 * jc + (lane & 15)) * kRNE);
-    };
-    float L[kRNE];
-#pragma unroll
-    for (int i = 0; i < kRNE; ++i) L[i] = 0.0f;
-    u32x4_t nv[2] = {xr[0], xr[1]};
-    f32x4_t qa[4], qb[4];   // codes of the even and odd groups (loaded straight into place)
-    load_q(0, qa);
-    stage(0, 0, nv);
-    __syncthreads();
-    auto group = [&](int g, const f32x4_t (&q)[4], f32x4_t (&qnext)[4]) {
-        const int buf = g & 1;
-        {   // next group's loads in flight during this group's chains (the last group re-reads itself)
-            const int gn = g + 1 < G ? g + 1 : g;
-            nv[0] = xr[8 * gn];
-            nv[1] = xr[8 * gn + 1];
-            load_q(gn, qnext);
-        }
-        float A[kRNE];
-#pragma unroll
-        for (int i = 0; i < kRNE; ++i) A[i] = 0.0f;
-#pragma unroll
-        for (int jc = 0; jc < 4; ++jc) {
-            f32x4_t xv[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) xv[c] = *reinterpret_cast<const f32x4_t *>(&xs[buf][lane][16 * jc + 4 * c]);
-            chunk_fmas<0>(A, xv, q[jc]);
-        }
-#pragma unroll
-        for (int i = 0; i < kRNE; ++i) L[i] = L[i] + A[i];
-        // the other buffer was last read in group g - 1, which every wave has finished
-        if (g + 1 < G) stage(buf ^ 1, g + 1, nv);
-        __syncthreads();
-    };
-    for (int g = 0; g < G; g += 2) {
-        group(g, qa, qb);
-        if (g + 1 < G) group(g + 1, qb, qa);
-    }
-    if (t >= T) return;
-#pragma unroll
-    for (int i = 0; i < kRNE; ++i) {
-        const int e = e0 + i;
-        if (e < E) logits[(size_t)t * E + e] = logit_bias ? L[i] + logit_bias[e] : L[i];
-    }
-}
-
 // Prefill router with the groups split across the waves of a workgroup: lane = token, the
 // workgroup = 64 tokens x kRNE experts, wave w computes the group sums A_g of groups
-// [w gw, (w + 1) gw) (gw = ceil(G / kKW)) with the same chains as k_router_tok and stores them
-// in LDS; after one barrier, wave i < kRNE folds expert i's sums in group order,
-// L = ((0 + A_0) + A_1) + ... + A_{G-1}, so the logits are bit-identical to k_router_tok's.
+// [w gw, (w + 1) gw) (gw = ceil(G / kKW)) as fma chains, each weight taken from lane j of a
+// 16-lane row by a row broadcast (DPP row_newbcast, no instruction spent on moving weights),
+// and stores them in LDS; after one barrier, wave i < kRNE folds expert i's sums in group
+// order, L = ((0 + A_0) + A_1) + ... + A_{G-1}.
 // A wave brings its groups' inputs in with coalesced loads (eight lanes per token row) into a
 // staging tile of its own in LDS and reads them back one token row per lane, so it waits on no
-// other wave until the fold. A workgroup carries a quarter of k_router_tok's experts and an
-// eighth of each wave's chain, which fills the chip when the chunk has few tokens (512 tokens:
-// 256 workgroups of 8 waves against 64 of 4). LDS: G x kRNE x 64 fp32 of group sums (d <= 4096)
-// and 8 staging tiles of 64 x 64 bf16.
+// other wave until the fold. A workgroup carries 64 tokens x 4 experts and an eighth of each
+// chain, which fills the chip when the chunk has few tokens (512 tokens: 256 workgroups of 8
+// waves; the matrix-core router has 64 of 4 there). LDS: G x kRNE x 64 fp32 of group sums
+// (d <= 4096) and 8 staging tiles of 64 x 64 bf16.
 // grid: (ceil(T / 64), ceil(E / kRNE)); block 64 kKW
 constexpr int kKW = 8;
 constexpr int kKSplitMaxG = 64;
@@ -326,7 +227,163 @@ __global__ __launch_bounds__(64 * kKW) void k_router_ksplit(const uint16_t *__re
     logits[(size_t)t * E + e] = logit_bias ? L + logit_bias[e] : L;
 }
 
-// The router table k_router_tok reads (weights fma(scale, q, bias) in fp32; layout above).
+// Prefill router on the matrix cores. v_mfma_f32_16x16x4_f32 performs its four fp32
+// multiply-adds in k order, each rounded once like an fma (checked on the device against
+// sequential fmaf over normal, subnormal and mixed operands), so 16 of them over one group's
+// 64 inputs (step s takes inputs 4 s .. 4 s + 3 as its k = 0..3) form exactly the chain
+// A_g = fma(x_63, w_63, ... fma(x_0, w_0, 0)) of the fixed order, for 16 tokens x 16 experts at
+// once; the group sums are then added in group order in registers, L = ((0 + A_0) + A_1) + ...
+// Workgroup: 64 tokens (wave w: tokens 16 w .. 16 w + 15) x 16 experts. The K loop takes kMG
+// groups per step: their x rows (bf16) and the 16 experts' weights (fp32, from the router
+// table's four 4-expert blocks) are staged in LDS transposed, so that the 16 operands one lane
+// needs for a group's chain (input 4 s + k for s = 0..15) are contiguous and come in with two
+// (x) and four (weights) 16-byte reads; the loads of the step after next run in registers
+// meanwhile (two register buffers). The chains of two groups run interleaved, one accumulator
+// each, and fold into L in group order. The expert block 0 also writes the fp16 copy of x.
+// Operand layout: lane l holds A[row l % 16][k l / 16] and B[k l / 16][column l % 16]; result
+// element v of lane l is row 4 (l / 16) + v, column l % 16.
+// LDS: x as [wave][row r][4 q + k][16 s] bf16 with rows 528 B apart, weights as
+// [4 q + k][expert r][16 s] fp32 with experts 80 B apart: the eight lanes of one 16-byte read
+// pass hit eight distinct 16-byte bank groups.
+// grid: (ceil(T / 64), ceil(E / 16)); block 256
+constexpr int kMG = 4;                         // groups per K step
+constexpr int kMXR = 4 * kMG * 16 + 8;         // bf16 per staged x row (528 B)
+constexpr int kMWE = 20;                       // fp32 per staged expert (80 B)
+__global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict__ x, int T, int d, int E,
+                                                     const float *__restrict__ tab, const float *__restrict__ logit_bias,
+                                                     float *__restrict__ logits, uint16_t *__restrict__ x16) {
+    __shared__ __align__(16) uint16_t xs[4][16][kMXR];
+    __shared__ __align__(16) float wsm[4 * kMG][16][kMWE];
+    const int G = d / 64, NB = cdiv(E, kRNE), NS = cdiv(G, kMG);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int t0 = blockIdx.x * 64, eb = blockIdx.y;
+    // x staging: lane l loads row l / 4 of its wave, 16 inputs of each group at 16 (l % 4)
+    const int xr = lane >> 2, xc = (lane & 3) * 16;
+    const int tx = t0 + 16 * wave + xr;
+    const bool tvalid = tx < T;
+    const uint16_t *xrow = x + (size_t)min(tx, T - 1) * d + xc;
+    // weight staging: thread tid loads experts 4 eq .. 4 eq + 3 of input 16 jc + jj of each group
+    const int eq = tid >> 6, jin = tid & 63;
+    const int wblk = kRNE * eb + eq;
+    const float *wsrc = tab + (size_t)min(wblk, NB - 1) * G * kRBlk + 4 * jin;
+    struct Buf {
+        u32x4_t xv[kMG][2];
+        f32x4_t wv[kMG];
+    };
+    Buf b0, b1;
+    auto load = [&](Buf &b, int st) {
+#pragma unroll
+        for (int q = 0; q < kMG; ++q) {
+            const int g = min(kMG * st + q, G - 1);
+            b.xv[q][0] = ld16(xrow + 64 * g);
+            b.xv[q][1] = ld16(xrow + 64 * g + 8);
+            b.wv[q] = *reinterpret_cast<const f32x4_t *>(wsrc + (size_t)g * kRBlk);
+        }
+    };
+    auto stage = [&](const Buf &b, int st) {
+#pragma unroll
+        for (int q = 0; q < kMG; ++q) {
+            // x: input xc + i of the group -> [4 q + (i % 4)][xc / 4 + i / 4]
+            const uint32_t *w32 = reinterpret_cast<const uint32_t *>(&b.xv[q][0]);   // 8 words, 16 bf16
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                // inputs kk, kk + 4, kk + 8, kk + 12 of the lane's 16
+                const uint32_t v0 = (kk & 1) ? (w32[kk >> 1] >> 16) : (w32[kk >> 1] & 0xFFFFu);
+                const uint32_t v1 = (kk & 1) ? (w32[2 + (kk >> 1)] >> 16) : (w32[2 + (kk >> 1)] & 0xFFFFu);
+                const uint32_t v2 = (kk & 1) ? (w32[4 + (kk >> 1)] >> 16) : (w32[4 + (kk >> 1)] & 0xFFFFu);
+                const uint32_t v3 = (kk & 1) ? (w32[6 + (kk >> 1)] >> 16) : (w32[6 + (kk >> 1)] & 0xFFFFu);
+                uint2 pk;
+                pk.x = v0 | (v1 << 16);
+                pk.y = v2 | (v3 << 16);
+                *reinterpret_cast<uint2 *>(&xs[wave][xr][(4 * q + kk) * 16 + xc / 4]) = pk;
+            }
+            // weights: input j = 16 jc + jj of experts 4 eq + i -> [4 q + j % 4][4 eq + i][j / 4]
+            const f32x4_t wq = wblk < NB ? b.wv[q] : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            const int j = jin;   // 16 jc + jj with jc = jin / 16, jj = jin % 16
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wsm[4 * q + (j & 3)][4 * eq + i][j >> 2] = wq[i];
+            const int g = kMG * st + q;
+            if (x16 && eb == 0 && tvalid && g < G) {
+                uint16_t *xo = x16 + (size_t)tx * d + 64 * g + xc;
+                *reinterpret_cast<u32x4_t *>(xo) = bf16x8_to_f16x8(b.xv[q][0]);
+                *reinterpret_cast<u32x4_t *>(xo + 8) = bf16x8_to_f16x8(b.xv[q][1]);
+            }
+        }
+    };
+    const int r = lane & 15, k = lane >> 4;
+    f32x4_t L = {0.0f, 0.0f, 0.0f, 0.0f};
+    // one group's operands for this lane: 16 x values (bf16) and 16 weights
+    struct Ops {
+        u32x4_t xa[2];
+        f32x4_t wb[4];
+    };
+    auto read_ops = [&](Ops &o, int q) {
+        const uint16_t *pa = &xs[wave][r][(4 * q + k) * 16];
+        o.xa[0] = *reinterpret_cast<const u32x4_t *>(pa);
+        o.xa[1] = *reinterpret_cast<const u32x4_t *>(pa + 8);
+        const float *pb = &wsm[4 * q + k][r][0];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o.wb[i] = *reinterpret_cast<const f32x4_t *>(pb + 4 * i);
+    };
+    auto xval = [](const Ops &o, int s4) {
+        const uint32_t w = o.xa[s4 >> 3][(s4 >> 1) & 3];
+        return bf16_to_f32((s4 & 1) ? (w >> 16) : (w & 0xFFFFu));
+    };
+    auto fold = [&](const f32x4_t &a) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) L[v] = L[v] + a[v];
+    };
+    auto compute = [&](int st) {
+        const int ng = min(kMG, G - kMG * st);
+        int q = 0;
+        for (; q + 2 <= ng; q += 2) {   // two chains interleaved
+            Ops o0, o1;
+            read_ops(o0, q);
+            read_ops(o1, q + 1);
+            f32x4_t a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s4 = 0; s4 < 16; ++s4) {
+                a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(xval(o0, s4), o0.wb[s4 >> 2][s4 & 3], a0, 0, 0, 0);
+                a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(xval(o1, s4), o1.wb[s4 >> 2][s4 & 3], a1, 0, 0, 0);
+            }
+            fold(a0);
+            fold(a1);
+        }
+        if (q < ng) {
+            Ops o0;
+            read_ops(o0, q);
+            f32x4_t a0 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s4 = 0; s4 < 16; ++s4)
+                a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(xval(o0, s4), o0.wb[s4 >> 2][s4 & 3], a0, 0, 0, 0);
+            fold(a0);
+        }
+    };
+    load(b0, 0);
+    if (NS > 1) load(b1, 1);
+    for (int st = 0; st < NS; st += 2) {
+        stage(b0, st);
+        __syncthreads();
+        if (st + 2 < NS) load(b0, st + 2);
+        compute(st);
+        __syncthreads();   // every wave is done with the staged step
+        if (st + 1 < NS) {
+            stage(b1, st + 1);
+            __syncthreads();
+            if (st + 3 < NS) load(b1, st + 3);
+            compute(st + 1);
+            __syncthreads();
+        }
+    }
+    const int e = kRNE * 4 * eb + r;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int t = t0 + 16 * wave + 4 * k + v;
+        if (t < T && e < E) logits[(size_t)t * E + e] = logit_bias ? L[v] + logit_bias[e] : L[v];
+    }
+}
+
+// The router table the prefill routers read (weights fma(scale, q, bias) in fp32; layout above).
 // grid ceil(n / 256) with n = ceil(E / kRNE) * G * kRBlk; block 256
 __global__ __launch_bounds__(256) void k_router_table(const uint8_t *__restrict__ q, const uint32_t *__restrict__ sb,
                                                       int E, int d, float *__restrict__ out) {
@@ -687,10 +744,12 @@ __global__ __launch_bounds__(256) void k_bucket_scatter(const int32_t *__restric
 
 }  // namespace
 
-// k_router_ksplit while its launch has at most kRouterKsplitMaxWG workgroups (five per compute
-// unit); both kernels give the same bits. Measured on the 2816-wide, 128-expert layer (router
-// kernel, ksplit against k_router_tok): 256 tokens 17.0 / 62.1 us, 512: 18.8 / 64.2, 1024:
-// 30.6 / 64.6, 2048: 52.3 / 65.0, 3072: 73.8 / 67.6.
+// k_router_ksplit while its launch has at most kRouterKsplitMaxWG workgroups (two per compute
+// unit), k_router_mfma above; both give the same bits. Measured on the 2816-wide, 128-expert
+// layer (router kernel, ksplit / mfma): 256 tokens 17.0 / 33.1 us, 512: 18.6 / 33.5, 1024:
+// 31.0 / 34.1, 1536: 42.3 / 35.2, 2048: 53.7 / 34.9, 3072: 44.9 (mfma), 4096: 46 (mfma; the
+// fp32 MFMAs at ~80 % of their rate). A single mfma workgroup's chain of 704 MFMAs sets its
+// floor at small chunks.
 static bool router_ksplit(int T, int E) { return (long)cdiv(T, 64) * cdiv(E, kRNE) <= kRouterKsplitMaxWG; }
 
 hipError_t launch_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s,
@@ -700,7 +759,7 @@ hipError_t launch_router(const moe_layer *L, const uint16_t *x, int T, float *lo
         launch(k_router_ksplit, dim3(cdiv(T, 64), cdiv(E, kRNE)), dim3(64 * kKW), 0, s, x, T, d, E, L->ws.rqf,
                L->w.logit_bias, logits, write_aux ? L->ws.x16 : nullptr);
     else
-        launch(k_router_tok, dim3(cdiv(T, 64), cdiv(E, 4 * kRNE)), dim3(256), 0, s, x, T, d, E, L->ws.rqf,
+        launch(k_router_mfma, dim3(cdiv(T, 64), cdiv(E, 4 * kRNE)), dim3(256), 0, s, x, T, d, E, L->ws.rqf,
                L->w.logit_bias, logits, write_aux ? L->ws.x16 : nullptr);
     return hipGetLastError();
 }

@@ -1,8 +1,9 @@
 """GPU parity on layer shapes away from the 2816-wide workload, through the C ABI: the
 widest model dimension the kernels take (8192: router lanes loop over 128 groups), many
 experts with the largest top-k (256 experts, top-16: four logits per lane in the top-k,
-every down-projection wave shared), the largest expert count (1024, top-8), top-1 (a single routing weight of exactly 1), and widths
-whose last prefill tile is only partly filled, and expert scales above 2^-4.
+every down-projection wave shared), the largest expert count (1024, top-8), top-1 (a single routing weight of exactly 1), widths
+whose last prefill tile is only partly filled, expert scales above 2^-4, and a chunk routed on
+the matrix cores with ragged token, expert and group counts.
 Each shape runs with affine group-64 experts and (except the rescaled-scale case, which is about
 affine metadata) with Q4_0 experts. Same bar as the other parity tests: top-k index sets and
 grouping bit-exact, outputs within max |err| <= 2e-3 * rms of the oracle.
@@ -33,6 +34,11 @@ SHAPES = {
     "large_scales": (synth.Dims(d_model=512, n_experts=8, top_k=2, d_expert=128, d_shared=192), 2, 140),
     # the largest expert count the library takes (sixteen logits per lane in the top-k)
     "e1024_top8": (synth.Dims(d_model=512, n_experts=1024, top_k=8, d_expert=64, d_shared=128), 4, 260),
+    # a chunk large enough for the matrix-core prefill router (32 x 18 router workgroups of the
+    # group-split kernel would exceed its limit), with its last 64-token tile a quarter full, the
+    # last 16-expert block half past the expert count, and an odd group count (9: three K steps of
+    # four groups, the last holding a single group)
+    "router_matrix_cores": (synth.Dims(d_model=576, n_experts=72, top_k=8, d_expert=128, d_shared=256), 2, 2000),
 }
 
 

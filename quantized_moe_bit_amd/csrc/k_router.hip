@@ -233,58 +233,73 @@ __global__ __launch_bounds__(64 * kKW) void k_router_ksplit(const uint16_t *__re
 // 64 inputs (step s takes inputs 4 s .. 4 s + 3 as its k = 0..3) form exactly the chain
 // A_g = fma(x_63, w_63, ... fma(x_0, w_0, 0)) of the fixed order, for 16 tokens x 16 experts at
 // once; the group sums are then added in group order in registers, L = ((0 + A_0) + A_1) + ...
-// Workgroup: 64 tokens (wave w: tokens 16 w .. 16 w + 15) x 16 experts. The K loop takes kMG
-// groups per step: their x rows (bf16) and the 16 experts' weights (fp32, from the router
-// table's four 4-expert blocks) are staged in LDS transposed, so that the 16 operands one lane
-// needs for a group's chain (input 4 s + k for s = 0..15) are contiguous and come in with two
-// (x) and four (weights) 16-byte reads; the loads of the step after next run in registers
-// meanwhile (two register buffers). The chains of two groups run interleaved, one accumulator
-// each, and fold into L in group order. The expert block 0 also writes the fp16 copy of x.
 // Operand layout: lane l holds A[row l % 16][k l / 16] and B[k l / 16][column l % 16]; result
 // element v of lane l is row 4 (l / 16) + v, column l % 16.
-// LDS: x as [wave][row r][4 q + k][16 s] bf16 with rows 528 B apart, weights as
-// [4 q + k][expert r][16 s] fp32 with experts 80 B apart: the eight lanes of one 16-byte read
-// pass hit eight distinct 16-byte bank groups.
-// grid: (ceil(T / 64), ceil(E / 16)); block 256
-constexpr int kMG = 4;                         // groups per K step
-constexpr int kMXR = 4 * kMG * 16 + 8;         // bf16 per staged x row (528 B)
-constexpr int kMWE = 20;                       // fp32 per staged expert (80 B)
-__global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict__ x, int T, int d, int E,
-                                                     const float *__restrict__ tab, const float *__restrict__ logit_bias,
-                                                     float *__restrict__ logits, uint16_t *__restrict__ x16) {
-    __shared__ __align__(16) uint16_t xs[4][16][kMXR];
-    __shared__ __align__(16) float wsm[4 * kMG][16][kMWE];
-    const int G = d / 64, NB = cdiv(E, kRNE), NS = cdiv(G, kMG);
+// Workgroup: 64 tokens (wave w: tokens 16 w .. 16 w + 15) x 16 experts. The MFMA router table
+// (below) stores each lane's 16 weight operands of a group contiguously; a K step of kMG
+// groups copies the step's table rows (4 KB per group, shared by the four waves) into LDS with
+// 80 B between lanes, and each wave writes the x rows of its 16 tokens into a tile of its own,
+// transposed so that a lane's 16 x operands of a group (input 4 s + k, s = 0..15) are
+// contiguous, rows 272 B apart; a lane's operands then come in with two (x) and four (weights)
+// 16-byte reads, each pass of eight lanes on eight distinct 16-byte bank groups. The LDS
+// (55.5 KB) and registers leave room for two workgroups per compute unit.
+// Software pipeline over two LDS stages and two register sets of operands, one barrier per K
+// step: step st runs its kMG chains (one accumulator each, interleaved) on operands read during
+// step st - 1, while the operands of step st + 1 come in from LDS, step st + 2 (loaded into
+// registers during step st - 1) is written into the stage step st's operands came from, and the
+// global loads of step st + 3 are issued; the group sums are folded into L in group order last.
+// The loads are issued on every path (past the last group they re-read it), so each wait is for
+// exactly its own step's data.
+// Tile order: workgroup b runs on XCD b % 8 and takes token block 8 (b / 8 / NEB) + b % 8 and
+// expert block (b / 8) % NEB, so an XCD runs the NEB expert blocks of a token block back to
+// back (its x rows fetched into that XCD's L2 once). Expert block eb also writes the fp16 copy
+// of x for the groups g with g % NEB = eb of its tokens, so the stores are spread evenly.
+// grid: 8 ceil(ceil(T / 64) / 8) ceil(E / 16); block 256
+constexpr int kMG = 2;                         // groups per K step
+constexpr int kMXR = 64 * kMG + 8;             // bf16 per staged x row (272 B)
+constexpr int kMTile = 1024;                   // MFMA table floats per (16-expert block, group)
+constexpr int kMWL = 20;                       // staged weight floats per lane (80 B)
+struct alignas(16) RouterMfmaSmem {
+    alignas(16) uint16_t xs[2][4][16][kMXR];
+    alignas(16) float wsm[2][kMG][64][kMWL];
+};
+template <bool X16>
+__device__ __forceinline__ f32x4_t router_mfma_tile(RouterMfmaSmem &sm, const uint16_t *__restrict__ x, int T, int d,
+                                                    int G, int tb, int eb, int NEB, const float *__restrict__ tab,
+                                                    uint16_t *__restrict__ x16) {
+    const int NS = cdiv(G, kMG);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int t0 = blockIdx.x * 64, eb = blockIdx.y;
-    // x staging: lane l loads row l / 4 of its wave, 16 inputs of each group at 16 (l % 4)
+    // x loads: lane l takes row l / 4 of its wave's 16, inputs 16 (l % 4) .. 16 (l % 4) + 15 of each group
     const int xr = lane >> 2, xc = (lane & 3) * 16;
-    const int tx = t0 + 16 * wave + xr;
-    const bool tvalid = tx < T;
+    const int tx = 64 * tb + 16 * wave + xr;
     const uint16_t *xrow = x + (size_t)min(tx, T - 1) * d + xc;
-    // weight staging: thread tid loads experts 4 eq .. 4 eq + 3 of input 16 jc + jj of each group
-    const int eq = tid >> 6, jin = tid & 63;
-    const int wblk = kRNE * eb + eq;
-    const float *wsrc = tab + (size_t)min(wblk, NB - 1) * G * kRBlk + 4 * jin;
-    struct Buf {
-        u32x4_t xv[kMG][2];
-        f32x4_t wv[kMG];
-    };
-    Buf b0, b1;
-    auto load = [&](Buf &b, int st) {
+    const bool wx16 = X16 && tx < T;
+    // weight loads: thread tid copies half tid % 2 of table lane (tid / 2) % 64 of group kMG st + tid / 128
+    const int wq = tid >> 7, wl = (tid >> 1) & 63, wh = tid & 1;
+    const float *wsrc = tab + ((size_t)eb * G * 64 + wl) * 16 + 8 * wh;
+    f32x4_t wv[2];
+    u32x4_t xv[kMG][2];
+    // weights first, so that staging waits for them alone before it waits for x
+    auto load = [&](int st) {
+        const f32x4_t *p = reinterpret_cast<const f32x4_t *>(wsrc + (size_t)min(kMG * st + wq, G - 1) * kMTile);
+        wv[0] = p[0];
+        wv[1] = p[1];
+        __builtin_amdgcn_sched_barrier(0);   // keeps this order of the loads on every path
 #pragma unroll
         for (int q = 0; q < kMG; ++q) {
             const int g = min(kMG * st + q, G - 1);
-            b.xv[q][0] = ld16(xrow + 64 * g);
-            b.xv[q][1] = ld16(xrow + 64 * g + 8);
-            b.wv[q] = *reinterpret_cast<const f32x4_t *>(wsrc + (size_t)g * kRBlk);
+            xv[q][0] = ld16(xrow + 64 * g);
+            xv[q][1] = ld16(xrow + 64 * g + 8);
         }
     };
-    auto stage = [&](const Buf &b, int st) {
+    // the loaded step into LDS stage b: x input xc + i of group q -> xs[b][wave][xr][16 (4 q + i % 4) + xc / 4 + i / 4];
+    // the fp16 copy of x is stored last
+    auto stage = [&](int b, int st) {
+        *reinterpret_cast<f32x4_t *>(&sm.wsm[b][wq][wl][8 * wh]) = wv[0];
+        *reinterpret_cast<f32x4_t *>(&sm.wsm[b][wq][wl][8 * wh + 4]) = wv[1];
 #pragma unroll
         for (int q = 0; q < kMG; ++q) {
-            // x: input xc + i of the group -> [4 q + (i % 4)][xc / 4 + i / 4]
-            const uint32_t *w32 = reinterpret_cast<const uint32_t *>(&b.xv[q][0]);   // 8 words, 16 bf16
+            const uint32_t *w32 = reinterpret_cast<const uint32_t *>(&xv[q][0]);   // 8 words, 16 bf16
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 // inputs kk, kk + 4, kk + 8, kk + 12 of the lane's 16
@@ -295,92 +310,157 @@ __global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict_
                 uint2 pk;
                 pk.x = v0 | (v1 << 16);
                 pk.y = v2 | (v3 << 16);
-                *reinterpret_cast<uint2 *>(&xs[wave][xr][(4 * q + kk) * 16 + xc / 4]) = pk;
+                *reinterpret_cast<uint2 *>(&sm.xs[b][wave][xr][(4 * q + kk) * 16 + xc / 4]) = pk;
             }
-            // weights: input j = 16 jc + jj of experts 4 eq + i -> [4 q + j % 4][4 eq + i][j / 4]
-            const f32x4_t wq = wblk < NB ? b.wv[q] : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            const int j = jin;   // 16 jc + jj with jc = jin / 16, jj = jin % 16
+        }
+        if constexpr (X16) {
+            if (wx16) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wsm[4 * q + (j & 3)][4 * eq + i][j >> 2] = wq[i];
-            const int g = kMG * st + q;
-            if (x16 && eb == 0 && tvalid && g < G) {
-                uint16_t *xo = x16 + (size_t)tx * d + 64 * g + xc;
-                *reinterpret_cast<u32x4_t *>(xo) = bf16x8_to_f16x8(b.xv[q][0]);
-                *reinterpret_cast<u32x4_t *>(xo + 8) = bf16x8_to_f16x8(b.xv[q][1]);
+                for (int q = 0; q < kMG; ++q) {
+                    const int g = kMG * st + q;
+                    if (g < G && g % NEB == eb) {
+                        uint16_t *xo = x16 + (size_t)tx * d + 64 * g + xc;
+                        *reinterpret_cast<u32x4_t *>(xo) = bf16x8_to_f16x8(xv[q][0]);
+                        *reinterpret_cast<u32x4_t *>(xo + 8) = bf16x8_to_f16x8(xv[q][1]);
+                    }
+                }
             }
         }
     };
     const int r = lane & 15, k = lane >> 4;
-    f32x4_t L = {0.0f, 0.0f, 0.0f, 0.0f};
-    // one group's operands for this lane: 16 x values (bf16) and 16 weights
     struct Ops {
-        u32x4_t xa[2];
-        f32x4_t wb[4];
+        u32x4_t xa[kMG][2];   // a lane's 16 x operands (bf16) of each group
+        f32x4_t wb[kMG][4];   // and its 16 weight operands
     };
-    auto read_ops = [&](Ops &o, int q) {
-        const uint16_t *pa = &xs[wave][r][(4 * q + k) * 16];
-        o.xa[0] = *reinterpret_cast<const u32x4_t *>(pa);
-        o.xa[1] = *reinterpret_cast<const u32x4_t *>(pa + 8);
-        const float *pb = &wsm[4 * q + k][r][0];
+    auto read_ops = [&](Ops &o, int b) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o.wb[i] = *reinterpret_cast<const f32x4_t *>(pb + 4 * i);
-    };
-    auto xval = [](const Ops &o, int s4) {
-        const uint32_t w = o.xa[s4 >> 3][(s4 >> 1) & 3];
-        return bf16_to_f32((s4 & 1) ? (w >> 16) : (w & 0xFFFFu));
-    };
-    auto fold = [&](const f32x4_t &a) {
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) L[v] = L[v] + a[v];
-    };
-    auto compute = [&](int st) {
-        const int ng = min(kMG, G - kMG * st);
-        int q = 0;
-        for (; q + 2 <= ng; q += 2) {   // two chains interleaved
-            Ops o0, o1;
-            read_ops(o0, q);
-            read_ops(o1, q + 1);
-            f32x4_t a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int s4 = 0; s4 < 16; ++s4) {
-                a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(xval(o0, s4), o0.wb[s4 >> 2][s4 & 3], a0, 0, 0, 0);
-                a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(xval(o1, s4), o1.wb[s4 >> 2][s4 & 3], a1, 0, 0, 0);
+            for (int q = 0; q < kMG; ++q) {
+                o.wb[q][i] = *reinterpret_cast<const f32x4_t *>(&sm.wsm[b][q][lane][4 * i]);
+                if (i < 2) o.xa[q][i] = *reinterpret_cast<const u32x4_t *>(&sm.xs[b][wave][r][(4 * q + k) * 16 + 8 * i]);
             }
-            fold(a0);
-            fold(a1);
-        }
-        if (q < ng) {
-            Ops o0;
-            read_ops(o0, q);
-            f32x4_t a0 = {0.0f, 0.0f, 0.0f, 0.0f};
+    };
+    f32x4_t L = {0.0f, 0.0f, 0.0f, 0.0f};
+    // the chains of step st (operands o), folded into L in group order; the next step's operands
+    // are read from LDS stage nb into `next` meanwhile, one read between every two MFMAs (a wave
+    // keeps at most 15 LDS reads in flight; issued all at once they would stall it)
+    auto mfma_step = [&](const Ops &o, int st, Ops &next, int nb, f32x4_t (&a)[kMG]) {
+        auto xval = [&](int q, int s4) {
+            const uint32_t v = o.xa[q][s4 >> 3][(s4 >> 1) & 3];
+            return bf16_to_f32((s4 & 1) ? (v >> 16) : (v & 0xFFFFu));
+        };
+        // every x operand converted before the first MFMA, each into a register of its own: a
+        // register an MFMA is still reading is never rewritten by the next conversion
+        float xf[kMG][16];
+#pragma unroll
+        for (int q = 0; q < kMG; ++q)
+#pragma unroll
+            for (int s4 = 0; s4 < 16; ++s4) xf[q][s4] = xval(q, s4);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < kMG; ++q) a[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        const int ng = min(kMG, G - kMG * st);
+        if (ng == kMG) {   // the chains interleaved
+            read_ops(next, nb);
 #pragma unroll
             for (int s4 = 0; s4 < 16; ++s4)
-                a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(xval(o0, s4), o0.wb[s4 >> 2][s4 & 3], a0, 0, 0, 0);
-            fold(a0);
+#pragma unroll
+                for (int q = 0; q < kMG; ++q)
+                    a[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(xf[q][s4], o.wb[q][s4 >> 2][s4 & 3], a[q], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 6 * kMG; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMAs
+            }
+        } else {
+            read_ops(next, nb);
+#pragma unroll
+            for (int q = 0; q < kMG; ++q)
+                if (q < ng)
+#pragma unroll
+                    for (int s4 = 0; s4 < 16; ++s4)
+                        a[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(xf[q][s4], o.wb[q][s4 >> 2][s4 & 3], a[q], 0, 0, 0);
         }
     };
-    load(b0, 0);
-    if (NS > 1) load(b1, 1);
+    // fold step st's group sums into L in group order (contraction is off for this file); the
+    // caller does this after staging, so the MFMAs run while the staging instructions issue
+    auto fold = [&](const f32x4_t (&a)[kMG], int st) {
+        const int ng = min(kMG, G - kMG * st);
+#pragma unroll
+        for (int q = 0; q < kMG; ++q)
+            if (q < ng)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) L[v] = L[v] + a[q][v];
+    };
+    // prologue: steps 0 and 1 staged, step 0's operands in registers, step 2 loading
+    Ops o0, o1;
+    load(0);
+    stage(0, 0);
+    load(1);
+    __syncthreads();
+    read_ops(o0, 0);
+    stage(1, 1);
+    load(2);
+    __syncthreads();
+    // step st: its operands are in registers, step st + 1 is staged in LDS stage (st + 1) % 2 and
+    // step st + 2 is loading; read step st + 1's operands, run step st's MFMAs, stage step st + 2
+    // into stage st % 2 (every wave has read it: barrier of step st - 1), issue step st + 3's loads
+    f32x4_t acc[kMG];
     for (int st = 0; st < NS; st += 2) {
-        stage(b0, st);
+        mfma_step(o0, st, o1, 1, acc);
+        stage(0, st + 2);
+        load(st + 3);
+        fold(acc, st);
         __syncthreads();
-        if (st + 2 < NS) load(b0, st + 2);
-        compute(st);
-        __syncthreads();   // every wave is done with the staged step
-        if (st + 1 < NS) {
-            stage(b1, st + 1);
-            __syncthreads();
-            if (st + 3 < NS) load(b1, st + 3);
-            compute(st + 1);
-            __syncthreads();
-        }
+        if (st + 1 >= NS) break;
+        mfma_step(o1, st + 1, o0, 0, acc);
+        stage(1, st + 3);
+        load(st + 4);
+        fold(acc, st + 1);
+        __syncthreads();
     }
-    const int e = kRNE * 4 * eb + r;
+    return L;
+}
+__global__ __launch_bounds__(256) void k_router_mfma(const uint16_t *__restrict__ x, int T, int d, int E,
+                                                     const float *__restrict__ tab, const float *__restrict__ logit_bias,
+                                                     float *__restrict__ logits, uint16_t *__restrict__ x16) {
+    __shared__ RouterMfmaSmem sm;
+    const int G = d / 64, NEB = cdiv(E, 16), NTB = cdiv(T, 64);
+    const int xq = blockIdx.x / kXcds;
+    const int eb = xq % NEB, tb = (xq / NEB) * kXcds + (int)(blockIdx.x % kXcds);
+    if (tb >= NTB) return;   // the whole workgroup
+    const f32x4_t L = x16 != nullptr ? router_mfma_tile<true>(sm, x, T, d, G, tb, eb, NEB, tab, x16)
+                                     : router_mfma_tile<false>(sm, x, T, d, G, tb, eb, NEB, tab, x16);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = 16 * eb + (lane & 15);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-        const int t = t0 + 16 * wave + 4 * k + v;
+        const int t = 64 * tb + 16 * wave + 4 * (lane >> 4) + v;
         if (t < T && e < E) logits[(size_t)t * E + e] = logit_bias ? L[v] + logit_bias[e] : L[v];
     }
+}
+
+// MFMA router table (built at layer creation, k_router_mtable): per 16-expert block eb and
+// group g, kMTile floats [lane l][s] with lane l = 16 k + c holding the weight of expert
+// 16 eb + c, input 4 s + k of the group (fp32 fma(scale, q, bias); experts past E are zero).
+// grid ceil(n / 256) with n = ceil(E / 16) * G * kMTile; block 256
+__global__ __launch_bounds__(256) void k_router_mtable(const uint8_t *__restrict__ q, const uint32_t *__restrict__ sb,
+                                                       int E, int d, float *__restrict__ out) {
+    const int G = d / 64;
+    const size_t n = (size_t)cdiv(E, 16) * G * kMTile;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int sidx = (int)(i % 16), l = (int)((i / 16) % 64);
+    const size_t bg = i / kMTile;
+    const int g = (int)(bg % G), eb = (int)(bg / G);
+    const int e = 16 * eb + (l & 15), j = 4 * sidx + (l >> 4);
+    float v = 0.0f;
+    if (e < E) {
+        const uint32_t w = sb[(size_t)e * G + g];
+        v = __builtin_fmaf(bf16_to_f32(w & 0xFFFFu), (float)q[(size_t)e * d + 64 * g + j], bf16_to_f32(w >> 16));
+    }
+    out[i] = v;
 }
 
 // The router table the prefill routers read (weights fma(scale, q, bias) in fp32; layout above).
@@ -746,10 +826,10 @@ __global__ __launch_bounds__(256) void k_bucket_scatter(const int32_t *__restric
 
 // k_router_ksplit while its launch has at most kRouterKsplitMaxWG workgroups (two per compute
 // unit), k_router_mfma above; both give the same bits. Measured on the 2816-wide, 128-expert
-// layer (router kernel, ksplit / mfma): 256 tokens 17.0 / 33.1 us, 512: 18.6 / 33.5, 1024:
-// 31.0 / 34.1, 1536: 42.3 / 35.2, 2048: 53.7 / 34.9, 3072: 44.9 (mfma), 4096: 46 (mfma; the
-// fp32 MFMAs at ~80 % of their rate). A single mfma workgroup's chain of 704 MFMAs sets its
-// floor at small chunks.
+// layer (router kernel, ksplit / mfma): 256 tokens 17.0 / 29.0 us, 512: 18.6 / 28.7, 1024:
+// 31.0 / 30.2, 1536: 42.3 / 30.1, 2048: 53.7 / 30.9, 3072: 44.5 (mfma), 4096: 46 (mfma). The
+// mfma kernel's floor at small chunks is one wave's 704 chained MFMAs, ~50 cycles apart in
+// this loop (32 for the instruction alone).
 static bool router_ksplit(int T, int E) { return (long)cdiv(T, 64) * cdiv(E, kRNE) <= kRouterKsplitMaxWG; }
 
 hipError_t launch_router(const moe_layer *L, const uint16_t *x, int T, float *logits, hipStream_t s,
@@ -759,18 +839,21 @@ hipError_t launch_router(const moe_layer *L, const uint16_t *x, int T, float *lo
         launch(k_router_ksplit, dim3(cdiv(T, 64), cdiv(E, kRNE)), dim3(64 * kKW), 0, s, x, T, d, E, L->ws.rqf,
                L->w.logit_bias, logits, write_aux ? L->ws.x16 : nullptr);
     else
-        launch(k_router_mfma, dim3(cdiv(T, 64), cdiv(E, 4 * kRNE)), dim3(256), 0, s, x, T, d, E, L->ws.rqf,
-               L->w.logit_bias, logits, write_aux ? L->ws.x16 : nullptr);
+        launch(k_router_mfma, dim3(kXcds * cdiv(cdiv(T, 64), kXcds) * cdiv(E, 16)), dim3(256), 0, s, x, T, d, E,
+               L->ws.rqm, L->w.logit_bias, logits, write_aux ? L->ws.x16 : nullptr);
     return hipGetLastError();
 }
 
 size_t router_table_floats(const moe_dims &D) { return (size_t)cdiv(D.n_experts, kRNE) * (D.d_model / 64) * kRBlk; }
+size_t router_mtable_floats(const moe_dims &D) { return (size_t)cdiv(D.n_experts, 16) * (D.d_model / 64) * kMTile; }
 
 hipError_t launch_router_table(const moe_layer *L, hipStream_t s) {
-    const size_t n = router_table_floats(L->dims);
-    launch(k_router_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-           static_cast<const uint8_t *>(L->w.router.codes), L->w.router.sb, L->dims.n_experts, L->dims.d_model,
-           L->ws.rqf);
+    const uint8_t *q = static_cast<const uint8_t *>(L->w.router.codes);
+    const size_t n = router_table_floats(L->dims), nm = router_mtable_floats(L->dims);
+    launch(k_router_table, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, q, L->w.router.sb, L->dims.n_experts,
+           L->dims.d_model, L->ws.rqf);
+    launch(k_router_mtable, dim3((unsigned)((nm + 255) / 256)), dim3(256), 0, s, q, L->w.router.sb,
+           L->dims.n_experts, L->dims.d_model, L->ws.rqm);
     return hipGetLastError();
 }
 

@@ -339,6 +339,7 @@ moe_status moe_layer_create(const moe_dims *dims, const moe_weights *w, uint32_t
     plan.take(&ws.sgate, w->shared_gate ? Tm : 0);
     plan.take(&ws.slot_faults, 1);
     plan.take(&ws.rqf, router_table_floats(D));
+    plan.take(&ws.rqm, router_mtable_floats(D));
     plan.take(&ws.flag, 1);
     plan.take(&ws.shift, 3 * (size_t)L->n_mats + 3);
     plan.take(&ws.dxg, dec_workspace_floats(D, L->max_dec, 0));

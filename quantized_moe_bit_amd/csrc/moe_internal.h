@@ -106,6 +106,7 @@ struct Workspace {
     float *sgate;         // [maxT]             decode: shared-expert gate values (layers with a gate)
     int32_t *slot_faults; // [1]                absent expert slots the kernels met (layers with slots)
     float *rqf;           // router weights fma(scale, q, bias) as fp32 (prefill router table)
+    float *rqm;           // the same weights in the matrix-core router's operand order
     int32_t *flag;        // [1]                layer-creation checks, non-finite counts
     int32_t *shift;       // [3 n_mats + 3]     fp16 staging exponents of the prefill GEMMs: routed
                           //                    gate, up, down (kind * n_mats + matrix), then shared
@@ -188,6 +189,7 @@ hipError_t launch_dec_router_glue(const moe_layer *L, const uint16_t *h_in, cons
                                   uint16_t *x_out, int T, hipStream_t s);
 hipError_t launch_router_table(const moe_layer *L, hipStream_t s);
 size_t router_table_floats(const moe_dims &D);
+size_t router_mtable_floats(const moe_dims &D);
 hipError_t launch_topk(const moe_layer *L, int T, const float *logits, int32_t *idx, float *w, hipStream_t s);
 hipError_t launch_bucket_rank(const moe_layer *L, int T, const int32_t *idx, hipStream_t s);
 hipError_t launch_bucket_scan(const moe_layer *L, int T, hipStream_t s);

@@ -240,9 +240,11 @@ __global__ __launch_bounds__(64 * kKW) void k_router_ksplit(const uint16_t *__re
 // groups copies the step's table rows (4 KB per group, shared by the four waves) into LDS with
 // 80 B between lanes, and each wave writes the x rows of its 16 tokens into a tile of its own,
 // transposed so that a lane's 16 x operands of a group (input 4 s + k, s = 0..15) are
-// contiguous, rows 272 B apart; a lane's operands then come in with two (x) and four (weights)
-// 16-byte reads, each pass of eight lanes on eight distinct 16-byte bank groups. The LDS
-// (55.5 KB) and registers leave room for two workgroups per compute unit.
+// contiguous; a lane's operands then come in with two (x) and four (weights) 16-byte reads.
+// The 16-byte pieces of x row r sit at piece u ^ xswz(r), which keeps the tile's writes (16
+// lanes x 8 B per pass) and reads (8 lanes x 16 B) free of bank conflicts for 32 as for 64 LDS
+// banks; the weights' 80-B lane pitch does the same for theirs. The LDS (53 KB) and registers
+// leave room for two workgroups per compute unit.
 // Software pipeline over two LDS stages and two register sets of operands, one barrier per K
 // step: step st runs its kMG chains (one accumulator each, interleaved) on operands read during
 // step st - 1, while the operands of step st + 1 come in from LDS, step st + 2 (loaded into
@@ -256,9 +258,11 @@ __global__ __launch_bounds__(64 * kKW) void k_router_ksplit(const uint16_t *__re
 // of x for the groups g with g % NEB = eb of its tokens, so the stores are spread evenly.
 // grid: 8 ceil(ceil(T / 64) / 8) ceil(E / 16); block 256
 constexpr int kMG = 2;                         // groups per K step
-constexpr int kMXR = 64 * kMG + 8;             // bf16 per staged x row (272 B)
+constexpr int kMXR = 64 * kMG;                 // bf16 per staged x row (256 B: 16 pieces of 16 B)
 constexpr int kMTile = 1024;                   // MFMA table floats per (16-expert block, group)
 constexpr int kMWL = 20;                       // staged weight floats per lane (80 B)
+// physical 16-byte piece of logical piece u in row r of the x tile: u ^ xswz(r)
+__device__ __forceinline__ int xswz(int r) { return (2 * (r & 3) + ((r >> 2) & 3)) & 15; }
 struct alignas(16) RouterMfmaSmem {
     alignas(16) uint16_t xs[2][4][16][kMXR];
     alignas(16) float wsm[2][kMG][64][kMWL];
@@ -274,8 +278,8 @@ __device__ __forceinline__ f32x4_t router_mfma_tile(RouterMfmaSmem &sm, const ui
     const int tx = 64 * tb + 16 * wave + xr;
     const uint16_t *xrow = x + (size_t)min(tx, T - 1) * d + xc;
     const bool wx16 = X16 && tx < T;
-    // weight loads: thread tid copies half tid % 2 of table lane (tid / 2) % 64 of group kMG st + tid / 128
-    const int wq = tid >> 7, wl = (tid >> 1) & 63, wh = tid & 1;
+    // weight loads: thread tid copies half (tid / 64) % 2 of table lane tid % 64 of group kMG st + tid / 128
+    const int wq = tid >> 7, wl = tid & 63, wh = (tid >> 6) & 1;
     const float *wsrc = tab + ((size_t)eb * G * 64 + wl) * 16 + 8 * wh;
     f32x4_t wv[2];
     u32x4_t xv[kMG][2];
@@ -292,7 +296,8 @@ __device__ __forceinline__ f32x4_t router_mfma_tile(RouterMfmaSmem &sm, const ui
             xv[q][1] = ld16(xrow + 64 * g + 8);
         }
     };
-    // the loaded step into LDS stage b: x input xc + i of group q -> xs[b][wave][xr][16 (4 q + i % 4) + xc / 4 + i / 4];
+    // the loaded step into LDS stage b: x input xc + i of group q -> logical element
+    // 16 (4 q + i % 4) + xc / 4 + i / 4 of row xr (16-byte piece 2 (4 q + i % 4) + xc / 32);
     // the fp16 copy of x is stored last
     auto stage = [&](int b, int st) {
         *reinterpret_cast<f32x4_t *>(&sm.wsm[b][wq][wl][8 * wh]) = wv[0];
@@ -310,7 +315,8 @@ __device__ __forceinline__ f32x4_t router_mfma_tile(RouterMfmaSmem &sm, const ui
                 uint2 pk;
                 pk.x = v0 | (v1 << 16);
                 pk.y = v2 | (v3 << 16);
-                *reinterpret_cast<uint2 *>(&sm.xs[b][wave][xr][(4 * q + kk) * 16 + xc / 4]) = pk;
+                const int u = 2 * (4 * q + kk) + (xc >> 5);
+                *reinterpret_cast<uint2 *>(&sm.xs[b][wave][xr][8 * (u ^ xswz(xr)) + ((xc >> 2) & 4)]) = pk;
             }
         }
         if constexpr (X16) {
@@ -338,7 +344,8 @@ __device__ __forceinline__ f32x4_t router_mfma_tile(RouterMfmaSmem &sm, const ui
 #pragma unroll
             for (int q = 0; q < kMG; ++q) {
                 o.wb[q][i] = *reinterpret_cast<const f32x4_t *>(&sm.wsm[b][q][lane][4 * i]);
-                if (i < 2) o.xa[q][i] = *reinterpret_cast<const u32x4_t *>(&sm.xs[b][wave][r][(4 * q + k) * 16 + 8 * i]);
+                if (i < 2)
+                    o.xa[q][i] = *reinterpret_cast<const u32x4_t *>(&sm.xs[b][wave][r][8 * ((2 * (4 * q + k) + i) ^ xswz(r))]);
             }
     };
     f32x4_t L = {0.0f, 0.0f, 0.0f, 0.0f};

@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 / fp16 MFMA, TFLOP/s
+FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 (vector, and matrix), TFLOP/s
 
 
 def log(msg):
@@ -370,6 +371,16 @@ def prefill_section(args, dev, name, label):
             pre["roofline_" + kname[4:]] = dict(bound="mfma", achieved=round(tf, 1), peak=MFMA_PEAK_TFLOPS,
                                                  unit="TFLOP/s", frac=round(tf / MFMA_PEAK_TFLOPS, 4),
                                                  flops=fl, avg_us=round(pk[kname], 2))
+    if "router" in pk:
+        # fp32 fixed-order chains: on fp32 MFMA (matrix-core router) or as VALU fma chains (the
+        # group-split router the library takes for small chunks); both peaks are 157.3 TFLOP/s
+        E = D.n_experts
+        valu = d // 64 <= 64 and -(-T // 64) * -(-E // 4) <= 512
+        fl = 2.0 * T * E * d
+        tf = fl / (pk["router"] * 1e-6) / 1e12
+        pre["roofline_router"] = dict(bound="alu" if valu else "mfma", achieved=round(tf, 1), peak=FP32_PEAK_TFLOPS,
+                                      unit="TFLOP/s", frac=round(tf / FP32_PEAK_TFLOPS, 4), flops=fl,
+                                      avg_us=round(pk["router"], 2))
     return lp, xpd, T, pre
 
 

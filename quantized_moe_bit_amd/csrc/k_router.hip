@@ -245,11 +245,12 @@ __global__ __launch_bounds__(64 * kKW) void k_router_ksplit(const uint16_t *__re
 // lanes x 8 B per pass) and reads (8 lanes x 16 B) free of bank conflicts for 32 as for 64 LDS
 // banks; the weights' 80-B lane pitch does the same for theirs. The LDS (53 KB) and registers
 // leave room for two workgroups per compute unit.
-// Software pipeline over two LDS stages and two register sets of operands, one barrier per K
-// step: step st runs its kMG chains (one accumulator each, interleaved) on operands read during
-// step st - 1, while the operands of step st + 1 come in from LDS, step st + 2 (loaded into
-// registers during step st - 1) is written into the stage step st's operands came from, and the
-// global loads of step st + 3 are issued; the group sums are folded into L in group order last.
+// Software pipeline over two LDS stages, two register sets of operands and two of global loads,
+// one barrier per K step: step st runs its kMG chains (one accumulator each, interleaved) on
+// operands read during step st - 1, while the operands of step st + 1 come in from LDS, step
+// st + 2 (loaded into registers during step st - 2) is written into the stage step st's operands
+// came from, and the global loads of step st + 4 are issued; the group sums are folded into L in
+// group order last.
 // The loads are issued on every path (past the last group they re-read it), so each wait is for
 // exactly its own step's data.
 // Tile order: workgroup b runs on XCD b % 8 and takes token block 8 (b / 8 / NEB) + b % 8 and
@@ -281,40 +282,40 @@ __device__ __forceinline__ f32x4_t router_mfma_tile(RouterMfmaSmem &sm, const ui
     // weight loads: thread tid copies half (tid / 64) % 2 of table lane tid % 64 of group kMG st + tid / 128
     const int wq = tid >> 7, wl = tid & 63, wh = (tid >> 6) & 1;
     const float *wsrc = tab + ((size_t)eb * G * 64 + wl) * 16 + 8 * wh;
-    f32x4_t wv[2];
-    u32x4_t xv[kMG][2];
+    struct Loaded {   // one step's global loads
+        f32x4_t wv[2];
+        u32x4_t xv[kMG][2];
+    };
     // weights first, so that staging waits for them alone before it waits for x
-    auto load = [&](int st) {
+    auto load = [&](Loaded &ld, int st) {
         const f32x4_t *p = reinterpret_cast<const f32x4_t *>(wsrc + (size_t)min(kMG * st + wq, G - 1) * kMTile);
-        wv[0] = p[0];
-        wv[1] = p[1];
+        ld.wv[0] = p[0];
+        ld.wv[1] = p[1];
         __builtin_amdgcn_sched_barrier(0);   // keeps this order of the loads on every path
 #pragma unroll
         for (int q = 0; q < kMG; ++q) {
             const int g = min(kMG * st + q, G - 1);
-            xv[q][0] = ld16(xrow + 64 * g);
-            xv[q][1] = ld16(xrow + 64 * g + 8);
+            ld.xv[q][0] = ld16(xrow + 64 * g);
+            ld.xv[q][1] = ld16(xrow + 64 * g + 8);
         }
     };
     // the loaded step into LDS stage b: x input xc + i of group q -> logical element
     // 16 (4 q + i % 4) + xc / 4 + i / 4 of row xr (16-byte piece 2 (4 q + i % 4) + xc / 32);
     // the fp16 copy of x is stored last
-    auto stage = [&](int b, int st) {
-        *reinterpret_cast<f32x4_t *>(&sm.wsm[b][wq][wl][8 * wh]) = wv[0];
-        *reinterpret_cast<f32x4_t *>(&sm.wsm[b][wq][wl][8 * wh + 4]) = wv[1];
+    auto stage = [&](int b, int st, const Loaded &ld) {
+        *reinterpret_cast<f32x4_t *>(&sm.wsm[b][wq][wl][8 * wh]) = ld.wv[0];
+        *reinterpret_cast<f32x4_t *>(&sm.wsm[b][wq][wl][8 * wh + 4]) = ld.wv[1];
 #pragma unroll
         for (int q = 0; q < kMG; ++q) {
-            const uint32_t *w32 = reinterpret_cast<const uint32_t *>(&xv[q][0]);   // 8 words, 16 bf16
+            const uint32_t *w32 = reinterpret_cast<const uint32_t *>(&ld.xv[q][0]);   // 8 words, 16 bf16
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                // inputs kk, kk + 4, kk + 8, kk + 12 of the lane's 16
-                const uint32_t v0 = (kk & 1) ? (w32[kk >> 1] >> 16) : (w32[kk >> 1] & 0xFFFFu);
-                const uint32_t v1 = (kk & 1) ? (w32[2 + (kk >> 1)] >> 16) : (w32[2 + (kk >> 1)] & 0xFFFFu);
-                const uint32_t v2 = (kk & 1) ? (w32[4 + (kk >> 1)] >> 16) : (w32[4 + (kk >> 1)] & 0xFFFFu);
-                const uint32_t v3 = (kk & 1) ? (w32[6 + (kk >> 1)] >> 16) : (w32[6 + (kk >> 1)] & 0xFFFFu);
+                // inputs kk, kk + 4, kk + 8, kk + 12 of the lane's 16: the same half (kk % 2) of
+                // words kk / 2, 2 + kk / 2, 4 + kk / 2, 6 + kk / 2, two per byte permute
+                const uint32_t sel = (kk & 1) ? 0x07060302u : 0x05040100u;
                 uint2 pk;
-                pk.x = v0 | (v1 << 16);
-                pk.y = v2 | (v3 << 16);
+                pk.x = __builtin_amdgcn_perm(w32[2 + (kk >> 1)], w32[kk >> 1], sel);
+                pk.y = __builtin_amdgcn_perm(w32[6 + (kk >> 1)], w32[4 + (kk >> 1)], sel);
                 const int u = 2 * (4 * q + kk) + (xc >> 5);
                 *reinterpret_cast<uint2 *>(&sm.xs[b][wave][xr][8 * (u ^ xswz(xr)) + ((xc >> 2) & 4)]) = pk;
             }
@@ -326,8 +327,8 @@ __device__ __forceinline__ f32x4_t router_mfma_tile(RouterMfmaSmem &sm, const ui
                     const int g = kMG * st + q;
                     if (g < G && g % NEB == eb) {
                         uint16_t *xo = x16 + (size_t)tx * d + 64 * g + xc;
-                        *reinterpret_cast<u32x4_t *>(xo) = bf16x8_to_f16x8(xv[q][0]);
-                        *reinterpret_cast<u32x4_t *>(xo + 8) = bf16x8_to_f16x8(xv[q][1]);
+                        *reinterpret_cast<u32x4_t *>(xo) = bf16x8_to_f16x8(ld.xv[q][0]);
+                        *reinterpret_cast<u32x4_t *>(xo + 8) = bf16x8_to_f16x8(ld.xv[q][1]);
                     }
                 }
             }
@@ -400,30 +401,33 @@ __device__ __forceinline__ f32x4_t router_mfma_tile(RouterMfmaSmem &sm, const ui
 #pragma unroll
                 for (int v = 0; v < 4; ++v) L[v] = L[v] + a[q][v];
     };
-    // prologue: steps 0 and 1 staged, step 0's operands in registers, step 2 loading
+    // prologue: steps 0 and 1 staged, step 0's operands in registers, steps 2 and 3 loading
     Ops o0, o1;
-    load(0);
-    stage(0, 0);
-    load(1);
+    Loaded la, lb;
+    load(la, 0);
+    load(lb, 1);
+    stage(0, 0, la);
+    load(la, 2);
     __syncthreads();
     read_ops(o0, 0);
-    stage(1, 1);
-    load(2);
+    stage(1, 1, lb);
+    load(lb, 3);
     __syncthreads();
     // step st: its operands are in registers, step st + 1 is staged in LDS stage (st + 1) % 2 and
-    // step st + 2 is loading; read step st + 1's operands, run step st's MFMAs, stage step st + 2
-    // into stage st % 2 (every wave has read it: barrier of step st - 1), issue step st + 3's loads
+    // steps st + 2 and st + 3 are loading; read step st + 1's operands, run step st's MFMAs, stage
+    // step st + 2 into stage st % 2 (every wave has read it: barrier of step st - 1), issue step
+    // st + 4's loads
     f32x4_t acc[kMG];
     for (int st = 0; st < NS; st += 2) {
         mfma_step(o0, st, o1, 1, acc);
-        stage(0, st + 2);
-        load(st + 3);
+        stage(0, st + 2, la);
+        load(la, st + 4);
         fold(acc, st);
         __syncthreads();
         if (st + 1 >= NS) break;
         mfma_step(o1, st + 1, o0, 0, acc);
-        stage(1, st + 3);
-        load(st + 4);
+        stage(1, st + 3, lb);
+        load(lb, st + 5);
         fold(acc, st + 1);
         __syncthreads();
     }

@@ -23,6 +23,9 @@ TOL = 2e-3
 SHAPES = {
     "w2816": (synth.WORKLOADS["decode"].dims, 300),
     "small": (synth.Dims(d_model=512, n_experts=16, top_k=4, d_expert=128, d_shared=256), 70),
+    # 72 input groups, more than the group-split prefill router takes: the matrix-core router
+    # reads the prologue's output, with its last 64-token block and 16-expert block part-filled
+    "wide_matrix_router": (synth.Dims(d_model=4608, n_experts=24, top_k=4, d_expert=128, d_shared=128), 100),
 }
 
 

@@ -204,6 +204,17 @@ def test_prefill_512_zipf():
     check_close(y.cpu().numpy(), y_ref, what="prefill512")
 
 
+def test_router_kernels_at_their_crossover():
+    """The 2816-wide, 128-expert layer routes 1024 tokens with the group-split prefill router
+    (512 workgroups, its limit) and 1090 with the matrix-core one (576; last 64-token block two
+    rows): both bit-exact against the oracle, so the two kernels agree bit for bit on the
+    tokens they share, including the tied ones."""
+    w, lay, x, tied, dl = workload("prefill4096")
+    for T in (1024, 1090):
+        say(f"route T={T}")
+        check_route(dl, lay, x[:T], tokens_to_device(x[:T]))
+
+
 def test_prefill_4096_zipf_ties_all_tokens():
     w, lay, x, tied, dl = workload("prefill4096")
     xd = tokens_to_device(x)

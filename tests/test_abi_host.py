@@ -283,3 +283,23 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         B.lib()
+
+
+def test_header_and_library_serve_a_plain_c99_program(tmp_path):
+    """tests/c/abi_from_c.c, built by gcc as strict C99 against include/moe.h and linked to the
+    library, runs the host-side calls (sizes, repack round trip, argument errors, create's
+    dimension checks) with no Python in between."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    B.lib()   # the library exists and matches its sources
+    libdir = os.path.dirname(B.LIB_PATH)
+    exe = str(tmp_path / "abi_from_c")
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c", "abi_from_c.c"), "-L", libdir, "-lmoe",
+                    f"-Wl,-rpath,{libdir}", "-o", exe], check=True, capture_output=True, text=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "C ABI host checks passed" in r.stdout

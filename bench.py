@@ -349,8 +349,15 @@ def prefill_section(args, dev, name, label):
         if c:
             pk[kname] = 1000.0 * ms / c
     B.moe_profile_enable(P.handle, False)
+    # weights the chunk streams: every expert it routes to, the shared expert and the router, once
+    # each (a small chunk is bound by streaming them, not by the matrix cores)
+    r = P.route(xpd, with_logits=False)
+    torch.cuda.synchronize()
+    n_used = int((np.diff(r["offsets"].cpu().numpy()) > 0).sum())
     P.close()
     d, I, Is, k = D.d_model, D.d_expert, D.d_shared, D.top_k
+    wbytes = (n_used * (2 * qmat_bytes(I, d, 4) + qmat_bytes(d, I, 4)) + 2 * qmat_bytes(Is, d, 4)
+              + qmat_bytes(d, Is, 4) + qmat_bytes(D.n_experts, d, 8))
     fl_gateup = 2.0 * (T * k * 2 * I * d + T * 2 * Is * d)
     fl_down = 2.0 * (T * k * d * I + T * d * Is)
     flops = fl_gateup + fl_down
@@ -362,6 +369,9 @@ def prefill_section(args, dev, name, label):
            "kernels_us": {n: round(v, 2) for n, v in pk.items()},
            "kernels_sum_us": round(sum(pk.values()), 2),
            "kernels_pass_us_per_step": round(1000.0 * ms_kpass, 2),
+           "experts_used": n_used, "weight_bytes_per_step": wbytes,
+           "weight_gbs": round(wbytes / (ms_pre * 1e-3) / 1e9, 1),
+           "weight_hbm_frac": round(wbytes / (ms_pre * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "note": "sustained back-to-back chunks lower the clock (the same chunk's GEMMs take up to ~25% "
                    "longer after a few chunks), so per-kernel times are compared with the step time of "
                    "their own instrumented pass"}

@@ -238,10 +238,11 @@ def test_prefill_4096_zipf_ties_all_tokens():
         say(f"prefill4096 oracle tokens {c}..{toks[-1]}")
     e = check_close(y, y_ref, what="prefill4096 all tokens")
     say(f"prefill4096: all {T} tokens within tolerance, max|err| {e:.2e} rms")
-    # determinism of the whole output
-    y2 = dl.prefill(xd)
-    torch.cuda.synchronize()
-    assert np.array_equal(y, y2.cpu().numpy())
+    # determinism of the whole output: two more runs, bit for bit
+    for _ in range(2):
+        y2 = dl.prefill(xd)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(np.asarray(y, np.float32).view(np.uint32), y2.cpu().numpy().view(np.uint32))
 
 
 @pytest.mark.parametrize("T", [1, 16])

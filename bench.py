@@ -662,6 +662,26 @@ def main():
                            "us_per_layer": round(1000.0 * ms_tok / NL, 3), "bytes_per_token": st_bytes,
                            "hbm_gbs": round(st_bytes / (ms_tok * 1e-3) / 1e9, 1),
                            "hbm_frac": round(st_bytes / (ms_tok * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        # the same stack recorded once (moe_stack_plan_create) and replayed per token on fixed
+        # buffers, each token's stream copied into the plan's h first (the copy is timed too)
+        hp = torch.empty_like(xb)
+        plan = B.moe_stack_plan_create(handles, hp, 1, xb, yb, hb)
+        for t in range(8):
+            hp.copy_(hd[t:t + 1])
+            B.moe_stack_plan_run(plan)
+        torch.cuda.synchronize()
+        s0.record()
+        for t in range(ws.tokens):
+            hp.copy_(hd[t:t + 1])
+            B.moe_stack_plan_run(plan)
+        s1.record()
+        torch.cuda.synchronize()
+        B.moe_stack_plan_destroy(plan)
+        ms_plan = s0.elapsed_time(s1) / ws.tokens
+        result["stack"]["recorded_plan"] = {
+            "tokens_per_s": round(1000.0 / ms_plan, 1), "us_per_layer": round(1000.0 * ms_plan / NL, 3),
+            "hbm_gbs": round(st_bytes / (ms_plan * 1e-3) / 1e9, 1),
+            "note": "moe_stack_plan_run per token, including a device copy of the token's stream into the plan's h"}
         for L in stack:
             L.close()
         del stack

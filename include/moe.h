@@ -320,6 +320,29 @@ moe_status moe_stack_glue(const uint16_t *h, const float *y, const uint16_t *pos
 moe_status moe_stack_forward_decode(moe_layer *const *layers, int32_t n_layers, uint16_t *h, int32_t T,
                                     uint16_t *x_buf, float *y_buf, uint16_t *h_buf, void *hip_stream);
 
+/*
+ * A decode stack recorded once, for callers that run the same layers on the same buffers
+ * token after token (Mference system design, "Decode": each token runs the layer stack in
+ * order). moe_stack_plan_create records exactly the kernels moe_stack_forward_decode(layers,
+ * n_layers, h, T, x_buf, y_buf, h_buf) enqueues, with the same arguments, as a HIP graph
+ * (captured on a stream of its own; nothing runs); moe_stack_plan_run launches that graph on
+ * hip_stream. A run computes what moe_stack_forward_decode computes on the buffers' contents
+ * at that point, bit for bit: the caller writes each token's stream into h before a run and
+ * reads h, x_buf and y_buf after it. The plan borrows the layers and the buffers: they must
+ * stay valid until moe_stack_plan_destroy, and runs on one plan, like calls on its layers,
+ * must be ordered on one stream. Create validates its arguments as moe_stack_forward_decode
+ * does and returns the same errors, except that T = 0 is MOE_E_SHAPE (nothing to record); it
+ * refuses (MOE_E_INVALID) layers created with MOE_FLAG_CHECK_FINITE or with profiling on, whose
+ * calls read device memory back, and a NULL out; MOE_E_DEVICE if HIP refuses the capture,
+ * MOE_E_NOMEM if the plan cannot be allocated. *out is NULL on error. Run: MOE_E_INVALID for a
+ * NULL plan, MOE_E_DEVICE if the launch fails. Destroy accepts NULL.
+ */
+typedef struct moe_stack_plan moe_stack_plan; /* opaque handle */
+moe_status moe_stack_plan_create(moe_layer *const *layers, int32_t n_layers, uint16_t *h, int32_t T,
+                                 uint16_t *x_buf, float *y_buf, uint16_t *h_buf, moe_stack_plan **out);
+moe_status moe_stack_plan_run(moe_stack_plan *plan, void *hip_stream);
+void moe_stack_plan_destroy(moe_stack_plan *plan);
+
 /* ---------------------------------------------------------------- host-side weight layout */
 
 /* Canonical host layout of one matrix or a stack of n_mats matrices [out, in]:

@@ -85,6 +85,9 @@ def lib() -> C.CDLL:
             "moe_forward_decode_noalloc": (st, [C.POINTER(moe_dims), C.POINTER(moe_weights), vp, i32, vp, vp]),
             "moe_stack_glue": (st, [vp, vp, vp, vp, vp, vp, i32, i32, vp]),
             "moe_stack_forward_decode": (st, [C.POINTER(vp), i32, vp, i32, vp, vp, vp, vp]),
+            "moe_stack_plan_create": (st, [C.POINTER(vp), i32, vp, i32, vp, vp, vp, C.POINTER(vp)]),
+            "moe_stack_plan_run": (st, [vp, vp]),
+            "moe_stack_plan_destroy": (None, [vp]),
             "moe_packed_bytes": (C.c_size_t, [i32, i32, i32, i32, i32]),
             "moe_repack": (st, [i32, i32, i32, i32, C.POINTER(moe_host_qmat), vp, vp]),
             "moe_unrepack": (st, [i32, i32, i32, i32, vp, vp, vp, vp, vp]),
@@ -201,6 +204,23 @@ def moe_stack_forward_decode(handles, h, T, x_buf, y_buf, h_buf, stream=None):
     arr = (C.c_void_p * len(handles))(*handles)
     _check(lib().moe_stack_forward_decode(arr, len(handles), _ptr(h), T, _ptr(x_buf), _ptr(y_buf), _ptr(h_buf),
                                           _stream(stream)), "moe_stack_forward_decode")
+
+
+def moe_stack_plan_create(handles, h, T, x_buf, y_buf, h_buf) -> int:
+    """The stack call recorded once as a graph; returns the plan handle."""
+    arr = (C.c_void_p * len(handles))(*handles)
+    out = C.c_void_p()
+    _check(lib().moe_stack_plan_create(arr, len(handles), _ptr(h), T, _ptr(x_buf), _ptr(y_buf), _ptr(h_buf),
+                                       C.byref(out)), "moe_stack_plan_create")
+    return out.value
+
+
+def moe_stack_plan_run(plan, stream=None):
+    _check(lib().moe_stack_plan_run(plan, _stream(stream)), "moe_stack_plan_run")
+
+
+def moe_stack_plan_destroy(plan):
+    lib().moe_stack_plan_destroy(plan)
 
 
 def moe_packed_bytes(bits, n_mats, out_dim, in_dim, part) -> int:

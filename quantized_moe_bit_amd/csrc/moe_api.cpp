@@ -593,6 +593,74 @@ moe_status moe_stack_forward_decode(moe_layer *const *layers, int32_t n_layers, 
     return MOE_OK;
 }
 
+struct moe_stack_plan {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+};
+
+void moe_stack_plan_destroy(moe_stack_plan *plan) {
+    if (!plan) return;
+    if (plan->exec) (void)hipGraphExecDestroy(plan->exec);
+    if (plan->graph) (void)hipGraphDestroy(plan->graph);
+    delete plan;
+}
+
+moe_status moe_stack_plan_create(moe_layer *const *layers, int32_t n_layers, uint16_t *h, int32_t T,
+                                 uint16_t *x_buf, float *y_buf, uint16_t *h_buf, moe_stack_plan **out) {
+    clear_error();
+    if (!out) return fail(MOE_E_INVALID, "moe_stack_plan_create: out is NULL");
+    *out = nullptr;
+    if (n_layers < 1 || !layers) return fail(MOE_E_INVALID, "moe_stack_plan_create: no layers");
+    if (T == 0) return fail(MOE_E_SHAPE, "moe_stack_plan_create: T = 0 (nothing to record)");
+    for (int l = 0; l < n_layers; ++l) {
+        const moe_layer *L = layers[l];
+        if (!L) return fail(MOE_E_INVALID, "moe_stack_plan_create: layer %d is NULL", l);
+        if (L->flags & MOE_FLAG_CHECK_FINITE)
+            return fail(MOE_E_INVALID, "moe_stack_plan_create: layer %d has MOE_FLAG_CHECK_FINITE (reads back)", l);
+        if (L->prof_on) return fail(MOE_E_INVALID, "moe_stack_plan_create: layer %d has profiling on", l);
+    }
+    moe_stack_plan *P = new (std::nothrow) moe_stack_plan();
+    if (!P) return fail(MOE_E_NOMEM, "moe_stack_plan_create: host allocation failed");
+    hipStream_t cs = nullptr;
+    hipError_t err = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+    if (err != hipSuccess) {
+        delete P;
+        return fail(MOE_E_DEVICE, "moe_stack_plan_create: stream: %s", hipGetErrorString(err));
+    }
+    err = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (err != hipSuccess) {
+        (void)hipStreamDestroy(cs);
+        delete P;
+        return fail(MOE_E_DEVICE, "moe_stack_plan_create: begin capture: %s", hipGetErrorString(err));
+    }
+    // the same validation and kernels as an ordinary call, recorded instead of run
+    const moe_status st = moe_stack_forward_decode(layers, n_layers, h, T, x_buf, y_buf, h_buf, cs);
+    char msg[sizeof g_err];
+    std::memcpy(msg, g_err, sizeof msg);
+    err = hipStreamEndCapture(cs, &P->graph);
+    (void)hipStreamDestroy(cs);
+    if (st != MOE_OK) {
+        moe_stack_plan_destroy(P);
+        clear_error();
+        return fail(st, "moe_stack_plan_create: %s", msg);
+    }
+    if (err == hipSuccess) err = hipGraphInstantiate(&P->exec, P->graph, nullptr, nullptr, 0);
+    if (err != hipSuccess) {
+        moe_stack_plan_destroy(P);
+        return fail(MOE_E_DEVICE, "moe_stack_plan_create: capture: %s", hipGetErrorString(err));
+    }
+    *out = P;
+    return MOE_OK;
+}
+
+moe_status moe_stack_plan_run(moe_stack_plan *plan, void *hip_stream) {
+    clear_error();
+    if (!plan) return fail(MOE_E_INVALID, "moe_stack_plan_run: plan is NULL");
+    const hipError_t err = hipGraphLaunch(plan->exec, static_cast<hipStream_t>(hip_stream));
+    if (err != hipSuccess) return fail(MOE_E_DEVICE, "moe_stack_plan_run: %s", hipGetErrorString(err));
+    return MOE_OK;
+}
+
 moe_status moe_prefill_route(moe_layer *L, const uint16_t *x, int32_t T, int32_t *expert_counts, void *hip_stream) {
     clear_error();
     moe_status st = check_tokens(L, T, "moe_prefill_route");

@@ -263,6 +263,16 @@ def test_calls_reject_null_layer_and_bad_sizes():
     assert L.moe_stack_forward_decode(None, 1, None, 1, None, None, None, None) == B.MOE_E_INVALID
     assert L.moe_stack_forward_decode(one_null, 0, None, 1, None, None, None, None) == B.MOE_E_INVALID
     assert L.moe_stack_forward_decode(one_null, 1, None, 1, None, None, None, None) == B.MOE_E_INVALID
+    # the recorded stack: argument checks before any stream or capture exists
+    plan = C.c_void_p(1)
+    assert L.moe_stack_plan_create(None, 1, None, 1, None, None, None, C.byref(plan)) == B.MOE_E_INVALID
+    assert plan.value is None   # *out is cleared on error
+    assert L.moe_stack_plan_create(one_null, 0, None, 1, None, None, None, C.byref(plan)) == B.MOE_E_INVALID
+    assert L.moe_stack_plan_create(one_null, 1, None, 0, None, None, None, C.byref(plan)) == B.MOE_E_SHAPE
+    assert L.moe_stack_plan_create(one_null, 1, None, 1, None, None, None, C.byref(plan)) == B.MOE_E_INVALID
+    assert L.moe_stack_plan_create(one_null, 1, None, 1, None, None, None, None) == B.MOE_E_INVALID
+    assert L.moe_stack_plan_run(None, None) == B.MOE_E_INVALID
+    L.moe_stack_plan_destroy(None)
     # expert slots and tiled prefill: argument checks happen before anything touches a device
     assert L.moe_slot_lookup(None, None, 1, None, None) == B.MOE_E_INVALID
     assert L.moe_slot_faults(None, 0, None, None) == B.MOE_E_INVALID

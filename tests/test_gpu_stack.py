@@ -128,3 +128,48 @@ def test_stack_rejects_mixed_widths_and_capacity():
     assert torch.equal(h, h0)
     a.close()
     b.close()
+
+
+def test_stack_plan_replays_match_the_direct_call():
+    """moe_stack_plan_create records the stack call once; every replay on the same buffers gives,
+    bit for bit, the direct call's h, x_buf and y_buf, with other work on the same layers (direct
+    calls on other buffers) and host copies of the next token's stream between the replays."""
+    w = synth.WORKLOADS["stack"]
+    D = w.dims
+    NL = 6
+    dev = torch.device("cuda:0")
+    layers = [DeviceLayer(synth.workload_layer(w, l), max_tokens=CALL, device=dev) for l in range(NL)]
+    handles = [L.handle for L in layers]
+    h0 = tokens_to_device(synth.gen_stack_tokens(D, 40, w.seed + 7), dev)
+    for T in (1, 4):
+        h = torch.empty((T, D.d_model), dtype=torch.int16, device=dev)
+        xb, hb = torch.empty_like(h), torch.empty_like(h)
+        yb = torch.empty((T, D.d_model), dtype=torch.float32, device=dev)
+        h2, xb2, hb2 = torch.empty_like(h), torch.empty_like(h), torch.empty_like(h)
+        yb2 = torch.empty_like(yb)
+        plan = B.moe_stack_plan_create(handles, h, T, xb, yb, hb)
+        try:
+            for step in range(8):
+                toks = h0[T * step: T * step + T]
+                h2.copy_(toks)
+                B.moe_stack_forward_decode(handles, h2, T, xb2, yb2, hb2)   # the direct call
+                h.copy_(toks)
+                B.moe_stack_plan_run(plan)
+                torch.cuda.synchronize()
+                np.testing.assert_array_equal(bits(h), bits(h2))
+                np.testing.assert_array_equal(bits(xb), bits(xb2))
+                np.testing.assert_array_equal(yb.cpu().numpy().view(np.uint32), yb2.cpu().numpy().view(np.uint32))
+        finally:
+            B.moe_stack_plan_destroy(plan)
+        say(f"stack plan, {NL} layers, T={T}: 8 replays bit-identical to the direct call")
+    # calls that read device memory back cannot be recorded
+    B.moe_profile_enable(handles[2], True)
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_stack_plan_create(handles, h, 1, xb, yb, hb)
+    assert ei.value.status == B.MOE_E_INVALID
+    B.moe_profile_enable(handles[2], False)
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_stack_plan_create(handles, h, CALL + 1, xb, yb, hb)
+    assert ei.value.status == B.MOE_E_CAPACITY
+    for L in layers:
+        L.close()
